@@ -1,0 +1,407 @@
+"""CPU oracle of one GPU's MoE expert layer.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import this module.  The GPU library
+never calls it and shares no code with it; the two meet only through the
+seeded generators in ``moe_synth``.
+
+Plain NumPy in fp64, one expert at a time, no blocking or fusion beyond what
+each definition states.  Inputs are the exact stored values (bf16 or fp32),
+widened to fp64.
+
+Pages cited (by title; sections as they appear on each page):
+  [MSR]  "MegaScale-MoE: 大规模通信高效的生产级混合专家模型训练系统"
+         (paper review on xllm-io.github.io)
+  [MSD]  "MegaScale-MoE: Large-Scale Communication-Efficient Training of
+         Mixture-of-Experts Models in Production" (research digest,
+         AI training network primer)
+  [DMoE] "DisagMoE：通过解耦的 AF-Pipe 并行实现计算与通信重叠的 MoE 训练"
+
+Readings of points the pages leave open (each also recorded in the design
+notes): softmax over the k selected logits; ties broken by lower expert index;
+SwiGLU = SiLU(x W1) * (x W3) then W2; gate weights applied in the combine;
+dropless dispatch ordered by expert then token; FP8 = OCP E4M3FN with
+round-to-nearest-even and saturation at +-448, per-token activation scales
+amax/448 and per-output-channel weight scales.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+E4M3_MAX = 448.0
+
+
+# --------------------------------------------------------------------------
+# Routing.  [DMoE] §2.1 / Fig. 2(a): a trainable gate scores every expert and
+# each token goes to its k highest-scoring experts, whose outputs are summed
+# with weights.  [MSR] §三, training flow: routing precedes dispatch.
+# --------------------------------------------------------------------------
+
+def router_logits(x: np.ndarray, w_gate: np.ndarray, bias: np.ndarray | None = None) -> np.ndarray:
+    """Gate GEMM ``L = x @ W_g (+ b)``.
+
+    The product is formed in fp64 and rounded once to fp32; the bias is then
+    added in fp32.  These fp32 logits are what the top-k step consumes.
+    """
+    L = (np.asarray(x, np.float64) @ np.asarray(w_gate, np.float64)).astype(np.float32)
+    if bias is not None:
+        L = (L + np.asarray(bias, np.float32)).astype(np.float32)
+    return L
+
+
+def topk_softmax(logits: np.ndarray, k: int):
+    """Top-k experts per token and their gate weights.
+
+    Experts are ordered by logit (descending), ties by expert index
+    (ascending); slot j holds the j-th expert in that order.  The weights are
+    the softmax of the k selected logits, computed in fp64, stored fp32.
+    Returns ``idx`` int32 ``[T, k]`` and ``w`` fp32 ``[T, k]``.
+    """
+    L = np.asarray(logits, np.float32)
+    T, E = L.shape
+    if not 1 <= k <= E:
+        raise ValueError("need 1 <= k <= E")
+    # stable sort of the negated logits keeps equal logits in index order
+    order = np.argsort(-L, axis=1, kind="stable")
+    idx = order[:, :k].astype(np.int32)
+    sel = np.take_along_axis(L, idx, axis=1).astype(np.float64)
+    z = np.exp(sel - sel[:, :1])
+    w = (z / z.sum(axis=1, keepdims=True)).astype(np.float32)
+    return idx, w
+
+
+# --------------------------------------------------------------------------
+# Dispatch into expert-contiguous rows.  [MSR] §四, adaptive EP: an extra
+# local scatter makes each expert's tokens contiguous.  [MSD] §3.3 Diagram C:
+# rows are ordered by expert, then by source; on one GPU the source is the
+# token index.  No token is dropped.
+# --------------------------------------------------------------------------
+
+def build_index(idx: np.ndarray, E: int):
+    """Per-expert counts, offsets, and the row each (token, slot) lands in.
+
+    ``counts[e]`` = number of (t, j) with ``idx[t, j] == e``;
+    ``offsets`` = exclusive prefix sum of counts, ``offsets[E] = T*k``;
+    ``dst_row[t, j] = offsets[e] + #{t' < t routed to e}``;
+    ``src_tok[dst_row[t, j]] = t``.
+    """
+    idx = np.asarray(idx)
+    T, k = idx.shape
+    counts = np.zeros(E, dtype=np.int64)
+    for e in idx.ravel():
+        counts[e] += 1
+    offsets = np.zeros(E + 1, dtype=np.int64)
+    offsets[1:] = np.cumsum(counts)
+    nxt = offsets[:-1].copy()
+    dst_row = np.empty((T, k), dtype=np.int64)
+    src_tok = np.empty(T * k, dtype=np.int64)
+    for t in range(T):
+        for j in range(k):
+            e = idx[t, j]
+            dst_row[t, j] = nxt[e]
+            src_tok[nxt[e]] = t
+            nxt[e] += 1
+    return (counts.astype(np.int32), offsets.astype(np.int32),
+            dst_row.astype(np.int32), src_tok.astype(np.int32))
+
+
+def permute(x: np.ndarray, dst_row: np.ndarray, row_scale: np.ndarray | None = None) -> np.ndarray:
+    """``Xp[dst_row[t, j]] = x[t]`` (times ``row_scale[t, j]`` when given)."""
+    T, k = dst_row.shape
+    out = np.empty((T * k,) + x.shape[1:], dtype=np.float64 if row_scale is not None else x.dtype)
+    for j in range(k):
+        v = x if row_scale is None else np.asarray(x, np.float64) * np.asarray(row_scale[:, j], np.float64)[:, None]
+        out[dst_row[:, j]] = v
+    return out
+
+
+def combine(yp: np.ndarray, dst_row: np.ndarray, w: np.ndarray | None) -> np.ndarray:
+    """Weighted un-permute ``y[t] = sum_j w[t, j] * Yp[dst_row[t, j]]`` (fp64).
+
+    [MSR] §三 training flow, token aggregation; [DMoE] §2.1: the selected
+    experts' outputs are reduced by a weighted sum.  ``w=None`` means weight 1
+    (the transpose of the dispatch copy, used for dX).
+    """
+    T, k = dst_row.shape
+    y = np.zeros((T,) + yp.shape[1:], dtype=np.float64)
+    for j in range(k):
+        g = np.asarray(yp[dst_row[:, j]], np.float64)
+        y += g if w is None else np.asarray(w[:, j], np.float64)[:, None] * g
+    return y
+
+
+# --------------------------------------------------------------------------
+# SwiGLU experts.  [MSR] §三 core formulas: each expert is a SwiGLU FFN with
+# three h x h_ffn matrices; [MSR] §四 selective recomputation names the two
+# layers FC1 and FC2.  FC1 produces gate G = Xp W1 and up U = Xp W3, the
+# activation is SiLU(G) * U, FC2 multiplies by W2.
+# --------------------------------------------------------------------------
+
+def silu(z: np.ndarray) -> np.ndarray:
+    """SiLU(z) = z * sigmoid(z) = z / (1 + exp(-z)), fp64."""
+    z = np.asarray(z, np.float64)
+    with np.errstate(over="ignore"):
+        return z / (1.0 + np.exp(-z))
+
+
+def sigmoid(z: np.ndarray) -> np.ndarray:
+    z = np.asarray(z, np.float64)
+    with np.errstate(over="ignore"):
+        return 1.0 / (1.0 + np.exp(-z))
+
+
+def expert_forward(xp, offsets, w1, w3, w2, keep=True):
+    """FC1 -> SwiGLU -> FC2 for every expert's contiguous rows (fp64).
+
+    Returns ``yp`` and, when ``keep``, the intermediates ``g, u, a``.
+    """
+    R = xp.shape[0]
+    E = len(offsets) - 1
+    h = w2.shape[2]
+    yp = np.zeros((R, h), dtype=np.float64)
+    if keep:
+        hf = w1.shape[2]
+        g_all = np.zeros((R, hf)); u_all = np.zeros((R, hf)); a_all = np.zeros((R, hf))
+    for e in range(E):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        if hi == lo:
+            continue
+        xe = np.asarray(xp[lo:hi], np.float64)
+        g = xe @ np.asarray(w1[e], np.float64)
+        u = xe @ np.asarray(w3[e], np.float64)
+        a = silu(g) * u
+        yp[lo:hi] = a @ np.asarray(w2[e], np.float64)
+        if keep:
+            g_all[lo:hi] = g; u_all[lo:hi] = u; a_all[lo:hi] = a
+    if keep:
+        return yp, g_all, u_all, a_all
+    return yp
+
+
+def layer_forward(x, w_gate, bias, w1, w3, w2, k, logits=None):
+    """The whole forward layer: route, dispatch, experts, combine.
+
+    ``logits`` may be supplied (fp32) to skip the gate GEMM.  Returns a dict
+    with every intermediate; ``y`` is fp64 (the caller rounds to its output
+    type).
+    """
+    E = w1.shape[0]
+    L = router_logits(x, w_gate, bias) if logits is None else np.asarray(logits, np.float32)
+    idx, w = topk_softmax(L, k)
+    counts, offsets, dst_row, src_tok = build_index(idx, E)
+    xp = permute(x, dst_row)
+    yp, g, u, a = expert_forward(xp, offsets, w1, w3, w2)
+    y = combine(yp, dst_row, w)
+    return dict(logits=L, idx=idx, w=w, counts=counts, offsets=offsets, dst_row=dst_row,
+                src_tok=src_tok, xp=xp, g=g, u=u, a=a, yp=yp, y=y)
+
+
+def layer_forward_tokens(x_rows, idx_rows, w_rows, w1, w3, w2):
+    """Per-token form of the layer, without any permutation.
+
+    ``y[t] = sum_j w[t, j] * FFN_{idx[t, j]}(x[t])``.  Works on any subset of
+    tokens, so it checks sampled outputs of a full-size run; it streams one
+    expert's weights at a time.
+    """
+    x_rows = np.asarray(x_rows, np.float64)
+    n = x_rows.shape[0]
+    y = np.zeros((n, w2.shape[2]), dtype=np.float64)
+    for e in np.unique(idx_rows):
+        tt, jj = np.nonzero(idx_rows == e)
+        xe = x_rows[tt]
+        a = silu(xe @ np.asarray(w1[e], np.float64)) * (xe @ np.asarray(w3[e], np.float64))
+        y[tt] += np.asarray(w_rows[tt, jj], np.float64)[:, None] * (a @ np.asarray(w2[e], np.float64))
+    return y
+
+
+# --------------------------------------------------------------------------
+# Backward of the expert path (routing held fixed).  [MSR] §四 selective
+# activation recomputation: FC2's backward needs its input and the gradient
+# of its output, and FC2's input is recomputed rather than stored; FC1's
+# input is obtained again rather than kept.  [MSR] §三 parameter update:
+# gradients accumulate in FP32.
+# --------------------------------------------------------------------------
+
+def layer_backward(dy, x, w, dst_row, offsets, w1, w3, w2, g=None, u=None):
+    """Gradients of ``y`` w.r.t. ``x`` (expert path only) and every expert weight.
+
+    dYp[dst_row[t,j]] = w[t,j] * dY[t]
+    dA = dYp W2^T;  dW2_e = A_e^T dYp_e
+    s = sigmoid(G); dG = dA * U * s * (1 + G (1 - s));  dU = dA * SiLU(G)
+    dXp = dG W1^T + dU W3^T;  dW1_e = Xp_e^T dG_e;  dW3_e = Xp_e^T dU_e
+    dX[t] = sum_j dXp[dst_row[t, j]]
+    All fp64.
+    """
+    E = w1.shape[0]
+    xp = permute(np.asarray(x, np.float64), dst_row)
+    dyp = permute(np.asarray(dy, np.float64), dst_row, row_scale=w)
+    R, h = xp.shape
+    dxp = np.zeros((R, h))
+    dw1 = np.zeros(w1.shape); dw3 = np.zeros(w3.shape); dw2 = np.zeros(w2.shape)
+    for e in range(E):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        if hi == lo:
+            continue
+        W1 = np.asarray(w1[e], np.float64); W3 = np.asarray(w3[e], np.float64)
+        W2 = np.asarray(w2[e], np.float64)
+        xe = xp[lo:hi]
+        ge = xe @ W1 if g is None else np.asarray(g[lo:hi], np.float64)
+        ue = xe @ W3 if u is None else np.asarray(u[lo:hi], np.float64)
+        s = sigmoid(ge)
+        a = ge * s * ue
+        dye = dyp[lo:hi]
+        da = dye @ W2.T
+        dw2[e] = a.T @ dye
+        dg = da * ue * s * (1.0 + ge * (1.0 - s))
+        du = da * ge * s
+        dxp[lo:hi] = dg @ W1.T + du @ W3.T
+        dw1[e] = xe.T @ dg
+        dw3[e] = xe.T @ du
+    dx = combine(dxp, dst_row, None)
+    return dict(dx=dx, dw1=dw1, dw3=dw3, dw2=dw2, dxp=dxp, dyp=dyp)
+
+
+# --------------------------------------------------------------------------
+# FP8 (E4M3) with per-token activation scales.  [MSR] §三 communication
+# compression layer and §四 (FP8 training row): per-token scales replace a
+# single per-tensor scale because SwiGLU widens the value range.  [MSD] §3.4:
+# FP8 traffic carries per-token scales and is summed in FP32.
+# --------------------------------------------------------------------------
+
+def e4m3_decode(codes: np.ndarray) -> np.ndarray:
+    """OCP E4M3FN code -> value (fp64).  0x7F / 0xFF are NaN."""
+    c = np.asarray(codes, np.uint8).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    ex = (c >> 3) & 0xF
+    man = c & 0x7
+    val = np.where(ex == 0, man * 2.0 ** -9, (1.0 + man / 8.0) * np.exp2(ex - 7.0))
+    val = np.where((c & 0x7F) == 0x7F, np.nan, val)
+    return sign * val
+
+
+def e4m3_encode(v: np.ndarray) -> np.ndarray:
+    """Value -> OCP E4M3FN code, round to nearest (ties to even), saturating.
+
+    Magnitudes above 448 map to 448.  The grid spacing is 2^-9 below 2^-6
+    (subnormals) and 2^(e-3) in [2^e, 2^(e+1)).  Rounding is done on the
+    exact input value (fp32 or fp64 input, evaluated in fp64).
+    """
+    v = np.asarray(v, np.float64)
+    neg = np.signbit(v)
+    a = np.minimum(np.abs(v), E4M3_MAX)
+    _, e2 = np.frexp(np.where(a > 0, a, 1.0))      # a = m * 2^e2, m in [0.5, 1)
+    e = np.maximum(e2 - 1, -6)                       # exponent of the binade, floored at the subnormal one
+    spacing = np.exp2(e - 3.0)
+    q = np.round(a / spacing) * spacing              # numpy rounds half to even
+    q = np.minimum(q, E4M3_MAX)
+    sub = q < 2.0 ** -6
+    _, qe2 = np.frexp(np.where(q > 0, q, 1.0))
+    qe = qe2 - 1
+    man_n = np.round((q / np.exp2(qe) - 1.0) * 8.0).astype(np.int64)
+    code_n = ((qe + 7) << 3) | man_n
+    code_s = np.round(q / 2.0 ** -9).astype(np.int64)
+    code = np.where(sub, code_s, code_n)
+    code = np.where(neg, code | 0x80, code)
+    return code.astype(np.uint8)
+
+
+def quant_scale(amax) -> np.ndarray:
+    """Scale ``amax / 448`` in fp32 (1 where amax is 0)."""
+    amax = np.asarray(amax, np.float32)
+    s = (amax / np.float32(E4M3_MAX)).astype(np.float32)
+    return np.where(amax > 0, s, np.float32(1.0)).astype(np.float32)
+
+
+def quantize_rows(v: np.ndarray):
+    """Per-row (per-token) quantization of fp32 values.
+
+    ``s[r] = amax_c |v[r, c]| / 448`` and ``q = E4M3(v / s)`` with the
+    division done in fp32.  Returns codes uint8 and scales fp32.
+    """
+    v = np.asarray(v, np.float32)
+    s = quant_scale(np.max(np.abs(v), axis=-1) if v.shape[-1] else np.zeros(v.shape[:-1]))
+    q = e4m3_encode((v / s[..., None]).astype(np.float32))
+    return q, s
+
+
+def quantize_cols(wm: np.ndarray):
+    """Per-output-channel quantization of a weight ``[in, out]`` (fp32 values).
+
+    ``s[n] = amax_i |W[i, n]| / 448``; ``q[i, n] = E4M3(W[i, n] / s[n])``.
+    """
+    wm = np.asarray(wm, np.float32)
+    s = quant_scale(np.max(np.abs(wm), axis=0))
+    q = e4m3_encode((wm / s[None, :]).astype(np.float32))
+    return q, s
+
+
+def layer_forward_fp8(x, w_gate, bias, w1, w3, w2, k, logits=None):
+    """Forward layer with FP8 GEMM inputs (quantization emulated exactly).
+
+    x is quantized per token before the dispatch copy, so each routed row
+    keeps its token's scale; W1, W3 per output channel over h, W2 per output
+    channel over h_ffn; FC1 result = (q_x . q_w) * s_x * s_w; A is quantized
+    per routed row from its fp64 value; FC2 result = (q_a . q_w2) * s_a * s_w2.
+    """
+    E = w1.shape[0]
+    L = router_logits(x, w_gate, bias) if logits is None else np.asarray(logits, np.float32)
+    idx, w = topk_softmax(L, k)
+    counts, offsets, dst_row, src_tok = build_index(idx, E)
+    qx, sx = quantize_rows(x)
+    qxp = permute(qx, dst_row)
+    sxp = sx[src_tok]
+    R = qxp.shape[0]
+    h = w2.shape[2]
+    yp = np.zeros((R, h))
+    a_all = np.zeros((R, w1.shape[2]))
+    qa_all = np.zeros((R, w1.shape[2]), np.uint8)
+    sa_all = np.ones(R, np.float64)
+    for e in range(E):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        if hi == lo:
+            continue
+        q1, s1 = quantize_cols(w1[e]); q3, s3 = quantize_cols(w3[e]); q2, s2 = quantize_cols(w2[e])
+        xe = e4m3_decode(qxp[lo:hi])
+        g = (xe @ e4m3_decode(q1)) * sxp[lo:hi, None].astype(np.float64) * s1[None, :].astype(np.float64)
+        u = (xe @ e4m3_decode(q3)) * sxp[lo:hi, None].astype(np.float64) * s3[None, :].astype(np.float64)
+        a = silu(g) * u
+        amax = np.max(np.abs(a), axis=1)
+        sa = np.where(amax > 0, amax / E4M3_MAX, 1.0)
+        qa = e4m3_encode(a / sa[:, None])
+        yp[lo:hi] = (e4m3_decode(qa) @ e4m3_decode(q2)) * sa[:, None] * s2[None, :].astype(np.float64)
+        a_all[lo:hi] = a; qa_all[lo:hi] = qa; sa_all[lo:hi] = sa
+    y = combine(yp, dst_row, w)
+    return dict(logits=L, idx=idx, w=w, counts=counts, offsets=offsets, dst_row=dst_row,
+                src_tok=src_tok, qx=qx, sx=sx, a=a_all, qa=qa_all, sa=sa_all, yp=yp, y=y)
+
+
+def layer_forward_fp8_tokens(x_rows, idx_rows, w_rows, w1, w3, w2, wq_cache=None):
+    """Per-token form of :func:`layer_forward_fp8` for sampled tokens."""
+    qx, sx = quantize_rows(x_rows)
+    xd = e4m3_decode(qx) * sx[:, None].astype(np.float64)
+    n = xd.shape[0]
+    y = np.zeros((n, w2.shape[2]))
+    cache = {} if wq_cache is None else wq_cache
+    for e in np.unique(idx_rows):
+        if e not in cache:
+            cache[e] = (quantize_cols(w1[e]), quantize_cols(w3[e]), quantize_cols(w2[e]))
+        (q1, s1), (q3, s3), (q2, s2) = cache[e]
+        tt, jj = np.nonzero(idx_rows == e)
+        xe = xd[tt]
+        g = (xe @ e4m3_decode(q1)) * s1[None, :].astype(np.float64)
+        u = (xe @ e4m3_decode(q3)) * s3[None, :].astype(np.float64)
+        a = silu(g) * u
+        amax = np.max(np.abs(a), axis=1)
+        sa = np.where(amax > 0, amax / E4M3_MAX, 1.0)
+        qa = e4m3_encode(a / sa[:, None])
+        ye = (e4m3_decode(qa) @ e4m3_decode(q2)) * sa[:, None] * s2[None, :].astype(np.float64)
+        y[tt] += np.asarray(w_rows[tt, jj], np.float64)[:, None] * ye
+    return y
+
+
+def topk_margin(logits: np.ndarray, k: int) -> np.ndarray:
+    """Gap between the k-th and (k+1)-th largest logit per token (inf if k == E)."""
+    L = np.sort(np.asarray(logits, np.float64), axis=1)[:, ::-1]
+    if k >= L.shape[1]:
+        return np.full(L.shape[0], np.inf)
+    return L[:, k - 1] - L[:, k]

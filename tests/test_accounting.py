@@ -1,0 +1,58 @@
+"""The byte / FLOP accounting reproduces the values the pages print."""
+import json
+import os
+
+import pytest
+
+import moe_synth
+from mixture_experts_layer_24_amd import accounting as acc
+
+G = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "page_numbers.json")))
+
+
+def test_worked_byte_table():
+    g = G["digest_3_2_worked_table"]
+    b, s, h, n, m, k = g["b"], g["s"], g["h"], g["n"], g["m"], g["k"]
+    assert acc.activation_bytes(b, s, h) / 1e6 == pytest.approx(g["activations_MB"], abs=0.05)
+    tp = acc.tp_attn_volume(b, s, h, n)
+    sp = acc.sp_attn_volume(b, s, h, n, m)
+    ep = acc.ep_ffn_volume(b, s, h, n, k)
+    assert tp / 1e6 == pytest.approx(g["tp_attention_MB"], abs=0.05)
+    assert sp / 1e6 == pytest.approx(g["sp_attention_MB"], abs=0.05)
+    assert ep / 1e6 == pytest.approx(g["ep_all_to_all_MB"], abs=0.05)
+    assert acc.tp_ffn_volume(b, s, h, n) == tp
+    assert (2 * tp) / (sp + ep) == pytest.approx(g["layer_ratio"], abs=0.05)
+    assert acc.dispatch_bytes_per_token(k, h) == g["dispatch_bytes_per_token"]
+    # the 352B workload's per-token dispatch write is the same figure
+    wl = moe_synth.WORKLOADS["m352b_zipf"]
+    assert wl.k * wl.h * 2 == g["dispatch_bytes_per_token"]
+
+
+def test_ratio_R():
+    g = G["digest_3_4_ratio"]
+    r = lambda hf, bw: acc.comp_comm_ratio(hf, bw, g["peak"], g["n"])
+    assert r(g["h_ff_352B"], g["nvlink"]) == pytest.approx(g["R_352B_nvlink"], abs=0.05)
+    assert r(g["h_ff_352B"], g["nic"]) == pytest.approx(g["R_352B_nic"], abs=0.05)
+    assert r(g["h_ff_dsmoe"], g["nvlink"]) == pytest.approx(g["R_dsmoe_nvlink"], abs=0.005)
+
+
+def test_throughput_check():
+    g = G["digest_5_throughput"]
+    assert g["batch"] * g["seq"] / g["step_s"] / 1e6 == pytest.approx(g["tokens_per_s_M"], abs=0.005)
+
+
+def test_workload_shapes_follow_model_table():
+    shapes = G["model_shapes"]
+    pairs = {"mixtral": "Mixtral-8x7B", "dsmoe": "DeepSeekMoE", "m352b_zipf": "Internal-352B",
+             "hunyuan_fp8": "Hunyuan-Large"}
+    for key, model in pairs.items():
+        wl = moe_synth.WORKLOADS[key]
+        assert dict(h=wl.h, h_ffn=wl.h_ffn, E=wl.E, k=wl.k) == shapes[model]
+
+
+def test_mixtral_counts():
+    c = acc.workload_counts(moe_synth.WORKLOADS["mixtral"])
+    assert c["R"] == 16384
+    assert c["flops_fwd"] == 6 * 16384 * 4096 * 14336
+    assert c["flops_fc1"] + c["flops_fc2"] == c["flops_fwd"]
+    assert c["permute_bytes"] == 8192 * 4096 * 2 + 16384 * 4096 * 2 + 4 * 16384

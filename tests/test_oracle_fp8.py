@@ -1,0 +1,101 @@
+"""Pins for the oracle's FP8 (OCP E4M3FN) codec and per-token / per-channel scales.
+
+Pins: torch's CPU ``float8_e4m3fn`` decode of all 256 codes and its cast of
+values within +-448 (a library routine), hand-listed boundary codes of the
+format, exact midpoints (ties to even) and the saturation rule.
+"""
+import numpy as np
+import pytest
+import torch
+
+import moe_synth
+from oracle import moe_ref as ref
+
+
+def _torch_decode(codes):
+    return torch.from_numpy(np.asarray(codes, np.uint8)).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+
+
+def _torch_encode(v):
+    return torch.from_numpy(np.asarray(v, np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def test_decode_all_codes():
+    codes = np.arange(256, dtype=np.uint8)
+    mine = ref.e4m3_decode(codes)
+    lib = _torch_decode(codes)
+    nan = np.isnan(lib)
+    assert nan.sum() == 2 and np.array_equal(np.isnan(mine), nan)
+    np.testing.assert_array_equal(mine[~nan], lib[~nan])
+
+
+def test_boundary_codes():
+    dec = ref.e4m3_decode
+    assert dec(np.uint8(0x7E)) == 448.0
+    assert dec(np.uint8(0x01)) == 2.0 ** -9          # smallest subnormal
+    assert dec(np.uint8(0x07)) == 7 * 2.0 ** -9      # largest subnormal
+    assert dec(np.uint8(0x08)) == 2.0 ** -6          # smallest normal
+    assert dec(np.uint8(0x38)) == 1.0
+    assert dec(np.uint8(0xB8)) == -1.0
+
+
+def test_roundtrip_all_finite_codes():
+    codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], np.uint8)
+    np.testing.assert_array_equal(ref.e4m3_encode(ref.e4m3_decode(codes)), codes)
+
+
+def test_encode_matches_torch_within_range():
+    rng = np.random.default_rng(0)
+    mags = np.exp2(rng.uniform(-13, np.log2(448.0), 200000))
+    v = (mags * rng.choice([-1, 1], mags.size)).astype(np.float32)
+    np.testing.assert_array_equal(ref.e4m3_encode(v), _torch_encode(v))
+
+
+def test_midpoints_round_to_even():
+    codes = np.arange(0, 0x7E, dtype=np.uint8)
+    lo = ref.e4m3_decode(codes); hi = ref.e4m3_decode(codes + 1)
+    mid = ((lo + hi) / 2).astype(np.float32)
+    assert np.all(mid.astype(np.float64) == (lo + hi) / 2)    # midpoints are exact in fp32
+    got = ref.e4m3_encode(mid)
+    want = np.where(codes % 2 == 0, codes, codes + 1)
+    np.testing.assert_array_equal(got, want.astype(np.uint8))
+    np.testing.assert_array_equal(got, _torch_encode(mid))
+
+
+def test_saturation():
+    v = np.array([448.0, 449.0, 463.99, 464.0, 1e6, np.float32(3e38)], np.float32)
+    assert ref.e4m3_encode(v).tolist() == [0x7E] * 6
+    assert ref.e4m3_encode(-v).tolist() == [0xFE] * 6
+
+
+def test_row_and_column_scales():
+    rng = np.random.default_rng(1)
+    x = rng.standard_normal((6, 40)).astype(np.float32)
+    x[3] = 0
+    q, s = ref.quantize_rows(x)
+    assert s.dtype == np.float32 and s[3] == 1.0 and np.all(q[3] == 0)
+    for r in (0, 1, 2, 4, 5):
+        c = int(np.argmax(np.abs(x[r])))
+        assert q[r, c] in (0x7E, 0xFE)
+        assert s[r] == np.float32(np.abs(x[r]).max() / np.float32(448.0))
+    err = np.abs(ref.e4m3_decode(q) * s[:, None] - x)
+    assert np.all(err <= np.abs(x) * 2 ** -4 + s[:, None] * 2.0 ** -10)
+    w = rng.standard_normal((40, 7)).astype(np.float32)
+    qw, sw = ref.quantize_cols(w)
+    np.testing.assert_array_equal(qw.T, ref.quantize_rows(w.T)[0])
+    np.testing.assert_array_equal(sw, ref.quantize_rows(w.T)[1])
+
+
+def test_fp8_layer_close_to_exact_layer():
+    wl = moe_synth.WORKLOADS["tiny"].scaled(k=1)
+    inp = moe_synth.gen_all(wl, seed=3)
+    args = (inp["x"], inp["w_gate"], inp["bias"], inp["w1"], inp["w3"], inp["w2"], wl.k)
+    exact = ref.layer_forward(*args)["y"]
+    q = ref.layer_forward_fp8(*args)
+    rms = np.sqrt(np.mean(exact ** 2))
+    err = q["y"] - exact
+    # three E4M3 roundings (x, weights, SwiGLU output) of about 2^-4 relative
+    # each: the layer error is a few percent of rms, and not zero
+    assert 1e-3 * rms < np.sqrt(np.mean(err ** 2)) < 0.1 * rms
+    yt = ref.layer_forward_fp8_tokens(inp["x"], q["idx"], q["w"], inp["w1"], inp["w3"], inp["w2"])
+    np.testing.assert_allclose(q["y"], yt, rtol=1e-12, atol=1e-12 * rms)
