@@ -1,0 +1,172 @@
+#!/usr/bin/env python3
+"""Benchmark one MoE expert layer step on one MI355X.
+
+A step is the whole hot path on one batch: route (gate GEMM + top-k softmax)
+-> dispatch (index build + permute) -> grouped SwiGLU GEMMs -> weighted
+combine, plus the backward for workloads that train.  Inputs are seeded,
+synthetic and already resident in HBM when the timed region starts; weights
+are packed once before it.
+
+Prints ONE JSON line (see the repository's design notes for every field).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK = {"bf16": 2.5e15, "fp8": 5.0e15, "f32": 157.3e12}   # dense MFMA FLOP/s, MI355X
+HBM_PEAK = 8.0e12                                          # B/s
+METRIC = "MoE layer tokens/s and GroupedGEMM TFLOP/s (% of MFMA peak) on 1 MI355X"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def cpu_baseline(wl, inp, n_tokens, seed=0):
+    """Time the CPU oracle on the first n_tokens tokens of the same batch."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from moe_synth import to_f32
+    from oracle import moe_ref as ref
+
+    class PerExpert:
+        def __init__(self, a):
+            self.a, self.shape = a, a.shape
+
+        def __getitem__(self, e):
+            return to_f32(self.a[e])
+
+    x = to_f32(inp["x"][:n_tokens])
+    wg = to_f32(inp["w_gate"])
+    w1, w3, w2 = PerExpert(inp["w1"]), PerExpert(inp["w3"]), PerExpert(inp["w2"])
+    t0 = time.perf_counter()
+    if wl.dtype == "fp8":
+        ref.layer_forward_fp8(x, wg, inp["bias"], w1, w3, w2, wl.k)
+    else:
+        out = ref.layer_forward(x, wg, inp["bias"], w1, w3, w2, wl.k)
+        if wl.backward:
+            dy = to_f32(inp["dy"][:n_tokens])
+            ref.layer_backward(dy, x, out["w"], out["dst_row"], out["offsets"], w1, w3, w2,
+                               g=out["g"], u=out["u"])
+    dt = time.perf_counter() - t0
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    return {"value": n_tokens / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"first {n_tokens} of {wl.T} tokens of the same seeded batch, full layer "
+                      f"{'fwd+bwd' if wl.backward else 'fwd'} in fp64 NumPy ({dt:.1f} s)"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="mixtral")
+    ap.add_argument("--cpu-tokens", type=int, default=2048,
+                    help="tokens in the CPU oracle sample (0 = skip)")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE={world}); "
+              "the multi-GPU layout is a design in the notes, not built here.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import moe_synth
+    from mixture_experts_layer_24_amd import accounting as acc
+    from mixture_experts_layer_24_amd import ops
+    from mixture_experts_layer_24_amd._lib import MOE_BF16, MOE_F32, MOE_FP8_E4M3
+
+    wl = moe_synth.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    log(f"bench: generating {wl.name} inputs")
+    inp = moe_synth.gen_all(wl, seed=0)
+
+    def t(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(a).to(dev)
+
+    code = {"f32": MOE_F32, "bf16": MOE_BF16, "fp8": MOE_FP8_E4M3}[wl.dtype]
+    x, wg, bias = t(inp["x"]), t(inp["w_gate"]), torch.from_numpy(inp["bias"]).to(dev)
+    w1, w3, w2 = t(inp["w1"]), t(inp["w3"]), t(inp["w2"])
+    P = ops.PackedWeights(w1, w3, w2, code)
+    del w1, w3, w2
+    layer = ops.MoELayer(wl.T, wl.h, wl.h_ffn, wl.E, wl.k, code, device=dev,
+                         save_for_backward=wl.backward)
+    dy = t(inp["dy"]) if wl.backward else None
+
+    def step():
+        layer.forward(x, wg, bias, P)
+        if wl.backward:
+            layer.backward(dy, x, P)
+
+    log(f"bench: warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"bench: timing {args.steps} steps")
+    ops.moe_timing_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    kern = ops.moe_timing_report()
+    ops.moe_timing_enable(False)
+    ms = elapsed * 1e3 / args.steps
+    counts = acc.workload_counts(wl)
+    avg = {k: v[1] / v[0] for k, v in kern.items()}          # ms per launch
+    per_step = {k: v[1] / args.steps for k, v in kern.items()}
+    flops_step = counts["flops_fwd"] + counts.get("flops_bwd", 0)
+    gemm_ms = sum(per_step.get(k, 0.0) for k in ("fc1", "fc2", "bwd_dA", "bwd_dW2", "bwd_dXp", "bwd_dW13"))
+    peak = PEAK[wl.dtype]
+    gemm_tflops = flops_step / (gemm_ms * 1e-3) / 1e12 if gemm_ms else None
+
+    dom = max(per_step, key=per_step.get)
+    flops_per_launch = {"fc1": counts["flops_fc1"], "fc2": counts["flops_fc2"]}
+    bytes_per_launch = {"permute": counts["permute_bytes"], "combine": counts["combine_bytes"],
+                        "route": counts["router_bytes"]}
+    if dom in flops_per_launch:
+        achieved = flops_per_launch[dom] / (avg[dom] * 1e-3)
+        roof = {"kernel": dom, "bound": "mfma", "achieved": achieved / 1e12, "peak": peak / 1e12,
+                "unit": "TFLOP/s", "frac": achieved / peak, "traffic": None}
+    else:
+        achieved = bytes_per_launch.get(dom, 0) / (avg[dom] * 1e-3)
+        roof = {"kernel": dom, "bound": "hbm", "achieved": achieved / 1e9, "peak": HBM_PEAK / 1e9,
+                "unit": "GB/s", "frac": achieved / HBM_PEAK, "traffic": None}
+    hbm = {}
+    for k2, b in bytes_per_launch.items():
+        if k2 in avg:
+            bw = b / (avg[k2] * 1e-3)
+            hbm[k2] = {"GB/s": round(bw / 1e9, 1), "frac": round(bw / HBM_PEAK, 4)}
+    out = {
+        "metric": METRIC, "value": wl.T / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": wl.dtype, "data": "synthetic",
+        "config": {"workload": f"{wl.name} MoE layer {'fwd+bwd' if wl.backward else 'fwd'}",
+                   "T": wl.T, "h": wl.h, "h_ffn": wl.h_ffn, "E": wl.E, "k": wl.k},
+        "gemm_tflops": gemm_tflops, "gemm_frac_of_peak": (gemm_tflops * 1e12 / peak) if gemm_tflops else None,
+        "kernel_ms_per_step": {k: round(v, 4) for k, v in per_step.items()},
+        "hbm": hbm,
+        "roofline": roof,
+    }
+    if args.cpu_tokens > 0:
+        log(f"bench: cpu oracle on {args.cpu_tokens} tokens")
+        out["cpu_baseline"] = cpu_baseline(wl, inp, min(args.cpu_tokens, wl.T))
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

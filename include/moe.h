@@ -1,0 +1,243 @@
+/*
+ * moe.h -- C ABI of one GPU's mixture-of-experts (MoE) expert layer on
+ * AMD MI355X (gfx950).
+ *
+ * The layer, as the MegaScale-MoE pages describe it:
+ *   route    -- a trainable gate scores the E experts of each token and keeps
+ *               the k best ("MegaScale-MoE: 大规模通信高效的生产级混合专家模型
+ *               训练系统", §三 MoE layer structure / Fig. 2 and the training
+ *               flow; DisagMoE page, §2.1 / Fig. 2(a));
+ *   permute  -- a local scatter makes every expert's tokens contiguous,
+ *               ordered by expert then by source (same review, §四 adaptive
+ *               EP communication; MegaScale-MoE research digest, §3.3
+ *               Diagram C);
+ *   grouped  -- one GroupedGEMM runs every expert's SwiGLU FFN: FC1 (gate
+ *               and up projections), SiLU(gate)*up, FC2 (review §三 core
+ *               formulas and §四 selective activation recomputation; digest
+ *               §3.3);
+ *   combine  -- each token's k expert outputs are summed with the gate
+ *               weights (review §三 training flow, token aggregation);
+ *   backward -- FC2/FC1 gradients with FC2's input recomputed, FP32 weight
+ *               gradients (review §四 selective recomputation, §三 parameter
+ *               update);
+ *   FP8      -- per-token E4M3 scales for activations (review §三
+ *               communication-compression layer, §四 FP8 row; digest §3.4).
+ *
+ * Conventions for every call
+ *   - Row-major, contiguous tensors; row-vector math y = x W.
+ *   - Every tensor pointer is a DEVICE pointer owned by the caller.  The
+ *     library allocates nothing on these paths, frees nothing, and keeps no
+ *     pointer after the call returns.  Scratch memory comes from the caller
+ *     as a workspace sized by the matching *_workspace_size() call.
+ *   - Every call only validates its arguments on the host and enqueues
+ *     kernels on `stream` (a hipStream_t; NULL = the null stream).  Nothing
+ *     synchronizes the host and no count is copied back to the host.
+ *   - Pointers must be 16-byte aligned.
+ *   - Return value: MOE_OK, or a negative MOE_ERR_* code.  Arguments are
+ *     checked before any launch; on an error nothing is enqueued and no
+ *     output is touched.  moe_last_error() returns a message for the last
+ *     failing call of the calling thread.
+ *   - T = 0 (or rows = 0) is a successful no-op, except that moe_permute
+ *     still writes zero counts and offsets when it builds an index.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_OK 0
+#define MOE_ERR_ARG (-1)       /* NULL pointer, bad count, misaligned pointer */
+#define MOE_ERR_DTYPE (-2)     /* unsupported element type or combination     */
+#define MOE_ERR_SHAPE (-3)     /* dimension outside what the kernels support  */
+#define MOE_ERR_WORKSPACE (-4) /* workspace missing or too small              */
+#define MOE_ERR_HIP (-5)       /* a HIP launch or query failed                */
+
+#define MOE_MAX_EXPERTS 256    /* E <= MOE_MAX_EXPERTS                         */
+#define MOE_MAX_TOPK 16        /* k <= MOE_MAX_TOPK                            */
+
+/* Element types. */
+#define MOE_F32 0
+#define MOE_BF16 1
+#define MOE_FP8_E4M3 2         /* OCP E4M3FN: bias 7, max 448, no infinities   */
+
+/*
+ * Expert weights in the layout the GroupedGEMM reads (filled by
+ * moe_pack_weights into caller-allocated buffers).
+ *   w13  [E][2*h_ffn][h]  FC1 weights transposed (h contiguous).  Packed row
+ *        p holds gate channel (p/64)*32 + p%32 when (p/32) is even and up
+ *        channel (p/64)*32 + p%32 when it is odd, so every 64 packed rows
+ *        hold 32 gate channels followed by the same 32 up channels.
+ *   w2   [E][h][h_ffn]    FC2 weight transposed (h_ffn contiguous).
+ *   w13_scale [E][2*h_ffn], w2_scale [E][h]: FP8 only, per packed row
+ *        (= per output channel) dequantization scales; NULL otherwise.
+ *   dtype: MOE_F32, MOE_BF16 or MOE_FP8_E4M3.
+ */
+typedef struct {
+  int dtype;
+  int E, h, h_ffn;
+  const void* w13;
+  const void* w2;
+  const float* w13_scale;
+  const float* w2_scale;
+} moe_weights;
+
+/* Bytes needed for w13 (`which`=0), w2 (1), w13_scale (2), w2_scale (3). */
+size_t moe_packed_weight_bytes(int which, int E, int h, int h_ffn, int dtype);
+
+/*
+ * Pack (and for FP8, quantize) expert weights.  Set-up work, outside the
+ * per-step path.
+ *   w1, w3  [E][h][h_ffn]  gate / up projections, element type in_dtype
+ *   w2      [E][h_ffn][h]  down projection
+ *   in_dtype: MOE_F32 or MOE_BF16.  out_dtype: MOE_F32 (needs in F32),
+ *   MOE_BF16 (needs in BF16) or MOE_FP8_E4M3 (needs in BF16).
+ *   FP8: per output channel s = amax/448 over the input dimension (1 when the
+ *   channel is all zero); codes = E4M3(w / s) rounded to nearest even with
+ *   the division in fp32, saturating at +-448.
+ *   Outputs: see moe_weights; scales are written only for FP8 (may be NULL
+ *   otherwise).  h and h_ffn must be multiples of 128.
+ */
+int moe_pack_weights(const void* w1, const void* w3, const void* w2, int in_dtype, int E, int h,
+                     int h_ffn, int out_dtype, void* w13, void* w2_packed, float* w13_scale,
+                     float* w2_scale, void* stream);
+
+/*
+ * Router: gate GEMM, top-k and softmax over the k selected logits.
+ *   x       [T][h] (MOE_F32 or MOE_BF16 = dtype), or NULL: then `logits` is
+ *           an INPUT of fp32 router logits [T][E] and the gate GEMM is
+ *           skipped (used to compare routing bit for bit against another
+ *           implementation given identical logits).
+ *   w_gate  [h][E] same dtype as x (ignored when x is NULL).
+ *   bias    [E] fp32 added to the logits, or NULL for none.
+ *   logits  [T][E] fp32: written when x != NULL and logits != NULL.
+ *   topk_idx[T][k] int32: experts of each token by logit descending, equal
+ *           logits by expert index ascending.
+ *   topk_w  [T][k] fp32: softmax of the k selected logits (sums to 1; k = 1
+ *           gives exactly 1).
+ *   Logits are x W_g accumulated in fp32, then + bias in fp32.
+ *   Limits: 1 <= k <= E <= MOE_MAX_EXPERTS, k <= MOE_MAX_TOPK; h a multiple
+ *   of 64 when x != NULL.
+ */
+int moe_route(const void* x, const void* w_gate, const float* bias, float* logits, int T, int h,
+              int E, int k, int dtype, int32_t* topk_idx, float* topk_w, void* stream);
+
+/* Workspace bytes for moe_permute with index building (topk_idx != NULL). */
+size_t moe_permute_workspace_size(int T, int E, int k);
+
+/*
+ * Dispatch: build the expert-contiguous index and copy rows into it.
+ *   src      [T][h] element type src_dtype (MOE_F32 or MOE_BF16).
+ *   topk_idx [T][k] int32 expert ids, or NULL to reuse an index built by an
+ *            earlier call (then counts/offsets/src_tok are not touched and
+ *            dst_row is an INPUT).  Ids outside [0, E) are dropped:
+ *            dst_row = -1 and they are not counted.
+ *   row_scale[T][k] fp32 or NULL: when given, routed row (t, j) receives
+ *            row_scale[t][j] * src[t] (the transpose of the weighted combine,
+ *            used for the upstream gradient).
+ *   counts   [E]   int32 rows per expert.
+ *   offsets  [E+1] int32 exclusive prefix sum; offsets[E] = rows kept.
+ *   dst_row  [T][k] int32 row of (t, j) in dst: offsets[e] + number of
+ *            tokens t' < t routed to e.  As an input, entries outside
+ *            [0, T*k) are skipped.
+ *   src_tok  [T*k] int32 token of every routed row.
+ *   dst      [T*k][h] element type dst_dtype: MOE_F32 (src F32), MOE_BF16
+ *            (src BF16) or MOE_FP8_E4M3 (src BF16; per-token quantization:
+ *            dst_scale[row] = amax_t / 448 (1 for an all-zero row), codes =
+ *            E4M3(src / scale) with the division in fp32, nearest even,
+ *            saturating).  row_scale must be NULL for FP8.
+ *   dst_scale[T*k] fp32, FP8 only (NULL otherwise).
+ *   ws / ws_bytes: workspace, at least moe_permute_workspace_size(T, E, k)
+ *            bytes when topk_idx != NULL (may be NULL otherwise).
+ *   h must be a multiple of 8.
+ */
+int moe_permute(const void* src, int src_dtype, const int32_t* topk_idx, const float* row_scale,
+                int T, int h, int E, int k, int32_t* counts, int32_t* offsets, int32_t* dst_row,
+                int32_t* src_tok, void* dst, int dst_dtype, float* dst_scale, void* ws,
+                size_t ws_bytes, void* stream);
+
+/* Workspace bytes for moe_grouped_swiglu_fwd (rows = T*k). */
+size_t moe_grouped_workspace_size(int rows, int h, int h_ffn, int E, int dtype);
+
+/*
+ * Forward GroupedGEMM of every expert's SwiGLU FFN over expert-contiguous rows.
+ *   xp       [rows][h] routed rows, element type W->dtype (FP8: codes).
+ *   xp_scale [rows] fp32 per-row scales (FP8 only, else NULL).
+ *   W        packed weights (moe_pack_weights).
+ *   offsets  [E+1] int32 device array from moe_permute; rows of expert e are
+ *            offsets[e] .. offsets[e+1]-1; offsets[E] <= rows.
+ *   h13_save [rows][2*h_ffn] bf16 or NULL: when given, FC1's output is kept
+ *            for the backward, columns in the packed order of W->w13.
+ *   yp       [rows][h] expert outputs: fp32 for MOE_F32 weights, else bf16.
+ *   Math: G = xp W1_e, U = xp W3_e (fp32 accumulation), A = SiLU(G) * U,
+ *   yp = A W2_e.  FP8: G, U carry xp_scale[row] * w13_scale[e][channel]; A
+ *   is quantized per row (amax/448 over the row's h_ffn values) before FC2,
+ *   whose result carries that scale times w2_scale.
+ *   Rows >= offsets[E] of yp are left untouched.  offsets is read on the
+ *   device and clamped to [0, rows].
+ *   Limits: h and h_ffn multiples of 128.
+ */
+int moe_grouped_swiglu_fwd(const void* xp, const float* xp_scale, const moe_weights* W,
+                           const int32_t* offsets, int rows, void* h13_save, void* yp, void* ws,
+                           size_t ws_bytes, void* stream);
+
+/* Workspace bytes for moe_grouped_swiglu_bwd. */
+size_t moe_grouped_bwd_workspace_size(int rows, int h, int h_ffn, int E, int dtype);
+
+/*
+ * Backward of the GroupedGEMM (BF16 weights), routing held fixed.
+ *   dyp      [rows][h] bf16: gradient of yp (the weighted dispatch of dY).
+ *   xp       [rows][h] bf16: the forward's routed input (re-gathered).
+ *   h13_save [rows][2*h_ffn] bf16: FC1's output kept by the forward.
+ *   dxp      [rows][h] bf16 out: gradient of xp.
+ *   dw1, dw3 [E][h][h_ffn] fp32 out; dw2 [E][h_ffn][h] fp32 out (zero for an
+ *            expert without rows).
+ *   Math: A = SiLU(G) * U is recomputed from h13_save; dA = dyp W2^T;
+ *   dW2 = A^T dyp; dG = dA * U * s * (1 + G (1 - s)) with s = sigmoid(G);
+ *   dU = dA * SiLU(G); dxp = dG W1^T + dU W3^T; dW1 = xp^T dG;
+ *   dW3 = xp^T dU.  Products accumulate in fp32.
+ */
+int moe_grouped_swiglu_bwd(const void* dyp, const void* xp, const void* h13_save,
+                           const moe_weights* W, const int32_t* offsets, int rows, void* dxp,
+                           float* dw1, float* dw3, float* dw2, void* ws, size_t ws_bytes,
+                           void* stream);
+
+/*
+ * Combine: y[t] = sum_{j<k} topk_w[t][j] * yp[dst_row[t][j]], accumulated in
+ * fp32 in increasing j, then rounded (nearest even) to y_dtype.
+ *   yp       [*][h] element type yp_dtype (MOE_F32 or MOE_BF16).
+ *   dst_row  [T][k] int32 rows in [0, T*k); other entries are skipped.
+ *   topk_w   [T][k] fp32, or NULL for weight 1 (the transpose of the
+ *            dispatch copy, used for dX).
+ *   y        [T][h] element type y_dtype (MOE_F32 or MOE_BF16).
+ *   h must be a multiple of 8.
+ */
+int moe_combine(const void* yp, int yp_dtype, const int32_t* dst_row, const float* topk_w, int T,
+                int h, int k, void* y, int y_dtype, void* stream);
+
+/*
+ * Kernel timing for benchmarks.  moe_timing_enable(1) starts recording a pair
+ * of HIP events around every kernel this library launches (on the launch
+ * stream); moe_timing_enable(0) stops.  moe_timing_report() waits for the
+ * recorded events and writes one line per kernel kind, "name count total_ms",
+ * into buf (NUL-terminated, truncated to len), then clears the record.
+ * Recording adds host work per launch; leave it off outside measurements.
+ */
+int moe_timing_enable(int on);
+int moe_timing_report(char* buf, size_t len);
+
+/* Message of the last failing call on this thread ("" if none). */
+const char* moe_last_error(void);
+
+/* ABI version of this library. */
+int moe_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MI355X_H */

@@ -1,0 +1,247 @@
+// C ABI entry points: argument validation on the host, then kernel launches.
+// Nothing here allocates or synchronizes; see include/moe.h for the contract.
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "common.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+bool al16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+#define REQ(cond, code, ...) \
+  do {                        \
+    if (!(cond)) return fail(code, __VA_ARGS__); \
+  } while (0)
+#define PTR(p) REQ((p) != nullptr && al16(p), MOE_ERR_ARG, "%s must be a non-NULL 16-byte aligned pointer", #p)
+#define OPT(p) REQ((p) == nullptr || al16(p), MOE_ERR_ARG, "%s must be 16-byte aligned", #p)
+
+int launched(int rc, const char* what) {
+  if (rc == MOE_OK) return MOE_OK;
+  if (rc == MOE_ERR_HIP) return fail(rc, "%s: HIP launch failed (%s)", what, moe_launch::last_hip_error());
+  return fail(rc, "%s failed", what);
+}
+
+thread_local const char* g_hip_err = "";
+
+size_t esize(int dt) { return dt == MOE_F32 ? 4 : dt == MOE_BF16 ? 2 : 1; }
+
+}  // namespace
+
+namespace moe_launch {
+void clear_status() { (void)hipGetLastError(); }
+int launch_status() {
+  hipError_t e = hipGetLastError();
+  if (e == hipSuccess) return MOE_OK;
+  g_hip_err = hipGetErrorString(e);
+  return MOE_ERR_HIP;
+}
+const char* last_hip_error() { return g_hip_err; }
+
+int num_cus() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (!cached[dev]) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+}  // namespace moe_launch
+
+extern "C" {
+
+const char* moe_last_error(void) { return g_err; }
+
+int moe_version(void) { return 1; }
+
+size_t moe_packed_weight_bytes(int which, int E, int h, int h_ffn, int dtype) {
+  if (E <= 0 || h <= 0 || h_ffn <= 0 || dtype < MOE_F32 || dtype > MOE_FP8_E4M3) return 0;
+  size_t e = size_t(E), hh = size_t(h), hf = size_t(h_ffn);
+  switch (which) {
+    case 0: return e * 2 * hf * hh * esize(dtype);
+    case 1: return e * hh * hf * esize(dtype);
+    case 2: return dtype == MOE_FP8_E4M3 ? e * 2 * hf * 4 : 0;
+    case 3: return dtype == MOE_FP8_E4M3 ? e * hh * 4 : 0;
+  }
+  return 0;
+}
+
+int moe_pack_weights(const void* w1, const void* w3, const void* w2, int in_dtype, int E, int h,
+                     int h_ffn, int out_dtype, void* w13, void* w2_packed, float* w13_scale,
+                     float* w2_scale, void* stream) {
+  REQ(E >= 1 && E <= MOE_MAX_EXPERTS, MOE_ERR_SHAPE, "E=%d outside [1, %d]", E, MOE_MAX_EXPERTS);
+  REQ(h > 0 && h % 128 == 0 && h_ffn > 0 && h_ffn % 128 == 0, MOE_ERR_SHAPE,
+      "h=%d and h_ffn=%d must be positive multiples of 128", h, h_ffn);
+  bool ok = (in_dtype == MOE_F32 && out_dtype == MOE_F32) ||
+            (in_dtype == MOE_BF16 && (out_dtype == MOE_BF16 || out_dtype == MOE_FP8_E4M3));
+  REQ(ok, MOE_ERR_DTYPE, "unsupported pack %d -> %d", in_dtype, out_dtype);
+  PTR(w1); PTR(w3); PTR(w2); PTR(w13); PTR(w2_packed);
+  if (out_dtype == MOE_FP8_E4M3) { PTR(w13_scale); PTR(w2_scale); }
+  moe_launch::clear_status();
+  return launched(moe_launch::pack_weights(w1, w3, w2, in_dtype, E, h, h_ffn, out_dtype, w13,
+                                           w2_packed, w13_scale, w2_scale, (hipStream_t)stream),
+                  "moe_pack_weights");
+}
+
+int moe_route(const void* x, const void* w_gate, const float* bias, float* logits, int T, int h,
+              int E, int k, int dtype, int32_t* topk_idx, float* topk_w, void* stream) {
+  REQ(T >= 0, MOE_ERR_ARG, "T=%d is negative", T);
+  REQ(E >= 1 && E <= MOE_MAX_EXPERTS, MOE_ERR_SHAPE, "E=%d outside [1, %d]", E, MOE_MAX_EXPERTS);
+  REQ(k >= 1 && k <= E && k <= MOE_MAX_TOPK, MOE_ERR_ARG, "k=%d outside [1, min(E, %d)]", k,
+      MOE_MAX_TOPK);
+  PTR(topk_idx); PTR(topk_w); OPT(bias); OPT(logits);
+  if (x == nullptr) {
+    REQ(logits != nullptr, MOE_ERR_ARG, "logits must be given when x is NULL");
+  } else {
+    PTR(x); PTR(w_gate);
+    REQ(dtype == MOE_F32 || dtype == MOE_BF16, MOE_ERR_DTYPE, "router dtype %d unsupported", dtype);
+    REQ(h > 0 && (dtype == MOE_F32 || h % 64 == 0), MOE_ERR_SHAPE,
+        "h=%d must be a positive multiple of 64 for bf16", h);
+  }
+  if (T == 0) return MOE_OK;
+  moe_launch::clear_status();
+  return launched(moe_launch::route(x, w_gate, bias, logits, T, h, E, k, dtype, topk_idx, topk_w,
+                                    (hipStream_t)stream),
+                  "moe_route");
+}
+
+size_t moe_permute_workspace_size(int T, int E, int k) {
+  (void)k;
+  if (T < 0 || E < 1) return 0;
+  return moe_launch::index_ws_bytes(T, E);
+}
+
+int moe_permute(const void* src, int src_dtype, const int32_t* topk_idx, const float* row_scale,
+                int T, int h, int E, int k, int32_t* counts, int32_t* offsets, int32_t* dst_row,
+                int32_t* src_tok, void* dst, int dst_dtype, float* dst_scale, void* ws,
+                size_t ws_bytes, void* stream) {
+  REQ(T >= 0, MOE_ERR_ARG, "T=%d is negative", T);
+  REQ(E >= 1 && E <= MOE_MAX_EXPERTS, MOE_ERR_SHAPE, "E=%d outside [1, %d]", E, MOE_MAX_EXPERTS);
+  REQ(k >= 1 && k <= E && k <= MOE_MAX_TOPK, MOE_ERR_ARG, "k=%d outside [1, min(E, %d)]", k,
+      MOE_MAX_TOPK);
+  REQ(h > 0 && h % 8 == 0, MOE_ERR_SHAPE, "h=%d must be a positive multiple of 8", h);
+  bool ok = (src_dtype == MOE_F32 && dst_dtype == MOE_F32) ||
+            (src_dtype == MOE_BF16 && (dst_dtype == MOE_BF16 || dst_dtype == MOE_FP8_E4M3));
+  REQ(ok, MOE_ERR_DTYPE, "unsupported permute %d -> %d", src_dtype, dst_dtype);
+  if (dst_dtype == MOE_FP8_E4M3) {
+    PTR(dst_scale);
+    REQ(row_scale == nullptr, MOE_ERR_ARG, "row_scale is not supported with FP8 output");
+  }
+  PTR(src); PTR(dst); PTR(dst_row); OPT(row_scale);
+  if (topk_idx) {
+    PTR(topk_idx); PTR(counts); PTR(offsets); PTR(src_tok);
+    size_t need = moe_launch::index_ws_bytes(T, E);
+    REQ(T == 0 || (ws != nullptr && ws_bytes >= need), MOE_ERR_WORKSPACE,
+        "workspace of %zu bytes needed, %zu given", need, ws ? ws_bytes : size_t(0));
+    OPT(ws);
+    moe_launch::clear_status();
+    int rc = moe_launch::index_build(topk_idx, T, E, k, counts, offsets, dst_row, src_tok, ws,
+                                     (hipStream_t)stream);
+    if (rc) return launched(rc, "moe_permute (index)");
+  }
+  if (T == 0) return MOE_OK;
+  moe_launch::clear_status();
+  return launched(moe_launch::permute_rows(src, src_dtype, dst_row, row_scale, T, h, k, dst,
+                                           dst_dtype, dst_scale, (hipStream_t)stream),
+                  "moe_permute");
+}
+
+static int check_weights(const moe_weights* W) {
+  REQ(W != nullptr, MOE_ERR_ARG, "W must not be NULL");
+  REQ(W->dtype == MOE_F32 || W->dtype == MOE_BF16 || W->dtype == MOE_FP8_E4M3, MOE_ERR_DTYPE,
+      "weight dtype %d unsupported", W->dtype);
+  REQ(W->E >= 1 && W->E <= MOE_MAX_EXPERTS, MOE_ERR_SHAPE, "E=%d outside [1, %d]", W->E,
+      MOE_MAX_EXPERTS);
+  REQ(W->h > 0 && W->h % 128 == 0 && W->h_ffn > 0 && W->h_ffn % 128 == 0, MOE_ERR_SHAPE,
+      "h=%d and h_ffn=%d must be positive multiples of 128", W->h, W->h_ffn);
+  const void* w13 = W->w13;
+  const void* w2 = W->w2;
+  PTR(w13); PTR(w2);
+  if (W->dtype == MOE_FP8_E4M3) {
+    const float* w13_scale = W->w13_scale;
+    const float* w2_scale = W->w2_scale;
+    PTR(w13_scale); PTR(w2_scale);
+  }
+  return MOE_OK;
+}
+
+size_t moe_grouped_workspace_size(int rows, int h, int h_ffn, int E, int dtype) {
+  if (rows < 0 || h <= 0 || h_ffn <= 0 || E < 1) return 0;
+  return moe_launch::grouped_fwd_ws_bytes(rows, h, h_ffn, E, dtype);
+}
+
+int moe_grouped_swiglu_fwd(const void* xp, const float* xp_scale, const moe_weights* W,
+                           const int32_t* offsets, int rows, void* h13_save, void* yp, void* ws,
+                           size_t ws_bytes, void* stream) {
+  int rc = check_weights(W);
+  if (rc) return rc;
+  REQ(rows >= 0, MOE_ERR_ARG, "rows=%d is negative", rows);
+  PTR(xp); PTR(offsets); PTR(yp); OPT(h13_save);
+  if (W->dtype == MOE_FP8_E4M3) PTR(xp_scale);
+  REQ(h13_save == nullptr || W->dtype == MOE_BF16, MOE_ERR_DTYPE,
+      "h13_save is only supported with bf16 weights");
+  if (rows == 0) return MOE_OK;
+  size_t need = moe_launch::grouped_fwd_ws_bytes(rows, W->h, W->h_ffn, W->E, W->dtype);
+  REQ(ws != nullptr && ws_bytes >= need, MOE_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given",
+      need, ws ? ws_bytes : size_t(0));
+  OPT(ws);
+  moe_launch::clear_status();
+  return launched(moe_launch::grouped_fwd(xp, xp_scale, W, offsets, rows, h13_save, yp, ws,
+                                          (hipStream_t)stream),
+                  "moe_grouped_swiglu_fwd");
+}
+
+size_t moe_grouped_bwd_workspace_size(int rows, int h, int h_ffn, int E, int dtype) {
+  if (rows < 0 || h <= 0 || h_ffn <= 0 || E < 1) return 0;
+  return moe_launch::grouped_bwd_ws_bytes(rows, h, h_ffn, E, dtype);
+}
+
+int moe_grouped_swiglu_bwd(const void* dyp, const void* xp, const void* h13_save,
+                           const moe_weights* W, const int32_t* offsets, int rows, void* dxp,
+                           float* dw1, float* dw3, float* dw2, void* ws, size_t ws_bytes,
+                           void* stream) {
+  int rc = check_weights(W);
+  if (rc) return rc;
+  REQ(W->dtype == MOE_BF16, MOE_ERR_DTYPE, "backward needs bf16 weights");
+  REQ(rows >= 0, MOE_ERR_ARG, "rows=%d is negative", rows);
+  PTR(dyp); PTR(xp); PTR(h13_save); PTR(offsets); PTR(dxp); PTR(dw1); PTR(dw3); PTR(dw2);
+  size_t need = moe_launch::grouped_bwd_ws_bytes(rows, W->h, W->h_ffn, W->E, W->dtype);
+  REQ(need == 0 || (ws != nullptr && ws_bytes >= need), MOE_ERR_WORKSPACE,
+      "workspace of %zu bytes needed, %zu given", need, ws ? ws_bytes : size_t(0));
+  OPT(ws);
+  moe_launch::clear_status();
+  return launched(moe_launch::grouped_bwd(dyp, xp, h13_save, W, offsets, rows, dxp, dw1, dw3, dw2,
+                                          ws, (hipStream_t)stream),
+                  "moe_grouped_swiglu_bwd");
+}
+
+int moe_combine(const void* yp, int yp_dtype, const int32_t* dst_row, const float* topk_w, int T,
+                int h, int k, void* y, int y_dtype, void* stream) {
+  REQ(T >= 0, MOE_ERR_ARG, "T=%d is negative", T);
+  REQ(k >= 1 && k <= MOE_MAX_TOPK, MOE_ERR_ARG, "k=%d outside [1, %d]", k, MOE_MAX_TOPK);
+  REQ(h > 0 && h % 8 == 0, MOE_ERR_SHAPE, "h=%d must be a positive multiple of 8", h);
+  REQ((yp_dtype == MOE_F32 || yp_dtype == MOE_BF16) && (y_dtype == MOE_F32 || y_dtype == MOE_BF16),
+      MOE_ERR_DTYPE, "combine dtypes %d -> %d unsupported", yp_dtype, y_dtype);
+  PTR(yp); PTR(dst_row); PTR(y); OPT(topk_w);
+  if (T == 0) return MOE_OK;
+  moe_launch::clear_status();
+  return launched(moe_launch::combine_rows(yp, yp_dtype, dst_row, topk_w, T, h, k, y, y_dtype,
+                                           (hipStream_t)stream),
+                  "moe_combine");
+}
+
+}  // extern "C"

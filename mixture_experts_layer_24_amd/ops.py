@@ -1,0 +1,214 @@
+"""Python binding of the C ABI, one function per entry point (same names).
+
+Each function takes torch tensors (device memory) or ``None`` and forwards
+their addresses, sizes and the current HIP stream to ``libmoe.so``.  No
+arithmetic of the layer happens here.  ``MoELayer`` preallocates every buffer
+of one layer call so a step launches kernels only.
+"""
+from __future__ import annotations
+
+import ctypes
+
+import torch
+
+from ._lib import (MOE_BF16, MOE_F32, MOE_FP8_E4M3, MoeWeights, check, lib)
+
+_TORCH_CODE = {torch.float32: MOE_F32, torch.bfloat16: MOE_BF16, torch.float8_e4m3fn: MOE_FP8_E4M3,
+               torch.uint8: MOE_FP8_E4M3}
+_CODE_TORCH = {MOE_F32: torch.float32, MOE_BF16: torch.bfloat16, MOE_FP8_E4M3: torch.uint8}
+
+
+def dtype_code(t) -> int:
+    return _TORCH_CODE[t if isinstance(t, torch.dtype) else t.dtype]
+
+
+def _p(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _s(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+# ---- entry points ---------------------------------------------------------
+
+def moe_packed_weight_bytes(which, E, h, h_ffn, dtype):
+    return lib().moe_packed_weight_bytes(which, E, h, h_ffn, dtype)
+
+
+def moe_pack_weights(w1, w3, w2, in_dtype, E, h, h_ffn, out_dtype, w13, w2_packed, w13_scale,
+                     w2_scale, stream=None):
+    return check(lib().moe_pack_weights(_p(w1), _p(w3), _p(w2), in_dtype, E, h, h_ffn, out_dtype,
+                                        _p(w13), _p(w2_packed), _p(w13_scale), _p(w2_scale),
+                                        _s(stream)))
+
+
+def moe_route(x, w_gate, bias, logits, T, h, E, k, dtype, topk_idx, topk_w, stream=None):
+    return check(lib().moe_route(_p(x), _p(w_gate), _p(bias), _p(logits), T, h, E, k, dtype,
+                                 _p(topk_idx), _p(topk_w), _s(stream)))
+
+
+def moe_permute_workspace_size(T, E, k):
+    return lib().moe_permute_workspace_size(T, E, k)
+
+
+def moe_permute(src, src_dtype, topk_idx, row_scale, T, h, E, k, counts, offsets, dst_row, src_tok,
+                dst, dst_dtype, dst_scale, ws, ws_bytes, stream=None):
+    return check(lib().moe_permute(_p(src), src_dtype, _p(topk_idx), _p(row_scale), T, h, E, k,
+                                   _p(counts), _p(offsets), _p(dst_row), _p(src_tok), _p(dst),
+                                   dst_dtype, _p(dst_scale), _p(ws), ws_bytes, _s(stream)))
+
+
+def moe_grouped_workspace_size(rows, h, h_ffn, E, dtype):
+    return lib().moe_grouped_workspace_size(rows, h, h_ffn, E, dtype)
+
+
+def moe_grouped_swiglu_fwd(xp, xp_scale, W, offsets, rows, h13_save, yp, ws, ws_bytes, stream=None):
+    return check(lib().moe_grouped_swiglu_fwd(_p(xp), _p(xp_scale), ctypes.byref(W), _p(offsets),
+                                              rows, _p(h13_save), _p(yp), _p(ws), ws_bytes,
+                                              _s(stream)))
+
+
+def moe_grouped_bwd_workspace_size(rows, h, h_ffn, E, dtype):
+    return lib().moe_grouped_bwd_workspace_size(rows, h, h_ffn, E, dtype)
+
+
+def moe_grouped_swiglu_bwd(dyp, xp, h13_save, W, offsets, rows, dxp, dw1, dw3, dw2, ws, ws_bytes,
+                           stream=None):
+    return check(lib().moe_grouped_swiglu_bwd(_p(dyp), _p(xp), _p(h13_save), ctypes.byref(W),
+                                              _p(offsets), rows, _p(dxp), _p(dw1), _p(dw3),
+                                              _p(dw2), _p(ws), ws_bytes, _s(stream)))
+
+
+def moe_combine(yp, yp_dtype, dst_row, topk_w, T, h, k, y, y_dtype, stream=None):
+    return check(lib().moe_combine(_p(yp), yp_dtype, _p(dst_row), _p(topk_w), T, h, k, _p(y),
+                                   y_dtype, _s(stream)))
+
+
+def moe_last_error() -> str:
+    return lib().moe_last_error().decode()
+
+
+def moe_version() -> int:
+    return lib().moe_version()
+
+
+# ---- one preallocated layer ------------------------------------------------
+
+class PackedWeights:
+    """Expert weights packed (and for FP8 quantized) by ``moe_pack_weights``."""
+
+    def __init__(self, w1, w3, w2, out_dtype: int, stream=None):
+        E, h, hf = w1.shape
+        dev = w1.device
+        in_dt = dtype_code(w1)
+        self.dtype, self.E, self.h, self.h_ffn = out_dtype, E, h, hf
+        sz = lambda which: moe_packed_weight_bytes(which, E, h, hf, out_dtype)
+        self.w13 = torch.empty(sz(0), dtype=torch.uint8, device=dev)
+        self.w2 = torch.empty(sz(1), dtype=torch.uint8, device=dev)
+        fp8 = out_dtype == MOE_FP8_E4M3
+        self.w13_scale = torch.empty(E, 2 * hf, dtype=torch.float32, device=dev) if fp8 else None
+        self.w2_scale = torch.empty(E, h, dtype=torch.float32, device=dev) if fp8 else None
+        moe_pack_weights(w1, w3, w2, in_dt, E, h, hf, out_dtype, self.w13, self.w2,
+                         self.w13_scale, self.w2_scale, stream)
+        self.struct = MoeWeights(out_dtype, E, h, hf, self.w13.data_ptr(), self.w2.data_ptr(),
+                                 self.w13_scale.data_ptr() if fp8 else None,
+                                 self.w2_scale.data_ptr() if fp8 else None)
+
+
+class MoELayer:
+    """Buffers and launch sequence of one MoE layer call on a fixed shape.
+
+    forward(): route -> permute (index + copy) -> grouped SwiGLU -> combine.
+    backward(): weighted dispatch of dY -> grouped backward -> combine (dX).
+    """
+
+    def __init__(self, T, h, h_ffn, E, k, dtype: int, device="cuda", save_for_backward=False):
+        self.T, self.h, self.h_ffn, self.E, self.k, self.dtype = T, h, h_ffn, E, k, dtype
+        R = T * k
+        self.R = R
+        dev = torch.device(device)
+        io = torch.float32 if dtype == MOE_F32 else torch.bfloat16
+        self.io_code = MOE_F32 if dtype == MOE_F32 else MOE_BF16
+        i32 = dict(dtype=torch.int32, device=dev)
+        f32 = dict(dtype=torch.float32, device=dev)
+        self.logits = torch.empty(T, E, **f32)
+        self.topk_idx = torch.empty(T, k, **i32)
+        self.topk_w = torch.empty(T, k, **f32)
+        self.counts = torch.empty(E, **i32)
+        self.offsets = torch.empty(E + 1, **i32)
+        self.dst_row = torch.empty(T, k, **i32)
+        self.src_tok = torch.empty(R, **i32)
+        self.pws_bytes = moe_permute_workspace_size(T, E, k)
+        self.pws = torch.empty(max(self.pws_bytes, 256), dtype=torch.uint8, device=dev)
+        xp_dt = torch.uint8 if dtype == MOE_FP8_E4M3 else io
+        self.xp = torch.empty(R, h, dtype=xp_dt, device=dev)
+        self.xp_scale = torch.empty(R, **f32) if dtype == MOE_FP8_E4M3 else None
+        self.h13 = torch.empty(R, 2 * h_ffn, dtype=torch.bfloat16, device=dev) if save_for_backward else None
+        self.yp = torch.empty(R, h, dtype=io, device=dev)
+        self.y = torch.empty(T, h, dtype=io, device=dev)
+        self.gws_bytes = moe_grouped_workspace_size(R, h, h_ffn, E, dtype)
+        self.gws = torch.empty(max(self.gws_bytes, 256), dtype=torch.uint8, device=dev)
+        self.bwd_ready = False
+
+    def forward(self, x, w_gate, bias, W: PackedWeights, logits_in=None, stream=None):
+        T, h, E, k = self.T, self.h, self.E, self.k
+        if logits_in is None:
+            moe_route(x, w_gate, bias, self.logits, T, h, E, k, dtype_code(x), self.topk_idx,
+                      self.topk_w, stream)
+        else:
+            moe_route(None, None, None, logits_in, T, h, E, k, dtype_code(logits_in),
+                      self.topk_idx, self.topk_w, stream)
+        moe_permute(x, dtype_code(x), self.topk_idx, None, T, h, E, k, self.counts, self.offsets,
+                    self.dst_row, self.src_tok, self.xp, self.dtype, self.xp_scale, self.pws,
+                    self.pws_bytes, stream)
+        moe_grouped_swiglu_fwd(self.xp, self.xp_scale, W.struct, self.offsets, self.R, self.h13,
+                               self.yp, self.gws, self.gws_bytes, stream)
+        moe_combine(self.yp, self.io_code, self.dst_row, self.topk_w, T, h, k, self.y,
+                    self.io_code, stream)
+        return self.y
+
+    def _alloc_bwd(self):
+        dev = self.y.device
+        R, h, hf, E = self.R, self.h, self.h_ffn, self.E
+        self.dyp = torch.empty(R, h, dtype=torch.bfloat16, device=dev)
+        self.dxp = torch.empty(R, h, dtype=torch.bfloat16, device=dev)
+        self.dx = torch.empty(self.T, h, dtype=torch.bfloat16, device=dev)
+        self.dw1 = torch.empty(E, h, hf, dtype=torch.float32, device=dev)
+        self.dw3 = torch.empty(E, h, hf, dtype=torch.float32, device=dev)
+        self.dw2 = torch.empty(E, hf, h, dtype=torch.float32, device=dev)
+        self.bws_bytes = moe_grouped_bwd_workspace_size(R, h, hf, E, self.dtype)
+        self.bws = torch.empty(max(self.bws_bytes, 256), dtype=torch.uint8, device=dev)
+        self.bwd_ready = True
+
+    def backward(self, dy, x, W: PackedWeights, stream=None):
+        if not self.bwd_ready:
+            self._alloc_bwd()
+        T, h, E, k = self.T, self.h, self.E, self.k
+        # dYp = w * dY in dispatch order; Xp re-gathered from x (index reused)
+        moe_permute(dy, MOE_BF16, None, self.topk_w, T, h, E, k, None, None, self.dst_row, None,
+                    self.dyp, MOE_BF16, None, None, 0, stream)
+        moe_permute(x, MOE_BF16, None, None, T, h, E, k, None, None, self.dst_row, None,
+                    self.xp, MOE_BF16, None, None, 0, stream)
+        moe_grouped_swiglu_bwd(self.dyp, self.xp, self.h13, W.struct, self.offsets, self.R,
+                               self.dxp, self.dw1, self.dw3, self.dw2, self.bws, self.bws_bytes,
+                               stream)
+        moe_combine(self.dxp, MOE_BF16, self.dst_row, None, T, h, k, self.dx, MOE_BF16, stream)
+        return self.dx
+
+
+def moe_timing_enable(on: bool) -> int:
+    return check(lib().moe_timing_enable(1 if on else 0))
+
+
+def moe_timing_report() -> dict:
+    """{kernel: (launches, total_ms)} recorded since timing was enabled."""
+    buf = ctypes.create_string_buffer(4096)
+    check(lib().moe_timing_report(buf, len(buf)))
+    out = {}
+    for line in buf.value.decode().splitlines():
+        name, n, ms = line.split()
+        out[name] = (int(n), float(ms))
+    return out

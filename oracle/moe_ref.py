@@ -205,7 +205,7 @@ def layer_forward_tokens(x_rows, idx_rows, w_rows, w1, w3, w2):
     """
     x_rows = np.asarray(x_rows, np.float64)
     n = x_rows.shape[0]
-    y = np.zeros((n, w2.shape[2]), dtype=np.float64)
+    y = np.zeros((n, np.shape(w2[0])[1]), dtype=np.float64)
     for e in np.unique(idx_rows):
         tt, jj = np.nonzero(idx_rows == e)
         xe = x_rows[tt]
@@ -380,7 +380,7 @@ def layer_forward_fp8_tokens(x_rows, idx_rows, w_rows, w1, w3, w2, wq_cache=None
     qx, sx = quantize_rows(x_rows)
     xd = e4m3_decode(qx) * sx[:, None].astype(np.float64)
     n = xd.shape[0]
-    y = np.zeros((n, w2.shape[2]))
+    y = np.zeros((n, np.shape(w2[0])[1]))
     cache = {} if wq_cache is None else wq_cache
     for e in np.unique(idx_rows):
         if e not in cache:

@@ -1,0 +1,110 @@
+"""Host-side checks of the C ABI that need no GPU: the library loads, exports
+every function the header declares, and rejects bad arguments before any HIP
+call (so the error paths run on a machine without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from mixture_experts_layer_24_amd import _lib as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+pytestmark = pytest.mark.skipif(not os.path.exists(L.LIB_PATH), reason="libmoe.so not built")
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "moe.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol():
+    names = _declared()
+    assert "moe_route" in names and "moe_grouped_swiglu_fwd" in names and len(names) >= 12
+    lib = L.lib()
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) <= set(L.SIGNATURES)
+    assert lib.moe_version() == 1
+
+
+A = ctypes.c_void_p(1 << 20)   # aligned, never dereferenced: validation fails first
+U = ctypes.c_void_p((1 << 20) + 4)  # misaligned
+
+
+def test_route_validation():
+    lib = L.lib()
+    ok_args = dict(x=A, wg=A, bias=None, logits=None, T=16, h=64, E=8, k=2, dt=L.MOE_BF16, idx=A, w=A)
+
+    def call(**kw):
+        a = {**ok_args, **kw}
+        return lib.moe_route(a["x"], a["wg"], a["bias"], a["logits"], a["T"], a["h"], a["E"], a["k"],
+                             a["dt"], a["idx"], a["w"], None)
+    assert call(T=-1) == L.MOE_ERR_ARG
+    assert call(k=9) == L.MOE_ERR_ARG
+    assert call(k=0) == L.MOE_ERR_ARG
+    assert call(E=0) == L.MOE_ERR_SHAPE
+    assert call(E=L.MOE_MAX_EXPERTS + 1) == L.MOE_ERR_SHAPE
+    assert call(idx=None) == L.MOE_ERR_ARG
+    assert call(idx=U) == L.MOE_ERR_ARG
+    assert call(dt=L.MOE_FP8_E4M3) == L.MOE_ERR_DTYPE
+    assert call(h=96) == L.MOE_ERR_SHAPE
+    assert call(x=None) == L.MOE_ERR_ARG        # logits-in mode needs logits
+    assert b"logits" in lib.moe_last_error()
+    assert call(T=0) == L.MOE_OK                # empty batch: nothing to launch
+
+
+def test_permute_validation():
+    lib = L.lib()
+    need = lib.moe_permute_workspace_size(1000, 8, 2)
+    assert need >= 4 * 8
+
+    def call(src=A, sdt=L.MOE_BF16, idx=A, T=1000, h=64, E=8, k=2, dst=A, ddt=L.MOE_BF16, scale=None,
+             ws=A, wsb=None, row_scale=None):
+        return lib.moe_permute(src, sdt, idx, row_scale, T, h, E, k, A, A, A, A, dst, ddt, scale, ws,
+                               need if wsb is None else wsb, None)
+    assert call(h=12) == L.MOE_ERR_SHAPE
+    assert call(sdt=L.MOE_F32) == L.MOE_ERR_DTYPE
+    assert call(ddt=L.MOE_FP8_E4M3) == L.MOE_ERR_ARG            # fp8 needs scales
+    assert call(ddt=L.MOE_FP8_E4M3, scale=A, row_scale=A) == L.MOE_ERR_ARG
+    assert call(wsb=need - 1) == L.MOE_ERR_WORKSPACE
+    assert call(ws=None) == L.MOE_ERR_WORKSPACE
+    assert call(dst=None) == L.MOE_ERR_ARG
+    assert call(k=3, E=2) == L.MOE_ERR_ARG
+
+
+def test_grouped_validation():
+    lib = L.lib()
+    W = L.MoeWeights(L.MOE_BF16, 8, 256, 384, A.value, A.value, None, None)
+    need = lib.moe_grouped_workspace_size(512, 256, 384, 8, L.MOE_BF16)
+    assert need >= 512 * 384 * 2
+
+    def call(W=W, rows=512, ws=A, wsb=need, save=None, scale=None):
+        return lib.moe_grouped_swiglu_fwd(A, scale, ctypes.byref(W), A, rows, save, A, ws, wsb, None)
+    assert call(wsb=need - 1) == L.MOE_ERR_WORKSPACE
+    assert call(rows=-1) == L.MOE_ERR_ARG
+    assert call(rows=0) == L.MOE_OK
+    bad = L.MoeWeights(L.MOE_BF16, 8, 200, 384, A.value, A.value, None, None)
+    assert call(W=bad) == L.MOE_ERR_SHAPE
+    bad = L.MoeWeights(7, 8, 256, 384, A.value, A.value, None, None)
+    assert call(W=bad) == L.MOE_ERR_DTYPE
+    f8 = L.MoeWeights(L.MOE_FP8_E4M3, 8, 256, 384, A.value, A.value, None, None)
+    assert call(W=f8) == L.MOE_ERR_ARG                    # fp8 weights need scales
+    f32 = L.MoeWeights(L.MOE_F32, 8, 256, 384, A.value, A.value, None, None)
+    assert call(W=f32, save=A) == L.MOE_ERR_DTYPE         # G|U kept only for bf16
+    assert lib.moe_grouped_swiglu_bwd(A, A, A, ctypes.byref(f32), A, 512, A, A, A, A, A, 1 << 30,
+                                      None) == L.MOE_ERR_DTYPE
+
+
+def test_combine_and_pack_validation():
+    lib = L.lib()
+    assert lib.moe_combine(A, L.MOE_BF16, A, A, 10, 12, 2, A, L.MOE_BF16, None) == L.MOE_ERR_SHAPE
+    assert lib.moe_combine(A, L.MOE_FP8_E4M3, A, A, 10, 16, 2, A, L.MOE_BF16, None) == L.MOE_ERR_DTYPE
+    assert lib.moe_combine(A, L.MOE_BF16, A, None, 0, 16, 2, A, L.MOE_BF16, None) == L.MOE_OK
+    assert lib.moe_pack_weights(A, A, A, L.MOE_F32, 8, 256, 384, L.MOE_BF16, A, A, None, None,
+                                None) == L.MOE_ERR_DTYPE
+    assert lib.moe_pack_weights(A, A, A, L.MOE_BF16, 8, 256, 384, L.MOE_FP8_E4M3, A, A, None, None,
+                                None) == L.MOE_ERR_ARG
+    assert lib.moe_packed_weight_bytes(0, 8, 256, 384, L.MOE_BF16) == 8 * 768 * 256 * 2
+    assert lib.moe_packed_weight_bytes(3, 8, 256, 384, L.MOE_FP8_E4M3) == 8 * 256 * 4
