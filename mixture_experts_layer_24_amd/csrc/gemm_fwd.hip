@@ -13,8 +13,11 @@
 //     MFMA operand directly.
 //   * Tile 256 x 256, 128 bytes of K per stage (64 bf16, 32 fp32, 128 fp8),
 //     four waves of 128 x 128 (4 x 4 MFMA 32x32 blocks, 256 fp32 accumulators
-//     per lane).  Two LDS stages (128 KB) give one barrier per K step; the
-//     next stage's global loads are in flight while the current one computes.
+//     per lane, held in AGPRs).  Two LDS stages (128 KB) give one barrier per
+//     K step.  Operands go global -> LDS directly (buffer_load ... lds, no
+//     VGPR staging); the next slab's loads are in flight while the current
+//     one computes, and the next slab's first fragments are read right after
+//     the barrier while the last substep's MFMAs still run.
 //   * LDS rows are 128 B with the 16-byte chunk index XOR-swizzled by
 //     (row/2)%8, so the 64 lanes of an operand read hit distinct banks.
 //   * Persistent: one workgroup per CU walks a tile list built on device from
@@ -65,6 +68,7 @@ struct Frag;
 template <> struct Frag<MOE_BF16> {
   u32x4 v;
   static constexpr int kSub = 4;  // substeps per 128-byte LDS row
+  static constexpr int kReads = 1, kMfma = 1;  // LDS reads per fragment, MFMAs per pair
   __device__ __forceinline__ void load(const unsigned char* base, int row, int s, int half) {
     v = *reinterpret_cast<const u32x4*>(base + lds_pos(row, 2 * s + half));
   }
@@ -76,6 +80,7 @@ template <> struct Frag<MOE_BF16> {
 template <> struct Frag<MOE_F32> {
   u32x4 v;
   static constexpr int kSub = 4;
+  static constexpr int kReads = 1, kMfma = 4;
   __device__ __forceinline__ void load(const unsigned char* base, int row, int s, int half) {
     v = *reinterpret_cast<const u32x4*>(base + lds_pos(row, 2 * s + half));
   }
@@ -89,6 +94,7 @@ template <> struct Frag<MOE_F32> {
 template <> struct Frag<MOE_FP8_E4M3> {
   u32x4 v0, v1;
   static constexpr int kSub = 2;
+  static constexpr int kReads = 2, kMfma = 1;
   __device__ __forceinline__ void load(const unsigned char* base, int row, int s, int half) {
     v0 = *reinterpret_cast<const u32x4*>(base + lds_pos(row, 4 * s + 2 * half));
     v1 = *reinterpret_cast<const u32x4*>(base + lds_pos(row, 4 * s + 2 * half + 1));
@@ -105,13 +111,163 @@ template <> struct Frag<MOE_FP8_E4M3> {
 
 __device__ __forceinline__ float silu_f(float g) { return g / (1.0f + __expf(-g)); }
 
+struct Tile {
+  int e, row0, row_end, n0;
+};
+
+// Which expert / m-tile / n-tile the t-th tile is: experts in order, m-tiles
+// fastest within an expert, so consecutive tiles share a weight column block.
+__device__ __forceinline__ Tile tile_of(int t, const int* tpre, const int* offs, int E) {
+  int lo = 0, hi = E - 1;  // expert e with tpre[e] <= t < tpre[e+1]
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (tpre[mid] <= t) lo = mid; else hi = mid - 1;
+  }
+  const int mt_e = ceil_div(offs[lo + 1] - offs[lo], kBM);
+  const int local = t - tpre[lo];
+  const int nt = local / mt_e, mt = local - nt * mt_e;
+  return Tile{lo, offs[lo] + mt * kBM, offs[lo + 1], nt * kBN};
+}
+
+// Buffer descriptors of a tile's A rows and B rows: reads past the end of
+// the A or B array return zero (ragged M tail of the last expert, N tail).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, size_t off, size_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<unsigned char*>(static_cast<const unsigned char*>(base) + off), (short)0,
+      int(bytes < 0x7FFFFFF0u ? bytes : 0x7FFFFFF0u), 0x00020000);
+}
+
+typedef __attribute__((address_space(3))) void lds_ptr_t;
+
+// One K slab (128 bytes per row) of A and B straight from memory into LDS
+// stage `st`.  Wave w fills row groups 8w..8w+7 of each operand; within an
+// 8-row group lane l lands at LDS byte 16*l (row l/8, position l%8), so it
+// fetches the chunk that the XOR swizzle keeps at that position.
+__device__ __forceinline__ void issue_slab(unsigned char* lds, int st, __amdgpu_buffer_rsrc_t ra,
+                                           __amdgpu_buffer_rsrc_t rb, int wave, int voff_e,
+                                           int voff_o, int rowB, int koff) {
+  unsigned char* A = lds + st * (2 * kStageB) + wave * 8 * 1024;
+  unsigned char* B = A + kStageB;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int v = ((i & 1) ? voff_o : voff_e) + i * 8 * rowB + koff;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t*)(A + i * 1024), 16, v, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr_t*)(B + i * 1024), 16, v, 0, 0, 0);
+  }
+}
+
+// Fragments of substep s of one LDS stage (4 A and 4 B fragments per wave).
+template <int DT>
+__device__ __forceinline__ void load_frags(Frag<DT> (&fa)[4], Frag<DT> (&fb)[4],
+                                           const unsigned char* As, int arow, int brow, int s,
+                                           int half) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) fa[i].load(As, arow + i * 32, s, half);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) fb[j].load(As + kStageB, brow + j * 32, s, half);
+}
+
+template <int DT>
+__device__ __forceinline__ void mma_all(f32x16 (&acc)[4][4], const Frag<DT> (&fa)[4],
+                                        const Frag<DT> (&fb)[4]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) Frag<DT>::mma(acc[i][j], fa[i], fb[j]);
+}
+
+template <int DT, int MODE>
+__device__ __forceinline__ void epilogue(const GemmArgs& g, f32x16 (&acc)[4][4], int e, int row0,
+                                         int row_end, int n0, int wm, int wn, int half, int l32) {
+  const int rbase = row0 + wm * 128;
+  if (MODE == kModeFC1) {
+    const int hf = g.N / 2;
+    const int chb = (n0 + wn * 128) / 2;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float rmax[16];
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        const int ch = chb + p * 32 + l32;
+        const int colg = n0 + wn * 128 + (2 * p) * 32 + l32;  // packed column of G
+        float sg = 1.f, su = 1.f;
+        if (DT == MOE_FP8_E4M3) {
+          sg = g.b_scale[size_t(e) * g.N + colg];
+          su = g.b_scale[size_t(e) * g.N + colg + 32];
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = rbase + i * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+          float G = acc[i][2 * p][r], U = acc[i][2 * p + 1][r];
+          if (DT == MOE_FP8_E4M3) {
+            const float xs = row < row_end ? g.a_scale[row] : 0.f;
+            G *= xs * sg;
+            U *= xs * su;
+          }
+          const float a = silu_f(G) * U;
+          if (row < row_end) {
+            if (DT == MOE_BF16) {
+              static_cast<uint16_t*>(g.out)[size_t(row) * hf + ch] = uint16_t(f32_to_bf16_bits(a));
+            } else {
+              // fp32 A; for FP8 the per-row quantization reads this exact value
+              static_cast<float*>(g.out)[size_t(row) * hf + ch] = a;
+              if (DT == MOE_FP8_E4M3) rmax[r] = p == 0 ? fabsf(a) : fmaxf(rmax[r], fabsf(a));
+            }
+            if (g.save) {
+              uint16_t* sv = static_cast<uint16_t*>(g.save) + size_t(row) * g.N + colg;
+              sv[0] = uint16_t(f32_to_bf16_bits(G));
+              sv[32] = uint16_t(f32_to_bf16_bits(U));
+            }
+          } else if (DT == MOE_FP8_E4M3) {
+            rmax[r] = 0.f;
+          }
+        }
+      }
+      if (DT == MOE_FP8_E4M3) {
+        // row max over this wave's 64 channels: reduce over the 32 lanes of a half
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float m = rmax[r];
+#pragma unroll
+          for (int o = 16; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+          const int row = rbase + i * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+          if (l32 == 0 && row < row_end) atomicMax(g.row_amax + row, __float_as_uint(m));
+        }
+      }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int col = n0 + wn * 128 + j * 32 + l32;
+        if (col >= g.N) continue;
+        float cs = 1.f;
+        if (DT == MOE_FP8_E4M3) cs = g.b_scale[size_t(e) * g.N + col];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = rbase + i * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+          if (row < row_end) {
+            float y = acc[i][j][r];
+            if (DT == MOE_FP8_E4M3) y *= g.a_scale[row] * cs;
+            if (DT == MOE_F32)
+              static_cast<float*>(g.out)[size_t(row) * g.N + col] = y;
+            else
+              static_cast<uint16_t*>(g.out)[size_t(row) * g.N + col] = uint16_t(f32_to_bf16_bits(y));
+          }
+        }
+      }
+  }
+}
+
 template <int DT, int MODE>
 __global__ void __launch_bounds__(256, 1) grouped_gemm_kernel(GemmArgs g) {
   extern __shared__ __align__(16) unsigned char lds[];
   __shared__ int tpre[MOE_MAX_EXPERTS + 1];
   __shared__ int offs[MOE_MAX_EXPERTS + 1];
   constexpr int EB = Elem<DT>::bytes;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int wm = wave >> 1, wn = wave & 1;
   const int half = lane >> 5, l32 = lane & 31;
   const int NT = ceil_div(g.N, kBN);  // FC2 may end in a 128-column tail
@@ -134,41 +290,45 @@ __global__ void __launch_bounds__(256, 1) grouped_gemm_kernel(GemmArgs g) {
   const int total = tpre[g.E];
   const int G = gridDim.x;
   const int b = blockIdx.x;
-  const int v = (G % 8 == 0) ? (b % 8) * (G / 8) + b / 8 : b;
+  // the 32 workgroups of one XCD (b % 8) take consecutive tiles
+  int t = (G % 8 == 0) ? (b % 8) * (G / 8) + b / 8 : b;
+  if (t >= total) return;
 
-  // global-load slots: 8 rows per thread, one 16-byte chunk each
-  const int ld_row = tid >> 3, ld_c = tid & 7;
-  const size_t rowB = size_t(g.K) * EB;  // bytes per operand row
-  const int nk = int(rowB / kRowB);
+  const int rowB = g.K * EB;  // bytes per operand row (K * element size)
+  const int nk = rowB / kRowB;
+  // loader geometry (see issue_slab)
+  const int lrow = wave * 64 + (lane >> 3);
+  const int sw = (lrow >> 1) & 7;
+  const int voff_e = lrow * rowB + (((lane & 7) ^ sw) << 4);
+  const int voff_o = lrow * rowB + (((lane & 7) ^ sw ^ 4) << 4);
+  // fragment rows inside a stage
+  const int arow = wm * 128 + l32, brow = wn * 128 + l32;
 
-  for (int t = v; t < total; t += G) {
-    int lo = 0, hi = g.E - 1;  // expert e with tpre[e] <= t < tpre[e+1]
-    while (lo < hi) {
-      int mid = (lo + hi + 1) >> 1;
-      if (tpre[mid] <= t) lo = mid; else hi = mid - 1;
-    }
-    const int e = lo;
-    const int m_rows = offs[e + 1] - offs[e];
-    const int mt_e = ceil_div(m_rows, kBM);
-    const int local = t - tpre[e];
-    const int nt = local / mt_e, mt = local - nt * mt_e;
-    const int row0 = offs[e] + mt * kBM;
-    const int row_end = offs[e + 1];
-    const int n0 = nt * kBN;
+  auto rsrc_a = [&](const Tile& c) {
+    return rsrc(g.A, size_t(c.row0) * rowB, size_t(g.rows - c.row0) * rowB);
+  };
+  auto rsrc_b = [&](const Tile& c) {
+    return rsrc(g.B, (size_t(c.e) * g.N + c.n0) * rowB, size_t(g.N - c.n0) * rowB);
+  };
 
-    // Buffer resources: rows past the end of A or B read as zero, so the
-    // ragged M tail and the N tail need no clamping.
-    const size_t a_bytes = size_t(g.rows - row0) * rowB;
-    const size_t b_bytes = size_t(g.N - n0) * rowB;
-    const __amdgpu_buffer_rsrc_t ra_src = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<unsigned char*>(static_cast<const unsigned char*>(g.A) + size_t(row0) * rowB),
-        (short)0, int(a_bytes < 0xFFFFFFF0u ? a_bytes : 0xFFFFFFF0u), 0x00020000);
-    const __amdgpu_buffer_rsrc_t rb_src = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<unsigned char*>(static_cast<const unsigned char*>(g.B) +
-                                   (size_t(e) * g.N + n0) * rowB),
-        (short)0, int(b_bytes < 0xFFFFFFF0u ? b_bytes : 0xFFFFFFF0u), 0x00020000);
-    const int voff = ld_row * int(rowB) + ld_c * 16;   // + 32*i rows via the scalar offset
-    const int wpos = lds_pos(ld_row, ld_c);            // + 4096*i (same swizzle every 32 rows)
+  constexpr int S = Frag<DT>::kSub;             // substeps per slab (even)
+  constexpr int NR = 8 * Frag<DT>::kReads;      // LDS reads per substep
+  constexpr int NM = 16 * Frag<DT>::kMfma;      // MFMAs per substep
+
+  Tile cur = tile_of(t, tpre, offs, g.E);
+  __amdgpu_buffer_rsrc_t ra = rsrc_a(cur), rb = rsrc_b(cur);
+  int st = 0;
+  issue_slab(lds, st, ra, rb, wave, voff_e, voff_o, rowB, 0);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  Frag<DT> fa[2][4], fb[2][4];
+  load_frags<DT>(fa[0], fb[0], lds, arow, brow, 0, half);
+
+  while (true) {
+    const int tn = t + G;
+    const bool has_next = tn < total;
+    const Tile nxt = has_next ? tile_of(tn, tpre, offs, g.E) : cur;
+    const __amdgpu_buffer_rsrc_t ra_n = rsrc_a(nxt), rb_n = rsrc_b(nxt);
 
     f32x16 acc[4][4];
 #pragma unroll
@@ -178,136 +338,43 @@ __global__ void __launch_bounds__(256, 1) grouped_gemm_kernel(GemmArgs g) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-    u32x4 ra[8], rb[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      ra[i] = __builtin_amdgcn_raw_buffer_load_b128(ra_src, voff, i * 32 * int(rowB), 0);
-      rb[i] = __builtin_amdgcn_raw_buffer_load_b128(rb_src, voff, i * 32 * int(rowB), 0);
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      *reinterpret_cast<u32x4*>(lds + wpos + i * 4096) = ra[i];
-      *reinterpret_cast<u32x4*>(lds + 2 * kStageB + wpos + i * 4096) = rb[i];
-    }
-    __syncthreads();
-
     for (int kt = 0; kt < nk; ++kt) {
-      const int st = kt & 1;
-      const bool more = kt + 1 < nk;
-      if (more) {
-        const int koff = (kt + 1) * kRowB;
+      // Stage st holds slab kt and fa[0]/fb[0] its first fragments.  Load
+      // slab kt+1 (or the next tile's first) into the other stage.
+      const bool last = kt + 1 == nk;
+      issue_slab(lds, st ^ 1, last ? ra_n : ra, last ? rb_n : rb, wave, voff_e, voff_o, rowB,
+                 last ? 0 : (kt + 1) * kRowB);
+      const unsigned char* As = lds + st * (2 * kStageB);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          ra[i] = __builtin_amdgcn_raw_buffer_load_b128(ra_src, voff, koff + i * 32 * int(rowB), 0);
-          rb[i] = __builtin_amdgcn_raw_buffer_load_b128(rb_src, voff, koff + i * 32 * int(rowB), 0);
+      for (int s = 0; s + 1 < S; ++s) {
+        load_frags<DT>(fa[(s + 1) & 1], fb[(s + 1) & 1], As, arow, brow, s + 1, half);
+        mma_all<DT>(acc, fa[s & 1], fb[s & 1]);
+      }
+      // interleave: one LDS read (and one global load early on) per MFMA
+#pragma unroll
+      for (int s = 0; s + 1 < S; ++s)
+#pragma unroll
+        for (int q = 0; q < NM; ++q) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          if (q < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          if (s == 0 && q < 16) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
         }
-      }
-      const unsigned char* As = lds + st * kStageB;
-      const unsigned char* Bs = lds + (2 + st) * kStageB;
-#pragma unroll
-      for (int s = 0; s < Frag<DT>::kSub; ++s) {
-        Frag<DT> fa[4], fb[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) fa[i].load(As, wm * 128 + i * 32 + l32, s, half);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) fb[j].load(Bs, wn * 128 + j * 32 + l32, s, half);
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) Frag<DT>::mma(acc[i][j], fa[i], fb[j]);
-      }
-      if (more) {
-        unsigned char* Ad = lds + (st ^ 1) * kStageB;
-        unsigned char* Bd = lds + (2 + (st ^ 1)) * kStageB;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          *reinterpret_cast<u32x4*>(Ad + wpos + i * 4096) = ra[i];
-          *reinterpret_cast<u32x4*>(Bd + wpos + i * 4096) = rb[i];
-        }
-      }
+      __builtin_amdgcn_s_waitcnt(0);  // stage st read out; slab kt+1 landed
       __syncthreads();
+      // next slab's first fragments load while the last substep multiplies
+      load_frags<DT>(fa[0], fb[0], lds + (st ^ 1) * (2 * kStageB), arow, brow, 0, half);
+      mma_all<DT>(acc, fa[1], fb[1]);
+      __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);
+      st ^= 1;
     }
 
-    // ---- epilogue ----
-    const int rbase = row0 + wm * 128;
-    if (MODE == kModeFC1) {
-      const int hf = g.N / 2;
-      const int chb = (n0 + wn * 128) / 2;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float rmax[16];
-#pragma unroll
-        for (int p = 0; p < 2; ++p) {
-          const int ch = chb + p * 32 + l32;
-          const int colg = n0 + wn * 128 + (2 * p) * 32 + l32;  // packed column of G
-          float sg = 1.f, su = 1.f;
-          if (DT == MOE_FP8_E4M3) {
-            sg = g.b_scale[size_t(e) * g.N + colg];
-            su = g.b_scale[size_t(e) * g.N + colg + 32];
-          }
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int row = rbase + i * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-            float G = acc[i][2 * p][r], U = acc[i][2 * p + 1][r];
-            if (DT == MOE_FP8_E4M3) {
-              const float xs = row < row_end ? g.a_scale[row] : 0.f;
-              G *= xs * sg;
-              U *= xs * su;
-            }
-            const float a = silu_f(G) * U;
-            if (row < row_end) {
-              if (DT == MOE_BF16) {
-                static_cast<uint16_t*>(g.out)[size_t(row) * hf + ch] = uint16_t(f32_to_bf16_bits(a));
-              } else {
-                // fp32 A; for FP8 the per-row quantization reads this exact value
-                static_cast<float*>(g.out)[size_t(row) * hf + ch] = a;
-                if (DT == MOE_FP8_E4M3) rmax[r] = p == 0 ? fabsf(a) : fmaxf(rmax[r], fabsf(a));
-              }
-              if (g.save) {
-                uint16_t* sv = static_cast<uint16_t*>(g.save) + size_t(row) * g.N + colg;
-                sv[0] = uint16_t(f32_to_bf16_bits(G));
-                sv[32] = uint16_t(f32_to_bf16_bits(U));
-              }
-            } else if (DT == MOE_FP8_E4M3) {
-              rmax[r] = 0.f;
-            }
-          }
-        }
-        if (DT == MOE_FP8_E4M3) {
-          // row max over this wave's 64 channels: reduce over the 32 lanes of a half
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            float m = rmax[r];
-#pragma unroll
-            for (int o = 16; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
-            const int row = rbase + i * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-            if (l32 == 0 && row < row_end) atomicMax(g.row_amax + row, __float_as_uint(m));
-          }
-        }
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int col = n0 + wn * 128 + j * 32 + l32;
-          if (col >= g.N) continue;
-          float cs = 1.f;
-          if (DT == MOE_FP8_E4M3) cs = g.b_scale[size_t(e) * g.N + col];
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int row = rbase + i * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-            if (row < row_end) {
-              float y = acc[i][j][r];
-              if (DT == MOE_FP8_E4M3) y *= g.a_scale[row] * cs;
-              if (DT == MOE_F32)
-                static_cast<float*>(g.out)[size_t(row) * g.N + col] = y;
-              else
-                static_cast<uint16_t*>(g.out)[size_t(row) * g.N + col] = uint16_t(f32_to_bf16_bits(y));
-            }
-          }
-        }
-    }
+    epilogue<DT, MODE>(g, acc, cur.e, cur.row0, cur.row_end, cur.n0, wm, wn, half, l32);
+    if (!has_next) break;
+    t = tn;
+    cur = nxt;
+    ra = ra_n;
+    rb = rb_n;
   }
 }
 
