@@ -100,7 +100,7 @@ def main():
     code = {"f32": MOE_F32, "bf16": MOE_BF16, "fp8": MOE_FP8_E4M3}[wl.dtype]
     x, wg, bias = t(inp["x"]), t(inp["w_gate"]), torch.from_numpy(inp["bias"]).to(dev)
     w1, w3, w2 = t(inp["w1"]), t(inp["w3"]), t(inp["w2"])
-    P = ops.PackedWeights(w1, w3, w2, code)
+    P = ops.PackedWeights(w1, w3, w2, code, backward=wl.backward)
     del w1, w3, w2
     layer = ops.MoELayer(wl.T, wl.h, wl.h_ffn, wl.E, wl.k, code, device=dev,
                          save_for_backward=wl.backward)
@@ -136,6 +136,9 @@ def main():
 
     dom = max(per_step, key=per_step.get)
     flops_per_launch = {"fc1": counts["flops_fc1"], "fc2": counts["flops_fc2"]}
+    if wl.backward:
+        rhf = wl.R * wl.h * wl.h_ffn
+        flops_per_launch.update(bwd_dA=2 * rhf, bwd_dW2=2 * rhf, bwd_dXp=4 * rhf, bwd_dW13=4 * rhf)
     bytes_per_launch = {"permute": counts["permute_bytes"], "combine": counts["combine_bytes"],
                         "route": counts["router_bytes"]}
     if dom in flops_per_launch:

@@ -75,6 +75,12 @@ extern "C" {
  *   w2   [E][h][h_ffn]    FC2 weight transposed (h_ffn contiguous).
  *   w13_scale [E][2*h_ffn], w2_scale [E][h]: FP8 only, per packed row
  *        (= per output channel) dequantization scales; NULL otherwise.
+ *   w13_bwd [E][h][2*h_ffn]: BF16 only, for the backward: W1 and W3 side by
+ *        side along h_ffn in the same 32-channel interleave as w13's rows
+ *        (column p holds W1 or W3 column (p/64)*32 + p%32 by the parity of
+ *        p/32).  NULL when no backward will run.
+ *   w2_bwd  [E][h_ffn][h]: BF16 only, W2 as given (h contiguous), for the
+ *        backward; NULL when no backward will run.
  *   dtype: MOE_F32, MOE_BF16 or MOE_FP8_E4M3.
  */
 typedef struct {
@@ -84,9 +90,12 @@ typedef struct {
   const void* w2;
   const float* w13_scale;
   const float* w2_scale;
+  const void* w13_bwd;
+  const void* w2_bwd;
 } moe_weights;
 
-/* Bytes needed for w13 (`which`=0), w2 (1), w13_scale (2), w2_scale (3). */
+/* Bytes needed for w13 (`which`=0), w2 (1), w13_scale (2), w2_scale (3),
+ * w13_bwd (4), w2_bwd (5). */
 size_t moe_packed_weight_bytes(int which, int E, int h, int h_ffn, int dtype);
 
 /*
@@ -100,11 +109,12 @@ size_t moe_packed_weight_bytes(int which, int E, int h, int h_ffn, int dtype);
  *   channel is all zero); codes = E4M3(w / s) rounded to nearest even with
  *   the division in fp32, saturating at +-448.
  *   Outputs: see moe_weights; scales are written only for FP8 (may be NULL
- *   otherwise).  h and h_ffn must be multiples of 128.
+ *   otherwise).  w13_bwd / w2_bwd are written when non-NULL (BF16 only).
+ *   h and h_ffn must be multiples of 128.
  */
 int moe_pack_weights(const void* w1, const void* w3, const void* w2, int in_dtype, int E, int h,
                      int h_ffn, int out_dtype, void* w13, void* w2_packed, float* w13_scale,
-                     float* w2_scale, void* stream);
+                     float* w2_scale, void* w13_bwd, void* w2_bwd, void* stream);
 
 /*
  * Router: gate GEMM, top-k and softmax over the k selected logits.
@@ -189,7 +199,8 @@ int moe_grouped_swiglu_fwd(const void* xp, const float* xp_scale, const moe_weig
 size_t moe_grouped_bwd_workspace_size(int rows, int h, int h_ffn, int E, int dtype);
 
 /*
- * Backward of the GroupedGEMM (BF16 weights), routing held fixed.
+ * Backward of the GroupedGEMM (BF16 weights with w13_bwd and w2_bwd packed),
+ * routing held fixed.
  *   dyp      [rows][h] bf16: gradient of yp (the weighted dispatch of dY).
  *   xp       [rows][h] bf16: the forward's routed input (re-gathered).
  *   h13_save [rows][2*h_ffn] bf16: FC1's output kept by the forward.

@@ -28,12 +28,13 @@ SZ = ctypes.c_size_t
 
 class MoeWeights(ctypes.Structure):
     _fields_ = [("dtype", I), ("E", I), ("h", I), ("h_ffn", I),
-                ("w13", P), ("w2", P), ("w13_scale", P), ("w2_scale", P)]
+                ("w13", P), ("w2", P), ("w13_scale", P), ("w2_scale", P),
+                ("w13_bwd", P), ("w2_bwd", P)]
 
 
 SIGNATURES = {
     "moe_packed_weight_bytes": (SZ, [I, I, I, I, I]),
-    "moe_pack_weights": (I, [P, P, P, I, I, I, I, I, P, P, P, P, P]),
+    "moe_pack_weights": (I, [P, P, P, I, I, I, I, I, P, P, P, P, P, P, P]),
     "moe_route": (I, [P, P, P, P, I, I, I, I, I, P, P, P]),
     "moe_permute_workspace_size": (SZ, [I, I, I]),
     "moe_permute": (I, [P, I, P, P, I, I, I, I, P, P, P, P, P, I, P, P, SZ, P]),

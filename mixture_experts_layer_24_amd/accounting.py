@@ -104,4 +104,7 @@ def workload_counts(wl) -> dict:
     )
     if wl.backward:
         out["flops_bwd"] = expert_flops_bwd(R, wl.h, wl.h_ffn)
+        # backward dispatch of dY (weighted) and re-gather of x, combine of dX
+        out["permute_bytes_bwd"] = 2 * permute_bytes(wl.T, wl.h, wl.k, s_in, s_in) + 4 * R
+        out["combine_bytes_bwd"] = combine_bytes(wl.T, wl.h, wl.k, s_in, s_in) - 4 * R
     return out

@@ -76,13 +76,15 @@ size_t moe_packed_weight_bytes(int which, int E, int h, int h_ffn, int dtype) {
     case 1: return e * hh * hf * esize(dtype);
     case 2: return dtype == MOE_FP8_E4M3 ? e * 2 * hf * 4 : 0;
     case 3: return dtype == MOE_FP8_E4M3 ? e * hh * 4 : 0;
+    case 4: return dtype == MOE_BF16 ? e * hh * 2 * hf * 2 : 0;
+    case 5: return dtype == MOE_BF16 ? e * hf * hh * 2 : 0;
   }
   return 0;
 }
 
 int moe_pack_weights(const void* w1, const void* w3, const void* w2, int in_dtype, int E, int h,
                      int h_ffn, int out_dtype, void* w13, void* w2_packed, float* w13_scale,
-                     float* w2_scale, void* stream) {
+                     float* w2_scale, void* w13_bwd, void* w2_bwd, void* stream) {
   REQ(E >= 1 && E <= MOE_MAX_EXPERTS, MOE_ERR_SHAPE, "E=%d outside [1, %d]", E, MOE_MAX_EXPERTS);
   REQ(h > 0 && h % 128 == 0 && h_ffn > 0 && h_ffn % 128 == 0, MOE_ERR_SHAPE,
       "h=%d and h_ffn=%d must be positive multiples of 128", h, h_ffn);
@@ -91,9 +93,13 @@ int moe_pack_weights(const void* w1, const void* w3, const void* w2, int in_dtyp
   REQ(ok, MOE_ERR_DTYPE, "unsupported pack %d -> %d", in_dtype, out_dtype);
   PTR(w1); PTR(w3); PTR(w2); PTR(w13); PTR(w2_packed);
   if (out_dtype == MOE_FP8_E4M3) { PTR(w13_scale); PTR(w2_scale); }
+  OPT(w13_bwd); OPT(w2_bwd);
+  REQ((w13_bwd == nullptr && w2_bwd == nullptr) || out_dtype == MOE_BF16, MOE_ERR_DTYPE,
+      "backward weight layouts are only produced for bf16");
   moe_launch::clear_status();
   return launched(moe_launch::pack_weights(w1, w3, w2, in_dtype, E, h, h_ffn, out_dtype, w13,
-                                           w2_packed, w13_scale, w2_scale, (hipStream_t)stream),
+                                           w2_packed, w13_scale, w2_scale, w13_bwd, w2_bwd,
+                                           (hipStream_t)stream),
                   "moe_pack_weights");
 }
 
@@ -217,6 +223,11 @@ int moe_grouped_swiglu_bwd(const void* dyp, const void* xp, const void* h13_save
   int rc = check_weights(W);
   if (rc) return rc;
   REQ(W->dtype == MOE_BF16, MOE_ERR_DTYPE, "backward needs bf16 weights");
+  {
+    const void* w13_bwd = W->w13_bwd;
+    const void* w2_bwd = W->w2_bwd;
+    PTR(w13_bwd); PTR(w2_bwd);
+  }
   REQ(rows >= 0, MOE_ERR_ARG, "rows=%d is negative", rows);
   PTR(dyp); PTR(xp); PTR(h13_save); PTR(offsets); PTR(dxp); PTR(dw1); PTR(dw3); PTR(dw2);
   size_t need = moe_launch::grouped_bwd_ws_bytes(rows, W->h, W->h_ffn, W->E, W->dtype);

@@ -108,7 +108,7 @@ int grouped_bwd(const void* dyp, const void* xp, const void* h13_save, const moe
 size_t grouped_bwd_ws_bytes(int rows, int h, int h_ffn, int E, int dtype);
 int pack_weights(const void* w1, const void* w3, const void* w2, int in_dt, int E, int h,
                  int h_ffn, int out_dt, void* w13, void* w2p, float* w13_scale, float* w2_scale,
-                 hipStream_t s);
+                 void* w13_bwd, void* w2_bwd, hipStream_t s);
 int num_cus();
 
 // Launch status: clear_status() before a call's first launch drops any error
@@ -121,7 +121,7 @@ const char* last_hip_error();
 // Optional per-kernel timing: when enabled (moe_timing_enable), a pair of HIP
 // events is recorded on the launch stream around every kernel of the layer.
 enum TimerId { kTRoute = 0, kTIndex, kTPermute, kTFc1, kTQuant, kTFc2, kTCombine, kTBwd1, kTBwd2,
-               kTBwd3, kTBwd4, kTPack, kNumTimers };
+               kTBwd3, kTBwd4, kTPack, kTXpose, kNumTimers };
 void timer_begin(int id, hipStream_t s);
 void timer_end(int id, hipStream_t s);
 }  // namespace moe_launch

@@ -1,10 +1,178 @@
-// Backward GroupedGEMM (placeholder until the backward kernels land).
-#include "common.h"
+// Backward of the SwiGLU expert GroupedGEMM, routing held fixed.
+//
+// FC2's backward needs FC2's input and the gradient of its output, and that
+// input is recomputed instead of kept (MegaScale-MoE paper review, §四
+// selective activation recomputation; research digest §3.3: activation
+// memory falls from a 3kf to a 2kf term).  Here the forward keeps FC1's
+// output G|U (the 2kf term); A = SiLU(G)*U is recomputed in the dA epilogue.
+// Weight gradients accumulate and are written in FP32 (review §三 parameter
+// update: FP32 gradient accumulation).
+//
+// Every product runs on the same NT engine (both operands K-contiguous):
+//   dA   = dYp W2^T            SchedM, B = W2 as [hf][h]  -> dG, dU, A (epilogue)
+//   dXp  = [dG|dU] W13^T       SchedM, B = W13 as [h][2hf packed]
+//   dW2  = A^T dYp             SchedK over transposed, zero-padded copies
+//   dW13 = Xp^T [dG|dU]        SchedK, epilogue splits dW1 / dW3
+// The weight-gradient products contract over each expert's rows, so their
+// operands are first transposed per expert into [C][K_e] blocks with K_e the
+// row count rounded up to 64 (zeros beyond it).
+#include "gemm_engine.h"
+
+namespace moe {
+
+// Per-expert transpose with zero padding: src [rows][C] (expert-contiguous
+// rows) -> dst, expert e at element kpre[e]*C laid out [C][Kp_e] with
+// Kp_e = roundup(M_e, 64).  One 64 x 64 tile per workgroup through LDS.
+__global__ void __launch_bounds__(256) xpose_kernel(const uint16_t* __restrict__ src, int C,
+                                                    const int32_t* __restrict__ offsets, int E,
+                                                    int rows, uint16_t* __restrict__ dst) {
+  __shared__ int kpre[MOE_MAX_EXPERTS + 1];
+  __shared__ int offs[MOE_MAX_EXPERTS + 1];
+  __shared__ uint16_t tile[64][64 + 8];
+  const int tid = threadIdx.x;
+  for (int e = tid; e <= E; e += 256) {
+    int o = offsets[e];
+    offs[e] = o < 0 ? 0 : (o > rows ? rows : o);
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int kp = 0, prev = offs[0];
+    for (int e = 0; e < E; ++e) {
+      int lo = prev, hi = offs[e + 1] < prev ? prev : offs[e + 1];
+      prev = hi;
+      offs[e] = lo;
+      kpre[e] = kp;
+      kp += ((hi - lo + kKPad - 1) / kKPad) * kKPad;
+    }
+    offs[E] = prev;
+    kpre[E] = kp;
+  }
+  __syncthreads();
+  const int k0g = blockIdx.y * 64;
+  if (k0g >= kpre[E]) return;
+  int lo = 0, hi = E - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (kpre[mid] <= k0g) lo = mid; else hi = mid - 1;
+  }
+  const int e = lo;
+  const int k0 = k0g - kpre[e], kp = kpre[e + 1] - kpre[e], m = offs[e + 1] - offs[e];
+  const int c0 = blockIdx.x * 64;
+  {  // load 64 rows x 64 columns (two 16-byte chunks per thread)
+    const int i = tid >> 2, cc = (tid & 3) * 16;
+    u32x4 v0 = {0, 0, 0, 0}, v1 = {0, 0, 0, 0};
+    if (k0 + i < m) {
+      const u32x4* p = reinterpret_cast<const u32x4*>(src + size_t(offs[e] + k0 + i) * C + c0 + cc);
+      v0 = p[0];
+      v1 = p[1];
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      tile[i][cc + 2 * q] = uint16_t(v0[q]);
+      tile[i][cc + 2 * q + 1] = uint16_t(v0[q] >> 16);
+      tile[i][cc + 8 + 2 * q] = uint16_t(v1[q]);
+      tile[i][cc + 8 + 2 * q + 1] = uint16_t(v1[q] >> 16);
+    }
+  }
+  __syncthreads();
+  {  // write 64 output rows (columns of src) x 64 k values
+    const int c = tid >> 2, kk = (tid & 3) * 16;
+    u32x4 w0, w1;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      w0[q] = uint32_t(tile[kk + 2 * q][c]) | (uint32_t(tile[kk + 2 * q + 1][c]) << 16);
+      w1[q] = uint32_t(tile[kk + 8 + 2 * q][c]) | (uint32_t(tile[kk + 8 + 2 * q + 1][c]) << 16);
+    }
+    u32x4* d = reinterpret_cast<u32x4*>(dst + size_t(kpre[e]) * C + size_t(c0 + c) * kp + k0 + kk);
+    d[0] = w0;
+    d[1] = w1;
+  }
+}
+
+}  // namespace moe
 
 namespace moe_launch {
-size_t grouped_bwd_ws_bytes(int, int, int, int, int) { return 0; }
-int grouped_bwd(const void*, const void*, const void*, const moe_weights*, const int32_t*, int,
-                void*, float*, float*, float*, void*, hipStream_t) {
-  return MOE_ERR_DTYPE;
+using namespace moe;
+
+static size_t al256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Upper bound of the padded K extent: sum_e roundup(M_e, 64) <= rows + 63 E.
+static size_t kpad_upper(int rows, int E) { return size_t(rows) + size_t(kKPad - 1) * E; }
+
+size_t grouped_bwd_ws_bytes(int rows, int h, int h_ffn, int E, int dtype) {
+  (void)dtype;
+  const size_t r = size_t(rows), hh = size_t(h), hf = size_t(h_ffn), kp = kpad_upper(rows, E);
+  return al256(r * 2 * hf * 2)          // dG|dU, packed like G|U
+         + al256(r * hf * 2)            // A recomputed
+         + 2 * al256(hh * kp * 2)       // Xp^T, dYp^T
+         + al256(hf * kp * 2)           // A^T
+         + al256(2 * hf * kp * 2);      // (dG|dU)^T
 }
+
+static int xpose(const void* src, int C, const int32_t* offsets, int E, int rows, void* dst,
+                 hipStream_t s) {
+  const size_t ky = (kpad_upper(rows, E) + 63) / 64;
+  hipLaunchKernelGGL(xpose_kernel, dim3(C / 64, unsigned(ky)), dim3(256), 0, s,
+                     (const uint16_t*)src, C, offsets, E, rows, (uint16_t*)dst);
+  return launch_status();
+}
+
+int grouped_bwd(const void* dyp, const void* xp, const void* h13_save, const moe_weights* W,
+                const int32_t* offsets, int rows, void* dxp, float* dw1, float* dw3, float* dw2,
+                void* ws, hipStream_t s) {
+  const int h = W->h, hf = W->h_ffn, E = W->E;
+  unsigned char* w = static_cast<unsigned char*>(ws);
+  const size_t r = size_t(rows), kp = kpad_upper(rows, E);
+  void* dgu = w;
+  w += al256(r * 2 * hf * 2);
+  void* act = w;
+  w += al256(r * hf * 2);
+  void* xpT = w;
+  w += al256(size_t(h) * kp * 2);
+  void* dypT = w;
+  w += al256(size_t(h) * kp * 2);
+  void* actT = w;
+  w += al256(size_t(hf) * kp * 2);
+  void* dguT = w;
+  int rc;
+  const long mt_upper = (long(rows) + kBM - 1) / kBM + E;
+
+  timer_begin(kTXpose, s);
+  if ((rc = xpose(xp, h, offsets, E, rows, xpT, s))) return rc;
+  if ((rc = xpose(dyp, h, offsets, E, rows, dypT, s))) return rc;
+  timer_end(kTXpose, s);
+
+  // dA = dYp W2^T, with dG, dU and A formed in the epilogue
+  GemmArgs ga{dyp, nullptr, W->w2_bwd, nullptr, offsets, E, h, hf, rows, 0,
+              dgu, act, const_cast<void*>(h13_save), nullptr};
+  if ((rc = launch_gemm<MOE_BF16, kModeBwdDA, kSchedM>(ga, mt_upper * ((hf + kBN - 1) / kBN),
+                                                       kTBwd1, s)))
+    return rc;
+
+  timer_begin(kTXpose, s);
+  if ((rc = xpose(act, hf, offsets, E, rows, actT, s))) return rc;
+  if ((rc = xpose(dgu, 2 * hf, offsets, E, rows, dguT, s))) return rc;
+  timer_end(kTXpose, s);
+
+  // dW2 = A^T dYp  (per expert [hf][h], fp32)
+  GemmArgs g2{actT, nullptr, dypT, nullptr, offsets, E, 0, h, rows, hf,
+              dw2, nullptr, nullptr, nullptr};
+  if ((rc = launch_gemm<MOE_BF16, kModeDW, kSchedK>(
+           g2, long(E) * ((hf + kBM - 1) / kBM) * ((h + kBN - 1) / kBN), kTBwd2, s)))
+    return rc;
+
+  // dXp = [dG|dU] W13^T
+  GemmArgs g3{dgu, nullptr, W->w13_bwd, nullptr, offsets, E, 2 * hf, h, rows, 0,
+              dxp, nullptr, nullptr, nullptr};
+  if ((rc = launch_gemm<MOE_BF16, kModeFC2, kSchedM>(g3, mt_upper * ((h + kBN - 1) / kBN), kTBwd3,
+                                                     s)))
+    return rc;
+
+  // dW1 | dW3 = Xp^T [dG|dU]  (per expert [h][hf] each, fp32)
+  GemmArgs g4{xpT, nullptr, dguT, nullptr, offsets, E, 0, 2 * hf, rows, h,
+              dw1, dw3, nullptr, nullptr};
+  return launch_gemm<MOE_BF16, kModeDW13, kSchedK>(
+      g4, long(E) * ((h + kBM - 1) / kBM) * ((2 * hf + kBN - 1) / kBN), kTBwd4, s);
+}
+
 }  // namespace moe_launch

@@ -1,0 +1,520 @@
+// GroupedGEMM engine shared by the forward and backward passes.
+//
+// C[m][n] = sum_k A[m][k] * B[n][k] for every expert, both operands
+// K-contiguous, fp32 accumulation on MFMA 32x32 (bf16 x16, fp32 x2, fp8 x64).
+// Two schedules:
+//   SchedM -- rows of A are the expert-contiguous routed rows (ragged M per
+//             expert, offsets on device), K fixed: the forward FC1/FC2 and the
+//             backward dA / dXp products;
+//   SchedK -- every expert has a fixed M x N output and a ragged K = its row
+//             count (padded to a 64 multiple with zeros): the weight gradients.
+// Tile 256 x 256, four waves of 128 x 128; operands go global -> LDS with
+// buffer_load ... lds into two XOR-swizzled stages of 128-byte rows.
+#pragma once
+#include "common.h"
+
+namespace moe {
+
+constexpr int kBM = 256, kBN = 256, kRowB = 128;  // tile rows, cols, bytes of K per LDS row
+constexpr int kStageB = kBM * kRowB;              // bytes of one operand stage (32 KB)
+constexpr int kGemmLds = 4 * kStageB;             // A and B, two stages each (128 KB)
+constexpr int kKPad = 64;                         // SchedK: per-expert K padded to this
+
+enum { kSchedM = 0, kSchedK = 1 };
+enum {
+  kModeFC1 = 0,   // SiLU(G)*U epilogue (+ optional G|U keep, FP8 row amax)
+  kModeFC2 = 1,   // plain output [rows][N] (bf16 / fp32; FP8 rescale)
+  kModeBwdDA = 2, // dG, dU from dA and the kept G|U; also A = SiLU(G)*U
+  kModeDW = 3,    // fp32 [E][M][N]
+  kModeDW13 = 4,  // fp32 [E][M][2*h_ffn packed] split into dW1 / dW3
+};
+
+struct GemmArgs {
+  const void* A;          // SchedM: [rows][K]; SchedK: expert e at kpre[e]*M elements, [M][K_e]
+  const float* a_scale;   // FP8: [rows]
+  const void* B;          // SchedM: [E][N][K]; SchedK: expert e at kpre[e]*N elements, [N][K_e]
+  const float* b_scale;   // FP8: [E][N]
+  const int32_t* offsets; // [E+1]
+  int E, K, N, rows, M;   // K: SchedM only; M: SchedK only
+  void* out;              // see the modes
+  void* out2;             // BwdDA: A [rows][N]; DW13: dW3
+  void* save;             // FC1: G|U out [rows][N] bf16 or null; BwdDA: G|U in [rows][2N]
+  uint32_t* row_amax;     // FC1 with FP8: [rows] (fp32 bits, atomic max)
+};
+
+// LDS byte position of 16-byte chunk c of row r: chunks XOR-swizzled by
+// (r/2)%8 so the 64 lanes of a fragment read hit distinct banks.
+__device__ __forceinline__ int lds_pos(int row, int c) {
+  return row * kRowB + ((c ^ ((row >> 1) & 7)) << 4);
+}
+
+template <int DT>
+struct Elem;
+template <> struct Elem<MOE_F32> { static constexpr int bytes = 4; };
+template <> struct Elem<MOE_BF16> { static constexpr int bytes = 2; };
+template <> struct Elem<MOE_FP8_E4M3> { static constexpr int bytes = 1; };
+
+// One 32x32 output block += A-fragment x B-fragment over 32 (bf16, f32) or
+// 64 (fp8) bytes of K per row.  The K order inside a fragment pair is the
+// same for A and B, which is all a dot product needs.
+template <int DT>
+struct Frag;
+template <> struct Frag<MOE_BF16> {
+  u32x4 v;
+  static constexpr int kSub = 4;  // substeps per 128-byte LDS row
+  static constexpr int kReads = 1, kMfma = 1;  // LDS reads per fragment, MFMAs per pair
+  __device__ __forceinline__ void load(const unsigned char* base, int row, int s, int half) {
+    v = *reinterpret_cast<const u32x4*>(base + lds_pos(row, 2 * s + half));
+  }
+  __device__ __forceinline__ static void mma(f32x16& c, const Frag& a, const Frag& b) {
+    c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a.v),
+                                                __builtin_bit_cast(bf16x8, b.v), c, 0, 0, 0);
+  }
+};
+template <> struct Frag<MOE_F32> {
+  u32x4 v;
+  static constexpr int kSub = 4;
+  static constexpr int kReads = 1, kMfma = 4;
+  __device__ __forceinline__ void load(const unsigned char* base, int row, int s, int half) {
+    v = *reinterpret_cast<const u32x4*>(base + lds_pos(row, 2 * s + half));
+  }
+  __device__ __forceinline__ static void mma(f32x16& c, const Frag& a, const Frag& b) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      c = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.v[i]), __uint_as_float(b.v[i]),
+                                               c, 0, 0, 0);
+  }
+};
+template <> struct Frag<MOE_FP8_E4M3> {
+  u32x4 v0, v1;
+  static constexpr int kSub = 2;
+  static constexpr int kReads = 2, kMfma = 1;
+  __device__ __forceinline__ void load(const unsigned char* base, int row, int s, int half) {
+    v0 = *reinterpret_cast<const u32x4*>(base + lds_pos(row, 4 * s + 2 * half));
+    v1 = *reinterpret_cast<const u32x4*>(base + lds_pos(row, 4 * s + 2 * half + 1));
+  }
+  __device__ __forceinline__ static void mma(f32x16& c, const Frag& a, const Frag& b) {
+    i32x8 av = {int(a.v0[0]), int(a.v0[1]), int(a.v0[2]), int(a.v0[3]),
+                int(a.v1[0]), int(a.v1[1]), int(a.v1[2]), int(a.v1[3])};
+    i32x8 bv = {int(b.v0[0]), int(b.v0[1]), int(b.v0[2]), int(b.v0[3]),
+                int(b.v1[0]), int(b.v1[1]), int(b.v1[2]), int(b.v1[3])};
+    // formats 0/0 = E4M3 x E4M3; E8M0 scales of 127 = 1.0
+    c = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, c, 0, 0, 0, 127, 0, 127);
+  }
+};
+
+__device__ __forceinline__ float silu_f(float g) { return g / (1.0f + __expf(-g)); }
+
+// One output tile: expert, first row / column, valid row end, K slabs, and
+// where its A and B rows live.
+struct Tile {
+  int e, row0, row_end, n0, nk, rowB;
+  size_t a_off, a_bytes, b_off, b_bytes;
+};
+
+// Buffer descriptors of a tile's A rows and B rows: reads past the end of
+// the A or B array return zero (ragged M tail, N tail, empty experts).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, size_t off, size_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<unsigned char*>(static_cast<const unsigned char*>(base) + off), (short)0,
+      int(bytes < 0x7FFFFFF0u ? bytes : 0x7FFFFFF0u), 0x00020000);
+}
+
+typedef __attribute__((address_space(3))) void lds_ptr_t;
+
+// Loader offsets for row pitch rowB (see issue_slab).
+struct LoadOff {
+  int e, o;
+};
+__device__ __forceinline__ LoadOff load_off(int rowB, int wave, int lane) {
+  const int lrow = wave * 64 + (lane >> 3);
+  const int sw = (lrow >> 1) & 7;
+  return LoadOff{lrow * rowB + (((lane & 7) ^ sw) << 4), lrow * rowB + (((lane & 7) ^ sw ^ 4) << 4)};
+}
+
+// One K slab (128 bytes per row) of A and B straight from memory into LDS
+// stage `st`.  Wave w fills row groups 8w..8w+7 of each operand; within an
+// 8-row group lane l lands at LDS byte 16*l (row l/8, position l%8), so it
+// fetches the chunk that the XOR swizzle keeps at that position.
+__device__ __forceinline__ void issue_slab(unsigned char* lds, int st, __amdgpu_buffer_rsrc_t ra,
+                                           __amdgpu_buffer_rsrc_t rb, int wave, LoadOff lo,
+                                           int rowB, int koff) {
+  unsigned char* A = lds + st * (2 * kStageB) + wave * 8 * 1024;
+  unsigned char* B = A + kStageB;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int v = ((i & 1) ? lo.o : lo.e) + i * 8 * rowB + koff;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t*)(A + i * 1024), 16, v, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr_t*)(B + i * 1024), 16, v, 0, 0, 0);
+  }
+}
+
+// Fragments of substep s of one LDS stage (4 A and 4 B fragments per wave).
+template <int DT>
+__device__ __forceinline__ void load_frags(Frag<DT> (&fa)[4], Frag<DT> (&fb)[4],
+                                           const unsigned char* As, int arow, int brow, int s,
+                                           int half) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) fa[i].load(As, arow + i * 32, s, half);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) fb[j].load(As + kStageB, brow + j * 32, s, half);
+}
+
+template <int DT>
+__device__ __forceinline__ void mma_all(f32x16 (&acc)[4][4], const Frag<DT> (&fa)[4],
+                                        const Frag<DT> (&fb)[4]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) Frag<DT>::mma(acc[i][j], fa[i], fb[j]);
+}
+
+// Row of accumulator register r of MFMA block i (relative to the wave's rows).
+__device__ __forceinline__ int acc_row(int i, int r, int half) {
+  return i * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+}
+
+template <int DT, int MODE>
+__device__ __forceinline__ void epilogue(const GemmArgs& g, f32x16 (&acc)[4][4], const Tile& T,
+                                         int wm, int wn, int half, int l32,
+                                         unsigned char* free_lds) {
+  const int e = T.e, row0 = T.row0, row_end = T.row_end, n0 = T.n0;
+  if (MODE == kModeFC1 || MODE == kModeFC2) {
+
+  const int rbase = row0 + wm * 128;
+  if (MODE == kModeFC1) {
+    const int hf = g.N / 2;
+    const int chb = (n0 + wn * 128) / 2;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float rmax[16];
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        const int ch = chb + p * 32 + l32;
+        const int colg = n0 + wn * 128 + (2 * p) * 32 + l32;  // packed column of G
+        float sg = 1.f, su = 1.f;
+        if (DT == MOE_FP8_E4M3) {
+          sg = g.b_scale[size_t(e) * g.N + colg];
+          su = g.b_scale[size_t(e) * g.N + colg + 32];
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = rbase + i * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+          float G = acc[i][2 * p][r], U = acc[i][2 * p + 1][r];
+          if (DT == MOE_FP8_E4M3) {
+            const float xs = row < row_end ? g.a_scale[row] : 0.f;
+            G *= xs * sg;
+            U *= xs * su;
+          }
+          const float a = silu_f(G) * U;
+          if (row < row_end) {
+            if (DT == MOE_BF16) {
+              static_cast<uint16_t*>(g.out)[size_t(row) * hf + ch] = uint16_t(f32_to_bf16_bits(a));
+            } else {
+              // fp32 A; for FP8 the per-row quantization reads this exact value
+              static_cast<float*>(g.out)[size_t(row) * hf + ch] = a;
+              if (DT == MOE_FP8_E4M3) rmax[r] = p == 0 ? fabsf(a) : fmaxf(rmax[r], fabsf(a));
+            }
+            if (g.save) {
+              uint16_t* sv = static_cast<uint16_t*>(g.save) + size_t(row) * g.N + colg;
+              sv[0] = uint16_t(f32_to_bf16_bits(G));
+              sv[32] = uint16_t(f32_to_bf16_bits(U));
+            }
+          } else if (DT == MOE_FP8_E4M3) {
+            rmax[r] = 0.f;
+          }
+        }
+      }
+      if (DT == MOE_FP8_E4M3) {
+        // row max over this wave's 64 channels: reduce over the 32 lanes of a half
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float m = rmax[r];
+#pragma unroll
+          for (int o = 16; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+          const int row = rbase + i * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+          if (l32 == 0 && row < row_end) atomicMax(g.row_amax + row, __float_as_uint(m));
+        }
+      }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int col = n0 + wn * 128 + j * 32 + l32;
+        if (col >= g.N) continue;
+        float cs = 1.f;
+        if (DT == MOE_FP8_E4M3) cs = g.b_scale[size_t(e) * g.N + col];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = rbase + i * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+          if (row < row_end) {
+            float y = acc[i][j][r];
+            if (DT == MOE_FP8_E4M3) y *= g.a_scale[row] * cs;
+            if (DT == MOE_F32)
+              static_cast<float*>(g.out)[size_t(row) * g.N + col] = y;
+            else
+              static_cast<uint16_t*>(g.out)[size_t(row) * g.N + col] = uint16_t(f32_to_bf16_bits(y));
+          }
+        }
+      }
+  }
+
+  } else if (MODE == kModeBwdDA) {
+    // dA tile -> dG, dU (packed like the forward's G|U) and A = SiLU(G)*U
+    // The kept G|U of this wave's 128 rows x 32 channels (64 packed columns,
+    // 128 B per row) go global -> LDS (the stage that is idle during the
+    // epilogue) in 16 direct loads, then come out of LDS as needed.
+    const int hf = g.N;
+    uint16_t* __restrict__ dgu = static_cast<uint16_t*>(g.out);
+    uint16_t* __restrict__ aout = static_cast<uint16_t*>(g.out2);
+    const int wrow0 = row0 + wm * 128;
+    const size_t rowb = size_t(2 * hf) * 2;  // bytes per G|U row
+    const __amdgpu_buffer_rsrc_t gsrc =
+        rsrc(g.save, size_t(wrow0) * rowb, size_t(g.rows > wrow0 ? g.rows - wrow0 : 0) * rowb);
+    unsigned char* wl = free_lds + (wm * 2 + wn) * 16384;
+    const uint16_t* wl16 = reinterpret_cast<const uint16_t*>(wl);
+    const int lane = half * 32 + l32;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {                // unrolled: acc stays in registers
+      const int fb0 = n0 + wn * 128 + j * 32;      // first channel of the group
+      const int pb = (fb0 >> 5) * 64;              // its first packed column
+      __builtin_amdgcn_s_waitcnt(0);              // earlier reads of this region done
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const int v = (q * 8 + (lane >> 3)) * int(rowb) + pb * 2 + (lane & 7) * 16;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(gsrc, (lds_ptr_t*)(wl + q * 1024), 16, v, 0, 0, 0);
+      }
+      __builtin_amdgcn_s_waitcnt(0);
+      const int f = fb0 + l32;
+      if (f >= hf) continue;
+      const int pg = pb + l32, pu = pg + 32;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int rl = acc_row(i, r, half);
+          const int row = wrow0 + rl;
+          if (row >= row_end) continue;
+          const float G = bf16_to_f32(wl16[rl * 64 + l32]), U = bf16_to_f32(wl16[rl * 64 + 32 + l32]);
+          const float sg = 1.0f / (1.0f + __expf(-G));
+          const float si = G * sg;
+          const float dA = acc[i][j][r];
+          const size_t b = size_t(row) * (2 * hf);
+          dgu[b + pg] = uint16_t(f32_to_bf16_bits(dA * U * sg * (1.0f + G * (1.0f - sg))));
+          dgu[b + pu] = uint16_t(f32_to_bf16_bits(dA * si));
+          aout[size_t(row) * hf + f] = uint16_t(f32_to_bf16_bits(si * U));
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();  // the idle stage is refilled by the next tile's loads
+  } else {
+    // weight gradients, fp32: rows m of expert e's [M][N] (DW13: N packed)
+    float* o1 = static_cast<float*>(g.out);
+    float* o2 = static_cast<float*>(g.out2);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int n = n0 + wn * 128 + j * 32 + l32;
+      if (n >= g.N) continue;
+      float* dst = o1;
+      int col = n, ld = g.N;
+      if (MODE == kModeDW13) {
+        dst = ((n >> 5) & 1) ? o2 : o1;
+        col = (n >> 6) * 32 + (n & 31);
+        ld = g.N / 2;
+      }
+      dst += size_t(e) * g.M * ld;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int m = row0 + wm * 128 + acc_row(i, r, half);
+          if (m < row_end) dst[size_t(m) * ld + col] = acc[i][j][r];
+        }
+    }
+  }
+}
+
+template <int DT, int MODE, int SCHED>
+__global__ void __launch_bounds__(256, 1) grouped_gemm_kernel(GemmArgs g) {
+  extern __shared__ __align__(16) unsigned char lds[];
+  __shared__ int tpre[MOE_MAX_EXPERTS + 1];  // tiles before expert e
+  __shared__ int offs[MOE_MAX_EXPERTS + 1];  // SchedM: row offsets; SchedK: padded K prefix
+  constexpr int EB = Elem<DT>::bytes;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+  const int wm = wave >> 1, wn = wave & 1;
+  const int half = lane >> 5, l32 = lane & 31;
+  const int NT = ceil_div(g.N, kBN);
+  const int MT = SCHED == kSchedK ? ceil_div(g.M, kBM) : 0;
+
+  for (int e = tid; e <= g.E; e += 256) {
+    int o = g.offsets[e];
+    offs[e] = o < 0 ? 0 : (o > g.rows ? g.rows : o);  // never address past `rows`
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int run = 0, kp = 0, prev = offs[0];
+    tpre[0] = 0;
+    for (int e = 0; e < g.E; ++e) {
+      int lo = prev, hi = offs[e + 1] < prev ? prev : offs[e + 1];
+      prev = hi;
+      if (SCHED == kSchedM) {
+        offs[e + 1] = hi;
+        run += ceil_div(hi - lo, kBM) * NT;
+      } else {
+        offs[e] = kp;  // becomes the padded K prefix
+        kp += ceil_div(hi - lo, kKPad) * kKPad;
+        run += MT * NT;
+      }
+      tpre[e + 1] = run;
+    }
+    if (SCHED == kSchedK) offs[g.E] = kp;
+  }
+  __syncthreads();
+  const int total = tpre[g.E];
+  const int G = gridDim.x;
+  const int b = blockIdx.x;
+  // the 32 workgroups of one XCD (b % 8) take consecutive tiles
+  int t = (G % 8 == 0) ? (b % 8) * (G / 8) + b / 8 : b;
+  if (t >= total) return;
+
+  auto tile_of = [&](int tt) {
+    int lo = 0, hi = g.E - 1;  // expert e with tpre[e] <= tt < tpre[e+1]
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (tpre[mid] <= tt) lo = mid; else hi = mid - 1;
+    }
+    Tile T;
+    T.e = lo;
+    const int local = tt - tpre[lo];
+    if (SCHED == kSchedM) {
+      // experts in order, m-tiles fastest: consecutive tiles share a weight block
+      const int mt_e = ceil_div(offs[lo + 1] - offs[lo], kBM);
+      const int nt = local / mt_e, mt = local - nt * mt_e;
+      T.row0 = offs[lo] + mt * kBM;
+      T.row_end = offs[lo + 1];
+      T.n0 = nt * kBN;
+      T.rowB = g.K * EB;
+      T.a_off = size_t(T.row0) * T.rowB;
+      T.a_bytes = size_t(g.rows - T.row0) * T.rowB;
+      T.b_off = (size_t(lo) * g.N + T.n0) * T.rowB;
+    } else {
+      const int nt = local / MT, mt = local - nt * MT;
+      const int k0 = offs[lo], ke = offs[lo + 1] - k0;
+      T.row0 = mt * kBM;
+      T.row_end = g.M;
+      T.n0 = nt * kBN;
+      T.rowB = ke * EB;
+      T.a_off = size_t(k0) * g.M * EB + size_t(T.row0) * T.rowB;
+      T.a_bytes = size_t(g.M - T.row0) * T.rowB;
+      T.b_off = size_t(k0) * g.N * EB + size_t(T.n0) * T.rowB;
+    }
+    T.b_bytes = size_t(g.N - T.n0) * T.rowB;
+    T.nk = T.rowB / kRowB;
+    return T;
+  };
+
+  constexpr int S = Frag<DT>::kSub;             // substeps per slab (even)
+  constexpr int NR = 8 * Frag<DT>::kReads;      // LDS reads per substep
+  constexpr int NM = 16 * Frag<DT>::kMfma;      // MFMAs per substep
+  // fragment rows inside a stage
+  const int arow = wm * 128 + l32, brow = wn * 128 + l32;
+
+  Tile cur = tile_of(t);
+  __amdgpu_buffer_rsrc_t ra = rsrc(g.A, cur.a_off, cur.a_bytes), rb = rsrc(g.B, cur.b_off, cur.b_bytes);
+  LoadOff lo = load_off(cur.rowB, wave, lane);
+  int st = 0;
+  issue_slab(lds, st, ra, rb, wave, lo, cur.rowB, 0);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  Frag<DT> fa[2][4], fb[2][4];
+  load_frags<DT>(fa[0], fb[0], lds, arow, brow, 0, half);
+
+  while (true) {
+    const int tn = t + G;
+    const bool has_next = tn < total;
+    const Tile nxt = has_next ? tile_of(tn) : cur;
+    const __amdgpu_buffer_rsrc_t ra_n = rsrc(g.A, nxt.a_off, nxt.a_bytes);
+    const __amdgpu_buffer_rsrc_t rb_n = rsrc(g.B, nxt.b_off, nxt.b_bytes);
+    const LoadOff lo_n = load_off(nxt.rowB, wave, lane);
+
+    f32x16 acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+    for (int kt = 0; kt < cur.nk; ++kt) {
+      // Stage st holds slab kt and fa[0]/fb[0] its first fragments.  Load
+      // slab kt+1 (or the next tile's first) into the other stage.
+      const bool last = kt + 1 == cur.nk;
+      issue_slab(lds, st ^ 1, last ? ra_n : ra, last ? rb_n : rb, wave, last ? lo_n : lo,
+                 last ? nxt.rowB : cur.rowB, last ? 0 : (kt + 1) * kRowB);
+      const unsigned char* As = lds + st * (2 * kStageB);
+#pragma unroll
+      for (int s = 0; s + 1 < S; ++s) {
+        load_frags<DT>(fa[(s + 1) & 1], fb[(s + 1) & 1], As, arow, brow, s + 1, half);
+        mma_all<DT>(acc, fa[s & 1], fb[s & 1]);
+      }
+      // interleave: one LDS read (and one global load early on) per MFMA
+#pragma unroll
+      for (int s = 0; s + 1 < S; ++s)
+#pragma unroll
+        for (int q = 0; q < NM; ++q) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          if (q < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          if (s == 0 && q < 16) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+        }
+      __builtin_amdgcn_s_waitcnt(0);  // stage st read out; slab kt+1 landed
+      __syncthreads();
+      // next slab's first fragments load while the last substep multiplies
+      load_frags<DT>(fa[0], fb[0], lds + (st ^ 1) * (2 * kStageB), arow, brow, 0, half);
+      mma_all<DT>(acc, fa[1], fb[1]);
+      __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);
+      st ^= 1;
+    }
+    if (cur.nk == 0 && has_next) {
+      // an empty-K tile prefetched nothing: bring in the next tile's first slab
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      issue_slab(lds, st, ra_n, rb_n, wave, lo_n, nxt.rowB, 0);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      load_frags<DT>(fa[0], fb[0], lds + st * (2 * kStageB), arow, brow, 0, half);
+    }
+
+    epilogue<DT, MODE>(g, acc, cur, wm, wn, half, l32, lds + (st ^ 1) * (2 * kStageB));
+    if (!has_next) break;
+    t = tn;
+    cur = nxt;
+    ra = ra_n;
+    rb = rb_n;
+    lo = lo_n;
+  }
+}
+
+}  // namespace moe
+
+namespace moe_launch {
+
+// Persistent launch: one workgroup per CU (or fewer if there are fewer tiles).
+template <int DT, int MODE, int SCHED>
+inline int launch_gemm(const moe::GemmArgs& a, long tiles_upper, int timer, hipStream_t s) {
+  using namespace moe;
+  static bool attr = allow_lds(grouped_gemm_kernel<DT, MODE, SCHED>, kGemmLds);
+  if (!attr) return MOE_ERR_HIP;
+  int grid = num_cus();
+  if (tiles_upper < grid) grid = int(tiles_upper);
+  if (grid < 1) grid = 1;
+  timer_begin(timer, s);
+  hipLaunchKernelGGL((grouped_gemm_kernel<DT, MODE, SCHED>), dim3(grid), dim3(256), kGemmLds, s, a);
+  timer_end(timer, s);
+  return launch_status();
+}
+
+}  // namespace moe_launch

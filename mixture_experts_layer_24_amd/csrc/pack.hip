@@ -68,6 +68,27 @@ __global__ void __launch_bounds__(256) transpose_kernel(const void* __restrict__
   }
 }
 
+// Backward layout of W1 | W3: dst[e][i][p] = (p/32 odd ? W3 : W1)[e][i][(p/64)*32 + p%32],
+// 16 bytes (8 bf16) per thread.
+__global__ void interleave13_kernel(const uint16_t* __restrict__ w1, const uint16_t* __restrict__ w3,
+                                    int E, int h, int hf, uint16_t* __restrict__ dst) {
+  const size_t q = size_t(blockIdx.x) * blockDim.x + threadIdx.x;  // 8-element chunk of dst
+  const size_t per_row = size_t(2 * hf) / 8;
+  const size_t total = size_t(E) * h * per_row;
+  if (q >= total) return;
+  const size_t row = q / per_row;                  // e * h + i
+  const int p = int(q - row * per_row) * 8;
+  const int ch = (p >> 6) * 32 + (p & 31);
+  const uint16_t* src = ((p >> 5) & 1) ? w3 : w1;
+  *reinterpret_cast<u32x4*>(dst + row * (2 * hf) + p) =
+      *reinterpret_cast<const u32x4*>(src + row * hf + ch);
+}
+
+__global__ void copy16_kernel(const u32x4* __restrict__ src, u32x4* __restrict__ dst, size_t n) {
+  const size_t q = size_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (q < n) dst[q] = src[q];
+}
+
 }  // namespace moe
 
 namespace moe_launch {
@@ -93,7 +114,7 @@ static void pack_all(const void* w1, const void* w3, const void* w2, int E, int 
 
 int pack_weights(const void* w1, const void* w3, const void* w2, int in_dt, int E, int h,
                  int h_ffn, int out_dt, void* w13, void* w2p, float* w13_scale, float* w2_scale,
-                 hipStream_t s) {
+                 void* w13_bwd, void* w2_bwd, hipStream_t s) {
   timer_begin(kTPack, s);
   if (in_dt == MOE_F32 && out_dt == MOE_F32)
     pack_all<true, MOE_F32>(w1, w3, w2, E, h, h_ffn, w13, w2p, nullptr, nullptr, s);
@@ -103,6 +124,16 @@ int pack_weights(const void* w1, const void* w3, const void* w2, int in_dt, int 
     pack_all<false, MOE_FP8_E4M3>(w1, w3, w2, E, h, h_ffn, w13, w2p, w13_scale, w2_scale, s);
   else
     return MOE_ERR_DTYPE;
+  if (w13_bwd) {
+    const size_t chunks = size_t(E) * h * (2 * size_t(h_ffn) / 8);
+    hipLaunchKernelGGL(interleave13_kernel, dim3(unsigned((chunks + 255) / 256)), dim3(256), 0, s,
+                       (const uint16_t*)w1, (const uint16_t*)w3, E, h, h_ffn, (uint16_t*)w13_bwd);
+  }
+  if (w2_bwd) {
+    const size_t n = size_t(E) * h_ffn * h * 2 / 16;
+    hipLaunchKernelGGL(copy16_kernel, dim3(unsigned((n + 255) / 256)), dim3(256), 0, s,
+                       (const u32x4*)w2, (u32x4*)w2_bwd, n);
+  }
   timer_end(kTPack, s);
   return launch_status();
 }

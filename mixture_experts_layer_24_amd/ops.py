@@ -39,10 +39,10 @@ def moe_packed_weight_bytes(which, E, h, h_ffn, dtype):
 
 
 def moe_pack_weights(w1, w3, w2, in_dtype, E, h, h_ffn, out_dtype, w13, w2_packed, w13_scale,
-                     w2_scale, stream=None):
+                     w2_scale, w13_bwd=None, w2_bwd=None, stream=None):
     return check(lib().moe_pack_weights(_p(w1), _p(w3), _p(w2), in_dtype, E, h, h_ffn, out_dtype,
                                         _p(w13), _p(w2_packed), _p(w13_scale), _p(w2_scale),
-                                        _s(stream)))
+                                        _p(w13_bwd), _p(w2_bwd), _s(stream)))
 
 
 def moe_route(x, w_gate, bias, logits, T, h, E, k, dtype, topk_idx, topk_w, stream=None):
@@ -100,7 +100,7 @@ def moe_version() -> int:
 class PackedWeights:
     """Expert weights packed (and for FP8 quantized) by ``moe_pack_weights``."""
 
-    def __init__(self, w1, w3, w2, out_dtype: int, stream=None):
+    def __init__(self, w1, w3, w2, out_dtype: int, backward: bool = False, stream=None):
         E, h, hf = w1.shape
         dev = w1.device
         in_dt = dtype_code(w1)
@@ -111,11 +111,14 @@ class PackedWeights:
         fp8 = out_dtype == MOE_FP8_E4M3
         self.w13_scale = torch.empty(E, 2 * hf, dtype=torch.float32, device=dev) if fp8 else None
         self.w2_scale = torch.empty(E, h, dtype=torch.float32, device=dev) if fp8 else None
+        self.w13_bwd = torch.empty(sz(4), dtype=torch.uint8, device=dev) if backward else None
+        self.w2_bwd = torch.empty(sz(5), dtype=torch.uint8, device=dev) if backward else None
         moe_pack_weights(w1, w3, w2, in_dt, E, h, hf, out_dtype, self.w13, self.w2,
-                         self.w13_scale, self.w2_scale, stream)
+                         self.w13_scale, self.w2_scale, self.w13_bwd, self.w2_bwd, stream)
+        ptr = lambda t: None if t is None else t.data_ptr()
         self.struct = MoeWeights(out_dtype, E, h, hf, self.w13.data_ptr(), self.w2.data_ptr(),
-                                 self.w13_scale.data_ptr() if fp8 else None,
-                                 self.w2_scale.data_ptr() if fp8 else None)
+                                 ptr(self.w13_scale), ptr(self.w2_scale), ptr(self.w13_bwd),
+                                 ptr(self.w2_bwd))
 
 
 class MoELayer:

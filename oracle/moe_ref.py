@@ -222,7 +222,14 @@ def layer_forward_tokens(x_rows, idx_rows, w_rows, w1, w3, w2):
 # gradients accumulate in FP32.
 # --------------------------------------------------------------------------
 
-def layer_backward(dy, x, w, dst_row, offsets, w1, w3, w2, g=None, u=None):
+def round_bf16(a: np.ndarray) -> np.ndarray:
+    """Round to fp32 (nearest even), then to bf16 (nearest even); fp64 result."""
+    b = np.ascontiguousarray(np.asarray(a, np.float64).astype(np.float32)).view(np.uint32)
+    r = ((b + np.uint32(0x7FFF) + ((b >> np.uint32(16)) & np.uint32(1))) & np.uint32(0xFFFF0000))
+    return r.view(np.float32).astype(np.float64)
+
+
+def layer_backward(dy, x, w, dst_row, offsets, w1, w3, w2, g=None, u=None, bf16_operands=False):
     """Gradients of ``y`` w.r.t. ``x`` (expert path only) and every expert weight.
 
     dYp[dst_row[t,j]] = w[t,j] * dY[t]
@@ -230,11 +237,15 @@ def layer_backward(dy, x, w, dst_row, offsets, w1, w3, w2, g=None, u=None):
     s = sigmoid(G); dG = dA * U * s * (1 + G (1 - s));  dU = dA * SiLU(G)
     dXp = dG W1^T + dU W3^T;  dW1_e = Xp_e^T dG_e;  dW3_e = Xp_e^T dU_e
     dX[t] = sum_j dXp[dst_row[t, j]]
-    All fp64.
+    All fp64.  With ``bf16_operands`` every matrix-product operand that a
+    BF16 training step holds in BF16 (dYp, the kept G and U, A, dG, dU, and
+    dXp before the sum over slots) is rounded to BF16 first; the arithmetic
+    stays fp64.  That is the BF16-storage counterpart of the exact result.
     """
     E = w1.shape[0]
+    rb = round_bf16 if bf16_operands else (lambda v: np.asarray(v, np.float64))
     xp = permute(np.asarray(x, np.float64), dst_row)
-    dyp = permute(np.asarray(dy, np.float64), dst_row, row_scale=w)
+    dyp = rb(permute(np.asarray(dy, np.float64), dst_row, row_scale=w))
     R, h = xp.shape
     dxp = np.zeros((R, h))
     dw1 = np.zeros(w1.shape); dw3 = np.zeros(w3.shape); dw2 = np.zeros(w2.shape)
@@ -245,20 +256,54 @@ def layer_backward(dy, x, w, dst_row, offsets, w1, w3, w2, g=None, u=None):
         W1 = np.asarray(w1[e], np.float64); W3 = np.asarray(w3[e], np.float64)
         W2 = np.asarray(w2[e], np.float64)
         xe = xp[lo:hi]
-        ge = xe @ W1 if g is None else np.asarray(g[lo:hi], np.float64)
-        ue = xe @ W3 if u is None else np.asarray(u[lo:hi], np.float64)
+        ge = rb(xe @ W1 if g is None else np.asarray(g[lo:hi], np.float64))
+        ue = rb(xe @ W3 if u is None else np.asarray(u[lo:hi], np.float64))
         s = sigmoid(ge)
-        a = ge * s * ue
+        a = rb(ge * s * ue)
         dye = dyp[lo:hi]
         da = dye @ W2.T
         dw2[e] = a.T @ dye
-        dg = da * ue * s * (1.0 + ge * (1.0 - s))
-        du = da * ge * s
-        dxp[lo:hi] = dg @ W1.T + du @ W3.T
+        dg = rb(da * ue * s * (1.0 + ge * (1.0 - s)))
+        du = rb(da * ge * s)
+        dxp[lo:hi] = rb(dg @ W1.T + du @ W3.T)
         dw1[e] = xe.T @ dg
         dw3[e] = xe.T @ du
     dx = combine(dxp, dst_row, None)
     return dict(dx=dx, dw1=dw1, dw3=dw3, dw2=dw2, dxp=dxp, dyp=dyp)
+
+
+def expert_grads(xe, dye, w1e, w3e, w2e, bf16_operands=False):
+    """One expert's gradients from its routed rows.
+
+    ``xe`` are the expert's routed inputs, ``dye`` the gradients of its
+    outputs (already weighted).  Returns dW1, dW3, dW2 and dXp for those rows.
+    ``bf16_operands`` as in :func:`layer_backward`.
+    """
+    rb = round_bf16 if bf16_operands else (lambda v: np.asarray(v, np.float64))
+    xe = np.asarray(xe, np.float64); dye = rb(dye)
+    W1 = np.asarray(w1e, np.float64); W3 = np.asarray(w3e, np.float64); W2 = np.asarray(w2e, np.float64)
+    g = rb(xe @ W1)
+    u = rb(xe @ W3)
+    s = sigmoid(g)
+    da = dye @ W2.T
+    dg = rb(da * u * s * (1.0 + g * (1.0 - s)))
+    du = rb(da * g * s)
+    return xe.T @ dg, xe.T @ du, rb(g * s * u).T @ dye, rb(dg @ W1.T + du @ W3.T)
+
+
+def layer_backward_tokens(dy_rows, x_rows, idx_rows, w_rows, w1, w3, w2, bf16_operands=False):
+    """dX for a subset of tokens: sum over their k experts of that expert's
+    input gradient at the token's weighted output gradient (per-token form of
+    :func:`layer_backward`)."""
+    x_rows = np.asarray(x_rows, np.float64)
+    dy_rows = np.asarray(dy_rows, np.float64)
+    dx = np.zeros_like(x_rows)
+    for e in np.unique(idx_rows):
+        tt, jj = np.nonzero(idx_rows == e)
+        dye = np.asarray(w_rows[tt, jj], np.float64)[:, None] * dy_rows[tt]
+        *_, dxe = expert_grads(x_rows[tt], dye, w1[e], w3[e], w2[e], bf16_operands)
+        np.add.at(dx, tt, dxe)
+    return dx
 
 
 # --------------------------------------------------------------------------
@@ -375,16 +420,21 @@ def layer_forward_fp8(x, w_gate, bias, w1, w3, w2, k, logits=None):
                 src_tok=src_tok, qx=qx, sx=sx, a=a_all, qa=qa_all, sa=sa_all, yp=yp, y=y)
 
 
-def layer_forward_fp8_tokens(x_rows, idx_rows, w_rows, w1, w3, w2, wq_cache=None):
-    """Per-token form of :func:`layer_forward_fp8` for sampled tokens."""
+def layer_forward_fp8_tokens(x_rows, idx_rows, w_rows, w1, w3, w2, wq_cache=None, cols=None):
+    """Per-token form of :func:`layer_forward_fp8` for sampled tokens.
+
+    ``cols`` restricts the output to those columns of y; W2's per-column
+    scales are independent, so only those columns of W2 are quantized.
+    """
     qx, sx = quantize_rows(x_rows)
     xd = e4m3_decode(qx) * sx[:, None].astype(np.float64)
     n = xd.shape[0]
-    y = np.zeros((n, np.shape(w2[0])[1]))
+    y = np.zeros((n, np.shape(w2[0])[1] if cols is None else len(cols)))
     cache = {} if wq_cache is None else wq_cache
     for e in np.unique(idx_rows):
         if e not in cache:
-            cache[e] = (quantize_cols(w1[e]), quantize_cols(w3[e]), quantize_cols(w2[e]))
+            w2e = w2[e] if cols is None else np.asarray(w2[e])[:, cols]
+            cache[e] = (quantize_cols(w1[e]), quantize_cols(w3[e]), quantize_cols(w2e))
         (q1, s1), (q3, s3), (q2, s2) = cache[e]
         tt, jj = np.nonzero(idx_rows == e)
         xe = xd[tt]

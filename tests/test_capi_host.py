@@ -95,6 +95,14 @@ def test_grouped_validation():
     assert call(W=f32, save=A) == L.MOE_ERR_DTYPE         # G|U kept only for bf16
     assert lib.moe_grouped_swiglu_bwd(A, A, A, ctypes.byref(f32), A, 512, A, A, A, A, A, 1 << 30,
                                       None) == L.MOE_ERR_DTYPE
+    # bf16 weights without the backward layouts
+    assert lib.moe_grouped_swiglu_bwd(A, A, A, ctypes.byref(W), A, 512, A, A, A, A, A, 1 << 30,
+                                      None) == L.MOE_ERR_ARG
+    Wb = L.MoeWeights(L.MOE_BF16, 8, 256, 384, A.value, A.value, None, None, A.value, A.value)
+    need = lib.moe_grouped_bwd_workspace_size(512, 256, 384, 8, L.MOE_BF16)
+    assert need > 0
+    assert lib.moe_grouped_swiglu_bwd(A, A, A, ctypes.byref(Wb), A, 512, A, A, A, A, A, need - 1,
+                                      None) == L.MOE_ERR_WORKSPACE
 
 
 def test_combine_and_pack_validation():
@@ -103,8 +111,12 @@ def test_combine_and_pack_validation():
     assert lib.moe_combine(A, L.MOE_FP8_E4M3, A, A, 10, 16, 2, A, L.MOE_BF16, None) == L.MOE_ERR_DTYPE
     assert lib.moe_combine(A, L.MOE_BF16, A, None, 0, 16, 2, A, L.MOE_BF16, None) == L.MOE_OK
     assert lib.moe_pack_weights(A, A, A, L.MOE_F32, 8, 256, 384, L.MOE_BF16, A, A, None, None,
-                                None) == L.MOE_ERR_DTYPE
+                                None, None, None) == L.MOE_ERR_DTYPE
     assert lib.moe_pack_weights(A, A, A, L.MOE_BF16, 8, 256, 384, L.MOE_FP8_E4M3, A, A, None, None,
-                                None) == L.MOE_ERR_ARG
+                                None, None, None) == L.MOE_ERR_ARG
+    assert lib.moe_pack_weights(A, A, A, L.MOE_BF16, 8, 256, 384, L.MOE_FP8_E4M3, A, A, A, A,
+                                A, A, None) == L.MOE_ERR_DTYPE   # backward layouts are bf16 only
+    assert lib.moe_packed_weight_bytes(4, 8, 256, 384, L.MOE_BF16) == 8 * 256 * 768 * 2
+    assert lib.moe_packed_weight_bytes(5, 8, 256, 384, L.MOE_FP8_E4M3) == 0
     assert lib.moe_packed_weight_bytes(0, 8, 256, 384, L.MOE_BF16) == 8 * 768 * 256 * 2
     assert lib.moe_packed_weight_bytes(3, 8, 256, 384, L.MOE_FP8_E4M3) == 8 * 256 * 4

@@ -419,3 +419,35 @@ def _full_size_sampled(name, n_sample=48, seed=0):
 @pytest.mark.slow
 def test_full_size_mixtral_sampled():
     _full_size_sampled("mixtral")
+
+
+@pytest.mark.slow
+def test_full_size_352b_zipf_sampled():
+    """Skewed routing: the hottest expert gets several times the mean load."""
+    _, layer = _full_size_sampled("m352b_zipf", n_sample=24)
+    counts = layer.counts.cpu().numpy()
+    say(f"  352B counts: max {counts.max()} ({counts.max() / counts.mean():.2f}x mean), min {counts.min()}")
+    assert counts.max() > 5 * counts.mean() and counts.min() > 0
+
+
+@pytest.mark.slow
+def test_full_size_hunyuan_fp8_sampled():
+    """FP8 layer at full size: tokens of one expert, a subset of output columns."""
+    wl = moe_synth.WORKLOADS["hunyuan_fp8"]
+    say("full-size hunyuan_fp8: generating inputs")
+    inp = moe_synth.gen_all(wl, seed=0)
+    layer, _ = _run_gpu_layer(wl, inp)
+    x32 = lambda rows: to_f32(inp["x"][rows])
+    rl = ref.router_logits(x32(np.arange(wl.T)), to_f32(inp["w_gate"]), inp["bias"])
+    ri, rw = ref.topk_softmax(rl, wl.k)
+    keep = ref.topk_margin(rl, wl.k) > 1e-3
+    np.testing.assert_array_equal(layer.topk_idx.cpu().numpy()[keep], ri[keep])
+    e = int(ri[0, 0])
+    toks = np.nonzero((ri[:, 0] == e) & keep)[0][:12]
+    cols = np.sort(np.random.default_rng(1).choice(wl.h, 64, replace=False))
+    say(f"full-size hunyuan_fp8: oracle on {len(toks)} tokens of expert {e}, {len(cols)} columns")
+    y_ref = ref.layer_forward_fp8_tokens(x32(toks), ri[toks], rw[toks], _PerExpert(inp["w1"]),
+                                         _PerExpert(inp["w3"]), _PerExpert(inp["w2"]), cols=cols)
+    y_gpu = host(layer.y)[toks][:, cols]
+    # k = 1: y is the bf16 expert output itself, one bf16 rounding
+    check_close(y_gpu, y_ref, 6e-2, HALF_ULP_BF16 * np.abs(y_ref), None, "full-size fp8 y")

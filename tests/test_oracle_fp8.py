@@ -99,3 +99,6 @@ def test_fp8_layer_close_to_exact_layer():
     assert 1e-3 * rms < np.sqrt(np.mean(err ** 2)) < 0.1 * rms
     yt = ref.layer_forward_fp8_tokens(inp["x"], q["idx"], q["w"], inp["w1"], inp["w3"], inp["w2"])
     np.testing.assert_allclose(q["y"], yt, rtol=1e-12, atol=1e-12 * rms)
+    cols = np.array([3, 17, 100, 255])
+    yc = ref.layer_forward_fp8_tokens(inp["x"], q["idx"], q["w"], inp["w1"], inp["w3"], inp["w2"], cols=cols)
+    np.testing.assert_allclose(yc, q["y"][:, cols], rtol=1e-12, atol=1e-12 * rms)

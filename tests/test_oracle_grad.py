@@ -43,6 +43,41 @@ def test_backward_matches_finite_differences(seed):
         assert np.abs(num - grad).max() <= 1e-6 * scale, name
 
 
+def test_per_token_and_per_expert_forms_match():
+    x, w1, w3, w2, dy, fw = _setup(7, T=11, h=6, hf=5, E=4, k=2)
+    bw = ref.layer_backward(dy, x, fw["w"], fw["dst_row"], fw["offsets"], w1, w3, w2)
+    dx = ref.layer_backward_tokens(dy, x, fw["idx"], fw["w"], w1, w3, w2)
+    np.testing.assert_allclose(dx, bw["dx"], rtol=1e-12, atol=1e-13)
+    xp = ref.permute(x, fw["dst_row"])
+    dyp = ref.permute(dy, fw["dst_row"], row_scale=fw["w"])
+    for e in range(4):
+        lo, hi = fw["offsets"][e], fw["offsets"][e + 1]
+        g1, g3, g2, dxp = ref.expert_grads(xp[lo:hi], dyp[lo:hi], w1[e], w3[e], w2[e])
+        np.testing.assert_allclose(g1, bw["dw1"][e], rtol=1e-12, atol=1e-13)
+        np.testing.assert_allclose(g3, bw["dw3"][e], rtol=1e-12, atol=1e-13)
+        np.testing.assert_allclose(g2, bw["dw2"][e], rtol=1e-12, atol=1e-13)
+        np.testing.assert_allclose(dxp, bw["dxp"][lo:hi], rtol=1e-12, atol=1e-13)
+
+
+def test_round_bf16_matches_torch():
+    rng = np.random.default_rng(3)
+    v = np.concatenate([rng.standard_normal(10000) * 10.0 ** rng.uniform(-5, 5, 10000),
+                        [0.0, -0.0, 1.0, 1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, -(1.0 + 2 ** -8)]])
+    want = torch.from_numpy(v).to(torch.float32).to(torch.bfloat16).to(torch.float64).numpy()
+    np.testing.assert_array_equal(ref.round_bf16(v), want)
+
+
+def test_bf16_operand_emulation_consistent():
+    x, w1, w3, w2, dy, fw = _setup(4, T=13, h=6, hf=5, E=3, k=2)
+    exact = ref.layer_backward(dy, x, fw["w"], fw["dst_row"], fw["offsets"], w1, w3, w2)
+    emu = ref.layer_backward(dy, x, fw["w"], fw["dst_row"], fw["offsets"], w1, w3, w2, bf16_operands=True)
+    dx = ref.layer_backward_tokens(dy, x, fw["idx"], fw["w"], w1, w3, w2, bf16_operands=True)
+    np.testing.assert_allclose(dx, emu["dx"], rtol=1e-12, atol=1e-13)
+    for k in ("dx", "dw1", "dw3", "dw2"):
+        rel = np.abs(emu[k] - exact[k]).max() / np.abs(exact[k]).max()
+        assert 0 < rel < 2e-2, k            # rounding happened, and is small
+
+
 def test_backward_matches_torch_autograd():
     x, w1, w3, w2, dy, fw = _setup(5, T=9, h=6, hf=7, E=4, k=3)
     bw = ref.layer_backward(dy, x, fw["w"], fw["dst_row"], fw["offsets"], w1, w3, w2)
