@@ -30,6 +30,30 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def gemm_source_sha() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in ("gemm_engine.h", "gemm_fwd.hip"):
+        with open(os.path.join(ROOT, "mixture_experts_layer_24_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def profiled_traffic(workload: str, kernel: str):
+    """HBM bytes per launch of `kernel` from the committed counter profile
+    (scaled FETCH_SIZE + WRITE_SIZE), or None when there is none or the GEMM
+    sources changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}_fwd.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        t = json.load(fh)
+    k = t.get("kernels", {}).get(kernel)
+    if k is None or t.get("source_sha") != gemm_source_sha():
+        return None
+    return (k["read_bytes"] + k["write_bytes"]) / 1e9
+
+
 def cpu_baseline(wl, inp, n_tokens, seed=0):
     """Time the CPU oracle on the first n_tokens tokens of the same batch."""
     import numpy as np
@@ -72,7 +96,20 @@ def main():
     ap.add_argument("--workload", default="mixtral")
     ap.add_argument("--cpu-tokens", type=int, default=2048,
                     help="tokens in the CPU oracle sample (0 = skip)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device copy of BYTES (3 times), to calibrate the "
+                         "FETCH_SIZE / WRITE_SIZE counters against a known byte count")
     args = ap.parse_args()
+    if args.copy_calibration:
+        import torch
+        n = args.copy_calibration
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": n, "launches": 3}))
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE={world}); "
@@ -149,6 +186,8 @@ def main():
         achieved = bytes_per_launch.get(dom, 0) / (avg[dom] * 1e-3)
         roof = {"kernel": dom, "bound": "hbm", "achieved": achieved / 1e9, "peak": HBM_PEAK / 1e9,
                 "unit": "GB/s", "frac": achieved / HBM_PEAK, "traffic": None}
+    roof["traffic"] = profiled_traffic(wl.name, dom)
+    roof["traffic_unit"] = "GB per launch (HBM bytes, rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)"
     hbm = {}
     for k2, b in bytes_per_launch.items():
         if k2 in avg:
