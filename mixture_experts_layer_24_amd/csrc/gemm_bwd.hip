@@ -135,7 +135,6 @@ int grouped_bwd(const void* dyp, const void* xp, const void* h13_save, const moe
   w += al256(size_t(hf) * kp * 2);
   void* dguT = w;
   int rc;
-  const long mt_upper = (long(rows) + kBM - 1) / kBM + E;
 
   timer_begin(kTXpose, s);
   if ((rc = xpose(xp, h, offsets, E, rows, xpT, s))) return rc;
@@ -145,8 +144,7 @@ int grouped_bwd(const void* dyp, const void* xp, const void* h13_save, const moe
   // dA = dYp W2^T, with dG, dU and A formed in the epilogue
   GemmArgs ga{dyp, nullptr, W->w2_bwd, nullptr, offsets, E, h, hf, rows, 0,
               dgu, act, const_cast<void*>(h13_save), nullptr};
-  if ((rc = launch_gemm<MOE_BF16, kModeBwdDA, kSchedM>(ga, mt_upper * ((hf + kBN - 1) / kBN),
-                                                       kTBwd1, s)))
+  if ((rc = launch_gemm<CfgBwd, MOE_BF16, kModeBwdDA, kSchedM>(ga, kTBwd1, s)))
     return rc;
 
   timer_begin(kTXpose, s);
@@ -157,22 +155,19 @@ int grouped_bwd(const void* dyp, const void* xp, const void* h13_save, const moe
   // dW2 = A^T dYp  (per expert [hf][h], fp32)
   GemmArgs g2{actT, nullptr, dypT, nullptr, offsets, E, 0, h, rows, hf,
               dw2, nullptr, nullptr, nullptr};
-  if ((rc = launch_gemm<MOE_BF16, kModeDW, kSchedK>(
-           g2, long(E) * ((hf + kBM - 1) / kBM) * ((h + kBN - 1) / kBN), kTBwd2, s)))
+  if ((rc = launch_gemm<CfgBwd, MOE_BF16, kModeDW, kSchedK>(g2, kTBwd2, s)))
     return rc;
 
   // dXp = [dG|dU] W13^T
   GemmArgs g3{dgu, nullptr, W->w13_bwd, nullptr, offsets, E, 2 * hf, h, rows, 0,
               dxp, nullptr, nullptr, nullptr};
-  if ((rc = launch_gemm<MOE_BF16, kModeFC2, kSchedM>(g3, mt_upper * ((h + kBN - 1) / kBN), kTBwd3,
-                                                     s)))
+  if ((rc = launch_gemm<CfgBwd, MOE_BF16, kModeFC2, kSchedM>(g3, kTBwd3, s)))
     return rc;
 
   // dW1 | dW3 = Xp^T [dG|dU]  (per expert [h][hf] each, fp32)
   GemmArgs g4{xpT, nullptr, dguT, nullptr, offsets, E, 0, 2 * hf, rows, h,
               dw1, dw3, nullptr, nullptr};
-  return launch_gemm<MOE_BF16, kModeDW13, kSchedK>(
-      g4, long(E) * ((h + kBM - 1) / kBM) * ((2 * hf + kBN - 1) / kBN), kTBwd4, s);
+  return launch_gemm<CfgBwd, MOE_BF16, kModeDW13, kSchedK>(g4, kTBwd4, s);
 }
 
 }  // namespace moe_launch

@@ -15,10 +15,36 @@
 
 namespace moe {
 
-constexpr int kBM = 256, kBN = 256, kRowB = 128;  // tile rows, cols, bytes of K per LDS row
-constexpr int kStageB = kBM * kRowB;              // bytes of one operand stage (32 KB)
-constexpr int kGemmLds = 4 * kStageB;             // A and B, two stages each (128 KB)
-constexpr int kKPad = 64;                         // SchedK: per-expert K padded to this
+constexpr int kRowB = 128;  // bytes of K per LDS row (one K slab)
+constexpr int kKPad = 64;   // SchedK: per-expert K padded to this
+
+// Tile shape: WM x WN waves, each owning MI x NJ MFMA blocks of 32 x 32, and
+// OCC workgroups resident per CU.  The tile is (32 WM MI) x (32 WN NJ); LDS
+// holds two stages, each a K slab of the tile's A rows followed by its B rows.
+template <int WM, int WN, int MI, int NJ, int OCC>
+struct GemmCfg {
+  static constexpr int kWM = WM, kWN = WN, kMI = MI, kNJ = NJ, kOcc = OCC;
+  static constexpr int kNW = WM * WN;             // waves per workgroup
+  static constexpr int kThreads = 64 * kNW;
+  static constexpr int kWavesPerSimd = kNW * OCC / 4;
+  static constexpr int kBM = 32 * WM * MI, kBN = 32 * WN * NJ;
+  static constexpr int kAStage = kBM * kRowB;     // A part of a stage
+  static constexpr int kStage = (kBM + kBN) * kRowB;
+  static constexpr int kLds = 2 * kStage;
+  static constexpr int kGA = kBM / 8 / kNW, kGB = kBN / 8 / kNW;  // 8-row load groups per wave
+  static_assert(kGA * 8 * kNW == kBM && kGB * 8 * kNW == kBN, "rows must split over waves");
+  static_assert(kNW % 4 == 0, "whole waves per SIMD");
+};
+
+// 256 x 256, four waves of 128 x 128 (256 accumulators per lane), one per SIMD.
+using CfgWide = GemmCfg<2, 2, 4, 4, 1>;
+// 256 x 256, eight waves of 128 x 64: two waves per SIMD, so one can issue
+// MFMAs while the other waits on a load.
+using CfgDual = GemmCfg<2, 4, 4, 2, 1>;
+
+// the configuration each pass runs with
+using CfgFwd = CfgDual;
+using CfgBwd = CfgDual;
 
 enum { kSchedM = 0, kSchedK = 1 };
 enum {
@@ -122,51 +148,61 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, size_t 
 
 typedef __attribute__((address_space(3))) void lds_ptr_t;
 
-// Loader offsets for row pitch rowB (see issue_slab).
+// Loader offsets of one lane for row pitch rowB.  An 8-row group lands in
+// 1 KB of LDS with lane l at byte 16*l (row l/8 of the group, position l%8),
+// so the lane fetches the chunk that the XOR swizzle keeps at that position;
+// the swizzle of row 8q + l/8 is 4*(q%2) + l/16, hence even and odd groups.
 struct LoadOff {
   int e, o;
 };
-__device__ __forceinline__ LoadOff load_off(int rowB, int wave, int lane) {
-  const int lrow = wave * 64 + (lane >> 3);
-  const int sw = (lrow >> 1) & 7;
-  return LoadOff{lrow * rowB + (((lane & 7) ^ sw) << 4), lrow * rowB + (((lane & 7) ^ sw ^ 4) << 4)};
+__device__ __forceinline__ LoadOff load_off(int rowB, int lane) {
+  const int r = lane >> 3, c = (lane & 7) ^ (r >> 1);
+  return LoadOff{r * rowB + (c << 4), r * rowB + ((c ^ 4) << 4)};
 }
 
 // One K slab (128 bytes per row) of A and B straight from memory into LDS
-// stage `st`.  Wave w fills row groups 8w..8w+7 of each operand; within an
-// 8-row group lane l lands at LDS byte 16*l (row l/8, position l%8), so it
-// fetches the chunk that the XOR swizzle keeps at that position.
+// stage `st`: wave w fills 8-row groups w*GA .. w*GA+GA-1 of A and
+// w*GB .. w*GB+GB-1 of B.
+template <class C>
 __device__ __forceinline__ void issue_slab(unsigned char* lds, int st, __amdgpu_buffer_rsrc_t ra,
                                            __amdgpu_buffer_rsrc_t rb, int wave, LoadOff lo,
                                            int rowB, int koff) {
-  unsigned char* A = lds + st * (2 * kStageB) + wave * 8 * 1024;
-  unsigned char* B = A + kStageB;
+  unsigned char* A = lds + st * C::kStage + wave * C::kGA * 1024;
+  unsigned char* B = lds + st * C::kStage + C::kAStage + wave * C::kGB * 1024;
+  const int ga0 = wave * C::kGA, gb0 = wave * C::kGB;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int v = ((i & 1) ? lo.o : lo.e) + i * 8 * rowB + koff;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t*)(A + i * 1024), 16, v, 0, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr_t*)(B + i * 1024), 16, v, 0, 0, 0);
+  for (int i = 0; i < (C::kGA > C::kGB ? C::kGA : C::kGB); ++i) {
+    if (i < C::kGA) {
+      const int q = ga0 + i;
+      const int v = ((q & 1) ? lo.o : lo.e) + q * 8 * rowB + koff;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t*)(A + i * 1024), 16, v, 0, 0, 0);
+    }
+    if (i < C::kGB) {
+      const int q = gb0 + i;
+      const int v = ((q & 1) ? lo.o : lo.e) + q * 8 * rowB + koff;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr_t*)(B + i * 1024), 16, v, 0, 0, 0);
+    }
   }
 }
 
-// Fragments of substep s of one LDS stage (4 A and 4 B fragments per wave).
-template <int DT>
-__device__ __forceinline__ void load_frags(Frag<DT> (&fa)[4], Frag<DT> (&fb)[4],
+// Fragments of substep s of one LDS stage (MI A and NJ B fragments per wave).
+template <class C, int DT>
+__device__ __forceinline__ void load_frags(Frag<DT> (&fa)[C::kMI], Frag<DT> (&fb)[C::kNJ],
                                            const unsigned char* As, int arow, int brow, int s,
                                            int half) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) fa[i].load(As, arow + i * 32, s, half);
+  for (int i = 0; i < C::kMI; ++i) fa[i].load(As, arow + i * 32, s, half);
 #pragma unroll
-  for (int j = 0; j < 4; ++j) fb[j].load(As + kStageB, brow + j * 32, s, half);
+  for (int j = 0; j < C::kNJ; ++j) fb[j].load(As + C::kAStage, brow + j * 32, s, half);
 }
 
-template <int DT>
-__device__ __forceinline__ void mma_all(f32x16 (&acc)[4][4], const Frag<DT> (&fa)[4],
-                                        const Frag<DT> (&fb)[4]) {
+template <class C, int DT>
+__device__ __forceinline__ void mma_all(f32x16 (&acc)[C::kMI][C::kNJ], const Frag<DT> (&fa)[C::kMI],
+                                        const Frag<DT> (&fb)[C::kNJ]) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < C::kMI; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) Frag<DT>::mma(acc[i][j], fa[i], fb[j]);
+    for (int j = 0; j < C::kNJ; ++j) Frag<DT>::mma(acc[i][j], fa[i], fb[j]);
 }
 
 // Row of accumulator register r of MFMA block i (relative to the wave's rows).
@@ -174,24 +210,24 @@ __device__ __forceinline__ int acc_row(int i, int r, int half) {
   return i * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
 }
 
-template <int DT, int MODE>
-__device__ __forceinline__ void epilogue(const GemmArgs& g, f32x16 (&acc)[4][4], const Tile& T,
-                                         int wm, int wn, int half, int l32,
-                                         unsigned char* free_lds) {
+template <class C, int DT, int MODE>
+__device__ __forceinline__ void epilogue(const GemmArgs& g, f32x16 (&acc)[C::kMI][C::kNJ],
+                                         const Tile& T, int wave, int wm, int wn, int half,
+                                         int l32, unsigned char* free_lds) {
+  constexpr int MI = C::kMI, NJ = C::kNJ;
   const int e = T.e, row0 = T.row0, row_end = T.row_end, n0 = T.n0;
-  if (MODE == kModeFC1 || MODE == kModeFC2) {
-
-  const int rbase = row0 + wm * 128;
+  const int rbase = row0 + wm * (MI * 32);   // the wave's first row
+  const int cbase = n0 + wn * (NJ * 32);     // the wave's first column
   if (MODE == kModeFC1) {
+    static_assert(MODE != kModeFC1 || NJ % 2 == 0, "FC1 pairs gate and up blocks");
     const int hf = g.N / 2;
-    const int chb = (n0 + wn * 128) / 2;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < MI; ++i) {
       float rmax[16];
 #pragma unroll
-      for (int p = 0; p < 2; ++p) {
-        const int ch = chb + p * 32 + l32;
-        const int colg = n0 + wn * 128 + (2 * p) * 32 + l32;  // packed column of G
+      for (int p = 0; p < NJ / 2; ++p) {
+        const int ch = cbase / 2 + p * 32 + l32;
+        const int colg = cbase + (2 * p) * 32 + l32;  // packed column of G
         float sg = 1.f, su = 1.f;
         if (DT == MOE_FP8_E4M3) {
           sg = g.b_scale[size_t(e) * g.N + colg];
@@ -199,7 +235,7 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, f32x16 (&acc)[4][4],
         }
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int row = rbase + i * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+          const int row = rbase + acc_row(i, r, half);
           float G = acc[i][2 * p][r], U = acc[i][2 * p + 1][r];
           if (DT == MOE_FP8_E4M3) {
             const float xs = row < row_end ? g.a_scale[row] : 0.f;
@@ -226,29 +262,29 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, f32x16 (&acc)[4][4],
         }
       }
       if (DT == MOE_FP8_E4M3) {
-        // row max over this wave's 64 channels: reduce over the 32 lanes of a half
+        // row max over this wave's channels: reduce over the 32 lanes of a half
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           float m = rmax[r];
 #pragma unroll
           for (int o = 16; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
-          const int row = rbase + i * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+          const int row = rbase + acc_row(i, r, half);
           if (l32 == 0 && row < row_end) atomicMax(g.row_amax + row, __float_as_uint(m));
         }
       }
     }
-  } else {
+  } else if (MODE == kModeFC2) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < MI; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int col = n0 + wn * 128 + j * 32 + l32;
+      for (int j = 0; j < NJ; ++j) {
+        const int col = cbase + j * 32 + l32;
         if (col >= g.N) continue;
         float cs = 1.f;
         if (DT == MOE_FP8_E4M3) cs = g.b_scale[size_t(e) * g.N + col];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int row = rbase + i * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+          const int row = rbase + acc_row(i, r, half);
           if (row < row_end) {
             float y = acc[i][j][r];
             if (DT == MOE_FP8_E4M3) y *= g.a_scale[row] * cs;
@@ -259,53 +295,61 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, f32x16 (&acc)[4][4],
           }
         }
       }
-  }
-
   } else if (MODE == kModeBwdDA) {
-    // dA tile -> dG, dU (packed like the forward's G|U) and A = SiLU(G)*U
-    // The kept G|U of this wave's 128 rows x 32 channels (64 packed columns,
-    // 128 B per row) go global -> LDS (the stage that is idle during the
-    // epilogue) in 16 direct loads, then come out of LDS as needed.
+    // dA tile -> dG, dU (packed like the forward's G|U) and A = SiLU(G)*U.
+    // For each 32-channel block j, the kept G|U of the wave's rows (64 packed
+    // columns, 128 B per row) go global -> LDS (the stage that is idle during
+    // the epilogue, split evenly over the waves) in direct loads, a chunk of
+    // rows at a time, then come out of LDS as needed.
+    constexpr int kRegion = C::kStage / C::kNW;              // bytes of LDS per wave
+    constexpr int kRows = kRegion / 128 < MI * 32 ? kRegion / 128 : MI * 32;
+    constexpr int kIPer = kRows / 32;                        // MFMA blocks per chunk
+    static_assert(kIPer >= 1 && MI % kIPer == 0, "chunk of whole MFMA blocks");
     const int hf = g.N;
     uint16_t* __restrict__ dgu = static_cast<uint16_t*>(g.out);
     uint16_t* __restrict__ aout = static_cast<uint16_t*>(g.out2);
-    const int wrow0 = row0 + wm * 128;
     const size_t rowb = size_t(2 * hf) * 2;  // bytes per G|U row
-    const __amdgpu_buffer_rsrc_t gsrc =
-        rsrc(g.save, size_t(wrow0) * rowb, size_t(g.rows > wrow0 ? g.rows - wrow0 : 0) * rowb);
-    unsigned char* wl = free_lds + (wm * 2 + wn) * 16384;
+    unsigned char* wl = free_lds + wave * kRegion;
     const uint16_t* wl16 = reinterpret_cast<const uint16_t*>(wl);
     const int lane = half * 32 + l32;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {                // unrolled: acc stays in registers
-      const int fb0 = n0 + wn * 128 + j * 32;      // first channel of the group
+    for (int j = 0; j < NJ; ++j) {                 // unrolled: acc stays in registers
+      const int fb0 = cbase + j * 32;              // first channel of the group
       const int pb = (fb0 >> 5) * 64;              // its first packed column
-      __builtin_amdgcn_s_waitcnt(0);              // earlier reads of this region done
-#pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        const int v = (q * 8 + (lane >> 3)) * int(rowb) + pb * 2 + (lane & 7) * 16;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(gsrc, (lds_ptr_t*)(wl + q * 1024), 16, v, 0, 0, 0);
-      }
-      __builtin_amdgcn_s_waitcnt(0);
       const int f = fb0 + l32;
-      if (f >= hf) continue;
       const int pg = pb + l32, pu = pg + 32;
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int ic = 0; ic < MI / kIPer; ++ic) {
+        const int crow0 = rbase + ic * kRows;
+        const __amdgpu_buffer_rsrc_t gsrc = rsrc(
+            g.save, size_t(crow0) * rowb, size_t(g.rows > crow0 ? g.rows - crow0 : 0) * rowb);
+        __builtin_amdgcn_s_waitcnt(0);             // earlier reads of this region done
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int rl = acc_row(i, r, half);
-          const int row = wrow0 + rl;
-          if (row >= row_end) continue;
-          const float G = bf16_to_f32(wl16[rl * 64 + l32]), U = bf16_to_f32(wl16[rl * 64 + 32 + l32]);
-          const float sg = 1.0f / (1.0f + __expf(-G));
-          const float si = G * sg;
-          const float dA = acc[i][j][r];
-          const size_t b = size_t(row) * (2 * hf);
-          dgu[b + pg] = uint16_t(f32_to_bf16_bits(dA * U * sg * (1.0f + G * (1.0f - sg))));
-          dgu[b + pu] = uint16_t(f32_to_bf16_bits(dA * si));
-          aout[size_t(row) * hf + f] = uint16_t(f32_to_bf16_bits(si * U));
+        for (int q = 0; q < kRows / 8; ++q) {
+          const int v = (q * 8 + (lane >> 3)) * int(rowb) + pb * 2 + (lane & 7) * 16;
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(gsrc, (lds_ptr_t*)(wl + q * 1024), 16, v, 0, 0, 0);
         }
+        __builtin_amdgcn_s_waitcnt(0);
+        if (f >= hf) continue;
+#pragma unroll
+        for (int ii = 0; ii < kIPer; ++ii) {
+          const int i = ic * kIPer + ii;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int rl = acc_row(ii, r, half);   // row inside the chunk
+            const int row = crow0 + rl;
+            if (row >= row_end) continue;
+            const float G = bf16_to_f32(wl16[rl * 64 + l32]), U = bf16_to_f32(wl16[rl * 64 + 32 + l32]);
+            const float sg = 1.0f / (1.0f + __expf(-G));
+            const float si = G * sg;
+            const float dA = acc[i][j][r];
+            const size_t b = size_t(row) * (2 * hf);
+            dgu[b + pg] = uint16_t(f32_to_bf16_bits(dA * U * sg * (1.0f + G * (1.0f - sg))));
+            dgu[b + pu] = uint16_t(f32_to_bf16_bits(dA * si));
+            aout[size_t(row) * hf + f] = uint16_t(f32_to_bf16_bits(si * U));
+          }
+        }
+      }
     }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();  // the idle stage is refilled by the next tile's loads
@@ -314,8 +358,8 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, f32x16 (&acc)[4][4],
     float* o1 = static_cast<float*>(g.out);
     float* o2 = static_cast<float*>(g.out2);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int n = n0 + wn * 128 + j * 32 + l32;
+    for (int j = 0; j < NJ; ++j) {
+      const int n = cbase + j * 32 + l32;
       if (n >= g.N) continue;
       float* dst = o1;
       int col = n, ld = g.N;
@@ -326,30 +370,31 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, f32x16 (&acc)[4][4],
       }
       dst += size_t(e) * g.M * ld;
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < MI; ++i)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int m = row0 + wm * 128 + acc_row(i, r, half);
+          const int m = rbase + acc_row(i, r, half);
           if (m < row_end) dst[size_t(m) * ld + col] = acc[i][j][r];
         }
     }
   }
 }
 
-template <int DT, int MODE, int SCHED>
-__global__ void __launch_bounds__(256, 1) grouped_gemm_kernel(GemmArgs g) {
+template <class C, int DT, int MODE, int SCHED>
+__global__ void __launch_bounds__(C::kThreads, C::kWavesPerSimd) grouped_gemm_kernel(GemmArgs g) {
+  constexpr int BM = C::kBM, BN = C::kBN, MI = C::kMI, NJ = C::kNJ;
   extern __shared__ __align__(16) unsigned char lds[];
   __shared__ int tpre[MOE_MAX_EXPERTS + 1];  // tiles before expert e
   __shared__ int offs[MOE_MAX_EXPERTS + 1];  // SchedM: row offsets; SchedK: padded K prefix
   constexpr int EB = Elem<DT>::bytes;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / C::kWN, wn = wave % C::kWN;
   const int half = lane >> 5, l32 = lane & 31;
-  const int NT = ceil_div(g.N, kBN);
-  const int MT = SCHED == kSchedK ? ceil_div(g.M, kBM) : 0;
+  const int NT = ceil_div(g.N, BN);
+  const int MT = SCHED == kSchedK ? ceil_div(g.M, BM) : 0;
 
-  for (int e = tid; e <= g.E; e += 256) {
+  for (int e = tid; e <= g.E; e += C::kThreads) {
     int o = g.offsets[e];
     offs[e] = o < 0 ? 0 : (o > g.rows ? g.rows : o);  // never address past `rows`
   }
@@ -362,7 +407,7 @@ __global__ void __launch_bounds__(256, 1) grouped_gemm_kernel(GemmArgs g) {
       prev = hi;
       if (SCHED == kSchedM) {
         offs[e + 1] = hi;
-        run += ceil_div(hi - lo, kBM) * NT;
+        run += ceil_div(hi - lo, BM) * NT;
       } else {
         offs[e] = kp;  // becomes the padded K prefix
         kp += ceil_div(hi - lo, kKPad) * kKPad;
@@ -376,7 +421,7 @@ __global__ void __launch_bounds__(256, 1) grouped_gemm_kernel(GemmArgs g) {
   const int total = tpre[g.E];
   const int G = gridDim.x;
   const int b = blockIdx.x;
-  // the 32 workgroups of one XCD (b % 8) take consecutive tiles
+  // the workgroups of one XCD (b % 8) take consecutive tiles
   int t = (G % 8 == 0) ? (b % 8) * (G / 8) + b / 8 : b;
   if (t >= total) return;
 
@@ -391,11 +436,11 @@ __global__ void __launch_bounds__(256, 1) grouped_gemm_kernel(GemmArgs g) {
     const int local = tt - tpre[lo];
     if (SCHED == kSchedM) {
       // experts in order, m-tiles fastest: consecutive tiles share a weight block
-      const int mt_e = ceil_div(offs[lo + 1] - offs[lo], kBM);
+      const int mt_e = ceil_div(offs[lo + 1] - offs[lo], BM);
       const int nt = local / mt_e, mt = local - nt * mt_e;
-      T.row0 = offs[lo] + mt * kBM;
+      T.row0 = offs[lo] + mt * BM;
       T.row_end = offs[lo + 1];
-      T.n0 = nt * kBN;
+      T.n0 = nt * BN;
       T.rowB = g.K * EB;
       T.a_off = size_t(T.row0) * T.rowB;
       T.a_bytes = size_t(g.rows - T.row0) * T.rowB;
@@ -403,9 +448,9 @@ __global__ void __launch_bounds__(256, 1) grouped_gemm_kernel(GemmArgs g) {
     } else {
       const int nt = local / MT, mt = local - nt * MT;
       const int k0 = offs[lo], ke = offs[lo + 1] - k0;
-      T.row0 = mt * kBM;
+      T.row0 = mt * BM;
       T.row_end = g.M;
-      T.n0 = nt * kBN;
+      T.n0 = nt * BN;
       T.rowB = ke * EB;
       T.a_off = size_t(k0) * g.M * EB + size_t(T.row0) * T.rowB;
       T.a_bytes = size_t(g.M - T.row0) * T.rowB;
@@ -416,21 +461,22 @@ __global__ void __launch_bounds__(256, 1) grouped_gemm_kernel(GemmArgs g) {
     return T;
   };
 
-  constexpr int S = Frag<DT>::kSub;             // substeps per slab (even)
-  constexpr int NR = 8 * Frag<DT>::kReads;      // LDS reads per substep
-  constexpr int NM = 16 * Frag<DT>::kMfma;      // MFMAs per substep
+  constexpr int S = Frag<DT>::kSub;                     // substeps per slab (even)
+  constexpr int NR = (MI + NJ) * Frag<DT>::kReads;      // LDS reads per substep
+  constexpr int NM = MI * NJ * Frag<DT>::kMfma;         // MFMAs per substep
+  constexpr int NV = C::kGA + C::kGB;                   // global loads per slab
   // fragment rows inside a stage
-  const int arow = wm * 128 + l32, brow = wn * 128 + l32;
+  const int arow = wm * (MI * 32) + l32, brow = wn * (NJ * 32) + l32;
 
   Tile cur = tile_of(t);
   __amdgpu_buffer_rsrc_t ra = rsrc(g.A, cur.a_off, cur.a_bytes), rb = rsrc(g.B, cur.b_off, cur.b_bytes);
-  LoadOff lo = load_off(cur.rowB, wave, lane);
+  LoadOff lo = load_off(cur.rowB, lane);
   int st = 0;
-  issue_slab(lds, st, ra, rb, wave, lo, cur.rowB, 0);
+  issue_slab<C>(lds, st, ra, rb, wave, lo, cur.rowB, 0);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  Frag<DT> fa[2][4], fb[2][4];
-  load_frags<DT>(fa[0], fb[0], lds, arow, brow, 0, half);
+  Frag<DT> fa[2][MI], fb[2][NJ];
+  load_frags<C, DT>(fa[0], fb[0], lds, arow, brow, 0, half);
 
   while (true) {
     const int tn = t + G;
@@ -438,13 +484,13 @@ __global__ void __launch_bounds__(256, 1) grouped_gemm_kernel(GemmArgs g) {
     const Tile nxt = has_next ? tile_of(tn) : cur;
     const __amdgpu_buffer_rsrc_t ra_n = rsrc(g.A, nxt.a_off, nxt.a_bytes);
     const __amdgpu_buffer_rsrc_t rb_n = rsrc(g.B, nxt.b_off, nxt.b_bytes);
-    const LoadOff lo_n = load_off(nxt.rowB, wave, lane);
+    const LoadOff lo_n = load_off(nxt.rowB, lane);
 
-    f32x16 acc[4][4];
+    f32x16 acc[MI][NJ];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < MI; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < NJ; ++j)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
@@ -452,13 +498,13 @@ __global__ void __launch_bounds__(256, 1) grouped_gemm_kernel(GemmArgs g) {
       // Stage st holds slab kt and fa[0]/fb[0] its first fragments.  Load
       // slab kt+1 (or the next tile's first) into the other stage.
       const bool last = kt + 1 == cur.nk;
-      issue_slab(lds, st ^ 1, last ? ra_n : ra, last ? rb_n : rb, wave, last ? lo_n : lo,
-                 last ? nxt.rowB : cur.rowB, last ? 0 : (kt + 1) * kRowB);
-      const unsigned char* As = lds + st * (2 * kStageB);
+      issue_slab<C>(lds, st ^ 1, last ? ra_n : ra, last ? rb_n : rb, wave, last ? lo_n : lo,
+                    last ? nxt.rowB : cur.rowB, last ? 0 : (kt + 1) * kRowB);
+      const unsigned char* As = lds + st * C::kStage;
 #pragma unroll
       for (int s = 0; s + 1 < S; ++s) {
-        load_frags<DT>(fa[(s + 1) & 1], fb[(s + 1) & 1], As, arow, brow, s + 1, half);
-        mma_all<DT>(acc, fa[s & 1], fb[s & 1]);
+        load_frags<C, DT>(fa[(s + 1) & 1], fb[(s + 1) & 1], As, arow, brow, s + 1, half);
+        mma_all<C, DT>(acc, fa[s & 1], fb[s & 1]);
       }
       // interleave: one LDS read (and one global load early on) per MFMA
 #pragma unroll
@@ -467,13 +513,13 @@ __global__ void __launch_bounds__(256, 1) grouped_gemm_kernel(GemmArgs g) {
         for (int q = 0; q < NM; ++q) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
           if (q < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-          if (s == 0 && q < 16) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+          if (s == 0 && q < NV) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
         }
       __builtin_amdgcn_s_waitcnt(0);  // stage st read out; slab kt+1 landed
       __syncthreads();
       // next slab's first fragments load while the last substep multiplies
-      load_frags<DT>(fa[0], fb[0], lds + (st ^ 1) * (2 * kStageB), arow, brow, 0, half);
-      mma_all<DT>(acc, fa[1], fb[1]);
+      load_frags<C, DT>(fa[0], fb[0], lds + (st ^ 1) * C::kStage, arow, brow, 0, half);
+      mma_all<C, DT>(acc, fa[1], fb[1]);
       __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);
       __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);
       st ^= 1;
@@ -482,13 +528,13 @@ __global__ void __launch_bounds__(256, 1) grouped_gemm_kernel(GemmArgs g) {
       // an empty-K tile prefetched nothing: bring in the next tile's first slab
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
-      issue_slab(lds, st, ra_n, rb_n, wave, lo_n, nxt.rowB, 0);
+      issue_slab<C>(lds, st, ra_n, rb_n, wave, lo_n, nxt.rowB, 0);
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
-      load_frags<DT>(fa[0], fb[0], lds + st * (2 * kStageB), arow, brow, 0, half);
+      load_frags<C, DT>(fa[0], fb[0], lds + st * C::kStage, arow, brow, 0, half);
     }
 
-    epilogue<DT, MODE>(g, acc, cur, wm, wn, half, l32, lds + (st ^ 1) * (2 * kStageB));
+    epilogue<C, DT, MODE>(g, acc, cur, wave, wm, wn, half, l32, lds + (st ^ 1) * C::kStage);
     if (!has_next) break;
     t = tn;
     cur = nxt;
@@ -502,17 +548,23 @@ __global__ void __launch_bounds__(256, 1) grouped_gemm_kernel(GemmArgs g) {
 
 namespace moe_launch {
 
-// Persistent launch: one workgroup per CU (or fewer if there are fewer tiles).
-template <int DT, int MODE, int SCHED>
-inline int launch_gemm(const moe::GemmArgs& a, long tiles_upper, int timer, hipStream_t s) {
+// Persistent launch: OCC workgroups per CU (fewer if there are fewer tiles).
+// The tile count bound needs no device data: SchedM has at most
+// ceil(rows/BM) + E row tiles, SchedK exactly E ceil(M/BM).
+template <class C, int DT, int MODE, int SCHED>
+inline int launch_gemm(const moe::GemmArgs& a, int timer, hipStream_t s) {
   using namespace moe;
-  static bool attr = allow_lds(grouped_gemm_kernel<DT, MODE, SCHED>, kGemmLds);
+  static bool attr = allow_lds(grouped_gemm_kernel<C, DT, MODE, SCHED>, C::kLds);
   if (!attr) return MOE_ERR_HIP;
-  int grid = num_cus();
-  if (tiles_upper < grid) grid = int(tiles_upper);
+  const long mt = SCHED == kSchedM ? (long(a.rows) + C::kBM - 1) / C::kBM + a.E
+                                   : long(a.E) * ((a.M + C::kBM - 1) / C::kBM);
+  const long tiles = mt * ((a.N + C::kBN - 1) / C::kBN);
+  long grid = long(num_cus()) * C::kOcc;
+  if (tiles < grid) grid = tiles;
   if (grid < 1) grid = 1;
   timer_begin(timer, s);
-  hipLaunchKernelGGL((grouped_gemm_kernel<DT, MODE, SCHED>), dim3(grid), dim3(256), kGemmLds, s, a);
+  hipLaunchKernelGGL((grouped_gemm_kernel<C, DT, MODE, SCHED>), dim3(unsigned(grid)),
+                     dim3(C::kThreads), C::kLds, s, a);
   timer_end(timer, s);
   return launch_status();
 }

@@ -77,12 +77,8 @@ size_t grouped_fwd_ws_bytes(int rows, int h, int h_ffn, int E, int dtype) {
 
 template <int DT, int MODE>
 static int launch_fwd_gemm(const GemmArgs& a, hipStream_t s) {
-  // upper bound of the tile count, known without reading offsets
-  long mt_max = (long(a.rows) + kBM - 1) / kBM + a.E;
-  long tiles = mt_max * ((a.N + kBN - 1) / kBN);
-  return launch_gemm<DT, MODE, kSchedM>(a, tiles, MODE == kModeFC1 ? kTFc1 : kTFc2, s);
+  return launch_gemm<CfgFwd, DT, MODE, kSchedM>(a, MODE == kModeFC1 ? kTFc1 : kTFc2, s);
 }
-
 
 template <int DT>
 static int fwd_typed(const void* xp, const float* xp_scale, const moe_weights* W,
