@@ -106,7 +106,8 @@ size_t grouped_bwd_ws_bytes(int rows, int h, int h_ffn, int E, int dtype) {
          + al256(r * hf * 2)            // A recomputed
          + 2 * al256(hh * kp * 2)       // Xp^T, dYp^T
          + al256(hf * kp * 2)           // A^T
-         + al256(2 * hf * kp * 2);      // (dG|dU)^T
+         + al256(2 * hf * kp * 2)       // (dG|dU)^T
+         + splitk_ws_bytes<CfgBwd>();   // split-K partial tiles
 }
 
 static int xpose(const void* src, int C, const int32_t* offsets, int E, int rows, void* dst,
@@ -134,6 +135,8 @@ int grouped_bwd(const void* dyp, const void* xp, const void* h13_save, const moe
   void* actT = w;
   w += al256(size_t(hf) * kp * 2);
   void* dguT = w;
+  w += al256(2 * size_t(hf) * kp * 2);
+  void* split_ws = w;
   int rc;
 
   timer_begin(kTXpose, s);
@@ -143,7 +146,8 @@ int grouped_bwd(const void* dyp, const void* xp, const void* h13_save, const moe
 
   // dA = dYp W2^T, with dG, dU and A formed in the epilogue
   GemmArgs ga{dyp, nullptr, W->w2_bwd, nullptr, offsets, E, h, hf, rows, 0,
-              dgu, act, const_cast<void*>(h13_save), nullptr};
+              dgu, act, const_cast<void*>(h13_save), nullptr, nullptr, nullptr};
+  splitk_ws_set<CfgBwd>(ga, split_ws);
   if ((rc = launch_gemm<CfgBwd, MOE_BF16, kModeBwdDA, kSchedM>(ga, kTBwd1, s)))
     return rc;
 
@@ -154,19 +158,22 @@ int grouped_bwd(const void* dyp, const void* xp, const void* h13_save, const moe
 
   // dW2 = A^T dYp  (per expert [hf][h], fp32)
   GemmArgs g2{actT, nullptr, dypT, nullptr, offsets, E, 0, h, rows, hf,
-              dw2, nullptr, nullptr, nullptr};
+              dw2, nullptr, nullptr, nullptr, nullptr, nullptr};
+  splitk_ws_set<CfgBwd>(g2, split_ws);
   if ((rc = launch_gemm<CfgBwd, MOE_BF16, kModeDW, kSchedK>(g2, kTBwd2, s)))
     return rc;
 
   // dXp = [dG|dU] W13^T
   GemmArgs g3{dgu, nullptr, W->w13_bwd, nullptr, offsets, E, 2 * hf, h, rows, 0,
-              dxp, nullptr, nullptr, nullptr};
+              dxp, nullptr, nullptr, nullptr, nullptr, nullptr};
+  splitk_ws_set<CfgBwd>(g3, split_ws);
   if ((rc = launch_gemm<CfgBwd, MOE_BF16, kModeFC2, kSchedM>(g3, kTBwd3, s)))
     return rc;
 
   // dW1 | dW3 = Xp^T [dG|dU]  (per expert [h][hf] each, fp32)
   GemmArgs g4{xpT, nullptr, dguT, nullptr, offsets, E, 0, 2 * hf, rows, h,
-              dw1, dw3, nullptr, nullptr};
+              dw1, dw3, nullptr, nullptr, nullptr, nullptr};
+  splitk_ws_set<CfgBwd>(g4, split_ws);
   return launch_gemm<CfgBwd, MOE_BF16, kModeDW13, kSchedK>(g4, kTBwd4, s);
 }
 

@@ -17,6 +17,8 @@ namespace moe {
 
 constexpr int kRowB = 128;  // bytes of K per LDS row (one K slab)
 constexpr int kKPad = 64;   // SchedK: per-expert K padded to this
+constexpr int kMaxGrid = 256;  // persistent grid cap (workgroups)
+constexpr int kMaxSplit = 8;   // K splits of one tile in the last round
 
 // Tile shape: WM x WN waves, each owning MI x NJ MFMA blocks of 32 x 32, and
 // OCC workgroups resident per CU.  The tile is (32 WM MI) x (32 WN NJ); LDS
@@ -66,6 +68,8 @@ struct GemmArgs {
   void* out2;             // BwdDA: A [rows][N]; DW13: dW3
   void* save;             // FC1: G|U out [rows][N] bf16 or null; BwdDA: G|U in [rows][2N]
   uint32_t* row_amax;     // FC1 with FP8: [rows] (fp32 bits, atomic max)
+  float* part;            // split-K partial tiles (kMaxGrid tiles) or null: no split
+  uint32_t* cnt;          // split-K arrival counters [kMaxGrid], zero before the launch
 };
 
 // LDS byte position of 16-byte chunk c of row r: chunks XOR-swizzled by
@@ -135,6 +139,8 @@ __device__ __forceinline__ float silu_f(float g) { return g / (1.0f + __expf(-g)
 // where its A and B rows live.
 struct Tile {
   int e, row0, row_end, n0, nk, rowB;
+  int kb;     // first K slab of this work item
+  int split;  // -1: whole tile; else the split index (last round only)
   size_t a_off, a_bytes, b_off, b_bytes;
 };
 
@@ -380,12 +386,63 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, f32x16 (&acc)[C::kMI
   }
 }
 
+// Split-K tail.  The tiles of a persistent grid's last, partial round are
+// split along K so that every workgroup has work in it.  Each split stores
+// its fp32 partial tile (1 KB per lane-row, coalesced); the split that
+// arrives last on the tile's device-scope counter adds all partials in split
+// order and goes on to the epilogue, so the sum does not depend on arrival
+// order.  Returns true in the workgroup that finishes the tile.
+template <class C>
+__device__ __forceinline__ bool splitk_combine(const GemmArgs& g, f32x16 (&acc)[C::kMI][C::kNJ],
+                                               int slot0, int f, int s, int cidx, int wave,
+                                               int lane, int* flag) {
+  constexpr int MI = C::kMI, NJ = C::kNJ;
+  constexpr size_t kSlot = size_t(C::kBM) * C::kBN / 4;  // f32x4 per partial tile
+  f32x4* base = reinterpret_cast<f32x4*>(g.part) + size_t(wave) * MI * NJ * 4 * 64 + lane;
+  f32x4* mine = base + size_t(slot0 + s) * kSlot;
+#pragma unroll
+  for (int i = 0; i < MI; ++i)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        mine[((i * NJ + j) * 4 + q) * 64] =
+            f32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+  __threadfence();  // release: partial visible device-wide before the count
+  __syncthreads();
+  if (threadIdx.x == 0) *flag = atomicAdd(g.cnt + cidx, 1u) == unsigned(f - 1);
+  __syncthreads();
+  if (!*flag) return false;
+  __threadfence();  // acquire: the other splits' partials
+#pragma unroll
+  for (int i = 0; i < MI; ++i)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+  for (int t = 0; t < f; ++t) {
+    const f32x4* p = base + size_t(slot0 + t) * kSlot;
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const f32x4 v = p[((i * NJ + j) * 4 + q) * 64];
+#pragma unroll
+          for (int c = 0; c < 4; ++c) acc[i][j][4 * q + c] += v[c];
+        }
+  }
+  return true;
+}
+
 template <class C, int DT, int MODE, int SCHED>
 __global__ void __launch_bounds__(C::kThreads, C::kWavesPerSimd) grouped_gemm_kernel(GemmArgs g) {
   constexpr int BM = C::kBM, BN = C::kBN, MI = C::kMI, NJ = C::kNJ;
   extern __shared__ __align__(16) unsigned char lds[];
   __shared__ int tpre[MOE_MAX_EXPERTS + 1];  // tiles before expert e
   __shared__ int offs[MOE_MAX_EXPERTS + 1];  // SchedM: row offsets; SchedK: padded K prefix
+  __shared__ int split_flag;
   constexpr int EB = Elem<DT>::bytes;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
@@ -421,9 +478,23 @@ __global__ void __launch_bounds__(C::kThreads, C::kWavesPerSimd) grouped_gemm_ke
   const int total = tpre[g.E];
   const int G = gridDim.x;
   const int b = blockIdx.x;
-  // the workgroups of one XCD (b % 8) take consecutive tiles
+  // Work items: tiles [0, full) whole, then each of the last `rem` tiles as
+  // f K splits (f = 1: no split).
+  int full = total, f = 1;
+  if (g.part != nullptr && total % G != 0) {
+    const int rem = total % G;
+    f = G / rem < kMaxSplit ? G / rem : kMaxSplit;
+    if (SCHED == kSchedM) {
+      const int nkm = g.K * EB / kRowB;
+      if (f > nkm) f = nkm > 1 ? nkm : 1;
+    }
+    if (f > 1) full = total - rem;
+    else f = 1;
+  }
+  const int work = full + (total - full) * f;
+  // the workgroups of one XCD (b % 8) take consecutive work items
   int t = (G % 8 == 0) ? (b % 8) * (G / 8) + b / 8 : b;
-  if (t >= total) return;
+  if (t >= work) return;
 
   auto tile_of = [&](int tt) {
     int lo = 0, hi = g.E - 1;  // expert e with tpre[e] <= tt < tpre[e+1]
@@ -458,6 +529,18 @@ __global__ void __launch_bounds__(C::kThreads, C::kWavesPerSimd) grouped_gemm_ke
     }
     T.b_bytes = size_t(g.N - T.n0) * T.rowB;
     T.nk = T.rowB / kRowB;
+    T.kb = 0;
+    T.split = -1;
+    return T;
+  };
+  auto item_of = [&](int w) {
+    if (w < full) return tile_of(w);
+    const int u = w - full, s = u % f;
+    Tile T = tile_of(full + u / f);
+    const int k0 = s * T.nk / f, k1 = (s + 1) * T.nk / f;
+    T.kb = k0;
+    T.nk = k1 - k0;
+    T.split = s;
     return T;
   };
 
@@ -468,11 +551,11 @@ __global__ void __launch_bounds__(C::kThreads, C::kWavesPerSimd) grouped_gemm_ke
   // fragment rows inside a stage
   const int arow = wm * (MI * 32) + l32, brow = wn * (NJ * 32) + l32;
 
-  Tile cur = tile_of(t);
+  Tile cur = item_of(t);
   __amdgpu_buffer_rsrc_t ra = rsrc(g.A, cur.a_off, cur.a_bytes), rb = rsrc(g.B, cur.b_off, cur.b_bytes);
   LoadOff lo = load_off(cur.rowB, lane);
   int st = 0;
-  issue_slab<C>(lds, st, ra, rb, wave, lo, cur.rowB, 0);
+  issue_slab<C>(lds, st, ra, rb, wave, lo, cur.rowB, cur.kb * kRowB);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   Frag<DT> fa[2][MI], fb[2][NJ];
@@ -480,8 +563,8 @@ __global__ void __launch_bounds__(C::kThreads, C::kWavesPerSimd) grouped_gemm_ke
 
   while (true) {
     const int tn = t + G;
-    const bool has_next = tn < total;
-    const Tile nxt = has_next ? tile_of(tn) : cur;
+    const bool has_next = tn < work;
+    const Tile nxt = has_next ? item_of(tn) : cur;
     const __amdgpu_buffer_rsrc_t ra_n = rsrc(g.A, nxt.a_off, nxt.a_bytes);
     const __amdgpu_buffer_rsrc_t rb_n = rsrc(g.B, nxt.b_off, nxt.b_bytes);
     const LoadOff lo_n = load_off(nxt.rowB, lane);
@@ -499,7 +582,7 @@ __global__ void __launch_bounds__(C::kThreads, C::kWavesPerSimd) grouped_gemm_ke
       // slab kt+1 (or the next tile's first) into the other stage.
       const bool last = kt + 1 == cur.nk;
       issue_slab<C>(lds, st ^ 1, last ? ra_n : ra, last ? rb_n : rb, wave, last ? lo_n : lo,
-                    last ? nxt.rowB : cur.rowB, last ? 0 : (kt + 1) * kRowB);
+                    last ? nxt.rowB : cur.rowB, (last ? nxt.kb : cur.kb + kt + 1) * kRowB);
       const unsigned char* As = lds + st * C::kStage;
 #pragma unroll
       for (int s = 0; s + 1 < S; ++s) {
@@ -528,13 +611,17 @@ __global__ void __launch_bounds__(C::kThreads, C::kWavesPerSimd) grouped_gemm_ke
       // an empty-K tile prefetched nothing: bring in the next tile's first slab
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
-      issue_slab<C>(lds, st, ra_n, rb_n, wave, lo_n, nxt.rowB, 0);
+      issue_slab<C>(lds, st, ra_n, rb_n, wave, lo_n, nxt.rowB, nxt.kb * kRowB);
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
       load_frags<C, DT>(fa[0], fb[0], lds + st * C::kStage, arow, brow, 0, half);
     }
 
-    epilogue<C, DT, MODE>(g, acc, cur, wave, wm, wn, half, l32, lds + (st ^ 1) * C::kStage);
+    // a split is its workgroup's last item: only the one that completes the
+    // tile runs the epilogue
+    if (cur.split < 0 || splitk_combine<C>(g, acc, ((t - full) / f) * f, f, cur.split,
+                                           (t - full) / f, wave, lane, &split_flag))
+      epilogue<C, DT, MODE>(g, acc, cur, wave, wm, wn, half, l32, lds + (st ^ 1) * C::kStage);
     if (!has_next) break;
     t = tn;
     cur = nxt;
@@ -551,18 +638,42 @@ namespace moe_launch {
 // Persistent launch: OCC workgroups per CU (fewer if there are fewer tiles).
 // The tile count bound needs no device data: SchedM has at most
 // ceil(rows/BM) + E row tiles, SchedK exactly E ceil(M/BM).
+template <int>
+__global__ void zero_u32_kernel(uint32_t* p, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0u;
+}
+
+// Bytes of split-K workspace a configuration needs (partial tiles + counters).
+template <class C>
+constexpr size_t splitk_ws_bytes() {
+  return size_t(moe::kMaxGrid) * C::kBM * C::kBN * 4 + size_t(moe::kMaxGrid) * 4;
+}
+template <class C>
+inline void splitk_ws_set(moe::GemmArgs& a, void* ws) {
+  a.part = static_cast<float*>(ws);
+  a.cnt = reinterpret_cast<uint32_t*>(static_cast<unsigned char*>(ws) +
+                                      size_t(moe::kMaxGrid) * C::kBM * C::kBN * 4);
+}
+
 template <class C, int DT, int MODE, int SCHED>
 inline int launch_gemm(const moe::GemmArgs& a, int timer, hipStream_t s) {
   using namespace moe;
   static bool attr = allow_lds(grouped_gemm_kernel<C, DT, MODE, SCHED>, C::kLds);
   if (!attr) return MOE_ERR_HIP;
-  const long mt = SCHED == kSchedM ? (long(a.rows) + C::kBM - 1) / C::kBM + a.E
-                                   : long(a.E) * ((a.M + C::kBM - 1) / C::kBM);
-  const long tiles = mt * ((a.N + C::kBN - 1) / C::kBN);
   long grid = long(num_cus()) * C::kOcc;
-  if (tiles < grid) grid = tiles;
+  if (grid > kMaxGrid) grid = kMaxGrid;
+  if (a.part == nullptr) {
+    // without split-K, no more workgroups than tiles
+    const long mt = SCHED == kSchedM ? (long(a.rows) + C::kBM - 1) / C::kBM + a.E
+                                     : long(a.E) * ((a.M + C::kBM - 1) / C::kBM);
+    const long tiles = mt * ((a.N + C::kBN - 1) / C::kBN);
+    if (tiles < grid) grid = tiles;
+  }
   if (grid < 1) grid = 1;
   timer_begin(timer, s);
+  if (a.part != nullptr)
+    hipLaunchKernelGGL(zero_u32_kernel<0>, dim3(1), dim3(kMaxGrid), 0, s, a.cnt, int(kMaxGrid));
   hipLaunchKernelGGL((grouped_gemm_kernel<C, DT, MODE, SCHED>), dim3(unsigned(grid)),
                      dim3(C::kThreads), C::kLds, s, a);
   timer_end(timer, s);

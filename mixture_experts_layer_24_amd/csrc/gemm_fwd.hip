@@ -72,7 +72,7 @@ size_t grouped_fwd_ws_bytes(int rows, int h, int h_ffn, int E, int dtype) {
   size_t r = size_t(rows), hf = size_t(h_ffn);
   size_t act = al256(r * hf * (dtype == MOE_BF16 ? 2 : 4));
   if (dtype == MOE_FP8_E4M3) act += al256(r * hf) + 2 * al256(r * 4);
-  return act;
+  return act + splitk_ws_bytes<CfgFwd>();
 }
 
 template <int DT, int MODE>
@@ -88,6 +88,7 @@ static int fwd_typed(const void* xp, const float* xp_scale, const moe_weights* W
   unsigned char* w = static_cast<unsigned char*>(ws);
   void* act = w;
   size_t act_b = al256(size_t(rows) * hf * (DT == MOE_BF16 ? 2 : 4));
+  void* split_ws = w + act_b + (DT == MOE_FP8_E4M3 ? al256(size_t(rows) * hf) + 2 * al256(size_t(rows) * 4) : 0);
   uint8_t* actq = nullptr;
   uint32_t* amax = nullptr;
   float* ascale = nullptr;
@@ -99,7 +100,8 @@ static int fwd_typed(const void* xp, const float* xp_scale, const moe_weights* W
                        size_t(rows), 0u);
   }
   GemmArgs a1{xp, xp_scale, W->w13, W->w13_scale, offsets, E, h, 2 * hf, rows, 0,
-              act, nullptr, h13_save, amax};
+              act, nullptr, h13_save, amax, nullptr, nullptr};
+  splitk_ws_set<CfgFwd>(a1, split_ws);
   int rc = launch_fwd_gemm<DT, kModeFC1>(a1, s);
   if (rc) return rc;
   if (DT == MOE_FP8_E4M3) {
@@ -107,10 +109,14 @@ static int fwd_typed(const void* xp, const float* xp_scale, const moe_weights* W
     hipLaunchKernelGGL(quant_act_kernel, dim3(ceil_div(rows, 4)), dim3(256), 0, s,
                        (const float*)act, amax, offsets, E, hf, actq, ascale);
     timer_end(kTQuant, s);
-    GemmArgs a2{actq, ascale, W->w2, W->w2_scale, offsets, E, hf, h, rows, 0, yp, nullptr, nullptr, nullptr};
+    GemmArgs a2{actq, ascale, W->w2, W->w2_scale, offsets, E, hf, h, rows, 0, yp, nullptr, nullptr, nullptr,
+                nullptr, nullptr};
+    splitk_ws_set<CfgFwd>(a2, split_ws);
     return launch_fwd_gemm<DT, kModeFC2>(a2, s);
   }
-  GemmArgs a2{act, nullptr, W->w2, nullptr, offsets, E, hf, h, rows, 0, yp, nullptr, nullptr, nullptr};
+  GemmArgs a2{act, nullptr, W->w2, nullptr, offsets, E, hf, h, rows, 0, yp, nullptr, nullptr, nullptr,
+              nullptr, nullptr};
+  splitk_ws_set<CfgFwd>(a2, split_ws);
   return launch_fwd_gemm<DT, kModeFC2>(a2, s);
 }
 
