@@ -94,6 +94,11 @@ __global__ void __launch_bounds__(256) xpose_kernel(const uint16_t* __restrict__
 namespace moe_launch {
 using namespace moe;
 
+using CfgB = CfgFor<MOE_BF16>::type;
+// dA stages the kept G|U through the one LDS stage idle during its epilogue:
+// 128-byte slabs in two stages leave 8 KB per wave there (64 rows at a time).
+using CfgDA = GemmCfg<2, 4, 4, 2, 1, 128, 2>;
+
 static size_t al256(size_t x) { return (x + 255) & ~size_t(255); }
 
 // Upper bound of the padded K extent: sum_e roundup(M_e, 64) <= rows + 63 E.
@@ -107,7 +112,7 @@ size_t grouped_bwd_ws_bytes(int rows, int h, int h_ffn, int E, int dtype) {
          + 2 * al256(hh * kp * 2)       // Xp^T, dYp^T
          + al256(hf * kp * 2)           // A^T
          + al256(2 * hf * kp * 2)       // (dG|dU)^T
-         + splitk_ws_bytes<CfgBwd>();   // split-K partial tiles
+         + splitk_ws_bytes<CfgB>();   // split-K partial tiles
 }
 
 static int xpose(const void* src, int C, const int32_t* offsets, int E, int rows, void* dst,
@@ -147,8 +152,8 @@ int grouped_bwd(const void* dyp, const void* xp, const void* h13_save, const moe
   // dA = dYp W2^T, with dG, dU and A formed in the epilogue
   GemmArgs ga{dyp, nullptr, W->w2_bwd, nullptr, offsets, E, h, hf, rows, 0,
               dgu, act, const_cast<void*>(h13_save), nullptr, nullptr, nullptr};
-  splitk_ws_set<CfgBwd>(ga, split_ws);
-  if ((rc = launch_gemm<CfgBwd, MOE_BF16, kModeBwdDA, kSchedM>(ga, kTBwd1, s)))
+  splitk_ws_set<CfgDA>(ga, split_ws);
+  if ((rc = launch_gemm<CfgDA, MOE_BF16, kModeBwdDA, kSchedM>(ga, kTBwd1, s)))
     return rc;
 
   timer_begin(kTXpose, s);
@@ -159,22 +164,22 @@ int grouped_bwd(const void* dyp, const void* xp, const void* h13_save, const moe
   // dW2 = A^T dYp  (per expert [hf][h], fp32)
   GemmArgs g2{actT, nullptr, dypT, nullptr, offsets, E, 0, h, rows, hf,
               dw2, nullptr, nullptr, nullptr, nullptr, nullptr};
-  splitk_ws_set<CfgBwd>(g2, split_ws);
-  if ((rc = launch_gemm<CfgBwd, MOE_BF16, kModeDW, kSchedK>(g2, kTBwd2, s)))
+  splitk_ws_set<CfgB>(g2, split_ws);
+  if ((rc = launch_gemm<CfgB, MOE_BF16, kModeDW, kSchedK>(g2, kTBwd2, s)))
     return rc;
 
   // dXp = [dG|dU] W13^T
   GemmArgs g3{dgu, nullptr, W->w13_bwd, nullptr, offsets, E, 2 * hf, h, rows, 0,
               dxp, nullptr, nullptr, nullptr, nullptr, nullptr};
-  splitk_ws_set<CfgBwd>(g3, split_ws);
-  if ((rc = launch_gemm<CfgBwd, MOE_BF16, kModeFC2, kSchedM>(g3, kTBwd3, s)))
+  splitk_ws_set<CfgB>(g3, split_ws);
+  if ((rc = launch_gemm<CfgB, MOE_BF16, kModeFC2, kSchedM>(g3, kTBwd3, s)))
     return rc;
 
   // dW1 | dW3 = Xp^T [dG|dU]  (per expert [h][hf] each, fp32)
   GemmArgs g4{xpT, nullptr, dguT, nullptr, offsets, E, 0, 2 * hf, rows, h,
               dw1, dw3, nullptr, nullptr, nullptr, nullptr};
-  splitk_ws_set<CfgBwd>(g4, split_ws);
-  return launch_gemm<CfgBwd, MOE_BF16, kModeDW13, kSchedK>(g4, kTBwd4, s);
+  splitk_ws_set<CfgB>(g4, split_ws);
+  return launch_gemm<CfgB, MOE_BF16, kModeDW13, kSchedK>(g4, kTBwd4, s);
 }
 
 }  // namespace moe_launch

@@ -15,38 +15,46 @@
 
 namespace moe {
 
-constexpr int kRowB = 128;  // bytes of K per LDS row (one K slab)
-constexpr int kKPad = 64;   // SchedK: per-expert K padded to this
+constexpr int kKPad = 64;      // SchedK: per-expert K padded to this
 constexpr int kMaxGrid = 256;  // persistent grid cap (workgroups)
 constexpr int kMaxSplit = 8;   // K splits of one tile in the last round
 
 // Tile shape: WM x WN waves, each owning MI x NJ MFMA blocks of 32 x 32, and
-// OCC workgroups resident per CU.  The tile is (32 WM MI) x (32 WN NJ); LDS
-// holds two stages, each a K slab of the tile's A rows followed by its B rows.
-template <int WM, int WN, int MI, int NJ, int OCC>
+// OCC workgroups resident per CU.  The tile is (32 WM MI) x (32 WN NJ).  A K
+// slab is ROWB bytes of every A and B row of the tile; LDS holds NS slabs in
+// a ring and the loads run NS-1 slabs ahead of the MFMAs.
+template <int WM, int WN, int MI, int NJ, int OCC, int ROWB, int NS>
 struct GemmCfg {
   static constexpr int kWM = WM, kWN = WN, kMI = MI, kNJ = NJ, kOcc = OCC;
+  static constexpr int kRowB = ROWB, kStages = NS;
   static constexpr int kNW = WM * WN;             // waves per workgroup
   static constexpr int kThreads = 64 * kNW;
   static constexpr int kWavesPerSimd = kNW * OCC / 4;
   static constexpr int kBM = 32 * WM * MI, kBN = 32 * WN * NJ;
-  static constexpr int kAStage = kBM * kRowB;     // A part of a stage
-  static constexpr int kStage = (kBM + kBN) * kRowB;
-  static constexpr int kLds = 2 * kStage;
-  static constexpr int kGA = kBM / 8 / kNW, kGB = kBN / 8 / kNW;  // 8-row load groups per wave
-  static_assert(kGA * 8 * kNW == kBM && kGB * 8 * kNW == kBN, "rows must split over waves");
+  static constexpr int kAStage = kBM * ROWB;      // A part of a stage
+  static constexpr int kStage = (kBM + kBN) * ROWB;
+  static constexpr int kLds = NS * kStage;
+  static constexpr int kRowsPerLoad = 1024 / ROWB;  // rows one 1 KB wave load fills
+  static constexpr int kGA = kBM / kRowsPerLoad / kNW, kGB = kBN / kRowsPerLoad / kNW;
+  static_assert(ROWB == 64 || ROWB == 128, "row pitch");
+  static_assert(NS >= 2 && NS <= 4, "stages");
+  static_assert(kGA * kRowsPerLoad * kNW == kBM && kGB * kRowsPerLoad * kNW == kBN,
+                "rows must split over waves");
   static_assert(kNW % 4 == 0, "whole waves per SIMD");
 };
 
-// 256 x 256, four waves of 128 x 128 (256 accumulators per lane), one per SIMD.
-using CfgWide = GemmCfg<2, 2, 4, 4, 1>;
-// 256 x 256, eight waves of 128 x 64: two waves per SIMD, so one can issue
-// MFMAs while the other waits on a load.
-using CfgDual = GemmCfg<2, 4, 4, 2, 1>;
-
-// the configuration each pass runs with
-using CfgFwd = CfgDual;
-using CfgBwd = CfgDual;
+// 256 x 256 on eight waves of 128 x 64 (two per SIMD, so one can issue MFMAs
+// while the other waits on a load).
+// bf16 / fp32: 64-byte slabs, four stages (three slabs in flight, 128 KB);
+// fp8: 128-byte slabs (one MFMA's K), two stages.
+template <int DT>
+struct CfgFor {
+  using type = GemmCfg<2, 4, 4, 2, 1, 128, 2>;
+};
+template <>
+struct CfgFor<MOE_FP8_E4M3> {
+  using type = GemmCfg<2, 4, 4, 2, 1, 128, 2>;
+};
 
 enum { kSchedM = 0, kSchedK = 1 };
 enum {
@@ -72,10 +80,13 @@ struct GemmArgs {
   uint32_t* cnt;          // split-K arrival counters [kMaxGrid], zero before the launch
 };
 
-// LDS byte position of 16-byte chunk c of row r: chunks XOR-swizzled by
-// (r/2)%8 so the 64 lanes of a fragment read hit distinct banks.
+// LDS byte position of 16-byte chunk c of row r (pitch RB bytes): chunks are
+// XOR-swizzled by (r / (256/RB)) % (RB/16), so the rows that one 256-byte
+// bank sweep covers use every chunk position once and the 64 lanes of a
+// fragment read hit distinct banks.
+template <int RB>
 __device__ __forceinline__ int lds_pos(int row, int c) {
-  return row * kRowB + ((c ^ ((row >> 1) & 7)) << 4);
+  return row * RB + ((c ^ ((row / (256 / RB)) % (RB / 16))) << 4);
 }
 
 template <int DT>
@@ -84,17 +95,18 @@ template <> struct Elem<MOE_F32> { static constexpr int bytes = 4; };
 template <> struct Elem<MOE_BF16> { static constexpr int bytes = 2; };
 template <> struct Elem<MOE_FP8_E4M3> { static constexpr int bytes = 1; };
 
-// One 32x32 output block += A-fragment x B-fragment over 32 (bf16, f32) or
-// 64 (fp8) bytes of K per row.  The K order inside a fragment pair is the
-// same for A and B, which is all a dot product needs.
+// One 32x32 output block += A-fragment x B-fragment over kKBytes of K per
+// row (16 bf16, 8 fp32 or 64 fp8 values).  The K order inside a fragment
+// pair is the same for A and B, which is all a dot product needs.
 template <int DT>
 struct Frag;
 template <> struct Frag<MOE_BF16> {
   u32x4 v;
-  static constexpr int kSub = 4;  // substeps per 128-byte LDS row
+  static constexpr int kKBytes = 32;
   static constexpr int kReads = 1, kMfma = 1;  // LDS reads per fragment, MFMAs per pair
+  template <int RB>
   __device__ __forceinline__ void load(const unsigned char* base, int row, int s, int half) {
-    v = *reinterpret_cast<const u32x4*>(base + lds_pos(row, 2 * s + half));
+    v = *reinterpret_cast<const u32x4*>(base + lds_pos<RB>(row, 2 * s + half));
   }
   __device__ __forceinline__ static void mma(f32x16& c, const Frag& a, const Frag& b) {
     c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a.v),
@@ -103,10 +115,11 @@ template <> struct Frag<MOE_BF16> {
 };
 template <> struct Frag<MOE_F32> {
   u32x4 v;
-  static constexpr int kSub = 4;
+  static constexpr int kKBytes = 32;
   static constexpr int kReads = 1, kMfma = 4;
+  template <int RB>
   __device__ __forceinline__ void load(const unsigned char* base, int row, int s, int half) {
-    v = *reinterpret_cast<const u32x4*>(base + lds_pos(row, 2 * s + half));
+    v = *reinterpret_cast<const u32x4*>(base + lds_pos<RB>(row, 2 * s + half));
   }
   __device__ __forceinline__ static void mma(f32x16& c, const Frag& a, const Frag& b) {
 #pragma unroll
@@ -116,27 +129,25 @@ template <> struct Frag<MOE_F32> {
   }
 };
 template <> struct Frag<MOE_FP8_E4M3> {
-  u32x4 v0, v1;
-  static constexpr int kSub = 2;
+  i32x8 v;  // two 16-byte chunks, consecutive registers as the MFMA wants them
+  static constexpr int kKBytes = 64;
   static constexpr int kReads = 2, kMfma = 1;
+  template <int RB>
   __device__ __forceinline__ void load(const unsigned char* base, int row, int s, int half) {
-    v0 = *reinterpret_cast<const u32x4*>(base + lds_pos(row, 4 * s + 2 * half));
-    v1 = *reinterpret_cast<const u32x4*>(base + lds_pos(row, 4 * s + 2 * half + 1));
+    const u32x4 lo = *reinterpret_cast<const u32x4*>(base + lds_pos<RB>(row, 4 * s + 2 * half));
+    const u32x4 hi = *reinterpret_cast<const u32x4*>(base + lds_pos<RB>(row, 4 * s + 2 * half + 1));
+    v = i32x8{int(lo[0]), int(lo[1]), int(lo[2]), int(lo[3]), int(hi[0]), int(hi[1]), int(hi[2]), int(hi[3])};
   }
   __device__ __forceinline__ static void mma(f32x16& c, const Frag& a, const Frag& b) {
-    i32x8 av = {int(a.v0[0]), int(a.v0[1]), int(a.v0[2]), int(a.v0[3]),
-                int(a.v1[0]), int(a.v1[1]), int(a.v1[2]), int(a.v1[3])};
-    i32x8 bv = {int(b.v0[0]), int(b.v0[1]), int(b.v0[2]), int(b.v0[3]),
-                int(b.v1[0]), int(b.v1[1]), int(b.v1[2]), int(b.v1[3])};
     // formats 0/0 = E4M3 x E4M3; E8M0 scales of 127 = 1.0
-    c = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, c, 0, 0, 0, 127, 0, 127);
+    c = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a.v, b.v, c, 0, 0, 0, 127, 0, 127);
   }
 };
 
 __device__ __forceinline__ float silu_f(float g) { return g / (1.0f + __expf(-g)); }
 
-// One output tile: expert, first row / column, valid row end, K slabs, and
-// where its A and B rows live.
+// One work item: expert, first row / column, valid row end, and where its A
+// and B rows live; K slabs [kb, kb + nk) of the tile.
 struct Tile {
   int e, row0, row_end, n0, nk, rowB;
   int kb;     // first K slab of this work item
@@ -154,25 +165,29 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, size_t 
 
 typedef __attribute__((address_space(3))) void lds_ptr_t;
 
-// Loader offsets of one lane for row pitch rowB.  An 8-row group lands in
-// 1 KB of LDS with lane l at byte 16*l (row l/8 of the group, position l%8),
-// so the lane fetches the chunk that the XOR swizzle keeps at that position;
-// the swizzle of row 8q + l/8 is 4*(q%2) + l/16, hence even and odd groups.
+// Loader offsets of one lane for global row pitch rowB.  A 1 KB wave load
+// fills 1024/RB rows of LDS with lane l at byte 16*l (row l/(RB/16),
+// position l%(RB/16)), so the lane fetches the chunk that the swizzle keeps
+// at that position.  With 128-byte rows the swizzle of a row group depends
+// on the group's parity (e / o); with 64-byte rows it does not.
 struct LoadOff {
   int e, o;
 };
+template <int RB>
 __device__ __forceinline__ LoadOff load_off(int rowB, int lane) {
-  const int r = lane >> 3, c = (lane & 7) ^ (r >> 1);
-  return LoadOff{r * rowB + (c << 4), r * rowB + ((c ^ 4) << 4)};
+  constexpr int LPR = RB / 16, RPL = 1024 / RB, SW = 256 / RB;
+  const int r = lane / LPR, p = lane % LPR;
+  const int ce = p ^ ((r / SW) % LPR), co = p ^ (((r + RPL) / SW) % LPR);
+  return LoadOff{r * rowB + (ce << 4), r * rowB + (co << 4)};
 }
 
-// One K slab (128 bytes per row) of A and B straight from memory into LDS
-// stage `st`: wave w fills 8-row groups w*GA .. w*GA+GA-1 of A and
-// w*GB .. w*GB+GB-1 of B.
+// One K slab of A and B straight from memory into LDS stage `st`: wave w
+// fills row groups w*GA .. w*GA+GA-1 of A and w*GB .. w*GB+GB-1 of B.
 template <class C>
 __device__ __forceinline__ void issue_slab(unsigned char* lds, int st, __amdgpu_buffer_rsrc_t ra,
                                            __amdgpu_buffer_rsrc_t rb, int wave, LoadOff lo,
                                            int rowB, int koff) {
+  constexpr int RPL = C::kRowsPerLoad;
   unsigned char* A = lds + st * C::kStage + wave * C::kGA * 1024;
   unsigned char* B = lds + st * C::kStage + C::kAStage + wave * C::kGB * 1024;
   const int ga0 = wave * C::kGA, gb0 = wave * C::kGB;
@@ -180,12 +195,12 @@ __device__ __forceinline__ void issue_slab(unsigned char* lds, int st, __amdgpu_
   for (int i = 0; i < (C::kGA > C::kGB ? C::kGA : C::kGB); ++i) {
     if (i < C::kGA) {
       const int q = ga0 + i;
-      const int v = ((q & 1) ? lo.o : lo.e) + q * 8 * rowB + koff;
+      const int v = ((q & 1) ? lo.o : lo.e) + q * RPL * rowB + koff;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t*)(A + i * 1024), 16, v, 0, 0, 0);
     }
     if (i < C::kGB) {
       const int q = gb0 + i;
-      const int v = ((q & 1) ? lo.o : lo.e) + q * 8 * rowB + koff;
+      const int v = ((q & 1) ? lo.o : lo.e) + q * RPL * rowB + koff;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr_t*)(B + i * 1024), 16, v, 0, 0, 0);
     }
   }
@@ -197,9 +212,10 @@ __device__ __forceinline__ void load_frags(Frag<DT> (&fa)[C::kMI], Frag<DT> (&fb
                                            const unsigned char* As, int arow, int brow, int s,
                                            int half) {
 #pragma unroll
-  for (int i = 0; i < C::kMI; ++i) fa[i].load(As, arow + i * 32, s, half);
+  for (int i = 0; i < C::kMI; ++i) fa[i].template load<C::kRowB>(As, arow + i * 32, s, half);
 #pragma unroll
-  for (int j = 0; j < C::kNJ; ++j) fb[j].load(As + C::kAStage, brow + j * 32, s, half);
+  for (int j = 0; j < C::kNJ; ++j)
+    fb[j].template load<C::kRowB>(As + C::kAStage, brow + j * 32, s, half);
 }
 
 template <class C, int DT>
@@ -209,6 +225,46 @@ __device__ __forceinline__ void mma_all(f32x16 (&acc)[C::kMI][C::kNJ], const Fra
   for (int i = 0; i < C::kMI; ++i)
 #pragma unroll
     for (int j = 0; j < C::kNJ; ++j) Frag<DT>::mma(acc[i][j], fa[i], fb[j]);
+}
+
+// Single-buffered fragments (fp8, whose 8-register fragments and
+// VGPR-resident accumulators leave no room for a second set): multiply,
+// and reload each fragment for substep s of stage As right after its last
+// MFMA.  B fragments go first (j outer), so the next substep's first MFMAs
+// find theirs loaded early.
+template <class C, int DT, bool reload>
+__device__ __forceinline__ void mma_reload(f32x16 (&acc)[C::kMI][C::kNJ], Frag<DT> (&fa)[C::kMI],
+                                           Frag<DT> (&fb)[C::kNJ], const unsigned char* As,
+                                           int arow, int brow, int s, int half) {
+#pragma unroll
+  for (int j = 0; j < C::kNJ; ++j) {
+#pragma unroll
+    for (int i = 0; i < C::kMI; ++i) {
+      Frag<DT>::mma(acc[i][j], fa[i], fb[j]);
+      if (j == C::kNJ - 1 && reload) fa[i].template load<C::kRowB>(As, arow + i * 32, s, half);
+    }
+    if (reload) fb[j].template load<C::kRowB>(As + C::kAStage, brow + j * 32, s, half);
+  }
+  // keep that order: a reload may only follow the last MFMA that reads the
+  // fragment it replaces
+  constexpr int R = Frag<DT>::kReads;
+#pragma unroll
+  for (int j = 0; j < C::kNJ; ++j) {
+#pragma unroll
+    for (int i = 0; i < C::kMI; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (j == C::kNJ - 1 && reload) __builtin_amdgcn_sched_group_barrier(0x100, R, 0);
+    }
+    if (reload) __builtin_amdgcn_sched_group_barrier(0x100, R, 0);
+  }
+}
+
+// s_waitcnt: at most N vector-memory operations outstanding and no LDS read
+// (lgkmcnt 0; expcnt not waited on).
+template <int N>
+__device__ __forceinline__ void wait_vm_lds() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | ((N >> 4) << 14));
 }
 
 // Row of accumulator register r of MFMA block i (relative to the wave's rows).
@@ -439,6 +495,7 @@ __device__ __forceinline__ bool splitk_combine(const GemmArgs& g, f32x16 (&acc)[
 template <class C, int DT, int MODE, int SCHED>
 __global__ void __launch_bounds__(C::kThreads, C::kWavesPerSimd) grouped_gemm_kernel(GemmArgs g) {
   constexpr int BM = C::kBM, BN = C::kBN, MI = C::kMI, NJ = C::kNJ;
+  constexpr int RB = C::kRowB, NS = C::kStages, D = NS - 1;  // D slabs in flight ahead
   extern __shared__ __align__(16) unsigned char lds[];
   __shared__ int tpre[MOE_MAX_EXPERTS + 1];  // tiles before expert e
   __shared__ int offs[MOE_MAX_EXPERTS + 1];  // SchedM: row offsets; SchedK: padded K prefix
@@ -475,7 +532,7 @@ __global__ void __launch_bounds__(C::kThreads, C::kWavesPerSimd) grouped_gemm_ke
     if (SCHED == kSchedK) offs[g.E] = kp;
   }
   __syncthreads();
-  const int total = tpre[g.E];
+  const int total = __builtin_amdgcn_readfirstlane(tpre[g.E]);
   const int G = gridDim.x;
   const int b = blockIdx.x;
   // Work items: tiles [0, full) whole, then each of the last `rem` tiles as
@@ -485,7 +542,7 @@ __global__ void __launch_bounds__(C::kThreads, C::kWavesPerSimd) grouped_gemm_ke
     const int rem = total % G;
     f = G / rem < kMaxSplit ? G / rem : kMaxSplit;
     if (SCHED == kSchedM) {
-      const int nkm = g.K * EB / kRowB;
+      const int nkm = g.K * EB / RB;
       if (f > nkm) f = nkm > 1 ? nkm : 1;
     }
     if (f > 1) full = total - rem;
@@ -496,21 +553,25 @@ __global__ void __launch_bounds__(C::kThreads, C::kWavesPerSimd) grouped_gemm_ke
   int t = (G % 8 == 0) ? (b % 8) * (G / 8) + b / 8 : b;
   if (t >= work) return;
 
+  // LDS values read here are the same in every lane: keep them in scalar
+  // registers, so the work-item state costs no vector registers.
+  auto sld = [](const int* p) { return __builtin_amdgcn_readfirstlane(*p); };
   auto tile_of = [&](int tt) {
     int lo = 0, hi = g.E - 1;  // expert e with tpre[e] <= tt < tpre[e+1]
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
-      if (tpre[mid] <= tt) lo = mid; else hi = mid - 1;
+      if (sld(tpre + mid) <= tt) lo = mid; else hi = mid - 1;
     }
     Tile T;
     T.e = lo;
-    const int local = tt - tpre[lo];
+    const int local = tt - sld(tpre + lo);
+    const int o0 = sld(offs + lo), o1 = sld(offs + lo + 1);
     if (SCHED == kSchedM) {
       // experts in order, m-tiles fastest: consecutive tiles share a weight block
-      const int mt_e = ceil_div(offs[lo + 1] - offs[lo], BM);
+      const int mt_e = ceil_div(o1 - o0, BM);
       const int nt = local / mt_e, mt = local - nt * mt_e;
-      T.row0 = offs[lo] + mt * BM;
-      T.row_end = offs[lo + 1];
+      T.row0 = o0 + mt * BM;
+      T.row_end = o1;
       T.n0 = nt * BN;
       T.rowB = g.K * EB;
       T.a_off = size_t(T.row0) * T.rowB;
@@ -518,7 +579,7 @@ __global__ void __launch_bounds__(C::kThreads, C::kWavesPerSimd) grouped_gemm_ke
       T.b_off = (size_t(lo) * g.N + T.n0) * T.rowB;
     } else {
       const int nt = local / MT, mt = local - nt * MT;
-      const int k0 = offs[lo], ke = offs[lo + 1] - k0;
+      const int k0 = o0, ke = o1 - o0;
       T.row0 = mt * BM;
       T.row_end = g.M;
       T.n0 = nt * BN;
@@ -528,7 +589,7 @@ __global__ void __launch_bounds__(C::kThreads, C::kWavesPerSimd) grouped_gemm_ke
       T.b_off = size_t(k0) * g.N * EB + size_t(T.n0) * T.rowB;
     }
     T.b_bytes = size_t(g.N - T.n0) * T.rowB;
-    T.nk = T.rowB / kRowB;
+    T.nk = T.rowB / RB;
     T.kb = 0;
     T.split = -1;
     return T;
@@ -544,31 +605,61 @@ __global__ void __launch_bounds__(C::kThreads, C::kWavesPerSimd) grouped_gemm_ke
     return T;
   };
 
-  constexpr int S = Frag<DT>::kSub;                     // substeps per slab (even)
+  constexpr int S = RB / Frag<DT>::kKBytes;             // substeps per slab
+  static_assert(S >= 2 && S % 2 == 0, "fragment double buffer needs an even substep count");
   constexpr int NR = (MI + NJ) * Frag<DT>::kReads;      // LDS reads per substep
   constexpr int NM = MI * NJ * Frag<DT>::kMfma;         // MFMAs per substep
-  constexpr int NV = C::kGA + C::kGB;                   // global loads per slab
+  constexpr int NV = C::kGA + C::kGB;                   // global loads per slab per wave
+  constexpr bool kSingle = Frag<DT>::kReads == 2;       // fp8: single-buffered fragments
   // fragment rows inside a stage
   const int arow = wm * (MI * 32) + l32, brow = wn * (NJ * 32) + l32;
 
-  Tile cur = item_of(t);
-  __amdgpu_buffer_rsrc_t ra = rsrc(g.A, cur.a_off, cur.a_bytes), rb = rsrc(g.B, cur.b_off, cur.b_bytes);
-  LoadOff lo = load_off(cur.rowB, lane);
-  int st = 0;
-  issue_slab<C>(lds, st, ra, rb, wave, lo, cur.rowB, cur.kb * kRowB);
-  __builtin_amdgcn_s_waitcnt(0);
+  // The slabs of this workgroup's work items form one stream; slab c of the
+  // stream sits in stage c % NS.  The loader walks the same items as the
+  // MFMAs, D slabs ahead, skipping items without K slabs.
+  int lw = t, lk = 0, issued = 0;
+  Tile lt = item_of(lw);
+  bool ldone = false;
+  while (lt.nk == 0) {
+    lw += G;
+    if (lw >= work) { ldone = true; break; }
+    lt = item_of(lw);
+  }
+  __amdgpu_buffer_rsrc_t lra = rsrc(g.A, lt.a_off, lt.a_bytes), lrb = rsrc(g.B, lt.b_off, lt.b_bytes);
+  LoadOff llo = load_off<RB>(lt.rowB, lane);
+  auto issue = [&]() {
+    if (ldone) return;
+    issue_slab<C>(lds, issued % NS, lra, lrb, wave, llo, lt.rowB, (lt.kb + lk) * RB);
+    ++issued;
+    if (++lk < lt.nk) return;
+    lk = 0;
+    do {
+      lw += G;
+      if (lw >= work) { ldone = true; return; }
+      lt = item_of(lw);
+    } while (lt.nk == 0);
+    lra = rsrc(g.A, lt.a_off, lt.a_bytes);
+    lrb = rsrc(g.B, lt.b_off, lt.b_bytes);
+    llo = load_off<RB>(lt.rowB, lane);
+  };
+  // wait until slab c has landed: n = slabs issued after it (in flight)
+  auto wait_slab = [&](int c) {
+    const int n = issued - 1 - c;
+    if (D >= 3 && n >= 2) wait_vm_lds<(D >= 3 ? 2 * NV : 0)>();
+    else if (D >= 2 && n >= 1) wait_vm_lds<(D >= 2 ? NV : 0)>();
+    else wait_vm_lds<0>();
+  };
+
+  for (int i = 0; i < D; ++i) issue();
+  wait_slab(0);
   __syncthreads();
   Frag<DT> fa[2][MI], fb[2][NJ];
-  load_frags<C, DT>(fa[0], fb[0], lds, arow, brow, 0, half);
+  if (issued > 0) load_frags<C, DT>(fa[0], fb[0], lds, arow, brow, 0, half);
 
+  int c = 0;             // stream slab the MFMAs consume next
+  bool drain = false;    // an epilogue's stores may be outstanding
   while (true) {
-    const int tn = t + G;
-    const bool has_next = tn < work;
-    const Tile nxt = has_next ? item_of(tn) : cur;
-    const __amdgpu_buffer_rsrc_t ra_n = rsrc(g.A, nxt.a_off, nxt.a_bytes);
-    const __amdgpu_buffer_rsrc_t rb_n = rsrc(g.B, nxt.b_off, nxt.b_bytes);
-    const LoadOff lo_n = load_off(nxt.rowB, lane);
-
+    const Tile cur = item_of(t);
     f32x16 acc[MI][NJ];
 #pragma unroll
     for (int i = 0; i < MI; ++i)
@@ -578,12 +669,31 @@ __global__ void __launch_bounds__(C::kThreads, C::kWavesPerSimd) grouped_gemm_ke
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
     for (int kt = 0; kt < cur.nk; ++kt) {
-      // Stage st holds slab kt and fa[0]/fb[0] its first fragments.  Load
-      // slab kt+1 (or the next tile's first) into the other stage.
-      const bool last = kt + 1 == cur.nk;
-      issue_slab<C>(lds, st ^ 1, last ? ra_n : ra, last ? rb_n : rb, wave, last ? lo_n : lo,
-                    last ? nxt.rowB : cur.rowB, (last ? nxt.kb : cur.kb + kt + 1) * kRowB);
-      const unsigned char* As = lds + st * C::kStage;
+      // Stage c % NS holds slab c and fa[0]/fb[0] its first fragments.
+      // Stores and loads share one counter and may complete out of order:
+      // after an epilogue, drain it before counting loads again.
+      if (drain) {
+        __builtin_amdgcn_s_waitcnt(0);
+        drain = false;
+      }
+      // slab c + D goes into the stage that slab c - 1 left (read out before
+      // the last barrier)
+      issue();
+      const unsigned char* As = lds + (c % NS) * C::kStage;
+      if (kSingle) {
+#pragma unroll
+        for (int s = 0; s + 1 < S; ++s)
+          mma_reload<C, DT, true>(acc, fa[0], fb[0], As, arow, brow, s + 1, half);
+        wait_slab(c + 1);
+        __syncthreads();
+        if (c + 1 < issued)
+          mma_reload<C, DT, true>(acc, fa[0], fb[0], lds + ((c + 1) % NS) * C::kStage, arow, brow, 0,
+                                  half);
+        else
+          mma_reload<C, DT, false>(acc, fa[0], fb[0], As, arow, brow, 0, half);
+        ++c;
+        continue;
+      }
 #pragma unroll
       for (int s = 0; s + 1 < S; ++s) {
         load_frags<C, DT>(fa[(s + 1) & 1], fb[(s + 1) & 1], As, arow, brow, s + 1, half);
@@ -598,36 +708,26 @@ __global__ void __launch_bounds__(C::kThreads, C::kWavesPerSimd) grouped_gemm_ke
           if (q < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
           if (s == 0 && q < NV) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
         }
-      __builtin_amdgcn_s_waitcnt(0);  // stage st read out; slab kt+1 landed
+      wait_slab(c + 1);  // this stage read out; slab c+1 landed
       __syncthreads();
       // next slab's first fragments load while the last substep multiplies
-      load_frags<C, DT>(fa[0], fb[0], lds + (st ^ 1) * C::kStage, arow, brow, 0, half);
+      if (c + 1 < issued)
+        load_frags<C, DT>(fa[0], fb[0], lds + ((c + 1) % NS) * C::kStage, arow, brow, 0, half);
       mma_all<C, DT>(acc, fa[1], fb[1]);
       __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);
       __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);
-      st ^= 1;
-    }
-    if (cur.nk == 0 && has_next) {
-      // an empty-K tile prefetched nothing: bring in the next tile's first slab
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
-      issue_slab<C>(lds, st, ra_n, rb_n, wave, lo_n, nxt.rowB, nxt.kb * kRowB);
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
-      load_frags<C, DT>(fa[0], fb[0], lds + st * C::kStage, arow, brow, 0, half);
+      ++c;
     }
 
-    // a split is its workgroup's last item: only the one that completes the
-    // tile runs the epilogue
+    // A split is its workgroup's last item: only the one that completes the
+    // tile runs the epilogue.  Stage (c - 1) % NS holds no slab in flight.
     if (cur.split < 0 || splitk_combine<C>(g, acc, ((t - full) / f) * f, f, cur.split,
                                            (t - full) / f, wave, lane, &split_flag))
-      epilogue<C, DT, MODE>(g, acc, cur, wave, wm, wn, half, l32, lds + (st ^ 1) * C::kStage);
-    if (!has_next) break;
-    t = tn;
-    cur = nxt;
-    ra = ra_n;
-    rb = rb_n;
-    lo = lo_n;
+      epilogue<C, DT, MODE>(g, acc, cur, wave, wm, wn, half, l32,
+                            lds + ((c + NS - 1) % NS) * C::kStage);
+    drain = true;
+    t += G;
+    if (t >= work) break;
   }
 }
 
@@ -645,6 +745,9 @@ __global__ void zero_u32_kernel(uint32_t* p, int n) {
 }
 
 // Bytes of split-K workspace a configuration needs (partial tiles + counters).
+static_assert(moe::CfgFor<MOE_BF16>::type::kBM * moe::CfgFor<MOE_BF16>::type::kBN ==
+                  moe::CfgFor<MOE_FP8_E4M3>::type::kBM * moe::CfgFor<MOE_FP8_E4M3>::type::kBN,
+              "one split-K workspace size for every dtype");
 template <class C>
 constexpr size_t splitk_ws_bytes() {
   return size_t(moe::kMaxGrid) * C::kBM * C::kBN * 4 + size_t(moe::kMaxGrid) * 4;

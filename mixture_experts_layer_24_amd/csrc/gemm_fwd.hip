@@ -72,12 +72,12 @@ size_t grouped_fwd_ws_bytes(int rows, int h, int h_ffn, int E, int dtype) {
   size_t r = size_t(rows), hf = size_t(h_ffn);
   size_t act = al256(r * hf * (dtype == MOE_BF16 ? 2 : 4));
   if (dtype == MOE_FP8_E4M3) act += al256(r * hf) + 2 * al256(r * 4);
-  return act + splitk_ws_bytes<CfgFwd>();
+  return act + splitk_ws_bytes<CfgFor<MOE_BF16>::type>();
 }
 
 template <int DT, int MODE>
 static int launch_fwd_gemm(const GemmArgs& a, hipStream_t s) {
-  return launch_gemm<CfgFwd, DT, MODE, kSchedM>(a, MODE == kModeFC1 ? kTFc1 : kTFc2, s);
+  return launch_gemm<typename CfgFor<DT>::type, DT, MODE, kSchedM>(a, MODE == kModeFC1 ? kTFc1 : kTFc2, s);
 }
 
 template <int DT>
@@ -101,7 +101,7 @@ static int fwd_typed(const void* xp, const float* xp_scale, const moe_weights* W
   }
   GemmArgs a1{xp, xp_scale, W->w13, W->w13_scale, offsets, E, h, 2 * hf, rows, 0,
               act, nullptr, h13_save, amax, nullptr, nullptr};
-  splitk_ws_set<CfgFwd>(a1, split_ws);
+  splitk_ws_set<typename CfgFor<DT>::type>(a1, split_ws);
   int rc = launch_fwd_gemm<DT, kModeFC1>(a1, s);
   if (rc) return rc;
   if (DT == MOE_FP8_E4M3) {
@@ -111,12 +111,12 @@ static int fwd_typed(const void* xp, const float* xp_scale, const moe_weights* W
     timer_end(kTQuant, s);
     GemmArgs a2{actq, ascale, W->w2, W->w2_scale, offsets, E, hf, h, rows, 0, yp, nullptr, nullptr, nullptr,
                 nullptr, nullptr};
-    splitk_ws_set<CfgFwd>(a2, split_ws);
+    splitk_ws_set<typename CfgFor<DT>::type>(a2, split_ws);
     return launch_fwd_gemm<DT, kModeFC2>(a2, s);
   }
   GemmArgs a2{act, nullptr, W->w2, nullptr, offsets, E, hf, h, rows, 0, yp, nullptr, nullptr, nullptr,
               nullptr, nullptr};
-  splitk_ws_set<CfgFwd>(a2, split_ws);
+  splitk_ws_set<typename CfgFor<DT>::type>(a2, split_ws);
   return launch_fwd_gemm<DT, kModeFC2>(a2, s);
 }
 
