@@ -46,12 +46,21 @@ __global__ void __launch_bounds__(256) quant_act_kernel(const float* __restrict_
   if (lane == 0) scale[row] = s;
   const f32x4* src = reinterpret_cast<const f32x4*>(act + size_t(row) * hf);
   uint32_t* dst = reinterpret_cast<uint32_t*>(q + size_t(row) * hf);
-  for (int c = lane; c < hf / 4; c += 64) {
-    f32x4 v = src[c];
-    uint32_t w = 0;
+  constexpr int kBatch = 8;  // 16-byte loads per lane in flight
+  const int n4 = hf / 4;
+  for (int c0 = lane; c0 < n4; c0 += 64 * kBatch) {
+    f32x4 v[kBatch];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) w |= f32_to_e4m3(v[i] / s) << (8 * i);
-    dst[c] = w;
+    for (int b = 0; b < kBatch; ++b)
+      if (c0 + 64 * b < n4) v[b] = src[c0 + 64 * b];
+#pragma unroll
+    for (int b = 0; b < kBatch; ++b) {
+      if (c0 + 64 * b >= n4) break;
+      uint32_t w = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) w |= f32_to_e4m3(v[b][i] / s) << (8 * i);
+      dst[c0 + 64 * b] = w;
+    }
   }
 }
 

@@ -38,24 +38,33 @@ __global__ void __launch_bounds__(256) permute_copy_kernel(const void* __restric
     sc[j] = row_scale ? row_scale[size_t(t) * k + j] : 1.f;
   }
   constexpr int EPC = kF32 ? 4 : 8;  // elements per 16-byte chunk
+  constexpr int kBatch = 8;          // chunks per lane in flight
   const int nch = h / EPC;
   const u32x4* s = reinterpret_cast<const u32x4*>(static_cast<const char*>(src) + size_t(t) * h * (16 / EPC));
-  for (int c = lane; c < nch; c += 64) {
-    u32x4 v = s[c];
-    for (int j = 0; j < k; ++j) {
-      if (rows[j] < 0 || rows[j] >= T * k) continue;
-      u32x4 o = v;
-      if (row_scale) {
-        if (kF32) {
+  for (int c0 = lane; c0 < nch; c0 += 64 * kBatch) {
+    u32x4 v[kBatch];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) o[i] = __float_as_uint(__uint_as_float(v[i]) * sc[j]);
-        } else {
+    for (int b = 0; b < kBatch; ++b)
+      if (c0 + 64 * b < nch) v[b] = s[c0 + 64 * b];
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            o[i] = pack_bf16x2(bf16_lo(v[i]) * sc[j], bf16_hi(v[i]) * sc[j]);
+    for (int b = 0; b < kBatch; ++b) {
+      const int c = c0 + 64 * b;
+      if (c >= nch) break;
+      for (int j = 0; j < k; ++j) {
+        if (rows[j] < 0 || rows[j] >= T * k) continue;
+        u32x4 o = v[b];
+        if (row_scale) {
+          if (kF32) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) o[i] = __float_as_uint(__uint_as_float(o[i]) * sc[j]);
+          } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              o[i] = pack_bf16x2(bf16_lo(o[i]) * sc[j], bf16_hi(o[i]) * sc[j]);
+          }
         }
+        reinterpret_cast<u32x4*>(static_cast<char*>(dst) + size_t(rows[j]) * h * (16 / EPC))[c] = o;
       }
-      reinterpret_cast<u32x4*>(static_cast<char*>(dst) + size_t(rows[j]) * h * (16 / EPC))[c] = o;
     }
   }
 }
@@ -70,38 +79,56 @@ __global__ void __launch_bounds__(256) permute_fp8_kernel(const uint16_t* __rest
   const int t = blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
   if (t >= T) return;
   const int nch = h / 8;
+  constexpr int kBatch = 16;  // chunks per lane in flight (h <= 8192: the whole row)
   const u32x4* s = reinterpret_cast<const u32x4*>(src + size_t(t) * h);
+  int rows[MOE_MAX_TOPK];
+  for (int j = 0; j < k; ++j) rows[j] = dst_row[size_t(t) * k + j];
+  u32x4 v[kBatch];
   float amax = 0.f;
-  for (int c = lane; c < nch; c += 64) {
-    u32x4 v = s[c];
-    float f[8];
-    unpack8(v, f);
+  for (int c0 = lane; c0 < nch; c0 += 64 * kBatch) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(f[i]));
+    for (int b = 0; b < kBatch; ++b) v[b] = c0 + 64 * b < nch ? s[c0 + 64 * b] : u32x4{0, 0, 0, 0};
+#pragma unroll
+    for (int b = 0; b < kBatch; ++b) {
+      float f[8];
+      unpack8(v[b], f);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(f[i]));
+    }
   }
   amax = wave_max(amax);
   const float scale = amax > 0.f ? amax / 448.0f : 1.0f;
-  int rows[MOE_MAX_TOPK];
-  for (int j = 0; j < k; ++j) rows[j] = dst_row[size_t(t) * k + j];
   if (lane < k && rows[lane] >= 0 && rows[lane] < T * k) dst_scale[rows[lane]] = scale;
-  for (int c = lane; c < nch; c += 64) {
-    u32x4 v = s[c];
-    float f[8];
-    unpack8(v, f);
-    uint32_t lo = 0, hi = 0;
+  const bool held = nch <= 64 * kBatch;  // v still holds the row
+  for (int c0 = lane; c0 < nch; c0 += 64 * kBatch) {
+    if (!held) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) lo |= f32_to_e4m3(f[i] / scale) << (8 * i);
+      for (int b = 0; b < kBatch; ++b)
+        if (c0 + 64 * b < nch) v[b] = s[c0 + 64 * b];
+    }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) hi |= f32_to_e4m3(f[4 + i] / scale) << (8 * i);
-    for (int j = 0; j < k; ++j) {
-      if (rows[j] < 0 || rows[j] >= T * k) continue;
-      uint2* d = reinterpret_cast<uint2*>(dst + size_t(rows[j]) * h);
-      d[c] = make_uint2(lo, hi);
+    for (int b = 0; b < kBatch; ++b) {
+      const int c = c0 + 64 * b;
+      if (c >= nch) break;
+      float f[8];
+      unpack8(v[b], f);
+      uint32_t lo = 0, hi = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) lo |= f32_to_e4m3(f[i] / scale) << (8 * i);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) hi |= f32_to_e4m3(f[4 + i] / scale) << (8 * i);
+      for (int j = 0; j < k; ++j) {
+        if (rows[j] < 0 || rows[j] >= T * k) continue;
+        uint2* d = reinterpret_cast<uint2*>(dst + size_t(rows[j]) * h);
+        d[c] = make_uint2(lo, hi);
+      }
     }
   }
 }
 
-template <bool kInF32, bool kOutF32>
+// KM >= k bounds the routed rows per token, so every load of a chunk
+// position is issued before the first add.
+template <bool kInF32, bool kOutF32, int KM>
 __global__ void __launch_bounds__(256) combine_kernel(const void* __restrict__ yp,
                                                       const int32_t* __restrict__ dst_row,
                                                       const float* __restrict__ w, int T, int h,
@@ -109,41 +136,69 @@ __global__ void __launch_bounds__(256) combine_kernel(const void* __restrict__ y
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
   if (t >= T) return;
-  int rows[MOE_MAX_TOPK];
-  float wt[MOE_MAX_TOPK];
-  for (int j = 0; j < k; ++j) {
-    rows[j] = dst_row[size_t(t) * k + j];
-    wt[j] = w ? w[size_t(t) * k + j] : 1.f;
-  }
-  const int nch = h / 8;  // 8 elements per step (two 16-byte chunks for fp32)
-  for (int c = lane; c < nch; c += 64) {
-    float acc[8];
+  int rows[KM];
+  float wt[KM];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) acc[i] = 0.f;
-    for (int j = 0; j < k; ++j) {
-      if (rows[j] < 0 || rows[j] >= T * k) continue;
-      float f[8];
-      if (kInF32) {
-        const f32x4* p = reinterpret_cast<const f32x4*>(static_cast<const float*>(yp) + size_t(rows[j]) * h + c * 8);
-        f32x4 a = p[0], b = p[1];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) { f[i] = a[i]; f[4 + i] = b[i]; }
-      } else {
-        u32x4 v = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(yp) + size_t(rows[j]) * h)[c];
-        unpack8(v, f);
-      }
-#pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] = fmaf(wt[j], f[i], acc[i]);
+  for (int j = 0; j < KM; ++j) {
+    rows[j] = -1;
+    wt[j] = 0.f;
+    if (j < k) {
+      const int r = dst_row[size_t(t) * k + j];
+      rows[j] = (r < 0 || r >= T * k) ? -1 : r;
+      wt[j] = w ? w[size_t(t) * k + j] : 1.f;
     }
-    if (kOutF32) {
-      f32x4* p = reinterpret_cast<f32x4*>(static_cast<float*>(y) + size_t(t) * h + c * 8);
-      p[0] = f32x4{acc[0], acc[1], acc[2], acc[3]};
-      p[1] = f32x4{acc[4], acc[5], acc[6], acc[7]};
-    } else {
-      u32x4 o;
+  }
+  constexpr int kBatch = KM <= 2 ? 8 : (16 / KM > 0 ? 16 / KM : 1);  // ~16 loads in flight
+  constexpr int kVec = kInF32 ? 2 : 1;     // 16-byte loads per 8 elements
+  const int nch = h / 8;
+  for (int c0 = lane; c0 < nch; c0 += 64 * kBatch) {
+    u32x4 v[kBatch][KM][kVec];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) o[i] = pack_bf16x2(acc[2 * i], acc[2 * i + 1]);
-      reinterpret_cast<u32x4*>(static_cast<uint16_t*>(y) + size_t(t) * h)[c] = o;
+    for (int b = 0; b < kBatch; ++b)
+#pragma unroll
+      for (int j = 0; j < KM; ++j)
+#pragma unroll
+        for (int q = 0; q < kVec; ++q) {
+          v[b][j][q] = u32x4{0, 0, 0, 0};
+          const int c = c0 + 64 * b;
+          if (rows[j] >= 0 && c < nch) {
+            const char* base = static_cast<const char*>(yp) + size_t(rows[j]) * h * (kInF32 ? 4 : 2);
+            v[b][j][q] = reinterpret_cast<const u32x4*>(base)[c * kVec + q];
+          }
+        }
+#pragma unroll
+    for (int b = 0; b < kBatch; ++b) {
+      const int c = c0 + 64 * b;
+      if (c >= nch) break;
+      float acc[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+#pragma unroll
+      for (int j = 0; j < KM; ++j) {
+        if (rows[j] < 0) continue;
+        float f[8];
+        if (kInF32) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            f[i] = __uint_as_float(v[b][j][0][i]);
+            f[4 + i] = __uint_as_float(v[b][j][kVec - 1][i]);
+          }
+        } else {
+          unpack8(v[b][j][0], f);
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] = fmaf(wt[j], f[i], acc[i]);
+      }
+      if (kOutF32) {
+        f32x4* p = reinterpret_cast<f32x4*>(static_cast<float*>(y) + size_t(t) * h + c * 8);
+        p[0] = f32x4{acc[0], acc[1], acc[2], acc[3]};
+        p[1] = f32x4{acc[4], acc[5], acc[6], acc[7]};
+      } else {
+        u32x4 o;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[i] = pack_bf16x2(acc[2 * i], acc[2 * i + 1]);
+        reinterpret_cast<u32x4*>(static_cast<uint16_t*>(y) + size_t(t) * h)[c] = o;
+      }
     }
   }
 }
@@ -172,20 +227,32 @@ int permute_rows(const void* src, int src_dt, const int32_t* dst_row, const floa
   return launch_status();
 }
 
+template <bool in32, bool out32>
+static void launch_combine(dim3 grid, dim3 block, const void* yp, const int32_t* dst_row,
+                           const float* w, int T, int h, int k, void* y, hipStream_t s) {
+  if (k <= 1)
+    hipLaunchKernelGGL((combine_kernel<in32, out32, 1>), grid, block, 0, s, yp, dst_row, w, T, h, k, y);
+  else if (k <= 2)
+    hipLaunchKernelGGL((combine_kernel<in32, out32, 2>), grid, block, 0, s, yp, dst_row, w, T, h, k, y);
+  else if (k <= 4)
+    hipLaunchKernelGGL((combine_kernel<in32, out32, 4>), grid, block, 0, s, yp, dst_row, w, T, h, k, y);
+  else if (k <= 8)
+    hipLaunchKernelGGL((combine_kernel<in32, out32, 8>), grid, block, 0, s, yp, dst_row, w, T, h, k, y);
+  else
+    hipLaunchKernelGGL((combine_kernel<in32, out32, MOE_MAX_TOPK>), grid, block, 0, s, yp, dst_row, w,
+                       T, h, k, y);
+}
+
 int combine_rows(const void* yp, int yp_dt, const int32_t* dst_row, const float* w, int T, int h,
                  int k, void* y, int y_dt, hipStream_t s) {
   if (T == 0) return MOE_OK;
   dim3 grid(ceil_div(T, kRowsPerBlock)), block(256);
-  bool in32 = yp_dt == MOE_F32, out32 = y_dt == MOE_F32;
+  const bool in32 = yp_dt == MOE_F32, out32 = y_dt == MOE_F32;
   timer_begin(kTCombine, s);
-  if (in32 && out32)
-    hipLaunchKernelGGL((combine_kernel<true, true>), grid, block, 0, s, yp, dst_row, w, T, h, k, y);
-  else if (in32)
-    hipLaunchKernelGGL((combine_kernel<true, false>), grid, block, 0, s, yp, dst_row, w, T, h, k, y);
-  else if (out32)
-    hipLaunchKernelGGL((combine_kernel<false, true>), grid, block, 0, s, yp, dst_row, w, T, h, k, y);
-  else
-    hipLaunchKernelGGL((combine_kernel<false, false>), grid, block, 0, s, yp, dst_row, w, T, h, k, y);
+  if (in32 && out32) launch_combine<true, true>(grid, block, yp, dst_row, w, T, h, k, y, s);
+  else if (in32) launch_combine<true, false>(grid, block, yp, dst_row, w, T, h, k, y, s);
+  else if (out32) launch_combine<false, true>(grid, block, yp, dst_row, w, T, h, k, y, s);
+  else launch_combine<false, false>(grid, block, yp, dst_row, w, T, h, k, y, s);
   timer_end(kTCombine, s);
   return launch_status();
 }

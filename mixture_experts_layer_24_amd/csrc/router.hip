@@ -6,20 +6,14 @@
 // the k kept logits and the tie rule (lower expert index first) are this
 // library's reading of the unspecified details.
 //
-// One workgroup of 256 threads handles 128 tokens.  BF16: the logits come
-// from MFMA 32x32x16 (each wave 32 tokens x all experts), reading x straight
-// from HBM in 16-byte loads and the gate weight through LDS in K slabs,
-// transposed so both operands are K-contiguous.  The 128 x E fp32 logits then
-// go to LDS and one thread per token selects its k experts.
+// BF16: logits on MFMA with x read once from HBM and W_g transposed through
+// LDS (see route_bf16_kernel); FP32 (small workloads) and given logits: a
+// plain dot-product kernel.  Top-k is one thread per token over its E logits.
 #include "common.h"
 
 namespace moe {
 
-constexpr int kRouteTokens = 128;
-constexpr int kRouteSlab = 64;  // K elements per LDS slab
-
-// LDS slab for W_g^T: [E_pad][kRouteSlab + 8] bf16 (row padded by 16 B).
-constexpr int kSlabStride = kRouteSlab + 8;
+constexpr int kRouteTokens = 128;  // tokens per workgroup of the generic kernel
 
 __device__ __forceinline__ void topk_select(const float* L, int E, int k, int32_t* idx_out,
                                             float* w_out) {
@@ -50,7 +44,19 @@ __device__ __forceinline__ void topk_select(const float* L, int E, int k, int32_
   }
 }
 
-template <int NT>  // NT = ceil(E / 32) expert tiles of 32
+// BF16 logits on MFMA 32x32x16: one workgroup of four waves per 32 tokens;
+// wave w takes the K range [w h/4, (w+1) h/4) in 64-element chunks.
+// x goes straight from HBM into A fragments (64 contiguous bytes per lane
+// per chunk).  The chunk's 64 rows of W_g are one contiguous block: the wave
+// reads it in 16-byte loads and writes it transposed into its own LDS region
+// ([expert][k], 144-byte rows), from where each lane's B fragment is one
+// 16-byte read.  The four partial 32 x E tiles are summed in LDS in wave
+// order, the bias added, and one thread per token picks its k experts.
+constexpr int kRtTokens = 32;
+constexpr int kRtChunk = 64;                // K elements per chunk
+constexpr int kRtStride = kRtChunk + 8;     // bf16 per LDS row of W^T
+
+template <int NT>  // NT = ceil(E / 32) expert blocks of 32
 __global__ void __launch_bounds__(256) route_bf16_kernel(const uint16_t* __restrict__ x,
                                                          const uint16_t* __restrict__ wg,
                                                          const float* __restrict__ bias,
@@ -59,16 +65,14 @@ __global__ void __launch_bounds__(256) route_bf16_kernel(const uint16_t* __restr
                                                          int32_t* __restrict__ topk_idx,
                                                          float* __restrict__ topk_w) {
   extern __shared__ __align__(16) unsigned char smem[];
-  uint16_t* slab = reinterpret_cast<uint16_t*>(smem);  // [NT*32][kSlabStride]
-  float* lg = reinterpret_cast<float*>(smem);          // [128][E+1] after the GEMM
-
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  const int t0 = blockIdx.x * kRouteTokens;
-  const int row = t0 + wave * 32 + (lane & 31);
-  const int half = lane >> 5;
+  const int half = lane >> 5, l32 = lane & 31;
+  const int t0 = blockIdx.x * kRtTokens;
+  const int row = t0 + l32;
   const int rowc = row < T ? row : T - 1;
-  const uint16_t* xr = x + size_t(rowc) * h + half * 32;
+  // this wave's W^T region: [NT*32][kRtStride] bf16
+  uint16_t* wt = reinterpret_cast<uint16_t*>(smem) + size_t(wave) * NT * 32 * kRtStride;
 
   f32x16 acc[NT];
 #pragma unroll
@@ -76,54 +80,73 @@ __global__ void __launch_bounds__(256) route_bf16_kernel(const uint16_t* __restr
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[n][r] = 0.f;
 
-  const int Ep = NT * 32;
-  for (int k0 = 0; k0 < h; k0 += kRouteSlab) {
-    // x: 64 contiguous bytes per lane (4 x 16 B) at k0 + 32*half.
+  const int kw = h / 4;  // h is a multiple of 64, so kw of 16
+  const int kbeg = wave * kw;
+  const uint16_t* xr = x + size_t(rowc) * h + half * 32;
+  for (int kc = kbeg; kc < kbeg + kw; kc += kRtChunk) {
+    const int kn = kbeg + kw - kc < kRtChunk ? kbeg + kw - kc : kRtChunk;  // 16, 32, 48 or 64
     u32x4 xa[4];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) xa[s] = *reinterpret_cast<const u32x4*>(xr + k0 + s * 8);
-    __syncthreads();  // previous slab fully consumed
-    for (int q = tid; q < kRouteSlab * Ep; q += 256) {
-      int kk = q / Ep, e = q - kk * Ep;
-      uint16_t v = e < E ? wg[size_t(k0 + kk) * E + e] : uint16_t(0);
-      slab[e * kSlabStride + kk] = v;
+    for (int s = 0; s < 4; ++s)
+      xa[s] = (half * 32 + s * 8 < kn) ? *reinterpret_cast<const u32x4*>(xr + kc + s * 8)
+                                       : u32x4{0, 0, 0, 0};
+    __syncthreads();  // previous chunk's fragments read out of wt
+    // W_g rows kc .. kc+kn-1 are kn*E contiguous values: 16-byte units
+    const uint16_t* src = wg + size_t(kc) * E;
+    const int units = kn * E / 8;
+    for (int u = lane; u < units; u += 64) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(src + size_t(u) * 8);
+      int q = u * 8, kk = q / E, e = q - kk * E;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        wt[e * kRtStride + kk] = uint16_t(v[i >> 1] >> (16 * (i & 1)));
+        if (++e == E) { e = 0; ++kk; }
+      }
     }
     __syncthreads();
 #pragma unroll
     for (int n = 0; n < NT; ++n) {
-      const uint16_t* br = slab + (n * 32 + (lane & 31)) * kSlabStride + half * 32;
+      const int e = n * 32 + l32;
+      const uint16_t* br = wt + e * kRtStride + half * 32;
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        u32x4 b = *reinterpret_cast<const u32x4*>(br + s * 8);
+        u32x4 b = (e < E && half * 32 + s * 8 < kn) ? *reinterpret_cast<const u32x4*>(br + s * 8)
+                                                   : u32x4{0, 0, 0, 0};
         acc[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
             __builtin_bit_cast(bf16x8, xa[s]), __builtin_bit_cast(bf16x8, b), acc[n], 0, 0, 0);
       }
     }
   }
   __syncthreads();
-  const int ls = E + 1;
+  // partial tiles -> LDS [wave][token][E], then sum in wave order
+  float* part = reinterpret_cast<float*>(smem);
 #pragma unroll
   for (int n = 0; n < NT; ++n) {
-    int e = n * 32 + (lane & 31);
+    const int e = n * 32 + l32;
     if (e < E) {
-      float b = bias ? bias[e] : 0.f;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        int i = wave * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-        lg[i * ls + e] = acc[n][r] + b;
+        const int i = 8 * (r >> 2) + 4 * half + (r & 3);
+        part[(wave * kRtTokens + i) * E + e] = acc[n][r];
       }
     }
   }
   __syncthreads();
-  if (logits_out) {
-    for (int q = tid; q < kRouteTokens * E; q += 256) {
-      int i = q / E, e = q - i * E;
-      if (t0 + i < T) logits_out[size_t(t0 + i) * E + e] = lg[i * ls + e];
-    }
+  // the sum replaces wave 0's partial in place: logits [32][E]
+  for (int q = tid; q < kRtTokens * E; q += 256) {
+    float v = part[q];
+    v += part[kRtTokens * E + q];
+    v += part[2 * kRtTokens * E + q];
+    v += part[3 * kRtTokens * E + q];
+    const int i = q / E, e = q - i * E;
+    if (bias) v += bias[e];
+    part[q] = v;
+    if (logits_out && t0 + i < T) logits_out[size_t(t0) * E + q] = v;
   }
-  if (tid < kRouteTokens && t0 + tid < T) {
-    int t = t0 + tid;
-    topk_select(lg + tid * ls, E, k, topk_idx + size_t(t) * k, topk_w + size_t(t) * k);
+  __syncthreads();
+  if (tid < kRtTokens && t0 + tid < T) {
+    const int t = t0 + tid;
+    topk_select(part + tid * E, E, k, topk_idx + size_t(t) * k, topk_w + size_t(t) * k);
   }
 }
 
@@ -171,12 +194,12 @@ using namespace moe;
 template <int NT>
 static void launch_route_bf16(const void* x, const void* wg, const float* bias, float* logits,
                               int T, int h, int E, int k, int32_t* idx, float* w, hipStream_t s) {
-  size_t slab = size_t(NT * 32) * kSlabStride * 2;
-  size_t lgb = size_t(kRouteTokens) * (E + 1) * 4;
-  size_t shm = slab > lgb ? slab : lgb;
+  const size_t wtb = size_t(4) * NT * 32 * kRtStride * 2;
+  const size_t redb = size_t(4) * kRtTokens * E * 4;
+  const size_t shm = wtb > redb ? wtb : redb;
   static bool ok = allow_lds(route_bf16_kernel<NT>, 160 * 1024);
   (void)ok;
-  hipLaunchKernelGGL(route_bf16_kernel<NT>, dim3(ceil_div(T, kRouteTokens)), dim3(256), shm, s,
+  hipLaunchKernelGGL(route_bf16_kernel<NT>, dim3(ceil_div(T, kRtTokens)), dim3(256), shm, s,
                      (const uint16_t*)x, (const uint16_t*)wg, bias, logits, T, h, E, k, idx, w);
 }
 
