@@ -455,3 +455,66 @@ def topk_margin(logits: np.ndarray, k: int) -> np.ndarray:
     if k >= L.shape[1]:
         return np.full(L.shape[0], np.inf)
     return L[:, k - 1] - L[:, k]
+
+
+# --------------------------------------------------------------------------
+# Router backward and the load-balance loss.  [MSR] §三 (MoE layer
+# structure): the gating network is trainable, so W_g (and the router bias)
+# get gradients through the gate weights of the combine.  [MSD] §3.2 (the
+# discussion of Figure 7): load balance uses an auxiliary loss "as in
+# DeepSeek-V2".  The pages print no formula; the reading taken is
+# DeepSeek-V2's expert-level balance loss
+#     L_aux = alpha * sum_e f_e * P_e,
+#     f_e   = E / (k T) * (number of (token, slot) pairs routed to e),
+#     P_e   = (1/T) * sum_t softmax(L_t)_e      (softmax over all E logits),
+# with f_e a count (no gradient) and P_e differentiable.  Routing (the top-k
+# selection) is piecewise constant in the logits and is held fixed.
+# --------------------------------------------------------------------------
+
+def softmax_rows(logits: np.ndarray) -> np.ndarray:
+    """Softmax over the last axis in fp64 (max subtracted first)."""
+    L = np.asarray(logits, np.float64)
+    z = np.exp(L - L.max(axis=-1, keepdims=True))
+    return z / z.sum(axis=-1, keepdims=True)
+
+
+def aux_balance_loss(logits: np.ndarray, idx: np.ndarray, E: int, k: int, alpha: float) -> float:
+    """``alpha * sum_e f_e P_e`` for the routing ``idx`` of these logits."""
+    T = logits.shape[0]
+    counts = np.bincount(np.asarray(idx).ravel(), minlength=E).astype(np.float64)
+    f = E / (k * T) * counts
+    P = softmax_rows(logits).mean(axis=0)
+    return float(alpha * np.sum(f * P))
+
+
+def router_backward(dy, ysel, x, w_gate, logits, idx, w, alpha):
+    """Gradients of ``sum_t <dy_t, y_t> + L_aux`` through the router.
+
+    ``ysel[t, j]`` is the output of expert ``idx[t, j]`` for token t (the row
+    ``Yp[dst_row[t, j]]``).  With ``y_t = sum_j w_tj ysel[t, j]`` and
+    ``w_t = softmax(L_t[idx_t])``:
+        dw[t, j]       = <dy_t, ysel[t, j]>
+        dL[t, idx_tj] += w_tj (dw_tj - sum_i w_ti dw_ti)       (top-k softmax)
+        dL[t, e]      += s_te (g_e - sum_e' s_te' g_e')        (aux loss)
+    with s_t = softmax(L_t) over all experts and g_e = alpha f_e / T.  Then
+    dW_g = x^T dL, the router's share of dX is dL W_g^T, and d(bias) = sum_t dL.
+    Returns a dict with dw, dL, dw_gate, dx, dbias (fp64)."""
+    dy = np.asarray(dy, np.float64)
+    ysel = np.asarray(ysel, np.float64)
+    x = np.asarray(x, np.float64)
+    wg = np.asarray(w_gate, np.float64)
+    L = np.asarray(logits, np.float64)
+    w = np.asarray(w, np.float64)
+    T, E = L.shape
+    k = idx.shape[1]
+    dw = np.einsum("th,tjh->tj", dy, ysel)
+    dL = np.zeros((T, E))
+    inner = np.sum(w * dw, axis=1)
+    for j in range(k):
+        dL[np.arange(T), idx[:, j]] += w[:, j] * (dw[:, j] - inner)
+    if alpha != 0.0:
+        counts = np.bincount(np.asarray(idx).ravel(), minlength=E).astype(np.float64)
+        g = alpha * (E / (k * T) * counts) / T
+        s = softmax_rows(L)
+        dL += s * (g[None, :] - (s @ g)[:, None])
+    return {"dw": dw, "dL": dL, "dw_gate": x.T @ dL, "dx": dL @ wg.T, "dbias": dL.sum(axis=0)}
