@@ -3,7 +3,8 @@
 
 A step is the whole hot path on one batch: route (gate GEMM + top-k softmax)
 -> dispatch (index build + permute) -> grouped SwiGLU GEMMs -> weighted
-combine, plus the backward for workloads that train.  Inputs are seeded,
+combine, plus, for workloads that train, the load-balance loss and the backward
+(experts and router).  Inputs are seeded,
 synthetic and already resident in HBM when the timed region starts; weights
 are packed once before it.
 
@@ -24,6 +25,7 @@ if ROOT not in sys.path:
 PEAK = {"bf16": 2.5e15, "fp8": 5.0e15, "f32": 157.3e12}   # dense MFMA FLOP/s, MI355X
 HBM_PEAK = 8.0e12                                          # B/s
 METRIC = "MoE layer tokens/s and GroupedGEMM TFLOP/s (% of MFMA peak) on 1 MI355X"
+AUX_ALPHA = 0.01  # weight of the load-balance loss in training steps
 
 
 def log(*a):
@@ -79,8 +81,11 @@ def cpu_baseline(wl, inp, n_tokens, seed=0):
         out = ref.layer_forward(x, wg, inp["bias"], w1, w3, w2, wl.k)
         if wl.backward:
             dy = to_f32(inp["dy"][:n_tokens])
+            ref.aux_balance_loss(out["logits"], out["idx"], wl.E, wl.k, AUX_ALPHA)
             ref.layer_backward(dy, x, out["w"], out["dst_row"], out["offsets"], w1, w3, w2,
                                g=out["g"], u=out["u"])
+            ref.router_backward(dy, out["yp"][out["dst_row"]], x, wg, out["logits"], out["idx"],
+                                out["w"], AUX_ALPHA)
     dt = time.perf_counter() - t0
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     return {"value": n_tokens / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
@@ -146,7 +151,8 @@ def main():
     def step():
         layer.forward(x, wg, bias, P)
         if wl.backward:
-            layer.backward(dy, x, P)
+            layer.aux_loss(AUX_ALPHA)
+            layer.backward(dy, x, P, w_gate=wg, alpha=AUX_ALPHA)
 
     log(f"bench: warmup {args.warmup}")
     for _ in range(args.warmup):

@@ -231,6 +231,49 @@ int moe_combine(const void* yp, int yp_dtype, const int32_t* dst_row, const floa
                 int h, int k, void* y, int y_dtype, void* stream);
 
 /*
+ * Router backward: gradients of  sum_t <dY_t, y_t> + L_aux  through the gate
+ * (MegaScale-MoE paper review, §三 MoE layer structure: the gating network is
+ * trainable), with the top-k selection held fixed.  For each token t,
+ *   dw[t][j]      = <dy[t], yp[dst_row[t][j]]>                 (fp32 sum over h)
+ *   dL[t][idx_j] += w_j (dw_j - sum_i w_i dw_i)                (softmax over the top k)
+ *   dL[t][e]     += s_te (g_e - sum_e' s_te' g_e')             (balance loss, alpha != 0)
+ * with s_t = softmax(logits[t]) over all E experts and
+ * g_e = alpha * E / (k T) * counts[e] / T (see moe_router_aux_loss).  Then
+ *   dw_gate = x^T dL,   dbias = sum_t dL[t],   dx = dx_in + dL W_g^T.
+ *   dy, yp   [T][h], [T*k][h] element type dtype (MOE_BF16 or MOE_F32): the
+ *            upstream gradient and the forward's expert outputs.
+ *   dst_row, topk_idx [T][k] int32, topk_w [T][k] fp32, logits [T][E] fp32
+ *            (bias included), counts [E] int32: the forward's routing.
+ *   x [T][h], w_gate [h][E]: dtype.
+ *   dx_in    [T][h] fp32 (the expert path's dX, e.g. from moe_combine with
+ *            y_dtype MOE_F32) or NULL for zero; dx [T][h] out, dtype (may not
+ *            alias dx_in).
+ *   dlogits  [T][E] fp32 out, or NULL (then dL stays in the workspace).
+ *   dw_gate  [h][E] fp32 out; dbias [E] fp32 out or NULL.
+ *   h must be a multiple of 64.  Every sum over tokens runs in a fixed order:
+ *   results are bit-for-bit repeatable.
+ */
+size_t moe_router_bwd_workspace_size(int T, int h, int E);
+int moe_router_bwd(const void* dy, const void* yp, const int32_t* dst_row, const int32_t* topk_idx,
+                   const float* topk_w, const float* logits, const int32_t* counts, int T, int h,
+                   int E, int k, float alpha, int dtype, const void* x, const void* w_gate,
+                   const float* dx_in, void* dx, float* dlogits, float* dw_gate, float* dbias,
+                   void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Load-balance loss (MegaScale-MoE research digest §3.2: an auxiliary loss
+ * balances the experts, as in DeepSeek-V2; the digest prints no formula, and
+ * DeepSeek-V2's expert-level form is used):
+ *   loss = alpha * sum_e f_e P_e,  f_e = E / (k T) * counts[e],
+ *   P_e  = (1/T) sum_t softmax(logits[t])_e.
+ *   logits [T][E] fp32, counts [E] int32 (from moe_permute), loss: one fp32
+ *   written on the device.  T >= 1.
+ */
+size_t moe_router_aux_workspace_size(int T, int E);
+int moe_router_aux_loss(const float* logits, const int32_t* counts, int T, int E, int k,
+                        float alpha, float* loss, void* ws, size_t ws_bytes, void* stream);
+
+/*
  * Kernel timing for benchmarks.  moe_timing_enable(1) starts recording a pair
  * of HIP events around every kernel this library launches (on the launch
  * stream); moe_timing_enable(0) stops.  moe_timing_report() waits for the

@@ -24,6 +24,7 @@ MOE_MAX_TOPK = 16
 P = ctypes.c_void_p
 I = ctypes.c_int
 SZ = ctypes.c_size_t
+F = ctypes.c_float
 
 
 class MoeWeights(ctypes.Structure):
@@ -43,6 +44,10 @@ SIGNATURES = {
     "moe_grouped_bwd_workspace_size": (SZ, [I, I, I, I, I]),
     "moe_grouped_swiglu_bwd": (I, [P, P, P, ctypes.POINTER(MoeWeights), P, I, P, P, P, P, P, SZ, P]),
     "moe_combine": (I, [P, I, P, P, I, I, I, P, I, P]),
+    "moe_router_bwd_workspace_size": (SZ, [I, I, I]),
+    "moe_router_bwd": (I, [P, P, P, P, P, P, P, I, I, I, I, F, I, P, P, P, P, P, P, P, P, SZ, P]),
+    "moe_router_aux_workspace_size": (SZ, [I, I]),
+    "moe_router_aux_loss": (I, [P, P, I, I, I, F, P, P, SZ, P]),
     "moe_timing_enable": (I, [I]),
     "moe_timing_report": (I, [ctypes.c_char_p, SZ]),
     "moe_last_error": (ctypes.c_char_p, []),

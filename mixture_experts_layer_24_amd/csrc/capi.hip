@@ -66,7 +66,7 @@ extern "C" {
 
 const char* moe_last_error(void) { return g_err; }
 
-int moe_version(void) { return 1; }
+int moe_version(void) { return 2; }
 
 size_t moe_packed_weight_bytes(int which, int E, int h, int h_ffn, int dtype) {
   if (E <= 0 || h <= 0 || h_ffn <= 0 || dtype < MOE_F32 || dtype > MOE_FP8_E4M3) return 0;
@@ -253,6 +253,58 @@ int moe_combine(const void* yp, int yp_dtype, const int32_t* dst_row, const floa
   return launched(moe_launch::combine_rows(yp, yp_dtype, dst_row, topk_w, T, h, k, y, y_dtype,
                                            (hipStream_t)stream),
                   "moe_combine");
+}
+
+size_t moe_router_bwd_workspace_size(int T, int h, int E) {
+  if (T <= 0 || h <= 0 || E <= 0) return 0;
+  return moe_launch::router_bwd_ws_bytes(T, h, E);
+}
+
+int moe_router_bwd(const void* dy, const void* yp, const int32_t* dst_row, const int32_t* topk_idx,
+                   const float* topk_w, const float* logits, const int32_t* counts, int T, int h,
+                   int E, int k, float alpha, int dtype, const void* x, const void* w_gate,
+                   const float* dx_in, void* dx, float* dlogits, float* dw_gate, float* dbias,
+                   void* ws, size_t ws_bytes, void* stream) {
+  REQ(T >= 0, MOE_ERR_ARG, "T=%d is negative", T);
+  REQ(E >= 1 && E <= MOE_MAX_EXPERTS, MOE_ERR_SHAPE, "E=%d outside [1, %d]", E, MOE_MAX_EXPERTS);
+  REQ(k >= 1 && k <= MOE_MAX_TOPK && k <= E, MOE_ERR_ARG, "k=%d outside [1, min(E, %d)]", k,
+      MOE_MAX_TOPK);
+  REQ(h > 0 && h % 64 == 0, MOE_ERR_SHAPE, "h=%d must be a positive multiple of 64", h);
+  REQ(dtype == MOE_F32 || dtype == MOE_BF16, MOE_ERR_DTYPE, "router backward dtype %d unsupported",
+      dtype);
+  REQ(alpha == alpha, MOE_ERR_ARG, "alpha is NaN");
+  PTR(dy); PTR(yp); PTR(dst_row); PTR(topk_idx); PTR(topk_w); PTR(logits); PTR(counts);
+  PTR(x); PTR(w_gate); PTR(dx); PTR(dw_gate); OPT(dx_in); OPT(dlogits); OPT(dbias);
+  REQ(static_cast<const void*>(dx_in) != dx, MOE_ERR_ARG, "dx may not alias dx_in");
+  if (T == 0) return MOE_OK;
+  const size_t need = moe_launch::router_bwd_ws_bytes(T, h, E);
+  REQ(ws != nullptr && ws_bytes >= need, MOE_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given",
+      need, ws ? ws_bytes : size_t(0));
+  moe_launch::clear_status();
+  return launched(moe_launch::router_bwd(dy, yp, dst_row, topk_idx, topk_w, logits, counts, T, h, E,
+                                         k, alpha, dtype, x, w_gate, dx_in, dx, dlogits, dw_gate,
+                                         dbias, ws, (hipStream_t)stream),
+                  "moe_router_bwd");
+}
+
+size_t moe_router_aux_workspace_size(int T, int E) {
+  if (T <= 0 || E <= 0) return 0;
+  return moe_launch::router_aux_ws_bytes(T, E);
+}
+
+int moe_router_aux_loss(const float* logits, const int32_t* counts, int T, int E, int k,
+                        float alpha, float* loss, void* ws, size_t ws_bytes, void* stream) {
+  REQ(T >= 1, MOE_ERR_ARG, "T=%d must be positive", T);
+  REQ(E >= 1 && E <= MOE_MAX_EXPERTS, MOE_ERR_SHAPE, "E=%d outside [1, %d]", E, MOE_MAX_EXPERTS);
+  REQ(k >= 1 && k <= MOE_MAX_TOPK && k <= E, MOE_ERR_ARG, "k=%d outside [1, min(E, %d)]", k,
+      MOE_MAX_TOPK);
+  PTR(logits); PTR(counts); PTR(loss);
+  const size_t need = moe_launch::router_aux_ws_bytes(T, E);
+  REQ(ws != nullptr && ws_bytes >= need, MOE_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given",
+      need, ws ? ws_bytes : size_t(0));
+  moe_launch::clear_status();
+  return launched(moe_launch::router_aux(logits, counts, T, E, k, alpha, loss, ws, (hipStream_t)stream),
+                  "moe_router_aux_loss");
 }
 
 }  // extern "C"

@@ -106,6 +106,15 @@ int grouped_bwd(const void* dyp, const void* xp, const void* h13_save, const moe
                 const int32_t* offsets, int rows, void* dxp, float* dw1, float* dw3, float* dw2,
                 void* ws, hipStream_t s);
 size_t grouped_bwd_ws_bytes(int rows, int h, int h_ffn, int E, int dtype);
+int router_bwd(const void* dy, const void* yp, const int32_t* dst_row, const int32_t* topk_idx,
+               const float* topk_w, const float* logits, const int32_t* counts, int T, int h,
+               int E, int k, float alpha, int dtype, const void* x, const void* w_gate,
+               const float* dx_in, void* dx, float* dlogits, float* dw_gate, float* dbias,
+               void* ws, hipStream_t s);
+size_t router_bwd_ws_bytes(int T, int h, int E);
+int router_aux(const float* logits, const int32_t* counts, int T, int E, int k, float alpha,
+               float* loss, void* ws, hipStream_t s);
+size_t router_aux_ws_bytes(int T, int E);
 int pack_weights(const void* w1, const void* w3, const void* w2, int in_dt, int E, int h,
                  int h_ffn, int out_dt, void* w13, void* w2p, float* w13_scale, float* w2_scale,
                  void* w13_bwd, void* w2_bwd, hipStream_t s);
@@ -121,7 +130,7 @@ const char* last_hip_error();
 // Optional per-kernel timing: when enabled (moe_timing_enable), a pair of HIP
 // events is recorded on the launch stream around every kernel of the layer.
 enum TimerId { kTRoute = 0, kTIndex, kTPermute, kTFc1, kTQuant, kTFc2, kTCombine, kTBwd1, kTBwd2,
-               kTBwd3, kTBwd4, kTPack, kTXpose, kNumTimers };
+               kTBwd3, kTBwd4, kTPack, kTXpose, kTRouterBwd, kTRouterAux, kNumTimers };
 void timer_begin(int id, hipStream_t s);
 void timer_end(int id, hipStream_t s);
 }  // namespace moe_launch

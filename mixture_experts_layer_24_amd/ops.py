@@ -87,6 +87,27 @@ def moe_combine(yp, yp_dtype, dst_row, topk_w, T, h, k, y, y_dtype, stream=None)
                                    y_dtype, _s(stream)))
 
 
+def moe_router_bwd_workspace_size(T, h, E):
+    return lib().moe_router_bwd_workspace_size(T, h, E)
+
+
+def moe_router_bwd(dy, yp, dst_row, topk_idx, topk_w, logits, counts, T, h, E, k, alpha, dtype, x,
+                   w_gate, dx_in, dx, dlogits, dw_gate, dbias, ws, ws_bytes, stream=None):
+    return check(lib().moe_router_bwd(_p(dy), _p(yp), _p(dst_row), _p(topk_idx), _p(topk_w),
+                                      _p(logits), _p(counts), T, h, E, k, float(alpha), dtype, _p(x),
+                                      _p(w_gate), _p(dx_in), _p(dx), _p(dlogits), _p(dw_gate),
+                                      _p(dbias), _p(ws), ws_bytes, _s(stream)))
+
+
+def moe_router_aux_workspace_size(T, E):
+    return lib().moe_router_aux_workspace_size(T, E)
+
+
+def moe_router_aux_loss(logits, counts, T, E, k, alpha, loss, ws, ws_bytes, stream=None):
+    return check(lib().moe_router_aux_loss(_p(logits), _p(counts), T, E, k, float(alpha), _p(loss),
+                                           _p(ws), ws_bytes, _s(stream)))
+
+
 def moe_last_error() -> str:
     return lib().moe_last_error().decode()
 
@@ -161,9 +182,11 @@ class MoELayer:
         if logits_in is None:
             moe_route(x, w_gate, bias, self.logits, T, h, E, k, dtype_code(x), self.topk_idx,
                       self.topk_w, stream)
+            self.logits_used = self.logits
         else:
             moe_route(None, None, None, logits_in, T, h, E, k, dtype_code(logits_in),
                       self.topk_idx, self.topk_w, stream)
+            self.logits_used = logits_in
         moe_permute(x, dtype_code(x), self.topk_idx, None, T, h, E, k, self.counts, self.offsets,
                     self.dst_row, self.src_tok, self.xp, self.dtype, self.xp_scale, self.pws,
                     self.pws_bytes, stream)
@@ -186,7 +209,30 @@ class MoELayer:
         self.bws = torch.empty(max(self.bws_bytes, 256), dtype=torch.uint8, device=dev)
         self.bwd_ready = True
 
-    def backward(self, dy, x, W: PackedWeights, stream=None):
+    def aux_loss(self, alpha, stream=None):
+        """Load-balance loss of the last forward's routing (a device scalar)."""
+        if not hasattr(self, "aux_ws"):
+            self.aux_ws_bytes = moe_router_aux_workspace_size(self.T, self.E)
+            self.aux_ws = torch.empty(max(self.aux_ws_bytes, 256), dtype=torch.uint8, device=self.y.device)
+            self.aux = torch.empty(4, dtype=torch.float32, device=self.y.device)
+        moe_router_aux_loss(self.logits_used, self.counts, self.T, self.E, self.k, alpha, self.aux,
+                            self.aux_ws, self.aux_ws_bytes, stream)
+        return self.aux[0]
+
+    def _alloc_router_bwd(self):
+        dev, T, h, E = self.y.device, self.T, self.h, self.E
+        f32 = dict(dtype=torch.float32, device=dev)
+        self.dx_expert = torch.empty(T, h, **f32)
+        self.dlogits = torch.empty(T, E, **f32)
+        self.dw_gate = torch.empty(h, E, **f32)
+        self.dbias = torch.empty(E, **f32)
+        self.rws_bytes = moe_router_bwd_workspace_size(T, h, E)
+        self.rws = torch.empty(max(self.rws_bytes, 256), dtype=torch.uint8, device=dev)
+
+    def backward(self, dy, x, W: PackedWeights, w_gate=None, alpha=0.0, stream=None):
+        """dX (expert path, plus the router path when ``w_gate`` is given),
+        per-expert dW1/dW3/dW2 and, with ``w_gate``, dW_g / d(bias) / dL
+        including the balance loss of weight ``alpha``."""
         if not self.bwd_ready:
             self._alloc_bwd()
         T, h, E, k = self.T, self.h, self.E, self.k
@@ -198,7 +244,17 @@ class MoELayer:
         moe_grouped_swiglu_bwd(self.dyp, self.xp, self.h13, W.struct, self.offsets, self.R,
                                self.dxp, self.dw1, self.dw3, self.dw2, self.bws, self.bws_bytes,
                                stream)
-        moe_combine(self.dxp, MOE_BF16, self.dst_row, None, T, h, k, self.dx, MOE_BF16, stream)
+        if w_gate is None:
+            moe_combine(self.dxp, MOE_BF16, self.dst_row, None, T, h, k, self.dx, MOE_BF16, stream)
+            return self.dx
+        if not hasattr(self, "dw_gate"):
+            self._alloc_router_bwd()
+        # expert path in fp32, then the router path adds dL W_g^T and rounds once
+        moe_combine(self.dxp, MOE_BF16, self.dst_row, None, T, h, k, self.dx_expert, MOE_F32, stream)
+        moe_router_bwd(dy, self.yp, self.dst_row, self.topk_idx, self.topk_w, self.logits_used,
+                       self.counts, T, h, E, k, alpha, dtype_code(dy), x, w_gate, self.dx_expert,
+                       self.dx, self.dlogits, self.dw_gate, self.dbias, self.rws, self.rws_bytes,
+                       stream)
         return self.dx
 
 

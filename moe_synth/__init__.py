@@ -35,7 +35,9 @@ from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 
-TENSOR_IDS = {"x": 1, "w_gate": 2, "w1": 3, "w3": 4, "w2": 5, "dy": 6}
+TENSOR_IDS = {"x": 1, "w_gate": 2, "w1": 3, "w3": 4, "w2": 5, "dy": 6,
+              # stand-ins for intermediate tensors when one step is tested alone
+              "yp": 7, "dx_in": 8}
 ROW_CHUNK = 1024  # token rows per generator stream for x and dy
 
 
@@ -108,6 +110,11 @@ def _normal(seed, tensor, chunk, shape, std, storage):
     v *= np.float32(std)
     v = v.reshape(shape)
     return f32_to_bf16_bits(v) if storage == "bf16" else v
+
+
+def gen_matrix(tensor: str, shape, std: float = 1.0, storage: str = "bf16", seed: int = 0) -> np.ndarray:
+    """A whole N(0, std^2) tensor from one stream (small test inputs)."""
+    return _normal(seed, tensor, 0, tuple(shape), std, storage)
 
 
 def gen_rows(wl: Workload, tensor: str, rows: np.ndarray, seed: int = 0) -> np.ndarray:

@@ -150,10 +150,12 @@ def sigmoid(z: np.ndarray) -> np.ndarray:
         return 1.0 / (1.0 + np.exp(-z))
 
 
-def expert_forward(xp, offsets, w1, w3, w2, keep=True):
+def expert_forward(xp, offsets, w1, w3, w2, keep=True, bf16_storage=False):
     """FC1 -> SwiGLU -> FC2 for every expert's contiguous rows (fp64).
 
-    Returns ``yp`` and, when ``keep``, the intermediates ``g, u, a``.
+    Returns ``yp`` and, when ``keep``, the intermediates ``g, u, a``.  With
+    ``bf16_storage`` the two values a BF16 layer stores between steps are
+    rounded to bf16 (nearest even): A before FC2, and Yp itself.
     """
     R = xp.shape[0]
     E = len(offsets) - 1
@@ -170,7 +172,11 @@ def expert_forward(xp, offsets, w1, w3, w2, keep=True):
         g = xe @ np.asarray(w1[e], np.float64)
         u = xe @ np.asarray(w3[e], np.float64)
         a = silu(g) * u
+        if bf16_storage:
+            a = round_bf16(a)
         yp[lo:hi] = a @ np.asarray(w2[e], np.float64)
+        if bf16_storage:
+            yp[lo:hi] = round_bf16(yp[lo:hi])
         if keep:
             g_all[lo:hi] = g; u_all[lo:hi] = u; a_all[lo:hi] = a
     if keep:

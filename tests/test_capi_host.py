@@ -26,7 +26,7 @@ def test_exports_every_declared_symbol():
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) <= set(L.SIGNATURES)
-    assert lib.moe_version() == 1
+    assert lib.moe_version() == 2
 
 
 A = ctypes.c_void_p(1 << 20)   # aligned, never dereferenced: validation fails first
@@ -120,3 +120,45 @@ def test_combine_and_pack_validation():
     assert lib.moe_packed_weight_bytes(5, 8, 256, 384, L.MOE_FP8_E4M3) == 0
     assert lib.moe_packed_weight_bytes(0, 8, 256, 384, L.MOE_BF16) == 8 * 768 * 256 * 2
     assert lib.moe_packed_weight_bytes(3, 8, 256, 384, L.MOE_FP8_E4M3) == 8 * 256 * 4
+
+
+def test_router_bwd_validation():
+    lib = L.lib()
+    T, h, E, k = 100, 128, 8, 2
+    need = lib.moe_router_bwd_workspace_size(T, h, E)
+    assert need > 0 and lib.moe_router_bwd_workspace_size(0, h, E) == 0
+    ok = dict(dy=A, yp=A, dst=A, idx=A, w=A, lg=A, cnt=A, T=T, h=h, E=E, k=k, alpha=0.01,
+              dt=L.MOE_BF16, x=A, wg=A, dxin=None, dx=ctypes.c_void_p(2 << 20), dl=None, dwg=A, db=None,
+              ws=A, wsb=need)
+
+    def call(**kw):
+        a = {**ok, **kw}
+        return lib.moe_router_bwd(a["dy"], a["yp"], a["dst"], a["idx"], a["w"], a["lg"], a["cnt"], a["T"],
+                                  a["h"], a["E"], a["k"], a["alpha"], a["dt"], a["x"], a["wg"], a["dxin"],
+                                  a["dx"], a["dl"], a["dwg"], a["db"], a["ws"], a["wsb"], None)
+    assert call(T=-1) == L.MOE_ERR_ARG
+    assert call(k=3, E=2) == L.MOE_ERR_ARG
+    assert call(E=0) == L.MOE_ERR_SHAPE
+    assert call(h=96) == L.MOE_ERR_SHAPE
+    assert call(dt=L.MOE_FP8_E4M3) == L.MOE_ERR_DTYPE
+    assert call(alpha=float("nan")) == L.MOE_ERR_ARG
+    assert call(dwg=None) == L.MOE_ERR_ARG
+    assert call(dxin=U) == L.MOE_ERR_ARG
+    assert call(dxin=ok["dx"]) == L.MOE_ERR_ARG          # in place is not allowed
+    assert call(wsb=need - 1) == L.MOE_ERR_WORKSPACE
+    assert call(ws=None) == L.MOE_ERR_WORKSPACE
+    assert call(T=0) == L.MOE_OK
+
+
+def test_router_aux_validation():
+    lib = L.lib()
+    need = lib.moe_router_aux_workspace_size(1000, 8)
+    assert need > 0
+
+    def call(T=1000, E=8, k=2, lg=A, cnt=A, loss=A, ws=A, wsb=need):
+        return lib.moe_router_aux_loss(lg, cnt, T, E, k, 0.01, loss, ws, wsb, None)
+    assert call(T=0) == L.MOE_ERR_ARG
+    assert call(E=L.MOE_MAX_EXPERTS + 1) == L.MOE_ERR_SHAPE
+    assert call(k=9) == L.MOE_ERR_ARG
+    assert call(loss=None) == L.MOE_ERR_ARG
+    assert call(wsb=need - 1) == L.MOE_ERR_WORKSPACE

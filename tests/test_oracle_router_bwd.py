@@ -129,3 +129,21 @@ def test_aux_gradient_alone_matches_finite_differences():
                              L, idx, np.full((T, k), 1.0 / k), alpha)
     num = _fd(lambda a: ref.aux_balance_loss(a, idx, E, k, alpha), L)
     assert np.abs(num - rb["dL"]).max() <= 1e-8 * np.abs(num).max()
+
+
+def test_bf16_storage_forward_rounds_a_and_yp_only():
+    rng = np.random.default_rng(11)
+    E, h, hf, R = 3, 8, 6, 20
+    xp = ref.round_bf16(rng.standard_normal((R, h)))
+    offs = np.array([0, 7, 7, 20])
+    w1, w3 = rng.standard_normal((E, h, hf)), rng.standard_normal((E, h, hf))
+    w2 = rng.standard_normal((E, hf, h))
+    ex, _, _, a = ref.expert_forward(xp, offs, w1, w3, w2)
+    st, _, _, a_st = ref.expert_forward(xp, offs, w1, w3, w2, bf16_storage=True)
+    np.testing.assert_array_equal(ref.round_bf16(st), st)          # Yp is bf16
+    np.testing.assert_array_equal(a_st, ref.round_bf16(a))         # A rounded once
+    for e in range(E):                                             # FC2 from the rounded A
+        lo, hi = offs[e], offs[e + 1]
+        np.testing.assert_array_equal(st[lo:hi], ref.round_bf16(ref.round_bf16(a[lo:hi]) @ w2[e]))
+    rel = np.abs(st - ex).max() / np.abs(ex).max()
+    assert 0 < rel < 2e-2
