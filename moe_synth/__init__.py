@@ -21,7 +21,8 @@ the workload is skewed), expert ``w1``/``w3`` ``[E, h, h_ffn]`` (gate / up),
 
 Workload shapes come from the model-shape table of the MegaScale-MoE pages
 (paper review, section 五 "基准测试配置"; research digest, Table 2 shapes):
-Mixtral-8x7B, DeepSeekMoE, Internal-352B and Hunyuan-Large.  The value
+Mixtral-8x7B, DeepSeekMoE, Internal-352B, Hunyuan-Large, Mixtral-8x22B and
+Phi-3.5-MoE (the table gives no batch; the last two use the Mixtral batch).  The value
 distributions (N(0,1) activations, N(0, 1/fan_in) expert weights, N(0, 0.02)
 router, Zipf(1.2) router bias for the skewed workload) are this project's
 synthetic stand-ins: the pages publish no weights or data.
@@ -72,6 +73,9 @@ WORKLOADS = {
     "dsmoe": Workload("dsmoe", 16384, 2048, 1408, 64, 6, "bf16", backward=True),
     "m352b_zipf": Workload("m352b_zipf", 8192, 4096, 14336, 32, 3, "bf16", zipf_s=1.2),
     "hunyuan_fp8": Workload("hunyuan_fp8", 32768, 6400, 18304, 16, 1, "fp8"),
+    # the two remaining shapes of the model table, at the Mixtral batch
+    "mixtral22b": Workload("mixtral22b", 8192, 6144, 16384, 8, 2, "bf16"),
+    "phi35": Workload("phi35", 8192, 4096, 6400, 16, 2, "bf16"),
 }
 
 

@@ -81,23 +81,29 @@ def build_index(idx: np.ndarray, E: int):
     """Per-expert counts, offsets, and the row each (token, slot) lands in.
 
     ``counts[e]`` = number of (t, j) with ``idx[t, j] == e``;
-    ``offsets`` = exclusive prefix sum of counts, ``offsets[E] = T*k``;
+    ``offsets`` = exclusive prefix sum of counts (``offsets[E]`` = rows kept);
     ``dst_row[t, j] = offsets[e] + #{t' < t routed to e}``;
     ``src_tok[dst_row[t, j]] = t``.
+    A pair whose id lies outside [0, E) is dropped: it is not counted and its
+    ``dst_row`` is -1 (the rows of other experts' GPUs, or dropped tokens).
+    ``src_tok`` has ``T*k`` entries; those past ``offsets[E]`` are -1.
     """
     idx = np.asarray(idx)
     T, k = idx.shape
     counts = np.zeros(E, dtype=np.int64)
     for e in idx.ravel():
-        counts[e] += 1
+        if 0 <= e < E:
+            counts[e] += 1
     offsets = np.zeros(E + 1, dtype=np.int64)
     offsets[1:] = np.cumsum(counts)
     nxt = offsets[:-1].copy()
-    dst_row = np.empty((T, k), dtype=np.int64)
-    src_tok = np.empty(T * k, dtype=np.int64)
+    dst_row = np.full((T, k), -1, dtype=np.int64)
+    src_tok = np.full(T * k, -1, dtype=np.int64)
     for t in range(T):
         for j in range(k):
             e = idx[t, j]
+            if not 0 <= e < E:
+                continue
             dst_row[t, j] = nxt[e]
             src_tok[nxt[e]] = t
             nxt[e] += 1
@@ -125,9 +131,27 @@ def combine(yp: np.ndarray, dst_row: np.ndarray, w: np.ndarray | None) -> np.nda
     T, k = dst_row.shape
     y = np.zeros((T,) + yp.shape[1:], dtype=np.float64)
     for j in range(k):
-        g = np.asarray(yp[dst_row[:, j]], np.float64)
+        kept = dst_row[:, j] >= 0                  # dropped pairs contribute nothing
+        g = np.zeros((T,) + yp.shape[1:], dtype=np.float64)
+        g[kept] = np.asarray(yp[dst_row[kept, j]], np.float64)
         y += g if w is None else np.asarray(w[:, j], np.float64)[:, None] * g
     return y
+
+
+def local_expert_ids(idx: np.ndarray, e_lo: int, e_count: int) -> np.ndarray:
+    """One GPU's share of expert parallelism: the ids of experts
+    [e_lo, e_lo + e_count) renumbered from 0, every other id -1.
+
+    [MSD] §3.2 (Diagram B: with the all-gather path each GPU scatters the
+    gathered tokens to its own experts and drops the rest, then fills its
+    partial outputs for the reduce-scatter); [MSR] §四 (adaptive EP
+    communication).  With the all-to-all path the same rows arrive ordered by
+    (local expert, source rank); when source ranks hold contiguous token
+    ranges that is the (expert, token) order of ``build_index``.
+    """
+    idx = np.asarray(idx)
+    inside = (idx >= e_lo) & (idx < e_lo + e_count)
+    return np.where(inside, idx - e_lo, -1)
 
 
 # --------------------------------------------------------------------------

@@ -293,6 +293,9 @@ LAYER_CASES = [
     ("bf16_e64_k6", dict(T=600, h=256, h_ffn=256, E=64, k=6, dtype="bf16"), 5),
     ("bf16_zipf", dict(T=1000, h=256, h_ffn=384, E=32, k=3, dtype="bf16", zipf_s=1.2), 6),
     ("bf16_one_expert", dict(T=333, h=256, h_ffn=256, E=1, k=1, dtype="bf16"), 7),
+    # Mixtral-8x22B and Phi-3.5-MoE proportions (h : h_ffn, E, k) at small size
+    ("bf16_8x22b_shape", dict(T=600, h=384, h_ffn=1024, E=8, k=2, dtype="bf16"), 8),
+    ("bf16_phi35_shape", dict(T=600, h=512, h_ffn=768, E=16, k=2, dtype="bf16"), 9),
 ]
 
 
@@ -419,6 +422,16 @@ def _full_size_sampled(name, n_sample=48, seed=0):
 @pytest.mark.slow
 def test_full_size_mixtral_sampled():
     _full_size_sampled("mixtral")
+
+
+@pytest.mark.slow
+def test_full_size_mixtral22b_sampled():
+    _full_size_sampled("mixtral22b", n_sample=24)
+
+
+@pytest.mark.slow
+def test_full_size_phi35_sampled():
+    _full_size_sampled("phi35")
 
 
 @pytest.mark.slow

@@ -76,3 +76,43 @@ def test_row_scaled_permute():
     for t in range(T):
         for j in range(k):
             np.testing.assert_allclose(xp[dst_row[t, j]], w[t, j] * x[t], rtol=1e-15)
+
+
+def test_build_index_drops_ids_outside_range():
+    idx = np.array([[0, 3], [-1, 1], [2, 7], [1, 0]])
+    counts, offsets, dst_row, src_tok = ref.build_index(idx, 4)
+    np.testing.assert_array_equal(counts, [2, 2, 1, 1])
+    np.testing.assert_array_equal(offsets, [0, 2, 4, 5, 6])
+    np.testing.assert_array_equal(dst_row, [[0, 5], [-1, 2], [4, -1], [3, 1]])
+    np.testing.assert_array_equal(src_tok, [0, 3, 1, 3, 2, 0, -1, -1])
+
+
+def test_expert_parallel_shares_partition_the_layer():
+    """n GPUs' shares (expert ranges) together route every pair exactly once,
+    and their partial combines add up to the full combine."""
+    rng = np.random.default_rng(3)
+    T, E, k, h, n = 40, 8, 3, 5, 4
+    L = rng.standard_normal((T, E))
+    idx, w = ref.topk_softmax(L, k)
+    counts, offsets, dst_row, _ = ref.build_index(idx, E)
+    yp = rng.standard_normal((T * k, h))
+    full = ref.combine(yp, dst_row, w)
+    total = np.zeros_like(full)
+    seen = np.zeros((T, k), int)
+    for r in range(n):
+        e_lo = r * E // n
+        loc = ref.local_expert_ids(idx, e_lo, E // n)
+        c_r, o_r, d_r, s_r = ref.build_index(loc, E // n)
+        np.testing.assert_array_equal(c_r, counts[e_lo:e_lo + E // n])   # a slice of the global counts
+        seen += d_r >= 0
+        # the rank's rows, in its own order, carry the same expert outputs
+        yp_r = np.zeros((max(int(o_r[-1]), 1), h))
+        yp_r[d_r[d_r >= 0]] = yp[dst_row[d_r >= 0]]
+        total += ref.combine(yp_r, d_r, w)
+        # rows of each local expert are ordered by token (= by source rank,
+        # when ranks own contiguous token ranges)
+        for e in range(E // n):
+            toks = s_r[o_r[e]:o_r[e + 1]]
+            assert np.all(np.diff(toks) > 0)
+    assert np.all(seen == 1)
+    np.testing.assert_allclose(total, full, rtol=1e-13, atol=1e-13)
