@@ -170,6 +170,29 @@ int moe_permute(const void* src, int src_dtype, const int32_t* topk_idx, const f
                 int32_t* src_tok, void* dst, int dst_dtype, float* dst_scale, void* ws,
                 size_t ws_bytes, void* stream);
 
+/*
+ * One GPU's share of expert parallelism (MegaScale-MoE research digest §3.2,
+ * Diagram B: scatter to the local experts and drop the rest; paper review §四
+ * adaptive EP communication): the dispatch of moe_permute restricted to the
+ * experts [e_lo, e_lo + e_count) of an E-expert layer, renumbered from 0.
+ * Pairs routed elsewhere get dst_row = -1 and are not counted; moe_combine
+ * over this share's rows (y_dtype MOE_F32) is the share's partial output,
+ * and the shares' partials add up to the layer's output (the reduce-scatter
+ * of the all-gather path).  Rows of each local expert are ordered by token,
+ * i.e. by (source rank, token) when source ranks hold contiguous token ranges
+ * (the order the all-to-all path delivers).
+ *   topk_idx [T][k] global expert ids; counts [e_count], offsets [e_count+1];
+ *   dst_row [T][k]; src_tok [T*k] (entries past offsets[e_count] untouched);
+ *   dst [T*k][h] (offsets[e_count] rows written); everything else as for
+ *   moe_permute with topk_idx given.  0 <= e_lo, 1 <= e_count,
+ *   e_lo + e_count <= E.
+ */
+size_t moe_permute_local_workspace_size(int T, int e_count, int k);
+int moe_permute_local(const void* src, int src_dtype, const int32_t* topk_idx, const float* row_scale,
+                      int T, int h, int E, int k, int e_lo, int e_count, int32_t* counts,
+                      int32_t* offsets, int32_t* dst_row, int32_t* src_tok, void* dst, int dst_dtype,
+                      float* dst_scale, void* ws, size_t ws_bytes, void* stream);
+
 /* Workspace bytes for moe_grouped_swiglu_fwd (rows = T*k). */
 size_t moe_grouped_workspace_size(int rows, int h, int h_ffn, int E, int dtype);
 

@@ -166,6 +166,54 @@ int moe_permute(const void* src, int src_dtype, const int32_t* topk_idx, const f
                   "moe_permute");
 }
 
+size_t moe_permute_local_workspace_size(int T, int e_count, int k) {
+  if (T < 0 || e_count < 1 || k < 1) return 0;
+  return ((size_t(T) * k * 4 + 255) & ~size_t(255)) + moe_launch::index_ws_bytes(T, e_count);
+}
+
+int moe_permute_local(const void* src, int src_dtype, const int32_t* topk_idx, const float* row_scale,
+                      int T, int h, int E, int k, int e_lo, int e_count, int32_t* counts,
+                      int32_t* offsets, int32_t* dst_row, int32_t* src_tok, void* dst, int dst_dtype,
+                      float* dst_scale, void* ws, size_t ws_bytes, void* stream) {
+  REQ(T >= 0, MOE_ERR_ARG, "T=%d is negative", T);
+  REQ(E >= 1 && E <= MOE_MAX_EXPERTS, MOE_ERR_SHAPE, "E=%d outside [1, %d]", E, MOE_MAX_EXPERTS);
+  REQ(k >= 1 && k <= E && k <= MOE_MAX_TOPK, MOE_ERR_ARG, "k=%d outside [1, min(E, %d)]", k,
+      MOE_MAX_TOPK);
+  REQ(e_count >= 1 && e_lo >= 0 && e_lo + e_count <= E, MOE_ERR_ARG,
+      "expert range [%d, %d) not inside [0, %d)", e_lo, e_lo + e_count, E);
+  PTR(topk_idx);
+  const size_t need = moe_permute_local_workspace_size(T, e_count, k);
+  REQ(T == 0 || (ws != nullptr && ws_bytes >= need), MOE_ERR_WORKSPACE,
+      "workspace of %zu bytes needed, %zu given", need, ws ? ws_bytes : size_t(0));
+  if (T == 0)  // the empty batch still clears counts / offsets
+    return moe_permute(src, src_dtype, topk_idx, row_scale, 0, h, e_count, e_count < k ? e_count : k,
+                       counts, offsets, dst_row, src_tok, dst, dst_dtype, dst_scale, ws, ws_bytes,
+                       stream);
+  // k may exceed e_count (a token meets at most one slot per local expert):
+  // the share is validated with the global E
+  REQ(h > 0 && h % 8 == 0, MOE_ERR_SHAPE, "h=%d must be a positive multiple of 8", h);
+  bool ok = (src_dtype == MOE_F32 && dst_dtype == MOE_F32) ||
+            (src_dtype == MOE_BF16 && (dst_dtype == MOE_BF16 || dst_dtype == MOE_FP8_E4M3));
+  REQ(ok, MOE_ERR_DTYPE, "unsupported permute %d -> %d", src_dtype, dst_dtype);
+  if (dst_dtype == MOE_FP8_E4M3) {
+    PTR(dst_scale);
+    REQ(row_scale == nullptr, MOE_ERR_ARG, "row_scale is not supported with FP8 output");
+  }
+  PTR(src); PTR(dst); PTR(dst_row); OPT(row_scale); PTR(counts); PTR(offsets); PTR(src_tok);
+  unsigned char* w = static_cast<unsigned char*>(ws);
+  int32_t* local = reinterpret_cast<int32_t*>(w);
+  const size_t lb = (size_t(T) * k * 4 + 255) & ~size_t(255);
+  moe_launch::clear_status();
+  int rc = moe_launch::local_ids(topk_idx, T * k, e_lo, e_count, local, (hipStream_t)stream);
+  if (rc) return launched(rc, "moe_permute_local (ids)");
+  rc = moe_launch::index_build(local, T, e_count, k, counts, offsets, dst_row, src_tok, w + lb,
+                               (hipStream_t)stream);
+  if (rc) return launched(rc, "moe_permute_local (index)");
+  return launched(moe_launch::permute_rows(src, src_dtype, dst_row, row_scale, T, h, k, dst, dst_dtype,
+                                           dst_scale, (hipStream_t)stream),
+                  "moe_permute_local");
+}
+
 static int check_weights(const moe_weights* W) {
   REQ(W != nullptr, MOE_ERR_ARG, "W must not be NULL");
   REQ(W->dtype == MOE_F32 || W->dtype == MOE_BF16 || W->dtype == MOE_FP8_E4M3, MOE_ERR_DTYPE,

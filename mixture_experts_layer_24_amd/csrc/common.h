@@ -94,6 +94,7 @@ int route(const void* x, const void* w_gate, const float* bias, float* logits, i
 int index_build(const int32_t* topk_idx, int T, int E, int k, int32_t* counts, int32_t* offsets,
                 int32_t* dst_row, int32_t* src_tok, void* ws, hipStream_t s);
 size_t index_ws_bytes(int T, int E);
+int local_ids(const int32_t* topk_idx, int n, int e_lo, int e_count, int32_t* out, hipStream_t s);
 int permute_rows(const void* src, int src_dt, const int32_t* dst_row, const float* row_scale,
                  int T, int h, int k, void* dst, int dst_dt, float* dst_scale, hipStream_t s);
 int combine_rows(const void* yp, int yp_dt, const int32_t* dst_row, const float* w, int T, int h,

@@ -103,10 +103,29 @@ __global__ void __launch_bounds__(kIdxBlock) idx_assign_kernel(const int32_t* __
   }
 }
 
+// One GPU's share of the experts: ids in [e_lo, e_lo + e_count) renumbered
+// from 0, every other id -1 (dropped by the index builder).
+__global__ void __launch_bounds__(256) idx_local_kernel(const int32_t* __restrict__ idx, int n,
+                                                        int e_lo, int e_count,
+                                                        int32_t* __restrict__ out) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n) {
+    const int e = idx[i];
+    out[i] = (e >= e_lo && e < e_lo + e_count) ? e - e_lo : -1;
+  }
+}
+
 }  // namespace moe
 
 namespace moe_launch {
 using namespace moe;
+
+int local_ids(const int32_t* topk_idx, int n, int e_lo, int e_count, int32_t* out, hipStream_t s) {
+  if (n > 0)
+    hipLaunchKernelGGL(idx_local_kernel, dim3(ceil_div(n, 256)), dim3(256), 0, s, topk_idx, n, e_lo,
+                       e_count, out);
+  return launch_status();
+}
 
 size_t index_ws_bytes(int T, int E) {
   size_t nb = size_t(ceil_div(T > 0 ? T : 1, kIdxBlock));

@@ -162,3 +162,20 @@ def test_router_aux_validation():
     assert call(k=9) == L.MOE_ERR_ARG
     assert call(loss=None) == L.MOE_ERR_ARG
     assert call(wsb=need - 1) == L.MOE_ERR_WORKSPACE
+
+
+def test_permute_local_validation():
+    lib = L.lib()
+    T, h, E, k = 100, 64, 16, 2
+    need = lib.moe_permute_local_workspace_size(T, 4, k)
+    assert need >= lib.moe_permute_workspace_size(T, 4, k)
+
+    def call(e_lo=4, e_count=4, ws=A, wsb=need, idx=A, dt=L.MOE_BF16):
+        return lib.moe_permute_local(A, L.MOE_BF16, idx, None, T, h, E, k, e_lo, e_count, A, A, A, A,
+                                     A, dt, None, ws, wsb, None)
+    assert call(e_lo=-1) == L.MOE_ERR_ARG
+    assert call(e_count=0) == L.MOE_ERR_ARG
+    assert call(e_lo=14, e_count=4) == L.MOE_ERR_ARG       # range past E
+    assert call(idx=None) == L.MOE_ERR_ARG
+    assert call(wsb=need - 1) == L.MOE_ERR_WORKSPACE
+    assert call(dt=L.MOE_F32) == L.MOE_ERR_DTYPE
