@@ -548,3 +548,25 @@ def router_backward(dy, ysel, x, w_gate, logits, idx, w, alpha):
         s = softmax_rows(L)
         dL += s * (g[None, :] - (s @ g)[:, None])
     return {"dw": dw, "dL": dL, "dw_gate": x.T @ dL, "dx": dL @ wg.T, "dbias": dL.sum(axis=0)}
+
+
+def capacity_drop(idx: np.ndarray, logits: np.ndarray, E: int, group: int, capacity: int) -> np.ndarray:
+    """Token dropping by affinity ([MSD] §3.2, the discussion of Figure 7:
+    "token dropping per GPU, as in DeepSeek-V2"; DeepSeek-V2 drops, on each
+    device, the tokens with the lowest affinity until the device's budget is
+    met).  A device here is a group of ``group`` consecutive experts (one
+    GPU's share; ``group = 1`` is a per-expert capacity).  Among the (t, j)
+    pairs routed into a group, the ``capacity`` pairs with the highest
+    affinity s = softmax(L_t)[e] (over all E experts) are kept, equal
+    affinities in dispatch order (expert, then token); the others get id -1,
+    which the dispatch drops.  Gate weights are left as they are."""
+    idx = np.asarray(idx)
+    T, k = idx.shape
+    s = softmax_rows(logits)
+    out = idx.copy()
+    for g0 in range(0, E, group):
+        pairs = [(t, j) for t in range(T) for j in range(k) if g0 <= idx[t, j] < g0 + group]
+        pairs.sort(key=lambda p: (-s[p[0], idx[p]], idx[p], p[0]))
+        for t, j in pairs[capacity:]:
+            out[t, j] = -1
+    return out
