@@ -193,6 +193,25 @@ int moe_permute_local(const void* src, int src_dtype, const int32_t* topk_idx, c
                       int32_t* offsets, int32_t* dst_row, int32_t* src_tok, void* dst, int dst_dtype,
                       float* dst_scale, void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * Token dropping by affinity (MegaScale-MoE research digest §3.2: tokens are
+ * dropped per GPU, as in DeepSeek-V2, which drops the lowest-affinity tokens
+ * of each device until its budget is met).  A device is a group of `group`
+ * consecutive experts (one GPU's share; group = 1 gives a per-expert
+ * capacity).  Among the (t, j) pairs routed into a group, the `capacity`
+ * pairs with the highest affinity s = softmax(logits[t])[e] (fp32, over all E
+ * experts) are kept, equal affinities in dispatch order (expert, then token);
+ * every other pair's id becomes -1 in topk_idx_out, which moe_permute then
+ * drops (and with it the pair's share of the combine and of the backward).
+ * Gate weights are not changed.
+ *   topk_idx [T][k] int32 in; topk_idx_out [T][k] int32 out (may be the same
+ *   buffer as topk_idx); logits [T][E] fp32 (bias included).
+ *   group divides E; capacity >= 0 rows per group.
+ */
+size_t moe_capacity_drop_workspace_size(int T, int E, int k);
+int moe_capacity_drop(const int32_t* topk_idx, const float* logits, int T, int E, int k, int group,
+                      int capacity, int32_t* topk_idx_out, void* ws, size_t ws_bytes, void* stream);
+
 /* Workspace bytes for moe_grouped_swiglu_fwd (rows = T*k). */
 size_t moe_grouped_workspace_size(int rows, int h, int h_ffn, int E, int dtype);
 

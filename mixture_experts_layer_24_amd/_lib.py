@@ -41,6 +41,8 @@ SIGNATURES = {
     "moe_permute": (I, [P, I, P, P, I, I, I, I, P, P, P, P, P, I, P, P, SZ, P]),
     "moe_permute_local_workspace_size": (SZ, [I, I, I]),
     "moe_permute_local": (I, [P, I, P, P, I, I, I, I, I, I, P, P, P, P, P, I, P, P, SZ, P]),
+    "moe_capacity_drop_workspace_size": (SZ, [I, I, I]),
+    "moe_capacity_drop": (I, [P, P, I, I, I, I, I, P, P, SZ, P]),
     "moe_grouped_workspace_size": (SZ, [I, I, I, I, I]),
     "moe_grouped_swiglu_fwd": (I, [P, P, ctypes.POINTER(MoeWeights), P, I, P, P, P, SZ, P]),
     "moe_grouped_bwd_workspace_size": (SZ, [I, I, I, I, I]),

@@ -214,6 +214,30 @@ int moe_permute_local(const void* src, int src_dtype, const int32_t* topk_idx, c
                   "moe_permute_local");
 }
 
+size_t moe_capacity_drop_workspace_size(int T, int E, int k) {
+  if (T <= 0 || E < 1 || k < 1) return 0;
+  return moe_launch::capacity_ws_bytes(T, E, k);
+}
+
+int moe_capacity_drop(const int32_t* topk_idx, const float* logits, int T, int E, int k, int group,
+                      int capacity, int32_t* topk_idx_out, void* ws, size_t ws_bytes, void* stream) {
+  REQ(T >= 0, MOE_ERR_ARG, "T=%d is negative", T);
+  REQ(E >= 1 && E <= MOE_MAX_EXPERTS, MOE_ERR_SHAPE, "E=%d outside [1, %d]", E, MOE_MAX_EXPERTS);
+  REQ(k >= 1 && k <= E && k <= MOE_MAX_TOPK, MOE_ERR_ARG, "k=%d outside [1, min(E, %d)]", k,
+      MOE_MAX_TOPK);
+  REQ(group >= 1 && E % group == 0, MOE_ERR_ARG, "group=%d must divide E=%d", group, E);
+  REQ(capacity >= 0, MOE_ERR_ARG, "capacity=%d is negative", capacity);
+  PTR(topk_idx); PTR(logits); PTR(topk_idx_out);
+  if (T == 0) return MOE_OK;
+  const size_t need = moe_launch::capacity_ws_bytes(T, E, k);
+  REQ(ws != nullptr && ws_bytes >= need, MOE_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given",
+      need, ws ? ws_bytes : size_t(0));
+  moe_launch::clear_status();
+  return launched(moe_launch::capacity_drop(topk_idx, logits, T, E, k, group, capacity, topk_idx_out,
+                                            ws, (hipStream_t)stream),
+                  "moe_capacity_drop");
+}
+
 static int check_weights(const moe_weights* W) {
   REQ(W != nullptr, MOE_ERR_ARG, "W must not be NULL");
   REQ(W->dtype == MOE_F32 || W->dtype == MOE_BF16 || W->dtype == MOE_FP8_E4M3, MOE_ERR_DTYPE,

@@ -116,6 +116,9 @@ size_t router_bwd_ws_bytes(int T, int h, int E);
 int router_aux(const float* logits, const int32_t* counts, int T, int E, int k, float alpha,
                float* loss, void* ws, hipStream_t s);
 size_t router_aux_ws_bytes(int T, int E);
+int capacity_drop(const int32_t* topk_idx, const float* logits, int T, int E, int k, int group,
+                  int capacity, int32_t* out, void* ws, hipStream_t s);
+size_t capacity_ws_bytes(int T, int E, int k);
 int pack_weights(const void* w1, const void* w3, const void* w2, int in_dt, int E, int h,
                  int h_ffn, int out_dt, void* w13, void* w2p, float* w13_scale, float* w2_scale,
                  void* w13_bwd, void* w2_bwd, hipStream_t s);
@@ -131,7 +134,7 @@ const char* last_hip_error();
 // Optional per-kernel timing: when enabled (moe_timing_enable), a pair of HIP
 // events is recorded on the launch stream around every kernel of the layer.
 enum TimerId { kTRoute = 0, kTIndex, kTPermute, kTFc1, kTQuant, kTFc2, kTCombine, kTBwd1, kTBwd2,
-               kTBwd3, kTBwd4, kTPack, kTXpose, kTRouterBwd, kTRouterAux, kNumTimers };
+               kTBwd3, kTBwd4, kTPack, kTXpose, kTRouterBwd, kTRouterAux, kTCapacity, kNumTimers };
 void timer_begin(int id, hipStream_t s);
 void timer_end(int id, hipStream_t s);
 }  // namespace moe_launch

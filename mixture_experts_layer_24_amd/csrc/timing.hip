@@ -17,7 +17,7 @@ namespace {
 const char* kNames[moe_launch::kNumTimers] = {"route", "index", "permute", "fc1", "quant_act",
                                               "fc2", "combine", "bwd_dA", "bwd_dW2",
                                               "bwd_dXp", "bwd_dW13", "pack", "xpose",
-                                              "router_bwd", "router_aux"};
+                                              "router_bwd", "router_aux", "capacity"};
 struct Rec { int id; hipEvent_t a, b; };
 std::mutex g_mu;
 bool g_on = false;

@@ -73,6 +73,16 @@ def moe_permute_local(src, src_dtype, topk_idx, row_scale, T, h, E, k, e_lo, e_c
                                          ws_bytes, _s(stream)))
 
 
+def moe_capacity_drop_workspace_size(T, E, k):
+    return lib().moe_capacity_drop_workspace_size(T, E, k)
+
+
+def moe_capacity_drop(topk_idx, logits, T, E, k, group, capacity, topk_idx_out, ws, ws_bytes,
+                      stream=None):
+    return check(lib().moe_capacity_drop(_p(topk_idx), _p(logits), T, E, k, group, capacity,
+                                         _p(topk_idx_out), _p(ws), ws_bytes, _s(stream)))
+
+
 def moe_grouped_workspace_size(rows, h, h_ffn, E, dtype):
     return lib().moe_grouped_workspace_size(rows, h, h_ffn, E, dtype)
 
@@ -189,7 +199,11 @@ class MoELayer:
         self.gws = torch.empty(max(self.gws_bytes, 256), dtype=torch.uint8, device=dev)
         self.bwd_ready = False
 
-    def forward(self, x, w_gate, bias, W: PackedWeights, logits_in=None, stream=None):
+    def forward(self, x, w_gate, bias, W: PackedWeights, logits_in=None, capacity=None, group=1,
+                stream=None):
+        """One layer forward.  With ``capacity``, pairs beyond the capacity of
+        each group of ``group`` experts are dropped by affinity before the
+        dispatch (moe_capacity_drop)."""
         T, h, E, k = self.T, self.h, self.E, self.k
         if logits_in is None:
             moe_route(x, w_gate, bias, self.logits, T, h, E, k, dtype_code(x), self.topk_idx,
@@ -199,6 +213,12 @@ class MoELayer:
             moe_route(None, None, None, logits_in, T, h, E, k, dtype_code(logits_in),
                       self.topk_idx, self.topk_w, stream)
             self.logits_used = logits_in
+        if capacity is not None:
+            if not hasattr(self, "cws"):
+                self.cws_bytes = moe_capacity_drop_workspace_size(T, E, k)
+                self.cws = torch.empty(max(self.cws_bytes, 256), dtype=torch.uint8, device=self.y.device)
+            moe_capacity_drop(self.topk_idx, self.logits_used, T, E, k, group, capacity, self.topk_idx,
+                              self.cws, self.cws_bytes, stream)
         moe_permute(x, dtype_code(x), self.topk_idx, None, T, h, E, k, self.counts, self.offsets,
                     self.dst_row, self.src_tok, self.xp, self.dtype, self.xp_scale, self.pws,
                     self.pws_bytes, stream)

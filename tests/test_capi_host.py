@@ -179,3 +179,19 @@ def test_permute_local_validation():
     assert call(idx=None) == L.MOE_ERR_ARG
     assert call(wsb=need - 1) == L.MOE_ERR_WORKSPACE
     assert call(dt=L.MOE_F32) == L.MOE_ERR_DTYPE
+
+
+def test_capacity_drop_validation():
+    lib = L.lib()
+    T, E, k = 100, 8, 2
+    need = lib.moe_capacity_drop_workspace_size(T, E, k)
+    assert need > 0
+
+    def call(group=2, cap=10, ws=A, wsb=need, T=T, out=A):
+        return lib.moe_capacity_drop(A, A, T, E, k, group, cap, out, ws, wsb, None)
+    assert call(group=3) == L.MOE_ERR_ARG          # must divide E
+    assert call(group=0) == L.MOE_ERR_ARG
+    assert call(cap=-1) == L.MOE_ERR_ARG
+    assert call(out=None) == L.MOE_ERR_ARG
+    assert call(wsb=need - 1) == L.MOE_ERR_WORKSPACE
+    assert call(T=0) == L.MOE_OK
