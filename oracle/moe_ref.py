@@ -570,3 +570,94 @@ def capacity_drop(idx: np.ndarray, logits: np.ndarray, E: int, group: int, capac
         for t, j in pairs[capacity:]:
             out[t, j] = -1
     return out
+
+
+# --------------------------------------------------------------------------
+# FP8 backward.  [MSR] §三 (FP8 training row): per-token quantization instead
+# of per-tensor; [MSD] §3.4: FP32 sums of FP8 products, per-token scales.  The
+# pages give no recipe for the backward products, so (reading):
+#   * activation-gradient products dA = dYp W2^T and dXp = [dG|dU] W13^T:
+#     the gradient operand per routed row (per token), the weight per output
+#     channel of that product, rank-1 rescale of the fp32 sum;
+#   * weight-gradient products dW2 = A^T dYp and dW13 = Xp^T [dG|dU] contract
+#     over tokens, where a per-token scale cannot leave the sum: both
+#     transposed operands are quantized per channel over the expert's rows,
+#     again a rank-1 rescale, fp32 dW;
+#   * dY is quantized per token before the dispatch copy, so routed row
+#     (t, j) carries the codes of dY_t and the scale w_tj * s_t;
+#   * the values a BF16 step stores (dYp for the weight gradient, A, dG|dU,
+#     dXp) are bf16 before they are quantized or summed.
+# --------------------------------------------------------------------------
+
+def quantize_weight_rows(m: np.ndarray):
+    """Per-row quantization of a weight block ``[out, in]`` (one scale per
+    output channel over the contracted dimension); codes and fp32 scales."""
+    return quantize_rows(np.asarray(m, np.float32))
+
+
+def layer_backward_fp8(dy, x, w, dst_row, offsets, w1, w3, w2, g, u, quant=True):
+    """Expert-path gradients with FP8 products (quantization emulated).
+
+    ``g``, ``u`` are the forward's kept G and U (per routed row).  With
+    ``quant=False`` every quantizer is the identity (codes = values, scales
+    1, and dYp the stored bf16 value): the data flow alone, equal to
+    ``layer_backward(bf16_operands=True)`` up to the fp64 summation order.
+    Returns dx, dw1, dw3, dw2, dxp."""
+    if quant:
+        qrows = lambda v: quantize_rows(np.asarray(v, np.float32))
+        dec = e4m3_decode
+    else:
+        qrows = lambda v: (np.asarray(v, np.float64), np.ones(np.shape(v)[0]))
+        dec = lambda c: np.asarray(c, np.float64)
+    E = w1.shape[0]
+    T, k = dst_row.shape
+    dy = np.asarray(dy, np.float64)
+    w = np.asarray(w, np.float64)
+    xp = permute(np.asarray(x, np.float64), dst_row)
+    R, h = xp.shape
+    # dYp as stored in bf16, for the weight gradient
+    dyp_b = round_bf16(permute(dy, dst_row, row_scale=w))
+    # dYp for the activation gradient: codes of dY_t, scale w_tj * s_t (without
+    # quantization: the stored bf16 dYp, as in the BF16 step)
+    if quant:
+        qdy, sdy = qrows(dy)
+        qdyp = permute(qdy, dst_row)
+        sdyp = np.ones(R)
+        for j in range(k):
+            kept = dst_row[:, j] >= 0
+            sdyp[dst_row[kept, j]] = np.asarray(w[kept, j], np.float32) * np.asarray(sdy[kept], np.float32)
+    else:
+        qdyp, sdyp = dyp_b, np.ones(R)
+    dxp = np.zeros((R, h))
+    dw1 = np.zeros(w1.shape); dw3 = np.zeros(w3.shape); dw2 = np.zeros(w2.shape)
+    for e in range(E):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        if hi == lo:
+            continue
+        W1 = np.asarray(w1[e], np.float64); W3 = np.asarray(w3[e], np.float64)
+        W2 = np.asarray(w2[e], np.float64)
+        hf = W1.shape[1]
+        # dA = dYp W2^T: B rows are W2's h_ffn rows (contracted over h)
+        qw2, sw2 = qrows(W2)
+        da = (dec(qdyp[lo:hi]) @ dec(qw2).T) * sdyp[lo:hi, None] * np.asarray(sw2, np.float64)[None, :]
+        ge = round_bf16(g[lo:hi]); ue = round_bf16(u[lo:hi])
+        s = sigmoid(ge)
+        a = round_bf16(ge * s * ue)
+        dgu = round_bf16(np.concatenate([da * ue * s * (1.0 + ge * (1.0 - s)), da * ge * s], axis=1))
+        # dXp = [dG|dU] [W1|W3]^T: B rows are the h rows of [W1 | W3]
+        w13 = np.concatenate([W1, W3], axis=1)                     # [h, 2hf]
+        qgu, sgu = qrows(dgu)
+        qw13, sw13 = qrows(w13)
+        dxp[lo:hi] = round_bf16((dec(qgu) @ dec(qw13).T) * np.asarray(sgu, np.float64)[:, None]
+                                * np.asarray(sw13, np.float64)[None, :])
+        # weight gradients: transposed operands per channel over the expert's rows
+        qat, sat = qrows(a.T)                                      # [hf, rows]
+        qdt, sdt = qrows(dyp_b[lo:hi].T)                           # [h, rows]
+        dw2[e] = (dec(qat) @ dec(qdt).T) * np.asarray(sat, np.float64)[:, None] * np.asarray(sdt, np.float64)[None, :]
+        qxt, sxt = qrows(xp[lo:hi].T)                              # [h, rows]
+        qgt, sgt = qrows(dgu.T)                                    # [2hf, rows]
+        dw13 = (dec(qxt) @ dec(qgt).T) * np.asarray(sxt, np.float64)[:, None] * np.asarray(sgt, np.float64)[None, :]
+        dw1[e] = dw13[:, :hf]
+        dw3[e] = dw13[:, hf:]
+    dx = combine(dxp, dst_row, None)
+    return dict(dx=dx, dw1=dw1, dw3=dw3, dw2=dw2, dxp=dxp)

@@ -102,3 +102,40 @@ def test_fp8_layer_close_to_exact_layer():
     cols = np.array([3, 17, 100, 255])
     yc = ref.layer_forward_fp8_tokens(inp["x"], q["idx"], q["w"], inp["w1"], inp["w3"], inp["w2"], cols=cols)
     np.testing.assert_allclose(yc, q["y"][:, cols], rtol=1e-12, atol=1e-12 * rms)
+
+
+def _bwd_setup(seed, T=9, h=16, hf=12, E=3, k=2):
+    rng = np.random.default_rng(seed)
+    x = ref.round_bf16(rng.standard_normal((T, h)))
+    wg = rng.standard_normal((h, E))
+    w1 = ref.round_bf16(rng.standard_normal((E, h, hf)) / np.sqrt(h))
+    w3 = ref.round_bf16(rng.standard_normal((E, h, hf)) / np.sqrt(h))
+    w2 = ref.round_bf16(rng.standard_normal((E, hf, h)) / np.sqrt(hf))
+    dy = ref.round_bf16(rng.standard_normal((T, h)))
+    fw = ref.layer_forward(x, wg, None, w1, w3, w2, k)
+    return x, dy, w1, w3, w2, fw
+
+
+def test_fp8_backward_data_flow_equals_bf16_storage_backward():
+    """With every quantizer the identity the FP8 backward is the BF16-storage
+    backward: same operands, scales and transposes."""
+    x, dy, w1, w3, w2, fw = _bwd_setup(0)
+    a = ref.layer_backward_fp8(dy, x, fw["w"], fw["dst_row"], fw["offsets"], w1, w3, w2, fw["g"], fw["u"],
+                               quant=False)
+    b = ref.layer_backward(dy, x, fw["w"], fw["dst_row"], fw["offsets"], w1, w3, w2, g=fw["g"], u=fw["u"],
+                           bf16_operands=True)
+    for key in ("dx", "dw1", "dw3", "dw2"):
+        np.testing.assert_allclose(a[key], b[key], rtol=1e-12, atol=1e-12 * np.abs(b[key]).max(), err_msg=key)
+
+
+def test_fp8_backward_close_to_exact():
+    """E4M3 keeps 3 mantissa bits (relative rounding <= 2^-4, ~2^-4/sqrt(3)
+    rms for uniform rounding): the FP8 gradients' rms error stays a few
+    percent of the exact gradients' rms."""
+    x, dy, w1, w3, w2, fw = _bwd_setup(1, T=40, h=64, hf=48, E=4, k=2)
+    a = ref.layer_backward_fp8(dy, x, fw["w"], fw["dst_row"], fw["offsets"], w1, w3, w2, fw["g"], fw["u"])
+    b = ref.layer_backward(dy, x, fw["w"], fw["dst_row"], fw["offsets"], w1, w3, w2, g=fw["g"], u=fw["u"])
+    for key in ("dx", "dw1", "dw3", "dw2"):
+        rms = np.sqrt(np.mean(b[key] ** 2))
+        err = np.sqrt(np.mean((a[key] - b[key]) ** 2)) / rms
+        assert 5e-3 < err < 0.08, (key, err)      # quantization happened, and is bounded
