@@ -70,6 +70,21 @@ def topk_softmax(logits: np.ndarray, k: int):
     return idx, w
 
 
+def topk_weight_bound(logits: np.ndarray, idx: np.ndarray) -> np.ndarray:
+    """Bound on |w' - w| for the fp32 gate weights w' of any implementation
+    that forms the k-logit softmax in fp32 (x_j = L_j - L_max rounded, an
+    exponential within (|x| + 4) u/2 relative, an fp32 sum of k terms, one
+    division; u = 2^-23), against `topk_softmax`'s w (the exact value rounded
+    to fp32, u/2 more): w (2 X + k + 8) u with X = max_j |x_j|."""
+    L = np.asarray(logits, np.float32)
+    sel = np.take_along_axis(L, np.asarray(idx, np.int64), axis=1).astype(np.float64)
+    z = np.exp(sel - sel[:, :1])
+    w = z / z.sum(axis=1, keepdims=True)
+    X = np.abs(sel - sel[:, :1]).max(axis=1, keepdims=True)
+    k = sel.shape[1]
+    return w * (2.0 * X + k + 8) * 2.0 ** -23
+
+
 # --------------------------------------------------------------------------
 # Dispatch into expert-contiguous rows.  [MSR] §四, adaptive EP: an extra
 # local scatter makes each expert's tokens contiguous.  [MSD] §3.3 Diagram C:
@@ -429,6 +444,7 @@ def layer_forward_fp8(x, w_gate, bias, w1, w3, w2, k, logits=None):
     h = w2.shape[2]
     yp = np.zeros((R, h))
     a_all = np.zeros((R, w1.shape[2]))
+    g_all = np.zeros((R, w1.shape[2])); u_all = np.zeros((R, w1.shape[2]))
     qa_all = np.zeros((R, w1.shape[2]), np.uint8)
     sa_all = np.ones(R, np.float64)
     for e in range(E):
@@ -445,9 +461,11 @@ def layer_forward_fp8(x, w_gate, bias, w1, w3, w2, k, logits=None):
         qa = e4m3_encode(a / sa[:, None])
         yp[lo:hi] = (e4m3_decode(qa) @ e4m3_decode(q2)) * sa[:, None] * s2[None, :].astype(np.float64)
         a_all[lo:hi] = a; qa_all[lo:hi] = qa; sa_all[lo:hi] = sa
+        g_all[lo:hi] = g; u_all[lo:hi] = u
     y = combine(yp, dst_row, w)
     return dict(logits=L, idx=idx, w=w, counts=counts, offsets=offsets, dst_row=dst_row,
-                src_tok=src_tok, qx=qx, sx=sx, a=a_all, qa=qa_all, sa=sa_all, yp=yp, y=y)
+                src_tok=src_tok, qx=qx, sx=sx, g=g_all, u=u_all, a=a_all, qa=qa_all, sa=sa_all,
+                yp=yp, y=y)
 
 
 def layer_forward_fp8_tokens(x_rows, idx_rows, w_rows, w1, w3, w2, wq_cache=None, cols=None):
@@ -595,13 +613,17 @@ def quantize_weight_rows(m: np.ndarray):
     return quantize_rows(np.asarray(m, np.float32))
 
 
-def layer_backward_fp8(dy, x, w, dst_row, offsets, w1, w3, w2, g, u, quant=True):
+def layer_backward_fp8(dy, x, w, dst_row, offsets, w1, w3, w2, g, u, quant=True, noise=None):
     """Expert-path gradients with FP8 products (quantization emulated).
 
     ``g``, ``u`` are the forward's kept G and U (per routed row).  With
     ``quant=False`` every quantizer is the identity (codes = values, scales
     1, and dYp the stored bf16 value): the data flow alone, equal to
     ``layer_backward(bf16_operands=True)`` up to the fp64 summation order.
+    ``noise(name, e, v)``, when given, returns a replacement for each value
+    that an implementation computes before rounding it (names "g", "u" for the
+    kept G, U; "da"; "dg", "du"; "a"; "dxp", "dw2", "dw13" for the fp32 sums)
+    so that a test can evaluate nearby implementations.
     Returns dx, dw1, dw3, dw2, dxp."""
     if quant:
         qrows = lambda v: quantize_rows(np.asarray(v, np.float32))
@@ -609,6 +631,7 @@ def layer_backward_fp8(dy, x, w, dst_row, offsets, w1, w3, w2, g, u, quant=True)
     else:
         qrows = lambda v: (np.asarray(v, np.float64), np.ones(np.shape(v)[0]))
         dec = lambda c: np.asarray(c, np.float64)
+    nz = noise if noise is not None else (lambda name, e, v: v)
     E = w1.shape[0]
     T, k = dst_row.shape
     dy = np.asarray(dy, np.float64)
@@ -640,24 +663,254 @@ def layer_backward_fp8(dy, x, w, dst_row, offsets, w1, w3, w2, g, u, quant=True)
         # dA = dYp W2^T: B rows are W2's h_ffn rows (contracted over h)
         qw2, sw2 = qrows(W2)
         da = (dec(qdyp[lo:hi]) @ dec(qw2).T) * sdyp[lo:hi, None] * np.asarray(sw2, np.float64)[None, :]
-        ge = round_bf16(g[lo:hi]); ue = round_bf16(u[lo:hi])
+        da = nz("da", e, da)
+        ge = round_bf16(nz("g", e, g[lo:hi])); ue = round_bf16(nz("u", e, u[lo:hi]))
         s = sigmoid(ge)
-        a = round_bf16(ge * s * ue)
-        dgu = round_bf16(np.concatenate([da * ue * s * (1.0 + ge * (1.0 - s)), da * ge * s], axis=1))
+        a = round_bf16(nz("a", e, ge * s * ue))
+        dgu = round_bf16(np.concatenate([nz("dg", e, da * ue * s * (1.0 + ge * (1.0 - s))),
+                                         nz("du", e, da * ge * s)], axis=1))
         # dXp = [dG|dU] [W1|W3]^T: B rows are the h rows of [W1 | W3]
         w13 = np.concatenate([W1, W3], axis=1)                     # [h, 2hf]
         qgu, sgu = qrows(dgu)
         qw13, sw13 = qrows(w13)
-        dxp[lo:hi] = round_bf16((dec(qgu) @ dec(qw13).T) * np.asarray(sgu, np.float64)[:, None]
-                                * np.asarray(sw13, np.float64)[None, :])
+        dxp[lo:hi] = round_bf16(nz("dxp", e, (dec(qgu) @ dec(qw13).T) * np.asarray(sgu, np.float64)[:, None]
+                                    * np.asarray(sw13, np.float64)[None, :]))
         # weight gradients: transposed operands per channel over the expert's rows
         qat, sat = qrows(a.T)                                      # [hf, rows]
         qdt, sdt = qrows(dyp_b[lo:hi].T)                           # [h, rows]
-        dw2[e] = (dec(qat) @ dec(qdt).T) * np.asarray(sat, np.float64)[:, None] * np.asarray(sdt, np.float64)[None, :]
+        dw2[e] = nz("dw2", e, (dec(qat) @ dec(qdt).T) * np.asarray(sat, np.float64)[:, None]
+                    * np.asarray(sdt, np.float64)[None, :])
         qxt, sxt = qrows(xp[lo:hi].T)                              # [h, rows]
         qgt, sgt = qrows(dgu.T)                                    # [2hf, rows]
-        dw13 = (dec(qxt) @ dec(qgt).T) * np.asarray(sxt, np.float64)[:, None] * np.asarray(sgt, np.float64)[None, :]
+        dw13 = nz("dw13", e, (dec(qxt) @ dec(qgt).T) * np.asarray(sxt, np.float64)[:, None]
+                  * np.asarray(sgt, np.float64)[None, :])
         dw1[e] = dw13[:, :hf]
         dw3[e] = dw13[:, hf:]
     dx = combine(dxp, dst_row, None)
     return dict(dx=dx, dw1=dw1, dw3=dw3, dw2=dw2, dxp=dxp)
+
+
+# --------------------------------------------------------------------------
+# Allowance of the FP8 backward.  A quantizer turns a tiny difference before
+# it into a whole code step (up to 1/8 of the value) when the value sits at a
+# rounding boundary, and into a new scale for its whole row when the row's
+# amax sits at a bf16 rounding boundary.  Every implementation that sums in
+# fp32 (any order) and evaluates the SwiGLU derivative in fp32 holds, before
+# each bf16 rounding, a value within a proven distance of the fp64 one; the
+# envelope below pushes those distances through the roundings, quantizers and
+# products, and bounds per output element how far such an implementation's
+# result can be from `layer_backward_fp8`'s.
+#
+# Error bounds used (u = 2^-23 bounds one fp32 rounding, truncating or not):
+#   * an fp32 sum whose addition tree has depth D (any order within it) is
+#     within gamma(D) * sum|terms| of the exact sum, gamma(D) = D u / (1 - D u)
+#     (the standard bound for summation trees); the class allowed here forms
+#     partial sums of at most 64 products (D <= 63), adds them one after the
+#     other (n/64) and then at most 8 partial results, and rescales (2 more
+#     roundings);
+#   * with s = 1 / (1 + exp(-G)) evaluated in fp32 (the exponential within
+#     (|G| + 4) u/2 relative), dG = dA U s (1 + G (1 - s)) is within
+#     6 u (1 + |G|)^2 |dA U s|, and dU = dA SiLU(G), A = SiLU(G) U within
+#     4 u (1 + |G|) of their magnitude (SiLU(G) = G s);
+#   * where the kept G, U are themselves only known within a span of bf16
+#     values, |SiLU'| <= 1.1 and |SiLU''| <= 0.55 bound the change.
+# --------------------------------------------------------------------------
+
+F32_U = 2.0 ** -23
+
+
+def fp32_sum_gamma(n):
+    """gamma of an fp32 sum of n terms in the class above: depth
+    63 + ceil(n / 64) + 8, plus 2 roundings of the rescale."""
+    d = 63 + (n + 63) // 64 + 8 + 2
+    return d * F32_U / (1.0 - d * F32_U)
+
+
+def bf16_span(v, d):
+    """Lowest and highest bf16 value that rounding any number within ``d``
+    of ``v`` can give (rounding is monotone)."""
+    v = np.asarray(v, np.float64)
+    return round_bf16(v - d), round_bf16(v + d)
+
+
+def rowq_spread(vo, lo, hi):
+    """Per-row quantization (``quantize_rows``) of the bf16 values ``vo``
+    against every matrix with elements in ``[lo, hi]`` (bf16 values, lo <=
+    vo <= hi).  Returns the dequantized values of ``vo`` and, per element, a
+    bound on the distance to the dequantized value of any such matrix.
+
+    For a fixed scale the quantizer is monotone, so the two ends of an
+    element's span decide.  A row's amax can take every bf16 value between
+    the largest lower and the largest upper magnitude; where that is one or
+    two values, both scales are evaluated at both ends.  Otherwise any
+    candidate b is within half an E4M3 step of its dequantized value (|b|/16
+    for normal codes, 2^-10 s below 2^-6 s) plus the saturation excess (at
+    most the amax's own span)."""
+    vo = np.asarray(vo, np.float64)
+    q, s = quantize_rows(vo)
+    s64 = s.astype(np.float64)[:, None]
+    qo = e4m3_decode(q) * s64
+    straddle = (lo <= 0) & (hi >= 0)
+    m_lo = np.where(straddle, 0.0, np.minimum(np.abs(lo), np.abs(hi)))
+    m_hi = np.maximum(np.abs(lo), np.abs(hi))
+    a_lo = m_lo.max(axis=1) if vo.shape[1] else np.zeros(vo.shape[0])
+    a_hi = m_hi.max(axis=1) if vo.shape[1] else np.zeros(vo.shape[0])
+    s_lo = quant_scale(a_lo)[:, None]
+    s_hi = quant_scale(a_hi)[:, None]
+    bits = lambda a: np.asarray(a, np.float32).view(np.uint32).astype(np.int64) >> 16
+    few = ((bits(a_hi) - bits(a_lo) <= 1) & (a_lo > 0))[:, None]
+
+    def deq(b, sc):
+        return e4m3_decode(e4m3_encode((np.asarray(b, np.float32) / sc).astype(np.float32))) * sc.astype(np.float64)
+
+    ends = np.maximum(np.abs(deq(lo, s_lo) - qo), np.abs(deq(hi, s_lo) - qo))
+    ends = np.maximum(ends, np.maximum(np.abs(deq(lo, s_hi) - qo), np.abs(deq(hi, s_hi) - qo)))
+    crude = (np.maximum(np.abs(qo - lo), np.abs(qo - hi)) + m_hi / 16.0
+             + 2.0 ** -10 * s_hi.astype(np.float64) + (a_hi - a_lo)[:, None] + 2.0 ** -20 * a_hi[:, None])
+    return qo, np.where((s_lo == s_hi) | few, ends, crude)
+
+
+def product_spread(ao, da, bo, db, n):
+    """Bound on |A' B'^T - ao bo^T| for |A' - ao| <= da, |B' - bo| <= db
+    elementwise, the product summed in fp32 over n terms and rescaled."""
+    aa, ab = np.abs(ao), np.abs(bo)
+    return da @ ab.T + aa @ db.T + da @ db.T + fp32_sum_gamma(n + 2) * ((aa + da) @ (ab + db).T)
+
+
+def fp8_forward_gu_bound(x, dst_row, offsets, w1, w3):
+    """Distance bound of an fp32 FC1 (FP8 operands, any summation order) from
+    the fp64 G and U of `layer_forward_fp8`, per routed row."""
+    qx, sx = quantize_rows(np.asarray(x, np.float32))
+    qxp = permute(qx, dst_row)
+    sxp = np.zeros(qxp.shape[0])
+    T, k = dst_row.shape
+    for j in range(k):
+        kept = dst_row[:, j] >= 0
+        sxp[dst_row[kept, j]] = sx[kept]
+    h = qxp.shape[1]
+    dg = np.zeros((qxp.shape[0], w1.shape[2])); du = np.zeros_like(dg)
+    for e in range(w1.shape[0]):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        if hi == lo:
+            continue
+        ax = np.abs(e4m3_decode(qxp[lo:hi])) * sxp[lo:hi, None]
+        for wm, out in ((w1[e], dg), (w3[e], du)):
+            q, s = quantize_cols(wm)
+            out[lo:hi] = fp32_sum_gamma(h + 2) * (ax @ (np.abs(e4m3_decode(q)) * s.astype(np.float64)[None, :]))
+    return dg, du
+
+
+def fp8_backward_envelope(dy, x, w, dst_row, offsets, w1, w3, w2, g, u, g_err=None, u_err=None, w_err=None):
+    """Per-element allowance of `layer_backward_fp8` (same arguments): a
+    bound on |result - layer_backward_fp8(...)| for every implementation
+    that follows the same recipe with fp32 sums and an fp32 SwiGLU
+    derivative.  ``g_err``, ``u_err``: distance bounds of the implementation's
+    G, U before their bf16 rounding (None: it keeps exactly round_bf16(g),
+    round_bf16(u)); ``w_err``: bounds of its gate weights' distance from
+    ``w`` ([T, k]; None: it uses ``w`` itself).
+
+    Returns the allowances of dx, dw1, dw3, dw2, dxp; the bounds d_g, d_u,
+    d_da, d_dg, d_du, d_a (per routed row) on the distance of the values an
+    implementation rounds from the fp64 ones; and d_dxp, d_dw2, d_dw13, the
+    bounds of each fp32 sum's own rounding error (over its own operands)."""
+    E = w1.shape[0]
+    T, k = dst_row.shape
+    dy = np.asarray(dy, np.float64)
+    w = np.asarray(w, np.float64)
+    xp = permute(np.asarray(x, np.float64), dst_row)
+    R, h = xp.shape
+    hf = w1.shape[2]
+    # dYp = w dY rounded to bf16: with the weights only known within w_err,
+    # any bf16 value in the span; the dA row scale w s_t moves by w_err s_t
+    wdy = permute(dy, dst_row, row_scale=w)
+    dyp_b = round_bf16(wdy)
+    w_err = np.zeros(w.shape) if w_err is None else np.asarray(w_err, np.float64)
+    w_rel = permute(np.ones((T, 1)), dst_row, row_scale=w_err / np.maximum(w, 1e-300))[:, 0]
+    d_wdy = permute(np.abs(dy), dst_row, row_scale=w_err) + (w_err > 0).any() * F32_U * np.abs(wdy)
+    dyp_l, dyp_h = bf16_span(wdy, d_wdy)
+    qdy, sdy = quantize_rows(np.asarray(dy, np.float32))
+    qdyp = permute(qdy, dst_row)
+    sdyp = np.ones(R)
+    for j in range(k):
+        kept = dst_row[:, j] >= 0
+        sdyp[dst_row[kept, j]] = np.asarray(w[kept, j], np.float32) * np.asarray(sdy[kept], np.float32)
+    g_err = np.zeros((R, hf)) if g_err is None else np.asarray(g_err, np.float64)
+    u_err = np.zeros((R, hf)) if u_err is None else np.asarray(u_err, np.float64)
+    out = {n: np.zeros((R, hf)) for n in ("d_da", "d_dg", "d_du", "d_a")}
+    out["d_g"], out["d_u"] = g_err, u_err
+    out["d_dxp"] = np.zeros((R, h)); out["dxp"] = np.zeros((R, h))
+    dxp_abs = np.zeros((R, h))
+    for n, shp in (("dw1", w1.shape), ("dw3", w3.shape), ("dw2", w2.shape), ("d_dw2", w2.shape),
+                   ("d_dw13", (E, h, 2 * hf))):
+        out[n] = np.zeros(shp)
+    for e in range(E):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        if hi == lo:
+            continue
+        n_e = hi - lo
+        # dA: exact codes, fp32 sum over h
+        qw2, sw2 = quantize_rows(np.asarray(w2[e], np.float32))
+        adyp = np.abs(e4m3_decode(qdyp[lo:hi])) * sdyp[lo:hi, None]
+        aw2 = np.abs(e4m3_decode(qw2)) * sw2.astype(np.float64)[:, None]
+        qdyv = e4m3_decode(qdyp[lo:hi]) * sdyp[lo:hi, None]
+        da = qdyv @ (e4m3_decode(qw2) * sw2.astype(np.float64)[:, None]).T
+        d_da = fp32_sum_gamma(h + 2) * (adyp @ aw2.T)
+        d_da = d_da + (w_rel[lo:hi, None] + F32_U * (w_rel[lo:hi, None] > 0)) * (np.abs(da) + d_da)
+        # the kept G, U: the bf16 values any such implementation may hold
+        gl, gh = bf16_span(g[lo:hi], g_err[lo:hi])
+        ul, uh = bf16_span(u[lo:hi], u_err[lo:hi])
+        ge, ue = round_bf16(g[lo:hi]), round_bf16(u[lo:hi])
+        dG, dU = gh - gl, uh - ul
+        umax = np.maximum(np.abs(ul), np.abs(uh))
+        s = sigmoid(ge)
+        gmax = np.abs(ge) + dG                       # |G'| for every candidate G'
+        smax = sigmoid(ge + dG)                      # s(G') <= s(ge + dG)
+        silu_max = np.abs(ge * s) + 1.1 * dG
+        dabs = np.abs(da) + d_da
+        # A = SiLU(G) U before its bf16 rounding
+        a0 = ge * s * ue
+        d_a = 1.1 * dG * umax + np.abs(ge * s) * dU + 4.0 * F32_U * (1.0 + gmax) * silu_max * umax
+        # dG, dU before their bf16 rounding
+        fgo = ue * s * (1.0 + ge * (1.0 - s))
+        d_dg = d_da * np.abs(fgo) + dabs * (1.1 * dU + 0.55 * umax * dG) \
+            + 6.0 * F32_U * (1.0 + gmax) ** 2 * dabs * umax * smax
+        d_du = d_da * np.abs(ge * s) + dabs * 1.1 * dG + 4.0 * F32_U * (1.0 + gmax) * dabs * silu_max
+        dg0, du0 = da * fgo, da * ge * s
+        for n, v in (("d_da", d_da), ("d_dg", d_dg), ("d_du", d_du), ("d_a", d_a)):
+            out[n][lo:hi] = v
+        a_o = round_bf16(a0)
+        a_l, a_h = bf16_span(a0, d_a)
+        gu0 = np.concatenate([dg0, du0], axis=1)
+        d_gu = np.concatenate([d_dg, d_du], axis=1)
+        gu_o = round_bf16(gu0)
+        gu_l, gu_h = bf16_span(gu0, d_gu)
+        # dXp = [dG|dU] W13^T: per-row codes of dG|dU, exact weight codes
+        qgu, sp_gu = rowq_spread(gu_o, gu_l, gu_h)
+        w13 = np.concatenate([np.asarray(w1[e], np.float64), np.asarray(w3[e], np.float64)], axis=1)
+        q13, s13 = quantize_rows(np.asarray(w13, np.float32))
+        b13 = e4m3_decode(q13) * s13.astype(np.float64)[:, None]
+        c = qgu @ b13.T
+        d_c = product_spread(qgu, sp_gu, b13, np.zeros_like(b13), 2 * hf)
+        out["d_dxp"][lo:hi] = fp32_sum_gamma(2 * hf + 2) * ((np.abs(qgu) + sp_gu) @ np.abs(b13).T)
+        # the stored bf16 dXp: any value between the roundings of the span's ends
+        c_o = round_bf16(c)
+        c_l, c_h = bf16_span(c, d_c)
+        out["dxp"][lo:hi] = np.maximum(c_h - c_o, c_o - c_l)
+        dxp_abs[lo:hi] = np.abs(c_o)
+        # dW2 = A^T dYp: A^T per channel (span), dYp^T exact
+        qat, sp_at = rowq_spread(a_o.T, a_l.T, a_h.T)
+        qdt, sp_dt = rowq_spread(dyp_b[lo:hi].T, dyp_l[lo:hi].T, dyp_h[lo:hi].T)
+        out["dw2"][e] = product_spread(qat, sp_at, qdt, sp_dt, n_e)
+        out["d_dw2"][e] = fp32_sum_gamma(n_e + 2) * ((np.abs(qat) + sp_at) @ np.abs(qdt).T)
+        # dW13 = Xp^T [dG|dU]: Xp^T exact, [dG|dU]^T per channel (span)
+        qxt, sp_xt = rowq_spread(xp[lo:hi].T, xp[lo:hi].T, xp[lo:hi].T)
+        qgt, sp_gt = rowq_spread(gu_o.T, gu_l.T, gu_h.T)
+        d13 = product_spread(qxt, sp_xt, qgt, sp_gt, n_e)
+        out["d_dw13"][e] = fp32_sum_gamma(n_e + 2) * (np.abs(qxt) @ (np.abs(qgt) + sp_gt).T)
+        out["dw1"][e] = d13[:, :hf]
+        out["dw3"][e] = d13[:, hf:]
+    # dX: the k stored rows of a token added in fp32 and rounded to bf16 once;
+    # that rounding of the result itself (half a bf16 ulp) is left to the caller
+    mag = combine(dxp_abs + out["dxp"], dst_row, None)
+    out["dx"] = combine(out["dxp"], dst_row, None) + fp32_sum_gamma(k) * mag + 2.0 ** -8 * combine(out["dxp"], dst_row, None)
+    return out

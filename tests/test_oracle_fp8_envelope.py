@@ -1,0 +1,168 @@
+"""Pins for the oracle's allowance of the FP8 backward (`fp8_backward_envelope`).
+
+The allowance claims: every implementation of the FP8 backward recipe whose
+values before each rounding lie within the stated distance of the fp64 ones
+(fp32 sums, an fp32 SwiGLU derivative, fp32 gate weights, an fp32 forward)
+ends within the allowance of `layer_backward_fp8`.  Pinned by
+  * brute force of the per-row quantizer's spread on tiny matrices (every
+    combination of candidate values enumerated);
+  * nearby implementations: every pre-rounding value replaced by a random
+    value within its bound (and the gate weights, G and U moved within
+    theirs) must stay inside the allowance;
+  * a genuine fp32 evaluation (dA summed in float32 in the allowed order
+    with the largest error, float32 exponentials and products for the SwiGLU
+    terms) must stay inside the allowance;
+  * the allowance is not vacuous: small on average, zero where no quantizer
+    input can move.
+"""
+import itertools
+
+import numpy as np
+import pytest
+
+import moe_synth
+from moe_synth import to_f32
+from oracle import moe_ref as ref
+
+
+def _case(seed, **over):
+    sh = dict(T=160, h=128, h_ffn=128, E=4, k=2)
+    sh.update(over)
+    wl = moe_synth.WORKLOADS["dsmoe"].scaled(name="env", dtype="fp8", **sh)
+    inp = moe_synth.gen_all(wl, seed=seed)
+    f = lambda key: to_f32(inp[key])
+    fw = ref.layer_forward_fp8(f("x"), f("w_gate"), inp["bias"], f("w1"), f("w3"), f("w2"), wl.k)
+    args = (f("dy"), f("x"), fw["w"], fw["dst_row"], fw["offsets"], f("w1"), f("w3"), f("w2"), fw["g"], fw["u"])
+    return fw, args
+
+
+def _excess(got, base, allow):
+    return {n: float(((np.abs(got[n] - base[n]) - allow[n]) / np.sqrt(np.mean(base[n] ** 2))).max())
+            for n in ("dx", "dw1", "dw3", "dw2")}
+
+
+def test_rowq_spread_brute_force():
+    """Every matrix with entries in [lo, hi] (bf16 values; here each entry has
+    one or two candidates, the amax too) quantizes within the spread."""
+    rng = np.random.default_rng(0)
+    checked = 0
+    for trial in range(60):
+        vo = ref.round_bf16(rng.normal(0, 1, (2, 4)) * rng.choice([1e-3, 1.0, 30.0]))
+        # step some entries (the amax included, sometimes) to their bf16 neighbour
+        ulp = np.abs(vo) * 2.0 ** -7
+        pick = rng.random(vo.shape) < 0.5
+        if trial % 3 == 0:
+            pick[:, np.argmax(np.abs(vo), axis=1)] = True
+        up = rng.random(vo.shape) < 0.5
+        lo = np.where(pick & ~up, ref.round_bf16(vo - ulp), vo)
+        hi = np.where(pick & up, ref.round_bf16(vo + ulp), vo)
+        qo, spread = ref.rowq_spread(vo, lo, hi)
+        q, s = ref.quantize_rows(vo)
+        np.testing.assert_array_equal(qo, ref.e4m3_decode(q) * s.astype(np.float64)[:, None])
+        cands = [sorted({a, b}) for a, b in zip(lo.ravel(), hi.ravel())]
+        for combo in itertools.product(*cands):
+            m = np.array(combo).reshape(vo.shape)
+            qm, sm = ref.quantize_rows(m)
+            dq = ref.e4m3_decode(qm) * sm.astype(np.float64)[:, None]
+            assert np.all(np.abs(dq - qo) <= spread), trial
+            checked += 1
+    assert checked > 1000
+
+
+def test_rowq_spread_is_zero_without_candidates():
+    v = ref.round_bf16(np.random.default_rng(1).normal(0, 1, (5, 33)))
+    _, spread = ref.rowq_spread(v, v, v)
+    assert not spread.any()
+
+
+@pytest.mark.parametrize("layer", [False, True], ids=["shared_gu", "layer"])
+def test_envelope_contains_nearby_implementations(layer):
+    fw, args = _case(2, T=240, E=6, k=3)
+    dy, x, w, dst_row, offsets, w1, w3, w2, g, u = args
+    if layer:
+        g_err, u_err = ref.fp8_forward_gu_bound(x, dst_row, offsets, w1, w3)
+        w_err = ref.topk_weight_bound(fw["logits"], fw["idx"])
+    else:
+        g_err = u_err = w_err = None
+    env = ref.fp8_backward_envelope(*args, g_err=g_err, u_err=u_err, w_err=w_err)
+    base = ref.layer_backward_fp8(*args)
+    rec = {}
+
+    def record(name, e, v):
+        rec[(name, e)] = np.array(v, copy=True)
+        return v
+
+    ref.layer_backward_fp8(*args, noise=record)
+    worst = -np.inf
+    for trial in range(4):
+        rng = np.random.default_rng(10 + trial)
+
+        def noise(name, e, v):
+            lo, hi = int(offsets[e]), int(offsets[e + 1])
+            mask = rng.random(v.shape) < 0.5
+            if name in ("dxp", "dw2", "dw13"):       # an fp32 sum of the implementation's own operands
+                d = env["d_dxp"][lo:hi] if name == "dxp" else env["d_" + name][e]
+                return v + d * rng.uniform(-1, 1, v.shape) * mask
+            return rec[(name, e)] + env["d_" + name][lo:hi] * rng.uniform(-1, 1, v.shape) * mask
+
+        w2_ = w if w_err is None else (w + 0.9 * w_err * rng.uniform(-1, 1, w.shape)).astype(np.float32)
+        got = ref.layer_backward_fp8(dy, x, w2_, dst_row, offsets, w1, w3, w2, g, u, noise=noise)
+        worst = max(worst, max(_excess(got, base, env).values()))
+    assert worst <= 0.0, worst
+
+
+def test_envelope_contains_fp32_evaluation():
+    """dA in float32 from the same codes and fp32 scales, summed as the worst
+    member of the allowed class does (one product after the other within
+    blocks of 64, then block after block: depth 63 + h/64), then the SwiGLU
+    terms in float32, as an fp32 kernel would form them."""
+    fw, args = _case(3, T=200, h=1024, h_ffn=128, E=4, k=2)
+    dy, x, w, dst_row, offsets, w1, w3, w2, g, u = args
+    env = ref.fp8_backward_envelope(*args)
+    base = ref.layer_backward_fp8(*args)
+    T, k = dst_row.shape
+    qdy, sdy = ref.quantize_rows(dy)
+    qdyp = ref.permute(qdy, dst_row)
+    sdyp = np.zeros(T * k, np.float32)
+    for j in range(k):
+        sdyp[dst_row[:, j]] = np.float32(1) * w[:, j].astype(np.float32) * sdy.astype(np.float32)
+    f32 = {}
+
+    def fp32(name, e, v):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        if name == "da":
+            qw2, sw2 = ref.quantize_rows(w2[e])
+            prod = (ref.e4m3_decode(qdyp[lo:hi]).astype(np.float32)[:, None, :]
+                    * ref.e4m3_decode(qw2).astype(np.float32)[None, :, :])       # exact in fp32
+            blk = prod.reshape(prod.shape[0], prod.shape[1], -1, 64)
+            part = np.add.accumulate(blk, axis=3, dtype=np.float32)[..., -1]
+            acc = np.add.accumulate(part, axis=2, dtype=np.float32)[:, :, -1]
+            f32["da"] = (acc * sdyp[lo:hi, None]) * sw2.astype(np.float32)[None, :]
+            return f32["da"].astype(np.float64)
+        if name in ("g", "u"):
+            f32[name] = ref.round_bf16(v).astype(np.float32)
+            return v
+        G, U, dA = f32["g"], f32["u"], f32["da"]
+        one = np.float32(1)
+        sg = one / (one + np.exp(-G))
+        if name == "a":
+            return ((G * sg) * U).astype(np.float64)
+        if name == "dg":
+            return (dA * U * sg * (one + G * (one - sg))).astype(np.float64)
+        if name == "du":
+            return (dA * (G * sg)).astype(np.float64)
+        return v
+
+    got = ref.layer_backward_fp8(*args, noise=fp32)
+    moved = {n: float(np.abs(got[n] - base[n]).max()) for n in ("dx", "dw1", "dw3", "dw2")}
+    assert max(_excess(got, base, env).values()) <= 0.0
+    assert max(moved.values()) > 0.0          # the fp32 evaluation did change something
+
+
+def test_envelope_is_small():
+    fw, args = _case(4, T=300, h=256, h_ffn=256, E=4, k=2)
+    env = ref.fp8_backward_envelope(*args)
+    base = ref.layer_backward_fp8(*args)
+    for n, bound in (("dx", 3e-2), ("dw1", 1e-2), ("dw3", 1e-2), ("dw2", 1e-2)):
+        rms = np.sqrt(np.mean(base[n] ** 2))
+        assert env[n].mean() / rms < bound, n
