@@ -76,7 +76,14 @@ def cpu_baseline(wl, inp, n_tokens, seed=0):
     w1, w3, w2 = PerExpert(inp["w1"]), PerExpert(inp["w3"]), PerExpert(inp["w2"])
     t0 = time.perf_counter()
     if wl.dtype == "fp8":
-        ref.layer_forward_fp8(x, wg, inp["bias"], w1, w3, w2, wl.k)
+        out = ref.layer_forward_fp8(x, wg, inp["bias"], w1, w3, w2, wl.k)
+        if wl.backward:
+            dy = to_f32(inp["dy"][:n_tokens])
+            ref.aux_balance_loss(out["logits"], out["idx"], wl.E, wl.k, AUX_ALPHA)
+            ref.layer_backward_fp8(dy, x, out["w"], out["dst_row"], out["offsets"], w1, w3, w2,
+                                   out["g"], out["u"])
+            ref.router_backward(dy, out["yp"][out["dst_row"]], x, wg, out["logits"], out["idx"],
+                                out["w"], AUX_ALPHA)
     else:
         out = ref.layer_forward(x, wg, inp["bias"], w1, w3, w2, wl.k)
         if wl.backward:

@@ -75,12 +75,14 @@ extern "C" {
  *   w2   [E][h][h_ffn]    FC2 weight transposed (h_ffn contiguous).
  *   w13_scale [E][2*h_ffn], w2_scale [E][h]: FP8 only, per packed row
  *        (= per output channel) dequantization scales; NULL otherwise.
- *   w13_bwd [E][h][2*h_ffn]: BF16 only, for the backward: W1 and W3 side by
- *        side along h_ffn in the same 32-channel interleave as w13's rows
+ *   w13_bwd [E][h][2*h_ffn]: for the backward (BF16 or FP8): W1 and W3 side
+ *        by side along h_ffn in the same 32-channel interleave as w13's rows
  *        (column p holds W1 or W3 column (p/64)*32 + p%32 by the parity of
  *        p/32).  NULL when no backward will run.
- *   w2_bwd  [E][h_ffn][h]: BF16 only, W2 as given (h contiguous), for the
- *        backward; NULL when no backward will run.
+ *   w2_bwd  [E][h_ffn][h]: for the backward (BF16 or FP8), W2 as given (h
+ *        contiguous); NULL when no backward will run.
+ *   w13_bwd_scale [E][h], w2_bwd_scale [E][h_ffn]: FP8 backward copies only,
+ *        one scale per row over that row (amax/448); NULL otherwise.
  *   dtype: MOE_F32, MOE_BF16 or MOE_FP8_E4M3.
  */
 typedef struct {
@@ -92,10 +94,12 @@ typedef struct {
   const float* w2_scale;
   const void* w13_bwd;
   const void* w2_bwd;
+  const float* w13_bwd_scale;
+  const float* w2_bwd_scale;
 } moe_weights;
 
 /* Bytes needed for w13 (`which`=0), w2 (1), w13_scale (2), w2_scale (3),
- * w13_bwd (4), w2_bwd (5). */
+ * w13_bwd (4), w2_bwd (5), w13_bwd_scale (6), w2_bwd_scale (7). */
 size_t moe_packed_weight_bytes(int which, int E, int h, int h_ffn, int dtype);
 
 /*
@@ -109,12 +113,15 @@ size_t moe_packed_weight_bytes(int which, int E, int h, int h_ffn, int dtype);
  *   channel is all zero); codes = E4M3(w / s) rounded to nearest even with
  *   the division in fp32, saturating at +-448.
  *   Outputs: see moe_weights; scales are written only for FP8 (may be NULL
- *   otherwise).  w13_bwd / w2_bwd are written when non-NULL (BF16 only).
+ *   otherwise).  w13_bwd / w2_bwd are written when non-NULL (BF16, or FP8
+ *   with w13_bwd_scale / w2_bwd_scale: one scale per row over the row, the
+ *   dimension the backward contracts).
  *   h and h_ffn must be multiples of 128.
  */
 int moe_pack_weights(const void* w1, const void* w3, const void* w2, int in_dtype, int E, int h,
                      int h_ffn, int out_dtype, void* w13, void* w2_packed, float* w13_scale,
-                     float* w2_scale, void* w13_bwd, void* w2_bwd, void* stream);
+                     float* w2_scale, void* w13_bwd, void* w2_bwd, float* w13_bwd_scale,
+                     float* w2_bwd_scale, void* stream);
 
 /*
  * Router: gate GEMM, top-k and softmax over the k selected logits.
@@ -159,7 +166,8 @@ size_t moe_permute_workspace_size(int T, int E, int k);
  *            (src BF16) or MOE_FP8_E4M3 (src BF16; per-token quantization:
  *            dst_scale[row] = amax_t / 448 (1 for an all-zero row), codes =
  *            E4M3(src / scale) with the division in fp32, nearest even,
- *            saturating).  row_scale must be NULL for FP8.
+ *            saturating).  With FP8 and row_scale the codes stay those of
+ *            src[t] and dst_scale[row] = row_scale[t][j] * scale (fp32).
  *   dst_scale[T*k] fp32, FP8 only (NULL otherwise).
  *   ws / ws_bytes: workspace, at least moe_permute_workspace_size(T, E, k)
  *            bytes when topk_idx != NULL (may be NULL otherwise).
@@ -222,7 +230,7 @@ size_t moe_grouped_workspace_size(int rows, int h, int h_ffn, int E, int dtype);
  *   W        packed weights (moe_pack_weights).
  *   offsets  [E+1] int32 device array from moe_permute; rows of expert e are
  *            offsets[e] .. offsets[e+1]-1; offsets[E] <= rows.
- *   h13_save [rows][2*h_ffn] bf16 or NULL: when given, FC1's output is kept
+ *   h13_save [rows][2*h_ffn] bf16 or NULL (BF16 or FP8 weights): when given, FC1's output is kept
  *            for the backward, columns in the packed order of W->w13.
  *   yp       [rows][h] expert outputs: fp32 for MOE_F32 weights, else bf16.
  *   Math: G = xp W1_e, U = xp W3_e (fp32 accumulation), A = SiLU(G) * U,
@@ -271,6 +279,30 @@ int moe_grouped_swiglu_bwd(const void* dyp, const void* xp, const void* h13_save
  */
 int moe_combine(const void* yp, int yp_dtype, const int32_t* dst_row, const float* topk_w, int T,
                 int h, int k, void* y, int y_dtype, void* stream);
+
+/*
+ * FP8 backward of the expert GroupedGEMM (MegaScale-MoE paper review §三:
+ * FP8 training with per-token instead of per-tensor scales; research digest
+ * §3.4: fp32 sums).  Same products as moe_grouped_swiglu_bwd, on E4M3 codes:
+ *   dA  = dYp W2^T: dYp codes per routed row (dyp_q, dyp_scale, from
+ *         moe_permute of dY to FP8 with row_scale = topk_w) and W2 per h_ffn
+ *         row (W->w2_bwd, w2_bwd_scale); dG, dU and A as in the BF16 backward,
+ *         kept in bf16;
+ *   dXp = [dG|dU] W13^T: dG|dU quantized per routed row, W13 per h row
+ *         (W->w13_bwd, w13_bwd_scale); dxp bf16;
+ *   dW2 = A^T dYp, dW13 = Xp^T [dG|dU]: these sum over tokens, where a
+ *         per-token scale cannot leave the sum, so both transposed operands
+ *         are quantized per channel over the expert's rows; fp32 out.
+ *   Every product is a rank-1 rescale of an fp32 MFMA sum.
+ *   dyp [rows][h] bf16: w * dY in dispatch order (moe_permute with row_scale),
+ *   for dW2; xp [rows][h] bf16; h13_save as for the BF16 backward.
+ *   W: dtype MOE_FP8_E4M3 with w13_bwd, w2_bwd and their scales.
+ */
+size_t moe_grouped_bwd_fp8_workspace_size(int rows, int h, int h_ffn, int E);
+int moe_grouped_swiglu_bwd_fp8(const void* dyp_q, const float* dyp_scale, const void* dyp,
+                               const void* xp, const void* h13_save, const moe_weights* W,
+                               const int32_t* offsets, int rows, void* dxp, float* dw1, float* dw3,
+                               float* dw2, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * Router backward: gradients of  sum_t <dY_t, y_t> + L_aux  through the gate

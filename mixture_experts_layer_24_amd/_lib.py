@@ -30,12 +30,12 @@ F = ctypes.c_float
 class MoeWeights(ctypes.Structure):
     _fields_ = [("dtype", I), ("E", I), ("h", I), ("h_ffn", I),
                 ("w13", P), ("w2", P), ("w13_scale", P), ("w2_scale", P),
-                ("w13_bwd", P), ("w2_bwd", P)]
+                ("w13_bwd", P), ("w2_bwd", P), ("w13_bwd_scale", P), ("w2_bwd_scale", P)]
 
 
 SIGNATURES = {
     "moe_packed_weight_bytes": (SZ, [I, I, I, I, I]),
-    "moe_pack_weights": (I, [P, P, P, I, I, I, I, I, P, P, P, P, P, P, P]),
+    "moe_pack_weights": (I, [P, P, P, I, I, I, I, I, P, P, P, P, P, P, P, P, P]),
     "moe_route": (I, [P, P, P, P, I, I, I, I, I, P, P, P]),
     "moe_permute_workspace_size": (SZ, [I, I, I]),
     "moe_permute": (I, [P, I, P, P, I, I, I, I, P, P, P, P, P, I, P, P, SZ, P]),
@@ -48,6 +48,8 @@ SIGNATURES = {
     "moe_grouped_bwd_workspace_size": (SZ, [I, I, I, I, I]),
     "moe_grouped_swiglu_bwd": (I, [P, P, P, ctypes.POINTER(MoeWeights), P, I, P, P, P, P, P, SZ, P]),
     "moe_combine": (I, [P, I, P, P, I, I, I, P, I, P]),
+    "moe_grouped_bwd_fp8_workspace_size": (SZ, [I, I, I, I]),
+    "moe_grouped_swiglu_bwd_fp8": (I, [P, P, P, P, P, ctypes.POINTER(MoeWeights), P, I, P, P, P, P, P, SZ, P]),
     "moe_router_bwd_workspace_size": (SZ, [I, I, I]),
     "moe_router_bwd": (I, [P, P, P, P, P, P, P, I, I, I, I, F, I, P, P, P, P, P, P, P, P, SZ, P]),
     "moe_router_aux_workspace_size": (SZ, [I, I]),

@@ -66,7 +66,7 @@ extern "C" {
 
 const char* moe_last_error(void) { return g_err; }
 
-int moe_version(void) { return 2; }
+int moe_version(void) { return 3; }
 
 size_t moe_packed_weight_bytes(int which, int E, int h, int h_ffn, int dtype) {
   if (E <= 0 || h <= 0 || h_ffn <= 0 || dtype < MOE_F32 || dtype > MOE_FP8_E4M3) return 0;
@@ -76,15 +76,18 @@ size_t moe_packed_weight_bytes(int which, int E, int h, int h_ffn, int dtype) {
     case 1: return e * hh * hf * esize(dtype);
     case 2: return dtype == MOE_FP8_E4M3 ? e * 2 * hf * 4 : 0;
     case 3: return dtype == MOE_FP8_E4M3 ? e * hh * 4 : 0;
-    case 4: return dtype == MOE_BF16 ? e * hh * 2 * hf * 2 : 0;
-    case 5: return dtype == MOE_BF16 ? e * hf * hh * 2 : 0;
+    case 4: return dtype == MOE_F32 ? 0 : e * hh * 2 * hf * esize(dtype);
+    case 5: return dtype == MOE_F32 ? 0 : e * hf * hh * esize(dtype);
+    case 6: return dtype == MOE_FP8_E4M3 ? e * hh * 4 : 0;
+    case 7: return dtype == MOE_FP8_E4M3 ? e * hf * 4 : 0;
   }
   return 0;
 }
 
 int moe_pack_weights(const void* w1, const void* w3, const void* w2, int in_dtype, int E, int h,
                      int h_ffn, int out_dtype, void* w13, void* w2_packed, float* w13_scale,
-                     float* w2_scale, void* w13_bwd, void* w2_bwd, void* stream) {
+                     float* w2_scale, void* w13_bwd, void* w2_bwd, float* w13_bwd_scale,
+                     float* w2_bwd_scale, void* stream) {
   REQ(E >= 1 && E <= MOE_MAX_EXPERTS, MOE_ERR_SHAPE, "E=%d outside [1, %d]", E, MOE_MAX_EXPERTS);
   REQ(h > 0 && h % 128 == 0 && h_ffn > 0 && h_ffn % 128 == 0, MOE_ERR_SHAPE,
       "h=%d and h_ffn=%d must be positive multiples of 128", h, h_ffn);
@@ -93,13 +96,17 @@ int moe_pack_weights(const void* w1, const void* w3, const void* w2, int in_dtyp
   REQ(ok, MOE_ERR_DTYPE, "unsupported pack %d -> %d", in_dtype, out_dtype);
   PTR(w1); PTR(w3); PTR(w2); PTR(w13); PTR(w2_packed);
   if (out_dtype == MOE_FP8_E4M3) { PTR(w13_scale); PTR(w2_scale); }
-  OPT(w13_bwd); OPT(w2_bwd);
-  REQ((w13_bwd == nullptr && w2_bwd == nullptr) || out_dtype == MOE_BF16, MOE_ERR_DTYPE,
-      "backward weight layouts are only produced for bf16");
+  OPT(w13_bwd); OPT(w2_bwd); OPT(w13_bwd_scale); OPT(w2_bwd_scale);
+  REQ((w13_bwd == nullptr && w2_bwd == nullptr) || out_dtype != MOE_F32, MOE_ERR_DTYPE,
+      "backward weight layouts are produced for bf16 and fp8");
+  if (out_dtype == MOE_FP8_E4M3) {
+    REQ(w13_bwd == nullptr || w13_bwd_scale != nullptr, MOE_ERR_ARG, "FP8 w13_bwd needs w13_bwd_scale");
+    REQ(w2_bwd == nullptr || w2_bwd_scale != nullptr, MOE_ERR_ARG, "FP8 w2_bwd needs w2_bwd_scale");
+  }
   moe_launch::clear_status();
   return launched(moe_launch::pack_weights(w1, w3, w2, in_dtype, E, h, h_ffn, out_dtype, w13,
                                            w2_packed, w13_scale, w2_scale, w13_bwd, w2_bwd,
-                                           (hipStream_t)stream),
+                                           w13_bwd_scale, w2_bwd_scale, (hipStream_t)stream),
                   "moe_pack_weights");
 }
 
@@ -143,10 +150,7 @@ int moe_permute(const void* src, int src_dtype, const int32_t* topk_idx, const f
   bool ok = (src_dtype == MOE_F32 && dst_dtype == MOE_F32) ||
             (src_dtype == MOE_BF16 && (dst_dtype == MOE_BF16 || dst_dtype == MOE_FP8_E4M3));
   REQ(ok, MOE_ERR_DTYPE, "unsupported permute %d -> %d", src_dtype, dst_dtype);
-  if (dst_dtype == MOE_FP8_E4M3) {
-    PTR(dst_scale);
-    REQ(row_scale == nullptr, MOE_ERR_ARG, "row_scale is not supported with FP8 output");
-  }
+  if (dst_dtype == MOE_FP8_E4M3) PTR(dst_scale);
   PTR(src); PTR(dst); PTR(dst_row); OPT(row_scale);
   if (topk_idx) {
     PTR(topk_idx); PTR(counts); PTR(offsets); PTR(src_tok);
@@ -195,10 +199,7 @@ int moe_permute_local(const void* src, int src_dtype, const int32_t* topk_idx, c
   bool ok = (src_dtype == MOE_F32 && dst_dtype == MOE_F32) ||
             (src_dtype == MOE_BF16 && (dst_dtype == MOE_BF16 || dst_dtype == MOE_FP8_E4M3));
   REQ(ok, MOE_ERR_DTYPE, "unsupported permute %d -> %d", src_dtype, dst_dtype);
-  if (dst_dtype == MOE_FP8_E4M3) {
-    PTR(dst_scale);
-    REQ(row_scale == nullptr, MOE_ERR_ARG, "row_scale is not supported with FP8 output");
-  }
+  if (dst_dtype == MOE_FP8_E4M3) PTR(dst_scale);
   PTR(src); PTR(dst); PTR(dst_row); OPT(row_scale); PTR(counts); PTR(offsets); PTR(src_tok);
   unsigned char* w = static_cast<unsigned char*>(ws);
   int32_t* local = reinterpret_cast<int32_t*>(w);
@@ -270,8 +271,8 @@ int moe_grouped_swiglu_fwd(const void* xp, const float* xp_scale, const moe_weig
   REQ(rows >= 0, MOE_ERR_ARG, "rows=%d is negative", rows);
   PTR(xp); PTR(offsets); PTR(yp); OPT(h13_save);
   if (W->dtype == MOE_FP8_E4M3) PTR(xp_scale);
-  REQ(h13_save == nullptr || W->dtype == MOE_BF16, MOE_ERR_DTYPE,
-      "h13_save is only supported with bf16 weights");
+  REQ(h13_save == nullptr || W->dtype != MOE_F32, MOE_ERR_DTYPE,
+      "h13_save is only supported with bf16 and fp8 weights");
   if (rows == 0) return MOE_OK;
   size_t need = moe_launch::grouped_fwd_ws_bytes(rows, W->h, W->h_ffn, W->E, W->dtype);
   REQ(ws != nullptr && ws_bytes >= need, MOE_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given",
@@ -325,6 +326,32 @@ int moe_combine(const void* yp, int yp_dtype, const int32_t* dst_row, const floa
   return launched(moe_launch::combine_rows(yp, yp_dtype, dst_row, topk_w, T, h, k, y, y_dtype,
                                            (hipStream_t)stream),
                   "moe_combine");
+}
+
+size_t moe_grouped_bwd_fp8_workspace_size(int rows, int h, int h_ffn, int E) {
+  if (rows < 0 || h <= 0 || h_ffn <= 0 || E <= 0) return 0;
+  return moe_launch::grouped_bwd_fp8_ws_bytes(rows > 0 ? rows : 1, h, h_ffn, E);
+}
+
+int moe_grouped_swiglu_bwd_fp8(const void* dyp_q, const float* dyp_scale, const void* dyp,
+                               const void* xp, const void* h13_save, const moe_weights* W,
+                               const int32_t* offsets, int rows, void* dxp, float* dw1, float* dw3,
+                               float* dw2, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_weights(W);
+  if (rc) return rc;
+  REQ(W->dtype == MOE_FP8_E4M3, MOE_ERR_DTYPE, "the FP8 backward needs FP8 weights");
+  REQ(W->w13_bwd && W->w2_bwd && W->w13_bwd_scale && W->w2_bwd_scale, MOE_ERR_ARG,
+      "FP8 backward weight layouts and scales are required");
+  REQ(rows >= 0, MOE_ERR_ARG, "rows=%d is negative", rows);
+  PTR(dyp_q); PTR(dyp_scale); PTR(dyp); PTR(xp); PTR(h13_save); PTR(offsets); PTR(dxp);
+  PTR(dw1); PTR(dw3); PTR(dw2);
+  const size_t need = moe_launch::grouped_bwd_fp8_ws_bytes(rows > 0 ? rows : 1, W->h, W->h_ffn, W->E);
+  REQ(ws != nullptr && ws_bytes >= need, MOE_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given",
+      need, ws ? ws_bytes : size_t(0));
+  moe_launch::clear_status();
+  return launched(moe_launch::grouped_bwd_fp8(dyp_q, dyp_scale, dyp, xp, h13_save, W, offsets, rows,
+                                              dxp, dw1, dw3, dw2, ws, (hipStream_t)stream),
+                  "moe_grouped_swiglu_bwd_fp8");
 }
 
 size_t moe_router_bwd_workspace_size(int T, int h, int E) {

@@ -76,6 +76,37 @@ __device__ __forceinline__ float wave_max(float v) {
 
 __host__ __device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
+// Per-row E4M3 quantization of a bf16 row (length a multiple of 8) by one
+// wave: scale s = amax / 448 (1 for an all-zero row), codes = E4M3(v / s)
+// with the division in fp32.
+__device__ __forceinline__ void rowq_wave(const uint16_t* __restrict__ src, int len,
+                                          uint8_t* __restrict__ dst, float* __restrict__ scale) {
+  const int lane = threadIdx.x & 63;
+  float amax = 0.f;
+  for (int c = lane * 8; c < len; c += 512) {
+    const u32x4 v = *reinterpret_cast<const u32x4*>(src + c);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) amax = fmaxf(amax, fmaxf(fabsf(bf16_lo(v[i])), fabsf(bf16_hi(v[i]))));
+  }
+  amax = wave_max(amax);
+  const float s = amax > 0.f ? amax / 448.0f : 1.0f;
+  if (lane == 0) *scale = s;
+  for (int c = lane * 8; c < len; c += 512) {
+    const u32x4 v = *reinterpret_cast<const u32x4*>(src + c);
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      lo |= f32_to_e4m3(bf16_lo(v[i]) / s) << (16 * i);
+      lo |= f32_to_e4m3(bf16_hi(v[i]) / s) << (16 * i + 8);
+      hi |= f32_to_e4m3(bf16_lo(v[2 + i]) / s) << (16 * i);
+      hi |= f32_to_e4m3(bf16_hi(v[2 + i]) / s) << (16 * i + 8);
+    }
+    *reinterpret_cast<uint2*>(dst + c) = make_uint2(lo, hi);
+  }
+}
+
+
+
 // Allow a kernel to use more than the default 64 KB of dynamic LDS (gfx950
 // has 160 KB per CU).  Called once per kernel before its first launch.
 template <typename Kernel>
@@ -121,7 +152,12 @@ int capacity_drop(const int32_t* topk_idx, const float* logits, int T, int E, in
 size_t capacity_ws_bytes(int T, int E, int k);
 int pack_weights(const void* w1, const void* w3, const void* w2, int in_dt, int E, int h,
                  int h_ffn, int out_dt, void* w13, void* w2p, float* w13_scale, float* w2_scale,
-                 void* w13_bwd, void* w2_bwd, hipStream_t s);
+                 void* w13_bwd, void* w2_bwd, float* w13_bwd_scale, float* w2_bwd_scale,
+                 hipStream_t s);
+int grouped_bwd_fp8(const void* dyp_q, const float* dyp_scale, const void* dyp, const void* xp,
+                    const void* h13_save, const moe_weights* W, const int32_t* offsets, int rows,
+                    void* dxp, float* dw1, float* dw3, float* dw2, void* ws, hipStream_t s);
+size_t grouped_bwd_fp8_ws_bytes(int rows, int h, int h_ffn, int E);
 int num_cus();
 
 // Launch status: clear_status() before a call's first launch drops any error

@@ -22,10 +22,11 @@ namespace moe {
 
 // Per-expert transpose with zero padding: src [rows][C] (expert-contiguous
 // rows) -> dst, expert e at element kpre[e]*C laid out [C][Kp_e] with
-// Kp_e = roundup(M_e, 64).  One 64 x 64 tile per workgroup through LDS.
+// Kp_e = roundup(M_e, pad) (pad a multiple of 64: one 128-byte K slab of the
+// GEMM's element type).  One 64 x 64 tile per workgroup through LDS.
 __global__ void __launch_bounds__(256) xpose_kernel(const uint16_t* __restrict__ src, int C,
                                                     const int32_t* __restrict__ offsets, int E,
-                                                    int rows, uint16_t* __restrict__ dst) {
+                                                    int rows, int pad, uint16_t* __restrict__ dst) {
   __shared__ int kpre[MOE_MAX_EXPERTS + 1];
   __shared__ int offs[MOE_MAX_EXPERTS + 1];
   __shared__ uint16_t tile[64][64 + 8];
@@ -42,7 +43,7 @@ __global__ void __launch_bounds__(256) xpose_kernel(const uint16_t* __restrict__
       prev = hi;
       offs[e] = lo;
       kpre[e] = kp;
-      kp += ((hi - lo + kKPad - 1) / kKPad) * kKPad;
+      kp += ((hi - lo + pad - 1) / pad) * pad;
     }
     offs[E] = prev;
     kpre[E] = kp;
@@ -89,6 +90,51 @@ __global__ void __launch_bounds__(256) xpose_kernel(const uint16_t* __restrict__
   }
 }
 
+// Rows r < n of length len (a multiple of 8): codes and scale[r].
+__global__ void __launch_bounds__(256) rowq_kernel(const uint16_t* __restrict__ src, int n, int len,
+                                                   uint8_t* __restrict__ dst,
+                                                   float* __restrict__ scale) {
+  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= n) return;
+  rowq_wave(src + size_t(r) * len, len, dst + size_t(r) * len, scale + r);
+}
+
+// The per-expert transposed blocks of xpose_kernel, quantized row by row:
+// row c of expert e (length Kp_e, at kpre[e]*C + c*Kp_e) -> codes at the same
+// place, scale[e][c] (1 for an expert without rows).  The zero padding
+// changes neither the scale nor the sums.
+__global__ void __launch_bounds__(256) rowq_xposed_kernel(const uint16_t* __restrict__ src, int C,
+                                                          const int32_t* __restrict__ offsets,
+                                                          int E, int rows, int pad,
+                                                          uint8_t* __restrict__ dst,
+                                                          float* __restrict__ scale) {
+  __shared__ int kpre[MOE_MAX_EXPERTS + 1];
+  if (threadIdx.x == 0) {
+    int kp = 0, prev = 0;
+    for (int e = 0; e < E; ++e) {
+      int o0 = offsets[e], o1 = offsets[e + 1];
+      o0 = o0 < 0 ? 0 : (o0 > rows ? rows : o0);
+      o1 = o1 < 0 ? 0 : (o1 > rows ? rows : o1);
+      const int lo = e == 0 ? o0 : prev, hi = o1 < lo ? lo : o1;
+      prev = hi;
+      kpre[e] = kp;
+      kp += ((hi - lo + pad - 1) / pad) * pad;
+    }
+    kpre[E] = kp;
+  }
+  __syncthreads();
+  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);  // r = e * C + c
+  if (r >= E * C) return;
+  const int e = r / C, c = r - e * C;
+  const int kp = kpre[e + 1] - kpre[e];
+  if (kp == 0) {
+    if ((threadIdx.x & 63) == 0) scale[r] = 1.0f;
+    return;
+  }
+  const size_t base = size_t(kpre[e]) * C + size_t(c) * kp;
+  rowq_wave(src + base, kp, dst + base, scale + r);
+}
+
 }  // namespace moe
 
 namespace moe_launch {
@@ -101,8 +147,10 @@ using CfgDA = GemmCfg<2, 4, 4, 2, 1, 128, 2>;
 
 static size_t al256(size_t x) { return (x + 255) & ~size_t(255); }
 
-// Upper bound of the padded K extent: sum_e roundup(M_e, 64) <= rows + 63 E.
-static size_t kpad_upper(int rows, int E) { return size_t(rows) + size_t(kKPad - 1) * E; }
+// Upper bound of the padded K extent: sum_e roundup(M_e, pad) <= rows + (pad-1) E.
+static size_t kpad_upper(int rows, int E, int pad = kpad_elems<MOE_BF16>()) {
+  return size_t(rows) + size_t(pad - 1) * E;
+}
 
 size_t grouped_bwd_ws_bytes(int rows, int h, int h_ffn, int E, int dtype) {
   (void)dtype;
@@ -116,10 +164,10 @@ size_t grouped_bwd_ws_bytes(int rows, int h, int h_ffn, int E, int dtype) {
 }
 
 static int xpose(const void* src, int C, const int32_t* offsets, int E, int rows, void* dst,
-                 hipStream_t s) {
-  const size_t ky = (kpad_upper(rows, E) + 63) / 64;
+                 hipStream_t s, int pad = kpad_elems<MOE_BF16>()) {
+  const size_t ky = (kpad_upper(rows, E, pad) + 63) / 64;
   hipLaunchKernelGGL(xpose_kernel, dim3(C / 64, unsigned(ky)), dim3(256), 0, s,
-                     (const uint16_t*)src, C, offsets, E, rows, (uint16_t*)dst);
+                     (const uint16_t*)src, C, offsets, E, rows, pad, (uint16_t*)dst);
   return launch_status();
 }
 
@@ -180,6 +228,101 @@ int grouped_bwd(const void* dyp, const void* xp, const void* h13_save, const moe
               dw1, dw3, nullptr, nullptr, nullptr, nullptr};
   splitk_ws_set<CfgB>(g4, split_ws);
   return launch_gemm<CfgB, MOE_BF16, kModeDW13, kSchedK>(g4, kTBwd4, s);
+}
+
+}  // namespace moe_launch
+
+namespace moe_launch {
+using namespace moe;
+
+using CfgQ = CfgFor<MOE_FP8_E4M3>::type;
+static_assert(CfgQ::kRowB == CfgDA::kRowB && CfgQ::kStages == CfgDA::kStages &&
+                  CfgQ::kBM == CfgDA::kBM && CfgQ::kBN == CfgDA::kBN,
+              "the FP8 dA epilogue stages G|U like the BF16 one");
+
+// FP8 backward workspace: bf16 dG|dU and A, dG|dU codes + row scales, one
+// bf16 transposed block reused for each operand, the four transposed code
+// blocks and their per-expert channel scales, split-K partials.
+size_t grouped_bwd_fp8_ws_bytes(int rows, int h, int h_ffn, int E) {
+  const size_t r = size_t(rows), hh = size_t(h), hf = size_t(h_ffn), e = size_t(E);
+  const size_t kp = kpad_upper(rows, E, kpad_elems<MOE_FP8_E4M3>());
+  const size_t cmax = hh > 2 * hf ? hh : 2 * hf;
+  return al256(r * 2 * hf * 2) + al256(r * hf * 2) + al256(r * 2 * hf) + al256(r * 4) +
+         al256(cmax * kp * 2) + 2 * al256(hh * kp) + al256(hf * kp) + al256(2 * hf * kp) +
+         2 * al256(e * hh * 4) + al256(e * hf * 4) + al256(e * 2 * hf * 4) + splitk_ws_bytes<CfgQ>();
+}
+
+static int xpose_q(const void* src, int C, const int32_t* offsets, int E, int rows, void* tmp,
+                   void* dst, float* scale, hipStream_t s) {
+  constexpr int pad = kpad_elems<MOE_FP8_E4M3>();
+  int rc = xpose(src, C, offsets, E, rows, tmp, s, pad);
+  if (rc) return rc;
+  hipLaunchKernelGGL(rowq_xposed_kernel, dim3(ceil_div(E * C, 4)), dim3(256), 0, s,
+                     (const uint16_t*)tmp, C, offsets, E, rows, pad, (uint8_t*)dst, scale);
+  return launch_status();
+}
+
+int grouped_bwd_fp8(const void* dyp_q, const float* dyp_scale, const void* dyp, const void* xp,
+                    const void* h13_save, const moe_weights* W, const int32_t* offsets, int rows,
+                    void* dxp, float* dw1, float* dw3, float* dw2, void* ws, hipStream_t s) {
+  const int h = W->h, hf = W->h_ffn, E = W->E;
+  const size_t r = size_t(rows), kp = kpad_upper(rows, E, kpad_elems<MOE_FP8_E4M3>());
+  const size_t cmax = size_t(h) > 2 * size_t(hf) ? size_t(h) : 2 * size_t(hf);
+  unsigned char* w = static_cast<unsigned char*>(ws);
+  auto take = [&](size_t bytes) { unsigned char* p = w; w += al256(bytes); return p; };
+  void* dgu = take(r * 2 * hf * 2);
+  void* act = take(r * hf * 2);
+  void* dgu_q = take(r * 2 * hf);
+  float* dgu_s = reinterpret_cast<float*>(take(r * 4));
+  void* tmp = take(cmax * kp * 2);
+  void* xpT = take(size_t(h) * kp);
+  void* dypT = take(size_t(h) * kp);
+  void* actT = take(size_t(hf) * kp);
+  void* dguT = take(2 * size_t(hf) * kp);
+  float* sx = reinterpret_cast<float*>(take(size_t(E) * h * 4));
+  float* sd = reinterpret_cast<float*>(take(size_t(E) * h * 4));
+  float* sa = reinterpret_cast<float*>(take(size_t(E) * hf * 4));
+  float* sg = reinterpret_cast<float*>(take(size_t(E) * 2 * hf * 4));
+  void* split_ws = w;
+  int rc;
+
+  timer_begin(kTXpose, s);
+  if ((rc = xpose_q(xp, h, offsets, E, rows, tmp, xpT, sx, s))) return rc;
+  if ((rc = xpose_q(dyp, h, offsets, E, rows, tmp, dypT, sd, s))) return rc;
+  timer_end(kTXpose, s);
+
+  // dA = dYp W2^T on FP8 codes; epilogue rescales and forms dG, dU and A
+  GemmArgs ga{dyp_q, dyp_scale, W->w2_bwd, W->w2_bwd_scale, offsets, E, h, hf, rows, 0,
+              dgu, act, const_cast<void*>(h13_save), nullptr, nullptr, nullptr};
+  splitk_ws_set<CfgQ>(ga, split_ws);
+  if ((rc = launch_gemm<CfgQ, MOE_FP8_E4M3, kModeBwdDA, kSchedM>(ga, kTBwd1, s))) return rc;
+
+  timer_begin(kTQuant, s);
+  hipLaunchKernelGGL(rowq_kernel, dim3(ceil_div(rows, 4)), dim3(256), 0, s, (const uint16_t*)dgu, rows,
+                     2 * hf, (uint8_t*)dgu_q, dgu_s);
+  timer_end(kTQuant, s);
+  timer_begin(kTXpose, s);
+  if ((rc = xpose_q(act, hf, offsets, E, rows, tmp, actT, sa, s))) return rc;
+  if ((rc = xpose_q(dgu, 2 * hf, offsets, E, rows, tmp, dguT, sg, s))) return rc;
+  timer_end(kTXpose, s);
+
+  // dW2 = A^T dYp  (per expert [hf][h], fp32)
+  GemmArgs g2{actT, sa, dypT, sd, offsets, E, 0, h, rows, hf, dw2, nullptr, nullptr, nullptr,
+              nullptr, nullptr};
+  splitk_ws_set<CfgQ>(g2, split_ws);
+  if ((rc = launch_gemm<CfgQ, MOE_FP8_E4M3, kModeDW, kSchedK>(g2, kTBwd2, s))) return rc;
+
+  // dXp = [dG|dU] W13^T
+  GemmArgs g3{dgu_q, dgu_s, W->w13_bwd, W->w13_bwd_scale, offsets, E, 2 * hf, h, rows, 0, dxp,
+              nullptr, nullptr, nullptr, nullptr, nullptr};
+  splitk_ws_set<CfgQ>(g3, split_ws);
+  if ((rc = launch_gemm<CfgQ, MOE_FP8_E4M3, kModeFC2, kSchedM>(g3, kTBwd3, s))) return rc;
+
+  // dW1 | dW3 = Xp^T [dG|dU]
+  GemmArgs g4{xpT, sx, dguT, sg, offsets, E, 0, 2 * hf, rows, h, dw1, dw3, nullptr, nullptr,
+              nullptr, nullptr};
+  splitk_ws_set<CfgQ>(g4, split_ws);
+  return launch_gemm<CfgQ, MOE_FP8_E4M3, kModeDW13, kSchedK>(g4, kTBwd4, s);
 }
 
 }  // namespace moe_launch

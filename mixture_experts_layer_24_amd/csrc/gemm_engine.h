@@ -15,7 +15,9 @@
 
 namespace moe {
 
-constexpr int kKPad = 64;      // SchedK: per-expert K padded to this
+// SchedK: per-expert K (rows) padded to one 128-byte slab of the element type
+template <int DT>
+constexpr int kpad_elems() { return DT == MOE_FP8_E4M3 ? 128 : DT == MOE_F32 ? 32 : 64; }
 constexpr int kMaxGrid = 256;  // persistent grid cap (workgroups)
 constexpr int kMaxSplit = 8;   // K splits of one tile in the last round
 
@@ -67,7 +69,7 @@ enum {
 
 struct GemmArgs {
   const void* A;          // SchedM: [rows][K]; SchedK: expert e at kpre[e]*M elements, [M][K_e]
-  const float* a_scale;   // FP8: [rows]
+  const float* a_scale;   // FP8: SchedM [rows]; SchedK [E][M]
   const void* B;          // SchedM: [E][N][K]; SchedK: expert e at kpre[e]*N elements, [N][K_e]
   const float* b_scale;   // FP8: [E][N]
   const int32_t* offsets; // [E+1]
@@ -404,7 +406,8 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, f32x16 (&acc)[C::kMI
             const float G = bf16_to_f32(wl16[rl * 64 + l32]), U = bf16_to_f32(wl16[rl * 64 + 32 + l32]);
             const float sg = 1.0f / (1.0f + __expf(-G));
             const float si = G * sg;
-            const float dA = acc[i][j][r];
+            float dA = acc[i][j][r];
+            if (DT == MOE_FP8_E4M3) dA *= g.a_scale[row] * g.b_scale[size_t(e) * g.N + f];
             const size_t b = size_t(row) * (2 * hf);
             dgu[b + pg] = uint16_t(f32_to_bf16_bits(dA * U * sg * (1.0f + G * (1.0f - sg))));
             dgu[b + pu] = uint16_t(f32_to_bf16_bits(dA * si));
@@ -436,7 +439,12 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, f32x16 (&acc)[C::kMI
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int m = rbase + acc_row(i, r, half);
-          if (m < row_end) dst[size_t(m) * ld + col] = acc[i][j][r];
+          if (m < row_end) {
+            float v = acc[i][j][r];
+            // FP8: per-expert channel scales of both transposed operands
+            if (DT == MOE_FP8_E4M3) v *= g.a_scale[size_t(e) * g.M + m] * g.b_scale[size_t(e) * g.N + n];
+            dst[size_t(m) * ld + col] = v;
+          }
         }
     }
   }
@@ -524,7 +532,7 @@ __global__ void __launch_bounds__(C::kThreads, C::kWavesPerSimd) grouped_gemm_ke
         run += ceil_div(hi - lo, BM) * NT;
       } else {
         offs[e] = kp;  // becomes the padded K prefix
-        kp += ceil_div(hi - lo, kKPad) * kKPad;
+        kp += ceil_div(hi - lo, kpad_elems<DT>()) * kpad_elems<DT>();
         run += MT * NT;
       }
       tpre[e + 1] = run;

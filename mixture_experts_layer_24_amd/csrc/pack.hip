@@ -84,6 +84,54 @@ __global__ void interleave13_kernel(const uint16_t* __restrict__ w1, const uint1
       *reinterpret_cast<const u32x4*>(src + row * hf + ch);
 }
 
+// FP8 backward copies: one scale per row over the contracted dimension.
+// w2_bwd rows are W2's rows (h_ffn channels over h); w13_bwd row i of expert e
+// interleaves W1[e][i][:] and W3[e][i][:] like interleave13_kernel, one scale
+// over both.  One wave per row.
+__global__ void __launch_bounds__(256) rowq_w2_kernel(const uint16_t* __restrict__ w2, int n, int h,
+                                                      uint8_t* __restrict__ dst,
+                                                      float* __restrict__ scale) {
+  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= n) return;
+  rowq_wave(w2 + size_t(r) * h, h, dst + size_t(r) * h, scale + r);
+}
+
+__global__ void __launch_bounds__(256) rowq_w13_kernel(const uint16_t* __restrict__ w1,
+                                                       const uint16_t* __restrict__ w3, int n,
+                                                       int hf, uint8_t* __restrict__ dst,
+                                                       float* __restrict__ scale) {
+  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);  // r = e * h + i
+  if (r >= n) return;
+  const int lane = threadIdx.x & 63;
+  const uint16_t* a = w1 + size_t(r) * hf;
+  const uint16_t* b = w3 + size_t(r) * hf;
+  float amax = 0.f;
+  for (int c = lane * 8; c < hf; c += 512) {
+    const u32x4 va = *reinterpret_cast<const u32x4*>(a + c), vb = *reinterpret_cast<const u32x4*>(b + c);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      amax = fmaxf(amax, fmaxf(fmaxf(fabsf(bf16_lo(va[i])), fabsf(bf16_hi(va[i]))),
+                               fmaxf(fabsf(bf16_lo(vb[i])), fabsf(bf16_hi(vb[i])))));
+  }
+  amax = wave_max(amax);
+  const float s = amax > 0.f ? amax / 448.0f : 1.0f;
+  if (lane == 0) scale[r] = s;
+  uint8_t* d = dst + size_t(r) * 2 * hf;
+  for (int p = lane * 8; p < 2 * hf; p += 512) {
+    const int ch = (p >> 6) * 32 + (p & 31);
+    const u32x4 v = *reinterpret_cast<const u32x4*>((((p >> 5) & 1) ? b : a) + ch);
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      lo |= f32_to_e4m3(bf16_lo(v[i]) / s) << (16 * i);
+      lo |= f32_to_e4m3(bf16_hi(v[i]) / s) << (16 * i + 8);
+      hi |= f32_to_e4m3(bf16_lo(v[2 + i]) / s) << (16 * i);
+      hi |= f32_to_e4m3(bf16_hi(v[2 + i]) / s) << (16 * i + 8);
+    }
+    *reinterpret_cast<uint2*>(d + p) = make_uint2(lo, hi);
+  }
+}
+
 __global__ void copy16_kernel(const u32x4* __restrict__ src, u32x4* __restrict__ dst, size_t n) {
   const size_t q = size_t(blockIdx.x) * blockDim.x + threadIdx.x;
   if (q < n) dst[q] = src[q];
@@ -114,7 +162,8 @@ static void pack_all(const void* w1, const void* w3, const void* w2, int E, int 
 
 int pack_weights(const void* w1, const void* w3, const void* w2, int in_dt, int E, int h,
                  int h_ffn, int out_dt, void* w13, void* w2p, float* w13_scale, float* w2_scale,
-                 void* w13_bwd, void* w2_bwd, hipStream_t s) {
+                 void* w13_bwd, void* w2_bwd, float* w13_bwd_scale, float* w2_bwd_scale,
+                 hipStream_t s) {
   timer_begin(kTPack, s);
   if (in_dt == MOE_F32 && out_dt == MOE_F32)
     pack_all<true, MOE_F32>(w1, w3, w2, E, h, h_ffn, w13, w2p, nullptr, nullptr, s);
@@ -124,12 +173,19 @@ int pack_weights(const void* w1, const void* w3, const void* w2, int in_dt, int 
     pack_all<false, MOE_FP8_E4M3>(w1, w3, w2, E, h, h_ffn, w13, w2p, w13_scale, w2_scale, s);
   else
     return MOE_ERR_DTYPE;
-  if (w13_bwd) {
+  if (out_dt == MOE_FP8_E4M3) {
+    if (w13_bwd)
+      hipLaunchKernelGGL(rowq_w13_kernel, dim3(ceil_div(E * h, 4)), dim3(256), 0, s, (const uint16_t*)w1,
+                         (const uint16_t*)w3, E * h, h_ffn, (uint8_t*)w13_bwd, w13_bwd_scale);
+    if (w2_bwd)
+      hipLaunchKernelGGL(rowq_w2_kernel, dim3(ceil_div(E * h_ffn, 4)), dim3(256), 0, s, (const uint16_t*)w2,
+                         E * h_ffn, h, (uint8_t*)w2_bwd, w2_bwd_scale);
+  } else if (w13_bwd) {
     const size_t chunks = size_t(E) * h * (2 * size_t(h_ffn) / 8);
     hipLaunchKernelGGL(interleave13_kernel, dim3(unsigned((chunks + 255) / 256)), dim3(256), 0, s,
                        (const uint16_t*)w1, (const uint16_t*)w3, E, h, h_ffn, (uint16_t*)w13_bwd);
   }
-  if (w2_bwd) {
+  if (w2_bwd && out_dt != MOE_FP8_E4M3) {
     const size_t n = size_t(E) * h_ffn * h * 2 / 16;
     hipLaunchKernelGGL(copy16_kernel, dim3(unsigned((n + 255) / 256)), dim3(256), 0, s,
                        (const u32x4*)w2, (u32x4*)w2_bwd, n);

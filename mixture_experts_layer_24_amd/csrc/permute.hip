@@ -70,8 +70,11 @@ __global__ void __launch_bounds__(256) permute_copy_kernel(const void* __restric
 }
 
 // BF16 rows -> per-token E4M3 codes + scale (amax / 448) on every routed copy.
+// With row_scale, routed row (t, j) keeps the codes of src[t] and its scale
+// becomes row_scale[t][j] * scale_t.
 __global__ void __launch_bounds__(256) permute_fp8_kernel(const uint16_t* __restrict__ src,
                                                           const int32_t* __restrict__ dst_row,
+                                                          const float* __restrict__ row_scale,
                                                           int T, int h, int k,
                                                           uint8_t* __restrict__ dst,
                                                           float* __restrict__ dst_scale) {
@@ -98,7 +101,8 @@ __global__ void __launch_bounds__(256) permute_fp8_kernel(const uint16_t* __rest
   }
   amax = wave_max(amax);
   const float scale = amax > 0.f ? amax / 448.0f : 1.0f;
-  if (lane < k && rows[lane] >= 0 && rows[lane] < T * k) dst_scale[rows[lane]] = scale;
+  if (lane < k && rows[lane] >= 0 && rows[lane] < T * k)
+    dst_scale[rows[lane]] = row_scale ? row_scale[size_t(t) * k + lane] * scale : scale;
   const bool held = nch <= 64 * kBatch;  // v still holds the row
   for (int c0 = lane; c0 < nch; c0 += 64 * kBatch) {
     if (!held) {
@@ -214,8 +218,8 @@ int permute_rows(const void* src, int src_dt, const int32_t* dst_row, const floa
   dim3 grid(ceil_div(T, kRowsPerBlock)), block(256);
   timer_begin(kTPermute, s);
   if (dst_dt == MOE_FP8_E4M3) {
-    hipLaunchKernelGGL(permute_fp8_kernel, grid, block, 0, s, (const uint16_t*)src, dst_row, T, h,
-                       k, (uint8_t*)dst, dst_scale);
+    hipLaunchKernelGGL(permute_fp8_kernel, grid, block, 0, s, (const uint16_t*)src, dst_row, row_scale,
+                       T, h, k, (uint8_t*)dst, dst_scale);
   } else if (src_dt == MOE_F32) {
     hipLaunchKernelGGL(permute_copy_kernel<true>, grid, block, 0, s, src, dst_row, row_scale, T, h,
                        k, dst);

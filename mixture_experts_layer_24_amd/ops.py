@@ -39,10 +39,12 @@ def moe_packed_weight_bytes(which, E, h, h_ffn, dtype):
 
 
 def moe_pack_weights(w1, w3, w2, in_dtype, E, h, h_ffn, out_dtype, w13, w2_packed, w13_scale,
-                     w2_scale, w13_bwd=None, w2_bwd=None, stream=None):
+                     w2_scale, w13_bwd=None, w2_bwd=None, w13_bwd_scale=None, w2_bwd_scale=None,
+                     stream=None):
     return check(lib().moe_pack_weights(_p(w1), _p(w3), _p(w2), in_dtype, E, h, h_ffn, out_dtype,
                                         _p(w13), _p(w2_packed), _p(w13_scale), _p(w2_scale),
-                                        _p(w13_bwd), _p(w2_bwd), _s(stream)))
+                                        _p(w13_bwd), _p(w2_bwd), _p(w13_bwd_scale), _p(w2_bwd_scale),
+                                        _s(stream)))
 
 
 def moe_route(x, w_gate, bias, logits, T, h, E, k, dtype, topk_idx, topk_w, stream=None):
@@ -130,6 +132,18 @@ def moe_router_aux_loss(logits, counts, T, E, k, alpha, loss, ws, ws_bytes, stre
                                            _p(ws), ws_bytes, _s(stream)))
 
 
+def moe_grouped_bwd_fp8_workspace_size(rows, h, h_ffn, E):
+    return lib().moe_grouped_bwd_fp8_workspace_size(rows, h, h_ffn, E)
+
+
+def moe_grouped_swiglu_bwd_fp8(dyp_q, dyp_scale, dyp, xp, h13_save, W, offsets, rows, dxp, dw1, dw3,
+                               dw2, ws, ws_bytes, stream=None):
+    return check(lib().moe_grouped_swiglu_bwd_fp8(_p(dyp_q), _p(dyp_scale), _p(dyp), _p(xp),
+                                                  _p(h13_save), ctypes.byref(W), _p(offsets), rows,
+                                                  _p(dxp), _p(dw1), _p(dw3), _p(dw2), _p(ws), ws_bytes,
+                                                  _s(stream)))
+
+
 def moe_last_error() -> str:
     return lib().moe_last_error().decode()
 
@@ -156,12 +170,16 @@ class PackedWeights:
         self.w2_scale = torch.empty(E, h, dtype=torch.float32, device=dev) if fp8 else None
         self.w13_bwd = torch.empty(sz(4), dtype=torch.uint8, device=dev) if backward else None
         self.w2_bwd = torch.empty(sz(5), dtype=torch.uint8, device=dev) if backward else None
+        bq = backward and fp8
+        self.w13_bwd_scale = torch.empty(E, h, dtype=torch.float32, device=dev) if bq else None
+        self.w2_bwd_scale = torch.empty(E, hf, dtype=torch.float32, device=dev) if bq else None
         moe_pack_weights(w1, w3, w2, in_dt, E, h, hf, out_dtype, self.w13, self.w2,
-                         self.w13_scale, self.w2_scale, self.w13_bwd, self.w2_bwd, stream)
+                         self.w13_scale, self.w2_scale, self.w13_bwd, self.w2_bwd,
+                         self.w13_bwd_scale, self.w2_bwd_scale, stream)
         ptr = lambda t: None if t is None else t.data_ptr()
         self.struct = MoeWeights(out_dtype, E, h, hf, self.w13.data_ptr(), self.w2.data_ptr(),
                                  ptr(self.w13_scale), ptr(self.w2_scale), ptr(self.w13_bwd),
-                                 ptr(self.w2_bwd))
+                                 ptr(self.w2_bwd), ptr(self.w13_bwd_scale), ptr(self.w2_bwd_scale))
 
 
 class MoELayer:
@@ -237,7 +255,13 @@ class MoELayer:
         self.dw1 = torch.empty(E, h, hf, dtype=torch.float32, device=dev)
         self.dw3 = torch.empty(E, h, hf, dtype=torch.float32, device=dev)
         self.dw2 = torch.empty(E, hf, h, dtype=torch.float32, device=dev)
-        self.bws_bytes = moe_grouped_bwd_workspace_size(R, h, hf, E, self.dtype)
+        if self.dtype == MOE_FP8_E4M3:
+            self.dyp_q = torch.empty(R, h, dtype=torch.uint8, device=dev)
+            self.dyp_s = torch.empty(R, dtype=torch.float32, device=dev)
+            self.xp_b = torch.empty(R, h, dtype=torch.bfloat16, device=dev)
+            self.bws_bytes = moe_grouped_bwd_fp8_workspace_size(R, h, hf, E)
+        else:
+            self.bws_bytes = moe_grouped_bwd_workspace_size(R, h, hf, E, self.dtype)
         self.bws = torch.empty(max(self.bws_bytes, 256), dtype=torch.uint8, device=dev)
         self.bwd_ready = True
 
@@ -271,11 +295,21 @@ class MoELayer:
         # dYp = w * dY in dispatch order; Xp re-gathered from x (index reused)
         moe_permute(dy, MOE_BF16, None, self.topk_w, T, h, E, k, None, None, self.dst_row, None,
                     self.dyp, MOE_BF16, None, None, 0, stream)
-        moe_permute(x, MOE_BF16, None, None, T, h, E, k, None, None, self.dst_row, None,
-                    self.xp, MOE_BF16, None, None, 0, stream)
-        moe_grouped_swiglu_bwd(self.dyp, self.xp, self.h13, W.struct, self.offsets, self.R,
-                               self.dxp, self.dw1, self.dw3, self.dw2, self.bws, self.bws_bytes,
-                               stream)
+        if self.dtype == MOE_FP8_E4M3:
+            # dY codes per token, routed row scale w * s (FP8 backward)
+            moe_permute(dy, MOE_BF16, None, self.topk_w, T, h, E, k, None, None, self.dst_row, None,
+                        self.dyp_q, MOE_FP8_E4M3, self.dyp_s, None, 0, stream)
+            moe_permute(x, MOE_BF16, None, None, T, h, E, k, None, None, self.dst_row, None,
+                        self.xp_b, MOE_BF16, None, None, 0, stream)
+            moe_grouped_swiglu_bwd_fp8(self.dyp_q, self.dyp_s, self.dyp, self.xp_b, self.h13, W.struct,
+                                       self.offsets, self.R, self.dxp, self.dw1, self.dw3, self.dw2,
+                                       self.bws, self.bws_bytes, stream)
+        else:
+            moe_permute(x, MOE_BF16, None, None, T, h, E, k, None, None, self.dst_row, None,
+                        self.xp, MOE_BF16, None, None, 0, stream)
+            moe_grouped_swiglu_bwd(self.dyp, self.xp, self.h13, W.struct, self.offsets, self.R,
+                                   self.dxp, self.dw1, self.dw3, self.dw2, self.bws, self.bws_bytes,
+                                   stream)
         if w_gate is None:
             moe_combine(self.dxp, MOE_BF16, self.dst_row, None, T, h, k, self.dx, MOE_BF16, stream)
             return self.dx

@@ -76,6 +76,8 @@ WORKLOADS = {
     # the two remaining shapes of the model table, at the Mixtral batch
     "mixtral22b": Workload("mixtral22b", 8192, 6144, 16384, 8, 2, "bf16"),
     "phi35": Workload("phi35", 8192, 4096, 6400, 16, 2, "bf16"),
+    # the DeepSeekMoE-shaped training step with per-token FP8 in both passes
+    "dsmoe_fp8": Workload("dsmoe_fp8", 16384, 2048, 1408, 64, 6, "fp8", backward=True),
 }
 
 

@@ -26,7 +26,7 @@ def test_exports_every_declared_symbol():
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) <= set(L.SIGNATURES)
-    assert lib.moe_version() == 2
+    assert lib.moe_version() == 3
 
 
 A = ctypes.c_void_p(1 << 20)   # aligned, never dereferenced: validation fails first
@@ -67,7 +67,6 @@ def test_permute_validation():
     assert call(h=12) == L.MOE_ERR_SHAPE
     assert call(sdt=L.MOE_F32) == L.MOE_ERR_DTYPE
     assert call(ddt=L.MOE_FP8_E4M3) == L.MOE_ERR_ARG            # fp8 needs scales
-    assert call(ddt=L.MOE_FP8_E4M3, scale=A, row_scale=A) == L.MOE_ERR_ARG
     assert call(wsb=need - 1) == L.MOE_ERR_WORKSPACE
     assert call(ws=None) == L.MOE_ERR_WORKSPACE
     assert call(dst=None) == L.MOE_ERR_ARG
@@ -98,7 +97,7 @@ def test_grouped_validation():
     # bf16 weights without the backward layouts
     assert lib.moe_grouped_swiglu_bwd(A, A, A, ctypes.byref(W), A, 512, A, A, A, A, A, 1 << 30,
                                       None) == L.MOE_ERR_ARG
-    Wb = L.MoeWeights(L.MOE_BF16, 8, 256, 384, A.value, A.value, None, None, A.value, A.value)
+    Wb = L.MoeWeights(L.MOE_BF16, 8, 256, 384, A.value, A.value, None, None, A.value, A.value, None, None)
     need = lib.moe_grouped_bwd_workspace_size(512, 256, 384, 8, L.MOE_BF16)
     assert need > 0
     assert lib.moe_grouped_swiglu_bwd(A, A, A, ctypes.byref(Wb), A, 512, A, A, A, A, A, need - 1,
@@ -111,13 +110,17 @@ def test_combine_and_pack_validation():
     assert lib.moe_combine(A, L.MOE_FP8_E4M3, A, A, 10, 16, 2, A, L.MOE_BF16, None) == L.MOE_ERR_DTYPE
     assert lib.moe_combine(A, L.MOE_BF16, A, None, 0, 16, 2, A, L.MOE_BF16, None) == L.MOE_OK
     assert lib.moe_pack_weights(A, A, A, L.MOE_F32, 8, 256, 384, L.MOE_BF16, A, A, None, None,
-                                None, None, None) == L.MOE_ERR_DTYPE
+                                None, None, None, None, None) == L.MOE_ERR_DTYPE
     assert lib.moe_pack_weights(A, A, A, L.MOE_BF16, 8, 256, 384, L.MOE_FP8_E4M3, A, A, None, None,
-                                None, None, None) == L.MOE_ERR_ARG
+                                None, None, None, None, None) == L.MOE_ERR_ARG
     assert lib.moe_pack_weights(A, A, A, L.MOE_BF16, 8, 256, 384, L.MOE_FP8_E4M3, A, A, A, A,
-                                A, A, None) == L.MOE_ERR_DTYPE   # backward layouts are bf16 only
+                                A, A, None, A, None) == L.MOE_ERR_ARG   # FP8 w13_bwd needs its scales
+    assert lib.moe_pack_weights(A, A, A, L.MOE_F32, 8, 256, 384, L.MOE_F32, A, A, None, None,
+                                A, A, None, None, None) == L.MOE_ERR_DTYPE   # no fp32 backward layouts
     assert lib.moe_packed_weight_bytes(4, 8, 256, 384, L.MOE_BF16) == 8 * 256 * 768 * 2
-    assert lib.moe_packed_weight_bytes(5, 8, 256, 384, L.MOE_FP8_E4M3) == 0
+    assert lib.moe_packed_weight_bytes(5, 8, 256, 384, L.MOE_FP8_E4M3) == 8 * 384 * 256
+    assert lib.moe_packed_weight_bytes(6, 8, 256, 384, L.MOE_FP8_E4M3) == 8 * 256 * 4
+    assert lib.moe_packed_weight_bytes(7, 8, 256, 384, L.MOE_BF16) == 0
     assert lib.moe_packed_weight_bytes(0, 8, 256, 384, L.MOE_BF16) == 8 * 768 * 256 * 2
     assert lib.moe_packed_weight_bytes(3, 8, 256, 384, L.MOE_FP8_E4M3) == 8 * 256 * 4
 
@@ -195,3 +198,19 @@ def test_capacity_drop_validation():
     assert call(out=None) == L.MOE_ERR_ARG
     assert call(wsb=need - 1) == L.MOE_ERR_WORKSPACE
     assert call(T=0) == L.MOE_OK
+
+
+def test_grouped_bwd_fp8_validation():
+    lib = L.lib()
+    need = lib.moe_grouped_bwd_fp8_workspace_size(1000, 256, 384, 8)
+    assert need > 0
+    Wq = L.MoeWeights(L.MOE_FP8_E4M3, 8, 256, 384, A.value, A.value, A.value, A.value, A.value, A.value,
+                      A.value, A.value)
+    call = lambda W, ws=A, wsb=need: lib.moe_grouped_swiglu_bwd_fp8(A, A, A, A, A, ctypes.byref(W), A, 1000, A,
+                                                                    A, A, A, ws, wsb, None)
+    assert call(Wq, wsb=need - 1) == L.MOE_ERR_WORKSPACE
+    Wb = L.MoeWeights(L.MOE_BF16, 8, 256, 384, A.value, A.value, None, None, A.value, A.value, None, None)
+    assert call(Wb) == L.MOE_ERR_DTYPE
+    Wn = L.MoeWeights(L.MOE_FP8_E4M3, 8, 256, 384, A.value, A.value, A.value, A.value, A.value, A.value,
+                      None, A.value)
+    assert call(Wn) == L.MOE_ERR_ARG

@@ -1,0 +1,135 @@
+"""GPU parity of the FP8 backward against the quantization-emulating oracle.
+
+Forward in FP8 (kept G|U in bf16), backward on E4M3 codes (see the oracle's
+`layer_backward_fp8` for the recipe); routing fed the oracle's fp32 logits.
+
+A quantizer turns the last-bit differences of fp32 vs fp64 arithmetic before
+it into whole code steps (up to 1/8 of a value, or a new scale for a whole
+row when the row's amax moves), so two correct implementations differ by more
+than the FP8 bar on a few elements.  The oracle's `fp8_backward_envelope`
+bounds, per element, the distance of any implementation with fp32 sums and
+an fp32 SwiGLU derivative from `layer_backward_fp8`; each of dX, dW1, dW3,
+dW2 must be within 6e-2 * rms of the emulating oracle once that allowance is
+granted (dX also half a bf16 ulp of its own output rounding), and its rms
+error below 1e-2 * rms.
+
+Unit test (`test_fp8_backward_unit`): the GPU backward gets the oracle's
+G|U (rounded to bf16, in the packed column order) in place of the kept
+forward output and the oracle's fp32 gate weights in place of its own; the
+envelope is tight (mean allowance ~1e-3 * rms for dW).
+Layer test (`test_fp8_backward_layer`): the GPU's own forward and router
+feed the backward; the envelope includes the forward's fp32 error on G, U
+and the fp32 softmax's on the gate weights.
+
+The FP8 backward weight copies are compared code for code with the oracle's
+per-row quantization.
+"""
+import numpy as np
+import pytest
+import torch
+
+import moe_synth
+from moe_synth import to_f32
+from oracle import moe_ref as ref
+
+from test_gpu_parity import DEV, HALF_ULP_BF16, check_close, dev_tensor, host, say
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    from mixture_experts_layer_24_amd import ops
+    from mixture_experts_layer_24_amd._lib import MOE_FP8_E4M3
+
+CASES = [
+    ("small", dict(T=300, h=256, h_ffn=384, E=8, k=2), 1),
+    ("tail_n", dict(T=513, h=384, h_ffn=256, E=4, k=2), 2),
+    ("e64_k6", dict(T=600, h=256, h_ffn=256, E=64, k=6), 3),
+    ("multi_tile", dict(T=2100, h=512, h_ffn=384, E=4, k=2), 4),
+    ("one_expert", dict(T=77, h=256, h_ffn=128, E=1, k=1), 6),
+]
+
+
+def test_fp8_backward_weight_copies():
+    wl = moe_synth.WORKLOADS["dsmoe"].scaled(name="packq", T=16, h=256, h_ffn=384, E=3, k=2)
+    inp = moe_synth.gen_all(wl, seed=3)
+    P = ops.PackedWeights(dev_tensor(inp["w1"]), dev_tensor(inp["w3"]), dev_tensor(inp["w2"]), MOE_FP8_E4M3,
+                          backward=True)
+    torch.cuda.synchronize()
+    E, h, hf = wl.E, wl.h, wl.h_ffn
+    w2b = P.w2_bwd.cpu().numpy().reshape(E, hf, h)
+    w13b = P.w13_bwd.cpu().numpy().reshape(E, h, 2 * hf)
+    for e in range(E):
+        q, s = ref.quantize_weight_rows(to_f32(inp["w2"][e]))                 # rows = h_ffn channels
+        np.testing.assert_array_equal(w2b[e], q)
+        np.testing.assert_array_equal(P.w2_bwd_scale[e].cpu().numpy(), s)
+        cat = np.concatenate([to_f32(inp["w1"][e]), to_f32(inp["w3"][e])], axis=1)   # [h, 2hf]
+        q, s = ref.quantize_weight_rows(cat)
+        np.testing.assert_array_equal(P.w13_bwd_scale[e].cpu().numpy(), s)
+        p = np.arange(2 * hf)
+        src = np.where((p // 32) % 2 == 1, hf, 0) + (p // 64) * 32 + p % 32   # interleaved column p
+        np.testing.assert_array_equal(w13b[e], q[:, src])
+
+
+def _packed_gu(g, u):
+    """[rows][2hf] G|U with 32-column groups of G and U interleaved (the
+    packed order of the kept forward output)."""
+    hf = g.shape[1]
+    p = np.arange(2 * hf)
+    src = np.where((p // 32) % 2 == 1, hf, 0) + (p // 64) * 32 + p % 32
+    return np.concatenate([g, u], axis=1)[:, src]
+
+
+def _check(got, emu, exact, allow):
+    for name in ("dx", "dw1", "dw3", "dw2"):
+        extra = HALF_ULP_BF16 * np.abs(emu[name]) if name == "dx" else 0.0
+        rms = np.sqrt(np.mean(emu[name] ** 2))
+        say(f"  {name}: allowance / rms mean {np.mean(allow[name]) / rms:.2e} max {np.max(allow[name]) / rms:.2e}")
+        check_close(got[name], emu[name], 6e-2, allow[name] + extra, None, name + " vs FP8-emulating oracle")
+        e_rms = np.sqrt(np.mean((got[name] - emu[name]) ** 2)) / rms
+        x_rms = np.sqrt(np.mean((got[name] - exact[name]) ** 2)) / np.sqrt(np.mean(exact[name] ** 2))
+        say(f"  {name}: rms err / rms vs emulating oracle {e_rms:.3e}, vs exact {x_rms:.3e}")
+        assert e_rms <= 1e-2, name
+
+
+def _run(case, over, seed, shared_gu):
+    wl = moe_synth.WORKLOADS["dsmoe"].scaled(name=case, dtype="fp8", **over)
+    say(f"fp8 backward {case}: {wl} shared G|U={shared_gu}")
+    inp = moe_synth.gen_all(wl, seed=seed)
+    f = lambda key: to_f32(inp[key])
+    fw = ref.layer_forward_fp8(f("x"), f("w_gate"), inp["bias"], f("w1"), f("w3"), f("w2"), wl.k)
+    args = (f("dy"), f("x"), fw["w"], fw["dst_row"], fw["offsets"], f("w1"), f("w3"), f("w2"), fw["g"], fw["u"])
+    emu = ref.layer_backward_fp8(*args)
+    if shared_gu:
+        g_err = u_err = w_err = None
+    else:
+        g_err, u_err = ref.fp8_forward_gu_bound(f("x"), fw["dst_row"], fw["offsets"], f("w1"), f("w3"))
+        w_err = ref.topk_weight_bound(fw["logits"], fw["idx"])
+    allow = ref.fp8_backward_envelope(*args, g_err=g_err, u_err=u_err, w_err=w_err)
+    exact = ref.layer_backward(f("dy"), f("x"), fw["w"], fw["dst_row"], fw["offsets"], f("w1"), f("w3"), f("w2"),
+                               g=fw["g"], u=fw["u"])
+    P = ops.PackedWeights(dev_tensor(inp["w1"]), dev_tensor(inp["w3"]), dev_tensor(inp["w2"]), MOE_FP8_E4M3,
+                          backward=True)
+    layer = ops.MoELayer(wl.T, wl.h, wl.h_ffn, wl.E, wl.k, MOE_FP8_E4M3, save_for_backward=True)
+    xd = dev_tensor(inp["x"])
+    layer.forward(xd, dev_tensor(inp["w_gate"]), torch.from_numpy(inp["bias"]).to(DEV), P,
+                  logits_in=torch.from_numpy(fw["logits"]).to(DEV))
+    if shared_gu:
+        gu = _packed_gu(np.asarray(fw["g"], np.float64), np.asarray(fw["u"], np.float64))
+        layer.h13.copy_(torch.from_numpy(gu.astype(np.float32)).to(DEV).to(torch.bfloat16))
+        layer.topk_w.copy_(torch.from_numpy(np.asarray(fw["w"], np.float32)).to(DEV))
+    layer.backward(dev_tensor(inp["dy"]), xd, P)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(layer.dst_row.cpu().numpy(), fw["dst_row"])
+    got = {"dx": host(layer.dx), "dw1": layer.dw1.cpu().numpy(), "dw3": layer.dw3.cpu().numpy(),
+           "dw2": layer.dw2.cpu().numpy()}
+    return got, emu, exact, allow
+
+
+@pytest.mark.parametrize("case,over,seed", CASES, ids=[c[0] for c in CASES])
+def test_fp8_backward_unit(case, over, seed):
+    _check(*_run(case, over, seed, True))
+
+
+@pytest.mark.parametrize("case,over,seed", CASES[:3], ids=[c[0] for c in CASES[:3]])
+def test_fp8_backward_layer(case, over, seed):
+    _check(*_run(case, over, seed, False))
