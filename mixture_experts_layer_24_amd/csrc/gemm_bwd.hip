@@ -21,25 +21,40 @@
 namespace moe {
 
 // Per-expert transpose with zero padding: src [rows][C] (expert-contiguous
-// rows) -> dst, expert e at element kpre[e]*C laid out [C][Kp_e] with
-// Kp_e = roundup(M_e, pad) (pad a multiple of 64: one 128-byte K slab of the
-// GEMM's element type).  One 64 x 64 tile per workgroup through LDS.
+// rows, C a multiple of 64) -> dst, expert e at element kpre[e]*C laid out
+// [C][Kp_e] with Kp_e = roundup(M_e, pad) (pad a multiple of 64: one 128-byte
+// K slab of the GEMM's element type) and zeros beyond M_e.
+//
+// One workgroup per (64 columns, expert) walks the expert's rows in blocks of
+// 64: each thread loads 16 bytes of two adjacent rows (eight threads cover a
+// 128-byte row segment), packs the two rows' values of each column into one
+// 32-bit word in LDS (column-major, 33 words per column: conflict-free
+// stores), then reads 8 words = 16 consecutive rows of one column and stores
+// them contiguously.  The next block's loads are issued before this block's
+// LDS work.
+//
+// kQ: E4M3 codes instead of bf16, quantized per channel over the expert's
+// rows (scale[e][c] = amax / 448, 1 for a zero channel or an expert without
+// rows); a first pass over the same rows takes the column amax.
+template <bool kQ>
 __global__ void __launch_bounds__(256) xpose_kernel(const uint16_t* __restrict__ src, int C,
                                                     const int32_t* __restrict__ offsets, int E,
-                                                    int rows, int pad, uint16_t* __restrict__ dst) {
+                                                    int rows, int pad, void* __restrict__ dst,
+                                                    float* __restrict__ scale) {
   __shared__ int kpre[MOE_MAX_EXPERTS + 1];
   __shared__ int offs[MOE_MAX_EXPERTS + 1];
-  __shared__ uint16_t tile[64][64 + 8];
+  __shared__ uint32_t tile[64 * 33];
+  __shared__ float cscale[64];
   const int tid = threadIdx.x;
   for (int e = tid; e <= E; e += 256) {
-    int o = offsets[e];
+    const int o = offsets[e];
     offs[e] = o < 0 ? 0 : (o > rows ? rows : o);
   }
   __syncthreads();
   if (tid == 0) {
     int kp = 0, prev = offs[0];
     for (int e = 0; e < E; ++e) {
-      int lo = prev, hi = offs[e + 1] < prev ? prev : offs[e + 1];
+      const int lo = prev, hi = offs[e + 1] < prev ? prev : offs[e + 1];
       prev = hi;
       offs[e] = lo;
       kpre[e] = kp;
@@ -49,44 +64,77 @@ __global__ void __launch_bounds__(256) xpose_kernel(const uint16_t* __restrict__
     kpre[E] = kp;
   }
   __syncthreads();
-  const int k0g = blockIdx.y * 64;
-  if (k0g >= kpre[E]) return;
-  int lo = 0, hi = E - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (kpre[mid] <= k0g) lo = mid; else hi = mid - 1;
+  const int e = blockIdx.y, c0 = blockIdx.x * 64;
+  const int r0 = offs[e], m = offs[e + 1] - r0, kp = kpre[e + 1] - kpre[e];
+  if (kp == 0) {
+    if (kQ && tid < 64 && c0 + tid < C) scale[size_t(e) * C + c0 + tid] = 1.0f;
+    return;
   }
-  const int e = lo;
-  const int k0 = k0g - kpre[e], kp = kpre[e + 1] - kpre[e], m = offs[e + 1] - offs[e];
-  const int c0 = blockIdx.x * 64;
-  {  // load 64 rows x 64 columns (two 16-byte chunks per thread)
-    const int i = tid >> 2, cc = (tid & 3) * 16;
-    u32x4 v0 = {0, 0, 0, 0}, v1 = {0, 0, 0, 0};
-    if (k0 + i < m) {
-      const u32x4* p = reinterpret_cast<const u32x4*>(src + size_t(offs[e] + k0 + i) * C + c0 + cc);
-      v0 = p[0];
-      v1 = p[1];
-    }
+  const int q = tid & 7, p = tid >> 3;  // 8-column chunk, row pair
+  const uint16_t* sp = src + size_t(r0) * C + c0 + q * 8;
+  auto ld = [&](int r) {
+    u32x4 v = {0, 0, 0, 0};
+    if (r < m) v = *reinterpret_cast<const u32x4*>(sp + size_t(r) * C);
+    return v;
+  };
+  if (kQ) {
+    float am[8];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      tile[i][cc + 2 * q] = uint16_t(v0[q]);
-      tile[i][cc + 2 * q + 1] = uint16_t(v0[q] >> 16);
-      tile[i][cc + 8 + 2 * q] = uint16_t(v1[q]);
-      tile[i][cc + 8 + 2 * q + 1] = uint16_t(v1[q] >> 16);
+    for (int j = 0; j < 8; ++j) am[j] = 0.f;
+    for (int r = p; r < m; r += 32) {
+      const u32x4 v = ld(r);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        am[2 * i] = fmaxf(am[2 * i], fabsf(bf16_lo(v[i])));
+        am[2 * i + 1] = fmaxf(am[2 * i + 1], fabsf(bf16_hi(v[i])));
+      }
     }
+    float* red = reinterpret_cast<float*>(tile);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) red[(q * 8 + j) * 33 + p] = am[j];
+    __syncthreads();
+    if (tid < 64) {
+      float a = 0.f;
+      for (int i = 0; i < 32; ++i) a = fmaxf(a, red[tid * 33 + i]);
+      const float sc = a > 0.f ? a / 448.0f : 1.0f;
+      cscale[tid] = sc;
+      if (c0 + tid < C) scale[size_t(e) * C + c0 + tid] = sc;
+    }
+    __syncthreads();
   }
-  __syncthreads();
-  {  // write 64 output rows (columns of src) x 64 k values
-    const int c = tid >> 2, kk = (tid & 3) * 16;
-    u32x4 w0, w1;
+  const int c = tid >> 2, kk = (tid & 3) * 16;  // output column, first of its 16 rows
+  const size_t obase = size_t(kpre[e]) * C + size_t(c0 + c) * kp + kk;
+  const float sc = kQ ? cscale[c] : 1.0f;
+  u32x4 va = ld(2 * p), vb = ld(2 * p + 1);
+  for (int k0 = 0; k0 < kp; k0 += 64) {
+    const u32x4 na = ld(k0 + 64 + 2 * p), nb = ld(k0 + 65 + 2 * p);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      w0[q] = uint32_t(tile[kk + 2 * q][c]) | (uint32_t(tile[kk + 2 * q + 1][c]) << 16);
-      w1[q] = uint32_t(tile[kk + 8 + 2 * q][c]) | (uint32_t(tile[kk + 8 + 2 * q + 1][c]) << 16);
+    for (int i = 0; i < 4; ++i) {
+      tile[(q * 8 + 2 * i) * 33 + p] = (va[i] & 0xFFFFu) | (vb[i] << 16);
+      tile[(q * 8 + 2 * i + 1) * 33 + p] = (va[i] >> 16) | (vb[i] & 0xFFFF0000u);
     }
-    u32x4* d = reinterpret_cast<u32x4*>(dst + size_t(kpre[e]) * C + size_t(c0 + c) * kp + k0 + kk);
-    d[0] = w0;
-    d[1] = w1;
+    __syncthreads();
+    uint32_t w[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) w[i] = tile[c * 33 + (kk >> 1) + i];
+    if (c0 + c < C) {
+      if (!kQ) {
+        u32x4* d = reinterpret_cast<u32x4*>(static_cast<uint16_t*>(dst) + obase + k0);
+        d[0] = u32x4{w[0], w[1], w[2], w[3]};
+        d[1] = u32x4{w[4], w[5], w[6], w[7]};
+      } else {
+        u32x4 o = {0, 0, 0, 0};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const uint32_t two = f32_to_e4m3(bf16_lo(w[i]) / sc) | (f32_to_e4m3(bf16_hi(w[i]) / sc) << 8);
+          o[i >> 1] |= two << (16 * (i & 1));
+        }
+        *reinterpret_cast<u32x4*>(static_cast<uint8_t*>(dst) + obase + k0) = o;
+      }
+    }
+    __syncthreads();
+    va = na;
+    vb = nb;
   }
 }
 
@@ -97,42 +145,6 @@ __global__ void __launch_bounds__(256) rowq_kernel(const uint16_t* __restrict__ 
   const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (r >= n) return;
   rowq_wave(src + size_t(r) * len, len, dst + size_t(r) * len, scale + r);
-}
-
-// The per-expert transposed blocks of xpose_kernel, quantized row by row:
-// row c of expert e (length Kp_e, at kpre[e]*C + c*Kp_e) -> codes at the same
-// place, scale[e][c] (1 for an expert without rows).  The zero padding
-// changes neither the scale nor the sums.
-__global__ void __launch_bounds__(256) rowq_xposed_kernel(const uint16_t* __restrict__ src, int C,
-                                                          const int32_t* __restrict__ offsets,
-                                                          int E, int rows, int pad,
-                                                          uint8_t* __restrict__ dst,
-                                                          float* __restrict__ scale) {
-  __shared__ int kpre[MOE_MAX_EXPERTS + 1];
-  if (threadIdx.x == 0) {
-    int kp = 0, prev = 0;
-    for (int e = 0; e < E; ++e) {
-      int o0 = offsets[e], o1 = offsets[e + 1];
-      o0 = o0 < 0 ? 0 : (o0 > rows ? rows : o0);
-      o1 = o1 < 0 ? 0 : (o1 > rows ? rows : o1);
-      const int lo = e == 0 ? o0 : prev, hi = o1 < lo ? lo : o1;
-      prev = hi;
-      kpre[e] = kp;
-      kp += ((hi - lo + pad - 1) / pad) * pad;
-    }
-    kpre[E] = kp;
-  }
-  __syncthreads();
-  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);  // r = e * C + c
-  if (r >= E * C) return;
-  const int e = r / C, c = r - e * C;
-  const int kp = kpre[e + 1] - kpre[e];
-  if (kp == 0) {
-    if ((threadIdx.x & 63) == 0) scale[r] = 1.0f;
-    return;
-  }
-  const size_t base = size_t(kpre[e]) * C + size_t(c) * kp;
-  rowq_wave(src + base, kp, dst + base, scale + r);
 }
 
 }  // namespace moe
@@ -165,9 +177,9 @@ size_t grouped_bwd_ws_bytes(int rows, int h, int h_ffn, int E, int dtype) {
 
 static int xpose(const void* src, int C, const int32_t* offsets, int E, int rows, void* dst,
                  hipStream_t s, int pad = kpad_elems<MOE_BF16>()) {
-  const size_t ky = (kpad_upper(rows, E, pad) + 63) / 64;
-  hipLaunchKernelGGL(xpose_kernel, dim3(C / 64, unsigned(ky)), dim3(256), 0, s,
-                     (const uint16_t*)src, C, offsets, E, rows, pad, (uint16_t*)dst);
+  if (C % 64 != 0) return MOE_ERR_SHAPE;
+  hipLaunchKernelGGL(xpose_kernel<false>, dim3(C / 64, E), dim3(256), 0, s, (const uint16_t*)src, C,
+                     offsets, E, rows, pad, dst, nullptr);
   return launch_status();
 }
 
@@ -240,25 +252,22 @@ static_assert(CfgQ::kRowB == CfgDA::kRowB && CfgQ::kStages == CfgDA::kStages &&
                   CfgQ::kBM == CfgDA::kBM && CfgQ::kBN == CfgDA::kBN,
               "the FP8 dA epilogue stages G|U like the BF16 one");
 
-// FP8 backward workspace: bf16 dG|dU and A, dG|dU codes + row scales, one
-// bf16 transposed block reused for each operand, the four transposed code
-// blocks and their per-expert channel scales, split-K partials.
+// FP8 backward workspace: bf16 dG|dU and A, dG|dU codes + row scales, the
+// four transposed code blocks and their per-expert channel scales, split-K
+// partials.
 size_t grouped_bwd_fp8_ws_bytes(int rows, int h, int h_ffn, int E) {
   const size_t r = size_t(rows), hh = size_t(h), hf = size_t(h_ffn), e = size_t(E);
   const size_t kp = kpad_upper(rows, E, kpad_elems<MOE_FP8_E4M3>());
-  const size_t cmax = hh > 2 * hf ? hh : 2 * hf;
   return al256(r * 2 * hf * 2) + al256(r * hf * 2) + al256(r * 2 * hf) + al256(r * 4) +
-         al256(cmax * kp * 2) + 2 * al256(hh * kp) + al256(hf * kp) + al256(2 * hf * kp) +
+         2 * al256(hh * kp) + al256(hf * kp) + al256(2 * hf * kp) +
          2 * al256(e * hh * 4) + al256(e * hf * 4) + al256(e * 2 * hf * 4) + splitk_ws_bytes<CfgQ>();
 }
 
-static int xpose_q(const void* src, int C, const int32_t* offsets, int E, int rows, void* tmp,
-                   void* dst, float* scale, hipStream_t s) {
-  constexpr int pad = kpad_elems<MOE_FP8_E4M3>();
-  int rc = xpose(src, C, offsets, E, rows, tmp, s, pad);
-  if (rc) return rc;
-  hipLaunchKernelGGL(rowq_xposed_kernel, dim3(ceil_div(E * C, 4)), dim3(256), 0, s,
-                     (const uint16_t*)tmp, C, offsets, E, rows, pad, (uint8_t*)dst, scale);
+static int xpose_q(const void* src, int C, const int32_t* offsets, int E, int rows, void* dst,
+                   float* scale, hipStream_t s) {
+  if (C % 64 != 0) return MOE_ERR_SHAPE;
+  hipLaunchKernelGGL(xpose_kernel<true>, dim3(C / 64, E), dim3(256), 0, s, (const uint16_t*)src, C,
+                     offsets, E, rows, kpad_elems<MOE_FP8_E4M3>(), dst, scale);
   return launch_status();
 }
 
@@ -267,14 +276,12 @@ int grouped_bwd_fp8(const void* dyp_q, const float* dyp_scale, const void* dyp, 
                     void* dxp, float* dw1, float* dw3, float* dw2, void* ws, hipStream_t s) {
   const int h = W->h, hf = W->h_ffn, E = W->E;
   const size_t r = size_t(rows), kp = kpad_upper(rows, E, kpad_elems<MOE_FP8_E4M3>());
-  const size_t cmax = size_t(h) > 2 * size_t(hf) ? size_t(h) : 2 * size_t(hf);
   unsigned char* w = static_cast<unsigned char*>(ws);
   auto take = [&](size_t bytes) { unsigned char* p = w; w += al256(bytes); return p; };
   void* dgu = take(r * 2 * hf * 2);
   void* act = take(r * hf * 2);
   void* dgu_q = take(r * 2 * hf);
   float* dgu_s = reinterpret_cast<float*>(take(r * 4));
-  void* tmp = take(cmax * kp * 2);
   void* xpT = take(size_t(h) * kp);
   void* dypT = take(size_t(h) * kp);
   void* actT = take(size_t(hf) * kp);
@@ -287,8 +294,8 @@ int grouped_bwd_fp8(const void* dyp_q, const float* dyp_scale, const void* dyp, 
   int rc;
 
   timer_begin(kTXpose, s);
-  if ((rc = xpose_q(xp, h, offsets, E, rows, tmp, xpT, sx, s))) return rc;
-  if ((rc = xpose_q(dyp, h, offsets, E, rows, tmp, dypT, sd, s))) return rc;
+  if ((rc = xpose_q(xp, h, offsets, E, rows, xpT, sx, s))) return rc;
+  if ((rc = xpose_q(dyp, h, offsets, E, rows, dypT, sd, s))) return rc;
   timer_end(kTXpose, s);
 
   // dA = dYp W2^T on FP8 codes; epilogue rescales and forms dG, dU and A
@@ -302,8 +309,8 @@ int grouped_bwd_fp8(const void* dyp_q, const float* dyp_scale, const void* dyp, 
                      2 * hf, (uint8_t*)dgu_q, dgu_s);
   timer_end(kTQuant, s);
   timer_begin(kTXpose, s);
-  if ((rc = xpose_q(act, hf, offsets, E, rows, tmp, actT, sa, s))) return rc;
-  if ((rc = xpose_q(dgu, 2 * hf, offsets, E, rows, tmp, dguT, sg, s))) return rc;
+  if ((rc = xpose_q(act, hf, offsets, E, rows, actT, sa, s))) return rc;
+  if ((rc = xpose_q(dgu, 2 * hf, offsets, E, rows, dguT, sg, s))) return rc;
   timer_end(kTXpose, s);
 
   // dW2 = A^T dYp  (per expert [hf][h], fp32)
