@@ -38,7 +38,8 @@
  *     output is touched.  moe_last_error() returns a message for the last
  *     failing call of the calling thread.
  *   - T = 0 (or rows = 0) is a successful no-op, except that moe_permute
- *     still writes zero counts and offsets when it builds an index.
+ *     still writes zero counts and offsets when it builds an index, and the
+ *     expert backward entry points still write zero weight gradients.
  */
 #ifndef MOE_MI355X_H
 #define MOE_MI355X_H

@@ -305,8 +305,9 @@ int grouped_bwd_fp8(const void* dyp_q, const float* dyp_scale, const void* dyp, 
   if ((rc = launch_gemm<CfgQ, MOE_FP8_E4M3, kModeBwdDA, kSchedM>(ga, kTBwd1, s))) return rc;
 
   timer_begin(kTQuant, s);
-  hipLaunchKernelGGL(rowq_kernel, dim3(ceil_div(rows, 4)), dim3(256), 0, s, (const uint16_t*)dgu, rows,
-                     2 * hf, (uint8_t*)dgu_q, dgu_s);
+  if (rows > 0)  // no rows: the weight gradients below are still written (as zeros)
+    hipLaunchKernelGGL(rowq_kernel, dim3(ceil_div(rows, 4)), dim3(256), 0, s, (const uint16_t*)dgu,
+                       rows, 2 * hf, (uint8_t*)dgu_q, dgu_s);
   timer_end(kTQuant, s);
   timer_begin(kTXpose, s);
   if ((rc = xpose_q(act, hf, offsets, E, rows, actT, sa, s))) return rc;

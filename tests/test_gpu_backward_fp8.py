@@ -22,7 +22,8 @@ feed the backward; the envelope includes the forward's fp32 error on G, U
 and the fp32 softmax's on the gate weights.
 
 The FP8 backward weight copies are compared code for code with the oracle's
-per-row quantization.
+per-row quantization.  Experts without rows get zero weight gradients, also
+when no expert has rows (rows = 0, FP8 and BF16).
 """
 import numpy as np
 import pytest
@@ -38,7 +39,7 @@ pytestmark = pytest.mark.gpu
 
 if torch.cuda.is_available():
     from mixture_experts_layer_24_amd import ops
-    from mixture_experts_layer_24_amd._lib import MOE_FP8_E4M3
+    from mixture_experts_layer_24_amd._lib import MOE_BF16, MOE_FP8_E4M3
 
 CASES = [
     ("small", dict(T=300, h=256, h_ffn=384, E=8, k=2), 1),
@@ -46,6 +47,7 @@ CASES = [
     ("e64_k6", dict(T=600, h=256, h_ffn=256, E=64, k=6), 3),
     ("multi_tile", dict(T=2100, h=512, h_ffn=384, E=4, k=2), 4),
     ("one_expert", dict(T=77, h=256, h_ffn=128, E=1, k=1), 6),
+    ("zipf_empty", dict(T=300, h=256, h_ffn=256, E=16, k=2, zipf_s=2.5), 7),
 ]
 
 
@@ -122,6 +124,10 @@ def _run(case, over, seed, shared_gu):
     np.testing.assert_array_equal(layer.dst_row.cpu().numpy(), fw["dst_row"])
     got = {"dx": host(layer.dx), "dw1": layer.dw1.cpu().numpy(), "dw3": layer.dw3.cpu().numpy(),
            "dw2": layer.dw2.cpu().numpy()}
+    # experts without rows: zero weight gradients, exactly
+    for e in np.nonzero(np.diff(fw["offsets"]) == 0)[0]:
+        for name in ("dw1", "dw3", "dw2"):
+            assert not got[name][e].any(), (name, e)
     return got, emu, exact, allow
 
 
@@ -133,3 +139,43 @@ def test_fp8_backward_unit(case, over, seed):
 @pytest.mark.parametrize("case,over,seed", CASES[:3], ids=[c[0] for c in CASES[:3]])
 def test_fp8_backward_layer(case, over, seed):
     _check(*_run(case, over, seed, False))
+
+
+def test_fp8_backward_has_empty_experts_case():
+    """The zipf_empty case does route no token to some experts."""
+    wl = moe_synth.WORKLOADS["dsmoe"].scaled(name="zipf_empty", dtype="fp8", T=300, h=256, h_ffn=256, E=16, k=2,
+                                             zipf_s=2.5)
+    inp = moe_synth.gen_all(wl, seed=7)
+    L = ref.router_logits(to_f32(inp["x"]), to_f32(inp["w_gate"]), inp["bias"])
+    idx, _ = ref.topk_softmax(L, wl.k)
+    assert (np.bincount(idx.ravel(), minlength=wl.E) == 0).any()
+
+
+@pytest.mark.parametrize("fp8", [True, False], ids=["fp8", "bf16"])
+def test_backward_no_rows(fp8):
+    """rows = 0: no error, and every expert's weight gradient is written as zeros."""
+    E, h, hf = 4, 256, 128
+    rng = np.random.default_rng(0)
+    w = lambda *sh: torch.from_numpy((rng.standard_normal(sh) * 0.05).astype(np.float32)).to(DEV).to(torch.bfloat16)
+    code = MOE_FP8_E4M3 if fp8 else MOE_BF16
+    P = ops.PackedWeights(w(E, h, hf), w(E, h, hf), w(E, hf, h), code, backward=True)
+    offsets = torch.zeros(E + 1, dtype=torch.int32, device=DEV)
+    dummy8 = torch.zeros(256, dtype=torch.uint8, device=DEV)
+    dummyf = torch.zeros(64, dtype=torch.float32, device=DEV)
+    dummyb = torch.zeros(128, dtype=torch.bfloat16, device=DEV)
+    dw1 = torch.full((E, h, hf), float("nan"), device=DEV)
+    dw3 = torch.full((E, h, hf), float("nan"), device=DEV)
+    dw2 = torch.full((E, hf, h), float("nan"), device=DEV)
+    if fp8:
+        wsb = ops.moe_grouped_bwd_fp8_workspace_size(0, h, hf, E)
+        ws = torch.empty(max(wsb, 256), dtype=torch.uint8, device=DEV)
+        ops.moe_grouped_swiglu_bwd_fp8(dummy8, dummyf, dummyb, dummyb, dummyb, P.struct, offsets, 0, dummyb, dw1,
+                                       dw3, dw2, ws, ws.numel())
+    else:
+        wsb = ops.moe_grouped_bwd_workspace_size(0, h, hf, E, MOE_BF16)
+        ws = torch.empty(max(wsb, 256), dtype=torch.uint8, device=DEV)
+        ops.moe_grouped_swiglu_bwd(dummyb, dummyb, dummyb, P.struct, offsets, 0, dummyb, dw1, dw3, dw2, ws,
+                                   ws.numel())
+    torch.cuda.synchronize()
+    for t in (dw1, dw3, dw2):
+        assert torch.equal(t, torch.zeros_like(t))
