@@ -95,7 +95,14 @@ def cpu_baseline(wl, inp, n_tokens, seed=0):
                                 out["w"], AUX_ALPHA)
     dt = time.perf_counter() - t0
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    cpu = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            cpu = next((l.split(":", 1)[1].strip() for l in fh if l.startswith("model name")), cpu)
+    except OSError:
+        pass
     return {"value": n_tokens / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "cpu": cpu, "affinity_cores": len(os.sched_getaffinity(0)),
             "sample": f"first {n_tokens} of {wl.T} tokens of the same seeded batch, full layer "
                       f"{'fwd+bwd' if wl.backward else 'fwd'} in fp64 NumPy ({dt:.1f} s)"}
 
@@ -106,8 +113,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="mixtral")
-    ap.add_argument("--cpu-tokens", type=int, default=2048,
-                    help="tokens in the CPU oracle sample (0 = skip)")
+    ap.add_argument("--cpu-tokens", type=int, default=8192,
+                    help="most tokens in the CPU oracle sample, sized for ~15 s (0 = skip)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES (3 times), to calibrate the "
                          "FETCH_SIZE / WRITE_SIZE counters against a known byte count")
@@ -176,6 +183,35 @@ def main():
     kern = ops.moe_timing_report()
     ops.moe_timing_enable(False)
     ms = elapsed * 1e3 / args.steps
+
+    # Figures beside `value`: per-step times (events around each step) warm,
+    # and cold: a 1 GiB read-modify-write before each step evicts L2 and the
+    # 256 MB Infinity Cache (outside the events).
+    def timed_steps(n, flush=None):
+        ts = []
+        for _ in range(n):
+            if flush is not None:
+                flush.add_(1)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            step()
+            b.record()
+            b.synchronize()
+            ts.append(a.elapsed_time(b))
+        return sorted(ts)
+
+    log("bench: per-step and cold-cache steps")
+    warm = timed_steps(args.steps)
+    flush_buf = torch.zeros(1 << 30, dtype=torch.uint8, device=dev)
+    cold = timed_steps(min(args.steps, 5), flush_buf)
+    del flush_buf
+    step_stats = lambda ts: {"median": round(ts[len(ts) // 2], 4), "min": round(ts[0], 4), "n": len(ts)}
+    # GEMM bound per expert: max(FLOPs / peak, weight bytes / HBM), summed (forward)
+    attainable = None
+    if not wl.backward:
+        cnt = layer.counts.cpu().tolist()
+        wbytes = 3 * wl.h * wl.h_ffn * (1 if wl.dtype == "fp8" else 4 if wl.dtype == "f32" else 2)
+        attainable = sum(max(6.0 * m * wl.h * wl.h_ffn / PEAK[wl.dtype], wbytes / HBM_PEAK) for m in cnt) * 1e3
     counts = acc.workload_counts(wl)
     avg = {k: v[1] / v[0] for k, v in kern.items()}          # ms per launch
     per_step = {k: v[1] / args.steps for k, v in kern.items()}
@@ -216,10 +252,17 @@ def main():
         "kernel_ms_per_step": {k: round(v, 4) for k, v in per_step.items()},
         "hbm": hbm,
         "roofline": roof,
+        "step_ms": step_stats(warm),
+        "cold_step_ms": dict(step_stats(cold), flush_bytes=1 << 30),
     }
+    if attainable is not None:
+        out["gemm_attainable_ms"] = round(attainable, 4)
     if args.cpu_tokens > 0:
-        log(f"bench: cpu oracle on {args.cpu_tokens} tokens")
-        out["cpu_baseline"] = cpu_baseline(wl, inp, min(args.cpu_tokens, wl.T))
+        # size the sample for about 15 s of oracle time from a short probe
+        probe = cpu_baseline(wl, inp, min(512, args.cpu_tokens, wl.T))
+        n = int(min(args.cpu_tokens, wl.T, max(512, probe["value"] * 15.0)))
+        log(f"bench: cpu oracle on {n} tokens")
+        out["cpu_baseline"] = cpu_baseline(wl, inp, n) if n > 512 else probe
     print(json.dumps(out), flush=True)
 
 

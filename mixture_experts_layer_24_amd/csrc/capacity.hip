@@ -1,7 +1,7 @@
 // Token dropping by affinity, per group of experts.
 //
 // MegaScale-MoE research digest §3.2 (the discussion of Figure 7): load
-// balance also drops tokens per GPU, "as in DeepSeek-V2", which drops on each
+// balance also drops tokens on each GPU, following DeepSeek-V2, which drops on each
 // device the tokens with the lowest affinity until the device's budget is
 // met.  A device is a group of `group` consecutive experts (one GPU's share;
 // group = 1 is a per-expert capacity): among the (token, slot) pairs routed

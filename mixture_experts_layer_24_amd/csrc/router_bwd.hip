@@ -3,7 +3,7 @@
 // The gating network is trainable (MegaScale-MoE paper review, §三 MoE layer
 // structure), so W_g and the router bias receive gradients through the gate
 // weights of the combine.  Load balance uses an auxiliary loss (research
-// digest §3.2, discussion of Figure 7, "as in DeepSeek-V2"); the pages print
+// digest §3.2, discussion of Figure 7, which points to DeepSeek-V2); the pages print
 // no formula, and the expert-level balance loss of DeepSeek-V2 is used:
 //     L_aux = alpha * sum_e f_e P_e,   f_e = E/(kT) * count_e,
 //     P_e   = (1/T) sum_t softmax(L_t)_e.

@@ -509,8 +509,8 @@ def topk_margin(logits: np.ndarray, k: int) -> np.ndarray:
 # Router backward and the load-balance loss.  [MSR] §三 (MoE layer
 # structure): the gating network is trainable, so W_g (and the router bias)
 # get gradients through the gate weights of the combine.  [MSD] §3.2 (the
-# discussion of Figure 7): load balance uses an auxiliary loss "as in
-# DeepSeek-V2".  The pages print no formula; the reading taken is
+# discussion of Figure 7): load balance uses an auxiliary loss, following
+# DeepSeek-V2.  The pages print no formula; the reading taken is
 # DeepSeek-V2's expert-level balance loss
 #     L_aux = alpha * sum_e f_e * P_e,
 #     f_e   = E / (k T) * (number of (token, slot) pairs routed to e),
@@ -570,7 +570,7 @@ def router_backward(dy, ysel, x, w_gate, logits, idx, w, alpha):
 
 def capacity_drop(idx: np.ndarray, logits: np.ndarray, E: int, group: int, capacity: int) -> np.ndarray:
     """Token dropping by affinity ([MSD] §3.2, the discussion of Figure 7:
-    "token dropping per GPU, as in DeepSeek-V2"; DeepSeek-V2 drops, on each
+    tokens are also dropped on each GPU, following DeepSeek-V2, which drops, on each
     device, the tokens with the lowest affinity until the device's budget is
     met).  A device here is a group of ``group`` consecutive experts (one
     GPU's share; ``group = 1`` is a per-expert capacity).  Among the (t, j)
