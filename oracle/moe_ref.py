@@ -535,7 +535,7 @@ def aux_balance_loss(logits: np.ndarray, idx: np.ndarray, E: int, k: int, alpha:
     return float(alpha * np.sum(f * P))
 
 
-def router_backward(dy, ysel, x, w_gate, logits, idx, w, alpha):
+def router_backward(dy, ysel, x, w_gate, logits, idx, w, alpha, counts=None, T_batch=None):
     """Gradients of ``sum_t <dy_t, y_t> + L_aux`` through the router.
 
     ``ysel[t, j]`` is the output of expert ``idx[t, j]`` for token t (the row
@@ -546,7 +546,9 @@ def router_backward(dy, ysel, x, w_gate, logits, idx, w, alpha):
         dL[t, e]      += s_te (g_e - sum_e' s_te' g_e')        (aux loss)
     with s_t = softmax(L_t) over all experts and g_e = alpha f_e / T.  Then
     dW_g = x^T dL, the router's share of dX is dL W_g^T, and d(bias) = sum_t dL.
-    Returns a dict with dw, dL, dw_gate, dx, dbias (fp64)."""
+    ``counts`` / ``T_batch``: the batch's expert counts and token count, when
+    the rows given are a subset of the batch (default: these rows are the
+    batch).  Returns a dict with dw, dL, dw_gate, dx, dbias (fp64)."""
     dy = np.asarray(dy, np.float64)
     ysel = np.asarray(ysel, np.float64)
     x = np.asarray(x, np.float64)
@@ -561,8 +563,10 @@ def router_backward(dy, ysel, x, w_gate, logits, idx, w, alpha):
     for j in range(k):
         dL[np.arange(T), idx[:, j]] += w[:, j] * (dw[:, j] - inner)
     if alpha != 0.0:
-        counts = np.bincount(np.asarray(idx).ravel(), minlength=E).astype(np.float64)
-        g = alpha * (E / (k * T) * counts) / T
+        if counts is None:
+            counts = np.bincount(np.asarray(idx).ravel(), minlength=E)
+        Tb = T if T_batch is None else T_batch
+        g = alpha * (E / (k * Tb) * np.asarray(counts, np.float64)) / Tb
         s = softmax_rows(L)
         dL += s * (g[None, :] - (s @ g)[:, None])
     return {"dw": dw, "dL": dL, "dw_gate": x.T @ dL, "dx": dL @ wg.T, "dbias": dL.sum(axis=0)}

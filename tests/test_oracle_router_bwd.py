@@ -147,3 +147,22 @@ def test_bf16_storage_forward_rounds_a_and_yp_only():
         np.testing.assert_array_equal(st[lo:hi], ref.round_bf16(ref.round_bf16(a[lo:hi]) @ w2[e]))
     rel = np.abs(st - ex).max() / np.abs(ex).max()
     assert 0 < rel < 2e-2
+
+
+def test_router_backward_on_a_subset_of_tokens():
+    """Rows of a subset, given the batch's counts and token count, equal the
+    same rows of the whole batch's evaluation (the balance-loss term depends
+    on the batch only through those two)."""
+    x, wg, b, w1, w3, w2, dy, idx = _setup(11, T=13, E=5, k=2)
+    L = x @ wg + b
+    w = ref.softmax_rows(np.take_along_axis(L, idx, axis=1))
+    ysel = np.stack([np.stack([ref.layer_forward_tokens(x[t:t + 1], idx[t:t + 1, j:j + 1],
+                                                       np.ones((1, 1)), w1, w3, w2)[0]
+                               for j in range(idx.shape[1])]) for t in range(x.shape[0])])
+    full = ref.router_backward(dy, ysel, x, wg, L, idx, w, 0.6)
+    sub = np.array([1, 4, 5, 11])
+    counts = np.bincount(idx.ravel(), minlength=wg.shape[1])
+    part = ref.router_backward(dy[sub], ysel[sub], x[sub], wg, L[sub], idx[sub], w[sub], 0.6, counts=counts,
+                               T_batch=x.shape[0])
+    np.testing.assert_allclose(part["dL"], full["dL"][sub], rtol=1e-13, atol=1e-15)
+    np.testing.assert_allclose(part["dx"], full["dx"][sub], rtol=1e-13, atol=1e-15)
