@@ -120,3 +120,64 @@ def test_full_size_dsmoe_backward_sampled():
     out_round = HALF_ULP_BF16 * np.abs(dx_em)
     check_close(got, dx_em, 2e-2, out_round, None, "dX sampled vs bf16-operand oracle")
     check_close(got, dx_ex, 2e-2, np.abs(dx_em - dx_ex) + out_round, None, "dX sampled vs exact oracle")
+
+
+@pytest.mark.slow
+def test_full_size_dsmoe_training_step_sampled():
+    """The DeepSeekMoE-shaped training step as bench.py runs it (expert and
+    router backward, balance loss of weight 0.01), at full size.  Token sums
+    cannot be sampled, so dW_g, d(bias) and the router's share of dX are
+    checked through properties that hold at any size; the balance loss
+    exactly; the total dX of sampled tokens against the oracle, as in the
+    small layer tests (bf16-storage oracle at the bar, exact oracle with the
+    storage distance allowed)."""
+    alpha = 0.01
+    wl = moe_synth.WORKLOADS["dsmoe"]
+    say("full-size dsmoe training step: generating inputs")
+    inp = moe_synth.gen_all(wl, seed=0)
+    x32, wg32, dy32 = to_f32(inp["x"]), to_f32(inp["w_gate"]), to_f32(inp["dy"])
+    L = ref.router_logits(x32, wg32, inp["bias"])
+    idx, w = ref.topk_softmax(L, wl.k)
+    say("full-size dsmoe training step: gpu")
+    P = ops.PackedWeights(dev_tensor(inp["w1"]), dev_tensor(inp["w3"]), dev_tensor(inp["w2"]), MOE_BF16,
+                          backward=True)
+    layer = ops.MoELayer(wl.T, wl.h, wl.h_ffn, wl.E, wl.k, MOE_BF16, save_for_backward=True)
+    xd, wgd = dev_tensor(inp["x"]), dev_tensor(inp["w_gate"])
+    layer.forward(xd, wgd, torch.from_numpy(inp["bias"]).to(DEV), P, logits_in=torch.from_numpy(L).to(DEV))
+    aux = float(layer.aux_loss(alpha).cpu())
+    layer.backward(dev_tensor(inp["dy"]), xd, P, w_gate=wgd, alpha=alpha)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(layer.topk_idx.cpu().numpy(), idx)
+    counts = np.bincount(idx.ravel(), minlength=wl.E)
+    assert aux == pytest.approx(ref.aux_balance_loss(L, idx, wl.E, wl.k, alpha), rel=1e-5)
+    # properties of the router gradient at full size
+    dL = layer.dlogits.cpu().numpy().astype(np.float64)
+    assert np.abs(dL.sum(axis=1)).max() <= 1e-4 * np.abs(dL).max()
+    check_close(layer.dbias.cpu().numpy(), dL.sum(axis=0), 1e-4, None, None, "d(bias) = column sums of dL")
+    check_close(layer.dw_gate.cpu().numpy(), x32.astype(np.float64).T @ dL, 1e-4, None, None, "dW_g = x^T dL")
+    want = layer.dx_expert.cpu().numpy().astype(np.float64) + dL @ wg32.astype(np.float64).T
+    check_close(host(layer.dx), want, 1e-4, HALF_ULP_BF16 * np.abs(want), None, "dX = expert part + dL W_g^T")
+    # sampled tokens: total dX against the oracle
+    toks = np.sort(np.random.default_rng(6).choice(wl.T, 32, replace=False))
+    W1, W3, W2 = (_PerExpert(inp[n]) for n in ("w1", "w3", "w2"))
+    pairs = sorted(((int(idx[t, j]), i, j) for i, t in enumerate(toks) for j in range(wl.k)))
+    offs = np.searchsorted([p[0] for p in pairs], np.arange(wl.E + 1)).astype(np.int64)
+    xp_s = x32[[toks[i] for _, i, _ in pairs]]
+
+    def ysel(st):
+        yp = ref.expert_forward(xp_s, offs, W1, W3, W2, keep=False, bf16_storage=st)
+        out = np.zeros((len(toks), wl.k, wl.h))
+        for r, (_, i, j) in enumerate(pairs):
+            out[i, j] = yp[r]
+        return out
+
+    targs = (dy32[toks], x32[toks], idx[toks], w[toks], W1, W3, W2)
+    res = {}
+    for st in (False, True):
+        rb = ref.router_backward(dy32[toks], ysel(st), x32[toks], wg32, L[toks], idx[toks], w[toks], alpha,
+                                 counts=counts, T_batch=wl.T)
+        res[st] = ref.layer_backward_tokens(*targs, bf16_operands=st) + rb["dx"]
+    got = host(layer.dx)[toks]
+    out_round = HALF_ULP_BF16 * np.abs(res[True])
+    check_close(got, res[True], 2e-2, out_round, None, "dX sampled vs bf16-storage oracle")
+    check_close(got, res[False], 2e-2, np.abs(res[True] - res[False]) + out_round, None, "dX sampled vs exact oracle")

@@ -380,7 +380,7 @@ class _PerExpert:
     """Widens one expert's bf16 weight to fp32 when the oracle asks for it."""
 
     def __init__(self, a):
-        self.a = a
+        self.a, self.shape = a, a.shape
 
     def __getitem__(self, e):
         return to_f32(self.a[e])
