@@ -337,7 +337,7 @@ int moe_router_bwd(const void* dy, const void* yp, const int32_t* dst_row, const
 
 /*
  * Load-balance loss (MegaScale-MoE research digest §3.2: an auxiliary loss
- * balances the experts, as in DeepSeek-V2; the digest prints no formula, and
+ * balances the experts, following DeepSeek-V2; the digest prints no formula, and
  * DeepSeek-V2's expert-level form is used):
  *   loss = alpha * sum_e f_e P_e,  f_e = E / (k T) * counts[e],
  *   P_e  = (1/T) sum_t softmax(logits[t])_e.
@@ -358,6 +358,19 @@ int moe_router_aux_loss(const float* logits, const int32_t* counts, int T, int E
  */
 int moe_timing_enable(int on);
 int moe_timing_report(char* buf, size_t len);
+
+/*
+ * Self-test of the FP8 encoder.  The activation quantizers (dispatch copy,
+ * A, dG|dU, the transposed weight-gradient operands) encode with the
+ * hardware's packed fp32 -> E4M3 conversion; this runs, for every finite
+ * fp32 of magnitude <= 464 (the quantizers pass at most 448 (1 + 2^-23)),
+ * that conversion and the library's bit-level reference encoder (OCP
+ * E4M3FN, round to nearest even, saturating), in pairs and quadruples, and
+ * writes the number of disagreements to *mismatches (one uint64 in device
+ * memory, written on the stream; 0 expected).  About 2^32 values: tens of
+ * milliseconds.
+ */
+int moe_fp8_convert_selftest(unsigned long long* mismatches, void* stream);
 
 /* Message of the last failing call on this thread ("" if none). */
 const char* moe_last_error(void);

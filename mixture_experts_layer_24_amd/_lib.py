@@ -58,6 +58,7 @@ SIGNATURES = {
     "moe_timing_report": (I, [ctypes.c_char_p, SZ]),
     "moe_last_error": (ctypes.c_char_p, []),
     "moe_version": (I, []),
+    "moe_fp8_convert_selftest": (I, [P, P]),
 }
 
 _lib = None

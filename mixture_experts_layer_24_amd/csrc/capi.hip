@@ -66,7 +66,7 @@ extern "C" {
 
 const char* moe_last_error(void) { return g_err; }
 
-int moe_version(void) { return 3; }
+int moe_version(void) { return 4; }
 
 size_t moe_packed_weight_bytes(int which, int E, int h, int h_ffn, int dtype) {
   if (E <= 0 || h <= 0 || h_ffn <= 0 || dtype < MOE_F32 || dtype > MOE_FP8_E4M3) return 0;
@@ -404,6 +404,13 @@ int moe_router_aux_loss(const float* logits, const int32_t* counts, int T, int E
   moe_launch::clear_status();
   return launched(moe_launch::router_aux(logits, counts, T, E, k, alpha, loss, ws, (hipStream_t)stream),
                   "moe_router_aux_loss");
+}
+
+int moe_fp8_convert_selftest(unsigned long long* mismatches, void* stream) {
+  PTR(mismatches);
+  moe_launch::clear_status();
+  return launched(moe_launch::fp8_convert_selftest(mismatches, (hipStream_t)stream),
+                  "moe_fp8_convert_selftest");
 }
 
 }  // extern "C"

@@ -59,6 +59,21 @@ __device__ __forceinline__ uint32_t f32_to_e4m3(float v) {
   return sign | code;
 }
 
+// The same encoding by the hardware's packed conversion, two or four values
+// at a time (bytes from low to high in argument order).  It rounds to
+// nearest even like f32_to_e4m3 and gives the same code for every finite
+// fp32 of magnitude <= 464 (moe_fp8_convert_selftest checks all of them on
+// the device); the quantizers pass v / s with |v| <= amax = 448 s, so
+// |v / s| <= 448 (1 + 2^-23).  One instruction per pair instead of the
+// bit manipulation above, which stays the reference.
+__device__ __forceinline__ uint32_t e4m3x2(float a, float b) {
+  return uint32_t(__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false)) & 0xFFFFu;
+}
+__device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
+  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  return uint32_t(__builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true));
+}
+
 __device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
   uint32_t s = (c & 0x80u) << 24;
   uint32_t e = (c >> 3) & 0xFu, m = c & 7u;
@@ -93,14 +108,8 @@ __device__ __forceinline__ void rowq_wave(const uint16_t* __restrict__ src, int 
   if (lane == 0) *scale = s;
   for (int c = lane * 8; c < len; c += 512) {
     const u32x4 v = *reinterpret_cast<const u32x4*>(src + c);
-    uint32_t lo = 0, hi = 0;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      lo |= f32_to_e4m3(bf16_lo(v[i]) / s) << (16 * i);
-      lo |= f32_to_e4m3(bf16_hi(v[i]) / s) << (16 * i + 8);
-      hi |= f32_to_e4m3(bf16_lo(v[2 + i]) / s) << (16 * i);
-      hi |= f32_to_e4m3(bf16_hi(v[2 + i]) / s) << (16 * i + 8);
-    }
+    const uint32_t lo = e4m3x4(bf16_lo(v[0]) / s, bf16_hi(v[0]) / s, bf16_lo(v[1]) / s, bf16_hi(v[1]) / s);
+    const uint32_t hi = e4m3x4(bf16_lo(v[2]) / s, bf16_hi(v[2]) / s, bf16_lo(v[3]) / s, bf16_hi(v[3]) / s);
     *reinterpret_cast<uint2*>(dst + c) = make_uint2(lo, hi);
   }
 }
@@ -126,6 +135,7 @@ int index_build(const int32_t* topk_idx, int T, int E, int k, int32_t* counts, i
                 int32_t* dst_row, int32_t* src_tok, void* ws, hipStream_t s);
 size_t index_ws_bytes(int T, int E);
 int local_ids(const int32_t* topk_idx, int n, int e_lo, int e_count, int32_t* out, hipStream_t s);
+int fp8_convert_selftest(unsigned long long* mismatches, hipStream_t s);
 int permute_rows(const void* src, int src_dt, const int32_t* dst_row, const float* row_scale,
                  int T, int h, int k, void* dst, int dst_dt, float* dst_scale, hipStream_t s);
 int combine_rows(const void* yp, int yp_dt, const int32_t* dst_row, const float* w, int T, int h,

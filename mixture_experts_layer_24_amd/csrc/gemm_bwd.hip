@@ -123,12 +123,11 @@ __global__ void __launch_bounds__(256) xpose_kernel(const uint16_t* __restrict__
         d[0] = u32x4{w[0], w[1], w[2], w[3]};
         d[1] = u32x4{w[4], w[5], w[6], w[7]};
       } else {
-        u32x4 o = {0, 0, 0, 0};
+        u32x4 o;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const uint32_t two = f32_to_e4m3(bf16_lo(w[i]) / sc) | (f32_to_e4m3(bf16_hi(w[i]) / sc) << 8);
-          o[i >> 1] |= two << (16 * (i & 1));
-        }
+        for (int i = 0; i < 4; ++i)
+          o[i] = e4m3x4(bf16_lo(w[2 * i]) / sc, bf16_hi(w[2 * i]) / sc, bf16_lo(w[2 * i + 1]) / sc,
+                        bf16_hi(w[2 * i + 1]) / sc);
         *reinterpret_cast<u32x4*>(static_cast<uint8_t*>(dst) + obase + k0) = o;
       }
     }

@@ -56,10 +56,7 @@ __global__ void __launch_bounds__(256) quant_act_kernel(const float* __restrict_
 #pragma unroll
     for (int b = 0; b < kBatch; ++b) {
       if (c0 + 64 * b >= n4) break;
-      uint32_t w = 0;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) w |= f32_to_e4m3(v[b][i] / s) << (8 * i);
-      dst[c0 + 64 * b] = w;
+      dst[c0 + 64 * b] = e4m3x4(v[b][0] / s, v[b][1] / s, v[b][2] / s, v[b][3] / s);
     }
   }
 }

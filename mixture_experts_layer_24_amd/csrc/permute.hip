@@ -116,11 +116,8 @@ __global__ void __launch_bounds__(256) permute_fp8_kernel(const uint16_t* __rest
       if (c >= nch) break;
       float f[8];
       unpack8(v[b], f);
-      uint32_t lo = 0, hi = 0;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) lo |= f32_to_e4m3(f[i] / scale) << (8 * i);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) hi |= f32_to_e4m3(f[4 + i] / scale) << (8 * i);
+      const uint32_t lo = e4m3x4(f[0] / scale, f[1] / scale, f[2] / scale, f[3] / scale);
+      const uint32_t hi = e4m3x4(f[4] / scale, f[5] / scale, f[6] / scale, f[7] / scale);
       for (int j = 0; j < k; ++j) {
         if (rows[j] < 0 || rows[j] >= T * k) continue;
         uint2* d = reinterpret_cast<uint2*>(dst + size_t(rows[j]) * h);

@@ -152,6 +152,10 @@ def moe_version() -> int:
     return lib().moe_version()
 
 
+def moe_fp8_convert_selftest(mismatches, stream=None):
+    return check(lib().moe_fp8_convert_selftest(_p(mismatches), _s(stream)))
+
+
 # ---- one preallocated layer ------------------------------------------------
 
 class PackedWeights:

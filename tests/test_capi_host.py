@@ -26,7 +26,7 @@ def test_exports_every_declared_symbol():
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) <= set(L.SIGNATURES)
-    assert lib.moe_version() == 3
+    assert lib.moe_version() == 4
 
 
 A = ctypes.c_void_p(1 << 20)   # aligned, never dereferenced: validation fails first

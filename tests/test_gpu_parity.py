@@ -193,6 +193,16 @@ def test_permute_drops_invalid_ids_and_empty_batch():
     assert lay0["counts"].cpu().tolist() == [0] * E and lay0["offsets"].cpu().tolist() == [0] * (E + 1)
 
 
+def test_fp8_hardware_encoder_matches_reference():
+    """The quantizers' hardware E4M3 conversion agrees with the library's
+    bit-level encoder on every finite fp32 of magnitude <= 464, packed in
+    pairs and quadruples (moe_fp8_convert_selftest)."""
+    n = torch.full((1,), -1, dtype=torch.int64, device=DEV)
+    ops.moe_fp8_convert_selftest(n)
+    torch.cuda.synchronize()
+    assert int(n.item()) == 0
+
+
 @pytest.mark.parametrize("T,E,k,h", [(300, 16, 1, 6400), (129, 8, 2, 256)])
 def test_permute_fp8_bit_exact(T, E, k, h):
     say(f"permute fp8 T={T} h={h}")
