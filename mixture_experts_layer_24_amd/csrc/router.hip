@@ -94,13 +94,25 @@ __global__ void __launch_bounds__(256) route_bf16_kernel(const uint16_t* __restr
     // W_g rows kc .. kc+kn-1 are kn*E contiguous values: 16-byte units
     const uint16_t* src = wg + size_t(kc) * E;
     const int units = kn * E / 8;
-    for (int u = lane; u < units; u += 64) {
-      const u32x4 v = *reinterpret_cast<const u32x4*>(src + size_t(u) * 8);
-      int q = u * 8, kk = q / E, e = q - kk * E;
+    if ((E & 7) == 0) {
+      // units k-fastest: neighbouring lanes store neighbouring k of one
+      // expert row of W^T (2-byte stores into the same or the next word)
+      for (int u = lane; u < units; u += 64) {
+        const int kk = u % kn, e8 = u / kn;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(src + size_t(kk) * E + e8 * 8);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        wt[e * kRtStride + kk] = uint16_t(v[i >> 1] >> (16 * (i & 1)));
-        if (++e == E) { e = 0; ++kk; }
+        for (int i = 0; i < 8; ++i)
+          wt[(e8 * 8 + i) * kRtStride + kk] = uint16_t(v[i >> 1] >> (16 * (i & 1)));
+      }
+    } else {
+      for (int u = lane; u < units; u += 64) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(src + size_t(u) * 8);
+        int q = u * 8, kk = q / E, e = q - kk * E;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          wt[e * kRtStride + kk] = uint16_t(v[i >> 1] >> (16 * (i & 1)));
+          if (++e == E) { e = 0; ++kk; }
+        }
       }
     }
     __syncthreads();
