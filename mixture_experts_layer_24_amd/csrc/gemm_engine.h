@@ -77,7 +77,7 @@ struct GemmArgs {
   void* out;              // see the modes
   void* out2;             // BwdDA: A [rows][N]; DW13: dW3
   void* save;             // FC1: G|U out [rows][N] bf16 or null; BwdDA: G|U in [rows][2N]
-  uint32_t* row_amax;     // FC1 with FP8: [rows] (fp32 bits, atomic max)
+  float* row_amax;        // FC1 with FP8: [rows][ceil(N / BN)] row maxima of |A|, one per column tile
   float* part;            // split-K partial tiles (kMaxGrid tiles) or null: no split
   uint32_t* cnt;          // split-K arrival counters [kMaxGrid], zero before the launch
 };
@@ -326,16 +326,34 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, f32x16 (&acc)[C::kMI
         }
       }
       if (DT == MOE_FP8_E4M3) {
-        // row max over this wave's channels: reduce over the 32 lanes of a half
+        // row max over this wave's channels: reduce over the 32 lanes of a
+        // half, then park it in the idle LDS stage ([wave column][tile row])
+        float* red = reinterpret_cast<float*>(free_lds);
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           float m = rmax[r];
 #pragma unroll
           for (int o = 16; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
-          const int row = rbase + acc_row(i, r, half);
-          if (l32 == 0 && row < row_end) atomicMax(g.row_amax + row, __float_as_uint(m));
+          if (l32 == 0) red[wn * C::kBM + wm * (MI * 32) + acc_row(i, r, half)] = m;
         }
       }
+    }
+    if (DT == MOE_FP8_E4M3) {
+      // the tile's row maxima over its channels: one plain store per row into
+      // this column tile's slot (every slot has exactly one writer, so no
+      // atomics and no reset); the quantization takes the max over slots.
+      // The idle stage is read here and refilled by the next tile's loads.
+      __syncthreads();
+      const float* red = reinterpret_cast<const float*>(free_lds);
+      const int ntn = (g.N + C::kBN - 1) / C::kBN;
+      for (int q = threadIdx.x; q < C::kBM; q += C::kThreads) {
+        float m = red[q];
+#pragma unroll
+        for (int w = 1; w < C::kWN; ++w) m = fmaxf(m, red[w * C::kBM + q]);
+        const int row = row0 + q;
+        if (row < row_end) g.row_amax[size_t(row) * ntn + n0 / C::kBN] = m;
+      }
+      __syncthreads();
     }
   } else if (MODE == kModeFC2) {
 #pragma unroll

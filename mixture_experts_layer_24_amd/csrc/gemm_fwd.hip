@@ -32,16 +32,19 @@
 
 namespace moe {
 
-// FP8: act (fp32) -> E4M3 codes with per-row scale amax/448, amax from FC1.
+// FP8: act (fp32) -> E4M3 codes with per-row scale amax/448; amax is the max
+// of the row's ntn per-column-tile maxima that FC1's epilogue stored.
 __global__ void __launch_bounds__(256) quant_act_kernel(const float* __restrict__ act,
-                                                        const uint32_t* __restrict__ row_amax,
+                                                        const float* __restrict__ row_amax, int ntn,
                                                         const int32_t* __restrict__ offsets,
                                                         int E, int hf, uint8_t* __restrict__ q,
                                                         float* __restrict__ scale) {
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= offsets[E]) return;
-  const float amax = __uint_as_float(row_amax[row]);
+  float amax = 0.f;
+  for (int j = lane; j < ntn; j += 64) amax = fmaxf(amax, row_amax[size_t(row) * ntn + j]);
+  amax = wave_max(amax);
   const float s = amax > 0.f ? amax / 448.0f : 1.0f;
   if (lane == 0) scale[row] = s;
   const f32x4* src = reinterpret_cast<const f32x4*>(act + size_t(row) * hf);
@@ -61,11 +64,6 @@ __global__ void __launch_bounds__(256) quant_act_kernel(const float* __restrict_
   }
 }
 
-__global__ void fill_u32_kernel(uint32_t* p, size_t n, uint32_t v) {
-  size_t i = size_t(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (i < n) p[i] = v;
-}
-
 }  // namespace moe
 
 namespace moe_launch {
@@ -73,11 +71,17 @@ using namespace moe;
 
 static size_t al256(size_t x) { return (x + 255) & ~size_t(255); }
 
+// FC1's column tiles (packed G|U, 2 h_ffn wide): one row-maximum slot each.
+static size_t fc1_col_tiles(int h_ffn) {
+  constexpr int BN = CfgFor<MOE_FP8_E4M3>::type::kBN;
+  return size_t((2 * h_ffn + BN - 1) / BN);
+}
+
 size_t grouped_fwd_ws_bytes(int rows, int h, int h_ffn, int E, int dtype) {
   (void)h; (void)E;
   size_t r = size_t(rows), hf = size_t(h_ffn);
   size_t act = al256(r * hf * (dtype == MOE_BF16 ? 2 : 4));
-  if (dtype == MOE_FP8_E4M3) act += al256(r * hf) + 2 * al256(r * 4);
+  if (dtype == MOE_FP8_E4M3) act += al256(r * hf) + al256(r * 4 * fc1_col_tiles(h_ffn)) + al256(r * 4);
   return act + splitk_ws_bytes<CfgFor<MOE_BF16>::type>();
 }
 
@@ -94,16 +98,16 @@ static int fwd_typed(const void* xp, const float* xp_scale, const moe_weights* W
   unsigned char* w = static_cast<unsigned char*>(ws);
   void* act = w;
   size_t act_b = al256(size_t(rows) * hf * (DT == MOE_BF16 ? 2 : 4));
-  void* split_ws = w + act_b + (DT == MOE_FP8_E4M3 ? al256(size_t(rows) * hf) + 2 * al256(size_t(rows) * 4) : 0);
+  const size_t ntn = fc1_col_tiles(hf);
+  const size_t amax_b = al256(size_t(rows) * 4 * ntn);
+  void* split_ws = w + act_b + (DT == MOE_FP8_E4M3 ? al256(size_t(rows) * hf) + amax_b + al256(size_t(rows) * 4) : 0);
   uint8_t* actq = nullptr;
-  uint32_t* amax = nullptr;
+  float* amax = nullptr;
   float* ascale = nullptr;
   if (DT == MOE_FP8_E4M3) {
     actq = reinterpret_cast<uint8_t*>(w + act_b);
-    amax = reinterpret_cast<uint32_t*>(w + act_b + al256(size_t(rows) * hf));
-    ascale = reinterpret_cast<float*>(w + act_b + al256(size_t(rows) * hf) + al256(size_t(rows) * 4));
-    hipLaunchKernelGGL(fill_u32_kernel, dim3(ceil_div(rows, 256)), dim3(256), 0, s, amax,
-                       size_t(rows), 0u);
+    amax = reinterpret_cast<float*>(w + act_b + al256(size_t(rows) * hf));
+    ascale = reinterpret_cast<float*>(w + act_b + al256(size_t(rows) * hf) + amax_b);
   }
   GemmArgs a1{xp, xp_scale, W->w13, W->w13_scale, offsets, E, h, 2 * hf, rows, 0,
               act, nullptr, h13_save, amax, nullptr, nullptr};
@@ -113,7 +117,7 @@ static int fwd_typed(const void* xp, const float* xp_scale, const moe_weights* W
   if (DT == MOE_FP8_E4M3) {
     timer_begin(kTQuant, s);
     hipLaunchKernelGGL(quant_act_kernel, dim3(ceil_div(rows, 4)), dim3(256), 0, s,
-                       (const float*)act, amax, offsets, E, hf, actq, ascale);
+                       (const float*)act, amax, int(ntn), offsets, E, hf, actq, ascale);
     timer_end(kTQuant, s);
     GemmArgs a2{actq, ascale, W->w2, W->w2_scale, offsets, E, hf, h, rows, 0, yp, nullptr, nullptr, nullptr,
                 nullptr, nullptr};
