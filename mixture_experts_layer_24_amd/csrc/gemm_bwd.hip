@@ -247,9 +247,11 @@ namespace moe_launch {
 using namespace moe;
 
 using CfgQ = CfgFor<MOE_FP8_E4M3>::type;
-static_assert(CfgQ::kRowB == CfgDA::kRowB && CfgQ::kStages == CfgDA::kStages &&
-                  CfgQ::kBM == CfgDA::kBM && CfgQ::kBN == CfgDA::kBN,
-              "the FP8 dA epilogue stages G|U like the BF16 one");
+// FP8 dA: FP8 accumulators live in VGPRs, and with 128 of them per lane the
+// dA epilogue (kept G|U staged through LDS, three outputs) spills; waves of
+// 64 x 64 (128 x 256 tiles) hold 64.
+using CfgDAq = GemmCfg<2, 4, 2, 2, 1, 128, 2>;
+static_assert(splitk_ws_bytes<CfgDAq>() <= splitk_ws_bytes<CfgQ>(), "one split-K area for all");
 
 // FP8 backward workspace: bf16 dG|dU and A, dG|dU codes + row scales, the
 // four transposed code blocks and their per-expert channel scales, split-K
@@ -300,8 +302,8 @@ int grouped_bwd_fp8(const void* dyp_q, const float* dyp_scale, const void* dyp, 
   // dA = dYp W2^T on FP8 codes; epilogue rescales and forms dG, dU and A
   GemmArgs ga{dyp_q, dyp_scale, W->w2_bwd, W->w2_bwd_scale, offsets, E, h, hf, rows, 0,
               dgu, act, const_cast<void*>(h13_save), nullptr, nullptr, nullptr};
-  splitk_ws_set<CfgQ>(ga, split_ws);
-  if ((rc = launch_gemm<CfgQ, MOE_FP8_E4M3, kModeBwdDA, kSchedM>(ga, kTBwd1, s))) return rc;
+  splitk_ws_set<CfgDAq>(ga, split_ws);
+  if ((rc = launch_gemm<CfgDAq, MOE_FP8_E4M3, kModeBwdDA, kSchedM>(ga, kTBwd1, s))) return rc;
 
   timer_begin(kTQuant, s);
   if (rows > 0)  // no rows: the weight gradients below are still written (as zeros)

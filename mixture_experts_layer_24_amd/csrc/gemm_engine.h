@@ -384,7 +384,7 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, f32x16 (&acc)[C::kMI
     // the epilogue, split evenly over the waves) in direct loads, a chunk of
     // rows at a time, then come out of LDS as needed.
     constexpr int kRegion = C::kStage / C::kNW;              // bytes of LDS per wave
-    constexpr int kRows = kRegion / 128 < MI * 32 ? kRegion / 128 : MI * 32;
+    constexpr int kRows = (kRegion / 128 < MI * 32 ? kRegion / 128 : MI * 32) / 32 * 32;  // whole blocks
     constexpr int kIPer = kRows / 32;                        // MFMA blocks per chunk
     static_assert(kIPer >= 1 && MI % kIPer == 0, "chunk of whole MFMA blocks");
     const int hf = g.N;
