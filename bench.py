@@ -114,7 +114,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="mixtral")
     ap.add_argument("--cpu-tokens", type=int, default=8192,
-                    help="most tokens in the CPU oracle sample, sized for ~15 s (0 = skip)")
+                    help="most tokens in the CPU oracle sample, kept under ~45 s (0 = skip)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES (3 times), to calibrate the "
                          "FETCH_SIZE / WRITE_SIZE counters against a known byte count")
@@ -258,9 +258,14 @@ def main():
     if attainable is not None:
         out["gemm_attainable_ms"] = round(attainable, 4)
     if args.cpu_tokens > 0:
-        # size the sample for about 15 s of oracle time from a short probe
-        probe = cpu_baseline(wl, inp, min(512, args.cpu_tokens, wl.T))
-        n = int(min(args.cpu_tokens, wl.T, max(512, probe["value"] * 15.0)))
+        # a short probe bounds the sample: the oracle's time grows at most
+        # linearly in tokens (it has a fixed per-expert part), so the whole
+        # requested sample runs unless the probe extrapolates past ~45 s
+        n0 = min(512, args.cpu_tokens, wl.T)
+        probe = cpu_baseline(wl, inp, n0)
+        n = min(args.cpu_tokens, wl.T)
+        if n0 / probe["value"] * n / n0 > 45.0:
+            n = int(max(n0, 45.0 * probe["value"]))
         log(f"bench: cpu oracle on {n} tokens")
         out["cpu_baseline"] = cpu_baseline(wl, inp, n) if n > 512 else probe
     print(json.dumps(out), flush=True)
