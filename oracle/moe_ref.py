@@ -425,14 +425,21 @@ def quantize_cols(wm: np.ndarray):
     return q, s
 
 
-def layer_forward_fp8(x, w_gate, bias, w1, w3, w2, k, logits=None):
+def layer_forward_fp8(x, w_gate, bias, w1, w3, w2, k, logits=None, noise=None):
     """Forward layer with FP8 GEMM inputs (quantization emulated exactly).
 
     x is quantized per token before the dispatch copy, so each routed row
     keeps its token's scale; W1, W3 per output channel over h, W2 per output
     channel over h_ffn; FC1 result = (q_x . q_w) * s_x * s_w; A is quantized
-    per routed row from its fp64 value; FC2 result = (q_a . q_w2) * s_a * s_w2.
+    per routed row in the kernel's precision (its value rounded to fp32, the
+    fp32 scale amax / 448, codes of the fp32 quotient: ``quantize_rows``);
+    FC2 result = (q_a . q_w2) * s_a * s_w2.  ``noise(name, e, v)``, when
+    given, replaces each value an implementation computes before rounding or
+    quantizing it ("g", "u", "a"; "yp" for FC2's fp32 sum; "w" with e = -1
+    for the gate weights), so that a test can evaluate nearby
+    implementations.
     """
+    nz = noise if noise is not None else (lambda name, e, v: v)
     E = w1.shape[0]
     L = router_logits(x, w_gate, bias) if logits is None else np.asarray(logits, np.float32)
     idx, w = topk_softmax(L, k)
@@ -453,16 +460,15 @@ def layer_forward_fp8(x, w_gate, bias, w1, w3, w2, k, logits=None):
             continue
         q1, s1 = quantize_cols(w1[e]); q3, s3 = quantize_cols(w3[e]); q2, s2 = quantize_cols(w2[e])
         xe = e4m3_decode(qxp[lo:hi])
-        g = (xe @ e4m3_decode(q1)) * sxp[lo:hi, None].astype(np.float64) * s1[None, :].astype(np.float64)
-        u = (xe @ e4m3_decode(q3)) * sxp[lo:hi, None].astype(np.float64) * s3[None, :].astype(np.float64)
-        a = silu(g) * u
-        amax = np.max(np.abs(a), axis=1)
-        sa = np.where(amax > 0, amax / E4M3_MAX, 1.0)
-        qa = e4m3_encode(a / sa[:, None])
-        yp[lo:hi] = (e4m3_decode(qa) @ e4m3_decode(q2)) * sa[:, None] * s2[None, :].astype(np.float64)
+        g = nz("g", e, (xe @ e4m3_decode(q1)) * sxp[lo:hi, None].astype(np.float64) * s1[None, :].astype(np.float64))
+        u = nz("u", e, (xe @ e4m3_decode(q3)) * sxp[lo:hi, None].astype(np.float64) * s3[None, :].astype(np.float64))
+        a = nz("a", e, silu(g) * u)
+        qa, sa = quantize_rows(a)
+        sa = sa.astype(np.float64)
+        yp[lo:hi] = nz("yp", e, (e4m3_decode(qa) @ e4m3_decode(q2)) * sa[:, None] * s2[None, :].astype(np.float64))
         a_all[lo:hi] = a; qa_all[lo:hi] = qa; sa_all[lo:hi] = sa
         g_all[lo:hi] = g; u_all[lo:hi] = u
-    y = combine(yp, dst_row, w)
+    y = combine(yp, dst_row, nz("w", -1, w))
     return dict(logits=L, idx=idx, w=w, counts=counts, offsets=offsets, dst_row=dst_row,
                 src_tok=src_tok, qx=qx, sx=sx, g=g_all, u=u_all, a=a_all, qa=qa_all, sa=sa_all,
                 yp=yp, y=y)
@@ -489,9 +495,8 @@ def layer_forward_fp8_tokens(x_rows, idx_rows, w_rows, w1, w3, w2, wq_cache=None
         g = (xe @ e4m3_decode(q1)) * s1[None, :].astype(np.float64)
         u = (xe @ e4m3_decode(q3)) * s3[None, :].astype(np.float64)
         a = silu(g) * u
-        amax = np.max(np.abs(a), axis=1)
-        sa = np.where(amax > 0, amax / E4M3_MAX, 1.0)
-        qa = e4m3_encode(a / sa[:, None])
+        qa, sa = quantize_rows(a)
+        sa = sa.astype(np.float64)
         ye = (e4m3_decode(qa) @ e4m3_decode(q2)) * sa[:, None] * s2[None, :].astype(np.float64)
         y[tt] += np.asarray(w_rows[tt, jj], np.float64)[:, None] * ye
     return y
@@ -917,4 +922,97 @@ def fp8_backward_envelope(dy, x, w, dst_row, offsets, w1, w3, w2, g, u, g_err=No
     # that rounding of the result itself (half a bf16 ulp) is left to the caller
     mag = combine(dxp_abs + out["dxp"], dst_row, None)
     out["dx"] = combine(out["dxp"], dst_row, None) + fp32_sum_gamma(k) * mag + 2.0 ** -8 * combine(out["dxp"], dst_row, None)
+    return out
+
+
+# --------------------------------------------------------------------------
+# Allowance of the FP8 forward.  A is quantized per routed row from the value
+# an implementation forms in fp32 (SiLU(G) U from an fp32 FC1); the same
+# reasoning as for the backward bounds how far the result of any such
+# implementation can be from `layer_forward_fp8`'s.  The row scale follows
+# the row's amax continuously here (A is not rounded to bf16 first), so the
+# quantizer is bounded through the ends of the value interval and of the
+# scale interval: for a fixed scale the code is monotone in the value, and
+# for a fixed code the dequantized value is monotone in the scale.
+# --------------------------------------------------------------------------
+
+def rowq_spread_interval(vo, lo, hi):
+    """``quantize_rows`` of the fp32 values ``vo`` against every matrix with
+    elements in [lo, hi] (fp32 values, lo <= vo <= hi) and any fp32 scale the
+    row's amax can give.  Returns the dequantized values of ``vo`` and a
+    per-element bound on the distance to those of any such matrix."""
+    vo = np.asarray(vo, np.float32)
+    q, s = quantize_rows(vo)
+    qo = e4m3_decode(q) * s.astype(np.float64)[:, None]
+    lo = np.asarray(lo, np.float32); hi = np.asarray(hi, np.float32)
+    straddle = (lo <= 0) & (hi >= 0)
+    m_lo = np.where(straddle, np.float32(0), np.minimum(np.abs(lo), np.abs(hi)))
+    m_hi = np.maximum(np.abs(lo), np.abs(hi))
+    s_lo = quant_scale(m_lo.max(axis=1) if vo.shape[1] else np.zeros(vo.shape[0]))[:, None]
+    s_hi = quant_scale(m_hi.max(axis=1) if vo.shape[1] else np.zeros(vo.shape[0]))[:, None]
+
+    def mag(m, sc, sc_out):
+        return e4m3_decode(e4m3_encode((m / sc).astype(np.float32))) * sc_out.astype(np.float64)
+
+    lower = mag(m_lo, s_hi, s_lo)
+    upper = mag(m_hi, s_lo, s_hi)
+    aq = np.abs(qo)
+    spread = np.where(straddle, aq + upper, np.maximum(aq - lower, upper - aq))
+    return qo, np.maximum(spread, 0.0)
+
+
+def fp8_forward_envelope(fw, w1, w3, w2, g_err=None, u_err=None, w_err=None):
+    """Per-element allowance of `layer_forward_fp8` (its result ``fw``): a
+    bound on |y - fw["y"]| for every implementation with an fp32 FC1 (G, U
+    within ``g_err`` / ``u_err`` of fw's), A = SiLU(G) U in fp32, the row
+    quantization of that fp32 A, FC2 summed in fp32 (trees as for the
+    backward), Yp stored in bf16, and gate weights within ``w_err``, added in
+    fp32 and the sum rounded once (the rounding of the result itself, half a
+    bf16 ulp of y, is left to the caller; the rounding of the allowance is
+    included).  Returns y, yp (the stored bf16 Yp against fw's unrounded
+    one), and the bounds d_a (A before quantization, fp32 evaluation only,
+    per routed row) and d_yp (FC2's own fp32 sum)."""
+    g, u = np.asarray(fw["g"], np.float64), np.asarray(fw["u"], np.float64)
+    R, hf = g.shape
+    dst_row, offsets = fw["dst_row"], fw["offsets"]
+    T, k = dst_row.shape
+    h = w2.shape[2]
+    g_err = np.zeros((R, hf)) if g_err is None else np.asarray(g_err, np.float64)
+    u_err = np.zeros((R, hf)) if u_err is None else np.asarray(u_err, np.float64)
+    out = dict(d_a=np.zeros((R, hf)), d_yp=np.zeros((R, h)), yp=np.zeros((R, h)))
+    dev = np.zeros((R, h))
+    ypo_abs = np.abs(np.asarray(fw["yp"], np.float64))
+    for e in range(w1.shape[0]):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        if hi == lo:
+            continue
+        ge, ue, dg, du = g[lo:hi], u[lo:hi], g_err[lo:hi], u_err[lo:hi]
+        umax = np.abs(ue) + du
+        silu_max = np.abs(silu(ge)) + 1.1 * dg
+        a0 = silu(ge) * ue
+        d_eval = 4.0 * F32_U * (1.0 + np.abs(ge) + dg) * silu_max * umax + F32_U * np.abs(a0)
+        d_a = 1.1 * dg * umax + silu_max * du + d_eval
+        out["d_a"][lo:hi] = d_eval
+        a_lo = (a0 - d_a).astype(np.float32); a_hi = (a0 + d_a).astype(np.float32)
+        qa, sp = rowq_spread_interval(a0.astype(np.float32), np.minimum(a_lo, a0.astype(np.float32)),
+                                      np.maximum(a_hi, a0.astype(np.float32)))
+        q2, s2 = quantize_cols(np.asarray(w2[e], np.float32))
+        b2 = e4m3_decode(q2) * s2.astype(np.float64)[None, :]          # [hf, h]
+        d_c = product_spread(qa, sp, b2.T, np.zeros_like(b2.T), hf)
+        out["d_yp"][lo:hi] = fp32_sum_gamma(hf + 2) * ((np.abs(qa) + sp) @ np.abs(b2))
+        c = qa @ b2
+        st_l, st_h = bf16_span(c, d_c)
+        ypo = np.asarray(fw["yp"], np.float64)[lo:hi]
+        dev[lo:hi] = np.maximum(np.abs(st_h - ypo), np.abs(ypo - st_l))
+    out["yp"] = dev
+    w = np.asarray(fw["w"], np.float64)
+    w_err = np.zeros(w.shape) if w_err is None else np.asarray(w_err, np.float64)
+    allow = np.zeros((T, h)); mag = np.zeros((T, h))
+    for j in range(k):
+        kept = dst_row[:, j] >= 0
+        r = dst_row[kept, j]
+        allow[kept] += np.abs(w[kept, j])[:, None] * dev[r] + w_err[kept, j][:, None] * (ypo_abs[r] + dev[r])
+        mag[kept] += (np.abs(w[kept, j]) + w_err[kept, j])[:, None] * (ypo_abs[r] + dev[r])
+    allow += fp32_sum_gamma(k) * mag
+    out["y"] = allow * (1.0 + 2.0 ** -8)
     return out

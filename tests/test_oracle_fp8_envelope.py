@@ -166,3 +166,98 @@ def test_envelope_is_small():
     for n, bound in (("dx", 3e-2), ("dw1", 1e-2), ("dw3", 1e-2), ("dw2", 1e-2)):
         rms = np.sqrt(np.mean(base[n] ** 2))
         assert env[n].mean() / rms < bound, n
+
+
+# ------------------------------------------------------------ forward
+
+def _fwd_case(seed, **sh):
+    wl = moe_synth.WORKLOADS["tiny"].scaled(name="fenv", dtype="fp8", **sh)
+    inp = moe_synth.gen_all(wl, seed=seed)
+    f = lambda key: to_f32(inp[key])
+    return wl, inp, f, ref.layer_forward_fp8(f("x"), f("w_gate"), inp["bias"], f("w1"), f("w3"), f("w2"), wl.k)
+
+
+def test_forward_rowq_spread_interval_brute_force():
+    """Every fp32 matrix with entries at the ends of [lo, hi] or at the value
+    itself quantizes within the spread (the scale following the amax)."""
+    rng = np.random.default_rng(5)
+    for trial in range(30):
+        vo = (rng.normal(0, 1, (2, 3)) * rng.choice([1e-3, 1.0, 30.0])).astype(np.float32)
+        d = np.abs(vo) * rng.choice([1e-7, 1e-5, 1e-3]) * (rng.random(vo.shape) < 0.6)
+        lo = (vo - d).astype(np.float32); hi = (vo + d).astype(np.float32)
+        qo, spread = ref.rowq_spread_interval(vo, lo, hi)
+        for combo in itertools.product(*[(a, b, c) for a, b, c in zip(lo.ravel(), vo.ravel(), hi.ravel())]):
+            m = np.array(combo, np.float32).reshape(vo.shape)
+            qm, sm = ref.quantize_rows(m)
+            dq = ref.e4m3_decode(qm) * sm.astype(np.float64)[:, None]
+            assert np.all(np.abs(dq - qo) <= spread * (1 + 1e-12) + 1e-300), trial
+
+
+def test_forward_envelope_contains_nearby_implementations():
+    wl, inp, f, fw = _fwd_case(3, T=263, h=256, h_ffn=128, E=9, k=5, zipf_s=1.2)
+    g_err, u_err = ref.fp8_forward_gu_bound(f("x"), fw["dst_row"], fw["offsets"], f("w1"), f("w3"))
+    w_err = ref.topk_weight_bound(fw["logits"], fw["idx"])
+    env = ref.fp8_forward_envelope(fw, f("w1"), f("w3"), f("w2"), g_err, u_err, w_err)
+    offs = fw["offsets"]
+    rms = np.sqrt(np.mean(fw["y"] ** 2))
+    worst = -np.inf
+    for trial in range(4):
+        rng = np.random.default_rng(30 + trial)
+
+        def noise(name, e, v):
+            m = rng.random(np.shape(v)) < 0.5
+            if name == "w":
+                return (v + 0.9 * w_err * rng.uniform(-1, 1, v.shape) * m).astype(np.float32)
+            lo, hi = int(offs[e]), int(offs[e + 1])
+            d = {"g": g_err, "u": u_err, "a": env["d_a"], "yp": env["d_yp"]}[name][lo:hi]
+            out = v + d * rng.uniform(-1, 1, v.shape) * m
+            return ref.round_bf16(out) if name == "yp" else out   # Yp is stored in bf16
+
+        got = ref.layer_forward_fp8(f("x"), f("w_gate"), inp["bias"], f("w1"), f("w3"), f("w2"), wl.k,
+                                    logits=fw["logits"], noise=noise)
+        worst = max(worst, float(((np.abs(got["y"] - fw["y"]) - env["y"]) / rms).max()))
+    assert worst <= 0.0, worst
+
+
+def test_forward_envelope_contains_fp32_evaluation():
+    """FC1 summed in float32 in the worst allowed order (64-product blocks,
+    then block after block) and SiLU(G) U in float32."""
+    wl, inp, f, fw = _fwd_case(4, T=200, h=512, h_ffn=128, E=4, k=2)
+    g_err, u_err = ref.fp8_forward_gu_bound(f("x"), fw["dst_row"], fw["offsets"], f("w1"), f("w3"))
+    env = ref.fp8_forward_envelope(fw, f("w1"), f("w3"), f("w2"), g_err, u_err)
+    qx, sx = ref.quantize_rows(f("x"))
+    qxp = ref.permute(qx, fw["dst_row"])
+    sxp = sx[fw["src_tok"]]
+    keep = {}
+
+    def fc1(e, wm):
+        lo, hi = int(fw["offsets"][e]), int(fw["offsets"][e + 1])
+        q, s = ref.quantize_cols(wm)
+        prod = (ref.e4m3_decode(qxp[lo:hi]).astype(np.float32)[:, None, :]
+                * ref.e4m3_decode(q).astype(np.float32).T[None, :, :])
+        blk = prod.reshape(prod.shape[0], prod.shape[1], -1, 64)
+        acc = np.add.accumulate(np.add.accumulate(blk, axis=3, dtype=np.float32)[..., -1], axis=2,
+                                dtype=np.float32)[:, :, -1]
+        return (acc * sxp[lo:hi, None].astype(np.float32)) * s.astype(np.float32)[None, :]
+
+    def fp32(name, e, v):
+        if name in ("g", "u"):
+            keep[name] = fc1(e, f("w1")[e] if name == "g" else f("w3")[e])
+            return keep[name].astype(np.float64)
+        if name == "a":
+            G, U = keep["g"], keep["u"]
+            return ((G / (np.float32(1) + np.exp(-G))) * U).astype(np.float64)
+        return v
+
+    got = ref.layer_forward_fp8(f("x"), f("w_gate"), inp["bias"], f("w1"), f("w3"), f("w2"), wl.k,
+                                logits=fw["logits"], noise=fp32)
+    rms = np.sqrt(np.mean(fw["y"] ** 2))
+    assert np.abs(got["y"] - fw["y"]).max() > 0
+    assert float(((np.abs(got["y"] - fw["y"]) - env["y"]) / rms).max()) <= 0.0
+
+
+def test_forward_envelope_is_small():
+    wl, inp, f, fw = _fwd_case(6, T=300, h=256, h_ffn=256, E=8, k=2)
+    g_err, u_err = ref.fp8_forward_gu_bound(f("x"), fw["dst_row"], fw["offsets"], f("w1"), f("w3"))
+    env = ref.fp8_forward_envelope(fw, f("w1"), f("w3"), f("w2"), g_err, u_err)
+    assert env["y"].mean() / np.sqrt(np.mean(fw["y"] ** 2)) < 2e-2
