@@ -373,7 +373,22 @@ def test_layer_forward_fp8(over, seed):
     r = ref.layer_forward_fp8(f("x"), f("w_gate"), inp["bias"], f("w1"), f("w3"), f("w2"), wl.k)
     layer, _ = _run_gpu_layer(wl, inp, logits_in=r["logits"])
     np.testing.assert_array_equal(layer.xp.cpu().numpy()[: wl.T * wl.k], ref.permute(r["qx"], r["dst_row"]))
-    check_close(host(layer.y), r["y"], 6e-2, storage_allowance(r), None, "y fp8")
+    check_fp8_forward(layer, wl, r, f)
+
+
+def check_fp8_forward(layer, wl, r, f):
+    """y of the FP8 forward against the quantization-emulating oracle: the FP8
+    bar (6e-2 * rms) once the oracle's allowance for fp32 implementations is
+    granted (A is quantized from an fp32 value, so a code or a row scale may
+    differ where that value sits at a rounding boundary; Yp stored in bf16),
+    plus half a bf16 ulp of y's own rounding; rms error below 1e-2 * rms."""
+    g_err, u_err = ref.fp8_forward_gu_bound(f("x"), r["dst_row"], r["offsets"], f("w1"), f("w3"))
+    env = ref.fp8_forward_envelope(r, f("w1"), f("w3"), f("w2"), g_err, u_err,
+                                   ref.topk_weight_bound(r["logits"], r["idx"]))
+    got = host(layer.y)
+    check_close(got, r["y"], 6e-2, env["y"] + HALF_ULP_BF16 * np.abs(r["y"]), None, "y fp8")
+    rms = np.sqrt(np.mean(r["y"] ** 2))
+    assert np.sqrt(np.mean((got - r["y"]) ** 2)) <= 1e-2 * rms
 
 
 def test_layer_deterministic():

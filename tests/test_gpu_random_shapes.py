@@ -1,0 +1,79 @@
+"""GPU parity on seeded random shapes: the layer forward and backward (BF16)
+and the FP8 forward, routing fed the oracle's fp32 logits.
+
+Shapes are drawn per seed: T from 1 to 700, h and h_ffn in {128, 256, 384}
+(one to three 128-wide blocks, so tiles end ragged in every dimension), E from
+1 to 47, k from 1 to min(E, 8), with or without a Zipf router bias (experts
+without rows appear).  The bars are those of the fixed-shape tests: routing,
+index and dispatch bit-exact; y and the gradients within 2e-2 * rms of the
+oracle with BF16 storage / operands, with the storage distance allowed against
+the exact oracle; the FP8 forward at 6e-2 * rms with the oracle's allowance
+for fp32 implementations (`check_fp8_forward`); experts without rows get zero
+weight gradients.
+"""
+import numpy as np
+import pytest
+import torch
+
+import moe_synth
+from moe_synth import to_f32
+from oracle import moe_ref as ref
+
+from test_gpu_parity import (HALF_ULP_BF16, _run_gpu_layer, check_close, check_fp8_forward, host, say,
+                             storage_allowance)
+from test_gpu_backward import _gpu_fwd_bwd
+
+pytestmark = pytest.mark.gpu
+
+
+def _shape(seed):
+    rng = np.random.default_rng(1000 + seed)
+    E = int(rng.integers(1, 48))
+    return dict(T=int(rng.integers(1, 701)), h=int(rng.choice([128, 256, 384])),
+                h_ffn=int(rng.choice([128, 256, 384])), E=E, k=int(rng.integers(1, min(E, 8) + 1)),
+                zipf_s=float(rng.choice([0.0, 1.2])))
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_shape_forward_backward(seed):
+    over = _shape(seed)
+    wl = moe_synth.WORKLOADS["dsmoe"].scaled(name=f"rand{seed}", **over)
+    say(f"random shape {seed}: {wl}")
+    inp = moe_synth.gen_all(wl, seed=seed)
+    f = lambda k: to_f32(inp[k])
+    fw = ref.layer_forward(f("x"), f("w_gate"), inp["bias"], f("w1"), f("w3"), f("w2"), wl.k)
+    layer = _gpu_fwd_bwd(wl, inp, fw["logits"])
+    np.testing.assert_array_equal(layer.topk_idx.cpu().numpy(), fw["idx"])
+    np.testing.assert_array_equal(layer.counts.cpu().numpy(), fw["counts"])
+    np.testing.assert_array_equal(layer.offsets.cpu().numpy(), fw["offsets"])
+    np.testing.assert_array_equal(layer.dst_row.cpu().numpy(), fw["dst_row"])
+    check_close(host(layer.y), fw["y"], 2e-2, storage_allowance(fw, True, True), None, "y")
+    args = (f("dy"), f("x"), fw["w"], fw["dst_row"], fw["offsets"], f("w1"), f("w3"), f("w2"))
+    bw = ref.layer_backward(*args)
+    emu = ref.layer_backward(*args, bf16_operands=True)
+    got = {"dx": host(layer.dx), "dw1": layer.dw1.cpu().numpy(), "dw3": layer.dw3.cpu().numpy(),
+           "dw2": layer.dw2.cpu().numpy()}
+    for name in ("dx", "dw1", "dw3", "dw2"):
+        if not np.any(emu[name]):
+            assert not np.any(got[name]), name
+            continue
+        out_round = HALF_ULP_BF16 * np.abs(emu[name]) if name == "dx" else None
+        check_close(got[name], emu[name], 2e-2, out_round, None, name + " vs bf16-operand oracle")
+        dist = np.abs(emu[name] - bw[name]) + (0 if out_round is None else out_round)
+        check_close(got[name], bw[name], 2e-2, dist, None, name + " vs exact oracle")
+    for e in np.nonzero(fw["counts"] == 0)[0]:
+        assert not layer.dw1[e].any() and not layer.dw3[e].any() and not layer.dw2[e].any()
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_random_shape_forward_fp8(seed):
+    over = _shape(20 + seed)
+    wl = moe_synth.WORKLOADS["tiny"].scaled(name=f"rand_fp8_{seed}", dtype="fp8", **over)
+    say(f"random shape fp8 {seed}: {wl}")
+    inp = moe_synth.gen_all(wl, seed=seed)
+    f = lambda k: to_f32(inp[k])
+    r = ref.layer_forward_fp8(f("x"), f("w_gate"), inp["bias"], f("w1"), f("w3"), f("w2"), wl.k)
+    layer, _ = _run_gpu_layer(wl, inp, logits_in=r["logits"])
+    np.testing.assert_array_equal(layer.topk_idx.cpu().numpy(), r["idx"])
+    np.testing.assert_array_equal(layer.xp.cpu().numpy()[: wl.T * wl.k], ref.permute(r["qx"], r["dst_row"]))
+    check_fp8_forward(layer, wl, r, f)
