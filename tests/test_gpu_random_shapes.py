@@ -1,5 +1,6 @@
-"""GPU parity on seeded random shapes: the layer forward and backward (BF16)
-and the FP8 forward, routing fed the oracle's fp32 logits.
+"""GPU parity on seeded random shapes: the layer forward and backward (BF16),
+the FP8 forward, the FP8 backward and the router backward, routing fed the
+oracle's fp32 logits.
 
 Shapes are drawn per seed: T from 1 to 700, h and h_ffn in {128, 256, 384}
 (one to three 128-wide blocks, so tiles end ragged in every dimension), E from
@@ -8,8 +9,9 @@ without rows appear).  The bars are those of the fixed-shape tests: routing,
 index and dispatch bit-exact; y and the gradients within 2e-2 * rms of the
 oracle with BF16 storage / operands, with the storage distance allowed against
 the exact oracle; the FP8 forward at 6e-2 * rms with the oracle's allowance
-for fp32 implementations (`check_fp8_forward`); experts without rows get zero
-weight gradients.
+for fp32 implementations (`check_fp8_forward`), the FP8 backward likewise
+against its allowance; the router backward within 1e-4 * rms; experts without
+rows get zero weight gradients.
 """
 import numpy as np
 import pytest
@@ -77,3 +79,23 @@ def test_random_shape_forward_fp8(seed):
     np.testing.assert_array_equal(layer.topk_idx.cpu().numpy(), r["idx"])
     np.testing.assert_array_equal(layer.xp.cpu().numpy()[: wl.T * wl.k], ref.permute(r["qx"], r["dst_row"]))
     check_fp8_forward(layer, wl, r, f)
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_random_shape_fp8_backward(seed):
+    """FP8 backward on shared G|U and gate weights (the unit form of the FP8
+    backward test, with the oracle's allowance)."""
+    from test_gpu_backward_fp8 import _check, _run
+    over = _shape(40 + seed)
+    over.pop("zipf_s")
+    _check(*_run(f"rand_bwd_fp8_{seed}", over, seed, True))
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_random_shape_router_backward(seed):
+    """Router backward on inputs the oracle receives exactly (the unit form
+    of the router backward test), BF16 storage, balance-loss weight 0.03."""
+    from test_gpu_router_bwd import test_router_bwd_unit
+    sh = _shape(60 + seed)
+    test_router_bwd_unit(f"rand_router_{seed}", dict(T=sh["T"], h=sh["h"], E=sh["E"], k=sh["k"]), 0.03,
+                         "bf16", 70 + seed)
