@@ -8,35 +8,38 @@
 // Weight gradients accumulate and are written in FP32 (review §三 parameter
 // update: FP32 gradient accumulation).
 //
-// Every product runs on the same NT engine (both operands K-contiguous):
+// Every product runs on the same engine:
 //   dA   = dYp W2^T            SchedM, B = W2 as [hf][h]  -> dG, dU, A (epilogue)
 //   dXp  = [dG|dU] W13^T       SchedM, B = W13 as [h][2hf packed]
-//   dW2  = A^T dYp             SchedK over transposed, zero-padded copies
-//   dW13 = Xp^T [dG|dU]        SchedK, epilogue splits dW1 / dW3
-// The weight-gradient products contract over each expert's rows, so their
-// operands are first transposed per expert into [C][K_e] blocks with K_e the
-// row count rounded up to 64 (zeros beyond it).
+//   dW2  = A^T dYp             SchedKR (BF16) / SchedK (FP8)
+//   dW13 = Xp^T [dG|dU]        the same; the epilogue splits dW1 / dW3
+// The weight-gradient products contract over each expert's rows.  In BF16
+// they read the row-major routed arrays directly (the LDS transpose read
+// turns the M-major slabs into MFMA fragments).  In FP8 the operands are
+// quantized per channel over the expert's rows, so they are first transposed
+// per expert into [C][K_e] code blocks with K_e the row count rounded up to
+// 128 (zeros beyond it), the quantization done in the same pass.
 #include "gemm_engine.h"
 
 namespace moe {
 
-// Per-expert transpose with zero padding: src [rows][C] (expert-contiguous
-// rows, C a multiple of 64) -> dst, expert e at element kpre[e]*C laid out
-// [C][Kp_e] with Kp_e = roundup(M_e, pad) (pad a multiple of 64: one 128-byte
-// K slab of the GEMM's element type) and zeros beyond M_e.
+// Per-expert quantizing transpose with zero padding: src [rows][C] bf16
+// (expert-contiguous rows, C a multiple of 64) -> dst E4M3 codes, expert e at
+// element kpre[e]*C laid out [C][Kp_e] with Kp_e = roundup(M_e, pad) (pad a
+// multiple of 64: one 128-byte K slab of the GEMM's element type) and zeros
+// beyond M_e.
 //
 // One workgroup per (64 columns, expert) walks the expert's rows in blocks of
 // 64: each thread loads 16 bytes of two adjacent rows (eight threads cover a
 // 128-byte row segment), packs the two rows' values of each column into one
 // 32-bit word in LDS (column-major, 33 words per column: conflict-free
 // stores), then reads 8 words = 16 consecutive rows of one column and stores
-// them contiguously.  The next block's loads are issued before this block's
-// LDS work.
+// their codes contiguously.  The next block's loads are issued before this
+// block's LDS work.
 //
-// kQ: E4M3 codes instead of bf16, quantized per channel over the expert's
-// rows (scale[e][c] = amax / 448, 1 for a zero channel or an expert without
-// rows); a first pass over the same rows takes the column amax.
-template <bool kQ>
+// Codes are quantized per channel over the expert's rows (scale[e][c] =
+// amax / 448, 1 for a zero channel or an expert without rows); a first pass
+// over the same rows takes the column amax.
 __global__ void __launch_bounds__(256) xpose_kernel(const uint16_t* __restrict__ src, int C,
                                                     const int32_t* __restrict__ offsets, int E,
                                                     int rows, int pad, void* __restrict__ dst,
@@ -67,7 +70,7 @@ __global__ void __launch_bounds__(256) xpose_kernel(const uint16_t* __restrict__
   const int e = blockIdx.y, c0 = blockIdx.x * 64;
   const int r0 = offs[e], m = offs[e + 1] - r0, kp = kpre[e + 1] - kpre[e];
   if (kp == 0) {
-    if (kQ && tid < 64 && c0 + tid < C) scale[size_t(e) * C + c0 + tid] = 1.0f;
+    if (tid < 64 && c0 + tid < C) scale[size_t(e) * C + c0 + tid] = 1.0f;
     return;
   }
   const int q = tid & 7, p = tid >> 3;  // 8-column chunk, row pair
@@ -77,7 +80,7 @@ __global__ void __launch_bounds__(256) xpose_kernel(const uint16_t* __restrict__
     if (r < m) v = *reinterpret_cast<const u32x4*>(sp + size_t(r) * C);
     return v;
   };
-  if (kQ) {
+  {
     float am[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) am[j] = 0.f;
@@ -104,7 +107,7 @@ __global__ void __launch_bounds__(256) xpose_kernel(const uint16_t* __restrict__
   }
   const int c = tid >> 2, kk = (tid & 3) * 16;  // output column, first of its 16 rows
   const size_t obase = size_t(kpre[e]) * C + size_t(c0 + c) * kp + kk;
-  const float sc = kQ ? cscale[c] : 1.0f;
+  const float sc = cscale[c];
   u32x4 va = ld(2 * p), vb = ld(2 * p + 1);
   for (int k0 = 0; k0 < kp; k0 += 64) {
     const u32x4 na = ld(k0 + 64 + 2 * p), nb = ld(k0 + 65 + 2 * p);
@@ -118,18 +121,12 @@ __global__ void __launch_bounds__(256) xpose_kernel(const uint16_t* __restrict__
 #pragma unroll
     for (int i = 0; i < 8; ++i) w[i] = tile[c * 33 + (kk >> 1) + i];
     if (c0 + c < C) {
-      if (!kQ) {
-        u32x4* d = reinterpret_cast<u32x4*>(static_cast<uint16_t*>(dst) + obase + k0);
-        d[0] = u32x4{w[0], w[1], w[2], w[3]};
-        d[1] = u32x4{w[4], w[5], w[6], w[7]};
-      } else {
-        u32x4 o;
+      u32x4 o;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          o[i] = e4m3x4(bf16_lo(w[2 * i]) / sc, bf16_hi(w[2 * i]) / sc, bf16_lo(w[2 * i + 1]) / sc,
-                        bf16_hi(w[2 * i + 1]) / sc);
-        *reinterpret_cast<u32x4*>(static_cast<uint8_t*>(dst) + obase + k0) = o;
-      }
+      for (int i = 0; i < 4; ++i)
+        o[i] = e4m3x4(bf16_lo(w[2 * i]) / sc, bf16_hi(w[2 * i]) / sc, bf16_lo(w[2 * i + 1]) / sc,
+                      bf16_hi(w[2 * i + 1]) / sc);
+      *reinterpret_cast<u32x4*>(static_cast<uint8_t*>(dst) + obase + k0) = o;
     }
     __syncthreads();
     va = na;
@@ -159,27 +156,18 @@ using CfgDA = GemmCfg<2, 4, 4, 2, 1, 128, 2>;
 static size_t al256(size_t x) { return (x + 255) & ~size_t(255); }
 
 // Upper bound of the padded K extent: sum_e roundup(M_e, pad) <= rows + (pad-1) E.
-static size_t kpad_upper(int rows, int E, int pad = kpad_elems<MOE_BF16>()) {
+static size_t kpad_upper(int rows, int E, int pad) {
   return size_t(rows) + size_t(pad - 1) * E;
 }
 
 size_t grouped_bwd_ws_bytes(int rows, int h, int h_ffn, int E, int dtype) {
   (void)dtype;
-  const size_t r = size_t(rows), hh = size_t(h), hf = size_t(h_ffn), kp = kpad_upper(rows, E);
+  (void)h;
+  (void)E;
+  const size_t r = size_t(rows), hf = size_t(h_ffn);
   return al256(r * 2 * hf * 2)          // dG|dU, packed like G|U
          + al256(r * hf * 2)            // A recomputed
-         + 2 * al256(hh * kp * 2)       // Xp^T, dYp^T
-         + al256(hf * kp * 2)           // A^T
-         + al256(2 * hf * kp * 2)       // (dG|dU)^T
          + splitk_ws_bytes<CfgB>();   // split-K partial tiles
-}
-
-static int xpose(const void* src, int C, const int32_t* offsets, int E, int rows, void* dst,
-                 hipStream_t s, int pad = kpad_elems<MOE_BF16>()) {
-  if (C % 64 != 0) return MOE_ERR_SHAPE;
-  hipLaunchKernelGGL(xpose_kernel<false>, dim3(C / 64, E), dim3(256), 0, s, (const uint16_t*)src, C,
-                     offsets, E, rows, pad, dst, nullptr);
-  return launch_status();
 }
 
 int grouped_bwd(const void* dyp, const void* xp, const void* h13_save, const moe_weights* W,
@@ -187,26 +175,13 @@ int grouped_bwd(const void* dyp, const void* xp, const void* h13_save, const moe
                 void* ws, hipStream_t s) {
   const int h = W->h, hf = W->h_ffn, E = W->E;
   unsigned char* w = static_cast<unsigned char*>(ws);
-  const size_t r = size_t(rows), kp = kpad_upper(rows, E);
+  const size_t r = size_t(rows);
   void* dgu = w;
   w += al256(r * 2 * hf * 2);
   void* act = w;
   w += al256(r * hf * 2);
-  void* xpT = w;
-  w += al256(size_t(h) * kp * 2);
-  void* dypT = w;
-  w += al256(size_t(h) * kp * 2);
-  void* actT = w;
-  w += al256(size_t(hf) * kp * 2);
-  void* dguT = w;
-  w += al256(2 * size_t(hf) * kp * 2);
   void* split_ws = w;
   int rc;
-
-  timer_begin(kTXpose, s);
-  if ((rc = xpose(xp, h, offsets, E, rows, xpT, s))) return rc;
-  if ((rc = xpose(dyp, h, offsets, E, rows, dypT, s))) return rc;
-  timer_end(kTXpose, s);
 
   // dA = dYp W2^T, with dG, dU and A formed in the epilogue
   GemmArgs ga{dyp, nullptr, W->w2_bwd, nullptr, offsets, E, h, hf, rows, 0,
@@ -215,16 +190,12 @@ int grouped_bwd(const void* dyp, const void* xp, const void* h13_save, const moe
   if ((rc = launch_gemm<CfgDA, MOE_BF16, kModeBwdDA, kSchedM>(ga, kTBwd1, s)))
     return rc;
 
-  timer_begin(kTXpose, s);
-  if ((rc = xpose(act, hf, offsets, E, rows, actT, s))) return rc;
-  if ((rc = xpose(dgu, 2 * hf, offsets, E, rows, dguT, s))) return rc;
-  timer_end(kTXpose, s);
-
-  // dW2 = A^T dYp  (per expert [hf][h], fp32)
-  GemmArgs g2{actT, nullptr, dypT, nullptr, offsets, E, 0, h, rows, hf,
+  // dW2 = A^T dYp  (per expert [hf][h], fp32), K = the expert's rows of the
+  // row-major A and dYp
+  GemmArgs g2{act, nullptr, dyp, nullptr, offsets, E, 0, h, rows, hf,
               dw2, nullptr, nullptr, nullptr, nullptr, nullptr};
   splitk_ws_set<CfgB>(g2, split_ws);
-  if ((rc = launch_gemm<CfgB, MOE_BF16, kModeDW, kSchedK>(g2, kTBwd2, s)))
+  if ((rc = launch_gemm<CfgB, MOE_BF16, kModeDW, kSchedKR>(g2, kTBwd2, s)))
     return rc;
 
   // dXp = [dG|dU] W13^T
@@ -234,11 +205,12 @@ int grouped_bwd(const void* dyp, const void* xp, const void* h13_save, const moe
   if ((rc = launch_gemm<CfgB, MOE_BF16, kModeFC2, kSchedM>(g3, kTBwd3, s)))
     return rc;
 
-  // dW1 | dW3 = Xp^T [dG|dU]  (per expert [h][hf] each, fp32)
-  GemmArgs g4{xpT, nullptr, dguT, nullptr, offsets, E, 0, 2 * hf, rows, h,
+  // dW1 | dW3 = Xp^T [dG|dU]  (per expert [h][hf] each, fp32), row-major
+  // operands as for dW2
+  GemmArgs g4{xp, nullptr, dgu, nullptr, offsets, E, 0, 2 * hf, rows, h,
               dw1, dw3, nullptr, nullptr, nullptr, nullptr};
   splitk_ws_set<CfgB>(g4, split_ws);
-  return launch_gemm<CfgB, MOE_BF16, kModeDW13, kSchedK>(g4, kTBwd4, s);
+  return launch_gemm<CfgB, MOE_BF16, kModeDW13, kSchedKR>(g4, kTBwd4, s);
 }
 
 }  // namespace moe_launch
@@ -267,7 +239,7 @@ size_t grouped_bwd_fp8_ws_bytes(int rows, int h, int h_ffn, int E) {
 static int xpose_q(const void* src, int C, const int32_t* offsets, int E, int rows, void* dst,
                    float* scale, hipStream_t s) {
   if (C % 64 != 0) return MOE_ERR_SHAPE;
-  hipLaunchKernelGGL(xpose_kernel<true>, dim3(C / 64, E), dim3(256), 0, s, (const uint16_t*)src, C,
+  hipLaunchKernelGGL(xpose_kernel, dim3(C / 64, E), dim3(256), 0, s, (const uint16_t*)src, C,
                      offsets, E, rows, kpad_elems<MOE_FP8_E4M3>(), dst, scale);
   return launch_status();
 }

@@ -7,7 +7,12 @@
 //             expert, offsets on device), K fixed: the forward FC1/FC2 and the
 //             backward dA / dXp products;
 //   SchedK -- every expert has a fixed M x N output and a ragged K = its row
-//             count (padded to a 64 multiple with zeros): the weight gradients.
+//             count (padded to a 64 multiple with zeros): the FP8 weight
+//             gradients, on transposed operands;
+//   SchedKR -- the same products read straight from the row-major routed
+//             arrays ([rows][M] and [rows][N], K = the expert's rows): K slabs
+//             of 64 rows land in LDS M-major and the fragments come out
+//             through the LDS transpose read (BF16 weight gradients).
 // Tile 256 x 256, four waves of 128 x 128; operands go global -> LDS with
 // buffer_load ... lds into two XOR-swizzled stages of 128-byte rows.
 #pragma once
@@ -58,7 +63,7 @@ struct CfgFor<MOE_FP8_E4M3> {
   using type = GemmCfg<2, 4, 4, 2, 1, 128, 2>;
 };
 
-enum { kSchedM = 0, kSchedK = 1 };
+enum { kSchedM = 0, kSchedK = 1, kSchedKR = 2 };
 enum {
   kModeFC1 = 0,   // SiLU(G)*U epilogue (+ optional G|U keep, FP8 row amax)
   kModeFC2 = 1,   // plain output [rows][N] (bf16 / fp32; FP8 rescale)
@@ -68,12 +73,14 @@ enum {
 };
 
 struct GemmArgs {
-  const void* A;          // SchedM: [rows][K]; SchedK: expert e at kpre[e]*M elements, [M][K_e]
+  const void* A;          // SchedM: [rows][K]; SchedK: expert e at kpre[e]*M elements, [M][K_e];
+                          // SchedKR: [rows][M]
   const float* a_scale;   // FP8: SchedM [rows]; SchedK [E][M]
-  const void* B;          // SchedM: [E][N][K]; SchedK: expert e at kpre[e]*N elements, [N][K_e]
+  const void* B;          // SchedM: [E][N][K]; SchedK: expert e at kpre[e]*N elements, [N][K_e];
+                          // SchedKR: [rows][N]
   const float* b_scale;   // FP8: [E][N]
   const int32_t* offsets; // [E+1]
-  int E, K, N, rows, M;   // K: SchedM only; M: SchedK only
+  int E, K, N, rows, M;   // K: SchedM only; M: SchedK / SchedKR only
   void* out;              // see the modes
   void* out2;             // BwdDA: A [rows][N]; DW13: dW3
   void* save;             // FC1: G|U out [rows][N] bf16 or null; BwdDA: G|U in [rows][2N]
@@ -154,6 +161,7 @@ struct Tile {
   int e, row0, row_end, n0, nk, rowB;
   int kb;     // first K slab of this work item
   int split;  // -1: whole tile; else the split index (last round only)
+  int kr;     // SchedKR: the expert's rows (K extent)
   size_t a_off, a_bytes, b_off, b_bytes;
 };
 
@@ -206,6 +214,69 @@ __device__ __forceinline__ void issue_slab(unsigned char* lds, int st, __amdgpu_
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr_t*)(B + i * 1024), 16, v, 0, 0, 0);
     }
   }
+}
+
+// SchedKR stage layout: each operand's part holds the slab's 64 K rows, row
+// k at k * 512 bytes (256 M- or N-columns of bf16).  The 16-byte chunk c of
+// row k sits at chunk c ^ kr_swz(k % 4): a transpose read takes four rows of
+// one 32-byte column pair per 16 lanes (and two neighbouring pairs per 32
+// lanes), and the XOR puts those four rows at distinct 128-byte and 256-byte
+// bank positions.
+__device__ __forceinline__ int kr_swz(int k4) { return (0xCA60 >> (4 * k4)) & 15; }
+
+// Loader offsets of one lane for a global row pitch: a 1 KB wave load fills
+// two K rows (lane l: row l / 32, chunk position l % 32); e / o for a row
+// pair of even / odd index (rows 4i, 4i+1 / 4i+2, 4i+3).
+__device__ __forceinline__ LoadOff load_off_kr(int pitch, int lane) {
+  const int r = lane >> 5, p = lane & 31;
+  return LoadOff{r * pitch + ((p ^ kr_swz(r)) << 4), r * pitch + ((p ^ kr_swz(r + 2)) << 4)};
+}
+
+// One 64-row K slab of A and B into LDS stage `st` (SchedKR): wave w fills
+// K-row pairs w*GA .. w*GA+GA-1 of A and w*GB .. of B.  The descriptors cover
+// this slab's rows only, starting at the tile's first column.
+template <class C>
+__device__ __forceinline__ void issue_slab_kr(unsigned char* lds, int st, __amdgpu_buffer_rsrc_t ra,
+                                              __amdgpu_buffer_rsrc_t rb, int wave, LoadOff la,
+                                              LoadOff lb, int pa, int pb) {
+  unsigned char* A = lds + st * C::kStage + wave * C::kGA * 1024;
+  unsigned char* B = lds + st * C::kStage + C::kAStage + wave * C::kGB * 1024;
+  const int ga0 = wave * C::kGA, gb0 = wave * C::kGB;
+#pragma unroll
+  for (int i = 0; i < (C::kGA > C::kGB ? C::kGA : C::kGB); ++i) {
+    if (i < C::kGA) {
+      const int q = ga0 + i;
+      const int v = ((q & 1) ? la.o : la.e) + 2 * q * pa;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t*)(A + i * 1024), 16, v, 0, 0, 0);
+    }
+    if (i < C::kGB) {
+      const int q = gb0 + i;
+      const int v = ((q & 1) ? lb.o : lb.e) + 2 * q * pb;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr_t*)(B + i * 1024), 16, v, 0, 0, 0);
+    }
+  }
+}
+
+// SchedKR fragment of substep s: lane l needs columns (m) mb + l % 32 and K
+// values 16 s + 8 (l / 32) + 0..7.  A transpose read hands 16 lanes a 4 x 16
+// block: the lanes 4j .. 4j+3 of a 16-lane group address four consecutive
+// columns of K row j, and lane i of the group receives column i of the four
+// rows.  Two reads give K + 0..3 and K + 4..7.  `off` is the lane's byte
+// offset inside the part for its column block (kr_lane_off), K row 0.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+__device__ __forceinline__ int kr_lane_off(int mb, int lane) {
+  const int sp = lane & 15, k4 = sp >> 2;
+  const int col = mb + ((lane >> 4) & 1) * 16 + 4 * (sp & 3);
+  return (8 * (lane >> 5) + k4) * 512 + (((col >> 3) ^ kr_swz(k4)) << 4) + (col & 7) * 2;
+}
+__device__ __forceinline__ void load_tr_frag(Frag<MOE_BF16>& f, const unsigned char* part, int off,
+                                             int s) {
+  const unsigned char* p = part + off + s * 16 * 512;
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(lds_ptr_t*)p);
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(lds_ptr_t*)(p + 4 * 512));
+  const u32x2 a = __builtin_bit_cast(u32x2, lo), b = __builtin_bit_cast(u32x2, hi);
+  f.v = u32x4{a[0], a[1], b[0], b[1]};
 }
 
 // Fragments of substep s of one LDS stage (MI A and NJ B fragments per wave).
@@ -524,7 +595,7 @@ __global__ void __launch_bounds__(C::kThreads, C::kWavesPerSimd) grouped_gemm_ke
   constexpr int RB = C::kRowB, NS = C::kStages, D = NS - 1;  // D slabs in flight ahead
   extern __shared__ __align__(16) unsigned char lds[];
   __shared__ int tpre[MOE_MAX_EXPERTS + 1];  // tiles before expert e
-  __shared__ int offs[MOE_MAX_EXPERTS + 1];  // SchedM: row offsets; SchedK: padded K prefix
+  __shared__ int offs[MOE_MAX_EXPERTS + 1];  // SchedM / KR: row offsets; SchedK: padded K prefix
   __shared__ int split_flag;
   constexpr int EB = Elem<DT>::bytes;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -532,7 +603,9 @@ __global__ void __launch_bounds__(C::kThreads, C::kWavesPerSimd) grouped_gemm_ke
   const int wm = wave / C::kWN, wn = wave % C::kWN;
   const int half = lane >> 5, l32 = lane & 31;
   const int NT = ceil_div(g.N, BN);
-  const int MT = SCHED == kSchedK ? ceil_div(g.M, BM) : 0;
+  const int MT = SCHED != kSchedM ? ceil_div(g.M, BM) : 0;
+  static_assert(SCHED != kSchedKR || (DT == MOE_BF16 && RB == 128 && BM == 256 && BN == 256),
+                "SchedKR: bf16, 64-row slabs of 512-byte LDS rows");
 
   for (int e = tid; e <= g.E; e += C::kThreads) {
     int o = g.offsets[e];
@@ -548,6 +621,9 @@ __global__ void __launch_bounds__(C::kThreads, C::kWavesPerSimd) grouped_gemm_ke
       if (SCHED == kSchedM) {
         offs[e + 1] = hi;
         run += ceil_div(hi - lo, BM) * NT;
+      } else if (SCHED == kSchedKR) {
+        offs[e + 1] = hi;
+        run += MT * NT;
       } else {
         offs[e] = kp;  // becomes the padded K prefix
         kp += ceil_div(hi - lo, kpad_elems<DT>()) * kpad_elems<DT>();
@@ -590,6 +666,7 @@ __global__ void __launch_bounds__(C::kThreads, C::kWavesPerSimd) grouped_gemm_ke
     }
     Tile T;
     T.e = lo;
+    T.kr = 0;
     const int local = tt - sld(tpre + lo);
     const int o0 = sld(offs + lo), o1 = sld(offs + lo + 1);
     if (SCHED == kSchedM) {
@@ -603,6 +680,21 @@ __global__ void __launch_bounds__(C::kThreads, C::kWavesPerSimd) grouped_gemm_ke
       T.a_off = size_t(T.row0) * T.rowB;
       T.a_bytes = size_t(g.rows - T.row0) * T.rowB;
       T.b_off = (size_t(lo) * g.N + T.n0) * T.rowB;
+    } else if (SCHED == kSchedKR) {
+      // m-tiles fastest: consecutive tiles share the expert's B columns
+      const int nt = local / MT, mt = local - nt * MT;
+      T.row0 = mt * BM;
+      T.row_end = g.M;
+      T.n0 = nt * BN;
+      T.rowB = 0;
+      T.kr = o1 - o0;
+      T.a_off = size_t(o0) * g.M * 2 + size_t(T.row0) * 2;
+      T.b_off = size_t(o0) * g.N * 2 + size_t(T.n0) * 2;
+      T.a_bytes = T.b_bytes = 0;
+      T.nk = ceil_div(T.kr, 64);
+      T.kb = 0;
+      T.split = -1;
+      return T;
     } else {
       const int nt = local / MT, mt = local - nt * MT;
       const int k0 = o0, ke = o1 - o0;
@@ -633,12 +725,30 @@ __global__ void __launch_bounds__(C::kThreads, C::kWavesPerSimd) grouped_gemm_ke
 
   constexpr int S = RB / Frag<DT>::kKBytes;             // substeps per slab
   static_assert(S >= 2 && S % 2 == 0, "fragment double buffer needs an even substep count");
-  constexpr int NR = (MI + NJ) * Frag<DT>::kReads;      // LDS reads per substep
+  constexpr int NR = (MI + NJ) * (SCHED == kSchedKR ? 2 : Frag<DT>::kReads);  // LDS reads per substep
   constexpr int NM = MI * NJ * Frag<DT>::kMfma;         // MFMAs per substep
   constexpr int NV = C::kGA + C::kGB;                   // global loads per slab per wave
   constexpr bool kSingle = Frag<DT>::kReads == 2;       // fp8: single-buffered fragments
   // fragment rows inside a stage
   const int arow = wm * (MI * 32) + l32, brow = wn * (NJ * 32) + l32;
+  // SchedKR: the lane's transpose-read offsets of its column blocks
+  int kra[SCHED == kSchedKR ? MI : 1], krb[SCHED == kSchedKR ? NJ : 1];
+  if (SCHED == kSchedKR) {
+#pragma unroll
+    for (int i = 0; i < MI; ++i) kra[i] = kr_lane_off(wm * (MI * 32) + i * 32, lane);
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) krb[j] = kr_lane_off(wn * (NJ * 32) + j * 32, lane);
+  }
+  auto frags = [&](Frag<DT>(&fa)[MI], Frag<DT>(&fb)[NJ], const unsigned char* st, int s) {
+    if constexpr (SCHED == kSchedKR) {
+#pragma unroll
+      for (int i = 0; i < MI; ++i) load_tr_frag(fa[i], st, kra[i], s);
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) load_tr_frag(fb[j], st + C::kAStage, krb[j], s);
+    } else {
+      load_frags<C, DT>(fa, fb, st, arow, brow, s, half);
+    }
+  };
 
   // The slabs of this workgroup's work items form one stream; slab c of the
   // stream sits in stage c % NS.  The loader walks the same items as the
@@ -653,9 +763,23 @@ __global__ void __launch_bounds__(C::kThreads, C::kWavesPerSimd) grouped_gemm_ke
   }
   __amdgpu_buffer_rsrc_t lra = rsrc(g.A, lt.a_off, lt.a_bytes), lrb = rsrc(g.B, lt.b_off, lt.b_bytes);
   LoadOff llo = load_off<RB>(lt.rowB, lane);
+  // SchedKR: row pitches of A and B, the lanes' loader offsets
+  const int pa = g.M * 2, pb = g.N * 2;
+  const LoadOff kla = load_off_kr(pa, lane), klb = load_off_kr(pb, lane);
   auto issue = [&]() {
     if (ldone) return;
-    issue_slab<C>(lds, issued % NS, lra, lrb, wave, llo, lt.rowB, (lt.kb + lk) * RB);
+    if (SCHED == kSchedKR) {
+      // descriptors of this slab's rows: rows past the expert's end, and
+      // columns past the last row's end, read as zeros
+      const int k0 = (lt.kb + lk) * 64, nr = lt.kr - k0 < 64 ? lt.kr - k0 : 64;
+      const __amdgpu_buffer_rsrc_t ra =
+          rsrc(g.A, lt.a_off + size_t(k0) * pa, size_t(nr) * pa - size_t(lt.row0) * 2);
+      const __amdgpu_buffer_rsrc_t rb =
+          rsrc(g.B, lt.b_off + size_t(k0) * pb, size_t(nr) * pb - size_t(lt.n0) * 2);
+      issue_slab_kr<C>(lds, issued % NS, ra, rb, wave, kla, klb, pa, pb);
+    } else {
+      issue_slab<C>(lds, issued % NS, lra, lrb, wave, llo, lt.rowB, (lt.kb + lk) * RB);
+    }
     ++issued;
     if (++lk < lt.nk) return;
     lk = 0;
@@ -664,9 +788,11 @@ __global__ void __launch_bounds__(C::kThreads, C::kWavesPerSimd) grouped_gemm_ke
       if (lw >= work) { ldone = true; return; }
       lt = item_of(lw);
     } while (lt.nk == 0);
-    lra = rsrc(g.A, lt.a_off, lt.a_bytes);
-    lrb = rsrc(g.B, lt.b_off, lt.b_bytes);
-    llo = load_off<RB>(lt.rowB, lane);
+    if (SCHED != kSchedKR) {
+      lra = rsrc(g.A, lt.a_off, lt.a_bytes);
+      lrb = rsrc(g.B, lt.b_off, lt.b_bytes);
+      llo = load_off<RB>(lt.rowB, lane);
+    }
   };
   // wait until slab c has landed: n = slabs issued after it (in flight)
   auto wait_slab = [&](int c) {
@@ -680,7 +806,7 @@ __global__ void __launch_bounds__(C::kThreads, C::kWavesPerSimd) grouped_gemm_ke
   wait_slab(0);
   __syncthreads();
   Frag<DT> fa[2][MI], fb[2][NJ];
-  if (issued > 0) load_frags<C, DT>(fa[0], fb[0], lds, arow, brow, 0, half);
+  if (issued > 0) frags(fa[0], fb[0], lds, 0);
 
   int c = 0;             // stream slab the MFMAs consume next
   bool drain = false;    // an epilogue's stores may be outstanding
@@ -722,23 +848,26 @@ __global__ void __launch_bounds__(C::kThreads, C::kWavesPerSimd) grouped_gemm_ke
       }
 #pragma unroll
       for (int s = 0; s + 1 < S; ++s) {
-        load_frags<C, DT>(fa[(s + 1) & 1], fb[(s + 1) & 1], As, arow, brow, s + 1, half);
+        frags(fa[(s + 1) & 1], fb[(s + 1) & 1], As, s + 1);
         mma_all<C, DT>(acc, fa[s & 1], fb[s & 1]);
       }
-      // interleave: one LDS read (and one global load early on) per MFMA
+      // interleave: the substep's LDS reads spread over its MFMAs (and one
+      // global load per MFMA early on)
 #pragma unroll
       for (int s = 0; s + 1 < S; ++s)
 #pragma unroll
         for (int q = 0; q < NM; ++q) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          if (q < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          constexpr int rq = NR / NM;
+          if (rq > 0) __builtin_amdgcn_sched_group_barrier(0x100, rq, 0);
+          if (q < NR % NM) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
           if (s == 0 && q < NV) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
         }
       wait_slab(c + 1);  // this stage read out; slab c+1 landed
       __syncthreads();
       // next slab's first fragments load while the last substep multiplies
       if (c + 1 < issued)
-        load_frags<C, DT>(fa[0], fb[0], lds + ((c + 1) % NS) * C::kStage, arow, brow, 0, half);
+        frags(fa[0], fb[0], lds + ((c + 1) % NS) * C::kStage, 0);
       mma_all<C, DT>(acc, fa[1], fb[1]);
       __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);
       __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);
