@@ -34,8 +34,8 @@ namespace moe {
 // 128-byte row segment), packs the two rows' values of each column into one
 // 32-bit word in LDS (column-major, 33 words per column: conflict-free
 // stores), then reads 8 words = 16 consecutive rows of one column and stores
-// their codes contiguously.  The next block's loads are issued before this
-// block's LDS work.
+// their codes contiguously.  The loads of the next two blocks are in flight
+// during this block's LDS work.
 //
 // Codes are quantized per channel over the expert's rows (scale[e][c] =
 // amax / 448, 1 for a zero channel or an expert without rows); a first pass
@@ -84,13 +84,18 @@ __global__ void __launch_bounds__(256) xpose_kernel(const uint16_t* __restrict__
     float am[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) am[j] = 0.f;
-    for (int r = p; r < m; r += 32) {
-      const u32x4 v = ld(r);
+    // four rows per thread in flight (rows past the expert read as zeros)
+    for (int r = p; r < m; r += 128) {
+      u32x4 v[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        am[2 * i] = fmaxf(am[2 * i], fabsf(bf16_lo(v[i])));
-        am[2 * i + 1] = fmaxf(am[2 * i + 1], fabsf(bf16_hi(v[i])));
-      }
+      for (int u = 0; u < 4; ++u) v[u] = ld(r + 32 * u);
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          am[2 * i] = fmaxf(am[2 * i], fabsf(bf16_lo(v[u][i])));
+          am[2 * i + 1] = fmaxf(am[2 * i + 1], fabsf(bf16_hi(v[u][i])));
+        }
     }
     float* red = reinterpret_cast<float*>(tile);
 #pragma unroll
@@ -108,9 +113,10 @@ __global__ void __launch_bounds__(256) xpose_kernel(const uint16_t* __restrict__
   const int c = tid >> 2, kk = (tid & 3) * 16;  // output column, first of its 16 rows
   const size_t obase = size_t(kpre[e]) * C + size_t(c0 + c) * kp + kk;
   const float sc = cscale[c];
-  u32x4 va = ld(2 * p), vb = ld(2 * p + 1);
+  // loads run two 64-row blocks ahead of the LDS work
+  u32x4 va = ld(2 * p), vb = ld(2 * p + 1), na = ld(64 + 2 * p), nb = ld(65 + 2 * p);
   for (int k0 = 0; k0 < kp; k0 += 64) {
-    const u32x4 na = ld(k0 + 64 + 2 * p), nb = ld(k0 + 65 + 2 * p);
+    const u32x4 fa = ld(k0 + 128 + 2 * p), fb = ld(k0 + 129 + 2 * p);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       tile[(q * 8 + 2 * i) * 33 + p] = (va[i] & 0xFFFFu) | (vb[i] << 16);
@@ -131,6 +137,8 @@ __global__ void __launch_bounds__(256) xpose_kernel(const uint16_t* __restrict__
     __syncthreads();
     va = na;
     vb = nb;
+    na = fa;
+    nb = fb;
   }
 }
 

@@ -51,9 +51,11 @@ struct GemmCfg {
 };
 
 // 256 x 256 on eight waves of 128 x 64 (two per SIMD, so one can issue MFMAs
-// while the other waits on a load).
-// bf16 / fp32: 64-byte slabs, four stages (three slabs in flight, 128 KB);
-// fp8: 128-byte slabs (one MFMA's K), two stages.
+// while the other waits on a load), 128-byte slabs in two stages (128 KB of
+// LDS; one slab in flight while the MFMAs consume the other).  Measured on the
+// Mixtral-shaped FC1, this beats four waves of 128 x 128 (whose 256
+// accumulators per lane push the epilogue into spills) and 64-byte slabs in
+// three or four stages (twice the barriers per K).
 template <int DT>
 struct CfgFor {
   using type = GemmCfg<2, 4, 4, 2, 1, 128, 2>;
