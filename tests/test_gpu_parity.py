@@ -222,9 +222,13 @@ def test_permute_fp8_bit_exact(T, E, k, h):
     np.testing.assert_array_equal(scale.cpu().numpy(), s[src_tok])
 
 
-def test_permute_row_scale_and_combine():
-    T, E, k, h = 333, 8, 3, 384
-    rng = np.random.default_rng(3)
+@pytest.mark.parametrize("T,E,k,h", [(333, 8, 3, 384), (257, 8, 2, 136), (64, 4, 1, 64)])
+def test_permute_row_scale_and_combine(T, E, k, h):
+    """Both dispatch kernels (one thread per chunk for k <= 2, one wave per
+    token above) and both combine splits (two waves per token when the row
+    has an even number of 8-element chunks, else one)."""
+    say(f"permute row_scale + combine T={T} E={E} k={k} h={h}")
+    rng = np.random.default_rng(3 + k)
     idx = np.argsort(rng.random((T, E)), axis=1)[:, :k].astype(np.int32)
     w = rng.random((T, k)).astype(np.float32)
     x = moe_synth.f32_to_bf16_bits(rng.standard_normal((T, h)).astype(np.float32))
