@@ -848,6 +848,12 @@ __global__ void __launch_bounds__(C::kThreads, C::kWavesPerSimd) grouped_gemm_ke
         ++c;
         continue;
       }
+      // The wave runs its MFMA substeps at raised issue priority, so where
+      // both waves of a SIMD have instructions ready the one in its MFMA
+      // phase goes first (Mixtral-shaped FC1 -1.5%, FC2 -0.7%); the barrier
+      // wait, the next slab's first fragments and the load issue run at the
+      // normal priority.
+      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int s = 0; s + 1 < S; ++s) {
         frags(fa[(s + 1) & 1], fb[(s + 1) & 1], As, s + 1);
@@ -865,6 +871,7 @@ __global__ void __launch_bounds__(C::kThreads, C::kWavesPerSimd) grouped_gemm_ke
           if (q < NR % NM) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
           if (s == 0 && q < NV) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
         }
+      __builtin_amdgcn_s_setprio(0);
       wait_slab(c + 1);  // this stage read out; slab c+1 landed
       __syncthreads();
       // next slab's first fragments load while the last substep multiplies

@@ -16,8 +16,9 @@
 //   dwg       dW_g partials x^T dL over 128-token chunks on fp32 MFMA (64
 //             columns x 64 experts per pass), then `dwg_reduce` adds the chunks
 //             in order (and the bias gradient, the column sums of dL);
-//   dx        dx = dx_in + dL W_g^T on fp32 MFMA, 32 tokens per workgroup with
-//             their dL in LDS and W_g rows in registers;
+//   dx        dx = dx_in + dL W_g^T, 32 tokens per workgroup: with a bf16 W_g
+//             and E <= 64 on bf16 MFMA with dL split into two bf16 parts,
+//             else on fp32 MFMA with the dL rows in LDS;
 //   aux       per-workgroup column sums of softmax(L_t), then one workgroup
 //             adds them in order and forms the loss.
 #include "common.h"
@@ -41,6 +42,18 @@ __device__ __forceinline__ void load8(const void* base, size_t elem, float* f) {
     const u32x4 v = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(base) + elem);
 #pragma unroll
     for (int i = 0; i < 4; ++i) { f[2 * i] = bf16_lo(v[i]); f[2 * i + 1] = bf16_hi(v[i]); }
+  }
+}
+
+// 8 values from one (bf16) or two (fp32) 16-byte words.
+template <bool kF32>
+__device__ __forceinline__ void unpack8f(const u32x4 (&v)[kF32 ? 2 : 1], float* f) {
+  if (kF32) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { f[i] = __uint_as_float(v[0][i]); f[4 + i] = __uint_as_float(v[kF32 ? 1 : 0][i]); }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { f[2 * i] = bf16_lo(v[0][i]); f[2 * i + 1] = bf16_hi(v[0][i]); }
   }
 }
 
@@ -106,20 +119,48 @@ __global__ void __launch_bounds__(256) rbwd_dlogits_kernel(
       wt[j] = topk_w[size_t(t) * k + j];
     }
   }
-  // dw_j = <dY_t, Yp_j>: lanes take 8-element chunks, then a butterfly sum
+  // dw_j = <dY_t, Yp_j>: lanes take 8-element chunks, then a butterfly sum.
+  // A batch of kB chunk positions has all its loads (dY and every routed
+  // row) issued before the first multiply; the routed rows are read once
+  // here, so their loads are nontemporal.
+  constexpr int kB = KM <= 2 ? 8 : (KM <= 4 ? 4 : (KM <= 8 ? 2 : 1));
+  constexpr int kVec = kF32 ? 2 : 1;  // 16-byte loads per 8 elements
+  const size_t esz = kF32 ? 4 : 2;
   float part[KM];
 #pragma unroll
   for (int j = 0; j < KM; ++j) part[j] = 0.f;
-  for (int c = lane * 8; c < h; c += 64 * 8) {
-    float d[8];
-    load8<kF32>(dy, size_t(t) * h + c, d);
+  for (int c0 = lane * 8; c0 < h; c0 += 64 * 8 * kB) {
+    u32x4 dv[kB][kVec], yv[kB][KM][kVec];
 #pragma unroll
-    for (int j = 0; j < KM; ++j) {
-      if (rows[j] < 0) continue;
-      float y[8];
-      load8<kF32>(yp, size_t(rows[j]) * h + c, y);
+    for (int b = 0; b < kB; ++b) {
+      const int c = c0 + 512 * b;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) part[j] = fmaf(d[i], y[i], part[j]);
+      for (int q = 0; q < kVec; ++q) {
+        dv[b][q] = u32x4{0, 0, 0, 0};
+        if (c < h)
+          dv[b][q] = reinterpret_cast<const u32x4*>(static_cast<const char*>(dy) + (size_t(t) * h + c) * esz)[q];
+      }
+#pragma unroll
+      for (int j = 0; j < KM; ++j)
+#pragma unroll
+        for (int q = 0; q < kVec; ++q) {
+          yv[b][j][q] = u32x4{0, 0, 0, 0};
+          if (c < h && rows[j] >= 0)
+            yv[b][j][q] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
+                static_cast<const char*>(yp) + (size_t(rows[j]) * h + c) * esz) + q);
+        }
+    }
+#pragma unroll
+    for (int b = 0; b < kB; ++b) {
+      float d[8];
+      unpack8f<kF32>(dv[b], d);
+#pragma unroll
+      for (int j = 0; j < KM; ++j) {
+        float y[8];
+        unpack8f<kF32>(yv[b][j], y);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) part[j] = fmaf(d[i], y[i], part[j]);
+      }
     }
   }
   float inner = 0.f;
@@ -353,6 +394,85 @@ __global__ void __launch_bounds__(256) rbwd_dx_kernel(const float* __restrict__ 
   }
 }
 
+// BF16 W_g with E <= 64: the same dx on bf16 MFMA 32x32x16.  dL is split
+// into hi = bf16(dL) and lo = bf16(dL - hi), and both parts multiply the
+// (exact) bf16 W_g with fp32 accumulation, which carries dL to ~2^-17
+// relative, at an eighth of the fp32 MFMA's issue time.  32 tokens per
+// workgroup: every lane keeps its token's dL fragments (hi and lo) in
+// registers; each wave takes 32-column blocks in turn, loads the block's
+// dx_in before its MFMAs and stores the sum as bf16.
+template <int KC>  // K steps of 16 experts, KC = ceil(E / 16) <= 4
+__global__ void __launch_bounds__(256) rbwd_dx_bf16_kernel(const float* __restrict__ dL,
+                                                           const uint16_t* __restrict__ wg,
+                                                           const float* __restrict__ dx_in, int T,
+                                                           int h, int E, uint16_t* __restrict__ dx) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int half = lane >> 5, l32 = lane & 31;
+  const int t0 = blockIdx.x * kDxTokens;
+  const int nt = T - t0 < kDxTokens ? T - t0 : kDxTokens;
+  // A fragments: token l32 (rows past the batch read token t0, never stored),
+  // experts 16 s + 8 half + i
+  const float* dlr = dL + size_t(t0 + (l32 < nt ? l32 : 0)) * E;
+  u32x4 ahi[KC], alo[KC];
+#pragma unroll
+  for (int st = 0; st < KC; ++st) {
+    float v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int e = 16 * st + 8 * half + i;
+      v[i] = e < E ? dlr[e] : 0.f;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t h0 = f32_to_bf16_bits(v[2 * i]), h1 = f32_to_bf16_bits(v[2 * i + 1]);
+      ahi[st][i] = h0 | (h1 << 16);
+      alo[st][i] = pack_bf16x2(v[2 * i] - __uint_as_float(h0 << 16), v[2 * i + 1] - __uint_as_float(h1 << 16));
+    }
+  }
+  const bool vec = (E & 7) == 0;
+  const int ncb = h / 32;
+  const int cb0 = blockIdx.y * kDxCbPer;
+  const int cbe = ncb < cb0 + kDxCbPer ? ncb : cb0 + kDxCbPer;
+  for (int cb = cb0 + wave; cb < cbe; cb += 4) {
+    const int c = cb * 32 + l32;
+    // C: row (token) 8(r/4) + 4 half + r%4, column l32
+    float din[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int tt = 8 * (r >> 2) + 4 * half + (r & 3);
+      din[r] = (dx_in && tt < nt) ? dx_in[size_t(t0 + tt) * h + c] : 0.f;
+    }
+    f32x16 acc;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+    const uint16_t* wr = wg + size_t(c) * E;
+#pragma unroll
+    for (int st = 0; st < KC; ++st) {
+      const int e0 = 16 * st + 8 * half;
+      u32x4 b = u32x4{0, 0, 0, 0};
+      if (vec) {
+        if (e0 < E) b = *reinterpret_cast<const u32x4*>(wr + e0);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t lo = e0 + 2 * i < E ? wr[e0 + 2 * i] : 0u;
+          const uint32_t hi = e0 + 2 * i + 1 < E ? wr[e0 + 2 * i + 1] : 0u;
+          b[i] = lo | (hi << 16);
+        }
+      }
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, ahi[st]),
+                                                    __builtin_bit_cast(bf16x8, b), acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, alo[st]),
+                                                    __builtin_bit_cast(bf16x8, b), acc, 0, 0, 0);
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int tt = 8 * (r >> 2) + 4 * half + (r & 3);
+      if (tt < nt) dx[size_t(t0 + tt) * h + c] = uint16_t(f32_to_bf16_bits(din[r] + acc[r]));
+    }
+  }
+}
+
 constexpr int kAuxTokens = 64;  // tokens per aux workgroup
 
 // colsum[b][e] = sum over the workgroup's 64 tokens (in token order) of
@@ -472,10 +592,20 @@ int router_bwd(const void* dy, const void* yp, const int32_t* dst_row, const int
   hipLaunchKernelGGL(rbwd_dwg_reduce_kernel, dim3(unsigned((n + 255) / 256)), dim3(256), 0, s, part,
                      part_b, nchunk, h, E, dw_gate, dbias);
   const dim3 gdx(ceil_div(T, kDxTokens), ceil_div(h / 32, kDxCbPer));
-  if (f32)
+  if (f32) {
     hipLaunchKernelGGL(rbwd_dx_kernel<true>, gdx, dim3(256), 0, s, dL, w_gate, dx_in, T, h, E, dx);
-  else
+  } else if (E <= 64) {
+    const uint16_t* wgb = static_cast<const uint16_t*>(w_gate);
+    uint16_t* dxb = static_cast<uint16_t*>(dx);
+    switch (ceil_div(E, 16)) {
+      case 1: hipLaunchKernelGGL(rbwd_dx_bf16_kernel<1>, gdx, dim3(256), 0, s, dL, wgb, dx_in, T, h, E, dxb); break;
+      case 2: hipLaunchKernelGGL(rbwd_dx_bf16_kernel<2>, gdx, dim3(256), 0, s, dL, wgb, dx_in, T, h, E, dxb); break;
+      case 3: hipLaunchKernelGGL(rbwd_dx_bf16_kernel<3>, gdx, dim3(256), 0, s, dL, wgb, dx_in, T, h, E, dxb); break;
+      default: hipLaunchKernelGGL(rbwd_dx_bf16_kernel<4>, gdx, dim3(256), 0, s, dL, wgb, dx_in, T, h, E, dxb); break;
+    }
+  } else {
     hipLaunchKernelGGL(rbwd_dx_kernel<false>, gdx, dim3(256), 0, s, dL, w_gate, dx_in, T, h, E, dx);
+  }
   timer_end(kTRouterBwd, s);
   return launch_status();
 }
