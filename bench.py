@@ -225,7 +225,12 @@ def main():
     if wl.backward:
         rhf = wl.R * wl.h * wl.h_ffn
         flops_per_launch.update(bwd_dA=2 * rhf, bwd_dW2=2 * rhf, bwd_dXp=4 * rhf, bwd_dW13=4 * rhf)
-    bytes_per_launch = {"permute": counts["permute_bytes"], "combine": counts["combine_bytes"],
+    # mean algorithmic bytes per launch over the step's launches of each kernel
+    # (a training step dispatches x, dY (and its FP8 codes) and re-gathers x;
+    # its second combine writes the expert path's dX in fp32)
+    mean = lambda v: sum(v) / len(v)
+    bytes_per_launch = {"permute": mean(counts["permute_launches"]),
+                        "combine": mean(counts["combine_launches"]),
                         "route": counts["router_bytes"]}
     if dom in flops_per_launch:
         achieved = flops_per_launch[dom] / (avg[dom] * 1e-3)

@@ -102,9 +102,23 @@ def workload_counts(wl) -> dict:
         combine_bytes=combine_bytes(wl.T, wl.h, wl.k, s_in, s_in),
         weight_bytes=gemm_weight_bytes(wl.E, wl.h, wl.h_ffn, s_g),
     )
+    # bytes of every dispatch / combine launch of one step, in launch order
+    out["permute_launches"] = [out["permute_bytes"]]
+    out["combine_launches"] = [out["combine_bytes"]]
     if wl.backward:
         out["flops_bwd"] = expert_flops_bwd(R, wl.h, wl.h_ffn)
-        # backward dispatch of dY (weighted) and re-gather of x, combine of dX
-        out["permute_bytes_bwd"] = 2 * permute_bytes(wl.T, wl.h, wl.k, s_in, s_in) + 4 * R
-        out["combine_bytes_bwd"] = combine_bytes(wl.T, wl.h, wl.k, s_in, s_in) - 4 * R
+        # dY dispatched with the gate weights as row scales (4 B each read)
+        dy_b = permute_bytes(wl.T, wl.h, wl.k, s_in, s_in) + 4 * R
+        xg_b = permute_bytes(wl.T, wl.h, wl.k, s_in, s_in)      # x re-gathered
+        if wl.dtype == "fp8":
+            # also dY as per-token E4M3 codes with scale w * s per routed row
+            dyq_b = permute_bytes(wl.T, wl.h, wl.k, s_in, 1, scales=True) + 4 * R
+            out["permute_launches"] += [dy_b, dyq_b, xg_b]
+        else:
+            out["permute_launches"] += [dy_b, xg_b]
+        # dX of the expert path: no gate weights read, fp32 output (the router
+        # backward adds its term and rounds once)
+        out["combine_launches"].append(combine_bytes(wl.T, wl.h, wl.k, s_in, 4) - 4 * R)
+        out["permute_bytes_bwd"] = sum(out["permute_launches"][1:])
+        out["combine_bytes_bwd"] = out["combine_launches"][1]
     return out

@@ -253,10 +253,11 @@ __global__ void __launch_bounds__(256) combine_kernel(const void* __restrict__ y
 namespace moe_launch {
 using namespace moe;
 
-// Dispatch copy: for k <= 2 one thread per 16-byte chunk with nontemporal
-// loads and stores (Mixtral-shaped batch in the layer: 0.74 -> 0.78 of HBM
-// peak); for larger k the wave-per-token kernel, whose k stores per loaded
-// chunk measured faster there (DeepSeekMoE-shaped, k = 6: 0.71 against 0.68).
+// Dispatch copy: for k <= 4 one thread per 16-byte chunk with nontemporal
+// loads and stores (measured in the layer: Mixtral-shaped, k = 2, 0.74 -> 0.78
+// of HBM peak; 352B-shaped, k = 3, 0.70 -> 0.79); for larger k the
+// wave-per-token kernel, whose k stores per loaded chunk measured faster there
+// (DeepSeekMoE-shaped, k = 6: 0.71 against 0.68).
 int permute_rows(const void* src, int src_dt, const int32_t* dst_row, const float* row_scale,
                  int T, int h, int k, void* dst, int dst_dt, float* dst_scale, hipStream_t s) {
   if (T == 0) return MOE_OK;
@@ -267,7 +268,7 @@ int permute_rows(const void* src, int src_dt, const int32_t* dst_row, const floa
   if (dst_dt == MOE_FP8_E4M3) {
     hipLaunchKernelGGL(permute_fp8_kernel, grid, block, 0, s, (const uint16_t*)src, dst_row, row_scale,
                        T, h, k, (uint8_t*)dst, dst_scale);
-  } else if (k <= 2) {
+  } else if (k <= 4) {
     if (f32)
       hipLaunchKernelGGL((permute_flat_kernel<true, true, true>), fgrid, block, 0, s, src, dst_row,
                          row_scale, T, h, k, dst);

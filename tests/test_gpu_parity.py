@@ -222,9 +222,9 @@ def test_permute_fp8_bit_exact(T, E, k, h):
     np.testing.assert_array_equal(scale.cpu().numpy(), s[src_tok])
 
 
-@pytest.mark.parametrize("T,E,k,h", [(333, 8, 3, 384), (257, 8, 2, 136), (64, 4, 1, 64)])
+@pytest.mark.parametrize("T,E,k,h", [(333, 8, 3, 384), (257, 8, 2, 136), (64, 4, 1, 64), (200, 12, 6, 256)])
 def test_permute_row_scale_and_combine(T, E, k, h):
-    """Both dispatch kernels (one thread per chunk for k <= 2, one wave per
+    """Both dispatch kernels (one thread per chunk for k <= 4, one wave per
     token above) and both combine splits (two waves per token when the row
     has an even number of 8-element chunks, else one)."""
     say(f"permute row_scale + combine T={T} E={E} k={k} h={h}")
