@@ -8,37 +8,67 @@
 //
 // BF16: logits on MFMA with x read once from HBM and W_g transposed through
 // LDS (see route_bf16_kernel); FP32 (small workloads) and given logits: a
-// plain dot-product kernel.  Top-k is one thread per token over its E logits.
+// plain dot-product kernel.  Top-k runs on eight lanes per token.
 #include "common.h"
 
 namespace moe {
 
 constexpr int kRouteTokens = 128;  // tokens per workgroup of the generic kernel
 
-__device__ __forceinline__ void topk_select(const float* L, int E, int k, int32_t* idx_out,
-                                            float* w_out) {
-  // j-th pick = the largest logit strictly after the previous pick in the
-  // (logit desc, index asc) order.
-  float pv = 0.f;
-  int pe = -1;
+// Top-k of one token's E logits and the softmax over the k kept ones, by 8
+// cooperating lanes (lanes 8q .. 8q+7 of a wave, `sub` = lane % 8).  Slot j
+// holds the j-th expert in the order (logit descending, expert index
+// ascending), so equal logits keep the lower index first.  Lane sub holds
+// experts sub, sub + 8, ... in registers (ME8 >= ceil(E / 8) of them); round j
+// takes every lane's best expert not yet taken and reduces the eight
+// candidates by shuffles.  Lane sub = 0 writes the k ids and weights.
+template <int ME8>
+__device__ __forceinline__ void topk_select8(const float* L, int E, int k, int sub,
+                                             int32_t* idx_out, float* w_out) {
+  static_assert(ME8 <= 32, "taken mask");
+  float v[ME8];
+  uint32_t taken = 0;
+#pragma unroll
+  for (int m = 0; m < ME8; ++m) {
+    const int e = sub + 8 * m;
+    v[m] = e < E ? L[e] : 0.f;
+    if (e >= E) taken |= 1u << m;
+  }
   float vals[MOE_MAX_TOPK];
   int ids[MOE_MAX_TOPK];
-  for (int j = 0; j < k; ++j) {
+#pragma unroll
+  for (int j = 0; j < MOE_MAX_TOPK; ++j) {
+    if (j >= k) break;
     float bv = 0.f;
     int be = -1;
-    for (int e = 0; e < E; ++e) {
-      float v = L[e];
-      bool after = pe < 0 || v < pv || (v == pv && e > pe);
-      if (after && (be < 0 || v > bv)) { bv = v; be = e; }
+#pragma unroll
+    for (int m = 0; m < ME8; ++m) {
+      const int e = sub + 8 * m;
+      if (!((taken >> m) & 1u) && (be < 0 || v[m] > bv)) { bv = v[m]; be = e; }
     }
-    vals[j] = bv; ids[j] = be;
-    pv = bv; pe = be;
+#pragma unroll
+    for (int off = 1; off < 8; off <<= 1) {
+      const float ov = __shfl_xor(bv, off, 8);
+      const int oe = __shfl_xor(be, off, 8);
+      if (oe >= 0 && (be < 0 || ov > bv || (ov == bv && oe < be))) { bv = ov; be = oe; }
+    }
+    vals[j] = bv;
+    ids[j] = be;
+    if (be >= 0 && (be & 7) == sub) taken |= 1u << (be >> 3);
   }
+  if (sub != 0) return;
   float z[MOE_MAX_TOPK];
-  float s = 0.f;
-  for (int j = 0; j < k; ++j) { z[j] = expf(vals[j] - vals[0]); s += z[j]; }
-  float inv = 1.0f / s;
-  for (int j = 0; j < k; ++j) {
+  float sum = 0.f;
+#pragma unroll
+  for (int j = 0; j < MOE_MAX_TOPK; ++j) {
+    if (j >= k) break;
+    z[j] = expf(vals[j] - vals[0]);
+    sum += z[j];
+  }
+  const float inv = 1.0f / sum;
+#pragma unroll
+  for (int j = 0; j < MOE_MAX_TOPK; ++j) {
+    if (j >= k) break;
     idx_out[j] = ids[j];
     w_out[j] = (k == 1) ? 1.0f : z[j] * inv;
   }
@@ -47,11 +77,12 @@ __device__ __forceinline__ void topk_select(const float* L, int E, int k, int32_
 // BF16 logits on MFMA 32x32x16: one workgroup of four waves per 32 tokens;
 // wave w takes the K range [w h/4, (w+1) h/4) in 64-element chunks.
 // x goes straight from HBM into A fragments (64 contiguous bytes per lane
-// per chunk).  The chunk's 64 rows of W_g are one contiguous block: the wave
-// reads it in 16-byte loads and writes it transposed into its own LDS region
-// ([expert][k], 144-byte rows), from where each lane's B fragment is one
-// 16-byte read.  The four partial 32 x E tiles are summed in LDS in wave
-// order, the bias added, and one thread per token picks its k experts.
+// per chunk), one chunk ahead of its MFMAs.  The chunk's 64 rows of W_g are
+// one contiguous block: the wave reads it in 16-byte loads (lane = row, up to
+// eight loads of a lane issued together) and writes it transposed into its
+// own LDS region ([expert][k], 144-byte rows), from where each lane's B
+// fragment is one 16-byte read.  The four partial 32 x E tiles are summed in LDS in wave
+// order, the bias added, and eight lanes per token pick its k experts.
 constexpr int kRtTokens = 32;
 constexpr int kRtChunk = 64;                // K elements per chunk
 constexpr int kRtStride = kRtChunk + 8;     // bf16 per LDS row of W^T
@@ -83,28 +114,53 @@ __global__ void __launch_bounds__(256) route_bf16_kernel(const uint16_t* __restr
   const int kw = h / 4;  // h is a multiple of 64, so kw of 16
   const int kbeg = wave * kw;
   const uint16_t* xr = x + size_t(rowc) * h + half * 32;
-  for (int kc = kbeg; kc < kbeg + kw; kc += kRtChunk) {
-    const int kn = kbeg + kw - kc < kRtChunk ? kbeg + kw - kc : kRtChunk;  // 16, 32, 48 or 64
-    u32x4 xa[4];
+  // x fragments of chunk kc (zero past the wave's K range)
+  auto load_x = [&](int kc, u32x4 (&xa)[4]) {
+    const int kn = kbeg + kw - kc < kRtChunk ? kbeg + kw - kc : kRtChunk;  // <= 0: none
 #pragma unroll
     for (int s = 0; s < 4; ++s)
       xa[s] = (half * 32 + s * 8 < kn) ? *reinterpret_cast<const u32x4*>(xr + kc + s * 8)
                                        : u32x4{0, 0, 0, 0};
-    __syncthreads();  // previous chunk's fragments read out of wt
-    // W_g rows kc .. kc+kn-1 are kn*E contiguous values: 16-byte units
+  };
+  constexpr int kWB = 8;  // W_g units (8 experts) per lane loaded before their LDS stores
+  u32x4 xa[4], xn[4];
+  load_x(kbeg, xa);
+  for (int kc = kbeg; kc < kbeg + kw; kc += kRtChunk) {
+    const int kn = kbeg + kw - kc < kRtChunk ? kbeg + kw - kc : kRtChunk;  // 16, 32, 48 or 64
+    // the next chunk's x loads fly during this chunk's W_g staging and MFMAs
+    load_x(kc + kRtChunk, xn);
+    // W_g rows kc .. kc+kn-1 are kn*E contiguous values.  With E % 8 == 0,
+    // lane kk takes row kc + kk in 16-byte units of 8 experts (the first kWB
+    // units loaded before the barrier) and stores them transposed, so
+    // neighbouring lanes store neighbouring k of one expert row of W^T;
+    // otherwise the units run in memory order.
     const uint16_t* src = wg + size_t(kc) * E;
-    const int units = kn * E / 8;
     if ((E & 7) == 0) {
-      // units k-fastest: neighbouring lanes store neighbouring k of one
-      // expert row of W^T (2-byte stores into the same or the next word)
-      for (int u = lane; u < units; u += 64) {
-        const int kk = u % kn, e8 = u / kn;
-        const u32x4 v = *reinterpret_cast<const u32x4*>(src + size_t(kk) * E + e8 * 8);
+      const int ne8 = E / 8;
+      const bool rowok = lane < kn;
+      u32x4 wv[kWB];
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
-          wt[(e8 * 8 + i) * kRtStride + kk] = uint16_t(v[i >> 1] >> (16 * (i & 1)));
+      for (int b = 0; b < kWB; ++b)
+        if (rowok && b < ne8) wv[b] = *reinterpret_cast<const u32x4*>(src + size_t(lane) * E + b * 8);
+      __syncthreads();  // previous chunk's fragments read out of wt
+      for (int e0 = 0; e0 < ne8; e0 += kWB) {
+        if (e0 > 0) {
+#pragma unroll
+          for (int b = 0; b < kWB; ++b)
+            if (rowok && e0 + b < ne8)
+              wv[b] = *reinterpret_cast<const u32x4*>(src + size_t(lane) * E + (e0 + b) * 8);
+        }
+#pragma unroll
+        for (int b = 0; b < kWB; ++b) {
+          if (!rowok || e0 + b >= ne8) continue;
+#pragma unroll
+          for (int i = 0; i < 8; ++i)
+            wt[((e0 + b) * 8 + i) * kRtStride + lane] = uint16_t(wv[b][i >> 1] >> (16 * (i & 1)));
+        }
       }
     } else {
+      __syncthreads();  // previous chunk's fragments read out of wt
+      const int units = kn * E / 8;
       for (int u = lane; u < units; u += 64) {
         const u32x4 v = *reinterpret_cast<const u32x4*>(src + size_t(u) * 8);
         int q = u * 8, kk = q / E, e = q - kk * E;
@@ -128,6 +184,8 @@ __global__ void __launch_bounds__(256) route_bf16_kernel(const uint16_t* __restr
             __builtin_bit_cast(bf16x8, xa[s]), __builtin_bit_cast(bf16x8, b), acc[n], 0, 0, 0);
       }
     }
+#pragma unroll
+    for (int s = 0; s < 4; ++s) xa[s] = xn[s];
   }
   __syncthreads();
   // partial tiles -> LDS [wave][token][E], then sum in wave order
@@ -156,9 +214,12 @@ __global__ void __launch_bounds__(256) route_bf16_kernel(const uint16_t* __restr
     if (logits_out && t0 + i < T) logits_out[size_t(t0) * E + q] = v;
   }
   __syncthreads();
-  if (tid < kRtTokens && t0 + tid < T) {
-    const int t = t0 + tid;
-    topk_select(part + tid * E, E, k, topk_idx + size_t(t) * k, topk_w + size_t(t) * k);
+  // eight lanes per token (256 threads = 32 tokens)
+  {
+    const int i = tid >> 3, t = t0 + i;
+    if (t < T)
+      topk_select8<4 * NT>(part + i * E, E, k, tid & 7, topk_idx + size_t(t) * k,
+                           topk_w + size_t(t) * k);
   }
 }
 
@@ -192,9 +253,12 @@ __global__ void __launch_bounds__(256) route_generic_kernel(const float* __restr
     lg[i * ls + e] = v;
   }
   __syncthreads();
-  if (tid < kRouteTokens && t0 + tid < T) {
-    int t = t0 + tid;
-    topk_select(lg + tid * ls, E, k, topk_idx + size_t(t) * k, topk_w + size_t(t) * k);
+  // eight lanes per token, 32 tokens per pass
+  for (int i = tid >> 3; i < kRouteTokens; i += 32) {
+    const int t = t0 + i;
+    if (t < T)
+      topk_select8<MOE_MAX_EXPERTS / 8>(lg + i * ls, E, k, tid & 7, topk_idx + size_t(t) * k,
+                                        topk_w + size_t(t) * k);
   }
 }
 
