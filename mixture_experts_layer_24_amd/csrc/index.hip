@@ -8,7 +8,8 @@
 // Three small kernels, all on device data (no host round trip):
 //   count  -- per block of 256 tokens, a per-expert histogram in LDS;
 //   scan   -- one workgroup: per-expert totals, the exclusive offsets, and each
-//             block's starting row inside every expert;
+//             block's starting row inside every expert (threads split the
+//             blocks of an expert into ranges);
 //   assign -- per block again: a token's rank among the block's tokens of the
 //             same expert comes from 64-bit lane masks (one per expert and
 //             wave) built with LDS atomic OR, then popcount of the lanes below.
@@ -38,33 +39,64 @@ __global__ void __launch_bounds__(kIdxBlock) idx_count_kernel(const int32_t* __r
 }
 
 // One workgroup of 256 threads.  blk_cnt [nb][E] is rewritten in place into
-// each block's first row per expert.
+// each block's first row per expert.  G = 256 / E threads (rounded down to a
+// power of two) share an expert, thread g owning a contiguous range of
+// blocks: it sums its range, the range sums are scanned per expert, the
+// expert totals across experts, and each thread then writes its range's
+// running offsets.  Loads go in batches of eight, so the chain of dependent
+// global reads is ~nb / (8 G) long instead of nb.
 __global__ void __launch_bounds__(256) idx_scan_kernel(int32_t* __restrict__ blk_cnt, int nb,
                                                        int E, int32_t* __restrict__ counts,
                                                        int32_t* __restrict__ offsets) {
   __shared__ int tot[MOE_MAX_EXPERTS + 1];
+  __shared__ int part[256];
   const int tid = threadIdx.x;
-  for (int e = tid; e < E; e += 256) {
-    int s = 0;
-    for (int b = 0; b < nb; ++b) {
-      int c = blk_cnt[size_t(b) * E + e];
-      blk_cnt[size_t(b) * E + e] = s;  // prefix within the expert, offset added below
-      s += c;
+  int G = 1;
+  while (G * 2 * E <= 256) G *= 2;
+  const int e = tid / G, g = tid - e * G;
+  const bool act = e < E;
+  const int b0 = act ? int(int64_t(nb) * g / G) : 0;
+  const int b1 = act ? int(int64_t(nb) * (g + 1) / G) : 0;
+  int s = 0;
+  for (int b = b0; b < b1; b += 8) {
+    int c[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) c[i] = b + i < b1 ? blk_cnt[size_t(b + i) * E + e] : 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) s += c[i];
+  }
+  part[tid] = s;
+  __syncthreads();
+  if (tid < E) {  // exclusive scan of expert tid's range sums
+    int run = 0;
+    for (int q = 0; q < G; ++q) {
+      const int v = part[tid * G + q];
+      part[tid * G + q] = run;
+      run += v;
     }
-    tot[e] = s;
-    counts[e] = s;
+    tot[tid] = run;
+    counts[tid] = run;
   }
   __syncthreads();
   if (tid == 0) {
     int run = 0;
-    for (int e = 0; e < E; ++e) { int c = tot[e]; tot[e] = run; run += c; }
+    for (int x = 0; x < E; ++x) { const int c = tot[x]; tot[x] = run; run += c; }
     tot[E] = run;
   }
   __syncthreads();
-  for (int e = tid; e <= E; e += 256) offsets[e] = tot[e];
-  for (int e = tid; e < E; e += 256) {
-    int base = tot[e];
-    for (int b = 0; b < nb; ++b) blk_cnt[size_t(b) * E + e] += base;
+  for (int x = tid; x <= E; x += 256) offsets[x] = tot[x];
+  if (act) {
+    int r = tot[e] + part[tid];
+    for (int b = b0; b < b1; b += 8) {
+      int c[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) c[i] = b + i < b1 ? blk_cnt[size_t(b + i) * E + e] : 0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        if (b + i < b1) blk_cnt[size_t(b + i) * E + e] = r;
+        r += c[i];
+      }
+    }
   }
 }
 

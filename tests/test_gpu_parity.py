@@ -131,6 +131,37 @@ def test_route_from_x(name, T):
     np.testing.assert_allclose(w.cpu().numpy()[keep], rw[keep], rtol=2e-5)
 
 
+@pytest.mark.parametrize("T,h,E,k", [(300, 256, 8, 2), (257, 512, 64, 6), (130, 192, 100, 4),
+                                     (96, 1024, 16, 1), (64, 128, 256, 16)])
+def test_route_from_x_selection_on_own_logits(T, h, E, k):
+    """The BF16 router's top-k and softmax, applied to the logits it wrote,
+    equal the oracle's selection on those same logits, element for element.
+    Columns of W_g are duplicated so that whole groups of experts tie
+    exactly (every column of the gate product runs the same instructions in
+    the same order), which exercises the index tie rule; E = 100 takes the
+    W_g staging path for E not a multiple of 8."""
+    say(f"route selection T={T} h={h} E={E} k={k}")
+    rng = np.random.default_rng(E * 7 + k)
+    x = moe_synth.f32_to_bf16_bits(rng.standard_normal((T, h)).astype(np.float32))
+    wg = (rng.standard_normal((h, E)) * 0.02).astype(np.float32)
+    for dst, src in ((3, 0), (5, 0), (E - 1, 1), (E // 2, 2), (E // 2 + 1, 2)):
+        if dst < E and src < E and dst != src:
+            wg[:, dst] = wg[:, src]
+    wg = moe_synth.f32_to_bf16_bits(wg)
+    bias = np.zeros(E, np.float32)
+    bias[E // 3] = 0.05
+    logits = torch.empty(T, E, dtype=torch.float32, device=DEV)
+    idx = torch.empty(T, k, dtype=torch.int32, device=DEV)
+    w = torch.empty(T, k, dtype=torch.float32, device=DEV)
+    ops.moe_route(dev_tensor(x), dev_tensor(wg), torch.from_numpy(bias).to(DEV), logits, T, h, E, k,
+                  MOE_BF16, idx, w)
+    gl = logits.cpu().numpy()
+    assert (gl[:, 3] == gl[:, 0]).all()                     # the ties are exact
+    ri, rw = ref.topk_softmax(gl, k)
+    np.testing.assert_array_equal(idx.cpu().numpy(), ri)
+    np.testing.assert_allclose(w.cpu().numpy(), rw, rtol=1e-6, atol=0)
+
+
 # ------------------------------------------------------- index + dispatch
 
 @pytest.mark.parametrize("T,E,k,h,dt", [(300, 8, 2, 64, "bf16"), (1000, 64, 6, 128, "bf16"),
