@@ -367,8 +367,11 @@ int moe_timing_report(char* buf, size_t len);
  * that conversion and the library's bit-level reference encoder (OCP
  * E4M3FN, round to nearest even, saturating), in pairs and quadruples, and
  * writes the number of disagreements to *mismatches (one uint64 in device
- * memory, written on the stream; 0 expected).  About 2^32 values: tens of
- * milliseconds.
+ * memory, written on the stream; 0 expected).  The count also includes the
+ * quantizers' quotient encoder (codes of v / s from one reciprocal per
+ * scale, with the division where a quotient lies near a rounding boundary)
+ * against the plain division, on 2^30 hashed quadruples of bf16 values with
+ * their scales.  About 2^32 + 2^32 values: tens of milliseconds.
  */
 int moe_fp8_convert_selftest(unsigned long long* mismatches, void* stream);
 

@@ -75,6 +75,40 @@ __device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
   return uint32_t(__builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true));
 }
 
+// E4M3 codes of the fp32 quotients v / s (the division rounded to nearest)
+// for one scale s and four values, mostly without dividing.  With r = RN(1/s)
+// the product q0 = RN(v r) is within (2^-23 + 2^-48) |v/s| of v/s, and RN(v/s)
+// within 2^-24 |v/s|, so RN(v/s) lies between q0 (1 - 2^-20) and q0 (1 + 2^-20)
+// (each end rounded toward q0 by at most 2^-24 relative, far inside the
+// margin).  The encoding is monotone, so when both ends give the same four
+// codes those are the codes of RN(v/s); otherwise (a value within ~2^-20 of
+// a rounding boundary) the division decides.  Below 2^-126 the relative
+// bound does not hold, but there every quotient in the interval encodes to
+// a signed zero.  `fast` is false when 1/s is not a normal number, and then
+// every quotient is divided.
+struct QuotScale {
+  float s, r;
+  bool fast;
+};
+__device__ __forceinline__ QuotScale quot_scale(float s) {
+  QuotScale q;
+  q.s = s;
+  q.r = 1.0f / s;
+  q.fast = s >= 0x1p-125f && s <= 0x1p125f;
+  return q;
+}
+__device__ __forceinline__ uint32_t e4m3x4_quot(float a, float b, float c, float d,
+                                                const QuotScale& q) {
+  if (q.fast) {
+    const float qa = a * q.r, qb = b * q.r, qc = c * q.r, qd = d * q.r;
+    constexpr float kLo = 1.0f - 0x1p-20f, kHi = 1.0f + 0x1p-20f;
+    const uint32_t lo = e4m3x4(qa * kLo, qb * kLo, qc * kLo, qd * kLo);
+    const uint32_t hi = e4m3x4(qa * kHi, qb * kHi, qc * kHi, qd * kHi);
+    if (lo == hi) return lo;
+  }
+  return e4m3x4(a / q.s, b / q.s, c / q.s, d / q.s);
+}
+
 __device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
   uint32_t s = (c & 0x80u) << 24;
   uint32_t e = (c >> 3) & 0xFu, m = c & 7u;
@@ -107,10 +141,11 @@ __device__ __forceinline__ void rowq_wave(const uint16_t* __restrict__ src, int 
   amax = wave_max(amax);
   const float s = amax > 0.f ? amax / 448.0f : 1.0f;
   if (lane == 0) *scale = s;
+  const QuotScale qs = quot_scale(s);
   for (int c = lane * 8; c < len; c += 512) {
     const u32x4 v = *reinterpret_cast<const u32x4*>(src + c);
-    const uint32_t lo = e4m3x4(bf16_lo(v[0]) / s, bf16_hi(v[0]) / s, bf16_lo(v[1]) / s, bf16_hi(v[1]) / s);
-    const uint32_t hi = e4m3x4(bf16_lo(v[2]) / s, bf16_hi(v[2]) / s, bf16_lo(v[3]) / s, bf16_hi(v[3]) / s);
+    const uint32_t lo = e4m3x4_quot(bf16_lo(v[0]), bf16_hi(v[0]), bf16_lo(v[1]), bf16_hi(v[1]), qs);
+    const uint32_t hi = e4m3x4_quot(bf16_lo(v[2]), bf16_hi(v[2]), bf16_lo(v[3]), bf16_hi(v[3]), qs);
     *reinterpret_cast<uint2*>(dst + c) = make_uint2(lo, hi);
   }
 }

@@ -113,6 +113,7 @@ __global__ void __launch_bounds__(256) xpose_kernel(const uint16_t* __restrict__
   const int c = tid >> 2, kk = (tid & 3) * 16;  // output column, first of its 16 rows
   const size_t obase = size_t(kpre[e]) * C + size_t(c0 + c) * kp + kk;
   const float sc = cscale[c];
+  const QuotScale qs = quot_scale(sc);
   // loads run two 64-row blocks ahead of the LDS work
   u32x4 va = ld(2 * p), vb = ld(2 * p + 1), na = ld(64 + 2 * p), nb = ld(65 + 2 * p);
   for (int k0 = 0; k0 < kp; k0 += 64) {
@@ -130,8 +131,8 @@ __global__ void __launch_bounds__(256) xpose_kernel(const uint16_t* __restrict__
       u32x4 o;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        o[i] = e4m3x4(bf16_lo(w[2 * i]) / sc, bf16_hi(w[2 * i]) / sc, bf16_lo(w[2 * i + 1]) / sc,
-                      bf16_hi(w[2 * i + 1]) / sc);
+        o[i] = e4m3x4_quot(bf16_lo(w[2 * i]), bf16_hi(w[2 * i]), bf16_lo(w[2 * i + 1]),
+                           bf16_hi(w[2 * i + 1]), qs);
       *reinterpret_cast<u32x4*>(static_cast<uint8_t*>(dst) + obase + k0) = o;
     }
     __syncthreads();

@@ -47,6 +47,7 @@ __global__ void __launch_bounds__(256) quant_act_kernel(const float* __restrict_
   amax = wave_max(amax);
   const float s = amax > 0.f ? amax / 448.0f : 1.0f;
   if (lane == 0) scale[row] = s;
+  const QuotScale qs = quot_scale(s);
   const f32x4* src = reinterpret_cast<const f32x4*>(act + size_t(row) * hf);
   uint32_t* dst = reinterpret_cast<uint32_t*>(q + size_t(row) * hf);
   constexpr int kBatch = 8;  // 16-byte loads per lane in flight
@@ -59,7 +60,7 @@ __global__ void __launch_bounds__(256) quant_act_kernel(const float* __restrict_
 #pragma unroll
     for (int b = 0; b < kBatch; ++b) {
       if (c0 + 64 * b >= n4) break;
-      dst[c0 + 64 * b] = e4m3x4(v[b][0] / s, v[b][1] / s, v[b][2] / s, v[b][3] / s);
+      dst[c0 + 64 * b] = e4m3x4_quot(v[b][0], v[b][1], v[b][2], v[b][3], qs);
     }
   }
 }

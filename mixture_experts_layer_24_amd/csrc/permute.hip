@@ -140,6 +140,7 @@ __global__ void __launch_bounds__(256) permute_fp8_kernel(const uint16_t* __rest
   const float scale = amax > 0.f ? amax / 448.0f : 1.0f;
   if (lane < k && rows[lane] >= 0 && rows[lane] < T * k)
     dst_scale[rows[lane]] = row_scale ? row_scale[size_t(t) * k + lane] * scale : scale;
+  const QuotScale qs = quot_scale(scale);
   const bool held = nch <= 64 * kBatch;  // v still holds the row
   for (int c0 = lane; c0 < nch; c0 += 64 * kBatch) {
     if (!held) {
@@ -153,8 +154,8 @@ __global__ void __launch_bounds__(256) permute_fp8_kernel(const uint16_t* __rest
       if (c >= nch) break;
       float f[8];
       unpack8(v[b], f);
-      const uint32_t lo = e4m3x4(f[0] / scale, f[1] / scale, f[2] / scale, f[3] / scale);
-      const uint32_t hi = e4m3x4(f[4] / scale, f[5] / scale, f[6] / scale, f[7] / scale);
+      const uint32_t lo = e4m3x4_quot(f[0], f[1], f[2], f[3], qs);
+      const uint32_t hi = e4m3x4_quot(f[4], f[5], f[6], f[7], qs);
       for (int j = 0; j < k; ++j) {
         if (rows[j] < 0 || rows[j] >= T * k) continue;
         uint2* d = reinterpret_cast<uint2*>(dst + size_t(rows[j]) * h);

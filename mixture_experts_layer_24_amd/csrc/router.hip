@@ -36,9 +36,7 @@ __device__ __forceinline__ void topk_select8(const float* L, int E, int k, int s
   }
   float vals[MOE_MAX_TOPK];
   int ids[MOE_MAX_TOPK];
-#pragma unroll
-  for (int j = 0; j < MOE_MAX_TOPK; ++j) {
-    if (j >= k) break;
+  for (int j = 0; j < k; ++j) {
     float bv = 0.f;
     int be = -1;
 #pragma unroll
