@@ -184,6 +184,8 @@ int grouped_bwd(const void* dyp, const void* xp, const void* h13_save, const moe
                 const int32_t* offsets, int rows, void* dxp, float* dw1, float* dw3, float* dw2,
                 void* ws, hipStream_t s);
 size_t grouped_bwd_ws_bytes(int rows, int h, int h_ffn, int E, int dtype);
+int dw_rows_bf16(const void* a, int M, const void* b, int N, const int32_t* offsets, int E,
+                 int rows, float* out, hipStream_t s);
 int router_bwd(const void* dy, const void* yp, const int32_t* dst_row, const int32_t* topk_idx,
                const float* topk_w, const float* logits, const int32_t* counts, int T, int h,
                int E, int k, float alpha, int dtype, const void* x, const void* w_gate,
@@ -215,6 +217,7 @@ const char* last_hip_error();
 
 // Optional per-kernel timing: when enabled (moe_timing_enable), a pair of HIP
 // events is recorded on the launch stream around every kernel of the layer.
+// A negative id records nothing (a kernel inside another timed span).
 enum TimerId { kTRoute = 0, kTIndex, kTPermute, kTFc1, kTQuant, kTFc2, kTCombine, kTBwd1, kTBwd2,
                kTBwd3, kTBwd4, kTPack, kTXpose, kTRouterBwd, kTRouterAux, kTCapacity, kNumTimers };
 void timer_begin(int id, hipStream_t s);

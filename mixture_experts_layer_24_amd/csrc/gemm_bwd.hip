@@ -169,6 +169,16 @@ static size_t kpad_upper(int rows, int E, int pad) {
   return size_t(rows) + size_t(pad - 1) * E;
 }
 
+// out[e] [M][N] (fp32) = A_e^T B_e for row-major bf16 A [rows][M] and
+// B [rows][N], K = rows offsets[e] .. offsets[e+1]: the weight-gradient
+// schedule, without split-K (the router backward's dW_g on token chunks).
+int dw_rows_bf16(const void* a, int M, const void* b, int N, const int32_t* offsets, int E,
+                 int rows, float* out, hipStream_t s) {
+  GemmArgs g{a, nullptr, b, nullptr, offsets, E, 0, N, rows, M,
+             out, nullptr, nullptr, nullptr, nullptr, nullptr};
+  return launch_gemm<CfgB, MOE_BF16, kModeDW, kSchedKR>(g, -1, s);
+}
+
 size_t grouped_bwd_ws_bytes(int rows, int h, int h_ffn, int E, int dtype) {
   (void)dtype;
   (void)h;

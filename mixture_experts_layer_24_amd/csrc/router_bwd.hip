@@ -13,9 +13,12 @@
 // deterministic):
 //   dlogits   one wave per token: dw_j = <dY_t, Yp[dst_row_tj]>, the top-k
 //             softmax backward, the aux-loss gradient, dL_t written in fp32;
-//   dwg       dW_g partials x^T dL over 128-token chunks on fp32 MFMA (64
-//             columns x 64 experts per pass), then `dwg_reduce` adds the chunks
-//             in order (and the bias gradient, the column sums of dL);
+//   dwg       dW_g = x^T dL: with bf16 x on the GroupedGEMM's weight-gradient
+//             schedule, dL split into two bf16 parts and the tokens in chunks
+//             (see rbwd_dl_split_kernel); with fp32 x, partials over 128-token
+//             chunks on fp32 MFMA (64 columns x 64 experts per pass); then the
+//             chunks are added in order (and the bias gradient, the column
+//             sums of dL);
 //   dx        dx = dx_in + dL W_g^T, 32 tokens per workgroup: with a bf16 W_g
 //             and E <= 64 on bf16 MFMA with dL split into two bf16 parts,
 //             else on fp32 MFMA with the dL rows in LDS;
@@ -302,6 +305,82 @@ __global__ void __launch_bounds__(256) rbwd_dwg_reduce_kernel(const float* __res
   }
 }
 
+// BF16 x: dW_g = x^T dL runs on the GroupedGEMM's weight-gradient schedule
+// (bf16 MFMA, row-major operands read through the LDS transpose read), with
+// the tokens cut into `nch` chunks that act as its experts, so the chunks'
+// products run side by side; dL enters as two bf16 parts (hi = bf16(dL),
+// lo = bf16(dL - hi), side by side in rows of E2 = 2E rounded up to 8
+// values; the pad columns are never read back), which carries it to ~2^-17
+// relative with fp32 sums.  Blocks [0, nconv) write the two parts (block 0
+// also the chunk boundaries); with dbias, block nconv + e sums column e of dL
+// in fp32 (thread j over tokens j, j + 256, ... in order, then the 256
+// partials in order).
+__global__ void __launch_bounds__(256) rbwd_dl_split_kernel(const float* __restrict__ dL, int T,
+                                                            int E, int E2, int chunk, int nch,
+                                                            int nconv,
+                                                            uint16_t* __restrict__ dlhl,
+                                                            int32_t* __restrict__ choff,
+                                                            float* __restrict__ dbias) {
+  const int tid = threadIdx.x;
+  if (int(blockIdx.x) < nconv) {
+    if (blockIdx.x == 0)
+      for (int q = tid; q <= nch; q += 256) choff[q] = int64_t(q) * chunk < T ? q * chunk : T;
+    const size_t n = size_t(T) * E;
+    for (size_t q = size_t(blockIdx.x) * 256 + tid; q < n; q += size_t(nconv) * 256) {
+      const size_t t = q / E, e = q - t * E;
+      const float v = dL[q];
+      const uint32_t hb = f32_to_bf16_bits(v);
+      uint16_t* row = dlhl + t * E2;
+      row[e] = uint16_t(hb);
+      row[E + e] = uint16_t(f32_to_bf16_bits(v - __uint_as_float(hb << 16)));
+    }
+    return;
+  }
+  __shared__ float ps[256];
+  const int e = blockIdx.x - nconv;
+  float v = 0.f;
+  for (int t0 = tid; t0 < T; t0 += 256 * 8) {
+    float a[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int t = t0 + 256 * i;
+      a[i] = t < T ? dL[size_t(t) * E + e] : 0.f;
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v += a[i];
+  }
+  ps[tid] = v;
+  __syncthreads();
+  if (tid == 0) {
+    float sum = 0.f;
+    for (int j = 0; j < 256; ++j) sum += ps[j];
+    dbias[e] = sum;
+  }
+}
+
+// dw_gate[c][e] = sum over chunks (in order) of P[ch][c][e] + P[ch][c][E + e]
+// (the products of the two parts of dL).
+__global__ void __launch_bounds__(256) rbwd_dwg_gemm_reduce_kernel(const float* __restrict__ P,
+                                                                   int nch, int h, int E, int E2,
+                                                                   float* __restrict__ dw_gate) {
+  const size_t n = size_t(h) * E, pitch = size_t(h) * E2;
+  const size_t i = size_t(blockIdx.x) * 256 + threadIdx.x;  // [c][e]
+  if (i >= n) return;
+  const size_t c = i / E, e = i - c * E;
+  const float* p = P + c * E2 + e;
+  float v = 0.f;
+  int q = 0;
+  for (; q + 4 <= nch; q += 4) {
+    float a[4], b[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) { a[j] = p[size_t(q + j) * pitch]; b[j] = p[size_t(q + j) * pitch + E]; }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) v += a[j] + b[j];
+  }
+  for (; q < nch; ++q) v += p[size_t(q) * pitch] + p[size_t(q) * pitch + E];
+  dw_gate[i] = v;
+}
+
 constexpr int kDxTokens = 32;
 constexpr int kDxEC = 64;           // experts per pass
 constexpr int kDxPad = kDxEC + 1;   // fp32 per LDS row
@@ -541,9 +620,28 @@ using namespace moe;
 
 static size_t al256(size_t x) { return (x + 255) & ~size_t(255); }
 
+// Token chunks of the BF16 dW_g product: about one persistent round of
+// GEMM tiles (256) over ceil(h/256) x ceil(E2/256) tiles per chunk; chunks
+// are whole 64-row slabs except the last.  E2 = 2E rounded up to 8.
+static int dwg_e2(int E) { return (2 * E + 7) / 8 * 8; }
+static void dwg_chunks(int T, int h, int E, int* chunk, int* nch) {
+  const int tiles = ceil_div(h, 256) * ceil_div(dwg_e2(E), 256);
+  int n = 256 / tiles > 1 ? 256 / tiles : 1;
+  int c = ceil_div(ceil_div(T, n), 64) * 64;
+  *chunk = c;
+  *nch = ceil_div(T, c);
+}
+
 size_t router_bwd_ws_bytes(int T, int h, int E) {
+  // fp32: chunk partials of the fp32 product; bf16: dL parts, GEMM partials,
+  // chunk boundaries and column sums
   const size_t nchunk = size_t(ceil_div(T, kDwTC));
-  return al256(size_t(T) * E * 4) + al256(nchunk * h * E * 4) + al256(nchunk * E * 4);
+  const size_t f32_ws = al256(nchunk * h * E * 4) + al256(nchunk * E * 4);
+  int chunk, nch;
+  dwg_chunks(T, h, E, &chunk, &nch);
+  const size_t bf_ws = al256(size_t(T) * dwg_e2(E) * 2) + al256(size_t(nch) * h * dwg_e2(E) * 4) +
+                       al256(size_t(nch + 1) * 4);
+  return al256(size_t(T) * E * 4) + (f32_ws > bf_ws ? f32_ws : bf_ws);
 }
 
 size_t router_aux_ws_bytes(int T, int E) { return al256(size_t(ceil_div(T, kAuxTokens)) * E * 4); }
@@ -575,22 +673,40 @@ int router_bwd(const void* dy, const void* yp, const int32_t* dst_row, const int
   unsigned char* w = static_cast<unsigned char*>(ws);
   float* dL = dlogits ? dlogits : reinterpret_cast<float*>(w);
   w += al256(size_t(T) * E * 4);
-  const int nchunk = ceil_div(T, kDwTC);
-  float* part = reinterpret_cast<float*>(w);
-  w += al256(size_t(nchunk) * h * E * 4);
-  float* part_b = reinterpret_cast<float*>(w);
 
   timer_begin(kTRouterBwd, s);
   if (f32) launch_dlogits<true>(dy, yp, dst_row, topk_idx, topk_w, logits, counts, T, h, E, k, alpha, dL, s);
   else launch_dlogits<false>(dy, yp, dst_row, topk_idx, topk_w, logits, counts, T, h, E, k, alpha, dL, s);
-  const dim3 gdw(h / kDwCols, nchunk);
-  if (f32)
-    hipLaunchKernelGGL(rbwd_dwg_kernel<true>, gdw, dim3(256), 0, s, x, dL, T, h, E, part, part_b);
-  else
-    hipLaunchKernelGGL(rbwd_dwg_kernel<false>, gdw, dim3(256), 0, s, x, dL, T, h, E, part, part_b);
   const size_t n = size_t(h) * E;
-  hipLaunchKernelGGL(rbwd_dwg_reduce_kernel, dim3(unsigned((n + 255) / 256)), dim3(256), 0, s, part,
-                     part_b, nchunk, h, E, dw_gate, dbias);
+  if (f32) {
+    const int nchunk = ceil_div(T, kDwTC);
+    float* part = reinterpret_cast<float*>(w);
+    float* part_b = reinterpret_cast<float*>(w + al256(size_t(nchunk) * h * E * 4));
+    const dim3 gdw(h / kDwCols, nchunk);
+    hipLaunchKernelGGL(rbwd_dwg_kernel<true>, gdw, dim3(256), 0, s, x, dL, T, h, E, part, part_b);
+    hipLaunchKernelGGL(rbwd_dwg_reduce_kernel, dim3(unsigned((n + 255) / 256)), dim3(256), 0, s,
+                       part, part_b, nchunk, h, E, dw_gate, dbias);
+  } else {
+    int chunk, nch;
+    dwg_chunks(T, h, E, &chunk, &nch);
+    const int E2 = dwg_e2(E);
+    uint16_t* dlhl = reinterpret_cast<uint16_t*>(w);
+    w += al256(size_t(T) * E2 * 2);
+    float* P = reinterpret_cast<float*>(w);
+    w += al256(size_t(nch) * h * E2 * 4);
+    int32_t* choff = reinterpret_cast<int32_t*>(w);
+    const size_t nel = size_t(T) * E;
+    const int nconv = int(nel / 256 + 1 < 1024 ? nel / 256 + 1 : 1024);
+    hipLaunchKernelGGL(rbwd_dl_split_kernel, dim3(unsigned(nconv + (dbias ? E : 0))), dim3(256), 0, s,
+                       dL, T, E, E2, chunk, nch, nconv, dlhl, choff, dbias);
+    const int rc = dw_rows_bf16(x, h, dlhl, E2, choff, nch, T, P, s);
+    if (rc != MOE_OK) {
+      timer_end(kTRouterBwd, s);
+      return rc;
+    }
+    hipLaunchKernelGGL(rbwd_dwg_gemm_reduce_kernel, dim3(unsigned((n + 255) / 256)), dim3(256), 0,
+                       s, P, nch, h, E, E2, dw_gate);
+  }
   const dim3 gdx(ceil_div(T, kDxTokens), ceil_div(h / 32, kDxCbPer));
   if (f32) {
     hipLaunchKernelGGL(rbwd_dx_kernel<true>, gdx, dim3(256), 0, s, dL, w_gate, dx_in, T, h, E, dx);

@@ -30,7 +30,7 @@ hipEvent_t g_open_ev[moe_launch::kNumTimers];
 
 namespace moe_launch {
 void timer_begin(int id, hipStream_t s) {
-  if (!g_on) return;
+  if (!g_on || id < 0) return;
   std::lock_guard<std::mutex> lk(g_mu);
   if (g_next + 2 > g_pool.size()) { g_open[id] = 0; return; }
   hipEvent_t a = g_pool[g_next++];
@@ -39,7 +39,7 @@ void timer_begin(int id, hipStream_t s) {
   g_open_ev[id] = a;
 }
 void timer_end(int id, hipStream_t s) {
-  if (!g_on) return;
+  if (!g_on || id < 0) return;
   std::lock_guard<std::mutex> lk(g_mu);
   if (!g_open[id] || g_next + 1 > g_pool.size()) return;
   hipEvent_t b = g_pool[g_next++];
