@@ -80,6 +80,13 @@ __global__ void __launch_bounds__(256) xpose_kernel(const uint16_t* __restrict__
     if (r < m) v = *reinterpret_cast<const u32x4*>(sp + size_t(r) * C);
     return v;
   };
+  // the encoding pass is the rows' last use: nontemporal loads (DeepSeekMoE-
+  // shaped FP8 step: the four transposes 1.09 -> 0.95 ms)
+  auto ldn = [&](int r) {
+    u32x4 v = {0, 0, 0, 0};
+    if (r < m) v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(sp + size_t(r) * C));
+    return v;
+  };
   {
     float am[8];
 #pragma unroll
@@ -115,9 +122,9 @@ __global__ void __launch_bounds__(256) xpose_kernel(const uint16_t* __restrict__
   const float sc = cscale[c];
   const QuotScale qs = quot_scale(sc);
   // loads run two 64-row blocks ahead of the LDS work
-  u32x4 va = ld(2 * p), vb = ld(2 * p + 1), na = ld(64 + 2 * p), nb = ld(65 + 2 * p);
+  u32x4 va = ldn(2 * p), vb = ldn(2 * p + 1), na = ldn(64 + 2 * p), nb = ldn(65 + 2 * p);
   for (int k0 = 0; k0 < kp; k0 += 64) {
-    const u32x4 fa = ld(k0 + 128 + 2 * p), fb = ld(k0 + 129 + 2 * p);
+    const u32x4 fa = ldn(k0 + 128 + 2 * p), fb = ldn(k0 + 129 + 2 * p);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       tile[(q * 8 + 2 * i) * 33 + p] = (va[i] & 0xFFFFu) | (vb[i] << 16);
