@@ -124,8 +124,8 @@ __global__ void __launch_bounds__(256) rbwd_dlogits_kernel(
   }
   // dw_j = <dY_t, Yp_j>: lanes take 8-element chunks, then a butterfly sum.
   // A batch of kB chunk positions has all its loads (dY and every routed
-  // row) issued before the first multiply; the routed rows are read once
-  // here, so their loads are nontemporal.
+  // row) issued before the first multiply; this is the last read of both,
+  // so the loads are nontemporal.
   constexpr int kB = KM <= 2 ? 8 : (KM <= 4 ? 4 : (KM <= 8 ? 2 : 1));
   constexpr int kVec = kF32 ? 2 : 1;  // 16-byte loads per 8 elements
   const size_t esz = kF32 ? 4 : 2;
@@ -141,7 +141,8 @@ __global__ void __launch_bounds__(256) rbwd_dlogits_kernel(
       for (int q = 0; q < kVec; ++q) {
         dv[b][q] = u32x4{0, 0, 0, 0};
         if (c < h)
-          dv[b][q] = reinterpret_cast<const u32x4*>(static_cast<const char*>(dy) + (size_t(t) * h + c) * esz)[q];
+          dv[b][q] = __builtin_nontemporal_load(
+              reinterpret_cast<const u32x4*>(static_cast<const char*>(dy) + (size_t(t) * h + c) * esz) + q);
       }
 #pragma unroll
       for (int j = 0; j < KM; ++j)
@@ -479,7 +480,8 @@ __global__ void __launch_bounds__(256) rbwd_dx_kernel(const float* __restrict__ 
 // relative, at an eighth of the fp32 MFMA's issue time.  32 tokens per
 // workgroup: every lane keeps its token's dL fragments (hi and lo) in
 // registers; each wave takes 32-column blocks in turn, loads the block's
-// dx_in before its MFMAs and stores the sum as bf16.
+// dx_in (its last read: nontemporal) before its MFMAs and stores the sum as
+// bf16.
 template <int KC>  // K steps of 16 experts, KC = ceil(E / 16) <= 4
 __global__ void __launch_bounds__(256) rbwd_dx_bf16_kernel(const float* __restrict__ dL,
                                                            const uint16_t* __restrict__ wg,
@@ -519,7 +521,8 @@ __global__ void __launch_bounds__(256) rbwd_dx_bf16_kernel(const float* __restri
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int tt = 8 * (r >> 2) + 4 * half + (r & 3);
-      din[r] = (dx_in && tt < nt) ? dx_in[size_t(t0 + tt) * h + c] : 0.f;
+      din[r] = (dx_in && tt < nt) ? __builtin_nontemporal_load(dx_in + size_t(t0 + tt) * h + c)
+                                  : 0.f;
     }
     f32x16 acc;
 #pragma unroll
