@@ -56,3 +56,27 @@ def test_mixtral_counts():
     assert c["flops_fwd"] == 6 * 16384 * 4096 * 14336
     assert c["flops_fc1"] + c["flops_fc2"] == c["flops_fwd"]
     assert c["permute_bytes"] == 8192 * 4096 * 2 + 16384 * 4096 * 2 + 4 * 16384
+
+
+def test_row_mover_launch_bytes():
+    """Bytes of every dispatch / combine launch of one step, written out
+    element by element for two workloads (what bench.py's `hbm` fractions
+    divide by)."""
+    wl = moe_synth.WORKLOADS["mixtral"]
+    c = acc.workload_counts(wl)
+    T, h, k = 8192, 4096, 2
+    R = T * k
+    assert c["permute_launches"] == [T * h * 2 + R * h * 2 + 4 * R]          # x read, k copies, dst_row
+    assert c["combine_launches"] == [R * h * 2 + T * h * 2 + 8 * R]          # rows, y, dst_row + w
+    wl = moe_synth.WORKLOADS["dsmoe"]
+    c = acc.workload_counts(wl)
+    T, h, k = 16384, 2048, 6
+    R = T * k
+    x_fwd = T * h * 2 + R * h * 2 + 4 * R
+    dy = x_fwd + 4 * R                       # the gate weights as row scales
+    assert c["permute_launches"] == [x_fwd, dy, x_fwd]                      # x, dY, x re-gathered
+    assert c["combine_launches"] == [R * h * 2 + T * h * 2 + 8 * R,          # y
+                                     R * h * 2 + T * h * 4 + 4 * R]          # dX in fp32, no weights
+    c8 = acc.workload_counts(moe_synth.WORKLOADS["dsmoe_fp8"])
+    x_fp8 = T * h * 2 + R * h * 1 + 4 * R + 4 * R                          # codes + a scale per row
+    assert c8["permute_launches"] == [x_fp8, dy, x_fp8 + 4 * R, x_fwd]      # x, dY, dY codes, x
