@@ -72,21 +72,26 @@ __device__ __forceinline__ void topk_select8(const float* L, int E, int k, int s
   }
 }
 
-// BF16 logits on MFMA 32x32x16: one workgroup of four waves per 32 tokens;
-// wave w takes the K range [w h/4, (w+1) h/4) in 64-element chunks.
+// BF16 logits on MFMA 32x32x16: one workgroup of four (or eight, see RES)
+// waves per 32 tokens; wave w takes the K range [w h/NW, (w+1) h/NW) in
+// 64-element chunks.
 // x goes straight from HBM into A fragments (64 contiguous bytes per lane
-// per chunk), one chunk ahead of its MFMAs.  The chunk's 64 rows of W_g are
+// per chunk), one chunk (three with W_g resident) ahead of its MFMAs.  The chunk's 64 rows of W_g are
 // one contiguous block: the wave reads it in 16-byte loads (lane = row, up to
 // eight loads of a lane issued together) and writes it transposed into its
 // own LDS region ([expert][k], 144-byte rows), from where each lane's B
-// fragment is one 16-byte read.  The four partial 32 x E tiles are summed in LDS in wave
+// fragment is one 16-byte read.  The waves' partial 32 x E tiles are summed in LDS in wave
 // order, the bias added, and eight lanes per token pick its k experts.
 constexpr int kRtTokens = 32;
 constexpr int kRtChunk = 64;                // K elements per chunk
 constexpr int kRtStride = kRtChunk + 8;     // bf16 per LDS row of W^T
 
-template <int NT>  // NT = ceil(E / 32) expert blocks of 32
-__global__ void __launch_bounds__(256) route_bf16_kernel(const uint16_t* __restrict__ x,
+// RES: eight waves (two per SIMD) split h, and each wave's whole K range of
+// W_g (E x h/8 values) is staged in LDS once, transposed ([E][h/8 + 8]), when
+// all eight ranges fit; the chunk loop then runs without barriers or W_g
+// loads.  Otherwise four waves split h and stage W_g chunk by chunk.
+template <int NT, bool RES>  // NT = ceil(E / 32) expert blocks of 32
+__global__ void __launch_bounds__(RES ? 512 : 256) route_bf16_kernel(const uint16_t* __restrict__ x,
                                                          const uint16_t* __restrict__ wg,
                                                          const float* __restrict__ bias,
                                                          float* __restrict__ logits_out, int T,
@@ -100,8 +105,45 @@ __global__ void __launch_bounds__(256) route_bf16_kernel(const uint16_t* __restr
   const int t0 = blockIdx.x * kRtTokens;
   const int row = t0 + l32;
   const int rowc = row < T ? row : T - 1;
-  // this wave's W^T region: [NT*32][kRtStride] bf16
-  uint16_t* wt = reinterpret_cast<uint16_t*>(smem) + size_t(wave) * NT * 32 * kRtStride;
+  constexpr int NW = RES ? 8 : 4;  // waves
+  const int kw = h / NW;  // h is a multiple of 64 (of 128 with RES), so kw of 16
+  const int kbeg = wave * kw;
+  // this wave's W^T region: [NT*32][kRtStride] bf16 per chunk, or (RES) the
+  // whole range [E][kw + 8]
+  const int rstride = RES ? kw + 8 : kRtStride;
+  uint16_t* wt = reinterpret_cast<uint16_t*>(smem) +
+                 size_t(wave) * (RES ? size_t(E) * rstride : size_t(NT) * 32 * kRtStride);
+  if (RES) {
+    // lane = row kk of the range, 16-byte units of 8 experts (E % 8 == 0),
+    // else single values; eight loads in flight per lane
+    const uint16_t* src = wg + size_t(kbeg) * E;
+    if ((E & 7) == 0) {
+      const int ne8 = E / 8, nu = kw * ne8;
+      for (int u0 = lane; u0 < nu; u0 += 64 * 8) {
+        u32x4 v[8];
+#pragma unroll
+        for (int b = 0; b < 8; ++b) {
+          const int u = u0 + 64 * b;
+          if (u < nu) v[b] = *reinterpret_cast<const u32x4*>(src + size_t(u % kw) * E + (u / kw) * 8);
+        }
+#pragma unroll
+        for (int b = 0; b < 8; ++b) {
+          const int u = u0 + 64 * b;
+          if (u >= nu) break;
+          const int kk = u % kw, e8 = u / kw;
+#pragma unroll
+          for (int i = 0; i < 8; ++i)
+            wt[(e8 * 8 + i) * rstride + kk] = uint16_t(v[b][i >> 1] >> (16 * (i & 1)));
+        }
+      }
+    } else {
+      for (int q = lane; q < kw * E; q += 64) {
+        const int kk = q / E, e = q - kk * E;
+        wt[e * rstride + kk] = src[q];
+      }
+    }
+    __syncthreads();
+  }
 
   f32x16 acc[NT];
 #pragma unroll
@@ -109,8 +151,6 @@ __global__ void __launch_bounds__(256) route_bf16_kernel(const uint16_t* __restr
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[n][r] = 0.f;
 
-  const int kw = h / 4;  // h is a multiple of 64, so kw of 16
-  const int kbeg = wave * kw;
   const uint16_t* xr = x + size_t(rowc) * h + half * 32;
   // x fragments of chunk kc (zero past the wave's K range)
   auto load_x = [&](int kc, u32x4 (&xa)[4]) {
@@ -121,19 +161,25 @@ __global__ void __launch_bounds__(256) route_bf16_kernel(const uint16_t* __restr
                                        : u32x4{0, 0, 0, 0};
   };
   constexpr int kWB = 8;  // W_g units (8 experts) per lane loaded before their LDS stores
-  u32x4 xa[4], xn[4];
-  load_x(kbeg, xa);
+  // x runs PF chunks ahead of the MFMAs (RES: three, with no barrier in the
+  // loop to pace the waves; else one, during the W_g staging)
+  constexpr int PF = RES ? 3 : 1;
+  u32x4 xq[PF + 1][4];
+#pragma unroll
+  for (int p = 0; p < PF; ++p) load_x(kbeg + p * kRtChunk, xq[p]);
   for (int kc = kbeg; kc < kbeg + kw; kc += kRtChunk) {
     const int kn = kbeg + kw - kc < kRtChunk ? kbeg + kw - kc : kRtChunk;  // 16, 32, 48 or 64
-    // the next chunk's x loads fly during this chunk's W_g staging and MFMAs
-    load_x(kc + kRtChunk, xn);
+    load_x(kc + PF * kRtChunk, xq[PF]);
+    u32x4 (&xa)[4] = xq[0];
     // W_g rows kc .. kc+kn-1 are kn*E contiguous values.  With E % 8 == 0,
     // lane kk takes row kc + kk in 16-byte units of 8 experts (the first kWB
     // units loaded before the barrier) and stores them transposed, so
     // neighbouring lanes store neighbouring k of one expert row of W^T;
     // otherwise the units run in memory order.
     const uint16_t* src = wg + size_t(kc) * E;
-    if ((E & 7) == 0) {
+    if (RES) {
+      // W^T of the whole range is resident
+    } else if ((E & 7) == 0) {
       const int ne8 = E / 8;
       const bool rowok = lane < kn;
       u32x4 wv[kWB];
@@ -169,11 +215,11 @@ __global__ void __launch_bounds__(256) route_bf16_kernel(const uint16_t* __restr
         }
       }
     }
-    __syncthreads();
+    if (!RES) __syncthreads();
 #pragma unroll
     for (int n = 0; n < NT; ++n) {
       const int e = n * 32 + l32;
-      const uint16_t* br = wt + e * kRtStride + half * 32;
+      const uint16_t* br = RES ? wt + e * rstride + (kc - kbeg) + half * 32 : wt + e * kRtStride + half * 32;
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         u32x4 b = (e < E && half * 32 + s * 8 < kn) ? *reinterpret_cast<const u32x4*>(br + s * 8)
@@ -183,7 +229,9 @@ __global__ void __launch_bounds__(256) route_bf16_kernel(const uint16_t* __restr
       }
     }
 #pragma unroll
-    for (int s = 0; s < 4; ++s) xa[s] = xn[s];
+    for (int p = 0; p < PF; ++p)
+#pragma unroll
+      for (int s = 0; s < 4; ++s) xq[p][s] = xq[p + 1][s];
   }
   __syncthreads();
   // partial tiles -> LDS [wave][token][E], then sum in wave order
@@ -201,11 +249,10 @@ __global__ void __launch_bounds__(256) route_bf16_kernel(const uint16_t* __restr
   }
   __syncthreads();
   // the sum replaces wave 0's partial in place: logits [32][E]
-  for (int q = tid; q < kRtTokens * E; q += 256) {
+  for (int q = tid; q < kRtTokens * E; q += NW * 64) {
     float v = part[q];
-    v += part[kRtTokens * E + q];
-    v += part[2 * kRtTokens * E + q];
-    v += part[3 * kRtTokens * E + q];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) v += part[w * kRtTokens * E + q];
     const int i = q / E, e = q - i * E;
     if (bias) v += bias[e];
     part[q] = v;
@@ -215,7 +262,7 @@ __global__ void __launch_bounds__(256) route_bf16_kernel(const uint16_t* __restr
   // eight lanes per token (256 threads = 32 tokens)
   {
     const int i = tid >> 3, t = t0 + i;
-    if (t < T)
+    if (i < kRtTokens && t < T)
       topk_select8<4 * NT>(part + i * E, E, k, tid & 7, topk_idx + size_t(t) * k,
                            topk_w + size_t(t) * k);
   }
@@ -268,12 +315,25 @@ using namespace moe;
 template <int NT>
 static void launch_route_bf16(const void* x, const void* wg, const float* bias, float* logits,
                               int T, int h, int E, int k, int32_t* idx, float* w, hipStream_t s) {
-  const size_t wtb = size_t(4) * NT * 32 * kRtStride * 2;
+  const dim3 grid(ceil_div(T, kRtTokens));
+  // the whole of W_g resident in LDS (eight waves) when it and the eight
+  // partial tiles fit in 150 KB
+  const size_t resb = size_t(8) * E * (h / 8 + 8) * 2;
+  const size_t redb8 = size_t(8) * kRtTokens * E * 4;
+  const size_t shm8 = resb > redb8 ? resb : redb8;
+  if (h % 128 == 0 && shm8 <= 150 * 1024) {
+    static bool ok = allow_lds(route_bf16_kernel<NT, true>, 160 * 1024);
+    (void)ok;
+    hipLaunchKernelGGL((route_bf16_kernel<NT, true>), grid, dim3(512), shm8, s,
+                       (const uint16_t*)x, (const uint16_t*)wg, bias, logits, T, h, E, k, idx, w);
+    return;
+  }
+  const dim3 block(256);
   const size_t redb = size_t(4) * kRtTokens * E * 4;
-  const size_t shm = wtb > redb ? wtb : redb;
-  static bool ok = allow_lds(route_bf16_kernel<NT>, 160 * 1024);
+  const size_t wtb = size_t(4) * NT * 32 * kRtStride * 2;
+  static bool ok = allow_lds(route_bf16_kernel<NT, false>, 160 * 1024);
   (void)ok;
-  hipLaunchKernelGGL(route_bf16_kernel<NT>, dim3(ceil_div(T, kRtTokens)), dim3(256), shm, s,
+  hipLaunchKernelGGL((route_bf16_kernel<NT, false>), grid, block, wtb > redb ? wtb : redb, s,
                      (const uint16_t*)x, (const uint16_t*)wg, bias, logits, T, h, E, k, idx, w);
 }
 
