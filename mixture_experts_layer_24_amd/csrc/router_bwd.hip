@@ -110,6 +110,12 @@ __global__ void __launch_bounds__(256) rbwd_dlogits_kernel(
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
+  if (E == 1) {
+    // one expert: the top-1 weight is 1 and the balance loss constant, so
+    // dL is exactly zero (the sums below would leave rounding noise)
+    if (lane == 0) dL[t] = 0.f;
+    return;
+  }
   int rows[KM];
   float wt[KM];
 #pragma unroll

@@ -73,6 +73,11 @@ def check_close(got, want, frac, allowance=None, mask=None, what=""):
         allowance = None if allowance is None else allowance[mask]
     rms = np.sqrt(np.mean(np.square(want, dtype=np.float64)))
     excess = np.abs(got.astype(np.float64) - want) - (0 if allowance is None else allowance)
+    if rms == 0:
+        # an all-zero reference (e.g. the router gradient with one expert) is matched exactly
+        say(f"  {what}: reference is zero; max|got| = {np.abs(got).max():.3e}")
+        assert not np.any(got), what
+        return 0.0
     worst = excess.max() / rms
     say(f"  {what} (max|err| - allowance)/rms = {worst:.3e} (bar {frac:g}); plain max|err|/rms = "
         f"{np.abs(got.astype(np.float64) - want).max() / rms:.3e}")

@@ -129,6 +129,8 @@ UNIT_CASES = [
     ("bf16_e100_k4", dict(T=700, h=192, E=100, k=4), 0.03, "bf16", 13),
     ("bf16_k1", dict(T=129, h=64, E=16, k=1), 0.05, "bf16", 14),
     ("f32_e8_k2", dict(T=257, h=128, E=8, k=2), 0.01, "f32", 15),
+    # one expert: dL, dW_g and d(bias) are exactly zero
+    ("bf16_e1", dict(T=163, h=256, E=1, k=1), 0.03, "bf16", 16),
 ]
 
 
