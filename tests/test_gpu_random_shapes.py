@@ -8,7 +8,11 @@ Shapes are drawn per seed: T from 1 to 700, h and h_ffn in {128, 256, 384}
 without rows appear).  The bars are those of the fixed-shape tests: routing,
 index and dispatch bit-exact; y and the gradients within 2e-2 * rms of the
 oracle with BF16 storage / operands, with the storage distance allowed against
-the exact oracle; the FP8 forward at 6e-2 * rms with the oracle's allowance
+the exact oracle; against the BF16-operand oracle the weight gradients also
+allow, per element, the largest change one operand rounded to the
+neighbouring BF16 value makes (`bf16_flip`: an fp32 and an fp64 value on either
+side of a BF16 rounding boundary; seeds 48, 91, 132 and 134 are shapes where
+that happened), in both checks; the FP8 forward at 6e-2 * rms with the oracle's allowance
 for fp32 implementations (`check_fp8_forward`), the FP8 backward likewise
 against its allowance; the router backward within 1e-4 * rms; experts without
 rows get zero weight gradients.
@@ -24,6 +28,7 @@ from oracle import moe_ref as ref
 from test_gpu_parity import (HALF_ULP_BF16, _run_gpu_layer, check_close, check_fp8_forward, host, say,
                              storage_allowance)
 from test_gpu_backward import _gpu_fwd_bwd
+from bf16_flip import weight_grad_flip_allowance
 
 pytestmark = pytest.mark.gpu
 
@@ -36,7 +41,7 @@ def _shape(seed):
                 zipf_s=float(rng.choice([0.0, 1.2])))
 
 
-@pytest.mark.parametrize("seed", range(12))
+@pytest.mark.parametrize("seed", list(range(12)) + [48, 91, 132, 134])
 def test_random_shape_forward_backward(seed):
     over = _shape(seed)
     wl = moe_synth.WORKLOADS["dsmoe"].scaled(name=f"rand{seed}", **over)
@@ -53,15 +58,16 @@ def test_random_shape_forward_backward(seed):
     args = (f("dy"), f("x"), fw["w"], fw["dst_row"], fw["offsets"], f("w1"), f("w3"), f("w2"))
     bw = ref.layer_backward(*args)
     emu = ref.layer_backward(*args, bf16_operands=True)
+    flip = weight_grad_flip_allowance(*args)
     got = {"dx": host(layer.dx), "dw1": layer.dw1.cpu().numpy(), "dw3": layer.dw3.cpu().numpy(),
            "dw2": layer.dw2.cpu().numpy()}
     for name in ("dx", "dw1", "dw3", "dw2"):
         if not np.any(emu[name]):
             assert not np.any(got[name]), name
             continue
-        out_round = HALF_ULP_BF16 * np.abs(emu[name]) if name == "dx" else None
-        check_close(got[name], emu[name], 2e-2, out_round, None, name + " vs bf16-operand oracle")
-        dist = np.abs(emu[name] - bw[name]) + (0 if out_round is None else out_round)
+        extra = HALF_ULP_BF16 * np.abs(emu[name]) if name == "dx" else flip[name]
+        check_close(got[name], emu[name], 2e-2, extra, None, name + " vs bf16-operand oracle")
+        dist = np.abs(emu[name] - bw[name]) + extra
         check_close(got[name], bw[name], 2e-2, dist, None, name + " vs exact oracle")
     for e in np.nonzero(fw["counts"] == 0)[0]:
         assert not layer.dw1[e].any() and not layer.dw3[e].any() and not layer.dw2[e].any()
