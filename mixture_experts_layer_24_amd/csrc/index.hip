@@ -12,7 +12,9 @@
 //             blocks of an expert into ranges);
 //   assign -- per block again: a token's rank among the block's tokens of the
 //             same expert comes from 64-bit lane masks (one per expert and
-//             wave) built with LDS atomic OR, then popcount of the lanes below.
+//             wave) built with LDS atomic OR, then popcount of the lanes below;
+//             a block where some token names an expert twice counts pairs per
+//             slot position instead, so those pairs take consecutive rows.
 // The result is deterministic and stable whatever the scheduling.
 #include "common.h"
 
@@ -112,24 +114,62 @@ __global__ void __launch_bounds__(kIdxBlock) idx_assign_kernel(const int32_t* __
   for (int q = tid; q < W * E; q += kIdxBlock) mask[q / E][q % E] = 0ull;
   __syncthreads();
   const int t = blockIdx.x * kIdxBlock + tid;
+  const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   int ex[MOE_MAX_TOPK];
+  int dup = 0;  // this token names one expert in two of its slots
   for (int j = 0; j < k; ++j) {
     int e = t < T ? idx[size_t(t) * k + j] : -1;
     ex[j] = (e >= 0 && e < E) ? e : -1;
+    for (int j2 = 0; j2 < j; ++j2) dup |= ex[j] >= 0 && ex[j2] == ex[j];
     if (ex[j] >= 0) atomicOr(&mask[wave][ex[j]], 1ull << lane);
   }
-  __syncthreads();
+  if (!__syncthreads_or(dup)) {
+    // every token counts at most once per expert: its rank among the
+    // block's pairs of that expert is the number of lanes below it (this
+    // wave) and in earlier waves that name the expert
+    if (t < T) {
+      const int32_t* base = blk_base + size_t(blockIdx.x) * E;
+      for (int j = 0; j < k; ++j) {
+        int e = ex[j];
+        int r = -1;
+        if (e >= 0) {
+          r = base[e] + __popcll(mask[wave][e] & below);
+          for (int w2 = 0; w2 < wave; ++w2) r += __popcll(mask[w2][e]);
+          src_tok[r] = t;
+        }
+        dst_row[size_t(t) * k + j] = r;
+      }
+    }
+    return;
+  }
+  // A token of this block names some expert twice: its pairs of that expert
+  // take consecutive rows in slot order (the order of (token, slot) pairs).
+  // Count, per slot position jj in turn, the pairs of earlier tokens at that
+  // position (masks rebuilt per position), plus the token's own earlier
+  // slots with the same expert.
+  int acc[MOE_MAX_TOPK];
+  for (int j = 0; j < k; ++j) {
+    acc[j] = 0;
+    for (int j2 = 0; j2 < j; ++j2) acc[j] += ex[j] >= 0 && ex[j2] == ex[j];
+  }
+  for (int jj = 0; jj < k; ++jj) {
+    __syncthreads();  // the previous position's masks are read out
+    for (int q = tid; q < W * E; q += kIdxBlock) mask[q / E][q % E] = 0ull;
+    __syncthreads();
+    if (ex[jj] >= 0) atomicOr(&mask[wave][ex[jj]], 1ull << lane);
+    __syncthreads();
+    for (int j = 0; j < k; ++j) {
+      const int e = ex[j];
+      if (e < 0) continue;
+      acc[j] += __popcll(mask[wave][e] & below);
+      for (int w2 = 0; w2 < wave; ++w2) acc[j] += __popcll(mask[w2][e]);
+    }
+  }
   if (t < T) {
-    const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
     const int32_t* base = blk_base + size_t(blockIdx.x) * E;
     for (int j = 0; j < k; ++j) {
-      int e = ex[j];
-      int r = -1;
-      if (e >= 0) {
-        r = base[e] + __popcll(mask[wave][e] & below);
-        for (int w2 = 0; w2 < wave; ++w2) r += __popcll(mask[w2][e]);
-        src_tok[r] = t;
-      }
+      const int r = ex[j] >= 0 ? base[ex[j]] + acc[j] : -1;
+      if (r >= 0) src_tok[r] = t;
       dst_row[size_t(t) * k + j] = r;
     }
   }

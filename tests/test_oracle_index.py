@@ -116,3 +116,21 @@ def test_expert_parallel_shares_partition_the_layer():
             assert np.all(np.diff(toks) > 0)
     assert np.all(seen == 1)
     np.testing.assert_allclose(total, full, rtol=1e-13, atol=1e-13)
+
+
+def test_index_with_repeated_ids_in_a_token():
+    """A token naming one expert in several slots: every (token, slot) pair
+    is its own row, the token's pairs consecutive and in slot order (the
+    stable argsort of the flattened ids), and un-permute after permute still
+    returns each pair's token."""
+    rng = np.random.default_rng(17)
+    T, E, k = 300, 6, 4
+    idx = rng.integers(0, E, size=(T, k)).astype(np.int32)    # repeats in most tokens
+    idx[5] = 2                                                # all four slots on one expert
+    counts, offsets, dst_row, src_tok = ref.build_index(idx, E)
+    np.testing.assert_array_equal(counts, np.bincount(idx.ravel(), minlength=E))
+    order = np.argsort(idx.ravel(), kind="stable")
+    np.testing.assert_array_equal(dst_row.ravel()[order], np.arange(T * k))
+    np.testing.assert_array_equal(src_tok, order // k)
+    assert np.all(np.diff(dst_row[5]) == 1)
+    assert len(np.unique(dst_row)) == T * k
