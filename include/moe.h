@@ -153,15 +153,18 @@ size_t moe_permute_workspace_size(int T, int E, int k);
  *   topk_idx [T][k] int32 expert ids, or NULL to reuse an index built by an
  *            earlier call (then counts/offsets/src_tok are not touched and
  *            dst_row is an INPUT).  Ids outside [0, E) are dropped:
- *            dst_row = -1 and they are not counted.
+ *            dst_row = -1 and they are not counted.  A token may name one
+ *            expert in several slots (moe_route never does): each such
+ *            (t, j) pair is counted and gets its own row, the pairs of one
+ *            token in slot order.
  *   row_scale[T][k] fp32 or NULL: when given, routed row (t, j) receives
  *            row_scale[t][j] * src[t] (the transpose of the weighted combine,
  *            used for the upstream gradient).
  *   counts   [E]   int32 rows per expert.
  *   offsets  [E+1] int32 exclusive prefix sum; offsets[E] = rows kept.
  *   dst_row  [T][k] int32 row of (t, j) in dst: offsets[e] + number of
- *            tokens t' < t routed to e.  As an input, entries outside
- *            [0, T*k) are skipped.
+ *            pairs (t', j') routed to e with t' < t, or t' = t and j' < j.
+ *            As an input, entries outside [0, T*k) are skipped.
  *   src_tok  [T*k] int32 token of every routed row.
  *   dst      [T*k][h] element type dst_dtype: MOE_F32 (src F32), MOE_BF16
  *            (src BF16) or MOE_FP8_E4M3 (src BF16; per-token quantization:
@@ -233,7 +236,10 @@ size_t moe_grouped_workspace_size(int rows, int h, int h_ffn, int E, int dtype);
  *            offsets[e] .. offsets[e+1]-1; offsets[E] <= rows.
  *   h13_save [rows][2*h_ffn] bf16 or NULL (BF16 or FP8 weights): when given, FC1's output is kept
  *            for the backward, columns in the packed order of W->w13.
- *   yp       [rows][h] expert outputs: fp32 for MOE_F32 weights, else bf16.
+ *   yp       [rows][h] expert outputs, element type yp_dtype: MOE_F32 (any
+ *            weights; FC2's fp32 sum is stored as it is) or MOE_BF16 (BF16
+ *            or FP8 weights; rounded to nearest even).  Any other pairing
+ *            returns MOE_ERR_DTYPE.
  *   Math: G = xp W1_e, U = xp W3_e (fp32 accumulation), A = SiLU(G) * U,
  *   yp = A W2_e.  FP8: G, U carry xp_scale[row] * w13_scale[e][channel]; A
  *   is quantized per row (amax/448 over the row's h_ffn values) before FC2,
@@ -243,8 +249,8 @@ size_t moe_grouped_workspace_size(int rows, int h, int h_ffn, int E, int dtype);
  *   Limits: h and h_ffn multiples of 128.
  */
 int moe_grouped_swiglu_fwd(const void* xp, const float* xp_scale, const moe_weights* W,
-                           const int32_t* offsets, int rows, void* h13_save, void* yp, void* ws,
-                           size_t ws_bytes, void* stream);
+                           const int32_t* offsets, int rows, void* h13_save, void* yp, int yp_dtype,
+                           void* ws, size_t ws_bytes, void* stream);
 
 /* Workspace bytes for moe_grouped_swiglu_bwd. */
 size_t moe_grouped_bwd_workspace_size(int rows, int h, int h_ffn, int E, int dtype);
@@ -315,8 +321,10 @@ int moe_grouped_swiglu_bwd_fp8(const void* dyp_q, const float* dyp_scale, const 
  * with s_t = softmax(logits[t]) over all E experts and
  * g_e = alpha * E / (k T) * counts[e] / T (see moe_router_aux_loss).  Then
  *   dw_gate = x^T dL,   dbias = sum_t dL[t],   dx = dx_in + dL W_g^T.
- *   dy, yp   [T][h], [T*k][h] element type dtype (MOE_BF16 or MOE_F32): the
- *            upstream gradient and the forward's expert outputs.
+ *   dy       [T][h] element type dtype (MOE_BF16 or MOE_F32): the upstream
+ *            gradient.
+ *   yp       [T*k][h] element type yp_dtype (MOE_BF16 or MOE_F32): the
+ *            forward's expert outputs.
  *   dst_row, topk_idx [T][k] int32, topk_w [T][k] fp32, logits [T][E] fp32
  *            (bias included), counts [E] int32: the forward's routing.
  *   x [T][h], w_gate [h][E]: dtype.
@@ -329,7 +337,8 @@ int moe_grouped_swiglu_bwd_fp8(const void* dyp_q, const float* dyp_scale, const 
  *   results are bit-for-bit repeatable.
  */
 size_t moe_router_bwd_workspace_size(int T, int h, int E);
-int moe_router_bwd(const void* dy, const void* yp, const int32_t* dst_row, const int32_t* topk_idx,
+int moe_router_bwd(const void* dy, const void* yp, int yp_dtype, const int32_t* dst_row,
+                   const int32_t* topk_idx,
                    const float* topk_w, const float* logits, const int32_t* counts, int T, int h,
                    int E, int k, float alpha, int dtype, const void* x, const void* w_gate,
                    const float* dx_in, void* dx, float* dlogits, float* dw_gate, float* dbias,

@@ -99,7 +99,8 @@ def workload_counts(wl) -> dict:
         router_flops=router_flops(wl.T, wl.h, wl.E),
         router_bytes=router_bytes(wl.T, wl.h, wl.E, wl.k, s_in),
         permute_bytes=permute_bytes(wl.T, wl.h, wl.k, s_in, s_g, scales=wl.dtype == "fp8"),
-        combine_bytes=combine_bytes(wl.T, wl.h, wl.k, s_in, s_in),
+        # the expert outputs Yp are kept in fp32 (4 bytes each)
+        combine_bytes=combine_bytes(wl.T, wl.h, wl.k, 4, s_in),
         weight_bytes=gemm_weight_bytes(wl.E, wl.h, wl.h_ffn, s_g),
     )
     # bytes of every dispatch / combine launch of one step, in launch order

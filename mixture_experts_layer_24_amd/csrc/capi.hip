@@ -264,10 +264,13 @@ size_t moe_grouped_workspace_size(int rows, int h, int h_ffn, int E, int dtype) 
 }
 
 int moe_grouped_swiglu_fwd(const void* xp, const float* xp_scale, const moe_weights* W,
-                           const int32_t* offsets, int rows, void* h13_save, void* yp, void* ws,
-                           size_t ws_bytes, void* stream) {
+                           const int32_t* offsets, int rows, void* h13_save, void* yp, int yp_dtype,
+                           void* ws, size_t ws_bytes, void* stream) {
   int rc = check_weights(W);
   if (rc) return rc;
+  REQ(yp_dtype == MOE_F32 || (yp_dtype == MOE_BF16 && W->dtype != MOE_F32), MOE_ERR_DTYPE,
+      "yp_dtype %d with weight dtype %d (fp32 always; bf16 with bf16 or fp8 weights)", yp_dtype,
+      int(W->dtype));
   REQ(rows >= 0, MOE_ERR_ARG, "rows=%d is negative", rows);
   PTR(xp); PTR(offsets); PTR(yp); OPT(h13_save);
   if (W->dtype == MOE_FP8_E4M3) PTR(xp_scale);
@@ -279,8 +282,8 @@ int moe_grouped_swiglu_fwd(const void* xp, const float* xp_scale, const moe_weig
       need, ws ? ws_bytes : size_t(0));
   OPT(ws);
   moe_launch::clear_status();
-  return launched(moe_launch::grouped_fwd(xp, xp_scale, W, offsets, rows, h13_save, yp, ws,
-                                          (hipStream_t)stream),
+  return launched(moe_launch::grouped_fwd(xp, xp_scale, W, offsets, rows, h13_save, yp, yp_dtype,
+                                          ws, (hipStream_t)stream),
                   "moe_grouped_swiglu_fwd");
 }
 
@@ -359,7 +362,8 @@ size_t moe_router_bwd_workspace_size(int T, int h, int E) {
   return moe_launch::router_bwd_ws_bytes(T, h, E);
 }
 
-int moe_router_bwd(const void* dy, const void* yp, const int32_t* dst_row, const int32_t* topk_idx,
+int moe_router_bwd(const void* dy, const void* yp, int yp_dtype, const int32_t* dst_row,
+                   const int32_t* topk_idx,
                    const float* topk_w, const float* logits, const int32_t* counts, int T, int h,
                    int E, int k, float alpha, int dtype, const void* x, const void* w_gate,
                    const float* dx_in, void* dx, float* dlogits, float* dw_gate, float* dbias,
@@ -371,6 +375,7 @@ int moe_router_bwd(const void* dy, const void* yp, const int32_t* dst_row, const
   REQ(h > 0 && h % 64 == 0, MOE_ERR_SHAPE, "h=%d must be a positive multiple of 64", h);
   REQ(dtype == MOE_F32 || dtype == MOE_BF16, MOE_ERR_DTYPE, "router backward dtype %d unsupported",
       dtype);
+  REQ(yp_dtype == MOE_F32 || yp_dtype == MOE_BF16, MOE_ERR_DTYPE, "yp dtype %d unsupported", yp_dtype);
   REQ(alpha == alpha, MOE_ERR_ARG, "alpha is NaN");
   PTR(dy); PTR(yp); PTR(dst_row); PTR(topk_idx); PTR(topk_w); PTR(logits); PTR(counts);
   PTR(x); PTR(w_gate); PTR(dx); PTR(dw_gate); OPT(dx_in); OPT(dlogits); OPT(dbias);
@@ -380,7 +385,7 @@ int moe_router_bwd(const void* dy, const void* yp, const int32_t* dst_row, const
   REQ(ws != nullptr && ws_bytes >= need, MOE_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given",
       need, ws ? ws_bytes : size_t(0));
   moe_launch::clear_status();
-  return launched(moe_launch::router_bwd(dy, yp, dst_row, topk_idx, topk_w, logits, counts, T, h, E,
+  return launched(moe_launch::router_bwd(dy, yp, yp_dtype, dst_row, topk_idx, topk_w, logits, counts, T, h, E,
                                          k, alpha, dtype, x, w_gate, dx_in, dx, dlogits, dw_gate,
                                          dbias, ws, (hipStream_t)stream),
                   "moe_router_bwd");

@@ -177,7 +177,7 @@ int permute_rows(const void* src, int src_dt, const int32_t* dst_row, const floa
 int combine_rows(const void* yp, int yp_dt, const int32_t* dst_row, const float* w, int T, int h,
                  int k, void* y, int y_dt, hipStream_t s);
 int grouped_fwd(const void* xp, const float* xp_scale, const moe_weights* W,
-                const int32_t* offsets, int rows, void* h13_save, void* yp, void* ws,
+                const int32_t* offsets, int rows, void* h13_save, void* yp, int yp_dtype, void* ws,
                 hipStream_t s);
 size_t grouped_fwd_ws_bytes(int rows, int h, int h_ffn, int E, int dtype);
 int grouped_bwd(const void* dyp, const void* xp, const void* h13_save, const moe_weights* W,
@@ -186,7 +186,7 @@ int grouped_bwd(const void* dyp, const void* xp, const void* h13_save, const moe
 size_t grouped_bwd_ws_bytes(int rows, int h, int h_ffn, int E, int dtype);
 int dw_rows_bf16(const void* a, int M, const void* b, int N, const int32_t* offsets, int E,
                  int rows, float* out, hipStream_t s);
-int router_bwd(const void* dy, const void* yp, const int32_t* dst_row, const int32_t* topk_idx,
+int router_bwd(const void* dy, const void* yp, int yp_dtype, const int32_t* dst_row, const int32_t* topk_idx,
                const float* topk_w, const float* logits, const int32_t* counts, int T, int h,
                int E, int k, float alpha, int dtype, const void* x, const void* w_gate,
                const float* dx_in, void* dx, float* dlogits, float* dw_gate, float* dbias,

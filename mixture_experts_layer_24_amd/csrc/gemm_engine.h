@@ -89,6 +89,7 @@ struct GemmArgs {
   float* row_amax;        // FC1 with FP8: [rows][ceil(N / BN)] row maxima of |A|, one per column tile
   float* part;            // split-K partial tiles (kMaxGrid tiles) or null: no split
   uint32_t* cnt;          // split-K arrival counters [kMaxGrid], zero before the launch
+  int out_f32;            // FC2: 1 stores the output in fp32 (bf16 and FP8 operands too)
 };
 
 // LDS byte position of 16-byte chunk c of row r (pitch RB bytes): chunks are
@@ -445,7 +446,7 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, f32x16 (&acc)[C::kMI
           if (row < row_end) {
             float y = acc[i][j][r];
             if (DT == MOE_FP8_E4M3) y *= g.a_scale[row] * cs;
-            if (DT == MOE_F32)
+            if (DT == MOE_F32 || g.out_f32)
               static_cast<float*>(g.out)[size_t(row) * g.N + col] = y;
             else
               static_cast<uint16_t*>(g.out)[size_t(row) * g.N + col] = uint16_t(f32_to_bf16_bits(y));

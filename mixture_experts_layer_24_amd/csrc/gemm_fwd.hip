@@ -93,8 +93,8 @@ static int launch_fwd_gemm(const GemmArgs& a, hipStream_t s) {
 
 template <int DT>
 static int fwd_typed(const void* xp, const float* xp_scale, const moe_weights* W,
-                     const int32_t* offsets, int rows, void* h13_save, void* yp, void* ws,
-                     hipStream_t s) {
+                     const int32_t* offsets, int rows, void* h13_save, void* yp, int yp_f32,
+                     void* ws, hipStream_t s) {
   const int h = W->h, hf = W->h_ffn, E = W->E;
   unsigned char* w = static_cast<unsigned char*>(ws);
   void* act = w;
@@ -121,25 +121,26 @@ static int fwd_typed(const void* xp, const float* xp_scale, const moe_weights* W
                        (const float*)act, amax, int(ntn), offsets, E, hf, actq, ascale);
     timer_end(kTQuant, s);
     GemmArgs a2{actq, ascale, W->w2, W->w2_scale, offsets, E, hf, h, rows, 0, yp, nullptr, nullptr, nullptr,
-                nullptr, nullptr};
+                nullptr, nullptr, yp_f32};
     splitk_ws_set<typename CfgFor<DT>::type>(a2, split_ws);
     return launch_fwd_gemm<DT, kModeFC2>(a2, s);
   }
   GemmArgs a2{act, nullptr, W->w2, nullptr, offsets, E, hf, h, rows, 0, yp, nullptr, nullptr, nullptr,
-              nullptr, nullptr};
+              nullptr, nullptr, yp_f32};
   splitk_ws_set<typename CfgFor<DT>::type>(a2, split_ws);
   return launch_fwd_gemm<DT, kModeFC2>(a2, s);
 }
 
 int grouped_fwd(const void* xp, const float* xp_scale, const moe_weights* W,
-                const int32_t* offsets, int rows, void* h13_save, void* yp, void* ws,
+                const int32_t* offsets, int rows, void* h13_save, void* yp, int yp_dtype, void* ws,
                 hipStream_t s) {
   if (rows == 0) return MOE_OK;
+  const int f = yp_dtype == MOE_F32;
   switch (W->dtype) {
-    case MOE_F32: return fwd_typed<MOE_F32>(xp, xp_scale, W, offsets, rows, h13_save, yp, ws, s);
-    case MOE_BF16: return fwd_typed<MOE_BF16>(xp, xp_scale, W, offsets, rows, h13_save, yp, ws, s);
+    case MOE_F32: return fwd_typed<MOE_F32>(xp, xp_scale, W, offsets, rows, h13_save, yp, 1, ws, s);
+    case MOE_BF16: return fwd_typed<MOE_BF16>(xp, xp_scale, W, offsets, rows, h13_save, yp, f, ws, s);
     case MOE_FP8_E4M3:
-      return fwd_typed<MOE_FP8_E4M3>(xp, xp_scale, W, offsets, rows, h13_save, yp, ws, s);
+      return fwd_typed<MOE_FP8_E4M3>(xp, xp_scale, W, offsets, rows, h13_save, yp, f, ws, s);
   }
   return MOE_ERR_DTYPE;
 }

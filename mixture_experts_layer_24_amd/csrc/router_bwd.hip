@@ -101,7 +101,8 @@ __device__ __forceinline__ void stage_tile64(const float* __restrict__ src, int 
 }
 
 // dL for one token per wave.  KM bounds k (all slots' dots run together).
-template <bool kF32, int KM>
+// kF32: dY is fp32 (else bf16); kYF32: the expert outputs Yp are fp32.
+template <bool kF32, bool kYF32, int KM>
 __global__ void __launch_bounds__(256) rbwd_dlogits_kernel(
     const void* __restrict__ dy, const void* __restrict__ yp, const int32_t* __restrict__ dst_row,
     const int32_t* __restrict__ topk_idx, const float* __restrict__ topk_w,
@@ -133,13 +134,14 @@ __global__ void __launch_bounds__(256) rbwd_dlogits_kernel(
   // row) issued before the first multiply; this is the last read of both,
   // so the loads are nontemporal.
   constexpr int kB = KM <= 2 ? 8 : (KM <= 4 ? 4 : (KM <= 8 ? 2 : 1));
-  constexpr int kVec = kF32 ? 2 : 1;  // 16-byte loads per 8 elements
-  const size_t esz = kF32 ? 4 : 2;
+  constexpr int kVec = kF32 ? 2 : 1;  // 16-byte loads per 8 elements of dY
+  constexpr int kVecY = kYF32 ? 2 : 1;  // and of Yp
+  const size_t esz = kF32 ? 4 : 2, eszy = kYF32 ? 4 : 2;
   float part[KM];
 #pragma unroll
   for (int j = 0; j < KM; ++j) part[j] = 0.f;
   for (int c0 = lane * 8; c0 < h; c0 += 64 * 8 * kB) {
-    u32x4 dv[kB][kVec], yv[kB][KM][kVec];
+    u32x4 dv[kB][kVec], yv[kB][KM][kVecY];
 #pragma unroll
     for (int b = 0; b < kB; ++b) {
       const int c = c0 + 512 * b;
@@ -153,11 +155,11 @@ __global__ void __launch_bounds__(256) rbwd_dlogits_kernel(
 #pragma unroll
       for (int j = 0; j < KM; ++j)
 #pragma unroll
-        for (int q = 0; q < kVec; ++q) {
+        for (int q = 0; q < kVecY; ++q) {
           yv[b][j][q] = u32x4{0, 0, 0, 0};
           if (c < h && rows[j] >= 0)
             yv[b][j][q] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
-                static_cast<const char*>(yp) + (size_t(rows[j]) * h + c) * esz) + q);
+                static_cast<const char*>(yp) + (size_t(rows[j]) * h + c) * eszy) + q);
         }
     }
 #pragma unroll
@@ -167,7 +169,7 @@ __global__ void __launch_bounds__(256) rbwd_dlogits_kernel(
 #pragma unroll
       for (int j = 0; j < KM; ++j) {
         float y[8];
-        unpack8f<kF32>(yv[b][j], y);
+        unpack8f<kYF32>(yv[b][j], y);
 #pragma unroll
         for (int i = 0; i < 8; ++i) part[j] = fmaf(d[i], y[i], part[j]);
       }
@@ -655,15 +657,15 @@ size_t router_bwd_ws_bytes(int T, int h, int E) {
 
 size_t router_aux_ws_bytes(int T, int E) { return al256(size_t(ceil_div(T, kAuxTokens)) * E * 4); }
 
-template <bool kF32>
+template <bool kF32, bool kYF32>
 static void launch_dlogits(const void* dy, const void* yp, const int32_t* dst_row,
                            const int32_t* idx, const float* w, const float* logits,
                            const int32_t* counts, int T, int h, int E, int k, float alpha,
                            float* dL, hipStream_t s) {
   const dim3 grid(ceil_div(T, 4)), block(256);
-#define MOE_DL(KM)                                                                              \
-  hipLaunchKernelGGL((rbwd_dlogits_kernel<kF32, KM>), grid, block, 0, s, dy, yp, dst_row, idx, \
-                     w, logits, counts, T, h, E, k, alpha, dL)
+#define MOE_DL(KM)                                                                               \
+  hipLaunchKernelGGL((rbwd_dlogits_kernel<kF32, kYF32, KM>), grid, block, 0, s, dy, yp, dst_row, \
+                     idx, w, logits, counts, T, h, E, k, alpha, dL)
   if (k <= 1) MOE_DL(1);
   else if (k <= 2) MOE_DL(2);
   else if (k <= 4) MOE_DL(4);
@@ -672,7 +674,7 @@ static void launch_dlogits(const void* dy, const void* yp, const int32_t* dst_ro
 #undef MOE_DL
 }
 
-int router_bwd(const void* dy, const void* yp, const int32_t* dst_row, const int32_t* topk_idx,
+int router_bwd(const void* dy, const void* yp, int yp_dtype, const int32_t* dst_row, const int32_t* topk_idx,
                const float* topk_w, const float* logits, const int32_t* counts, int T, int h,
                int E, int k, float alpha, int dtype, const void* x, const void* w_gate,
                const float* dx_in, void* dx, float* dlogits, float* dw_gate, float* dbias,
@@ -684,8 +686,15 @@ int router_bwd(const void* dy, const void* yp, const int32_t* dst_row, const int
   w += al256(size_t(T) * E * 4);
 
   timer_begin(kTRouterBwd, s);
-  if (f32) launch_dlogits<true>(dy, yp, dst_row, topk_idx, topk_w, logits, counts, T, h, E, k, alpha, dL, s);
-  else launch_dlogits<false>(dy, yp, dst_row, topk_idx, topk_w, logits, counts, T, h, E, k, alpha, dL, s);
+  const bool yf32 = yp_dtype == MOE_F32;
+  if (f32 && yf32)
+    launch_dlogits<true, true>(dy, yp, dst_row, topk_idx, topk_w, logits, counts, T, h, E, k, alpha, dL, s);
+  else if (f32)
+    launch_dlogits<true, false>(dy, yp, dst_row, topk_idx, topk_w, logits, counts, T, h, E, k, alpha, dL, s);
+  else if (yf32)
+    launch_dlogits<false, true>(dy, yp, dst_row, topk_idx, topk_w, logits, counts, T, h, E, k, alpha, dL, s);
+  else
+    launch_dlogits<false, false>(dy, yp, dst_row, topk_idx, topk_w, logits, counts, T, h, E, k, alpha, dL, s);
   const size_t n = size_t(h) * E;
   if (f32) {
     const int nchunk = ceil_div(T, kDwTC);

@@ -89,9 +89,10 @@ def moe_grouped_workspace_size(rows, h, h_ffn, E, dtype):
     return lib().moe_grouped_workspace_size(rows, h, h_ffn, E, dtype)
 
 
-def moe_grouped_swiglu_fwd(xp, xp_scale, W, offsets, rows, h13_save, yp, ws, ws_bytes, stream=None):
+def moe_grouped_swiglu_fwd(xp, xp_scale, W, offsets, rows, h13_save, yp, yp_dtype, ws, ws_bytes,
+                           stream=None):
     return check(lib().moe_grouped_swiglu_fwd(_p(xp), _p(xp_scale), ctypes.byref(W), _p(offsets),
-                                              rows, _p(h13_save), _p(yp), _p(ws), ws_bytes,
+                                              rows, _p(h13_save), _p(yp), yp_dtype, _p(ws), ws_bytes,
                                               _s(stream)))
 
 
@@ -115,9 +116,9 @@ def moe_router_bwd_workspace_size(T, h, E):
     return lib().moe_router_bwd_workspace_size(T, h, E)
 
 
-def moe_router_bwd(dy, yp, dst_row, topk_idx, topk_w, logits, counts, T, h, E, k, alpha, dtype, x,
-                   w_gate, dx_in, dx, dlogits, dw_gate, dbias, ws, ws_bytes, stream=None):
-    return check(lib().moe_router_bwd(_p(dy), _p(yp), _p(dst_row), _p(topk_idx), _p(topk_w),
+def moe_router_bwd(dy, yp, yp_dtype, dst_row, topk_idx, topk_w, logits, counts, T, h, E, k, alpha,
+                   dtype, x, w_gate, dx_in, dx, dlogits, dw_gate, dbias, ws, ws_bytes, stream=None):
+    return check(lib().moe_router_bwd(_p(dy), _p(yp), yp_dtype, _p(dst_row), _p(topk_idx), _p(topk_w),
                                       _p(logits), _p(counts), T, h, E, k, float(alpha), dtype, _p(x),
                                       _p(w_gate), _p(dx_in), _p(dx), _p(dlogits), _p(dw_gate),
                                       _p(dbias), _p(ws), ws_bytes, _s(stream)))
@@ -191,9 +192,12 @@ class MoELayer:
 
     forward(): route -> permute (index + copy) -> grouped SwiGLU -> combine.
     backward(): weighted dispatch of dY -> grouped backward -> combine (dX).
+    The expert outputs Yp are kept in fp32 (``yp_dtype``; MOE_BF16 stores
+    them rounded, half the bytes).
     """
 
-    def __init__(self, T, h, h_ffn, E, k, dtype: int, device="cuda", save_for_backward=False):
+    def __init__(self, T, h, h_ffn, E, k, dtype: int, device="cuda", save_for_backward=False,
+                 yp_dtype: int = MOE_F32):
         self.T, self.h, self.h_ffn, self.E, self.k, self.dtype = T, h, h_ffn, E, k, dtype
         R = T * k
         self.R = R
@@ -215,7 +219,9 @@ class MoELayer:
         self.xp = torch.empty(R, h, dtype=xp_dt, device=dev)
         self.xp_scale = torch.empty(R, **f32) if dtype == MOE_FP8_E4M3 else None
         self.h13 = torch.empty(R, 2 * h_ffn, dtype=torch.bfloat16, device=dev) if save_for_backward else None
-        self.yp = torch.empty(R, h, dtype=io, device=dev)
+        self.yp_code = MOE_F32 if dtype == MOE_F32 else yp_dtype
+        self.yp = torch.empty(R, h, dtype=torch.float32 if self.yp_code == MOE_F32 else torch.bfloat16,
+                              device=dev)
         self.y = torch.empty(T, h, dtype=io, device=dev)
         self.gws_bytes = moe_grouped_workspace_size(R, h, h_ffn, E, dtype)
         self.gws = torch.empty(max(self.gws_bytes, 256), dtype=torch.uint8, device=dev)
@@ -245,8 +251,8 @@ class MoELayer:
                     self.dst_row, self.src_tok, self.xp, self.dtype, self.xp_scale, self.pws,
                     self.pws_bytes, stream)
         moe_grouped_swiglu_fwd(self.xp, self.xp_scale, W.struct, self.offsets, self.R, self.h13,
-                               self.yp, self.gws, self.gws_bytes, stream)
-        moe_combine(self.yp, self.io_code, self.dst_row, self.topk_w, T, h, k, self.y,
+                               self.yp, self.yp_code, self.gws, self.gws_bytes, stream)
+        moe_combine(self.yp, self.yp_code, self.dst_row, self.topk_w, T, h, k, self.y,
                     self.io_code, stream)
         return self.y
 
@@ -321,7 +327,7 @@ class MoELayer:
             self._alloc_router_bwd()
         # expert path in fp32, then the router path adds dL W_g^T and rounds once
         moe_combine(self.dxp, MOE_BF16, self.dst_row, None, T, h, k, self.dx_expert, MOE_F32, stream)
-        moe_router_bwd(dy, self.yp, self.dst_row, self.topk_idx, self.topk_w, self.logits_used,
+        moe_router_bwd(dy, self.yp, self.yp_code, self.dst_row, self.topk_idx, self.topk_w, self.logits_used,
                        self.counts, T, h, E, k, alpha, dtype_code(dy), x, w_gate, self.dx_expert,
                        self.dx, self.dlogits, self.dw_gate, self.dbias, self.rws, self.rws_bytes,
                        stream)

@@ -193,8 +193,9 @@ def expert_forward(xp, offsets, w1, w3, w2, keep=True, bf16_storage=False):
     """FC1 -> SwiGLU -> FC2 for every expert's contiguous rows (fp64).
 
     Returns ``yp`` and, when ``keep``, the intermediates ``g, u, a``.  With
-    ``bf16_storage`` the two values a BF16 layer stores between steps are
-    rounded to bf16 (nearest even): A before FC2, and Yp itself.
+    ``bf16_storage`` the value a BF16 layer stores between FC1 and FC2 is
+    rounded to bf16 (nearest even): A; Yp stays as computed (the layer keeps
+    it in fp32).
     """
     R = xp.shape[0]
     E = len(offsets) - 1
@@ -214,8 +215,6 @@ def expert_forward(xp, offsets, w1, w3, w2, keep=True, bf16_storage=False):
         if bf16_storage:
             a = round_bf16(a)
         yp[lo:hi] = a @ np.asarray(w2[e], np.float64)
-        if bf16_storage:
-            yp[lo:hi] = round_bf16(yp[lo:hi])
         if keep:
             g_all[lo:hi] = g; u_all[lo:hi] = u; a_all[lo:hi] = a
     if keep:
@@ -414,6 +413,18 @@ def quantize_rows(v: np.ndarray):
     return q, s
 
 
+def quantize_rows_exact(v: np.ndarray):
+    """Per-row quantization of exact (fp64) values, for A = SiLU(G) U.
+
+    ``s[r] = amax_c |v[r, c]| / 448`` and ``q = E4M3(v / s)``, both from the
+    fp64 values (1 for an all-zero row).  Returns codes uint8 and fp64 scales.
+    """
+    v = np.asarray(v, np.float64)
+    amax = np.max(np.abs(v), axis=-1) if v.shape[-1] else np.zeros(v.shape[:-1])
+    s = np.where(amax > 0, amax / E4M3_MAX, 1.0)
+    return e4m3_encode(v / s[..., None]), s
+
+
 def quantize_cols(wm: np.ndarray):
     """Per-output-channel quantization of a weight ``[in, out]`` (fp32 values).
 
@@ -425,21 +436,22 @@ def quantize_cols(wm: np.ndarray):
     return q, s
 
 
-def layer_forward_fp8(x, w_gate, bias, w1, w3, w2, k, logits=None, noise=None):
+def layer_forward_fp8(x, w_gate, bias, w1, w3, w2, k, logits=None, noise=None, quant_a=None):
     """Forward layer with FP8 GEMM inputs (quantization emulated exactly).
 
     x is quantized per token before the dispatch copy, so each routed row
     keeps its token's scale; W1, W3 per output channel over h, W2 per output
     channel over h_ffn; FC1 result = (q_x . q_w) * s_x * s_w; A is quantized
-    per routed row in the kernel's precision (its value rounded to fp32, the
-    fp32 scale amax / 448, codes of the fp32 quotient: ``quantize_rows``);
-    FC2 result = (q_a . q_w2) * s_a * s_w2.  ``noise(name, e, v)``, when
+    per routed row from its fp64 value (scale amax / 448 and the quotient in
+    fp64: ``quantize_rows_exact``); FC2 result = (q_a . q_w2) * s_a * s_w2.  ``noise(name, e, v)``, when
     given, replaces each value an implementation computes before rounding or
     quantizing it ("g", "u", "a"; "yp" for FC2's fp32 sum; "w" with e = -1
     for the gate weights), so that a test can evaluate nearby
-    implementations.
+    implementations; ``quant_a``, when given, replaces A's quantizer (a test
+    passes an fp32 one to emulate an implementation).
     """
     nz = noise if noise is not None else (lambda name, e, v: v)
+    qa_fn = quantize_rows_exact if quant_a is None else quant_a
     E = w1.shape[0]
     L = router_logits(x, w_gate, bias) if logits is None else np.asarray(logits, np.float32)
     idx, w = topk_softmax(L, k)
@@ -463,8 +475,8 @@ def layer_forward_fp8(x, w_gate, bias, w1, w3, w2, k, logits=None, noise=None):
         g = nz("g", e, (xe @ e4m3_decode(q1)) * sxp[lo:hi, None].astype(np.float64) * s1[None, :].astype(np.float64))
         u = nz("u", e, (xe @ e4m3_decode(q3)) * sxp[lo:hi, None].astype(np.float64) * s3[None, :].astype(np.float64))
         a = nz("a", e, silu(g) * u)
-        qa, sa = quantize_rows(a)
-        sa = sa.astype(np.float64)
+        qa, sa = qa_fn(a)
+        sa = np.asarray(sa, np.float64)
         yp[lo:hi] = nz("yp", e, (e4m3_decode(qa) @ e4m3_decode(q2)) * sa[:, None] * s2[None, :].astype(np.float64))
         a_all[lo:hi] = a; qa_all[lo:hi] = qa; sa_all[lo:hi] = sa
         g_all[lo:hi] = g; u_all[lo:hi] = u
@@ -495,8 +507,7 @@ def layer_forward_fp8_tokens(x_rows, idx_rows, w_rows, w1, w3, w2, wq_cache=None
         g = (xe @ e4m3_decode(q1)) * s1[None, :].astype(np.float64)
         u = (xe @ e4m3_decode(q3)) * s3[None, :].astype(np.float64)
         a = silu(g) * u
-        qa, sa = quantize_rows(a)
-        sa = sa.astype(np.float64)
+        qa, sa = quantize_rows_exact(a)
         ye = (e4m3_decode(qa) @ e4m3_decode(q2)) * sa[:, None] * s2[None, :].astype(np.float64)
         y[tt] += np.asarray(w_rows[tt, jj], np.float64)[:, None] * ye
     return y
@@ -735,6 +746,22 @@ def fp32_sum_gamma(n):
     return d * F32_U / (1.0 - d * F32_U)
 
 
+def swiglu_eval_bound(g_abs, u_abs, s, silu_abs, da_abs):
+    """Bounds of an fp32 evaluation of the SwiGLU terms, from magnitudes:
+    |G|, |U|, s = sigmoid(G), |SiLU(G)| = |G s| and |dA| (upper bounds of
+    them where G, U, dA are only known within a span).  The class bounded:
+    s = 1 / (1 + exp(-G)) with the exponential within (|G| + 4) u/2
+    relative and one rounding per operation, u = 2^-23.  Returns the bounds
+      A  = SiLU(G) U:                 4 u (1 + |G|) |SiLU(G)| |U|
+      dG = dA U s (1 + G (1 - s)):    6 u (1 + |G|)^2 |dA| |U| s
+      dU = dA SiLU(G):                4 u (1 + |G|) |dA| |SiLU(G)|
+    (the final rounding of each result to fp32 is not included)."""
+    a = 4.0 * F32_U * (1.0 + g_abs) * silu_abs * u_abs
+    dg = 6.0 * F32_U * (1.0 + g_abs) ** 2 * da_abs * u_abs * s
+    du = 4.0 * F32_U * (1.0 + g_abs) * da_abs * silu_abs
+    return a, dg, du
+
+
 def bf16_span(v, d):
     """Lowest and highest bf16 value that rounding any number within ``d``
     of ``v`` can give (rounding is monotone)."""
@@ -876,14 +903,15 @@ def fp8_backward_envelope(dy, x, w, dst_row, offsets, w1, w3, w2, g, u, g_err=No
         smax = sigmoid(ge + dG)                      # s(G') <= s(ge + dG)
         silu_max = np.abs(ge * s) + 1.1 * dG
         dabs = np.abs(da) + d_da
+        # the fp32 evaluation of the SwiGLU terms, at the spans' largest magnitudes
+        ev_a, ev_dg, ev_du = swiglu_eval_bound(gmax, umax, smax, silu_max, dabs)
         # A = SiLU(G) U before its bf16 rounding
         a0 = ge * s * ue
-        d_a = 1.1 * dG * umax + np.abs(ge * s) * dU + 4.0 * F32_U * (1.0 + gmax) * silu_max * umax
+        d_a = 1.1 * dG * umax + np.abs(ge * s) * dU + ev_a
         # dG, dU before their bf16 rounding
         fgo = ue * s * (1.0 + ge * (1.0 - s))
-        d_dg = d_da * np.abs(fgo) + dabs * (1.1 * dU + 0.55 * umax * dG) \
-            + 6.0 * F32_U * (1.0 + gmax) ** 2 * dabs * umax * smax
-        d_du = d_da * np.abs(ge * s) + dabs * 1.1 * dG + 4.0 * F32_U * (1.0 + gmax) * dabs * silu_max
+        d_dg = d_da * np.abs(fgo) + dabs * (1.1 * dU + 0.55 * umax * dG) + ev_dg
+        d_du = d_da * np.abs(ge * s) + dabs * 1.1 * dG + ev_du
         dg0, du0 = da * fgo, da * ge * s
         for n, v in (("d_da", d_da), ("d_dg", d_dg), ("d_du", d_du), ("d_a", d_a)):
             out[n][lo:hi] = v
@@ -926,51 +954,57 @@ def fp8_backward_envelope(dy, x, w, dst_row, offsets, w1, w3, w2, g, u, g_err=No
 
 
 # --------------------------------------------------------------------------
-# Allowance of the FP8 forward.  A is quantized per routed row from the value
-# an implementation forms in fp32 (SiLU(G) U from an fp32 FC1); the same
-# reasoning as for the backward bounds how far the result of any such
-# implementation can be from `layer_forward_fp8`'s.  The row scale follows
-# the row's amax continuously here (A is not rounded to bf16 first), so the
-# quantizer is bounded through the ends of the value interval and of the
-# scale interval: for a fixed scale the code is monotone in the value, and
-# for a fixed code the dequantized value is monotone in the scale.
+# Allowance of the FP8 forward.  The oracle quantizes A = SiLU(G) U per
+# routed row from its fp64 value; an implementation forms A in fp32 from an
+# fp32 FC1, takes the row's amax of that, rounds amax / 448 to an fp32 scale
+# and encodes the fp32 quotient.  Where an A value or the row's amax sits at a
+# rounding boundary the two choose different codes or scales, and the
+# allowance below bounds, per output element, how far any such implementation
+# can be from `layer_forward_fp8`.  For a fixed scale the code is monotone in
+# the value, and for a fixed code the dequantized value is monotone in the
+# scale, so the ends of the value and scale intervals decide.
 # --------------------------------------------------------------------------
 
 def rowq_spread_interval(vo, lo, hi):
-    """``quantize_rows`` of the fp32 values ``vo`` against every matrix with
-    elements in [lo, hi] (fp32 values, lo <= vo <= hi) and any fp32 scale the
-    row's amax can give.  Returns the dequantized values of ``vo`` and a
-    per-element bound on the distance to those of any such matrix."""
-    vo = np.asarray(vo, np.float32)
-    q, s = quantize_rows(vo)
-    qo = e4m3_decode(q) * s.astype(np.float64)[:, None]
-    lo = np.asarray(lo, np.float32); hi = np.asarray(hi, np.float32)
+    """``quantize_rows_exact`` of the fp64 values ``vo`` against the per-row
+    quantization of any matrix A' with entries in [lo, hi] (lo <= vo <= hi)
+    whose scale is amax(|A'|) / 448 rounded to fp32 and whose codes are those
+    of the fp32 quotients (each within 2^-24 relative of the exact one).
+    Returns the oracle's dequantized values and a per-element bound on the
+    distance to the dequantized values of any such A'."""
+    vo = np.asarray(vo, np.float64)
+    q, s = quantize_rows_exact(vo)
+    qo = e4m3_decode(q) * s[:, None]
+    lo = np.asarray(lo, np.float64); hi = np.asarray(hi, np.float64)
     straddle = (lo <= 0) & (hi >= 0)
-    m_lo = np.where(straddle, np.float32(0), np.minimum(np.abs(lo), np.abs(hi)))
+    m_lo = np.where(straddle, 0.0, np.minimum(np.abs(lo), np.abs(hi)))
     m_hi = np.maximum(np.abs(lo), np.abs(hi))
-    s_lo = quant_scale(m_lo.max(axis=1) if vo.shape[1] else np.zeros(vo.shape[0]))[:, None]
-    s_hi = quant_scale(m_hi.max(axis=1) if vo.shape[1] else np.zeros(vo.shape[0]))[:, None]
-
-    def mag(m, sc, sc_out):
-        return e4m3_decode(e4m3_encode((m / sc).astype(np.float32))) * sc_out.astype(np.float64)
-
-    lower = mag(m_lo, s_hi, s_lo)
-    upper = mag(m_hi, s_lo, s_hi)
+    r = 2.0 ** -24                                    # one fp32 rounding, relative
+    a_lo = m_lo.max(axis=1) if vo.shape[1] else np.zeros(vo.shape[0])
+    a_hi = m_hi.max(axis=1) if vo.shape[1] else np.zeros(vo.shape[0])
+    s_lo = (a_lo / E4M3_MAX * (1 - r))[:, None]
+    s_hi = (a_hi / E4M3_MAX * (1 + r))[:, None]
+    with np.errstate(divide="ignore", invalid="ignore"):
+        lower = e4m3_decode(e4m3_encode(m_lo / s_hi * (1 - r))) * s_lo
+        upper = e4m3_decode(e4m3_encode(np.where(s_lo > 0, m_hi / s_lo * (1 + r), E4M3_MAX))) * s_hi
     aq = np.abs(qo)
     spread = np.where(straddle, aq + upper, np.maximum(aq - lower, upper - aq))
-    return qo, np.maximum(spread, 0.0)
+    # a row that may be all zero (amax interval reaching 0): any scale, every
+    # dequantized magnitude at most amax(|A'|) * (1 + 1/16) (saturation aside)
+    crude = aq + m_hi.max(axis=1, initial=0.0)[:, None] * (1 + 2.0 ** -4) * (1 + 4 * r)
+    return qo, np.maximum(np.where(a_lo[:, None] > 0, spread, crude), 0.0)
 
 
 def fp8_forward_envelope(fw, w1, w3, w2, g_err=None, u_err=None, w_err=None):
     """Per-element allowance of `layer_forward_fp8` (its result ``fw``): a
     bound on |y - fw["y"]| for every implementation with an fp32 FC1 (G, U
     within ``g_err`` / ``u_err`` of fw's), A = SiLU(G) U in fp32, the row
-    quantization of that fp32 A, FC2 summed in fp32 (trees as for the
-    backward), Yp stored in bf16, and gate weights within ``w_err``, added in
-    fp32 and the sum rounded once (the rounding of the result itself, half a
-    bf16 ulp of y, is left to the caller; the rounding of the allowance is
-    included).  Returns y, yp (the stored bf16 Yp against fw's unrounded
-    one), and the bounds d_a (A before quantization, fp32 evaluation only,
+    quantization of that fp32 A (fp32 scale and quotient), FC2 summed in fp32
+    (trees as for the backward) and stored in fp32, and gate weights within
+    ``w_err``, added in fp32 and the sum rounded once (the rounding of the
+    result itself, half a bf16 ulp of y, is left to the caller; the rounding
+    of the allowance is included).  Returns y, yp (the stored Yp against
+    fw's), and the bounds d_a (A before quantization, fp32 evaluation only,
     per routed row) and d_yp (FC2's own fp32 sum)."""
     g, u = np.asarray(fw["g"], np.float64), np.asarray(fw["u"], np.float64)
     R, hf = g.shape
@@ -990,20 +1024,19 @@ def fp8_forward_envelope(fw, w1, w3, w2, g_err=None, u_err=None, w_err=None):
         umax = np.abs(ue) + du
         silu_max = np.abs(silu(ge)) + 1.1 * dg
         a0 = silu(ge) * ue
-        d_eval = 4.0 * F32_U * (1.0 + np.abs(ge) + dg) * silu_max * umax + F32_U * np.abs(a0)
+        # fp32 evaluation of SiLU(G) U at the largest magnitudes, and the
+        # rounding of A itself to fp32
+        ev_a, _, _ = swiglu_eval_bound(np.abs(ge) + dg, umax, 0.0, silu_max, 0.0)
+        d_eval = ev_a + F32_U * np.abs(a0)
         d_a = 1.1 * dg * umax + silu_max * du + d_eval
         out["d_a"][lo:hi] = d_eval
-        a_lo = (a0 - d_a).astype(np.float32); a_hi = (a0 + d_a).astype(np.float32)
-        qa, sp = rowq_spread_interval(a0.astype(np.float32), np.minimum(a_lo, a0.astype(np.float32)),
-                                      np.maximum(a_hi, a0.astype(np.float32)))
+        qa, sp = rowq_spread_interval(a0, a0 - d_a, a0 + d_a)
         q2, s2 = quantize_cols(np.asarray(w2[e], np.float32))
         b2 = e4m3_decode(q2) * s2.astype(np.float64)[None, :]          # [hf, h]
         d_c = product_spread(qa, sp, b2.T, np.zeros_like(b2.T), hf)
         out["d_yp"][lo:hi] = fp32_sum_gamma(hf + 2) * ((np.abs(qa) + sp) @ np.abs(b2))
-        c = qa @ b2
-        st_l, st_h = bf16_span(c, d_c)
-        ypo = np.asarray(fw["yp"], np.float64)[lo:hi]
-        dev[lo:hi] = np.maximum(np.abs(st_h - ypo), np.abs(ypo - st_l))
+        # Yp is stored in fp32: the rescaled fp32 sum itself
+        dev[lo:hi] = d_c
     out["yp"] = dev
     w = np.asarray(fw["w"], np.float64)
     w_err = np.zeros(w.shape) if w_err is None else np.asarray(w_err, np.float64)

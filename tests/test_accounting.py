@@ -67,7 +67,7 @@ def test_row_mover_launch_bytes():
     T, h, k = 8192, 4096, 2
     R = T * k
     assert c["permute_launches"] == [T * h * 2 + R * h * 2 + 4 * R]          # x read, k copies, dst_row
-    assert c["combine_launches"] == [R * h * 2 + T * h * 2 + 8 * R]          # rows, y, dst_row + w
+    assert c["combine_launches"] == [R * h * 4 + T * h * 2 + 8 * R]          # fp32 rows, y, dst_row + w
     wl = moe_synth.WORKLOADS["dsmoe"]
     c = acc.workload_counts(wl)
     T, h, k = 16384, 2048, 6
@@ -75,7 +75,7 @@ def test_row_mover_launch_bytes():
     x_fwd = T * h * 2 + R * h * 2 + 4 * R
     dy = x_fwd + 4 * R                       # the gate weights as row scales
     assert c["permute_launches"] == [x_fwd, dy, x_fwd]                      # x, dY, x re-gathered
-    assert c["combine_launches"] == [R * h * 2 + T * h * 2 + 8 * R,          # y
+    assert c["combine_launches"] == [R * h * 4 + T * h * 2 + 8 * R,          # y from fp32 Yp
                                      R * h * 2 + T * h * 4 + 4 * R]          # dX in fp32, no weights
     c8 = acc.workload_counts(moe_synth.WORKLOADS["dsmoe_fp8"])
     x_fp8 = T * h * 2 + R * h * 1 + 4 * R + 4 * R                          # codes + a scale per row

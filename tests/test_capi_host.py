@@ -79,8 +79,8 @@ def test_grouped_validation():
     need = lib.moe_grouped_workspace_size(512, 256, 384, 8, L.MOE_BF16)
     assert need >= 512 * 384 * 2
 
-    def call(W=W, rows=512, ws=A, wsb=need, save=None, scale=None):
-        return lib.moe_grouped_swiglu_fwd(A, scale, ctypes.byref(W), A, rows, save, A, ws, wsb, None)
+    def call(W=W, rows=512, ws=A, wsb=need, save=None, scale=None, ypdt=L.MOE_F32):
+        return lib.moe_grouped_swiglu_fwd(A, scale, ctypes.byref(W), A, rows, save, A, ypdt, ws, wsb, None)
     assert call(wsb=need - 1) == L.MOE_ERR_WORKSPACE
     assert call(rows=-1) == L.MOE_ERR_ARG
     assert call(rows=0) == L.MOE_OK
@@ -88,6 +88,9 @@ def test_grouped_validation():
     assert call(W=bad) == L.MOE_ERR_SHAPE
     bad = L.MoeWeights(7, 8, 256, 384, A.value, A.value, None, None)
     assert call(W=bad) == L.MOE_ERR_DTYPE
+    assert call(ypdt=L.MOE_FP8_E4M3) == L.MOE_ERR_DTYPE
+    f32w = L.MoeWeights(L.MOE_F32, 8, 256, 384, A.value, A.value, None, None)
+    assert call(W=f32w, ypdt=L.MOE_BF16) == L.MOE_ERR_DTYPE   # fp32 weights keep fp32 outputs
     f8 = L.MoeWeights(L.MOE_FP8_E4M3, 8, 256, 384, A.value, A.value, None, None)
     assert call(W=f8) == L.MOE_ERR_ARG                    # fp8 weights need scales
     f32 = L.MoeWeights(L.MOE_F32, 8, 256, 384, A.value, A.value, None, None)
@@ -130,13 +133,13 @@ def test_router_bwd_validation():
     T, h, E, k = 100, 128, 8, 2
     need = lib.moe_router_bwd_workspace_size(T, h, E)
     assert need > 0 and lib.moe_router_bwd_workspace_size(0, h, E) == 0
-    ok = dict(dy=A, yp=A, dst=A, idx=A, w=A, lg=A, cnt=A, T=T, h=h, E=E, k=k, alpha=0.01,
+    ok = dict(dy=A, yp=A, ypdt=L.MOE_F32, dst=A, idx=A, w=A, lg=A, cnt=A, T=T, h=h, E=E, k=k, alpha=0.01,
               dt=L.MOE_BF16, x=A, wg=A, dxin=None, dx=ctypes.c_void_p(2 << 20), dl=None, dwg=A, db=None,
               ws=A, wsb=need)
 
     def call(**kw):
         a = {**ok, **kw}
-        return lib.moe_router_bwd(a["dy"], a["yp"], a["dst"], a["idx"], a["w"], a["lg"], a["cnt"], a["T"],
+        return lib.moe_router_bwd(a["dy"], a["yp"], a["ypdt"], a["dst"], a["idx"], a["w"], a["lg"], a["cnt"], a["T"],
                                   a["h"], a["E"], a["k"], a["alpha"], a["dt"], a["x"], a["wg"], a["dxin"],
                                   a["dx"], a["dl"], a["dwg"], a["db"], a["ws"], a["wsb"], None)
     assert call(T=-1) == L.MOE_ERR_ARG
@@ -144,6 +147,7 @@ def test_router_bwd_validation():
     assert call(E=0) == L.MOE_ERR_SHAPE
     assert call(h=96) == L.MOE_ERR_SHAPE
     assert call(dt=L.MOE_FP8_E4M3) == L.MOE_ERR_DTYPE
+    assert call(ypdt=L.MOE_FP8_E4M3) == L.MOE_ERR_DTYPE
     assert call(alpha=float("nan")) == L.MOE_ERR_ARG
     assert call(dwg=None) == L.MOE_ERR_ARG
     assert call(dxin=U) == L.MOE_ERR_ARG

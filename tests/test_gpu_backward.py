@@ -1,12 +1,17 @@
 """GPU parity of the backward (dX, dW1, dW3, dW2) against the CPU oracle.
 
 Routing is fed the oracle's fp32 logits so every token is compared.  Two
-checks per tensor, both at the 2e-2 * rms(ref) max-norm bar:
-  * against the oracle with BF16 matrix-product operands (dYp, the kept
-    G|U, A, dG, dU and dXp rounded to BF16, as a BF16 step holds them), plus
-    half a bf16 ulp for dX's own output rounding;
-  * against the exact fp64 oracle, allowing per element the distance between
-    the exact and the BF16-operand results (what BF16 storage alone costs).
+checks per tensor:
+  * max-norm, 2e-2 * rms(ref), against the oracle with BF16 matrix-product
+    operands (dYp, the kept G|U, A, dG, dU and dXp rounded to BF16, as a BF16
+    step holds them), plus half a bf16 ulp for dX's own output rounding;
+  * rms, against the exact fp64 oracle: rms(got - exact) <= 1e-2 * rms(exact)
+    (EXACT_RMS).  Rounding those operands to BF16 alone puts the BF16-operand
+    oracle 2.5-3.5e-3 rms from the exact result on these shapes (each stored
+    operand moves by ~2^-9/sqrt(3) relative rms, and a gradient passes
+    through three or four of them), so the bar leaves about 3x for the fp32
+    sums; one wrong row among M of an expert moves its dW by ~sqrt(2/M) rms
+    (0.03 at M = 2000), and a dropped term by more.
 """
 import numpy as np
 import pytest
@@ -16,7 +21,9 @@ import moe_synth
 from moe_synth import to_f32
 from oracle import moe_ref as ref
 
-from test_gpu_parity import DEV, HALF_ULP_BF16, check_close, dev_tensor, host, say, _PerExpert
+from test_gpu_parity import DEV, HALF_ULP_BF16, check_close, check_rms, dev_tensor, host, say, _PerExpert
+
+EXACT_RMS = 1e-2
 
 pytestmark = pytest.mark.gpu
 
@@ -62,9 +69,8 @@ def test_backward(case, over, seed):
            "dw2": layer.dw2.cpu().numpy()}
     for name in ("dx", "dw1", "dw3", "dw2"):
         out_round = HALF_ULP_BF16 * np.abs(emu[name]) if name == "dx" else None
-        check_close(got[name], emu[name], 2e-2, out_round, None, name + " vs bf16-operand oracle")
-        dist = np.abs(emu[name] - bw[name]) + (0 if out_round is None else out_round)
-        check_close(got[name], bw[name], 2e-2, dist, None, name + " vs exact oracle")
+        check_close(got[name], emu[name], 2e-2, None, None, name + " vs bf16-operand oracle", rounding=out_round)
+        check_rms(got[name], bw[name], EXACT_RMS, name + " vs exact oracle")
     # experts without rows get exactly zero gradients
     empty = np.nonzero(fw["counts"] == 0)[0]
     for e in empty:
@@ -110,7 +116,7 @@ def test_full_size_dsmoe_backward_sampled():
         for q, name in enumerate(("dw1", "dw3", "dw2")):
             got = getattr(layer, name)[e].cpu().numpy()
             check_close(got, em[q], 2e-2, None, None, f"{name}[{e}] vs bf16-operand oracle")
-            check_close(got, ex[q], 2e-2, np.abs(em[q] - ex[q]), None, f"{name}[{e}] vs exact oracle")
+            check_rms(got, ex[q], EXACT_RMS, f"{name}[{e}] vs exact oracle")
     # dX of sampled tokens
     toks = np.sort(np.random.default_rng(5).choice(wl.T, 48, replace=False))
     targs = (dy32[toks], x32[toks], idx[toks], w[toks], W1, W3, W2)
@@ -118,8 +124,8 @@ def test_full_size_dsmoe_backward_sampled():
     dx_em = ref.layer_backward_tokens(*targs, bf16_operands=True)
     got = host(layer.dx)[toks]
     out_round = HALF_ULP_BF16 * np.abs(dx_em)
-    check_close(got, dx_em, 2e-2, out_round, None, "dX sampled vs bf16-operand oracle")
-    check_close(got, dx_ex, 2e-2, np.abs(dx_em - dx_ex) + out_round, None, "dX sampled vs exact oracle")
+    check_close(got, dx_em, 2e-2, None, None, "dX sampled vs bf16-operand oracle", rounding=out_round)
+    check_rms(got, dx_ex, EXACT_RMS, "dX sampled vs exact oracle")
 
 
 @pytest.mark.slow
@@ -130,7 +136,7 @@ def test_full_size_dsmoe_training_step_sampled():
     checked through properties that hold at any size; the balance loss
     exactly; the total dX of sampled tokens against the oracle, as in the
     small layer tests (bf16-storage oracle at the bar, exact oracle with the
-    storage distance allowed)."""
+    rms bar)."""
     alpha = 0.01
     wl = moe_synth.WORKLOADS["dsmoe"]
     say("full-size dsmoe training step: generating inputs")
@@ -156,7 +162,8 @@ def test_full_size_dsmoe_training_step_sampled():
     check_close(layer.dbias.cpu().numpy(), dL.sum(axis=0), 1e-4, None, None, "d(bias) = column sums of dL")
     check_close(layer.dw_gate.cpu().numpy(), x32.astype(np.float64).T @ dL, 1e-4, None, None, "dW_g = x^T dL")
     want = layer.dx_expert.cpu().numpy().astype(np.float64) + dL @ wg32.astype(np.float64).T
-    check_close(host(layer.dx), want, 1e-4, HALF_ULP_BF16 * np.abs(want), None, "dX = expert part + dL W_g^T")
+    check_close(host(layer.dx), want, 1e-4, None, None, "dX = expert part + dL W_g^T",
+                rounding=HALF_ULP_BF16 * np.abs(want))
     # sampled tokens: total dX against the oracle
     toks = np.sort(np.random.default_rng(6).choice(wl.T, 32, replace=False))
     W1, W3, W2 = (_PerExpert(inp[n]) for n in ("w1", "w3", "w2"))
@@ -179,5 +186,5 @@ def test_full_size_dsmoe_training_step_sampled():
         res[st] = ref.layer_backward_tokens(*targs, bf16_operands=st) + rb["dx"]
     got = host(layer.dx)[toks]
     out_round = HALF_ULP_BF16 * np.abs(res[True])
-    check_close(got, res[True], 2e-2, out_round, None, "dX sampled vs bf16-storage oracle")
-    check_close(got, res[False], 2e-2, np.abs(res[True] - res[False]) + out_round, None, "dX sampled vs exact oracle")
+    check_close(got, res[True], 2e-2, None, None, "dX sampled vs bf16-storage oracle", rounding=out_round)
+    check_rms(got, res[False], EXACT_RMS, "dX sampled vs exact oracle")

@@ -6,8 +6,9 @@ bit-exact against the oracle's share (local_expert_ids + build_index); each
 share runs its own GroupedGEMM on its slice of the weights and a partial
 combine in fp32; the four partials added together (the reduce-scatter's sum,
 done here on the host as a stand-in for the collective) must match the
-oracle's layer output within the bf16 layer bar (2e-2 * rms plus half a bf16
-ulp of every stored expert output).  Routing is fed the oracle's fp32 logits.
+oracle's layer output within the bf16 layer bar (2e-2 * rms; the expert
+outputs and the partial sums are fp32).  Routing is fed the oracle's fp32
+logits.
 """
 import numpy as np
 import pytest
@@ -17,7 +18,7 @@ import moe_synth
 from moe_synth import to_f32
 from oracle import moe_ref as ref
 
-from test_gpu_parity import DEV, HALF_ULP_BF16, check_close, dev_tensor, host, say
+from test_gpu_parity import DEV, check_close, dev_tensor, host, say
 
 pytestmark = pytest.mark.gpu
 
@@ -37,7 +38,6 @@ def test_expert_parallel_shares(T, h, hf, E, k, n):
     idx = torch.from_numpy(fw["idx"].astype(np.int32)).to(DEV)
     w = torch.from_numpy(fw["w"].astype(np.float32)).to(DEV)
     total = np.zeros((T, h))
-    yabs = np.zeros((T, h))
     for r in range(n):
         e_lo, e_cnt = r * E // n, (r + 1) * E // n - r * E // n
         say(f"share {r}: experts [{e_lo}, {e_lo + e_cnt})")
@@ -61,17 +61,14 @@ def test_expert_parallel_shares(T, h, hf, E, k, n):
         sl = slice(e_lo, e_lo + e_cnt)
         P = ops.PackedWeights(dev_tensor(inp["w1"][sl]), dev_tensor(inp["w3"][sl]), dev_tensor(inp["w2"][sl]),
                               MOE_BF16)
-        yp = torch.empty(max(rows, 1), h, dtype=torch.bfloat16, device=DEV)
+        yp = torch.empty(max(rows, 1), h, dtype=torch.float32, device=DEV)
         gwsb = ops.moe_grouped_workspace_size(max(rows, 1), h, hf, e_cnt, MOE_BF16)
         gws = torch.empty(gwsb, dtype=torch.uint8, device=DEV)
         if rows:
-            ops.moe_grouped_swiglu_fwd(xp, None, P.struct, offsets, rows, None, yp, gws, gwsb)
+            ops.moe_grouped_swiglu_fwd(xp, None, P.struct, offsets, rows, None, yp, MOE_F32, gws, gwsb)
         part = torch.empty(T, h, dtype=torch.float32, device=DEV)
-        ops.moe_combine(yp, MOE_BF16, dst_row, w, T, h, k, part, MOE_F32)
+        ops.moe_combine(yp, MOE_F32, dst_row, w, T, h, k, part, MOE_F32)
         torch.cuda.synchronize()
         total += part.cpu().numpy()
-        if rows:
-            yp_ref = ref.expert_forward(ref.permute(f("x"), d_r)[:rows], o_r, f("w1")[sl], f("w3")[sl],
-                                        f("w2")[sl], keep=False)
-            yabs += np.abs(ref.combine(np.abs(yp_ref), d_r, np.abs(fw["w"])))
-    check_close(total, fw["y"], 2e-2, HALF_ULP_BF16 * yabs, None, "sum of the shares' partial outputs")
+    # expert outputs and partial sums in fp32: the plain bar
+    check_close(total, fw["y"], 2e-2, None, None, "sum of the shares' partial outputs")

@@ -6,13 +6,13 @@ end-to-end outputs within 2e-2 * rms(ref) (bf16) on tokens whose k-th vs
 (k+1)-th logit margin exceeds 1e-3; FP8 within 6e-2 * rms(ref) of the
 quantization-emulating oracle.
 
-The rms bars bound the arithmetic.  Each value the pipeline stores in bf16
-(the expert outputs Yp, and y itself when the output is bf16) is in addition
-rounded to nearest, which moves it by at most 2^-8 of its own magnitude;
-that allowance is added per element from the oracle's own values
-(``storage_allowance``).  Without it the bar is below the output format's
-rounding: outputs reach 5x rms, and rounding such a value to bf16 alone
-moves it by ~2e-2 * rms.
+The rms bars bound the arithmetic.  The expert outputs Yp are kept in fp32;
+when y itself is bf16, its own rounding to nearest (at most 2^-8 of its
+magnitude) is allowed per element (``y_rounding``): outputs reach 5x rms, and
+rounding such a value to bf16 alone moves it by ~2e-2 * rms.  Every check
+also counts the elements whose pass needed an allowance (plain error above
+the bar) and fails when more than a stated small fraction did, so that a
+misplaced row cannot hide inside an allowance.
 """
 import os
 import sys
@@ -55,34 +55,57 @@ def host(t):
 HALF_ULP_BF16 = 2.0 ** -8
 
 
-def storage_allowance(r, out_bf16=True, yp_bf16=True):
-    """Worst-case effect of bf16 stores of Yp (and of y) on each output element."""
-    a = np.zeros_like(r["y"])
-    if yp_bf16:
-        for j in range(r["dst_row"].shape[1]):
-            a += np.abs(r["w"][:, j:j + 1].astype(np.float64)) * np.abs(r["yp"][r["dst_row"][:, j]])
-    if out_bf16:
-        a += np.abs(r["y"])
-    return HALF_ULP_BF16 * a
+def y_rounding(y):
+    """Half a bf16 ulp of each output value: its own rounding to bf16."""
+    return HALF_ULP_BF16 * np.abs(y)
 
 
-def check_close(got, want, frac, allowance=None, mask=None, what=""):
-    """max |got - want| - allowance <= frac * rms(want); returns the worst ratio."""
+# At most this fraction of a check's elements may need its allowance (plain
+# |err| above the bar).  A misplaced or dropped routed row moves every one of
+# its token's h outputs by about rms(ref), far outside any allowance here,
+# and is 1/T of the elements or more; the values whose own bf16 rounding or
+# quantization boundary the allowances cover are rare (|y| > ~4 rms, or an
+# FP8 code at a rounding tie).
+MAX_NEED = 1e-3
+
+
+def check_close(got, want, frac, allowance=None, mask=None, what="", max_need=MAX_NEED, rounding=None):
+    """max(|got - want| - rounding - allowance) <= frac * rms(want), where
+    ``rounding`` is the output's own rounding to its storage type (allowed
+    everywhere) and ``allowance`` any other per-element allowance; at most a
+    fraction ``max_need`` of the elements may have |got - want| - rounding
+    above frac * rms(want) (they passed only through the allowance).  Prints
+    the plain max and rms errors.  Returns the worst ratio."""
     if mask is not None:
         got, want = got[mask], want[mask]
         allowance = None if allowance is None else allowance[mask]
+        rounding = None if rounding is None else rounding[mask]
     rms = np.sqrt(np.mean(np.square(want, dtype=np.float64)))
-    excess = np.abs(got.astype(np.float64) - want) - (0 if allowance is None else allowance)
+    err = np.abs(got.astype(np.float64) - want)
+    err_r = err - (0 if rounding is None else rounding)
+    excess = err_r - (0 if allowance is None else allowance)
     if rms == 0:
         # an all-zero reference (e.g. the router gradient with one expert) is matched exactly
         say(f"  {what}: reference is zero; max|got| = {np.abs(got).max():.3e}")
         assert not np.any(got), what
         return 0.0
     worst = excess.max() / rms
-    say(f"  {what} (max|err| - allowance)/rms = {worst:.3e} (bar {frac:g}); plain max|err|/rms = "
-        f"{np.abs(got.astype(np.float64) - want).max() / rms:.3e}")
+    need = int(np.count_nonzero(err_r > frac * rms))
+    say(f"  {what}: (max|err| - allowance)/rms = {worst:.3e} (bar {frac:g}); plain max|err|/rms = "
+        f"{err.max() / rms:.3e}, rms err/rms = {np.sqrt(np.mean(err ** 2)) / rms:.3e}; "
+        f"{need} of {err.size} elements needed the allowance")
     assert worst <= frac, what
+    assert need <= max_need * err.size, f"{what}: {need} of {err.size} elements needed the allowance"
     return worst
+
+
+def check_rms(got, want, frac, what=""):
+    """rms(got - want) <= frac * rms(want)."""
+    rms = np.sqrt(np.mean(np.square(want, dtype=np.float64)))
+    r = np.sqrt(np.mean(np.square(got.astype(np.float64) - want))) / rms
+    say(f"  {what}: rms err/rms = {r:.3e} (bar {frac:g})")
+    assert r <= frac, what
+    return r
 
 
 def rel_err(got, want, mask=None):
@@ -377,7 +400,7 @@ def test_layer_forward(case, over, seed):
     np.testing.assert_array_equal(layer.topk_idx.cpu().numpy()[keep], r["idx"][keep])
     np.testing.assert_array_equal(layer.counts.cpu().numpy().sum(), wl.T * wl.k)
     bf = wl.dtype == "bf16"
-    check_close(host(layer.y), r["y"], 2e-2, storage_allowance(r, bf, bf), keep, "y")
+    check_close(host(layer.y), r["y"], 2e-2, None, keep, "y", rounding=y_rounding(r["y"]) if bf else None)
 
 
 @pytest.mark.parametrize("case,over,seed", LAYER_CASES[:5], ids=[c[0] for c in LAYER_CASES[:5]])
@@ -392,16 +415,15 @@ def test_layer_forward_logits_mode(case, over, seed):
     np.testing.assert_array_equal(layer.offsets.cpu().numpy(), r["offsets"])
     bf = wl.dtype == "bf16"
     say(f"layer logits-mode {case}")
-    check_close(host(layer.y), r["y"], 2e-2, storage_allowance(r, bf, bf), None, "y")
-    # expert outputs before the combine, row by row
+    check_close(host(layer.y), r["y"], 2e-2, None, None, "y", rounding=y_rounding(r["y"]) if bf else None)
+    # expert outputs before the combine (fp32), row by row: the plain bar
     R = wl.T * wl.k
-    check_close(host(layer.yp)[:R], r["yp"], 2e-2, HALF_ULP_BF16 * np.abs(r["yp"]) if bf else None,
-                None, "Yp")
+    check_close(host(layer.yp)[:R], r["yp"], 2e-2, None, None, "Yp")
     if bf:
-        # same layer with an fp32 output: only the Yp store is rounded
+        # same layer with an fp32 output: nothing is rounded to bf16 after FC2
         y32 = torch.empty(wl.T, wl.h, dtype=torch.float32, device=DEV)
-        ops.moe_combine(layer.yp, MOE_BF16, layer.dst_row, layer.topk_w, wl.T, wl.h, wl.k, y32, MOE_F32)
-        check_close(y32.cpu().numpy(), r["y"], 2e-2, storage_allowance(r, False, True), None, "y fp32")
+        ops.moe_combine(layer.yp, MOE_F32, layer.dst_row, layer.topk_w, wl.T, wl.h, wl.k, y32, MOE_F32)
+        check_close(y32.cpu().numpy(), r["y"], 2e-2, None, None, "y fp32")
 
 
 @pytest.mark.parametrize("over,seed", [(dict(T=300, h=256, h_ffn=384, E=8, k=1, dtype="fp8"), 8),
@@ -416,19 +438,54 @@ def test_layer_forward_fp8(over, seed):
     check_fp8_forward(layer, wl, r, f)
 
 
+def test_layer_forward_fp8_hand_case():
+    """The FP8 layer worked out by hand (tests/golden/fp8_hand_case.json),
+    zero-padded to h = h_ffn = 128.  Every value of it is exact in fp32 as
+    well (power-of-two weight scales, SiLU(G) = G in fp32 for G >= 49), so
+    the GPU must reproduce it exactly: the dispatched x codes and per-token
+    scales, Yp (kept in fp32) value for value, including A's round-up
+    (280 -> 288) and its tie to the even code (168 -> 160), and y as Yp
+    rounded once to bf16.  The padding stays zero."""
+    import json
+    with open(os.path.join(os.path.dirname(__file__), "golden", "fp8_hand_case.json")) as fh:
+        g = json.load(fh)
+    T, h, hf = 2, 128, 128
+    x = np.zeros((T, h), np.float32); x[:, :4] = g["x"]
+    w1 = np.zeros((1, h, hf), np.float32); w1[0, :4, :2] = g["w1"]
+    w3 = np.zeros((1, h, hf), np.float32); w3[0, :4, :2] = g["w3"]
+    w2 = np.zeros((1, hf, h), np.float32); w2[0, :2, :4] = g["w2"]
+    b = moe_synth.f32_to_bf16_bits
+    assert np.array_equal(to_f32(b(x)), x) and np.array_equal(to_f32(b(w1)), w1)
+    inp = dict(x=b(x), w1=b(w1), w3=b(w3), w2=b(w2), w_gate=b(np.zeros((h, 1), np.float32)),
+               bias=np.zeros(1, np.float32))
+    wl = moe_synth.Workload("fp8_hand", T, h, hf, 1, 1, "fp8")
+    layer, _ = _run_gpu_layer(wl, inp, logits_in=np.zeros((T, 1), np.float32))
+    xq = layer.xp.cpu().numpy()[:T]
+    np.testing.assert_array_equal(xq[:, :4], np.array(g["x_codes"], np.uint8))
+    assert not xq[:, 4:].any()
+    np.testing.assert_array_equal(layer.xp_scale.cpu().numpy()[:T], np.array(g["x_scale"], np.float32))
+    yp = layer.yp.cpu().numpy()[:T]
+    np.testing.assert_array_equal(yp[:, :4], np.array(g["yp"], np.float32))
+    assert not yp[:, 4:].any()
+    y = host(layer.y)
+    np.testing.assert_array_equal(y[:, :4], ref.round_bf16(np.array(g["y"])))
+    assert not y[:, 4:].any()
+
+
 def check_fp8_forward(layer, wl, r, f):
-    """y of the FP8 forward against the quantization-emulating oracle: the FP8
-    bar (6e-2 * rms) once the oracle's allowance for fp32 implementations is
-    granted (A is quantized from an fp32 value, so a code or a row scale may
-    differ where that value sits at a rounding boundary; Yp stored in bf16),
-    plus half a bf16 ulp of y's own rounding; rms error below 1e-2 * rms."""
+    """y of the FP8 forward against the quantization-emulating oracle (A
+    quantized from its fp64 value): the FP8 bar (6e-2 * rms) once the
+    oracle's allowance for fp32 implementations is granted (the GPU forms A
+    in fp32 and quantizes it with an fp32 scale and quotient, so a code or a
+    row scale may differ where A or the row's amax sits at a rounding
+    boundary), plus half a bf16 ulp of y's own rounding, with few elements
+    needing the allowance; rms error below 1e-2 * rms."""
     g_err, u_err = ref.fp8_forward_gu_bound(f("x"), r["dst_row"], r["offsets"], f("w1"), f("w3"))
     env = ref.fp8_forward_envelope(r, f("w1"), f("w3"), f("w2"), g_err, u_err,
                                    ref.topk_weight_bound(r["logits"], r["idx"]))
     got = host(layer.y)
-    check_close(got, r["y"], 6e-2, env["y"] + HALF_ULP_BF16 * np.abs(r["y"]), None, "y fp8")
-    rms = np.sqrt(np.mean(r["y"] ** 2))
-    assert np.sqrt(np.mean((got - r["y"]) ** 2)) <= 1e-2 * rms
+    check_close(got, r["y"], 6e-2, env["y"], None, "y fp8", rounding=y_rounding(r["y"]))
+    check_rms(got, r["y"], 1e-2, "y fp8")
 
 
 def test_layer_deterministic():
@@ -473,15 +530,8 @@ def _full_size_sampled(name, n_sample=48, seed=0):
     w1, w3, w2 = (_PerExpert(inp[n]) for n in ("w1", "w3", "w2"))
     y_ref = fn(xs[keep], ri[keep], rw[keep], w1, w3, w2)
     y_gpu = host(layer.y)[toks][keep]
-    # storage allowance without per-row Yp values: bound |Yp_j| by the
-    # per-token expert outputs recomputed one expert at a time
-    yp_abs = np.zeros_like(y_ref)
-    for j in range(wl.k):
-        yj = fn(xs[keep], ri[keep][:, j:j + 1], np.ones((int(keep.sum()), 1), np.float32), w1, w3, w2)
-        yp_abs += np.abs(rw[keep][:, j:j + 1].astype(np.float64)) * np.abs(yj)
-    allow = HALF_ULP_BF16 * (yp_abs + np.abs(y_ref))
     frac = 2e-2 if wl.dtype == "bf16" else 6e-2
-    return check_close(y_gpu, y_ref, frac, allow, None, f"full-size {name} y"), layer
+    return check_close(y_gpu, y_ref, frac, None, None, f"full-size {name} y", rounding=y_rounding(y_ref)), layer
 
 
 @pytest.mark.slow
@@ -527,5 +577,5 @@ def test_full_size_hunyuan_fp8_sampled():
     y_ref = ref.layer_forward_fp8_tokens(x32(toks), ri[toks], rw[toks], _PerExpert(inp["w1"]),
                                          _PerExpert(inp["w3"]), _PerExpert(inp["w2"]), cols=cols)
     y_gpu = host(layer.y)[toks][:, cols]
-    # k = 1: y is the bf16 expert output itself, one bf16 rounding
-    check_close(y_gpu, y_ref, 6e-2, HALF_ULP_BF16 * np.abs(y_ref), None, "full-size fp8 y")
+    # k = 1: y is the expert output rounded once to bf16
+    check_close(y_gpu, y_ref, 6e-2, None, None, "full-size fp8 y", rounding=y_rounding(y_ref))

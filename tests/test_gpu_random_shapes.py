@@ -6,13 +6,14 @@ Shapes are drawn per seed: T from 1 to 700, h and h_ffn in {128, 256, 384}
 (one to three 128-wide blocks, so tiles end ragged in every dimension), E from
 1 to 47, k from 1 to min(E, 8), with or without a Zipf router bias (experts
 without rows appear).  The bars are those of the fixed-shape tests: routing,
-index and dispatch bit-exact; y and the gradients within 2e-2 * rms of the
-oracle with BF16 storage / operands, with the storage distance allowed against
-the exact oracle; against the BF16-operand oracle the weight gradients also
-allow, per element, the largest change one operand rounded to the
-neighbouring BF16 value makes (`bf16_flip`: an fp32 and an fp64 value on either
-side of a BF16 rounding boundary; seeds 48, 91, 132 and 134 are shapes where
-that happened), in both checks; the FP8 forward at 6e-2 * rms with the oracle's allowance
+index and dispatch bit-exact; y within 2e-2 * rms of the oracle (plus y's
+own bf16 rounding); the gradients within 2e-2 * rms (max-norm) of the oracle
+with BF16 operands and within 1e-2 * rms (rms) of the exact oracle; against
+the BF16-operand oracle the weight gradients also allow, per element, the
+largest change one operand rounded to the neighbouring BF16 value makes
+(`bf16_flip`: an fp32 and an fp64 value on either side of a BF16 rounding
+boundary; seeds 48, 91, 132 and 134 are shapes where that happened), and at
+most a small fraction of elements may need it; the FP8 forward at 6e-2 * rms with the oracle's allowance
 for fp32 implementations (`check_fp8_forward`), the FP8 backward likewise
 against its allowance; the router backward within 1e-4 * rms; experts without
 rows get zero weight gradients.
@@ -25,8 +26,8 @@ import moe_synth
 from moe_synth import to_f32
 from oracle import moe_ref as ref
 
-from test_gpu_parity import (HALF_ULP_BF16, _run_gpu_layer, check_close, check_fp8_forward, host, say,
-                             storage_allowance)
+from test_gpu_parity import (HALF_ULP_BF16, _run_gpu_layer, check_close, check_fp8_forward, check_rms, host,
+                             say, y_rounding)
 from test_gpu_backward import _gpu_fwd_bwd
 from bf16_flip import weight_grad_flip_allowance
 
@@ -54,7 +55,7 @@ def test_random_shape_forward_backward(seed):
     np.testing.assert_array_equal(layer.counts.cpu().numpy(), fw["counts"])
     np.testing.assert_array_equal(layer.offsets.cpu().numpy(), fw["offsets"])
     np.testing.assert_array_equal(layer.dst_row.cpu().numpy(), fw["dst_row"])
-    check_close(host(layer.y), fw["y"], 2e-2, storage_allowance(fw, True, True), None, "y")
+    check_close(host(layer.y), fw["y"], 2e-2, None, None, "y", rounding=y_rounding(fw["y"]))
     args = (f("dy"), f("x"), fw["w"], fw["dst_row"], fw["offsets"], f("w1"), f("w3"), f("w2"))
     bw = ref.layer_backward(*args)
     emu = ref.layer_backward(*args, bf16_operands=True)
@@ -65,10 +66,12 @@ def test_random_shape_forward_backward(seed):
         if not np.any(emu[name]):
             assert not np.any(got[name]), name
             continue
-        extra = HALF_ULP_BF16 * np.abs(emu[name]) if name == "dx" else flip[name]
-        check_close(got[name], emu[name], 2e-2, extra, None, name + " vs bf16-operand oracle")
-        dist = np.abs(emu[name] - bw[name]) + extra
-        check_close(got[name], bw[name], 2e-2, dist, None, name + " vs exact oracle")
+        if name == "dx":
+            check_close(got[name], emu[name], 2e-2, None, None, name + " vs bf16-operand oracle",
+                        rounding=HALF_ULP_BF16 * np.abs(emu[name]))
+        else:
+            check_close(got[name], emu[name], 2e-2, flip[name], None, name + " vs bf16-operand oracle")
+        check_rms(got[name], bw[name], 1e-2, name + " vs exact oracle")
     for e in np.nonzero(fw["counts"] == 0)[0]:
         assert not layer.dw1[e].any() and not layer.dw3[e].any() and not layer.dw2[e].any()
 

@@ -139,3 +139,32 @@ def test_fp8_backward_close_to_exact():
         rms = np.sqrt(np.mean(b[key] ** 2))
         err = np.sqrt(np.mean((a[key] - b[key]) ** 2)) / rms
         assert 5e-3 < err < 0.08, (key, err)      # quantization happened, and is bounded
+
+
+def test_hand_worked_fp8_layer():
+    """The oracle reproduces, value for value, a two-token FP8 layer worked
+    out by hand (tests/golden/fp8_hand_case.json): per-token x scales on the
+    rows, per-output-channel weight scales on the columns, A's per-row scale
+    from its exact value, an E4M3 round-up (280 -> 288) and a tie rounded to
+    the even code (168 -> 160)."""
+    import json
+    import os
+    with open(os.path.join(os.path.dirname(__file__), "golden", "fp8_hand_case.json")) as fh:
+        g = json.load(fh)
+    arr = lambda k: np.array(g[k], np.float64)
+    x = arr("x").astype(np.float32)
+    w1, w3, w2 = (arr(k)[None].astype(np.float32) for k in ("w1", "w3", "w2"))
+    T = x.shape[0]
+    r = ref.layer_forward_fp8(x, np.zeros((x.shape[1], 1), np.float32), None, w1, w3, w2, 1,
+                              logits=np.zeros((T, 1), np.float32))
+    np.testing.assert_array_equal(r["sx"], arr("x_scale"))
+    np.testing.assert_array_equal(r["qx"], np.array(g["x_codes"], np.uint8))
+    np.testing.assert_array_equal(r["g"], arr("g"))
+    np.testing.assert_array_equal(r["u"], arr("u"))
+    np.testing.assert_array_equal(r["a"], arr("a"))
+    np.testing.assert_array_equal(r["sa"], arr("a_scale"))
+    np.testing.assert_array_equal(r["qa"], np.array(g["a_codes"], np.uint8))
+    np.testing.assert_array_equal(r["yp"], arr("yp"))
+    np.testing.assert_array_equal(r["y"], arr("y"))
+    # the codes decode to the values the derivation names
+    np.testing.assert_array_equal(ref.e4m3_decode(r["qa"]), [[448, 288], [-448, 160]])

@@ -177,20 +177,54 @@ def _fwd_case(seed, **sh):
     return wl, inp, f, ref.layer_forward_fp8(f("x"), f("w_gate"), inp["bias"], f("w1"), f("w3"), f("w2"), wl.k)
 
 
+def _fp32_quant(a):
+    """An implementation's quantizer of A: fp32 values, fp32 scale
+    amax / 448, codes of the fp32 quotient."""
+    return ref.quantize_rows(np.asarray(a, np.float32))
+
+
 def test_forward_rowq_spread_interval_brute_force():
-    """Every fp32 matrix with entries at the ends of [lo, hi] or at the value
-    itself quantizes within the spread (the scale following the amax)."""
+    """Against the exact (fp64) quantization of vo, every fp32 matrix with
+    entries at the ends of [lo, hi] or at the fp32 values next to vo,
+    quantized in fp32 (scale and quotient), lands within the spread."""
     rng = np.random.default_rng(5)
-    for trial in range(30):
-        vo = (rng.normal(0, 1, (2, 3)) * rng.choice([1e-3, 1.0, 30.0])).astype(np.float32)
-        d = np.abs(vo) * rng.choice([1e-7, 1e-5, 1e-3]) * (rng.random(vo.shape) < 0.6)
-        lo = (vo - d).astype(np.float32); hi = (vo + d).astype(np.float32)
+    checked = 0
+    for trial in range(40):
+        vo = rng.normal(0, 1, (2, 3)) * rng.choice([1e-3, 1.0, 30.0])
+        d = np.abs(vo) * rng.choice([1e-7, 1e-5, 1e-3]) * (rng.random(vo.shape) < 0.6) + np.abs(vo) * 2.0 ** -23
+        lo, hi = vo - d, vo + d
         qo, spread = ref.rowq_spread_interval(vo, lo, hi)
-        for combo in itertools.product(*[(a, b, c) for a, b, c in zip(lo.ravel(), vo.ravel(), hi.ravel())]):
+        q, s = ref.quantize_rows_exact(vo)
+        np.testing.assert_array_equal(qo, ref.e4m3_decode(q) * s[:, None])
+        up = lambda v: np.nextafter(np.float32(v), np.float32(np.inf))
+        dn = lambda v: np.nextafter(np.float32(v), np.float32(-np.inf))
+        cands = [(np.float32(a) if np.float32(a) >= a else up(a), np.float32(b), dn(c) if np.float32(c) > c else np.float32(c))
+                 for a, b, c in zip(lo.ravel(), vo.ravel(), hi.ravel())]
+        for combo in itertools.product(*cands):
             m = np.array(combo, np.float32).reshape(vo.shape)
-            qm, sm = ref.quantize_rows(m)
+            qm, sm = _fp32_quant(m)
             dq = ref.e4m3_decode(qm) * sm.astype(np.float64)[:, None]
             assert np.all(np.abs(dq - qo) <= spread * (1 + 1e-12) + 1e-300), trial
+            checked += 1
+    assert checked > 5000
+
+
+def test_forward_rowq_spread_interval_at_a_midpoint():
+    """A row whose exact quotient v / s is an E4M3 midpoint (1.1875, between
+    the codes of 1.125 and 1.25) with a scale fp32 does not hold (amax 64,
+    s = 1/7): the exact quantizer rounds the tie to the even code (1.25); an
+    fp32 implementation holding the same values gets the quotient 1.1874999
+    and the code of 1.125.  The spread covers that whole code step although
+    the value interval has zero width (the fp32 scale and quotient alone)."""
+    vo = np.array([[64.0, 1.1875 / 7.0, -0.5]])
+    q, s = ref.quantize_rows_exact(vo)
+    assert s[0] == 64.0 / 448.0 and ref.e4m3_decode(q)[0, 1] == 1.25
+    qm, sm = _fp32_quant(vo)
+    assert ref.e4m3_decode(qm)[0, 1] == 1.125
+    deq32 = ref.e4m3_decode(qm)[0, 1] * float(sm[0])
+    qo, spread = ref.rowq_spread_interval(vo, vo, vo)
+    assert abs(deq32 - qo[0, 1]) > 0.12 * float(s[0])
+    assert abs(deq32 - qo[0, 1]) <= spread[0, 1]
 
 
 def test_forward_envelope_contains_nearby_implementations():
@@ -211,10 +245,10 @@ def test_forward_envelope_contains_nearby_implementations():
             lo, hi = int(offs[e]), int(offs[e + 1])
             d = {"g": g_err, "u": u_err, "a": env["d_a"], "yp": env["d_yp"]}[name][lo:hi]
             out = v + d * rng.uniform(-1, 1, v.shape) * m
-            return ref.round_bf16(out) if name == "yp" else out   # Yp is stored in bf16
+            return out.astype(np.float32).astype(np.float64)     # fp32 values (Yp stored in fp32)
 
         got = ref.layer_forward_fp8(f("x"), f("w_gate"), inp["bias"], f("w1"), f("w3"), f("w2"), wl.k,
-                                    logits=fw["logits"], noise=noise)
+                                    logits=fw["logits"], noise=noise, quant_a=_fp32_quant)
         worst = max(worst, float(((np.abs(got["y"] - fw["y"]) - env["y"]) / rms).max()))
     assert worst <= 0.0, worst
 
@@ -250,7 +284,7 @@ def test_forward_envelope_contains_fp32_evaluation():
         return v
 
     got = ref.layer_forward_fp8(f("x"), f("w_gate"), inp["bias"], f("w1"), f("w3"), f("w2"), wl.k,
-                                logits=fw["logits"], noise=fp32)
+                                logits=fw["logits"], noise=fp32, quant_a=_fp32_quant)
     rms = np.sqrt(np.mean(fw["y"] ** 2))
     assert np.abs(got["y"] - fw["y"]).max() > 0
     assert float(((np.abs(got["y"] - fw["y"]) - env["y"]) / rms).max()) <= 0.0

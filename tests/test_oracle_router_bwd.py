@@ -131,7 +131,7 @@ def test_aux_gradient_alone_matches_finite_differences():
     assert np.abs(num - rb["dL"]).max() <= 1e-8 * np.abs(num).max()
 
 
-def test_bf16_storage_forward_rounds_a_and_yp_only():
+def test_bf16_storage_forward_rounds_a_only():
     rng = np.random.default_rng(11)
     E, h, hf, R = 3, 8, 6, 20
     xp = ref.round_bf16(rng.standard_normal((R, h)))
@@ -140,11 +140,10 @@ def test_bf16_storage_forward_rounds_a_and_yp_only():
     w2 = rng.standard_normal((E, hf, h))
     ex, _, _, a = ref.expert_forward(xp, offs, w1, w3, w2)
     st, _, _, a_st = ref.expert_forward(xp, offs, w1, w3, w2, bf16_storage=True)
-    np.testing.assert_array_equal(ref.round_bf16(st), st)          # Yp is bf16
     np.testing.assert_array_equal(a_st, ref.round_bf16(a))         # A rounded once
-    for e in range(E):                                             # FC2 from the rounded A
+    for e in range(E):                                             # FC2 from the rounded A, not rounded
         lo, hi = offs[e], offs[e + 1]
-        np.testing.assert_array_equal(st[lo:hi], ref.round_bf16(ref.round_bf16(a[lo:hi]) @ w2[e]))
+        np.testing.assert_array_equal(st[lo:hi], ref.round_bf16(a[lo:hi]) @ w2[e])
     rel = np.abs(st - ex).max() / np.abs(ex).max()
     assert 0 < rel < 2e-2
 
