@@ -42,9 +42,10 @@ def gemm_source_sha() -> str:
 
 
 def profiled_traffic(workload: str, kernel: str):
-    """HBM bytes per launch of `kernel` from the committed counter profile
-    (scaled FETCH_SIZE + WRITE_SIZE), or None when there is none or the GEMM
-    sources changed since it was taken."""
+    """Bytes per launch of `kernel` read and written beyond L2 (scaled
+    FETCH_SIZE + WRITE_SIZE, which include Infinity Cache hits) from the
+    committed counter profile, or None when there is none or the GEMM sources
+    changed since it was taken."""
     path = os.path.join(ROOT, "profiles", f"traffic_{workload}_fwd.json")
     if not os.path.exists(path):
         return None
@@ -241,7 +242,10 @@ def main():
         roof = {"kernel": dom, "bound": "hbm", "achieved": achieved / 1e9, "peak": HBM_PEAK / 1e9,
                 "unit": "GB/s", "frac": achieved / HBM_PEAK, "traffic": None}
     roof["traffic"] = profiled_traffic(wl.name, dom)
-    roof["traffic_unit"] = "GB per launch (HBM bytes, rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)"
+    roof["traffic_unit"] = ("GB per launch read and written beyond L2 (rocprofv3 FETCH_SIZE + WRITE_SIZE, "
+                            "copy-calibrated; Infinity Cache hits included)")
+    roof["time_source"] = ("mean launch time of the kernel over the timed steps, HIP events recorded on the "
+                           "launch stream around each launch")
     hbm = {}
     for k2, b in bytes_per_launch.items():
         if k2 in avg:

@@ -13,8 +13,10 @@
 //             arrays ([rows][M] and [rows][N], K = the expert's rows): K slabs
 //             of 64 rows land in LDS M-major and the fragments come out
 //             through the LDS transpose read (BF16 weight gradients).
-// Tile 256 x 256, four waves of 128 x 128; operands go global -> LDS with
-// buffer_load ... lds into two XOR-swizzled stages of 128-byte rows.
+// Tile 256 x 256 on eight waves of 128 x 64 (two per SIMD, 128 fp32
+// accumulators per lane; the FP8 dA uses 128 x 256 tiles, see gemm_bwd.hip);
+// operands go global -> LDS with buffer_load ... lds into two XOR-swizzled
+// stages of 128-byte rows.
 #pragma once
 #include "common.h"
 

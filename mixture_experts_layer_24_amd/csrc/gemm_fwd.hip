@@ -12,9 +12,9 @@
 //     weights [E][N][K], so every 16-byte global load and LDS read feeds an
 //     MFMA operand directly.
 //   * Tile 256 x 256, 128 bytes of K per stage (64 bf16, 32 fp32, 128 fp8),
-//     four waves of 128 x 128 (4 x 4 MFMA 32x32 blocks, 256 fp32 accumulators
-//     per lane, held in AGPRs).  Two LDS stages (128 KB) give one barrier per
-//     K step.  Operands go global -> LDS directly (buffer_load ... lds, no
+//     eight waves of 128 x 64 (4 x 2 MFMA 32x32 blocks, 128 fp32 accumulators
+//     per lane), two per SIMD so that one can issue MFMAs while the other
+//     waits on a load.  Two LDS stages (128 KB) give one barrier per K step.  Operands go global -> LDS directly (buffer_load ... lds, no
 //     VGPR staging); the next slab's loads are in flight while the current
 //     one computes, and the next slab's first fragments are read right after
 //     the barrier while the last substep's MFMAs still run.

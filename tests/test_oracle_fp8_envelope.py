@@ -295,3 +295,80 @@ def test_forward_envelope_is_small():
     g_err, u_err = ref.fp8_forward_gu_bound(f("x"), fw["dst_row"], fw["offsets"], f("w1"), f("w3"))
     env = ref.fp8_forward_envelope(fw, f("w1"), f("w3"), f("w2"), g_err, u_err)
     assert env["y"].mean() / np.sqrt(np.mean(fw["y"] ** 2)) < 2e-2
+
+
+# -------------------------------------------- single terms, pinned alone
+
+def _fast_exp32(x, ulps):
+    """exp(x) as a fast fp32 exponential forms it: 2^(fl32(x * log2 e)),
+    rounded to fp32 and moved by ``ulps`` units in the last place (the
+    hardware exp2 is within one)."""
+    t = (np.float32(x) * np.float32(1.4426950408889634)).astype(np.float32)
+    e = np.exp2(t.astype(np.float64)).astype(np.float32)
+    for _ in range(abs(ulps)):
+        e = np.nextafter(e, np.float32(np.inf) if ulps > 0 else np.float32(0))
+    return e
+
+
+def test_swiglu_eval_bound_against_float32():
+    """The fp32 SwiGLU terms of both allowances (`swiglu_eval_bound`): A =
+    SiLU(G) U, dG = dA U s (1 + G (1 - s)) and dU = dA SiLU(G) evaluated in
+    float32 in the kernels' order, with a fast exponential off by up to one
+    ulp either way, stay within the bound plus their own final rounding on
+    every sample; and on some samples the error exceeds that final rounding
+    alone, so the term is needed."""
+    rng = np.random.default_rng(41)
+    n = 200000
+    G = np.concatenate([rng.normal(0, 3, n // 2), rng.uniform(-40, 40, n // 2)]).astype(np.float32)
+    U = rng.normal(0, 2, n).astype(np.float32)
+    dA = rng.normal(0, 2, n).astype(np.float32)
+    g64, u64, d64 = G.astype(np.float64), U.astype(np.float64), dA.astype(np.float64)
+    s64 = ref.sigmoid(g64)
+    a64, dg64, du64 = g64 * s64 * u64, d64 * u64 * s64 * (1 + g64 * (1 - s64)), d64 * g64 * s64
+    ev_a, ev_dg, ev_du = ref.swiglu_eval_bound(np.abs(g64), np.abs(u64), s64, np.abs(g64 * s64), np.abs(d64))
+    one = np.float32(1)
+    needed = {"a": 0.0, "dg": 0.0, "du": 0.0}
+    for ulps in (-1, 0, 1):
+        with np.errstate(over="ignore"):
+            s = (one / (one + _fast_exp32(-G, ulps))).astype(np.float32)
+        a = ((G * s) * U).astype(np.float64)                     # SiLU(G) U
+        dg = (dA * U * s * (one + G * (one - s))).astype(np.float64)
+        du = (dA * (G * s)).astype(np.float64)
+        for name, got, want, ev in (("a", a, a64, ev_a), ("dg", dg, dg64, ev_dg), ("du", du, du64, ev_du)):
+            err = np.abs(got - want) - ref.F32_U * np.abs(want)   # less the final rounding
+            assert np.all(err <= ev), (name, ulps, float((err - ev).max()))
+            needed[name] = max(needed[name], float(err.max()))
+    assert all(v > 0 for v in needed.values()), needed
+
+
+def test_fp32_sum_bound_covers_worst_order_dA():
+    """dA = dYp W2^T summed in float32 in the allowed order with the most
+    roundings (64-product blocks one after the other, then block after block)
+    stays within the dA term of the backward allowance; the term is needed
+    (float32 moves dA)."""
+    fw, args = _case(7, T=120, h=2048, h_ffn=128, E=2, k=1)
+    dy, x, w, dst_row, offsets, w1, w3, w2, g, u = args
+    env = ref.fp8_backward_envelope(*args)
+    T, k = dst_row.shape
+    qdy, sdy = ref.quantize_rows(dy)
+    qdyp = ref.permute(qdy, dst_row)
+    sdyp = np.zeros(T * k, np.float32)
+    for j in range(k):
+        sdyp[dst_row[:, j]] = w[:, j].astype(np.float32) * sdy.astype(np.float32)
+    worst, moved = -np.inf, 0.0
+    for e in range(w1.shape[0]):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        if hi == lo:
+            continue
+        qw2, sw2 = ref.quantize_rows(w2[e])
+        a = ref.e4m3_decode(qdyp[lo:hi])
+        b = ref.e4m3_decode(qw2)
+        prod = (a.astype(np.float32)[:, None, :] * b.astype(np.float32)[None, :, :])   # exact in fp32
+        blk = prod.reshape(prod.shape[0], prod.shape[1], -1, 64)
+        acc = np.add.accumulate(np.add.accumulate(blk, axis=3, dtype=np.float32)[..., -1], axis=2,
+                                dtype=np.float32)[:, :, -1]
+        da32 = ((acc * sdyp[lo:hi, None]) * sw2.astype(np.float32)[None, :]).astype(np.float64)
+        da64 = (a @ b.T) * sdyp[lo:hi, None].astype(np.float64) * sw2.astype(np.float64)[None, :]
+        worst = max(worst, float((np.abs(da32 - da64) - env["d_da"][lo:hi]).max()))
+        moved = max(moved, float(np.abs(da32 - da64).max()))
+    assert worst <= 0.0 and moved > 0.0
