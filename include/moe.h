@@ -183,6 +183,24 @@ int moe_permute(const void* src, int src_dtype, const int32_t* topk_idx, const f
                 size_t ws_bytes, void* stream);
 
 /*
+ * moe_permute without a workspace, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc).  Same arguments and results as moe_permute, minus ws and
+ * ws_bytes: the index builder's per-block histograms live in a file-scope
+ * device array of MOE_NOALLOC_SCRATCH_BYTES, one per GPU, held until the
+ * process ends.  Nothing is allocated or freed.  Returns MOE_ERR_WORKSPACE
+ * (nothing written) when the index needs more than that scratch:
+ * ceil(T / 256) * E * 4 bytes (rounded up to 256) must fit, e.g. T up to
+ * 262144 with E = 256.  Every call on one GPU shares that GPU's array, which
+ * keeps the last call's contents (each call rewrites every byte it reads), so
+ * calls that overlap on one GPU (different streams, or threads) race.
+ */
+#define MOE_NOALLOC_SCRATCH_BYTES (1 << 20)
+int moe_permute_noalloc(const void* src, int src_dtype, const int32_t* topk_idx, const float* row_scale,
+                        int T, int h, int E, int k, int32_t* counts, int32_t* offsets, int32_t* dst_row,
+                        int32_t* src_tok, void* dst, int dst_dtype, float* dst_scale, void* stream);
+
+/*
  * One GPU's share of expert parallelism (MegaScale-MoE research digest §3.2,
  * Diagram B: scatter to the local experts and drop the rest; paper review §四
  * adaptive EP communication): the dispatch of moe_permute restricted to the

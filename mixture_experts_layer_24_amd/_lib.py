@@ -39,6 +39,7 @@ SIGNATURES = {
     "moe_route": (I, [P, P, P, P, I, I, I, I, I, P, P, P]),
     "moe_permute_workspace_size": (SZ, [I, I, I]),
     "moe_permute": (I, [P, I, P, P, I, I, I, I, P, P, P, P, P, I, P, P, SZ, P]),
+    "moe_permute_noalloc": (I, [P, I, P, P, I, I, I, I, P, P, P, P, P, I, P, P]),
     "moe_permute_local_workspace_size": (SZ, [I, I, I]),
     "moe_permute_local": (I, [P, I, P, P, I, I, I, I, I, I, P, P, P, P, P, I, P, P, SZ, P]),
     "moe_capacity_drop_workspace_size": (SZ, [I, I, I]),

@@ -3,6 +3,8 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <mutex>
+
 #include "common.h"
 
 namespace {
@@ -136,6 +138,58 @@ size_t moe_permute_workspace_size(int T, int E, int k) {
   (void)k;
   if (T < 0 || E < 1) return 0;
   return moe_launch::index_ws_bytes(T, E);
+}
+
+}  // extern "C"
+
+// Scratch of moe_permute_noalloc: the index builder's per-block histograms,
+// in a file-scope device array instead of a caller's workspace.  Each device
+// holds its own copy until the process ends.  Host code uses the address
+// hipGetSymbolAddress returns for the current device, never the array's name.
+static __device__ __align__(256) unsigned char scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[64] = {};
+
+// This device's copy of `scratch`, looked up on the first call on the device.
+int scratch_ptr(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  REQ(e == hipSuccess && dev >= 0 && dev < 64, MOE_ERR_HIP, "no usable current device (%s)",
+      hipGetErrorString(e));
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    REQ(e == hipSuccess && p != nullptr, MOE_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s",
+        dev, hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
+}
+}  // namespace
+
+extern "C" {
+
+int moe_permute_noalloc(const void* src, int src_dtype, const int32_t* topk_idx, const float* row_scale,
+                        int T, int h, int E, int k, int32_t* counts, int32_t* offsets, int32_t* dst_row,
+                        int32_t* src_tok, void* dst, int dst_dtype, float* dst_scale, void* stream) {
+  if (topk_idx == nullptr)  // no index to build: moe_permute needs no workspace then
+    return moe_permute(src, src_dtype, topk_idx, row_scale, T, h, E, k, counts, offsets, dst_row,
+                       src_tok, dst, dst_dtype, dst_scale, nullptr, 0, stream);
+  REQ(T >= 0, MOE_ERR_ARG, "T=%d is negative", T);
+  REQ(E >= 1 && E <= MOE_MAX_EXPERTS, MOE_ERR_SHAPE, "E=%d outside [1, %d]", E, MOE_MAX_EXPERTS);
+  const size_t need = moe_launch::index_ws_bytes(T, E);
+  REQ(need <= MOE_NOALLOC_SCRATCH_BYTES, MOE_ERR_WORKSPACE,
+      "moe_permute_noalloc: T=%d, E=%d need %zu bytes of scratch, more than its %d", T, E, need,
+      MOE_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  int rc = scratch_ptr(&ws);
+  if (rc) return rc;
+  return moe_permute(src, src_dtype, topk_idx, row_scale, T, h, E, k, counts, offsets, dst_row,
+                     src_tok, dst, dst_dtype, dst_scale, ws, MOE_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 int moe_permute(const void* src, int src_dtype, const int32_t* topk_idx, const float* row_scale,

@@ -63,6 +63,13 @@ def moe_permute(src, src_dtype, topk_idx, row_scale, T, h, E, k, counts, offsets
                                    dst_dtype, _p(dst_scale), _p(ws), ws_bytes, _s(stream)))
 
 
+def moe_permute_noalloc(src, src_dtype, topk_idx, row_scale, T, h, E, k, counts, offsets, dst_row,
+                        src_tok, dst, dst_dtype, dst_scale, stream=None):
+    return check(lib().moe_permute_noalloc(_p(src), src_dtype, _p(topk_idx), _p(row_scale), T, h, E, k,
+                                           _p(counts), _p(offsets), _p(dst_row), _p(src_tok), _p(dst),
+                                           dst_dtype, _p(dst_scale), _s(stream)))
+
+
 def moe_permute_local_workspace_size(T, e_count, k):
     return lib().moe_permute_local_workspace_size(T, e_count, k)
 
