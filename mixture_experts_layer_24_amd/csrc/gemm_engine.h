@@ -237,27 +237,27 @@ __device__ __forceinline__ LoadOff load_off_kr(int pitch, int lane) {
   return LoadOff{r * pitch + ((p ^ kr_swz(r)) << 4), r * pitch + ((p ^ kr_swz(r + 2)) << 4)};
 }
 
-// One 64-row K slab of A and B into LDS stage `st` (SchedKR): wave w fills
+// One 64-row K slab of A and B into LDS stage `stage` (SchedKR): wave w fills
 // K-row pairs w*GA .. w*GA+GA-1 of A and w*GB .. of B.  The descriptors cover
 // this slab's rows only, starting at the tile's first column.
 template <class C>
-__device__ __forceinline__ void issue_slab_kr(unsigned char* lds, int st, __amdgpu_buffer_rsrc_t ra,
+__device__ __forceinline__ void issue_slab_kr(unsigned char* stage, __amdgpu_buffer_rsrc_t ra,
                                               __amdgpu_buffer_rsrc_t rb, int wave, LoadOff la,
                                               LoadOff lb, int pa, int pb) {
-  unsigned char* A = lds + st * C::kStage + wave * C::kGA * 1024;
-  unsigned char* B = lds + st * C::kStage + C::kAStage + wave * C::kGB * 1024;
+  unsigned char* A = stage + wave * C::kGA * 1024;
+  unsigned char* B = stage + C::kAStage + wave * C::kGB * 1024;
   const int ga0 = wave * C::kGA, gb0 = wave * C::kGB;
 #pragma unroll
   for (int i = 0; i < (C::kGA > C::kGB ? C::kGA : C::kGB); ++i) {
     if (i < C::kGA) {
       const int q = ga0 + i;
-      const int v = ((q & 1) ? la.o : la.e) + 2 * q * pa;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t*)(A + i * 1024), 16, v, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t*)(A + i * 1024), 16, (q & 1) ? la.o : la.e,
+                                               2 * q * pa, 0, 0);
     }
     if (i < C::kGB) {
       const int q = gb0 + i;
-      const int v = ((q & 1) ? lb.o : lb.e) + 2 * q * pb;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr_t*)(B + i * 1024), 16, v, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr_t*)(B + i * 1024), 16, (q & 1) ? lb.o : lb.e,
+                                               2 * q * pb, 0, 0);
     }
   }
 }
@@ -601,6 +601,14 @@ __global__ void __launch_bounds__(C::kThreads, C::kWavesPerSimd) grouped_gemm_ke
   constexpr int BM = C::kBM, BN = C::kBN, MI = C::kMI, NJ = C::kNJ;
   constexpr int RB = C::kRowB, NS = C::kStages, D = NS - 1;  // D slabs in flight ahead
   extern __shared__ __align__(16) unsigned char lds[];
+  // SchedKR keeps its two stages in arrays of their own and runs the K loop
+  // with the stage parity known at compile time: the compiler can then tell
+  // that a transpose read of one stage does not touch the slab the LDS-DMA
+  // loads are filling in the other (through one array, with a run-time
+  // offset, it waits for every load in flight before each transpose read).
+  constexpr int KRS = SCHED == kSchedKR ? C::kStage : 16;
+  __shared__ __align__(16) unsigned char kr0[KRS];
+  __shared__ __align__(16) unsigned char kr1[KRS];
   __shared__ int tpre[MOE_MAX_EXPERTS + 1];  // tiles before expert e
   __shared__ int offs[MOE_MAX_EXPERTS + 1];  // SchedM / KR: row offsets; SchedK: padded K prefix
   __shared__ int split_flag;
@@ -611,8 +619,8 @@ __global__ void __launch_bounds__(C::kThreads, C::kWavesPerSimd) grouped_gemm_ke
   const int half = lane >> 5, l32 = lane & 31;
   const int NT = ceil_div(g.N, BN);
   const int MT = SCHED != kSchedM ? ceil_div(g.M, BM) : 0;
-  static_assert(SCHED != kSchedKR || (DT == MOE_BF16 && RB == 128 && BM == 256 && BN == 256),
-                "SchedKR: bf16, 64-row slabs of 512-byte LDS rows");
+  static_assert(SCHED != kSchedKR || (DT == MOE_BF16 && RB == 128 && BM == 256 && BN == 256 && NS == 2),
+                "SchedKR: bf16, 64-row slabs of 512-byte LDS rows, two stages");
 
   for (int e = tid; e <= g.E; e += C::kThreads) {
     int o = g.offsets[e];
@@ -773,7 +781,8 @@ __global__ void __launch_bounds__(C::kThreads, C::kWavesPerSimd) grouped_gemm_ke
   // SchedKR: row pitches of A and B, the lanes' loader offsets
   const int pa = g.M * 2, pb = g.N * 2;
   const LoadOff kla = load_off_kr(pa, lane), klb = load_off_kr(pb, lane);
-  auto issue = [&]() {
+  // kdst: the stage SchedKR's slab goes to (slab `issued` of the stream)
+  auto issue = [&](unsigned char* kdst) {
     if (ldone) return;
     if (SCHED == kSchedKR) {
       // descriptors of this slab's rows: rows past the expert's end, and
@@ -783,7 +792,7 @@ __global__ void __launch_bounds__(C::kThreads, C::kWavesPerSimd) grouped_gemm_ke
           rsrc(g.A, lt.a_off + size_t(k0) * pa, size_t(nr) * pa - size_t(lt.row0) * 2);
       const __amdgpu_buffer_rsrc_t rb =
           rsrc(g.B, lt.b_off + size_t(k0) * pb, size_t(nr) * pb - size_t(lt.n0) * 2);
-      issue_slab_kr<C>(lds, issued % NS, ra, rb, wave, kla, klb, pa, pb);
+      issue_slab_kr<C>(kdst, ra, rb, wave, kla, klb, pa, pb);
     } else {
       issue_slab<C>(lds, issued % NS, lra, lrb, wave, llo, lt.rowB, (lt.kb + lk) * RB);
     }
@@ -809,17 +818,81 @@ __global__ void __launch_bounds__(C::kThreads, C::kWavesPerSimd) grouped_gemm_ke
     else wait_vm_lds<0>();
   };
 
-  for (int i = 0; i < D; ++i) issue();
+  // stage i of the ring; SchedKR's two stages are its own arrays
+  auto stage = [&](int i) -> unsigned char* {
+    if constexpr (SCHED == kSchedKR) return i ? kr1 : kr0;
+    else return lds + i * C::kStage;
+  };
+  for (int i = 0; i < D; ++i) issue(stage(i));
   wait_slab(0);
   __syncthreads();
   Frag<DT> fa[2][MI], fb[2][NJ];
-  if (issued > 0) frags(fa[0], fb[0], lds, 0);
+  if (issued > 0) frags(fa[0], fb[0], stage(0), 0);
 
   int c = 0;             // stream slab the MFMAs consume next
   bool drain = false;    // an epilogue's stores may be outstanding
+  f32x16 acc[MI][NJ];    // the current item's accumulators
+  // One K slab: As is stage c % NS (holding slab c, fa[0]/fb[0] its first
+  // fragments), Nx stage (c + 1) % NS.  SchedKR (two stages) loads slab c + 1
+  // into Nx.
+  auto kstep = [&](const unsigned char* As, unsigned char* Nx) {
+    // Stores and loads share one counter and may complete out of order:
+    // after an epilogue, drain it before counting loads again.
+    if (drain) {
+      __builtin_amdgcn_s_waitcnt(0);
+      drain = false;
+    }
+    // slab c + D goes into the stage that slab c - 1 left (read out before
+    // the last barrier)
+    issue(Nx);
+    if (kSingle) {
+#pragma unroll
+      for (int s = 0; s + 1 < S; ++s)
+        mma_reload<C, DT, true>(acc, fa[0], fb[0], As, arow, brow, s + 1, half);
+      wait_slab(c + 1);
+      __syncthreads();
+      if (c + 1 < issued)
+        mma_reload<C, DT, true>(acc, fa[0], fb[0], Nx, arow, brow, 0, half);
+      else
+        mma_reload<C, DT, false>(acc, fa[0], fb[0], As, arow, brow, 0, half);
+      ++c;
+      return;
+    }
+    // The wave runs its MFMA substeps at raised issue priority, so where
+    // both waves of a SIMD have instructions ready the one in its MFMA
+    // phase goes first (Mixtral-shaped FC1 -1.5%, FC2 -0.7%); the barrier
+    // wait, the next slab's first fragments and the load issue run at the
+    // normal priority.
+    __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+    for (int s = 0; s + 1 < S; ++s) {
+      frags(fa[(s + 1) & 1], fb[(s + 1) & 1], As, s + 1);
+      mma_all<C, DT>(acc, fa[s & 1], fb[s & 1]);
+    }
+    // interleave: the substep's LDS reads spread over its MFMAs (and one
+    // global load per MFMA early on)
+#pragma unroll
+    for (int s = 0; s + 1 < S; ++s)
+#pragma unroll
+      for (int q = 0; q < NM; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        constexpr int rq = NR / NM;
+        if (rq > 0) __builtin_amdgcn_sched_group_barrier(0x100, rq, 0);
+        if (q < NR % NM) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        if (s == 0 && q < NV) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      }
+    __builtin_amdgcn_s_setprio(0);
+    wait_slab(c + 1);  // this stage read out; slab c+1 landed
+    __syncthreads();
+    // next slab's first fragments load while the last substep multiplies
+    if (c + 1 < issued) frags(fa[0], fb[0], Nx, 0);
+    mma_all<C, DT>(acc, fa[1], fb[1]);
+    __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);
+    ++c;
+  };
   while (true) {
     const Tile cur = item_of(t);
-    f32x16 acc[MI][NJ];
 #pragma unroll
     for (int i = 0; i < MI; ++i)
 #pragma unroll
@@ -827,65 +900,22 @@ __global__ void __launch_bounds__(C::kThreads, C::kWavesPerSimd) grouped_gemm_ke
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-    for (int kt = 0; kt < cur.nk; ++kt) {
-      // Stage c % NS holds slab c and fa[0]/fb[0] its first fragments.
-      // Stores and loads share one counter and may complete out of order:
-      // after an epilogue, drain it before counting loads again.
-      if (drain) {
-        __builtin_amdgcn_s_waitcnt(0);
-        drain = false;
+    if constexpr (SCHED == kSchedKR) {
+      // stage parity known in each copy of the step: an odd first slab, then
+      // pairs, then an even last slab (one step under a run-time parity
+      // branch instead keeps both copies' fragments live and spills)
+      int kt = 0;
+      if ((c & 1) && cur.nk > 0) {
+        kstep(kr1, kr0);
+        kt = 1;
       }
-      // slab c + D goes into the stage that slab c - 1 left (read out before
-      // the last barrier)
-      issue();
-      const unsigned char* As = lds + (c % NS) * C::kStage;
-      if (kSingle) {
-#pragma unroll
-        for (int s = 0; s + 1 < S; ++s)
-          mma_reload<C, DT, true>(acc, fa[0], fb[0], As, arow, brow, s + 1, half);
-        wait_slab(c + 1);
-        __syncthreads();
-        if (c + 1 < issued)
-          mma_reload<C, DT, true>(acc, fa[0], fb[0], lds + ((c + 1) % NS) * C::kStage, arow, brow, 0,
-                                  half);
-        else
-          mma_reload<C, DT, false>(acc, fa[0], fb[0], As, arow, brow, 0, half);
-        ++c;
-        continue;
+      for (; kt + 1 < cur.nk; kt += 2) {
+        kstep(kr0, kr1);
+        kstep(kr1, kr0);
       }
-      // The wave runs its MFMA substeps at raised issue priority, so where
-      // both waves of a SIMD have instructions ready the one in its MFMA
-      // phase goes first (Mixtral-shaped FC1 -1.5%, FC2 -0.7%); the barrier
-      // wait, the next slab's first fragments and the load issue run at the
-      // normal priority.
-      __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-      for (int s = 0; s + 1 < S; ++s) {
-        frags(fa[(s + 1) & 1], fb[(s + 1) & 1], As, s + 1);
-        mma_all<C, DT>(acc, fa[s & 1], fb[s & 1]);
-      }
-      // interleave: the substep's LDS reads spread over its MFMAs (and one
-      // global load per MFMA early on)
-#pragma unroll
-      for (int s = 0; s + 1 < S; ++s)
-#pragma unroll
-        for (int q = 0; q < NM; ++q) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          constexpr int rq = NR / NM;
-          if (rq > 0) __builtin_amdgcn_sched_group_barrier(0x100, rq, 0);
-          if (q < NR % NM) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-          if (s == 0 && q < NV) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-        }
-      __builtin_amdgcn_s_setprio(0);
-      wait_slab(c + 1);  // this stage read out; slab c+1 landed
-      __syncthreads();
-      // next slab's first fragments load while the last substep multiplies
-      if (c + 1 < issued)
-        frags(fa[0], fb[0], lds + ((c + 1) % NS) * C::kStage, 0);
-      mma_all<C, DT>(acc, fa[1], fb[1]);
-      __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);
-      ++c;
+      if (kt < cur.nk) kstep(kr0, kr1);
+    } else {
+      for (int kt = 0; kt < cur.nk; ++kt) kstep(stage(c % NS), stage((c + 1) % NS));
     }
 
     // A split is its workgroup's last item: only the one that completes the
@@ -893,7 +923,7 @@ __global__ void __launch_bounds__(C::kThreads, C::kWavesPerSimd) grouped_gemm_ke
     if (cur.split < 0 || splitk_combine<C>(g, acc, ((t - full) / f) * f, f, cur.split,
                                            (t - full) / f, wave, lane, &split_flag))
       epilogue<C, DT, MODE>(g, acc, cur, wave, wm, wn, half, l32,
-                            lds + ((c + NS - 1) % NS) * C::kStage);
+                            stage((c + NS - 1) % NS));
     drain = true;
     t += G;
     if (t >= work) break;
@@ -931,7 +961,9 @@ inline void splitk_ws_set(moe::GemmArgs& a, void* ws) {
 template <class C, int DT, int MODE, int SCHED>
 inline int launch_gemm(const moe::GemmArgs& a, int timer, hipStream_t s) {
   using namespace moe;
-  static bool attr = allow_lds(grouped_gemm_kernel<C, DT, MODE, SCHED>, C::kLds);
+  // SchedKR's stages are static arrays of the kernel
+  constexpr size_t dyn = SCHED == kSchedKR ? 0 : C::kLds;
+  static bool attr = allow_lds(grouped_gemm_kernel<C, DT, MODE, SCHED>, dyn);
   if (!attr) return MOE_ERR_HIP;
   long grid = long(num_cus()) * C::kOcc;
   if (grid > kMaxGrid) grid = kMaxGrid;
@@ -947,7 +979,7 @@ inline int launch_gemm(const moe::GemmArgs& a, int timer, hipStream_t s) {
   if (a.part != nullptr)
     hipLaunchKernelGGL(zero_u32_kernel<0>, dim3(1), dim3(kMaxGrid), 0, s, a.cnt, int(kMaxGrid));
   hipLaunchKernelGGL((grouped_gemm_kernel<C, DT, MODE, SCHED>), dim3(unsigned(grid)),
-                     dim3(C::kThreads), C::kLds, s, a);
+                     dim3(C::kThreads), dyn, s, a);
   timer_end(timer, s);
   return launch_status();
 }
