@@ -107,7 +107,10 @@ __global__ void __launch_bounds__(RES ? 512 : 256) route_bf16_kernel(const uint1
   const int rowc = row < T ? row : T - 1;
   constexpr int NW = RES ? 8 : 4;  // waves
   const int kw = h / NW;  // h is a multiple of 64 (of 128 with RES), so kw of 16
-  const int kbeg = wave * kw;
+  // K ranges rotated by workgroup (see route_tr_kernel); partial tiles are
+  // summed in range order
+  const int kr = (wave + int(blockIdx.x)) % NW;
+  const int kbeg = kr * kw;
   // this wave's W^T region: [NT*32][kRtStride] bf16 per chunk, or (RES) the
   // whole range [E][kw + 8]
   const int rstride = RES ? kw + 8 : kRtStride;
@@ -234,7 +237,7 @@ __global__ void __launch_bounds__(RES ? 512 : 256) route_bf16_kernel(const uint1
       for (int s = 0; s < 4; ++s) xq[p][s] = xq[p + 1][s];
   }
   __syncthreads();
-  // partial tiles -> LDS [wave][token][E], then sum in wave order
+  // partial tiles -> LDS [K range][token][E], then sum in range order
   float* part = reinterpret_cast<float*>(smem);
 #pragma unroll
   for (int n = 0; n < NT; ++n) {
@@ -243,7 +246,7 @@ __global__ void __launch_bounds__(RES ? 512 : 256) route_bf16_kernel(const uint1
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int i = 8 * (r >> 2) + 4 * half + (r & 3);
-        part[(wave * kRtTokens + i) * E + e] = acc[n][r];
+        part[(kr * kRtTokens + i) * E + e] = acc[n][r];
       }
     }
   }
@@ -269,14 +272,14 @@ __global__ void __launch_bounds__(RES ? 512 : 256) route_bf16_kernel(const uint1
 }
 
 // BF16 logits with W_g read in its own [h][E] layout (E a multiple of 8, at
-// most 32): eight waves split h, each streaming its K range in 64-row chunks.
+// most 64): eight waves split h, each streaming its K range in 64-row chunks.
 // x goes from HBM straight into A fragments (64 contiguous bytes per lane per
 // chunk); the chunk's W_g rows come into registers with 16-byte loads and
 // are written unchanged into the wave's own LDS buffer, from where transpose
 // reads (ds_read_b64_tr_b16) hand each lane four K-consecutive values of one
-// expert column: W_g is never rearranged.  x and W_g run three chunks ahead
-// of the MFMAs; the waves meet only to sum their partial 32 x E tiles (in
-// K-range order), add the bias and pick the top k.
+// expert column: W_g is never rearranged.  x runs three chunks ahead of the
+// MFMAs, W_g three (E > 32: two); the waves meet only to sum their partial
+// 32 x E tiles (in K-range order), add the bias and pick the top k.
 typedef __attribute__((address_space(3))) void rt_lds_t;
 typedef short rt_s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) rt_s16x4 rt_lds_s16x4;
@@ -286,16 +289,25 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rt_rsrc(const void* base, size
       int(bytes < 0x7FFFFFF0u ? bytes : 0x7FFFFFF0u), 0x00020000);
 }
 
-template <int E8, int NW>  // E = 8 E8, E8 <= 4; NW waves split h
+template <int E8, int NW>  // E = 8 E8; NW waves split h
 __global__ void __launch_bounds__(NW * 64) route_tr_kernel(const uint16_t* __restrict__ x,
-                                                       const uint16_t* __restrict__ wg,
-                                                       const float* __restrict__ bias,
-                                                       float* __restrict__ logits_out, int T, int h,
-                                                       int E, int k, int32_t* __restrict__ topk_idx,
-                                                       float* __restrict__ topk_w) {
-  static_assert(E8 >= 1 && E8 <= 4, "one 32-expert block");
-  constexpr int RB = 16 * E8;  // bytes per W_g row
-  constexpr int CB = 64 * RB;  // bytes per 64-row chunk: E8 pieces of 1 KB
+                                                           const uint16_t* __restrict__ wg,
+                                                           const float* __restrict__ bias,
+                                                           float* __restrict__ logits_out, int T,
+                                                           int h, int E, int k,
+                                                           int32_t* __restrict__ topk_idx,
+                                                           float* __restrict__ topk_w) {
+  static_assert(E8 >= 1 && E8 <= 8, "E <= 64");
+  constexpr int NT = (E8 + 3) / 4;  // 32-expert blocks
+  constexpr int RB = 16 * E8;       // bytes per W_g row
+  constexpr int CB = 64 * RB;       // bytes per 64-row chunk: E8 pieces of 1 KB
+  // W_g chunks in flight: four register slots (loaded three chunks ahead), or
+  // for E > 32 two (two ahead), which keeps a wave within its registers
+  constexpr int WS = E8 <= 4 ? 4 : 2, WD = WS == 4 ? 3 : 2;
+  // 128-byte rows: rows 2 and 3 (mod 4) keep their 16-byte pieces at p ^ 4,
+  // so the four rows of a transpose read fall on distinct banks
+  constexpr bool kSwz = E8 == 8;
+  constexpr int NQ = (kRtTokens * 8 * E8 + NW * 64 - 1) / (NW * 64);  // logits summed per thread
   // a wave's chunk buffer; after the K loop the partial tiles [NW][32][E] fp32
   __shared__ __align__(16) unsigned char wbuf[NW * CB];
   const int tid = threadIdx.x, lane = tid & 63;
@@ -316,63 +328,82 @@ __global__ void __launch_bounds__(NW * 64) route_tr_kernel(const uint16_t* __res
   const __amdgpu_buffer_rsrc_t rw = rt_rsrc(wg, size_t(kbeg) * RB, size_t(kw) * RB);
   const int xoff = (l32 * h + kbeg + half * 32) * 2;
   unsigned char* buf = wbuf + wave * CB;
-  // transpose-read offset: lanes 4j .. 4j+3 of a 16-lane group address row j
-  // of a 4-row block, columns 4 (lane & 3) + 16 g; lane i of the group
-  // receives column i.  Columns past E wrap onto real ones: they only feed
-  // output columns past E, which are never read.
-  const int tro = (half * 32 + ((lane & 15) >> 2)) * RB +
-                  (((((lane >> 4) & 1) * 16 + 4 * (lane & 3)) % E) * 2);
-  // chunks in rings of four register slots: chunk c sits in slot c % 4
-  u32x4 xq[4][4], wq[4][E8];
-  auto load = [&](int c, u32x4(&xa)[4], u32x4(&wa)[E8]) {
+  // where lane l writes its 16 bytes of each 1 KB piece of a chunk
+  const int wpos = kSwz ? (lane >> 3) * RB + (((lane & 7) ^ (((lane >> 4) & 1) * 4)) << 4) : lane * 16;
+  // transpose-read offsets: lanes 4j .. 4j+3 of a 16-lane group address row j
+  // of a 4-row block, columns 4 (lane & 3) + 16 g (+ 32 nb); lane i of the
+  // group receives column i.  Columns past E wrap onto real ones: they only
+  // feed output columns past E, which are never read.
+  int tro[NT];
+#pragma unroll
+  for (int nb = 0; nb < NT; ++nb) {
+    const int r = (lane & 15) >> 2;
+    const int byte = ((nb * 32 + ((lane >> 4) & 1) * 16 + 4 * (lane & 3)) % E) * 2;
+    const int piece = kSwz ? ((byte >> 4) ^ (((r >> 1) & 1) * 4)) : (byte >> 4);
+    tro[nb] = (half * 32 + r) * RB + piece * 16 + (byte & 15);
+  }
+  // x chunk c sits in register slot c % 4, W_g chunk c in slot c % WS
+  u32x4 xq[4][4], wq[WS][E8];
+  auto load_x = [&](int c, u32x4(&xa)[4]) {
 #pragma unroll
     for (int s = 0; s < 4; ++s)
       xa[s] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, xoff + c * 128 + s * 16, 0, 0));
+  };
+  auto load_w = [&](int c, u32x4(&wa)[E8]) {
 #pragma unroll
     for (int i = 0; i < E8; ++i)
       wa[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, lane * 16, c * CB + i * 1024, 0));
   };
   auto put = [&](const u32x4(&wa)[E8]) {
 #pragma unroll
-    for (int i = 0; i < E8; ++i) *reinterpret_cast<u32x4*>(buf + i * 1024 + lane * 16) = wa[i];
+    for (int i = 0; i < E8; ++i) *reinterpret_cast<u32x4*>(buf + i * 1024 + wpos) = wa[i];
   };
-  f32x16 acc;
+  f32x16 acc[NT];
 #pragma unroll
-  for (int r = 0; r < 16; ++r) acc[r] = 0.f;
-  // the bias of the (at most two) logits this thread sums at the end
-  static_assert(kRtTokens * 8 * E8 <= 2 * NW * 64, "two logits per thread");
-  float bq[2];
+  for (int n = 0; n < NT; ++n)
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
+    for (int r = 0; r < 16; ++r) acc[n][r] = 0.f;
+  // the bias of the logits this thread sums at the end
+  float bq[NQ];
+#pragma unroll
+  for (int j = 0; j < NQ; ++j) {
     const int q = tid + j * NW * 64;
     bq[j] = bias && q < kRtTokens * E ? bias[q % E] : 0.f;
   }
 
 #pragma unroll
   for (int p = 0; p < 3; ++p)
-    if (p < nch) load(p, xq[p], wq[p]);
+    if (p < nch) load_x(p, xq[p]);
+#pragma unroll
+  for (int p = 0; p < WD; ++p)
+    if (p < nch) load_w(p, wq[p]);
   put(wq[0]);
-  // chunk c (Q = c % 4, known in each copy of the step): load chunk c + 3,
-  // multiply chunk c out of the LDS buffer, then write chunk c + 1 into it
-  // (a wave's LDS operations run in order, so the reads of chunk c come first)
+  // chunk c (Q = c % 4, known in each copy of the step): load x chunk c + 3
+  // and W_g chunk c + WD, multiply chunk c out of the LDS buffer, then write
+  // chunk c + 1 into it (a wave's LDS operations run in order, so the reads of
+  // chunk c come first)
   auto step = [&](auto qc, int c) {
     constexpr int Q = decltype(qc)::value;
-    if (c + 3 < nch) load(c + 3, xq[(Q + 3) & 3], wq[(Q + 3) & 3]);
-    // K past the wave's range (the last chunk when h / 8 is not a multiple
+    if (c + 3 < nch) load_x(c + 3, xq[(Q + 3) & 3]);
+    if (c + WD < nch) load_w(c + WD, wq[(Q + WD) % WS]);
+    // K past the wave's range (the last chunk when h / NW is not a multiple
     // of 64) multiplies zero
     const bool ragged = (c + 1) * 64 > kw;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      const unsigned char* p = buf + tro + s * 8 * RB;
-      const rt_s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((rt_lds_s16x4*)(rt_lds_t*)p);
-      const rt_s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((rt_lds_s16x4*)(rt_lds_t*)(p + 4 * RB));
-      const u32x2 a = __builtin_bit_cast(u32x2, lo), b = __builtin_bit_cast(u32x2, hi);
-      const u32x4 bf = u32x4{a[0], a[1], b[0], b[1]};
       const u32x4 xa = ragged && c * 64 + half * 32 + s * 8 >= kw ? u32x4{0, 0, 0, 0} : xq[Q][s];
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, xa),
-                                                    __builtin_bit_cast(bf16x8, bf), acc, 0, 0, 0);
+#pragma unroll
+      for (int nb = 0; nb < NT; ++nb) {
+        const unsigned char* p = buf + tro[nb] + s * 8 * RB;
+        const rt_s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((rt_lds_s16x4*)(rt_lds_t*)p);
+        const rt_s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((rt_lds_s16x4*)(rt_lds_t*)(p + 4 * RB));
+        const u32x2 a = __builtin_bit_cast(u32x2, lo), b = __builtin_bit_cast(u32x2, hi);
+        const u32x4 bf = u32x4{a[0], a[1], b[0], b[1]};
+        acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, xa),
+                                                         __builtin_bit_cast(bf16x8, bf), acc[nb], 0, 0, 0);
+      }
     }
-    if (c + 1 < nch) put(wq[(Q + 1) & 3]);
+    if (c + 1 < nch) put(wq[(Q + 1) % WS]);
   };
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
@@ -391,16 +422,20 @@ __global__ void __launch_bounds__(NW * 64) route_tr_kernel(const uint16_t* __res
   __syncthreads();
   // partial tiles -> LDS [K range][token][E], then sum in range order
   float* part = reinterpret_cast<float*>(wbuf);
-  if (l32 < E) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int i = 8 * (r >> 2) + 4 * half + (r & 3);
-      part[(kr * kRtTokens + i) * E + l32] = acc[r];
+  for (int nb = 0; nb < NT; ++nb) {
+    const int e = nb * 32 + l32;
+    if (e < E) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int i = 8 * (r >> 2) + 4 * half + (r & 3);
+        part[(kr * kRtTokens + i) * E + e] = acc[nb][r];
+      }
     }
   }
   __syncthreads();
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
+  for (int j = 0; j < NQ; ++j) {
     const int q = tid + j * NW * 64;
     if (q < kRtTokens * E) {
       float v = part[q];
@@ -418,7 +453,7 @@ __global__ void __launch_bounds__(NW * 64) route_tr_kernel(const uint16_t* __res
   // the logits last: no barrier waits for these stores
   if (logits_out) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+    for (int j = 0; j < NQ; ++j) {
       const int q = tid + j * NW * 64;
       if (q < nrow * E) logits_out[size_t(t0) * E + q] = part[q];
     }
@@ -498,20 +533,21 @@ int route(const void* x, const void* w_gate, const float* bias, float* logits, i
           int E, int k, int dtype, int32_t* topk_idx, float* topk_w, hipStream_t s) {
   if (T == 0) return MOE_OK;
   timer_begin(kTRoute, s);
-  if (x && dtype == MOE_BF16 && E % 8 == 0 && E <= 32) {
+  if (x && dtype == MOE_BF16 && E % 8 == 0 && E <= 64) {
     // sixteen waves (each K range a multiple of 8) where E = 8 keeps a
     // wave's registers within the 128 that four waves per SIMD allow
     const bool w16 = h % 128 == 0 && E == 8;
     const dim3 grid(ceil_div(T, kRtTokens)), block(w16 ? 1024 : 512);
     const uint16_t* xb = (const uint16_t*)x;
     const uint16_t* wb = (const uint16_t*)w_gate;
-    switch (E / 8 + (w16 ? 4 : 0)) {
+    switch (E / 8 + (w16 ? 8 : 0)) {
 #define MOE_RT(n, e8, nw)                                                                          \
   case n:                                                                                          \
     hipLaunchKernelGGL((route_tr_kernel<e8, nw>), grid, block, 0, s, xb, wb, bias, logits, T, h,  \
                        E, k, topk_idx, topk_w);                                                    \
     break;
-      MOE_RT(1, 1, 8) MOE_RT(2, 2, 8) MOE_RT(3, 3, 8) MOE_RT(4, 4, 8) MOE_RT(5, 1, 16)
+      MOE_RT(1, 1, 8) MOE_RT(2, 2, 8) MOE_RT(3, 3, 8) MOE_RT(4, 4, 8) MOE_RT(5, 5, 8)
+      MOE_RT(6, 6, 8) MOE_RT(7, 7, 8) MOE_RT(8, 8, 8) MOE_RT(9, 1, 16)
 #undef MOE_RT
     }
   } else if (x && dtype == MOE_BF16) {
