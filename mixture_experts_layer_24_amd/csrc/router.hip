@@ -272,14 +272,14 @@ __global__ void __launch_bounds__(RES ? 512 : 256) route_bf16_kernel(const uint1
 }
 
 // BF16 logits with W_g read in its own [h][E] layout (E a multiple of 8, at
-// most 64): eight waves split h, each streaming its K range in 64-row chunks.
+// most 64): eight (E = 8: sixteen) waves share out h in 64-row chunks.
 // x goes from HBM straight into A fragments (64 contiguous bytes per lane per
 // chunk); the chunk's W_g rows come into registers with 16-byte loads and
 // are written unchanged into the wave's own LDS buffer, from where transpose
 // reads (ds_read_b64_tr_b16) hand each lane four K-consecutive values of one
 // expert column: W_g is never rearranged.  x runs three chunks ahead of the
 // MFMAs, W_g three (E > 32: two); the waves meet only to sum their partial
-// 32 x E tiles (in K-range order), add the bias and pick the top k.
+// 32 x E tiles (in wave order), add the bias and pick the top k.
 typedef __attribute__((address_space(3))) void rt_lds_t;
 typedef short rt_s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) rt_s16x4 rt_lds_s16x4;
@@ -314,19 +314,24 @@ __global__ void __launch_bounds__(NW * 64) route_tr_kernel(const uint16_t* __res
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int half = lane >> 5, l32 = lane & 31;
   const int t0 = blockIdx.x * kRtTokens;
-  // Wave w takes K range (w + block) % NW: with the same range for the same
-  // wave everywhere, every workgroup would read the same offsets inside its
-  // rows at the same time, and with a power-of-two row pitch those land on
-  // a few HBM channels.  Partial tiles are summed in range order, so the
-  // rotation does not change the result.
-  const int kr = (wave + int(blockIdx.x)) % NW;
-  const int kw = h / NW, kbeg = kr * kw, nch = (kw + 63) / 64;
+  // The 64-row K chunks are dealt to the waves in turn (wave w: chunks w,
+  // w + NW, ...), so at any time the workgroup's waves read one contiguous
+  // span of every row (DRAM pages are opened for long runs, not 128 bytes
+  // per row), and each workgroup starts at its own place in its waves'
+  // sequences (with all of them at the same row offsets at once, a
+  // power-of-two row pitch would put their reads on a few HBM channels).
+  // A wave's partial tile is its chunks' products summed in its own order;
+  // the tiles are summed in wave order.
+  const int ncht = h / 64;                     // chunks of a row
+  const int nch = (ncht + NW - 1) / NW;        // steps per wave (chunks past ncht read zero)
+  const int rot = int(blockIdx.x) % nch;
+  auto chunk = [&](int j) { return (j + rot < nch ? j + rot : j + rot - nch) * NW + wave; };
   const int nrow = T - t0 < kRtTokens ? T - t0 : kRtTokens;
-  // x rows t0 .. t0 + nrow - 1 and the W_g rows of this wave's K range: the
-  // buffer descriptors read zero past them
+  // x rows t0 .. t0 + nrow - 1 and all of W_g: the buffer descriptors read
+  // zero past them
   const __amdgpu_buffer_rsrc_t rx = rt_rsrc(x, size_t(t0) * h * 2, size_t(nrow) * h * 2);
-  const __amdgpu_buffer_rsrc_t rw = rt_rsrc(wg, size_t(kbeg) * RB, size_t(kw) * RB);
-  const int xoff = (l32 * h + kbeg + half * 32) * 2;
+  const __amdgpu_buffer_rsrc_t rw = rt_rsrc(wg, 0, size_t(h) * RB);
+  const int xoff = (l32 * h + half * 32) * 2;
   unsigned char* buf = wbuf + wave * CB;
   // where lane l writes its 16 bytes of each 1 KB piece of a chunk
   const int wpos = kSwz ? (lane >> 3) * RB + (((lane & 7) ^ (((lane >> 4) & 1) * 4)) << 4) : lane * 16;
@@ -344,15 +349,18 @@ __global__ void __launch_bounds__(NW * 64) route_tr_kernel(const uint16_t* __res
   }
   // x chunk c sits in register slot c % 4, W_g chunk c in slot c % WS
   u32x4 xq[4][4], wq[WS][E8];
-  auto load_x = [&](int c, u32x4(&xa)[4]) {
+  // (step j works on chunk chunk(j))
+  auto load_x = [&](int j, u32x4(&xa)[4]) {
+    const int g = chunk(j);
 #pragma unroll
     for (int s = 0; s < 4; ++s)
-      xa[s] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, xoff + c * 128 + s * 16, 0, 0));
+      xa[s] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, xoff + s * 16, g * 128, 0));
   };
-  auto load_w = [&](int c, u32x4(&wa)[E8]) {
+  auto load_w = [&](int j, u32x4(&wa)[E8]) {
+    const int g = chunk(j);
 #pragma unroll
     for (int i = 0; i < E8; ++i)
-      wa[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, lane * 16, c * CB + i * 1024, 0));
+      wa[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, lane * 16, g * CB + i * 1024, 0));
   };
   auto put = [&](const u32x4(&wa)[E8]) {
 #pragma unroll
@@ -386,12 +394,12 @@ __global__ void __launch_bounds__(NW * 64) route_tr_kernel(const uint16_t* __res
     constexpr int Q = decltype(qc)::value;
     if (c + 3 < nch) load_x(c + 3, xq[(Q + 3) & 3]);
     if (c + WD < nch) load_w(c + WD, wq[(Q + WD) % WS]);
-    // K past the wave's range (the last chunk when h / NW is not a multiple
-    // of 64) multiplies zero
-    const bool ragged = (c + 1) * 64 > kw;
+    // a chunk past the row's end (h / 64 not a multiple of NW) multiplies
+    // zero: W_g reads zero there, and x would read the next row
+    const bool past = chunk(c) >= ncht;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      const u32x4 xa = ragged && c * 64 + half * 32 + s * 8 >= kw ? u32x4{0, 0, 0, 0} : xq[Q][s];
+      const u32x4 xa = past ? u32x4{0, 0, 0, 0} : xq[Q][s];
 #pragma unroll
       for (int nb = 0; nb < NT; ++nb) {
         const unsigned char* p = buf + tro[nb] + s * 8 * RB;
@@ -420,7 +428,7 @@ __global__ void __launch_bounds__(NW * 64) route_tr_kernel(const uint16_t* __res
   if (c + 1 < nch) step(I1{}, c + 1);
   if (c + 2 < nch) step(I2{}, c + 2);
   __syncthreads();
-  // partial tiles -> LDS [K range][token][E], then sum in range order
+  // partial tiles -> LDS [wave][token][E], then sum in wave order
   float* part = reinterpret_cast<float*>(wbuf);
 #pragma unroll
   for (int nb = 0; nb < NT; ++nb) {
@@ -429,7 +437,7 @@ __global__ void __launch_bounds__(NW * 64) route_tr_kernel(const uint16_t* __res
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int i = 8 * (r >> 2) + 4 * half + (r & 3);
-        part[(kr * kRtTokens + i) * E + e] = acc[nb][r];
+        part[(wave * kRtTokens + i) * E + e] = acc[nb][r];
       }
     }
   }
