@@ -160,14 +160,16 @@ def test_route_from_x(name, T):
 
 
 @pytest.mark.parametrize("T,h,E,k", [(300, 256, 8, 2), (257, 512, 64, 6), (130, 192, 100, 4),
-                                     (96, 1024, 16, 1), (64, 128, 256, 16)])
+                                     (96, 1024, 16, 1), (64, 128, 256, 16), (200, 384, 24, 3),
+                                     (150, 640, 40, 5), (97, 1152, 56, 4)])
 def test_route_from_x_selection_on_own_logits(T, h, E, k):
     """The BF16 router's top-k and softmax, applied to the logits it wrote,
     equal the oracle's selection on those same logits, element for element.
     Columns of W_g are duplicated so that whole groups of experts tie
     exactly (every column of the gate product runs the same instructions in
     the same order), which exercises the index tie rule; E = 100 takes the
-    W_g staging path for E not a multiple of 8."""
+    W_g staging path for E not a multiple of 8; E = 24, 40, 56 have a last
+    32-expert block that is partly empty (its columns wrap onto real ones)."""
     say(f"route selection T={T} h={h} E={E} k={k}")
     rng = np.random.default_rng(E * 7 + k)
     x = moe_synth.f32_to_bf16_bits(rng.standard_normal((T, h)).astype(np.float32))
