@@ -382,7 +382,10 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, f32x16 (&acc)[C::kMI
             G *= xs * sg;
             U *= xs * su;
           }
-          const float a = silu_f(G) * U;
+          // BF16 stores A rounded to 8 bits, so the hardware reciprocal (1 ulp)
+          // replaces the division there (Mixtral-shaped FC1 -0.6%); FP8
+          // quantizes the fp32 A itself and keeps the correctly rounded division
+          const float a = (DT == MOE_BF16 ? G * __builtin_amdgcn_rcpf(1.0f + __expf(-G)) : silu_f(G)) * U;
           if (row < row_end) {
             if (DT == MOE_BF16) {
               static_cast<uint16_t*>(g.out)[size_t(row) * hf + ch] = uint16_t(f32_to_bf16_bits(a));
