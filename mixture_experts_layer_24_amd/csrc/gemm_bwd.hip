@@ -29,8 +29,9 @@ namespace moe {
 // multiple of 64: one 128-byte K slab of the GEMM's element type) and zeros
 // beyond M_e.
 //
-// One workgroup per (64 columns, expert) walks the expert's rows in blocks of
-// 64: each thread loads 16 bytes of two adjacent rows (eight threads cover a
+// A work item is (64 columns, expert); workgroups take items i, i + G, ...
+// (G = gridDim.x), the 64-column strips of one expert being consecutive items.
+// An item walks the expert's rows in blocks of 64: each thread loads 16 bytes of two adjacent rows (eight threads cover a
 // 128-byte row segment), packs the two rows' values of each column into one
 // 32-bit word in LDS (column-major, 33 words per column: conflict-free
 // stores), then reads 8 words = 16 consecutive rows of one column and stores
@@ -39,7 +40,9 @@ namespace moe {
 //
 // Codes are quantized per channel over the expert's rows (scale[e][c] =
 // amax / 448, 1 for a zero channel or an expert without rows); a first pass
-// over the same rows takes the column amax.
+// over the same rows takes the column amax.  The second pass re-reads them
+// from the Infinity Cache when the strips of the items in progress fit there,
+// which the launcher arranges by bounding the grid.
 __global__ void __launch_bounds__(256) xpose_kernel(const uint16_t* __restrict__ src, int C,
                                                     const int32_t* __restrict__ offsets, int E,
                                                     int rows, int pad, void* __restrict__ dst,
@@ -67,86 +70,91 @@ __global__ void __launch_bounds__(256) xpose_kernel(const uint16_t* __restrict__
     kpre[E] = kp;
   }
   __syncthreads();
-  const int e = blockIdx.y, c0 = blockIdx.x * 64;
-  const int r0 = offs[e], m = offs[e + 1] - r0, kp = kpre[e + 1] - kpre[e];
-  if (kp == 0) {
-    if (tid < 64 && c0 + tid < C) scale[size_t(e) * C + c0 + tid] = 1.0f;
-    return;
-  }
   const int q = tid & 7, p = tid >> 3;  // 8-column chunk, row pair
-  const uint16_t* sp = src + size_t(r0) * C + c0 + q * 8;
-  auto ld = [&](int r) {
-    u32x4 v = {0, 0, 0, 0};
-    if (r < m) v = *reinterpret_cast<const u32x4*>(sp + size_t(r) * C);
-    return v;
-  };
-  // the encoding pass is the rows' last use: nontemporal loads (DeepSeekMoE-
-  // shaped FP8 step: the four transposes 1.09 -> 0.95 ms)
-  auto ldn = [&](int r) {
-    u32x4 v = {0, 0, 0, 0};
-    if (r < m) v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(sp + size_t(r) * C));
-    return v;
-  };
-  {
-    float am[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) am[j] = 0.f;
-    // four rows per thread in flight (rows past the expert read as zeros)
-    for (int r = p; r < m; r += 128) {
-      u32x4 v[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) v[u] = ld(r + 32 * u);
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          am[2 * i] = fmaxf(am[2 * i], fabsf(bf16_lo(v[u][i])));
-          am[2 * i + 1] = fmaxf(am[2 * i + 1], fabsf(bf16_hi(v[u][i])));
-        }
+  const int ns = C / 64;
+  // every barrier below is reached by the whole workgroup: the item loop's
+  // bounds and kp are uniform
+  for (int item = blockIdx.x; item < ns * E; item += gridDim.x) {
+    const int e = item / ns, c0 = (item - e * ns) * 64;
+    const int r0 = offs[e], m = offs[e + 1] - r0, kp = kpre[e + 1] - kpre[e];
+    if (kp == 0) {
+      if (tid < 64 && c0 + tid < C) scale[size_t(e) * C + c0 + tid] = 1.0f;
+      continue;
     }
-    float* red = reinterpret_cast<float*>(tile);
+    const uint16_t* sp = src + size_t(r0) * C + c0 + q * 8;
+    auto ld = [&](int r) {
+      u32x4 v = {0, 0, 0, 0};
+      if (r < m) v = *reinterpret_cast<const u32x4*>(sp + size_t(r) * C);
+      return v;
+    };
+    // the encoding pass is the rows' last use: nontemporal loads (DeepSeekMoE-
+    // shaped FP8 step: the four transposes 1.09 -> 0.95 ms)
+    auto ldn = [&](int r) {
+      u32x4 v = {0, 0, 0, 0};
+      if (r < m) v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(sp + size_t(r) * C));
+      return v;
+    };
+    {
+      float am[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) red[(q * 8 + j) * 33 + p] = am[j];
-    __syncthreads();
-    if (tid < 64) {
-      float a = 0.f;
-      for (int i = 0; i < 32; ++i) a = fmaxf(a, red[tid * 33 + i]);
-      const float sc = a > 0.f ? a / 448.0f : 1.0f;
-      cscale[tid] = sc;
-      if (c0 + tid < C) scale[size_t(e) * C + c0 + tid] = sc;
+      for (int j = 0; j < 8; ++j) am[j] = 0.f;
+      // four rows per thread in flight (rows past the expert read as zeros)
+      for (int r = p; r < m; r += 128) {
+        u32x4 v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) v[u] = ld(r + 32 * u);
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            am[2 * i] = fmaxf(am[2 * i], fabsf(bf16_lo(v[u][i])));
+            am[2 * i + 1] = fmaxf(am[2 * i + 1], fabsf(bf16_hi(v[u][i])));
+          }
+      }
+      float* red = reinterpret_cast<float*>(tile);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) red[(q * 8 + j) * 33 + p] = am[j];
+      __syncthreads();
+      if (tid < 64) {
+        float a = 0.f;
+        for (int i = 0; i < 32; ++i) a = fmaxf(a, red[tid * 33 + i]);
+        const float sc = a > 0.f ? a / 448.0f : 1.0f;
+        cscale[tid] = sc;
+        if (c0 + tid < C) scale[size_t(e) * C + c0 + tid] = sc;
+      }
+      __syncthreads();
     }
-    __syncthreads();
-  }
-  const int c = tid >> 2, kk = (tid & 3) * 16;  // output column, first of its 16 rows
-  const size_t obase = size_t(kpre[e]) * C + size_t(c0 + c) * kp + kk;
-  const float sc = cscale[c];
-  const QuotScale qs = quot_scale(sc);
-  // loads run two 64-row blocks ahead of the LDS work
-  u32x4 va = ldn(2 * p), vb = ldn(2 * p + 1), na = ldn(64 + 2 * p), nb = ldn(65 + 2 * p);
-  for (int k0 = 0; k0 < kp; k0 += 64) {
-    const u32x4 fa = ldn(k0 + 128 + 2 * p), fb = ldn(k0 + 129 + 2 * p);
+    const int c = tid >> 2, kk = (tid & 3) * 16;  // output column, first of its 16 rows
+    const size_t obase = size_t(kpre[e]) * C + size_t(c0 + c) * kp + kk;
+    const float sc = cscale[c];
+    const QuotScale qs = quot_scale(sc);
+    // loads run two 64-row blocks ahead of the LDS work
+    u32x4 va = ldn(2 * p), vb = ldn(2 * p + 1), na = ldn(64 + 2 * p), nb = ldn(65 + 2 * p);
+    for (int k0 = 0; k0 < kp; k0 += 64) {
+      const u32x4 fa = ldn(k0 + 128 + 2 * p), fb = ldn(k0 + 129 + 2 * p);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      tile[(q * 8 + 2 * i) * 33 + p] = (va[i] & 0xFFFFu) | (vb[i] << 16);
-      tile[(q * 8 + 2 * i + 1) * 33 + p] = (va[i] >> 16) | (vb[i] & 0xFFFF0000u);
+      for (int i = 0; i < 4; ++i) {
+        tile[(q * 8 + 2 * i) * 33 + p] = (va[i] & 0xFFFFu) | (vb[i] << 16);
+        tile[(q * 8 + 2 * i + 1) * 33 + p] = (va[i] >> 16) | (vb[i] & 0xFFFF0000u);
+      }
+      __syncthreads();
+      uint32_t w[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) w[i] = tile[c * 33 + (kk >> 1) + i];
+      if (c0 + c < C) {
+        u32x4 o;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          o[i] = e4m3x4_quot(bf16_lo(w[2 * i]), bf16_hi(w[2 * i]), bf16_lo(w[2 * i + 1]),
+                             bf16_hi(w[2 * i + 1]), qs);
+        *reinterpret_cast<u32x4*>(static_cast<uint8_t*>(dst) + obase + k0) = o;
+      }
+      __syncthreads();
+      va = na;
+      vb = nb;
+      na = fa;
+      nb = fb;
     }
-    __syncthreads();
-    uint32_t w[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) w[i] = tile[c * 33 + (kk >> 1) + i];
-    if (c0 + c < C) {
-      u32x4 o;
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        o[i] = e4m3x4_quot(bf16_lo(w[2 * i]), bf16_hi(w[2 * i]), bf16_lo(w[2 * i + 1]),
-                           bf16_hi(w[2 * i + 1]), qs);
-      *reinterpret_cast<u32x4*>(static_cast<uint8_t*>(dst) + obase + k0) = o;
-    }
-    __syncthreads();
-    va = na;
-    vb = nb;
-    na = fa;
-    nb = fb;
   }
 }
 
@@ -265,7 +273,20 @@ size_t grouped_bwd_fp8_ws_bytes(int rows, int h, int h_ffn, int E) {
 static int xpose_q(const void* src, int C, const int32_t* offsets, int E, int rows, void* dst,
                    float* scale, hipStream_t s) {
   if (C % 64 != 0) return MOE_ERR_SHAPE;
-  hipLaunchKernelGGL(xpose_kernel, dim3(C / 64, E), dim3(256), 0, s, (const uint16_t*)src, C,
+  // Workgroups per CU: as many as keep the strips of the items in progress
+  // (128 bytes per row of the expert, read twice) within ~192 MiB, so the
+  // encoding pass finds them in the 256 MB Infinity Cache; at least 4 to keep
+  // enough loads in flight, at most 8 (the occupancy the kernel reaches).
+  // DeepSeekMoE-shaped FP8 step (1536 rows per expert): 4 per CU, the four
+  // transposes 0.95 -> 0.86 ms; with 6-8 per CU the strips no longer fit and
+  // with 3 or fewer the loads in flight fall short (both 0.95 ms).
+  const int items = (C / 64) * E;
+  const double strip = 128.0 * (double(rows) / (E > 0 ? E : 1) + 1.0);
+  int per_cu = int((192.0 * 1024 * 1024) / (double(num_cus()) * strip));
+  per_cu = per_cu < 4 ? 4 : (per_cu > 8 ? 8 : per_cu);
+  const int grid = items < num_cus() * per_cu ? items : num_cus() * per_cu;
+  if (grid <= 0) return MOE_OK;
+  hipLaunchKernelGGL(xpose_kernel, dim3(grid), dim3(256), 0, s, (const uint16_t*)src, C,
                      offsets, E, rows, kpad_elems<MOE_FP8_E4M3>(), dst, scale);
   return launch_status();
 }

@@ -48,6 +48,9 @@ CASES = [
     ("multi_tile", dict(T=2100, h=512, h_ffn=384, E=4, k=2), 4),
     ("one_expert", dict(T=77, h=256, h_ffn=128, E=1, k=1), 6),
     ("zipf_empty", dict(T=300, h=256, h_ffn=256, E=16, k=2, zipf_s=2.5), 7),
+    # dG|dU has 2816 columns: 44 strips x 64 experts = 2816 transpose work
+    # items, more than the transposes' bounded grid, so workgroups take several
+    ("many_strips", dict(T=200, h=256, h_ffn=1408, E=64, k=6), 8),
 ]
 
 
