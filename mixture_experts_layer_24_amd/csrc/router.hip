@@ -350,11 +350,15 @@ __global__ void __launch_bounds__(NW * 64) route_tr_kernel(const uint16_t* __res
   // x chunk c sits in register slot c % 4, W_g chunk c in slot c % WS
   u32x4 xq[4][4], wq[WS][E8];
   // (step j works on chunk chunk(j))
+  // a chunk past the row's end (h / 64 not a multiple of NW) is loaded from
+  // an offset beyond the descriptor, which reads zeros (in place it would
+  // read the next row); W_g reads zero there too, so such a chunk adds 0
   auto load_x = [&](int j, u32x4(&xa)[4]) {
     const int g = chunk(j);
+    const int so = g < ncht ? g * 128 : (1 << 30);
 #pragma unroll
     for (int s = 0; s < 4; ++s)
-      xa[s] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, xoff + s * 16, g * 128, 0));
+      xa[s] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, xoff + s * 16, so, 0));
   };
   auto load_w = [&](int j, u32x4(&wa)[E8]) {
     const int g = chunk(j);
@@ -394,12 +398,9 @@ __global__ void __launch_bounds__(NW * 64) route_tr_kernel(const uint16_t* __res
     constexpr int Q = decltype(qc)::value;
     if (c + 3 < nch) load_x(c + 3, xq[(Q + 3) & 3]);
     if (c + WD < nch) load_w(c + WD, wq[(Q + WD) % WS]);
-    // a chunk past the row's end (h / 64 not a multiple of NW) multiplies
-    // zero: W_g reads zero there, and x would read the next row
-    const bool past = chunk(c) >= ncht;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      const u32x4 xa = past ? u32x4{0, 0, 0, 0} : xq[Q][s];
+      const u32x4 xa = xq[Q][s];
 #pragma unroll
       for (int nb = 0; nb < NT; ++nb) {
         const unsigned char* p = buf + tro[nb] + s * 8 * RB;
