@@ -31,11 +31,11 @@ namespace moe {
 //
 // A work item is (64 columns, expert); workgroups take items i, i + G, ...
 // (G = gridDim.x), the 64-column strips of one expert being consecutive items.
-// An item walks the expert's rows in blocks of 64: each thread loads 16 bytes of two adjacent rows (eight threads cover a
-// 128-byte row segment), packs the two rows' values of each column into one
-// 32-bit word in LDS (column-major, 33 words per column: conflict-free
-// stores), then reads 8 words = 16 consecutive rows of one column and stores
-// their codes contiguously.  The loads of the next two blocks are in flight
+// An item walks the expert's rows in blocks of 64: each thread loads 16 bytes
+// of two adjacent rows (eight threads cover a 128-byte row segment), packs the
+// two rows' values of each column into one 32-bit word in LDS (column-major,
+// 33 words per column: conflict-free stores), then reads 8 words = 16
+// consecutive rows of one column and stores their codes contiguously.  The loads of the next two blocks are in flight
 // during this block's LDS work.
 //
 // Codes are quantized per channel over the expert's rows (scale[e][c] =
