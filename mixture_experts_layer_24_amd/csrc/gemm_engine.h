@@ -358,6 +358,8 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, f32x16 (&acc)[C::kMI
   const int e = T.e, row0 = T.row0, row_end = T.row_end, n0 = T.n0;
   const int rbase = row0 + wm * (MI * 32);   // the wave's first row
   const int cbase = n0 + wn * (NJ * 32);     // the wave's first column
+  const int wrow = __builtin_amdgcn_readfirstlane(wm * (MI * 32));  // the same, relative to the tile
+  const int nrow = row_end - row0 < C::kBM ? row_end - row0 : C::kBM;  // rows of the tile
   if (MODE == kModeFC1) {
     static_assert(MODE != kModeFC1 || NJ % 2 == 0, "FC1 pairs gate and up blocks");
     const int hf = g.N / 2;
@@ -373,6 +375,40 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, f32x16 (&acc)[C::kMI
           sg = g.b_scale[size_t(e) * g.N + colg];
           su = g.b_scale[size_t(e) * g.N + colg + 32];
         }
+        if constexpr (DT == MOE_BF16) {
+          // Buffer stores: the row offset (uniform in the wave) goes in the
+          // scalar offset, the lane's column in the vector offset, and the
+          // descriptors end at the expert's last row, so rows past it are
+          // dropped without a compare and a branch per value (in place of a
+          // 64-bit address per value: Mixtral-shaped FC1 3.47 -> 3.41 ms; with
+          // the same change in the FC2, dA and weight-gradient epilogues the
+          // DeepSeekMoE-shaped training step 7.39 -> 7.30 ms).  A is stored
+          // rounded to bf16, so the hardware reciprocal (1 ulp) replaces the
+          // division (Mixtral-shaped FC1 -0.6%).
+          const int rowa = hf * 2, rows = g.N * 2;
+          const __amdgpu_buffer_rsrc_t ra = rsrc(g.out, size_t(row0) * rowa, size_t(nrow) * rowa);
+          const __amdgpu_buffer_rsrc_t rs =
+              rsrc(g.save ? g.save : g.out, size_t(row0) * rows, g.save ? size_t(nrow) * rows : 0);
+          const int va = 4 * half * rowa + ch * 2, vs = 4 * half * rows + colg * 2;
+          auto stores = [&](auto keep) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int srow = wrow + acc_row(i, r, 0);  // the lane's row, less 4 * half
+              const float G = acc[i][2 * p][r], U = acc[i][2 * p + 1][r];
+              const float a = G * __builtin_amdgcn_rcpf(1.0f + __expf(-G)) * U;
+              __builtin_amdgcn_raw_buffer_store_b16(uint16_t(f32_to_bf16_bits(a)), ra, va, srow * rowa, 0);
+              if constexpr (decltype(keep)::value) {
+                // G|U kept for the backward, read again only there:
+                // nontemporal stores (DeepSeekMoE-shaped FC1 -2%)
+                __builtin_amdgcn_raw_buffer_store_b16(uint16_t(f32_to_bf16_bits(G)), rs, vs, srow * rows, 2);
+                __builtin_amdgcn_raw_buffer_store_b16(uint16_t(f32_to_bf16_bits(U)), rs, vs + 64, srow * rows, 2);
+              }
+            }
+          };
+          if (g.save) stores(std::true_type{});
+          else stores(std::false_type{});
+          continue;
+        }
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int row = rbase + acc_row(i, r, half);
@@ -382,14 +418,10 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, f32x16 (&acc)[C::kMI
             G *= xs * sg;
             U *= xs * su;
           }
-          // BF16 stores A rounded to 8 bits, so the hardware reciprocal (1 ulp)
-          // replaces the division there (Mixtral-shaped FC1 -0.6%); FP8
-          // quantizes the fp32 A itself and keeps the correctly rounded division
-          const float a = (DT == MOE_BF16 ? G * __builtin_amdgcn_rcpf(1.0f + __expf(-G)) : silu_f(G)) * U;
+          // fp32 A (FP8 quantizes this exact value): the correctly rounded division
+          const float a = silu_f(G) * U;
           if (row < row_end) {
-            if (DT == MOE_BF16) {
-              static_cast<uint16_t*>(g.out)[size_t(row) * hf + ch] = uint16_t(f32_to_bf16_bits(a));
-            } else {
+            {
               // fp32 A; for FP8 the per-row quantization reads this exact value
               static_cast<float*>(g.out)[size_t(row) * hf + ch] = a;
               if (DT == MOE_FP8_E4M3) rmax[r] = p == 0 ? fabsf(a) : fmaxf(rmax[r], fabsf(a));
@@ -436,6 +468,33 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, f32x16 (&acc)[C::kMI
       }
       __syncthreads();
     }
+  } else if (MODE == kModeFC2 && DT != MOE_FP8_E4M3) {
+    // buffer stores as in FC1: row offset scalar, column per lane, rows past
+    // the expert dropped by the descriptor
+    const bool f32o = DT == MOE_F32 || g.out_f32;
+    const int rowb = g.N * (f32o ? 4 : 2);
+    const __amdgpu_buffer_rsrc_t ro = rsrc(g.out, size_t(row0) * rowb, size_t(nrow) * rowb);
+    auto stores = [&](auto f32c) {
+      constexpr bool F = decltype(f32c)::value;
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const int col = cbase + j * 32 + l32;
+        if (col >= g.N) continue;
+        const int vo = 4 * half * rowb + col * (F ? 4 : 2);
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int so = (wrow + acc_row(i, r, 0)) * rowb;
+            if constexpr (F)
+              __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[i][j][r]), ro, vo, so, 0);
+            else
+              __builtin_amdgcn_raw_buffer_store_b16(uint16_t(f32_to_bf16_bits(acc[i][j][r])), ro, vo, so, 0);
+          }
+      }
+    };
+    if (f32o) stores(std::true_type{});
+    else stores(std::false_type{});
   } else if (MODE == kModeFC2) {
 #pragma unroll
     for (int i = 0; i < MI; ++i)
@@ -494,6 +553,33 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, f32x16 (&acc)[C::kMI
         }
         __builtin_amdgcn_s_waitcnt(0);
         if (f >= hf) continue;
+        if constexpr (DT != MOE_FP8_E4M3) {
+          // buffer stores (row offset scalar, column per lane, rows past the
+          // expert dropped by the descriptors), as in the forward epilogues
+          const int rgu = 4 * hf, ra = 2 * hf;  // bytes per dG|dU row, per A row
+          const __amdgpu_buffer_rsrc_t dgr = rsrc(g.out, size_t(row0) * rgu, size_t(nrow) * rgu);
+          const __amdgpu_buffer_rsrc_t ar = rsrc(g.out2, size_t(row0) * ra, size_t(nrow) * ra);
+          const int vg = 4 * half * rgu + pg * 2, vaa = 4 * half * ra + f * 2;
+#pragma unroll
+          for (int ii = 0; ii < kIPer; ++ii) {
+            const int i = ic * kIPer + ii;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int rl = acc_row(ii, r, half);   // row inside the chunk
+              const int srow = wrow + ic * kRows + acc_row(ii, r, 0);  // tile row, less 4 * half
+              const float G = bf16_to_f32(wl16[rl * 64 + l32]), U = bf16_to_f32(wl16[rl * 64 + 32 + l32]);
+              const float sg = 1.0f / (1.0f + __expf(-G));
+              const float si = G * sg;
+              const float dA = acc[i][j][r];
+              __builtin_amdgcn_raw_buffer_store_b16(
+                  uint16_t(f32_to_bf16_bits(dA * U * sg * (1.0f + G * (1.0f - sg)))), dgr, vg, srow * rgu, 0);
+              __builtin_amdgcn_raw_buffer_store_b16(uint16_t(f32_to_bf16_bits(dA * si)), dgr, vg + 64,
+                                                    srow * rgu, 0);
+              __builtin_amdgcn_raw_buffer_store_b16(uint16_t(f32_to_bf16_bits(si * U)), ar, vaa, srow * ra, 0);
+            }
+          }
+          continue;
+        }
 #pragma unroll
         for (int ii = 0; ii < kIPer; ++ii) {
           const int i = ic * kIPer + ii;
@@ -517,6 +603,28 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, f32x16 (&acc)[C::kMI
     }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();  // the idle stage is refilled by the next tile's loads
+  } else if (DT != MOE_FP8_E4M3) {
+    // weight gradients, fp32: rows m of expert e's [M][N] (DW13: N packed,
+    // 32-column blocks alternating dW1 / dW3, so the target is uniform per
+    // block); buffer stores as in the forward epilogues
+    const int ld = MODE == kModeDW13 ? g.N / 2 : g.N;
+    const int rowb = ld * 4;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int n = cbase + j * 32 + l32;
+      if (n >= g.N) continue;
+      const int nb = (cbase >> 5) + j;  // 32-column block
+      const void* dst = (MODE == kModeDW13 && (nb & 1)) ? g.out2 : g.out;
+      const int col = MODE == kModeDW13 ? (nb >> 1) * 32 + l32 : n;
+      const __amdgpu_buffer_rsrc_t ro = rsrc(dst, (size_t(e) * g.M + row0) * rowb, size_t(nrow) * rowb);
+      const int vo = 4 * half * rowb + col * 4;
+#pragma unroll
+      for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[i][j][r]), ro, vo,
+                                                (wrow + acc_row(i, r, 0)) * rowb, 0);
+    }
   } else {
     // weight gradients, fp32: rows m of expert e's [M][N] (DW13: N packed)
     float* o1 = static_cast<float*>(g.out);
