@@ -409,34 +409,39 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, f32x16 (&acc)[C::kMI
           else stores(std::false_type{});
           continue;
         }
+        // FP8 and fp32: fp32 A through the same buffer stores; FP8 reads each
+        // row's scale through a descriptor ending at the expert too, so a row
+        // past it has scale 0, A = 0 and adds nothing to the row maxima
+        const int rowa = hf * 4, rows = g.N * 2;
+        const __amdgpu_buffer_rsrc_t ra = rsrc(g.out, size_t(row0) * rowa, size_t(nrow) * rowa);
+        const __amdgpu_buffer_rsrc_t rs =
+            rsrc(g.save ? g.save : g.out, size_t(row0) * rows, g.save ? size_t(nrow) * rows : 0);
+        const __amdgpu_buffer_rsrc_t rx = rsrc(DT == MOE_FP8_E4M3 ? static_cast<const void*>(g.a_scale) : g.out,
+                                               size_t(row0) * 4, DT == MOE_FP8_E4M3 ? size_t(nrow) * 4 : 0);
+        const int va = 4 * half * rowa + ch * 4, vs = 4 * half * rows + colg * 2, vx = 4 * half * 4;
+        auto rows_out = [&](auto keep) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = rbase + acc_row(i, r, half);
-          float G = acc[i][2 * p][r], U = acc[i][2 * p + 1][r];
-          if (DT == MOE_FP8_E4M3) {
-            const float xs = row < row_end ? g.a_scale[row] : 0.f;
-            G *= xs * sg;
-            U *= xs * su;
-          }
-          // fp32 A (FP8 quantizes this exact value): the correctly rounded division
-          const float a = silu_f(G) * U;
-          if (row < row_end) {
-            {
-              // fp32 A; for FP8 the per-row quantization reads this exact value
-              static_cast<float*>(g.out)[size_t(row) * hf + ch] = a;
-              if (DT == MOE_FP8_E4M3) rmax[r] = p == 0 ? fabsf(a) : fmaxf(rmax[r], fabsf(a));
+          for (int r = 0; r < 16; ++r) {
+            const int srow = wrow + acc_row(i, r, 0);  // the lane's row, less 4 * half
+            float G = acc[i][2 * p][r], U = acc[i][2 * p + 1][r];
+            if (DT == MOE_FP8_E4M3) {
+              const float xs = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rx, vx, srow * 4, 0));
+              G *= xs * sg;
+              U *= xs * su;
             }
-            if (g.save) {
+            // fp32 A, which FP8 quantizes per row: the correctly rounded division
+            const float a = silu_f(G) * U;
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(a), ra, va, srow * rowa, 0);
+            if (DT == MOE_FP8_E4M3) rmax[r] = p == 0 ? fabsf(a) : fmaxf(rmax[r], fabsf(a));
+            if constexpr (decltype(keep)::value) {
               // G|U kept for the backward, read again only there: nontemporal
-              // stores (DeepSeekMoE-shaped FC1 -2%)
-              uint16_t* sv = static_cast<uint16_t*>(g.save) + size_t(row) * g.N + colg;
-              __builtin_nontemporal_store(uint16_t(f32_to_bf16_bits(G)), sv);
-              __builtin_nontemporal_store(uint16_t(f32_to_bf16_bits(U)), sv + 32);
+              __builtin_amdgcn_raw_buffer_store_b16(uint16_t(f32_to_bf16_bits(G)), rs, vs, srow * rows, 2);
+              __builtin_amdgcn_raw_buffer_store_b16(uint16_t(f32_to_bf16_bits(U)), rs, vs + 64, srow * rows, 2);
             }
-          } else if (DT == MOE_FP8_E4M3) {
-            rmax[r] = 0.f;
           }
-        }
+        };
+        if (g.save) rows_out(std::true_type{});
+        else rows_out(std::false_type{});
       }
       if (DT == MOE_FP8_E4M3) {
         // row max over this wave's channels: reduce over the 32 lanes of a
@@ -468,12 +473,15 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, f32x16 (&acc)[C::kMI
       }
       __syncthreads();
     }
-  } else if (MODE == kModeFC2 && DT != MOE_FP8_E4M3) {
+  } else if (MODE == kModeFC2) {
     // buffer stores as in FC1: row offset scalar, column per lane, rows past
-    // the expert dropped by the descriptor
+    // the expert dropped by the descriptor (FP8: their scales read 0)
     const bool f32o = DT == MOE_F32 || g.out_f32;
     const int rowb = g.N * (f32o ? 4 : 2);
     const __amdgpu_buffer_rsrc_t ro = rsrc(g.out, size_t(row0) * rowb, size_t(nrow) * rowb);
+    const __amdgpu_buffer_rsrc_t rx = rsrc(DT == MOE_FP8_E4M3 ? static_cast<const void*>(g.a_scale) : g.out,
+                                           size_t(row0) * 4, DT == MOE_FP8_E4M3 ? size_t(nrow) * 4 : 0);
+    const int vx = 4 * half * 4;
     auto stores = [&](auto f32c) {
       constexpr bool F = decltype(f32c)::value;
 #pragma unroll
@@ -481,42 +489,25 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, f32x16 (&acc)[C::kMI
         const int col = cbase + j * 32 + l32;
         if (col >= g.N) continue;
         const int vo = 4 * half * rowb + col * (F ? 4 : 2);
+        float cs = 1.f;
+        if (DT == MOE_FP8_E4M3) cs = g.b_scale[size_t(e) * g.N + col];
 #pragma unroll
         for (int i = 0; i < MI; ++i)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int so = (wrow + acc_row(i, r, 0)) * rowb;
+            float y = acc[i][j][r];
+            if (DT == MOE_FP8_E4M3)
+              y *= __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rx, vx, (wrow + acc_row(i, r, 0)) * 4, 0)) * cs;
             if constexpr (F)
-              __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[i][j][r]), ro, vo, so, 0);
+              __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(y), ro, vo, so, 0);
             else
-              __builtin_amdgcn_raw_buffer_store_b16(uint16_t(f32_to_bf16_bits(acc[i][j][r])), ro, vo, so, 0);
+              __builtin_amdgcn_raw_buffer_store_b16(uint16_t(f32_to_bf16_bits(y)), ro, vo, so, 0);
           }
       }
     };
     if (f32o) stores(std::true_type{});
     else stores(std::false_type{});
-  } else if (MODE == kModeFC2) {
-#pragma unroll
-    for (int i = 0; i < MI; ++i)
-#pragma unroll
-      for (int j = 0; j < NJ; ++j) {
-        const int col = cbase + j * 32 + l32;
-        if (col >= g.N) continue;
-        float cs = 1.f;
-        if (DT == MOE_FP8_E4M3) cs = g.b_scale[size_t(e) * g.N + col];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = rbase + acc_row(i, r, half);
-          if (row < row_end) {
-            float y = acc[i][j][r];
-            if (DT == MOE_FP8_E4M3) y *= g.a_scale[row] * cs;
-            if (DT == MOE_F32 || g.out_f32)
-              static_cast<float*>(g.out)[size_t(row) * g.N + col] = y;
-            else
-              static_cast<uint16_t*>(g.out)[size_t(row) * g.N + col] = uint16_t(f32_to_bf16_bits(y));
-          }
-        }
-      }
   } else if (MODE == kModeBwdDA) {
     // dA tile -> dG, dU (packed like the forward's G|U) and A = SiLU(G)*U.
     // For each 32-channel block j, the kept G|U of the wave's rows (64 packed
@@ -528,8 +519,6 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, f32x16 (&acc)[C::kMI
     constexpr int kIPer = kRows / 32;                        // MFMA blocks per chunk
     static_assert(kIPer >= 1 && MI % kIPer == 0, "chunk of whole MFMA blocks");
     const int hf = g.N;
-    uint16_t* __restrict__ dgu = static_cast<uint16_t*>(g.out);
-    uint16_t* __restrict__ aout = static_cast<uint16_t*>(g.out2);
     const size_t rowb = size_t(2 * hf) * 2;  // bytes per G|U row
     unsigned char* wl = free_lds + wave * kRegion;
     const uint16_t* wl16 = reinterpret_cast<const uint16_t*>(wl);
@@ -539,7 +528,7 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, f32x16 (&acc)[C::kMI
       const int fb0 = cbase + j * 32;              // first channel of the group
       const int pb = (fb0 >> 5) * 64;              // its first packed column
       const int f = fb0 + l32;
-      const int pg = pb + l32, pu = pg + 32;
+      const int pg = pb + l32;
 #pragma unroll
       for (int ic = 0; ic < MI / kIPer; ++ic) {
         const int crow0 = rbase + ic * kRows;
@@ -553,12 +542,17 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, f32x16 (&acc)[C::kMI
         }
         __builtin_amdgcn_s_waitcnt(0);
         if (f >= hf) continue;
-        if constexpr (DT != MOE_FP8_E4M3) {
+        {
           // buffer stores (row offset scalar, column per lane, rows past the
-          // expert dropped by the descriptors), as in the forward epilogues
+          // expert dropped by the descriptors), as in the forward epilogues;
+          // FP8 reads the rows' scales the same way
           const int rgu = 4 * hf, ra = 2 * hf;  // bytes per dG|dU row, per A row
           const __amdgpu_buffer_rsrc_t dgr = rsrc(g.out, size_t(row0) * rgu, size_t(nrow) * rgu);
           const __amdgpu_buffer_rsrc_t ar = rsrc(g.out2, size_t(row0) * ra, size_t(nrow) * ra);
+          const __amdgpu_buffer_rsrc_t rx =
+              rsrc(DT == MOE_FP8_E4M3 ? static_cast<const void*>(g.a_scale) : g.out, size_t(row0) * 4,
+                   DT == MOE_FP8_E4M3 ? size_t(nrow) * 4 : 0);
+          const float bs = DT == MOE_FP8_E4M3 ? g.b_scale[size_t(e) * g.N + f] : 1.f;
           const int vg = 4 * half * rgu + pg * 2, vaa = 4 * half * ra + f * 2;
 #pragma unroll
           for (int ii = 0; ii < kIPer; ++ii) {
@@ -570,7 +564,9 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, f32x16 (&acc)[C::kMI
               const float G = bf16_to_f32(wl16[rl * 64 + l32]), U = bf16_to_f32(wl16[rl * 64 + 32 + l32]);
               const float sg = 1.0f / (1.0f + __expf(-G));
               const float si = G * sg;
-              const float dA = acc[i][j][r];
+              float dA = acc[i][j][r];
+              if (DT == MOE_FP8_E4M3)
+                dA *= __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rx, 4 * half * 4, srow * 4, 0)) * bs;
               __builtin_amdgcn_raw_buffer_store_b16(
                   uint16_t(f32_to_bf16_bits(dA * U * sg * (1.0f + G * (1.0f - sg)))), dgr, vg, srow * rgu, 0);
               __builtin_amdgcn_raw_buffer_store_b16(uint16_t(f32_to_bf16_bits(dA * si)), dgr, vg + 64,
@@ -578,35 +574,16 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, f32x16 (&acc)[C::kMI
               __builtin_amdgcn_raw_buffer_store_b16(uint16_t(f32_to_bf16_bits(si * U)), ar, vaa, srow * ra, 0);
             }
           }
-          continue;
-        }
-#pragma unroll
-        for (int ii = 0; ii < kIPer; ++ii) {
-          const int i = ic * kIPer + ii;
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int rl = acc_row(ii, r, half);   // row inside the chunk
-            const int row = crow0 + rl;
-            if (row >= row_end) continue;
-            const float G = bf16_to_f32(wl16[rl * 64 + l32]), U = bf16_to_f32(wl16[rl * 64 + 32 + l32]);
-            const float sg = 1.0f / (1.0f + __expf(-G));
-            const float si = G * sg;
-            float dA = acc[i][j][r];
-            if (DT == MOE_FP8_E4M3) dA *= g.a_scale[row] * g.b_scale[size_t(e) * g.N + f];
-            const size_t b = size_t(row) * (2 * hf);
-            dgu[b + pg] = uint16_t(f32_to_bf16_bits(dA * U * sg * (1.0f + G * (1.0f - sg))));
-            dgu[b + pu] = uint16_t(f32_to_bf16_bits(dA * si));
-            aout[size_t(row) * hf + f] = uint16_t(f32_to_bf16_bits(si * U));
-          }
         }
       }
     }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();  // the idle stage is refilled by the next tile's loads
-  } else if (DT != MOE_FP8_E4M3) {
+  } else {
     // weight gradients, fp32: rows m of expert e's [M][N] (DW13: N packed,
     // 32-column blocks alternating dW1 / dW3, so the target is uniform per
-    // block); buffer stores as in the forward epilogues
+    // block); buffer stores as in the forward epilogues, FP8 reading the
+    // per-expert channel scales of both transposed operands
     const int ld = MODE == kModeDW13 ? g.N / 2 : g.N;
     const int rowb = ld * 4;
 #pragma unroll
@@ -617,41 +594,19 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, f32x16 (&acc)[C::kMI
       const void* dst = (MODE == kModeDW13 && (nb & 1)) ? g.out2 : g.out;
       const int col = MODE == kModeDW13 ? (nb >> 1) * 32 + l32 : n;
       const __amdgpu_buffer_rsrc_t ro = rsrc(dst, (size_t(e) * g.M + row0) * rowb, size_t(nrow) * rowb);
+      const __amdgpu_buffer_rsrc_t rx =
+          rsrc(DT == MOE_FP8_E4M3 ? static_cast<const void*>(g.a_scale) : dst, (size_t(e) * g.M + row0) * 4,
+               DT == MOE_FP8_E4M3 ? size_t(nrow) * 4 : 0);
+      const float bs = DT == MOE_FP8_E4M3 ? g.b_scale[size_t(e) * g.N + n] : 1.f;
       const int vo = 4 * half * rowb + col * 4;
 #pragma unroll
       for (int i = 0; i < MI; ++i)
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[i][j][r]), ro, vo,
-                                                (wrow + acc_row(i, r, 0)) * rowb, 0);
-    }
-  } else {
-    // weight gradients, fp32: rows m of expert e's [M][N] (DW13: N packed)
-    float* o1 = static_cast<float*>(g.out);
-    float* o2 = static_cast<float*>(g.out2);
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      const int n = cbase + j * 32 + l32;
-      if (n >= g.N) continue;
-      float* dst = o1;
-      int col = n, ld = g.N;
-      if (MODE == kModeDW13) {
-        dst = ((n >> 5) & 1) ? o2 : o1;
-        col = (n >> 6) * 32 + (n & 31);
-        ld = g.N / 2;
-      }
-      dst += size_t(e) * g.M * ld;
-#pragma unroll
-      for (int i = 0; i < MI; ++i)
-#pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int m = rbase + acc_row(i, r, half);
-          if (m < row_end) {
-            float v = acc[i][j][r];
-            // FP8: per-expert channel scales of both transposed operands
-            if (DT == MOE_FP8_E4M3) v *= g.a_scale[size_t(e) * g.M + m] * g.b_scale[size_t(e) * g.N + n];
-            dst[size_t(m) * ld + col] = v;
-          }
+          float v = acc[i][j][r];
+          if (DT == MOE_FP8_E4M3)
+            v *= __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rx, 4 * half * 4, (wrow + acc_row(i, r, 0)) * 4, 0)) * bs;
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), ro, vo, (wrow + acc_row(i, r, 0)) * rowb, 0);
         }
     }
   }
