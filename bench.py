@@ -108,34 +108,14 @@ def cpu_baseline(wl, inp, n_tokens, seed=0):
                       f"{'fwd+bwd' if wl.backward else 'fwd'} in fp64 NumPy ({dt:.1f} s)"}
 
 
-def main():
-    ap = argparse.ArgumentParser(description=__doc__)
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="mixtral")
-    ap.add_argument("--cpu-tokens", type=int, default=8192,
-                    help="most tokens in the CPU oracle sample, kept under ~45 s (0 = skip)")
-    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
-                    help="only run a plain device copy of BYTES (3 times), to calibrate the "
-                         "FETCH_SIZE / WRITE_SIZE counters against a known byte count")
-    args = ap.parse_args()
-    if args.copy_calibration:
-        import torch
-        n = args.copy_calibration
-        src = torch.ones(n, dtype=torch.uint8, device="cuda")
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        print(json.dumps({"copy_bytes": n, "launches": 3}))
-        return
-    world = int(os.environ.get("WORLD_SIZE", "1"))
-    if args.gpus != 1 or world != 1:
-        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE={world}); "
-              "the multi-GPU layout is a design in the notes, not built here.", file=sys.stderr)
-        sys.exit(2)
+# Workloads timed beside the primary one when bench.py runs without --workload
+# (each a shape from the pages' model table; see moe_synth.WORKLOADS).
+OTHER_WORKLOADS = ("dsmoe", "dsmoe_fp8", "hunyuan_fp8", "m352b_zipf", "mixtral22b", "phi35")
 
+
+def measure(name, steps, warmup, cold):
+    """Generate one workload's inputs, time `steps` layer steps after `warmup`
+    untimed ones, and return (the JSON fields, the workload, its host inputs)."""
     import numpy as np
     import torch
 
@@ -144,7 +124,7 @@ def main():
     from mixture_experts_layer_24_amd import ops
     from mixture_experts_layer_24_amd._lib import MOE_BF16, MOE_F32, MOE_FP8_E4M3
 
-    wl = moe_synth.WORKLOADS[args.workload]
+    wl = moe_synth.WORKLOADS[name]
     dev = torch.device("cuda:0")
     log(f"bench: generating {wl.name} inputs")
     inp = moe_synth.gen_all(wl, seed=0)
@@ -169,21 +149,21 @@ def main():
             layer.aux_loss(AUX_ALPHA)
             layer.backward(dy, x, P, w_gate=wg, alpha=AUX_ALPHA)
 
-    log(f"bench: warmup {args.warmup}")
-    for _ in range(args.warmup):
+    log(f"bench: warmup {warmup}")
+    for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    log(f"bench: timing {args.steps} steps")
+    log(f"bench: timing {steps} steps")
     ops.moe_timing_enable(True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
+    for _ in range(steps):
         step()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     kern = ops.moe_timing_report()
     ops.moe_timing_enable(False)
-    ms = elapsed * 1e3 / args.steps
+    ms = elapsed * 1e3 / steps
 
     # Figures beside `value`: per-step times (events around each step) warm,
     # and cold: a 1 GiB read-modify-write before each step evicts L2 and the
@@ -201,11 +181,12 @@ def main():
             ts.append(a.elapsed_time(b))
         return sorted(ts)
 
-    log("bench: per-step and cold-cache steps")
-    warm = timed_steps(args.steps)
-    flush_buf = torch.zeros(1 << 30, dtype=torch.uint8, device=dev)
-    cold = timed_steps(min(args.steps, 5), flush_buf)
-    del flush_buf
+    log("bench: per-step" + (" and cold-cache steps" if cold else " times"))
+    warm = timed_steps(steps)
+    if cold:
+        flush_buf = torch.zeros(1 << 30, dtype=torch.uint8, device=dev)
+        cold_ts = timed_steps(min(steps, 5), flush_buf)
+        del flush_buf
     step_stats = lambda ts: {"median": round(ts[len(ts) // 2], 4), "min": round(ts[0], 4), "n": len(ts)}
     # GEMM bound per expert: max(FLOPs / peak, weight bytes / HBM), summed (forward)
     attainable = None
@@ -215,7 +196,7 @@ def main():
         attainable = sum(max(6.0 * m * wl.h * wl.h_ffn / PEAK[wl.dtype], wbytes / HBM_PEAK) for m in cnt) * 1e3
     counts = acc.workload_counts(wl)
     avg = {k: v[1] / v[0] for k, v in kern.items()}          # ms per launch
-    per_step = {k: v[1] / args.steps for k, v in kern.items()}
+    per_step = {k: v[1] / steps for k, v in kern.items()}
     flops_step = counts["flops_fwd"] + counts.get("flops_bwd", 0)
     gemm_ms = sum(per_step.get(k, 0.0) for k in ("fc1", "fc2", "bwd_dA", "bwd_dW2", "bwd_dXp", "bwd_dW13"))
     peak = PEAK[wl.dtype]
@@ -253,7 +234,7 @@ def main():
             hbm[k2] = {"GB/s": round(bw / 1e9, 1), "frac": round(bw / HBM_PEAK, 4)}
     out = {
         "metric": METRIC, "value": wl.T / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
+        "steps": steps, "warmup": warmup, "ms_per_step": ms, "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": wl.dtype, "data": "synthetic",
         "config": {"workload": f"{wl.name} MoE layer {'fwd+bwd' if wl.backward else 'fwd'}",
                    "T": wl.T, "h": wl.h, "h_ffn": wl.h_ffn, "E": wl.E, "k": wl.k},
@@ -262,10 +243,62 @@ def main():
         "hbm": hbm,
         "roofline": roof,
         "step_ms": step_stats(warm),
-        "cold_step_ms": dict(step_stats(cold), flush_bytes=1 << 30),
     }
+    if cold:
+        out["cold_step_ms"] = dict(step_stats(cold_ts), flush_bytes=1 << 30)
     if attainable is not None:
         out["gemm_attainable_ms"] = round(attainable, 4)
+    del P, layer, x, wg, bias, dy
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return out, wl, inp
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=None,
+                    help="one workload only (default: mixtral, then the other shapes as `other_workloads`)")
+    ap.add_argument("--cpu-tokens", type=int, default=8192,
+                    help="most tokens in the CPU oracle sample, kept under ~45 s (0 = skip)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device copy of BYTES (3 times), to calibrate the "
+                         "FETCH_SIZE / WRITE_SIZE counters against a known byte count")
+    args = ap.parse_args()
+    if args.copy_calibration:
+        import torch
+        n = args.copy_calibration
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": n, "launches": 3}))
+        return
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE={world}); "
+              "the multi-GPU layout is a design in the notes, not built here.", file=sys.stderr)
+        sys.exit(2)
+
+    primary = args.workload or "mixtral"
+    out, wl, inp = measure(primary, args.steps, args.warmup, cold=True)
+    if args.workload is None:
+        # the other workloads of the same build, timed in the same run with the
+        # same step counts (no cold-cache pass): figures beside `value`
+        others = {}
+        for name in OTHER_WORKLOADS:
+            o, _, _ = measure(name, args.steps, args.warmup, cold=False)
+            others[name] = {k: o[k] for k in ("value", "unit", "ms_per_step", "dtype", "config",
+                                              "gemm_tflops", "gemm_frac_of_peak", "roofline",
+                                              "hbm", "kernel_ms_per_step", "step_ms")}
+            others[name]["roofline"] = {k: o["roofline"][k]
+                                        for k in ("kernel", "bound", "achieved", "peak", "unit", "frac")}
+            if "gemm_attainable_ms" in o:
+                others[name]["gemm_attainable_ms"] = o["gemm_attainable_ms"]
+        out["other_workloads"] = others
     if args.cpu_tokens > 0:
         # a short probe bounds the sample: the oracle's time grows at most
         # linearly in tokens (it has a fixed per-expert part), so the whole
