@@ -33,6 +33,7 @@ import moe_synth
 from moe_synth import to_f32
 from oracle import moe_ref as ref
 
+import fp8_sub
 from test_gpu_parity import DEV, HALF_ULP_BF16, check_close, dev_tensor, host, say
 
 pytestmark = pytest.mark.gpu
@@ -78,10 +79,7 @@ def test_fp8_backward_weight_copies():
 def _packed_gu(g, u):
     """[rows][2hf] G|U with 32-column groups of G and U interleaved (the
     packed order of the kept forward output)."""
-    hf = g.shape[1]
-    p = np.arange(2 * hf)
-    src = np.where((p // 32) % 2 == 1, hf, 0) + (p // 64) * 32 + p % 32
-    return np.concatenate([g, u], axis=1)[:, src]
+    return np.concatenate([g, u], axis=1)[:, fp8_sub.gu_src_columns(g.shape[1])]
 
 
 def _check(got, emu, exact, allow):
@@ -183,3 +181,64 @@ def test_backward_no_rows(fp8):
     torch.cuda.synchronize()
     for t in (dw1, dw3, dw2):
         assert torch.equal(t, torch.zeros_like(t))
+
+
+
+@pytest.mark.slow
+def test_full_size_dsmoe_fp8_backward_sampled():
+    """The DeepSeekMoE-shaped FP8 backward at full size (T 16384, h 2048,
+    h_ffn 1408, E 64, k 6), in the launch configuration the benchmark times.
+    The oracle runs on sub-problems whose FP8 quantizers see exactly the
+    values they see in the whole layer (`fp8_sub`): every routed row of one
+    expert, for three experts, gives their complete dW1, dW3, dW2; the routed
+    rows of 32 sampled tokens give their dX.  Both take the GPU's kept G|U and
+    gate weights (the unit test's setting, so the envelope needs no forward
+    error terms) and the FP8 bars of the small cases."""
+    wl = moe_synth.WORKLOADS["dsmoe_fp8"]
+    say("full-size dsmoe fp8 backward: generating inputs")
+    inp = moe_synth.gen_all(wl, seed=0)
+    x32, dy32 = to_f32(inp["x"]), to_f32(inp["dy"])
+    L = ref.router_logits(x32, to_f32(inp["w_gate"]), inp["bias"])
+    idx, _ = ref.topk_softmax(L, wl.k)
+    say("full-size dsmoe fp8 backward: gpu")
+    P = ops.PackedWeights(dev_tensor(inp["w1"]), dev_tensor(inp["w3"]), dev_tensor(inp["w2"]), MOE_FP8_E4M3,
+                          backward=True)
+    layer = ops.MoELayer(wl.T, wl.h, wl.h_ffn, wl.E, wl.k, MOE_FP8_E4M3, save_for_backward=True)
+    xd = dev_tensor(inp["x"])
+    layer.forward(xd, dev_tensor(inp["w_gate"]), torch.from_numpy(inp["bias"]).to(DEV), P,
+                  logits_in=torch.from_numpy(L).to(DEV))
+    layer.backward(dev_tensor(inp["dy"]), xd, P)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(layer.topk_idx.cpu().numpy(), idx)
+    offsets, dst_row, src_tok = (layer.offsets.cpu().numpy(), layer.dst_row.cpu().numpy(),
+                                 layer.src_tok.cpu().numpy())
+    w_gpu = layer.topk_w.cpu().numpy()
+    g_rows, u_rows = fp8_sub.unpack_gu(host(layer.h13))
+    W = [to_f32(inp[n]) for n in ("w1", "w3", "w2")]
+    got_w = {n: getattr(layer, n).cpu().numpy() for n in ("dw1", "dw3", "dw2")}
+
+    def oracle(toks, slots, experts):
+        args = fp8_sub.subproblem(dy32, x32, w_gpu, idx, dst_row, g_rows, u_rows, *W, toks, slots, experts)
+        return (ref.layer_backward_fp8(*args), ref.fp8_backward_envelope(*args),
+                ref.layer_backward(*args[:8], g=args[8], u=args[9]))
+
+    def compare(got, em, ex, al, what, rounding=None):
+        check_close(got, em, 6e-2, al, None, what + " vs FP8-emulating oracle", rounding=rounding)
+        e_rms = np.sqrt(np.mean((got - em) ** 2)) / np.sqrt(np.mean(em ** 2))
+        x_rms = np.sqrt(np.mean((got - ex) ** 2)) / np.sqrt(np.mean(ex ** 2))
+        say(f"  {what}: rms err / rms vs emulating oracle {e_rms:.3e}, vs exact {x_rms:.3e}")
+        assert e_rms <= 1e-2, what
+
+    counts = np.diff(offsets)
+    for e in (0, int(np.argmax(counts)), wl.E - 1):
+        toks, slots = fp8_sub.expert_rows(e, offsets, dst_row, src_tok)
+        say(f"  expert {e}: {len(toks)} rows, oracle")
+        emu, allow, exact = oracle(toks, slots, [e])
+        for name in ("dw1", "dw3", "dw2"):
+            compare(got_w[name][e], emu[name][0], exact[name][0], allow[name][0], f"{name}[{e}]")
+    tok_s = np.sort(np.random.default_rng(7).choice(wl.T, 32, replace=False))
+    toks, slots, experts = fp8_sub.token_rows(tok_s, idx)
+    say(f"  dX of {len(tok_s)} tokens ({len(toks)} routed rows, {len(experts)} experts), oracle")
+    emu, allow, exact = oracle(toks, slots, experts)
+    em, ex, al = (fp8_sub.token_sum(d["dx"], tok_s, toks) for d in (emu, exact, allow))
+    compare(host(layer.dx)[tok_s], em, ex, al, "dX sampled", rounding=HALF_ULP_BF16 * np.abs(em))

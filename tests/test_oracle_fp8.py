@@ -168,3 +168,37 @@ def test_hand_worked_fp8_layer():
     np.testing.assert_array_equal(r["y"], arr("y"))
     # the codes decode to the values the derivation names
     np.testing.assert_array_equal(ref.e4m3_decode(r["qa"]), [[448, 288], [-448, 160]])
+
+
+def test_fp8_backward_subproblems_equal_the_whole_layer():
+    """The full-size FP8 backward test hands the oracle sub-problems (one
+    expert's routed rows; the routed rows of sampled tokens, each as a token
+    of its own).  Pin that premise: on a small layer, the sub-problems give
+    the whole-layer oracle's dW1, dW3, dW2 of that expert and dX of those
+    tokens, and the same envelope, up to the fp64 summation order."""
+    import fp8_sub
+    from moe_synth import to_f32
+    wl = moe_synth.WORKLOADS["dsmoe"].scaled(name="sub", dtype="fp8", T=240, h=128, h_ffn=192, E=6, k=3)
+    inp = moe_synth.gen_all(wl, seed=11)
+    f = lambda key: to_f32(inp[key])
+    fw = ref.layer_forward_fp8(f("x"), f("w_gate"), inp["bias"], f("w1"), f("w3"), f("w2"), wl.k)
+    g, u = ref.round_bf16(fw["g"]), ref.round_bf16(fw["u"])
+    W = [f("w1"), f("w3"), f("w2")]
+    whole = (f("dy"), f("x"), fw["w"], fw["dst_row"], fw["offsets"], *W, g, u)
+    emu, env = ref.layer_backward_fp8(*whole), ref.fp8_backward_envelope(*whole)
+    _, _, _, src_tok = ref.build_index(fw["idx"], wl.E)
+    for e in range(wl.E):
+        toks, slots = fp8_sub.expert_rows(e, fw["offsets"], fw["dst_row"], src_tok)
+        args = fp8_sub.subproblem(f("dy"), f("x"), fw["w"], fw["idx"], fw["dst_row"], g, u, *W, toks, slots, [e])
+        se, sv = ref.layer_backward_fp8(*args), ref.fp8_backward_envelope(*args)
+        for name in ("dw1", "dw3", "dw2"):
+            np.testing.assert_allclose(se[name][0], emu[name][e], rtol=1e-12, atol=1e-12 * np.abs(emu[name]).max())
+            np.testing.assert_allclose(sv[name][0], env[name][e], rtol=1e-9, atol=1e-12 * np.abs(env[name]).max())
+    tok_s = np.array([0, 5, 17, 100, 239])
+    toks, slots, experts = fp8_sub.token_rows(tok_s, fw["idx"])
+    args = fp8_sub.subproblem(f("dy"), f("x"), fw["w"], fw["idx"], fw["dst_row"], g, u, *W, toks, slots, experts)
+    se, sv = ref.layer_backward_fp8(*args), ref.fp8_backward_envelope(*args)
+    np.testing.assert_allclose(fp8_sub.token_sum(se["dx"], tok_s, toks), emu["dx"][tok_s], rtol=1e-12,
+                               atol=1e-12 * np.abs(emu["dx"]).max())
+    np.testing.assert_allclose(fp8_sub.token_sum(sv["dx"], tok_s, toks), env["dx"][tok_s], rtol=1e-9,
+                               atol=1e-12 * np.abs(env["dx"]).max())
