@@ -39,14 +39,16 @@ namespace moe {
 // during this block's LDS work.
 //
 // Codes are quantized per channel over the expert's rows (scale[e][c] =
-// amax / 448, 1 for a zero channel or an expert without rows); a first pass
-// over the same rows takes the column amax.  The second pass re-reads them
-// from the Infinity Cache when the strips of the items in progress fit there,
-// which the launcher arranges by bounding the grid.
+// amax / 448, 1 for a zero channel or an expert without rows).  With
+// have_amax, scale[e][c] holds the column amax on entry (the dA epilogue
+// takes it for A and dG|dU); otherwise a first pass over the same rows takes
+// it, and the second pass re-reads them from the Infinity Cache when the
+// strips of the items in progress fit there, which the launcher arranges by
+// bounding the grid.
 __global__ void __launch_bounds__(256) xpose_kernel(const uint16_t* __restrict__ src, int C,
                                                     const int32_t* __restrict__ offsets, int E,
                                                     int rows, int pad, void* __restrict__ dst,
-                                                    float* __restrict__ scale) {
+                                                    float* __restrict__ scale, int have_amax) {
   __shared__ int kpre[MOE_MAX_EXPERTS + 1];
   __shared__ int offs[MOE_MAX_EXPERTS + 1];
   __shared__ uint32_t tile[64 * 33];
@@ -94,7 +96,15 @@ __global__ void __launch_bounds__(256) xpose_kernel(const uint16_t* __restrict__
       if (r < m) v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(sp + size_t(r) * C));
       return v;
     };
-    {
+    if (have_amax) {
+      if (tid < 64 && c0 + tid < C) {
+        const float a = scale[size_t(e) * C + c0 + tid];
+        const float sc = a > 0.f ? a / 448.0f : 1.0f;
+        cscale[tid] = sc;
+        scale[size_t(e) * C + c0 + tid] = sc;
+      }
+      __syncthreads();
+    } else {
       float am[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) am[j] = 0.f;
@@ -270,11 +280,11 @@ size_t grouped_bwd_fp8_ws_bytes(int rows, int h, int h_ffn, int E) {
   const size_t kp = kpad_upper(rows, E, kpad_elems<MOE_FP8_E4M3>());
   return al256(r * 2 * hf * 2) + al256(r * hf * 2) + al256(r * 2 * hf) + al256(r * 4) +
          2 * al256(hh * kp) + al256(hf * kp) + al256(2 * hf * kp) +
-         2 * al256(e * hh * 4) + al256(e * hf * 4) + al256(e * 2 * hf * 4) + splitk_ws_bytes<CfgQ>();
+         2 * al256(e * hh * 4) + al256(e * 3 * hf * 4) + splitk_ws_bytes<CfgQ>();
 }
 
 static int xpose_q(const void* src, int C, const int32_t* offsets, int E, int rows, void* dst,
-                   float* scale, hipStream_t s) {
+                   float* scale, bool have_amax, hipStream_t s) {
   if (C % 64 != 0) return MOE_ERR_SHAPE;
   // Workgroups per CU: as many as keep the strips of the items in progress
   // (128 bytes per row of the expert, read twice) within ~192 MiB, so the
@@ -287,10 +297,11 @@ static int xpose_q(const void* src, int C, const int32_t* offsets, int E, int ro
   const double strip = 128.0 * (double(rows) / (E > 0 ? E : 1) + 1.0);
   int per_cu = int((192.0 * 1024 * 1024) / (double(num_cus()) * strip));
   per_cu = per_cu < 4 ? 4 : (per_cu > 8 ? 8 : per_cu);
+  if (have_amax) per_cu = 8;  // one pass: nothing to keep in the Infinity Cache
   const int grid = items < num_cus() * per_cu ? items : num_cus() * per_cu;
   if (grid <= 0) return MOE_OK;
   hipLaunchKernelGGL(xpose_kernel, dim3(grid), dim3(256), 0, s, (const uint16_t*)src, C,
-                     offsets, E, rows, kpad_elems<MOE_FP8_E4M3>(), dst, scale);
+                     offsets, E, rows, kpad_elems<MOE_FP8_E4M3>(), dst, scale, int(have_amax));
   return launch_status();
 }
 
@@ -311,19 +322,27 @@ int grouped_bwd_fp8(const void* dyp_q, const float* dyp_scale, const void* dyp, 
   void* dguT = take(2 * size_t(hf) * kp);
   float* sx = reinterpret_cast<float*>(take(size_t(E) * h * 4));
   float* sd = reinterpret_cast<float*>(take(size_t(E) * h * 4));
-  float* sa = reinterpret_cast<float*>(take(size_t(E) * hf * 4));
-  float* sg = reinterpret_cast<float*>(take(size_t(E) * 2 * hf * 4));
+  // A's channel scales, then dG|dU's: one array, which the dA epilogue fills
+  // with the column maxima first
+  float* sa = reinterpret_cast<float*>(take(size_t(E) * 3 * hf * 4));
+  float* sg = sa + size_t(E) * hf;
   void* split_ws = w;
   int rc;
 
   timer_begin(kTXpose, s);
-  if ((rc = xpose_q(xp, h, offsets, E, rows, xpT, sx, s))) return rc;
-  if ((rc = xpose_q(dyp, h, offsets, E, rows, dypT, sd, s))) return rc;
+  if ((rc = xpose_q(xp, h, offsets, E, rows, xpT, sx, false, s))) return rc;
+  if ((rc = xpose_q(dyp, h, offsets, E, rows, dypT, sd, false, s))) return rc;
+  {
+    const int n = E * 3 * hf;  // the column maxima start from zero
+    hipLaunchKernelGGL(zero_u32_kernel<0>, dim3(ceil_div(n, 256)), dim3(256), 0, s,
+                       reinterpret_cast<uint32_t*>(sa), n);
+  }
   timer_end(kTXpose, s);
 
-  // dA = dYp W2^T on FP8 codes; epilogue rescales and forms dG, dU and A
+  // dA = dYp W2^T on FP8 codes; epilogue rescales, forms dG, dU and A and
+  // takes their column maxima per expert
   GemmArgs ga{dyp_q, dyp_scale, W->w2_bwd, W->w2_bwd_scale, offsets, E, h, hf, rows, 0,
-              dgu, act, const_cast<void*>(h13_save), nullptr, nullptr, nullptr};
+              dgu, act, const_cast<void*>(h13_save), sa, nullptr, nullptr};
   splitk_ws_set<CfgDAq>(ga, split_ws);
   if ((rc = launch_gemm<CfgDAq, MOE_FP8_E4M3, kModeBwdDA, kSchedM>(ga, kTBwd1, s))) return rc;
 
@@ -333,8 +352,8 @@ int grouped_bwd_fp8(const void* dyp_q, const float* dyp_scale, const void* dyp, 
                        rows, 2 * hf, (uint8_t*)dgu_q, dgu_s);
   timer_end(kTQuant, s);
   timer_begin(kTXpose, s);
-  if ((rc = xpose_q(act, hf, offsets, E, rows, actT, sa, s))) return rc;
-  if ((rc = xpose_q(dgu, 2 * hf, offsets, E, rows, dguT, sg, s))) return rc;
+  if ((rc = xpose_q(act, hf, offsets, E, rows, actT, sa, true, s))) return rc;
+  if ((rc = xpose_q(dgu, 2 * hf, offsets, E, rows, dguT, sg, true, s))) return rc;
   timer_end(kTXpose, s);
 
   // dW2 = A^T dYp  (per expert [hf][h], fp32)
