@@ -330,6 +330,25 @@ int moe_grouped_swiglu_bwd_fp8(const void* dyp_q, const float* dyp_scale, const 
                                float* dw2, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * The same FP8 backward, same results bit for bit, reading dY and x in token
+ * order in place of their routed bf16 copies dyp and xp: the weight-gradient
+ * operands are gathered row by row where they are transposed and quantized
+ * (each value of dYp formed as bf16(w * dY), as moe_permute with row_scale
+ * forms it), so the caller dispatches neither copy.
+ *   dy, x    [T][h] bf16.
+ *   dst_row  [T][k] int32 (moe_permute's output; pairs outside [0, rows) are
+ *            skipped), topk_w [T][k] fp32: each routed row's token and weight.
+ *   rows <= T*k; a row in [0, rows) that no pair targets reads as zeros.
+ *   Everything else, the workspace size included, as
+ *   moe_grouped_swiglu_bwd_fp8.
+ */
+int moe_grouped_swiglu_bwd_fp8_tok(const void* dyp_q, const float* dyp_scale, const void* dy,
+                                   const void* x, const int32_t* dst_row, const float* topk_w, int T,
+                                   int k, const void* h13_save, const moe_weights* W,
+                                   const int32_t* offsets, int rows, void* dxp, float* dw1, float* dw3,
+                                   float* dw2, void* ws, size_t ws_bytes, void* stream);
+
+/*
  * Router backward: gradients of  sum_t <dY_t, y_t> + L_aux  through the gate
  * (MegaScale-MoE paper review, §三 MoE layer structure: the gating network is
  * trainable), with the top-k selection held fixed.  For each token t,

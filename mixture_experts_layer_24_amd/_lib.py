@@ -51,6 +51,8 @@ SIGNATURES = {
     "moe_combine": (I, [P, I, P, P, I, I, I, P, I, P]),
     "moe_grouped_bwd_fp8_workspace_size": (SZ, [I, I, I, I]),
     "moe_grouped_swiglu_bwd_fp8": (I, [P, P, P, P, P, ctypes.POINTER(MoeWeights), P, I, P, P, P, P, P, SZ, P]),
+    "moe_grouped_swiglu_bwd_fp8_tok": (I, [P, P, P, P, P, P, I, I, P, ctypes.POINTER(MoeWeights), P, I, P, P, P,
+                                           P, P, SZ, P]),
     "moe_router_bwd_workspace_size": (SZ, [I, I, I]),
     "moe_router_bwd": (I, [P, P, I, P, P, P, P, P, I, I, I, I, F, I, P, P, P, P, P, P, P, P, SZ, P]),
     "moe_router_aux_workspace_size": (SZ, [I, I]),

@@ -112,9 +112,10 @@ def workload_counts(wl) -> dict:
         dy_b = permute_bytes(wl.T, wl.h, wl.k, s_in, s_in) + 4 * R
         xg_b = permute_bytes(wl.T, wl.h, wl.k, s_in, s_in)      # x re-gathered
         if wl.dtype == "fp8":
-            # also dY as per-token E4M3 codes with scale w * s per routed row
+            # dY only as per-token E4M3 codes with scale w * s per routed row:
+            # the FP8 weight gradients gather w * dY and Xp from dY and x
             dyq_b = permute_bytes(wl.T, wl.h, wl.k, s_in, 1, scales=True) + 4 * R
-            out["permute_launches"] += [dy_b, dyq_b, xg_b]
+            out["permute_launches"] += [dyq_b]
         else:
             out["permute_launches"] += [dy_b, xg_b]
         # dX of the expert path: no gate weights read, fp32 output (the router

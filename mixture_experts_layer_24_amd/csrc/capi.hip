@@ -411,6 +411,32 @@ int moe_grouped_swiglu_bwd_fp8(const void* dyp_q, const float* dyp_scale, const 
                   "moe_grouped_swiglu_bwd_fp8");
 }
 
+int moe_grouped_swiglu_bwd_fp8_tok(const void* dyp_q, const float* dyp_scale, const void* dy,
+                                   const void* x, const int32_t* dst_row, const float* topk_w, int T,
+                                   int k, const void* h13_save, const moe_weights* W,
+                                   const int32_t* offsets, int rows, void* dxp, float* dw1, float* dw3,
+                                   float* dw2, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_weights(W);
+  if (rc) return rc;
+  REQ(W->dtype == MOE_FP8_E4M3, MOE_ERR_DTYPE, "the FP8 backward needs FP8 weights");
+  REQ(W->w13_bwd && W->w2_bwd && W->w13_bwd_scale && W->w2_bwd_scale, MOE_ERR_ARG,
+      "FP8 backward weight layouts and scales are required");
+  REQ(rows >= 0, MOE_ERR_ARG, "rows=%d is negative", rows);
+  REQ(T >= 0, MOE_ERR_ARG, "T=%d is negative", T);
+  REQ(k >= 1 && k <= MOE_MAX_TOPK, MOE_ERR_ARG, "k=%d outside [1, %d]", k, MOE_MAX_TOPK);
+  REQ(rows <= T * k, MOE_ERR_ARG, "rows=%d exceeds T*k=%d", rows, T * k);
+  PTR(dyp_q); PTR(dyp_scale); PTR(dy); PTR(x); PTR(dst_row); PTR(topk_w); PTR(h13_save); PTR(offsets);
+  PTR(dxp); PTR(dw1); PTR(dw3); PTR(dw2);
+  const size_t need = moe_launch::grouped_bwd_fp8_ws_bytes(rows > 0 ? rows : 1, W->h, W->h_ffn, W->E);
+  REQ(ws != nullptr && ws_bytes >= need, MOE_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given",
+      need, ws ? ws_bytes : size_t(0));
+  moe_launch::clear_status();
+  return launched(moe_launch::grouped_bwd_fp8(dyp_q, dyp_scale, dy, x, h13_save, W, offsets, rows, dxp,
+                                              dw1, dw3, dw2, ws, (hipStream_t)stream, dst_row, topk_w,
+                                              T, k),
+                  "moe_grouped_swiglu_bwd_fp8_tok");
+}
+
 size_t moe_router_bwd_workspace_size(int T, int h, int E) {
   if (T <= 0 || h <= 0 || E <= 0) return 0;
   return moe_launch::router_bwd_ws_bytes(T, h, E);

@@ -204,7 +204,9 @@ int pack_weights(const void* w1, const void* w3, const void* w2, int in_dt, int 
                  hipStream_t s);
 int grouped_bwd_fp8(const void* dyp_q, const float* dyp_scale, const void* dyp, const void* xp,
                     const void* h13_save, const moe_weights* W, const int32_t* offsets, int rows,
-                    void* dxp, float* dw1, float* dw3, float* dw2, void* ws, hipStream_t s);
+                    void* dxp, float* dw1, float* dw3, float* dw2, void* ws, hipStream_t s,
+                    const int32_t* dst_row = nullptr, const float* topk_w = nullptr, int T = 0,
+                    int k = 0);
 size_t grouped_bwd_fp8_ws_bytes(int rows, int h, int h_ffn, int E);
 int num_cus();
 

@@ -45,10 +45,18 @@ namespace moe {
 // it, and the second pass re-reads them from the Infinity Cache when the
 // strips of the items in progress fit there, which the launcher arranges by
 // bounding the grid.
+//
+// With row_src, src is token-major ([ntok][C]) and routed row r is gathered
+// from token row row_src[r] - 1 (x for Xp; 0 marks a row no pair targets,
+// which reads as zeros); with row_w too, each value becomes bf16(row_w[r] * v),
+// the value the weighted dispatch copy stores (dY for dYp).  The routed copies
+// are then never written.
 __global__ void __launch_bounds__(256) xpose_kernel(const uint16_t* __restrict__ src, int C,
                                                     const int32_t* __restrict__ offsets, int E,
                                                     int rows, int pad, void* __restrict__ dst,
-                                                    float* __restrict__ scale, int have_amax) {
+                                                    float* __restrict__ scale, int have_amax,
+                                                    const int32_t* __restrict__ row_src,
+                                                    const float* __restrict__ row_w, int ntok) {
   __shared__ int kpre[MOE_MAX_EXPERTS + 1];
   __shared__ int offs[MOE_MAX_EXPERTS + 1];
   __shared__ uint32_t tile[64 * 33];
@@ -96,6 +104,25 @@ __global__ void __launch_bounds__(256) xpose_kernel(const uint16_t* __restrict__
       if (r < m) v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(sp + size_t(r) * C));
       return v;
     };
+    // Gathered rows: the row's token (loaded a step ahead of its data, so the
+    // data load does not wait on it), the token row's chunk, and the row's
+    // weight, applied where the value is used, as the weighted dispatch copy
+    // rounds it.  A gathered token row serves its other routed rows too, so
+    // it keeps the plain loads.
+    auto gidx = [&](int r) { return r < m ? row_src[r0 + r] : 0; };
+    auto graw = [&](int t1) {
+      u32x4 v = {0, 0, 0, 0};
+      if (t1 > 0 && t1 <= ntok) v = *reinterpret_cast<const u32x4*>(src + size_t(t1 - 1) * C + c0 + q * 8);
+      return v;
+    };
+    auto gw = [&](int r) { return row_w && r < m ? row_w[r0 + r] : 1.0f; };
+    auto weigh = [&](u32x4 v, float w) {
+      if (row_w) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = pack_bf16x2(bf16_lo(v[i]) * w, bf16_hi(v[i]) * w);
+      }
+      return v;
+    };
     if (have_amax) {
       if (tid < 64 && c0 + tid < C) {
         const float a = scale[size_t(e) * C + c0 + tid];
@@ -109,10 +136,31 @@ __global__ void __launch_bounds__(256) xpose_kernel(const uint16_t* __restrict__
 #pragma unroll
       for (int j = 0; j < 8; ++j) am[j] = 0.f;
       // four rows per thread in flight (rows past the expert read as zeros)
+      int ti[4];
+      if (row_src)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) ti[u] = gidx(p + 32 * u);
       for (int r = p; r < m; r += 128) {
         u32x4 v[4];
+        if (row_src) {
+          int tn[4];
+          float wv[4];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) v[u] = ld(r + 32 * u);
+          for (int u = 0; u < 4; ++u) tn[u] = gidx(r + 128 + 32 * u);
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            v[u] = graw(ti[u]);
+            wv[u] = gw(r + 32 * u);
+          }
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            v[u] = weigh(v[u], wv[u]);
+            ti[u] = tn[u];
+          }
+        } else {
+#pragma unroll
+          for (int u = 0; u < 4; ++u) v[u] = ld(r + 32 * u);
+        }
 #pragma unroll
         for (int u = 0; u < 4; ++u)
 #pragma unroll
@@ -138,10 +186,9 @@ __global__ void __launch_bounds__(256) xpose_kernel(const uint16_t* __restrict__
     const size_t obase = size_t(kpre[e]) * C + size_t(c0 + c) * kp + kk;
     const float sc = cscale[c];
     const QuotScale qs = quot_scale(sc);
-    // loads run two 64-row blocks ahead of the LDS work
-    u32x4 va = ldn(2 * p), vb = ldn(2 * p + 1), na = ldn(64 + 2 * p), nb = ldn(65 + 2 * p);
-    for (int k0 = 0; k0 < kp; k0 += 64) {
-      const u32x4 fa = ldn(k0 + 128 + 2 * p), fb = ldn(k0 + 129 + 2 * p);
+    // one 64-row block: the thread's rows 2p, 2p + 1 (va, vb) into the LDS
+    // tile, then 16 consecutive rows of one column out, encoded
+    auto encode = [&](int k0, const u32x4& va, const u32x4& vb) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         tile[(q * 8 + 2 * i) * 33 + p] = (va[i] & 0xFFFFu) | (vb[i] << 16);
@@ -160,10 +207,40 @@ __global__ void __launch_bounds__(256) xpose_kernel(const uint16_t* __restrict__
         *reinterpret_cast<u32x4*>(static_cast<uint8_t*>(dst) + obase + k0) = o;
       }
       __syncthreads();
-      va = na;
-      vb = nb;
-      na = fa;
-      nb = fb;
+    };
+    if (row_src) {
+      // data two 64-row blocks ahead of the LDS work, tokens three
+      int fia = gidx(128 + 2 * p), fib = gidx(129 + 2 * p);
+      u32x4 va = graw(gidx(2 * p)), vb = graw(gidx(2 * p + 1));
+      u32x4 na = graw(gidx(64 + 2 * p)), nb = graw(gidx(65 + 2 * p));
+      float wa = gw(2 * p), wb = gw(2 * p + 1), nwa = gw(64 + 2 * p), nwb = gw(65 + 2 * p);
+      for (int k0 = 0; k0 < kp; k0 += 64) {
+        const int xa = gidx(k0 + 192 + 2 * p), xb = gidx(k0 + 193 + 2 * p);
+        const u32x4 fa = graw(fia), fb = graw(fib);
+        const float fwa = gw(k0 + 128 + 2 * p), fwb = gw(k0 + 129 + 2 * p);
+        encode(k0, weigh(va, wa), weigh(vb, wb));
+        va = na;
+        vb = nb;
+        wa = nwa;
+        wb = nwb;
+        na = fa;
+        nb = fb;
+        nwa = fwa;
+        nwb = fwb;
+        fia = xa;
+        fib = xb;
+      }
+    } else {
+      // loads run two 64-row blocks ahead of the LDS work
+      u32x4 va = ldn(2 * p), vb = ldn(2 * p + 1), na = ldn(64 + 2 * p), nb = ldn(65 + 2 * p);
+      for (int k0 = 0; k0 < kp; k0 += 64) {
+        const u32x4 fa = ldn(k0 + 128 + 2 * p), fb = ldn(k0 + 129 + 2 * p);
+        encode(k0, va, vb);
+        va = na;
+        vb = nb;
+        na = fa;
+        nb = fb;
+      }
     }
   }
 }
@@ -175,6 +252,20 @@ __global__ void __launch_bounds__(256) rowq_kernel(const uint16_t* __restrict__ 
   const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (r >= n) return;
   rowq_wave(src + size_t(r) * len, len, dst + size_t(r) * len, scale + r);
+}
+
+// The token (plus one) and gate weight of each routed row: the inverse of
+// dst_row, into arrays cleared to zero.
+__global__ void __launch_bounds__(256) rowmap_kernel(const int32_t* __restrict__ dst_row,
+                                                     const float* __restrict__ topk_w, int n, int k,
+                                                     int rows, int32_t* __restrict__ row_src,
+                                                     float* __restrict__ row_w) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  const int r = dst_row[i];
+  if (r < 0 || r >= rows) return;  // a dropped pair
+  row_src[r] = i / k + 1;
+  row_w[r] = topk_w[i];
 }
 
 }  // namespace moe
@@ -280,11 +371,12 @@ size_t grouped_bwd_fp8_ws_bytes(int rows, int h, int h_ffn, int E) {
   const size_t kp = kpad_upper(rows, E, kpad_elems<MOE_FP8_E4M3>());
   return al256(r * 2 * hf * 2) + al256(r * hf * 2) + al256(r * 2 * hf) + al256(r * 4) +
          2 * al256(hh * kp) + al256(hf * kp) + al256(2 * hf * kp) +
-         2 * al256(e * hh * 4) + al256(e * 3 * hf * 4) + splitk_ws_bytes<CfgQ>();
+         2 * al256(e * hh * 4) + al256(e * 3 * hf * 4) + 2 * al256(r * 4) + splitk_ws_bytes<CfgQ>();
 }
 
 static int xpose_q(const void* src, int C, const int32_t* offsets, int E, int rows, void* dst,
-                   float* scale, bool have_amax, hipStream_t s) {
+                   float* scale, bool have_amax, hipStream_t s, const int32_t* row_src = nullptr,
+                   const float* row_w = nullptr, int ntok = 0) {
   if (C % 64 != 0) return MOE_ERR_SHAPE;
   // Workgroups per CU: as many as keep the strips of the items in progress
   // (128 bytes per row of the expert, read twice) within ~192 MiB, so the
@@ -297,17 +389,23 @@ static int xpose_q(const void* src, int C, const int32_t* offsets, int E, int ro
   const double strip = 128.0 * (double(rows) / (E > 0 ? E : 1) + 1.0);
   int per_cu = int((192.0 * 1024 * 1024) / (double(num_cus()) * strip));
   per_cu = per_cu < 4 ? 4 : (per_cu > 8 ? 8 : per_cu);
-  if (have_amax) per_cu = 8;  // one pass: nothing to keep in the Infinity Cache
+  // one pass, or gathered rows of a token-major source the Infinity Cache holds
+  // whole: nothing to bound
+  if (have_amax || row_src) per_cu = 8;
   const int grid = items < num_cus() * per_cu ? items : num_cus() * per_cu;
   if (grid <= 0) return MOE_OK;
   hipLaunchKernelGGL(xpose_kernel, dim3(grid), dim3(256), 0, s, (const uint16_t*)src, C,
-                     offsets, E, rows, kpad_elems<MOE_FP8_E4M3>(), dst, scale, int(have_amax));
+                     offsets, E, rows, kpad_elems<MOE_FP8_E4M3>(), dst, scale, int(have_amax), row_src,
+                     row_w, ntok);
   return launch_status();
 }
 
+// With dst_row, dyp and xp are the token-major dY and x ([T][h]) and the
+// weight-gradient operands are gathered from them (topk_w weighting dY).
 int grouped_bwd_fp8(const void* dyp_q, const float* dyp_scale, const void* dyp, const void* xp,
                     const void* h13_save, const moe_weights* W, const int32_t* offsets, int rows,
-                    void* dxp, float* dw1, float* dw3, float* dw2, void* ws, hipStream_t s) {
+                    void* dxp, float* dw1, float* dw3, float* dw2, void* ws, hipStream_t s,
+                    const int32_t* dst_row, const float* topk_w, int T, int k) {
   const int h = W->h, hf = W->h_ffn, E = W->E;
   const size_t r = size_t(rows), kp = kpad_upper(rows, E, kpad_elems<MOE_FP8_E4M3>());
   unsigned char* w = static_cast<unsigned char*>(ws);
@@ -326,12 +424,23 @@ int grouped_bwd_fp8(const void* dyp_q, const float* dyp_scale, const void* dyp, 
   // with the column maxima first
   float* sa = reinterpret_cast<float*>(take(size_t(E) * 3 * hf * 4));
   float* sg = sa + size_t(E) * hf;
+  int32_t* row_src = reinterpret_cast<int32_t*>(take(r * 4));
+  float* row_w = reinterpret_cast<float*>(take(r * 4));
   void* split_ws = w;
   int rc;
+  if (dst_row == nullptr) {
+    row_src = nullptr;
+    row_w = nullptr;
+  } else if (rows > 0) {
+    hipLaunchKernelGGL(zero_u32_kernel<0>, dim3(ceil_div(rows, 256)), dim3(256), 0, s,
+                       reinterpret_cast<uint32_t*>(row_src), rows);
+    hipLaunchKernelGGL(rowmap_kernel, dim3(ceil_div(T * k, 256)), dim3(256), 0, s, dst_row, topk_w,
+                       T * k, k, rows, row_src, row_w);
+  }
 
   timer_begin(kTXpose, s);
-  if ((rc = xpose_q(xp, h, offsets, E, rows, xpT, sx, false, s))) return rc;
-  if ((rc = xpose_q(dyp, h, offsets, E, rows, dypT, sd, false, s))) return rc;
+  if ((rc = xpose_q(xp, h, offsets, E, rows, xpT, sx, false, s, row_src, nullptr, T))) return rc;
+  if ((rc = xpose_q(dyp, h, offsets, E, rows, dypT, sd, false, s, row_src, row_w, T))) return rc;
   {
     const int n = E * 3 * hf;  // the column maxima start from zero
     hipLaunchKernelGGL(zero_u32_kernel<0>, dim3(ceil_div(n, 256)), dim3(256), 0, s,

@@ -152,6 +152,14 @@ def moe_grouped_swiglu_bwd_fp8(dyp_q, dyp_scale, dyp, xp, h13_save, W, offsets, 
                                                   _s(stream)))
 
 
+def moe_grouped_swiglu_bwd_fp8_tok(dyp_q, dyp_scale, dy, x, dst_row, topk_w, T, k, h13_save, W, offsets, rows,
+                                   dxp, dw1, dw3, dw2, ws, ws_bytes, stream=None):
+    return check(lib().moe_grouped_swiglu_bwd_fp8_tok(_p(dyp_q), _p(dyp_scale), _p(dy), _p(x), _p(dst_row),
+                                                      _p(topk_w), T, k, _p(h13_save), ctypes.byref(W),
+                                                      _p(offsets), rows, _p(dxp), _p(dw1), _p(dw3), _p(dw2),
+                                                      _p(ws), ws_bytes, _s(stream)))
+
+
 def moe_last_error() -> str:
     return lib().moe_last_error().decode()
 
@@ -266,7 +274,6 @@ class MoELayer:
     def _alloc_bwd(self):
         dev = self.y.device
         R, h, hf, E = self.R, self.h, self.h_ffn, self.E
-        self.dyp = torch.empty(R, h, dtype=torch.bfloat16, device=dev)
         self.dxp = torch.empty(R, h, dtype=torch.bfloat16, device=dev)
         self.dx = torch.empty(self.T, h, dtype=torch.bfloat16, device=dev)
         self.dw1 = torch.empty(E, h, hf, dtype=torch.float32, device=dev)
@@ -275,9 +282,9 @@ class MoELayer:
         if self.dtype == MOE_FP8_E4M3:
             self.dyp_q = torch.empty(R, h, dtype=torch.uint8, device=dev)
             self.dyp_s = torch.empty(R, dtype=torch.float32, device=dev)
-            self.xp_b = torch.empty(R, h, dtype=torch.bfloat16, device=dev)
             self.bws_bytes = moe_grouped_bwd_fp8_workspace_size(R, h, hf, E)
         else:
+            self.dyp = torch.empty(R, h, dtype=torch.bfloat16, device=dev)
             self.bws_bytes = moe_grouped_bwd_workspace_size(R, h, hf, E, self.dtype)
         self.bws = torch.empty(max(self.bws_bytes, 256), dtype=torch.uint8, device=dev)
         self.bwd_ready = True
@@ -309,19 +316,19 @@ class MoELayer:
         if not self.bwd_ready:
             self._alloc_bwd()
         T, h, E, k = self.T, self.h, self.E, self.k
-        # dYp = w * dY in dispatch order; Xp re-gathered from x (index reused)
-        moe_permute(dy, MOE_BF16, None, self.topk_w, T, h, E, k, None, None, self.dst_row, None,
-                    self.dyp, MOE_BF16, None, None, 0, stream)
         if self.dtype == MOE_FP8_E4M3:
-            # dY codes per token, routed row scale w * s (FP8 backward)
+            # dY codes per token, routed row scale w * s; the weight gradients'
+            # operands w * dY and Xp are gathered from dY and x where they are
+            # quantized (no routed bf16 copies)
             moe_permute(dy, MOE_BF16, None, self.topk_w, T, h, E, k, None, None, self.dst_row, None,
                         self.dyp_q, MOE_FP8_E4M3, self.dyp_s, None, 0, stream)
-            moe_permute(x, MOE_BF16, None, None, T, h, E, k, None, None, self.dst_row, None,
-                        self.xp_b, MOE_BF16, None, None, 0, stream)
-            moe_grouped_swiglu_bwd_fp8(self.dyp_q, self.dyp_s, self.dyp, self.xp_b, self.h13, W.struct,
-                                       self.offsets, self.R, self.dxp, self.dw1, self.dw3, self.dw2,
-                                       self.bws, self.bws_bytes, stream)
+            moe_grouped_swiglu_bwd_fp8_tok(self.dyp_q, self.dyp_s, dy, x, self.dst_row, self.topk_w, T, k,
+                                           self.h13, W.struct, self.offsets, self.R, self.dxp, self.dw1,
+                                           self.dw3, self.dw2, self.bws, self.bws_bytes, stream)
         else:
+            # dYp = w * dY in dispatch order; Xp re-gathered from x (index reused)
+            moe_permute(dy, MOE_BF16, None, self.topk_w, T, h, E, k, None, None, self.dst_row, None,
+                        self.dyp, MOE_BF16, None, None, 0, stream)
             moe_permute(x, MOE_BF16, None, None, T, h, E, k, None, None, self.dst_row, None,
                         self.xp, MOE_BF16, None, None, 0, stream)
             moe_grouped_swiglu_bwd(self.dyp, self.xp, self.h13, W.struct, self.offsets, self.R,

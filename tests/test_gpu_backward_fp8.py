@@ -242,3 +242,37 @@ def test_full_size_dsmoe_fp8_backward_sampled():
     emu, allow, exact = oracle(toks, slots, experts)
     em, ex, al = (fp8_sub.token_sum(d["dx"], tok_s, toks) for d in (emu, exact, allow))
     compare(host(layer.dx)[tok_s], em, ex, al, "dX sampled", rounding=HALF_ULP_BF16 * np.abs(em))
+
+
+@pytest.mark.parametrize("case,over,seed", [CASES[0], CASES[2], CASES[5], CASES[6]],
+                         ids=[CASES[i][0] for i in (0, 2, 5, 6)])
+def test_fp8_backward_token_gather_entry_is_bit_identical(case, over, seed):
+    """moe_grouped_swiglu_bwd_fp8_tok (w * dY and Xp gathered from dY and x
+    where they are quantized) against moe_grouped_swiglu_bwd_fp8 on the
+    dispatched bf16 copies of the same values: every output bit-identical."""
+    wl = moe_synth.WORKLOADS["dsmoe"].scaled(name=case, dtype="fp8", **over)
+    inp = moe_synth.gen_all(wl, seed=seed)
+    T, h, hf, E, k = wl.T, wl.h, wl.h_ffn, wl.E, wl.k
+    P = ops.PackedWeights(dev_tensor(inp["w1"]), dev_tensor(inp["w3"]), dev_tensor(inp["w2"]), MOE_FP8_E4M3,
+                          backward=True)
+    layer = ops.MoELayer(T, h, hf, E, k, MOE_FP8_E4M3, save_for_backward=True)
+    xd, dyd = dev_tensor(inp["x"]), dev_tensor(inp["dy"])
+    layer.forward(xd, dev_tensor(inp["w_gate"]), torch.from_numpy(inp["bias"]).to(DEV), P)
+    layer.backward(dyd, xd, P)   # the layer's own path: the token-gather entry
+    R = layer.R
+    dyp = torch.empty(R, h, dtype=torch.bfloat16, device=DEV)
+    xp = torch.empty(R, h, dtype=torch.bfloat16, device=DEV)
+    ops.moe_permute(dyd, MOE_BF16, None, layer.topk_w, T, h, E, k, None, None, layer.dst_row, None,
+                    dyp, MOE_BF16, None, None, 0)
+    ops.moe_permute(xd, MOE_BF16, None, None, T, h, E, k, None, None, layer.dst_row, None,
+                    xp, MOE_BF16, None, None, 0)
+    outs = {n: torch.full_like(getattr(layer, n), float("nan")) for n in ("dxp", "dw1", "dw3", "dw2")}
+    ws = torch.empty_like(layer.bws)
+    ops.moe_grouped_swiglu_bwd_fp8(layer.dyp_q, layer.dyp_s, dyp, xp, layer.h13, P.struct, layer.offsets, R,
+                                   outs["dxp"], outs["dw1"], outs["dw3"], outs["dw2"], ws, layer.bws_bytes)
+    torch.cuda.synchronize()
+    for n, t in outs.items():
+        got = getattr(layer, n)
+        same = torch.equal(got.view(torch.int16) if got.dtype == torch.bfloat16 else got.view(torch.int32),
+                           t.view(torch.int16) if t.dtype == torch.bfloat16 else t.view(torch.int32))
+        assert same, n
