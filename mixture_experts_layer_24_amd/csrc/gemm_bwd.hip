@@ -18,7 +18,9 @@
 // turns the M-major slabs into MFMA fragments).  In FP8 the operands are
 // quantized per channel over the expert's rows, so they are first transposed
 // per expert into [C][K_e] code blocks with K_e the row count rounded up to
-// 128 (zeros beyond it), the quantization done in the same pass.
+// 128 (zeros beyond it), the quantization done in the same pass; Xp and
+// w * dY are gathered there from the token-major x and dY (no routed bf16
+// copies of either), A and dG|dU read as the dA epilogue stored them.
 #include "gemm_engine.h"
 
 namespace moe {
@@ -35,8 +37,8 @@ namespace moe {
 // of two adjacent rows (eight threads cover a 128-byte row segment), packs the
 // two rows' values of each column into one 32-bit word in LDS (column-major,
 // 33 words per column: conflict-free stores), then reads 8 words = 16
-// consecutive rows of one column and stores their codes contiguously.  The loads of the next two blocks are in flight
-// during this block's LDS work.
+// consecutive rows of one column and stores their codes contiguously.  The
+// loads of the next two blocks are in flight during this block's LDS work.
 //
 // Codes are quantized per channel over the expert's rows (scale[e][c] =
 // amax / 448, 1 for a zero channel or an expert without rows).  With

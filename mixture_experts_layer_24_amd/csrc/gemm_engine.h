@@ -2,21 +2,20 @@
 //
 // C[m][n] = sum_k A[m][k] * B[n][k] for every expert, both operands
 // K-contiguous, fp32 accumulation on MFMA 32x32 (bf16 x16, fp32 x2, fp8 x64).
-// Two schedules:
+// Three schedules:
 //   SchedM -- rows of A are the expert-contiguous routed rows (ragged M per
 //             expert, offsets on device), K fixed: the forward FC1/FC2 and the
 //             backward dA / dXp products;
 //   SchedK -- every expert has a fixed M x N output and a ragged K = its row
-//             count (padded to a 64 multiple with zeros): the FP8 weight
-//             gradients, on transposed operands;
+//             count (padded with zeros to whole 128-byte slabs: 128 rows in
+//             FP8): the FP8 weight gradients, on transposed operands;
 //   SchedKR -- the same products read straight from the row-major routed
 //             arrays ([rows][M] and [rows][N], K = the expert's rows): K slabs
 //             of 64 rows land in LDS M-major and the fragments come out
 //             through the LDS transpose read (BF16 weight gradients).
-// Tile 256 x 256 on eight waves of 128 x 64 (two per SIMD, 128 fp32
-// accumulators per lane; the FP8 dA uses 128 x 256 tiles, see gemm_bwd.hip);
-// operands go global -> LDS with buffer_load ... lds into two XOR-swizzled
-// stages of 128-byte rows.
+// Every product runs 256 x 256 tiles on eight waves of 128 x 64 (two per
+// SIMD, 128 fp32 accumulators per lane); operands go global -> LDS with
+// buffer_load ... lds into two XOR-swizzled stages of 128-byte rows.
 #pragma once
 #include "common.h"
 
