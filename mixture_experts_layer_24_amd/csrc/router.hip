@@ -6,9 +6,11 @@
 // the k kept logits and the tie rule (lower expert index first) are this
 // library's reading of the unspecified details.
 //
-// BF16: logits on MFMA with x read once from HBM and W_g transposed through
-// LDS (see route_bf16_kernel); FP32 (small workloads) and given logits: a
-// plain dot-product kernel.  Top-k runs on eight lanes per token.
+// BF16: logits on MFMA with x read once from HBM: for E a multiple of 8 up
+// to 64, route_tr_kernel (W_g rows as loaded, fragments through the LDS
+// transpose read); other E, route_bf16_kernel (W_g transposed through LDS).
+// FP32 (small workloads) and given logits: a plain dot-product kernel.  Top-k
+// runs on eight lanes per token.
 #include "common.h"
 
 namespace moe {
@@ -272,8 +274,8 @@ __global__ void __launch_bounds__(RES ? 512 : 256) route_bf16_kernel(const uint1
 }
 
 // BF16 logits with W_g read in its own [h][E] layout (E a multiple of 8, at
-// most 64): eight (E = 8: sixteen) waves share out h in 64-row chunks.
-// x goes from HBM straight into A fragments (64 contiguous bytes per lane per
+// most 64): eight waves (E = 8: sixteen; E >= 32: four) share out h in
+// 64-row chunks.  x goes from HBM straight into A fragments (64 contiguous bytes per lane per
 // chunk); the chunk's W_g rows come into registers with 16-byte loads and
 // are written unchanged into the wave's own LDS buffer, from where transpose
 // reads (ds_read_b64_tr_b16) hand each lane four K-consecutive values of one
