@@ -244,8 +244,11 @@ def test_full_size_dsmoe_fp8_backward_sampled():
     compare(host(layer.dx)[tok_s], em, ex, al, "dX sampled", rounding=HALF_ULP_BF16 * np.abs(em))
 
 
-@pytest.mark.parametrize("case,over,seed", [CASES[0], CASES[2], CASES[5], CASES[6]],
-                         ids=[CASES[i][0] for i in (0, 2, 5, 6)])
+GATHER_CASES = [CASES[0], CASES[2], CASES[5], CASES[6],
+                ("e72", dict(T=200, h=256, h_ffn=256, E=72, k=4), 9)]
+
+
+@pytest.mark.parametrize("case,over,seed", GATHER_CASES, ids=[c[0] for c in GATHER_CASES])
 def test_fp8_backward_token_gather_entry_is_bit_identical(case, over, seed):
     """moe_grouped_swiglu_bwd_fp8_tok (w * dY and Xp gathered from dY and x
     where they are quantized) against moe_grouped_swiglu_bwd_fp8 on the
