@@ -218,3 +218,23 @@ def test_grouped_bwd_fp8_validation():
     Wn = L.MoeWeights(L.MOE_FP8_E4M3, 8, 256, 384, A.value, A.value, A.value, A.value, A.value, A.value,
                       None, A.value)
     assert call(Wn) == L.MOE_ERR_ARG
+
+
+def test_grouped_bwd_fp8_tok_validation():
+    """The token-gather FP8 backward rejects bad arguments before any launch."""
+    lib = L.lib()
+    need = lib.moe_grouped_bwd_fp8_workspace_size(1000, 256, 384, 8)
+    Wq = L.MoeWeights(L.MOE_FP8_E4M3, 8, 256, 384, A.value, A.value, A.value, A.value, A.value, A.value,
+                      A.value, A.value)
+
+    def call(W=Wq, T=500, k=2, rows=1000, dy=A, x=A, dst_row=A, topk_w=A, ws=A, wsb=need):
+        return lib.moe_grouped_swiglu_bwd_fp8_tok(A, A, dy, x, dst_row, topk_w, T, k, A, ctypes.byref(W), A, rows,
+                                                  A, A, A, A, ws, wsb, None)
+    assert call(wsb=need - 1) == L.MOE_ERR_WORKSPACE
+    assert call(rows=1001) == L.MOE_ERR_ARG          # more rows than pairs
+    assert call(k=0) == L.MOE_ERR_ARG
+    assert call(T=-1) == L.MOE_ERR_ARG
+    for name in ("dy", "x", "dst_row", "topk_w"):
+        assert call(**{name: None}) == L.MOE_ERR_ARG, name
+    Wb = L.MoeWeights(L.MOE_BF16, 8, 256, 384, A.value, A.value, None, None, A.value, A.value, None, None)
+    assert call(W=Wb) == L.MOE_ERR_DTYPE
