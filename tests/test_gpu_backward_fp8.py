@@ -153,9 +153,11 @@ def test_fp8_backward_has_empty_experts_case():
     assert (np.bincount(idx.ravel(), minlength=wl.E) == 0).any()
 
 
-@pytest.mark.parametrize("fp8", [True, False], ids=["fp8", "bf16"])
-def test_backward_no_rows(fp8):
-    """rows = 0: no error, and every expert's weight gradient is written as zeros."""
+@pytest.mark.parametrize("form", ["fp8", "fp8_tok", "bf16"])
+def test_backward_no_rows(form):
+    """rows = 0: no error, and every expert's weight gradient is written as
+    zeros (fp8_tok: every pair of three tokens dropped)."""
+    fp8 = form != "bf16"
     E, h, hf = 4, 256, 128
     rng = np.random.default_rng(0)
     w = lambda *sh: torch.from_numpy((rng.standard_normal(sh) * 0.05).astype(np.float32)).to(DEV).to(torch.bfloat16)
@@ -168,7 +170,16 @@ def test_backward_no_rows(fp8):
     dw1 = torch.full((E, h, hf), float("nan"), device=DEV)
     dw3 = torch.full((E, h, hf), float("nan"), device=DEV)
     dw2 = torch.full((E, hf, h), float("nan"), device=DEV)
-    if fp8:
+    if form == "fp8_tok":
+        wsb = ops.moe_grouped_bwd_fp8_workspace_size(0, h, hf, E)
+        ws = torch.empty(max(wsb, 256), dtype=torch.uint8, device=DEV)
+        T, k = 3, 2
+        tok = torch.zeros(T, h, dtype=torch.bfloat16, device=DEV)
+        dst_row = torch.full((T, k), -1, dtype=torch.int32, device=DEV)
+        topk_w = torch.full((T, k), 0.5, dtype=torch.float32, device=DEV)
+        ops.moe_grouped_swiglu_bwd_fp8_tok(dummy8, dummyf, tok, tok, dst_row, topk_w, T, k, dummyb, P.struct,
+                                           offsets, 0, dummyb, dw1, dw3, dw2, ws, ws.numel())
+    elif fp8:
         wsb = ops.moe_grouped_bwd_fp8_workspace_size(0, h, hf, E)
         ws = torch.empty(max(wsb, 256), dtype=torch.uint8, device=DEV)
         ops.moe_grouped_swiglu_bwd_fp8(dummy8, dummyf, dummyb, dummyb, dummyb, P.struct, offsets, 0, dummyb, dw1,
