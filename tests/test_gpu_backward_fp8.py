@@ -255,12 +255,15 @@ def test_full_size_dsmoe_fp8_backward_sampled():
     compare(host(layer.dx)[tok_s], em, ex, al, "dX sampled", rounding=HALF_ULP_BF16 * np.abs(em))
 
 
-GATHER_CASES = [CASES[0], CASES[2], CASES[5], CASES[6],
-                ("e72", dict(T=200, h=256, h_ffn=256, E=72, k=4), 9)]
+GATHER_CASES = [c + (None,) for c in (CASES[0], CASES[2], CASES[5], CASES[6])] + [
+    ("e72", dict(T=200, h=256, h_ffn=256, E=72, k=4), 9, None),
+    # pairs beyond a per-expert capacity dropped before the dispatch: fewer
+    # kept rows than pairs, and dropped pairs in dst_row
+    ("capacity", dict(T=300, h=256, h_ffn=256, E=8, k=2), 10, 60)]
 
 
-@pytest.mark.parametrize("case,over,seed", GATHER_CASES, ids=[c[0] for c in GATHER_CASES])
-def test_fp8_backward_token_gather_entry_is_bit_identical(case, over, seed):
+@pytest.mark.parametrize("case,over,seed,cap", GATHER_CASES, ids=[c[0] for c in GATHER_CASES])
+def test_fp8_backward_token_gather_entry_is_bit_identical(case, over, seed, cap):
     """moe_grouped_swiglu_bwd_fp8_tok (w * dY and Xp gathered from dY and x
     where they are quantized) against moe_grouped_swiglu_bwd_fp8 on the
     dispatched bf16 copies of the same values: every output bit-identical."""
@@ -271,7 +274,9 @@ def test_fp8_backward_token_gather_entry_is_bit_identical(case, over, seed):
                           backward=True)
     layer = ops.MoELayer(T, h, hf, E, k, MOE_FP8_E4M3, save_for_backward=True)
     xd, dyd = dev_tensor(inp["x"]), dev_tensor(inp["dy"])
-    layer.forward(xd, dev_tensor(inp["w_gate"]), torch.from_numpy(inp["bias"]).to(DEV), P)
+    layer.forward(xd, dev_tensor(inp["w_gate"]), torch.from_numpy(inp["bias"]).to(DEV), P, capacity=cap)
+    if cap is not None:
+        assert int(layer.offsets[E]) < T * k and int((layer.dst_row < 0).sum()) > 0
     layer.backward(dyd, xd, P)   # the layer's own path: the token-gather entry
     R = layer.R
     dyp = torch.empty(R, h, dtype=torch.bfloat16, device=DEV)
@@ -285,8 +290,11 @@ def test_fp8_backward_token_gather_entry_is_bit_identical(case, over, seed):
     ops.moe_grouped_swiglu_bwd_fp8(layer.dyp_q, layer.dyp_s, dyp, xp, layer.h13, P.struct, layer.offsets, R,
                                    outs["dxp"], outs["dw1"], outs["dw3"], outs["dw2"], ws, layer.bws_bytes)
     torch.cuda.synchronize()
+    kept = int(layer.offsets[E])  # rows past the kept ones are written by neither entry
     for n, t in outs.items():
         got = getattr(layer, n)
+        if n == "dxp":
+            got, t = got[:kept], t[:kept]
         same = torch.equal(got.view(torch.int16) if got.dtype == torch.bfloat16 else got.view(torch.int32),
                            t.view(torch.int16) if t.dtype == torch.bfloat16 else t.view(torch.int32))
         assert same, n
