@@ -262,13 +262,11 @@ GATHER_CASES = [c + (None,) for c in (CASES[0], CASES[2], CASES[5], CASES[6])] +
     ("capacity", dict(T=300, h=256, h_ffn=256, E=8, k=2), 10, 60)]
 
 
-@pytest.mark.parametrize("case,over,seed,cap", GATHER_CASES, ids=[c[0] for c in GATHER_CASES])
-def test_fp8_backward_token_gather_entry_is_bit_identical(case, over, seed, cap):
-    """moe_grouped_swiglu_bwd_fp8_tok (w * dY and Xp gathered from dY and x
-    where they are quantized) against moe_grouped_swiglu_bwd_fp8 on the
-    dispatched bf16 copies of the same values: every output bit-identical."""
-    wl = moe_synth.WORKLOADS["dsmoe"].scaled(name=case, dtype="fp8", **over)
-    inp = moe_synth.gen_all(wl, seed=seed)
+def gather_entry_matches(wl, inp, cap=None):
+    """Run the layer (FP8 backward through moe_grouped_swiglu_bwd_fp8_tok),
+    then moe_grouped_swiglu_bwd_fp8 on dispatched bf16 copies of w * dY and
+    x, and require every output bit-identical (dXp on the kept rows: rows
+    past them are written by neither entry)."""
     T, h, hf, E, k = wl.T, wl.h, wl.h_ffn, wl.E, wl.k
     P = ops.PackedWeights(dev_tensor(inp["w1"]), dev_tensor(inp["w3"]), dev_tensor(inp["w2"]), MOE_FP8_E4M3,
                           backward=True)
@@ -290,7 +288,7 @@ def test_fp8_backward_token_gather_entry_is_bit_identical(case, over, seed, cap)
     ops.moe_grouped_swiglu_bwd_fp8(layer.dyp_q, layer.dyp_s, dyp, xp, layer.h13, P.struct, layer.offsets, R,
                                    outs["dxp"], outs["dw1"], outs["dw3"], outs["dw2"], ws, layer.bws_bytes)
     torch.cuda.synchronize()
-    kept = int(layer.offsets[E])  # rows past the kept ones are written by neither entry
+    kept = int(layer.offsets[E])
     for n, t in outs.items():
         got = getattr(layer, n)
         if n == "dxp":
@@ -298,3 +296,12 @@ def test_fp8_backward_token_gather_entry_is_bit_identical(case, over, seed, cap)
         same = torch.equal(got.view(torch.int16) if got.dtype == torch.bfloat16 else got.view(torch.int32),
                            t.view(torch.int16) if t.dtype == torch.bfloat16 else t.view(torch.int32))
         assert same, n
+
+
+@pytest.mark.parametrize("case,over,seed,cap", GATHER_CASES, ids=[c[0] for c in GATHER_CASES])
+def test_fp8_backward_token_gather_entry_is_bit_identical(case, over, seed, cap):
+    """moe_grouped_swiglu_bwd_fp8_tok (w * dY and Xp gathered from dY and x
+    where they are quantized) against moe_grouped_swiglu_bwd_fp8 on the
+    dispatched bf16 copies of the same values: every output bit-identical."""
+    wl = moe_synth.WORKLOADS["dsmoe"].scaled(name=case, dtype="fp8", **over)
+    gather_entry_matches(wl, moe_synth.gen_all(wl, seed=seed), cap)

@@ -108,3 +108,14 @@ def test_random_shape_router_backward(seed):
     sh = _shape(60 + seed)
     test_router_bwd_unit(f"rand_router_{seed}", dict(T=sh["T"], h=sh["h"], E=sh["E"], k=sh["k"]), 0.03,
                          "bf16", 70 + seed)
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_random_shape_fp8_token_gather_bit_identical(seed):
+    """The FP8 backward's two entry points (operands gathered from dY and x,
+    or read from their dispatched bf16 copies) agree bit for bit."""
+    from test_gpu_backward_fp8 import gather_entry_matches
+    over = _shape(100 + seed)
+    wl = moe_synth.WORKLOADS["dsmoe"].scaled(name=f"randg{seed}", dtype="fp8", **over)
+    say(f"random shape (FP8 gather) {seed}: {wl}")
+    gather_entry_matches(wl, moe_synth.gen_all(wl, seed=seed))
