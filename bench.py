@@ -113,9 +113,11 @@ def cpu_baseline(wl, inp, n_tokens, seed=0):
 OTHER_WORKLOADS = ("dsmoe", "dsmoe_fp8", "hunyuan_fp8", "m352b_zipf", "mixtral22b", "phi35")
 
 
-def measure(name, steps, warmup, cold):
+def measure(name, steps, warmup, cold, arrival=False):
     """Generate one workload's inputs, time `steps` layer steps after `warmup`
-    untimed ones, and return (the JSON fields, the workload, its host inputs)."""
+    untimed ones, and return (the JSON fields, the workload, its host inputs).
+    With `arrival` (BF16 workloads) the layer overlaps its dispatch copy and
+    FC1 by tile arrival (moe_dispatch_swiglu_fwd)."""
     import numpy as np
     import torch
 
@@ -144,7 +146,7 @@ def measure(name, steps, warmup, cold):
     dy = t(inp["dy"]) if wl.backward else None
 
     def step():
-        layer.forward(x, wg, bias, P)
+        layer.forward(x, wg, bias, P, arrival=arrival)
         if wl.backward:
             layer.aux_loss(AUX_ALPHA)
             layer.backward(dy, x, P, w_gate=wg, alpha=AUX_ALPHA)
@@ -237,7 +239,8 @@ def measure(name, steps, warmup, cold):
         "steps": steps, "warmup": warmup, "ms_per_step": ms, "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": wl.dtype, "data": "synthetic",
         "config": {"workload": f"{wl.name} MoE layer {'fwd+bwd' if wl.backward else 'fwd'}",
-                   "T": wl.T, "h": wl.h, "h_ffn": wl.h_ffn, "E": wl.E, "k": wl.k},
+                   "T": wl.T, "h": wl.h, "h_ffn": wl.h_ffn, "E": wl.E, "k": wl.k,
+                   **({"dispatch": "tile arrival (copy and FC1 overlapped)"} if arrival else {})},
         "gemm_tflops": gemm_tflops, "gemm_frac_of_peak": (gemm_tflops * 1e12 / peak) if gemm_tflops else None,
         "kernel_ms_per_step": {k: round(v, 4) for k, v in per_step.items()},
         "hbm": hbm,
@@ -254,6 +257,11 @@ def measure(name, steps, warmup, cold):
     return out, wl, inp
 
 
+def moe_synth_dtype(name):
+    import moe_synth
+    return moe_synth.WORKLOADS[name].dtype
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -261,6 +269,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=None,
                     help="one workload only (default: mixtral, then the other shapes as `other_workloads`)")
+    ap.add_argument("--arrival", action="store_true",
+                    help="with --workload (BF16): overlap the dispatch copy and FC1 by tile arrival")
     ap.add_argument("--cpu-tokens", type=int, default=8192,
                     help="most tokens in the CPU oracle sample, kept under ~45 s (0 = skip)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
@@ -284,7 +294,10 @@ def main():
         sys.exit(2)
 
     primary = args.workload or "mixtral"
-    out, wl, inp = measure(primary, args.steps, args.warmup, cold=True)
+    if args.arrival and (args.workload is None or moe_synth_dtype(primary) != "bf16"):
+        print("--arrival needs --workload with a BF16 workload", file=sys.stderr)
+        sys.exit(2)
+    out, wl, inp = measure(primary, args.steps, args.warmup, cold=True, arrival=args.arrival)
     if args.workload is None:
         # the other workloads of the same build, timed in the same run with the
         # same step counts (no cold-cache pass): figures beside `value`

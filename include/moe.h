@@ -349,6 +349,34 @@ int moe_grouped_swiglu_bwd_fp8_tok(const void* dyp_q, const float* dyp_scale, co
                                    float* dw2, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * The index, the dispatch copy and the expert forward in one call, with the
+ * copy and FC1 overlapped by tile arrival (MegaScale-MoE research digest
+ * §3.3 Diagram C and paper review §四 intra-operator overlap: the GEMM starts
+ * a tile as soon as its rows have arrived, flagged on the device, instead of
+ * after the whole exchange).  On one GPU the dispatch copy plays the
+ * exchange: it runs on a second stream of the library's own, in row order,
+ * and releases each expert's rows as they land; FC1 waits until a tile's
+ * expert has landed whole before loading the tile (the flag is per expert, so
+ * the workgroups that share the expert's slabs in L2 start together).  Results
+ * are those of moe_permute (index and BF16 copy) followed by
+ * moe_grouped_swiglu_fwd, bit for bit.
+ *   x [T][h] bf16; topk_idx [T][k] as for moe_permute; counts, offsets,
+ *   dst_row, src_tok: moe_permute's index outputs; xp [T*k][h] bf16 out.
+ *   W: MOE_BF16 weights; h13_save, yp, yp_dtype as moe_grouped_swiglu_fwd.
+ *   status: one int32 on the device, set to 0 by the call, and to 1 if a wait
+ *   of FC1 for its rows gave up after ~0.5 s (the copy found no room beside
+ *   it, e.g. another process filling the GPU): then yp and h13_save are not
+ *   valid.
+ *   The call returns once everything is enqueued on `stream`; later work on
+ *   `stream` runs after the copy too.
+ */
+size_t moe_dispatch_swiglu_fwd_workspace_size(int T, int k, int h, int h_ffn, int E);
+int moe_dispatch_swiglu_fwd(const void* x, const int32_t* topk_idx, int T, int k, int32_t* counts,
+                            int32_t* offsets, int32_t* dst_row, int32_t* src_tok, const moe_weights* W,
+                            void* xp, void* h13_save, void* yp, int yp_dtype, int32_t* status, void* ws,
+                            size_t ws_bytes, void* stream);
+
+/*
  * Router backward: gradients of  sum_t <dY_t, y_t> + L_aux  through the gate
  * (MegaScale-MoE paper review, §三 MoE layer structure: the gating network is
  * trainable), with the top-k selection held fixed.  For each token t,

@@ -53,6 +53,8 @@ SIGNATURES = {
     "moe_grouped_swiglu_bwd_fp8": (I, [P, P, P, P, P, ctypes.POINTER(MoeWeights), P, I, P, P, P, P, P, SZ, P]),
     "moe_grouped_swiglu_bwd_fp8_tok": (I, [P, P, P, P, P, P, I, I, P, ctypes.POINTER(MoeWeights), P, I, P, P, P,
                                            P, P, SZ, P]),
+    "moe_dispatch_swiglu_fwd_workspace_size": (SZ, [I, I, I, I, I]),
+    "moe_dispatch_swiglu_fwd": (I, [P, P, I, I, P, P, P, P, ctypes.POINTER(MoeWeights), P, P, P, I, P, P, SZ, P]),
     "moe_router_bwd_workspace_size": (SZ, [I, I, I]),
     "moe_router_bwd": (I, [P, P, I, P, P, P, P, P, I, I, I, I, F, I, P, P, P, P, P, P, P, P, SZ, P]),
     "moe_router_aux_workspace_size": (SZ, [I, I]),

@@ -437,6 +437,34 @@ int moe_grouped_swiglu_bwd_fp8_tok(const void* dyp_q, const float* dyp_scale, co
                   "moe_grouped_swiglu_bwd_fp8_tok");
 }
 
+size_t moe_dispatch_swiglu_fwd_workspace_size(int T, int k, int h, int h_ffn, int E) {
+  if (T < 0 || k < 1 || h <= 0 || h_ffn <= 0 || E < 1) return 0;
+  return moe_launch::arrival_ws_bytes(T, k, h, h_ffn, E);
+}
+
+int moe_dispatch_swiglu_fwd(const void* x, const int32_t* topk_idx, int T, int k, int32_t* counts,
+                            int32_t* offsets, int32_t* dst_row, int32_t* src_tok, const moe_weights* W,
+                            void* xp, void* h13_save, void* yp, int yp_dtype, int32_t* status, void* ws,
+                            size_t ws_bytes, void* stream) {
+  int rc = check_weights(W);
+  if (rc) return rc;
+  REQ(W->dtype == MOE_BF16, MOE_ERR_DTYPE, "the tile-arrival forward needs BF16 weights");
+  REQ(yp_dtype == MOE_BF16 || yp_dtype == MOE_F32, MOE_ERR_DTYPE, "yp dtype %d unsupported", yp_dtype);
+  REQ(T >= 0, MOE_ERR_ARG, "T=%d is negative", T);
+  REQ(k >= 1 && k <= W->E && k <= MOE_MAX_TOPK, MOE_ERR_ARG, "k=%d outside [1, min(E, %d)]", k,
+      MOE_MAX_TOPK);
+  PTR(x); PTR(topk_idx); PTR(counts); PTR(offsets); PTR(dst_row); PTR(src_tok); PTR(xp); PTR(yp);
+  PTR(status); OPT(h13_save);
+  const size_t need = moe_launch::arrival_ws_bytes(T, k, W->h, W->h_ffn, W->E);
+  REQ(ws != nullptr && ws_bytes >= need, MOE_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given",
+      need, ws ? ws_bytes : size_t(0));
+  moe_launch::clear_status();
+  return launched(moe_launch::dispatch_swiglu_fwd(x, topk_idx, T, k, counts, offsets, dst_row, src_tok, W,
+                                                  xp, h13_save, yp, yp_dtype == MOE_F32, status, ws,
+                                                  (hipStream_t)stream),
+                  "moe_dispatch_swiglu_fwd");
+}
+
 size_t moe_router_bwd_workspace_size(int T, int h, int E) {
   if (T <= 0 || h <= 0 || E <= 0) return 0;
   return moe_launch::router_bwd_ws_bytes(T, h, E);

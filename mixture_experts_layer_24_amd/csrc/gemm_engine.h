@@ -73,6 +73,8 @@ enum {
   kModeBwdDA = 2, // dG, dU from dA and the kept G|U; also A = SiLU(G)*U
   kModeDW = 3,    // fp32 [E][M][N]
   kModeDW13 = 4,  // fp32 [E][M][2*h_ffn packed] split into dW1 / dW3
+  kModeFC1Arr = 5,  // FC1 (bf16) whose row tiles wait until a concurrent dispatch copy has
+                    // released their rows (see GemmArgs::ready)
 };
 
 struct GemmArgs {
@@ -94,6 +96,11 @@ struct GemmArgs {
   float* part;            // split-K partial tiles (kMaxGrid tiles) or null: no split
   uint32_t* cnt;          // split-K arrival counters [kMaxGrid], zero before the launch
   int out_f32;            // FC2: 1 stores the output in fp32 (bf16 and FP8 operands too)
+  // FC1Arr: rows of each expert that the dispatch copy has written and
+  // released, the rows written in all, and a word set to 1 if a wait gave up
+  const uint32_t* ready;
+  const uint32_t* done;
+  int32_t* status;
 };
 
 // LDS byte position of 16-byte chunk c of row r (pitch RB bytes): chunks are
@@ -714,6 +721,9 @@ __global__ void __launch_bounds__(C::kThreads, C::kWavesPerSimd) grouped_gemm_ke
   __shared__ int offs[MOE_MAX_EXPERTS + 1];  // SchedM / KR: row offsets; SchedK: padded K prefix
   __shared__ int split_flag;
   constexpr int EB = Elem<DT>::bytes;
+  constexpr bool ARR = MODE == kModeFC1Arr;
+  constexpr int EMODE = ARR ? kModeFC1 : MODE;  // the epilogue's mode
+  static_assert(!ARR || (SCHED == kSchedM && DT == MOE_BF16), "tile arrival: bf16 FC1");
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int wm = wave / C::kWN, wn = wave % C::kWN;
@@ -885,6 +895,43 @@ __global__ void __launch_bounds__(C::kThreads, C::kWavesPerSimd) grouped_gemm_ke
   // SchedKR: row pitches of A and B, the lanes' loader offsets
   const int pa = g.M * 2, pb = g.N * 2;
   const LoadOff kla = load_off_kr(pa, lane), klb = load_off_kr(pb, lane);
+  // FC1Arr: before a row tile's first slab is loaded, wait until the
+  // dispatch copy has released all rows of its expert (a bounded wait: thread 0
+  // polls the counts, the workgroup meets it at a barrier, and sleeps between
+  // polls), then acquire.  Once the copy has released every row no tile waits
+  // again.  The poll's result goes through split_flag, which the split-K
+  // combine uses only after a workgroup's last item has loaded its slabs.
+  // Returns true once the copy has released every row.
+  auto gate = [&](const Tile& T) -> bool {
+    const uint32_t need = uint32_t(T.row_end - sld(offs + T.e));
+    const uint32_t total = uint32_t(sld(offs + g.E));
+    int f = 0;
+    for (int it = 0;; ++it) {
+      if (tid == 0) {
+        const uint32_t r = __hip_atomic_load(g.ready + T.e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const uint32_t d = __hip_atomic_load(g.done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        split_flag = (r >= need ? 1 : 0) | (d >= total ? 2 : 0);
+      }
+      __syncthreads();
+      f = split_flag;
+      __syncthreads();
+      if (f) break;
+      if (it == (1 << 20)) {  // ~0.5 s: the copy is not running beside this kernel
+        if (tid == 0) atomicOr(g.status, 1);
+        f = 2;
+        break;
+      }
+      __builtin_amdgcn_s_sleep(16);
+    }
+    // acquire only (agent scope): drop stale lines, no write-back of this
+    // XCD's dirty lines
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    return (f & 2) != 0;
+  };
+  bool all_ready = !ARR;
+  if constexpr (ARR) {
+    if (!ldone) all_ready = gate(lt);
+  }
   // kdst: the stage SchedKR's slab goes to (slab `issued` of the stream)
   auto issue = [&](unsigned char* kdst) {
     if (ldone) return;
@@ -912,6 +959,9 @@ __global__ void __launch_bounds__(C::kThreads, C::kWavesPerSimd) grouped_gemm_ke
       lra = rsrc(g.A, lt.a_off, lt.a_bytes);
       lrb = rsrc(g.B, lt.b_off, lt.b_bytes);
       llo = load_off<RB>(lt.rowB, lane);
+    }
+    if constexpr (ARR) {
+      if (!all_ready) all_ready = gate(lt);
     }
   };
   // wait until slab c has landed: n = slabs issued after it (in flight)
@@ -1039,7 +1089,7 @@ __global__ void __launch_bounds__(C::kThreads, C::kWavesPerSimd) grouped_gemm_ke
     // tile runs the epilogue.  Stage (c - 1) % NS holds no slab in flight.
     if (cur.split < 0 || splitk_combine<C>(g, acc, ((t - full) / f) * f, f, cur.split,
                                            (t - full) / f, wave, lane, &split_flag))
-      epilogue<C, DT, MODE>(g, acc, cur, wave, wm, wn, half, l32,
+      epilogue<C, DT, EMODE>(g, acc, cur, wave, wm, wn, half, l32,
                             stage((c + NS - 1) % NS));
     drain = true;
     t += G;

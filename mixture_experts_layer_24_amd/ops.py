@@ -160,6 +160,17 @@ def moe_grouped_swiglu_bwd_fp8_tok(dyp_q, dyp_scale, dy, x, dst_row, topk_w, T, 
                                                       _p(ws), ws_bytes, _s(stream)))
 
 
+def moe_dispatch_swiglu_fwd_workspace_size(T, k, h, h_ffn, E):
+    return lib().moe_dispatch_swiglu_fwd_workspace_size(T, k, h, h_ffn, E)
+
+
+def moe_dispatch_swiglu_fwd(x, topk_idx, T, k, counts, offsets, dst_row, src_tok, W, xp, h13_save, yp, yp_dtype,
+                            status, ws, ws_bytes, stream=None):
+    return check(lib().moe_dispatch_swiglu_fwd(_p(x), _p(topk_idx), T, k, _p(counts), _p(offsets), _p(dst_row),
+                                               _p(src_tok), ctypes.byref(W), _p(xp), _p(h13_save), _p(yp), yp_dtype,
+                                               _p(status), _p(ws), ws_bytes, _s(stream)))
+
+
 def moe_last_error() -> str:
     return lib().moe_last_error().decode()
 
@@ -243,10 +254,12 @@ class MoELayer:
         self.bwd_ready = False
 
     def forward(self, x, w_gate, bias, W: PackedWeights, logits_in=None, capacity=None, group=1,
-                stream=None):
+                stream=None, arrival=False):
         """One layer forward.  With ``capacity``, pairs beyond the capacity of
         each group of ``group`` experts are dropped by affinity before the
-        dispatch (moe_capacity_drop)."""
+        dispatch (moe_capacity_drop).  With ``arrival`` (BF16), the dispatch
+        copy and FC1 overlap by tile arrival (moe_dispatch_swiglu_fwd; the
+        status word is ``self.arrival_status``)."""
         T, h, E, k = self.T, self.h, self.E, self.k
         if logits_in is None:
             moe_route(x, w_gate, bias, self.logits, T, h, E, k, dtype_code(x), self.topk_idx,
@@ -262,11 +275,20 @@ class MoELayer:
                 self.cws = torch.empty(max(self.cws_bytes, 256), dtype=torch.uint8, device=self.y.device)
             moe_capacity_drop(self.topk_idx, self.logits_used, T, E, k, group, capacity, self.topk_idx,
                               self.cws, self.cws_bytes, stream)
-        moe_permute(x, dtype_code(x), self.topk_idx, None, T, h, E, k, self.counts, self.offsets,
-                    self.dst_row, self.src_tok, self.xp, self.dtype, self.xp_scale, self.pws,
-                    self.pws_bytes, stream)
-        moe_grouped_swiglu_fwd(self.xp, self.xp_scale, W.struct, self.offsets, self.R, self.h13,
-                               self.yp, self.yp_code, self.gws, self.gws_bytes, stream)
+        if arrival:
+            if not hasattr(self, "aws"):
+                self.aws_bytes = moe_dispatch_swiglu_fwd_workspace_size(T, k, h, self.h_ffn, E)
+                self.aws = torch.empty(max(self.aws_bytes, 256), dtype=torch.uint8, device=self.y.device)
+                self.arrival_status = torch.zeros(1, dtype=torch.int32, device=self.y.device)
+            moe_dispatch_swiglu_fwd(x, self.topk_idx, T, k, self.counts, self.offsets, self.dst_row, self.src_tok,
+                                    W.struct, self.xp, self.h13, self.yp, self.yp_code, self.arrival_status,
+                                    self.aws, self.aws_bytes, stream)
+        else:
+            moe_permute(x, dtype_code(x), self.topk_idx, None, T, h, E, k, self.counts, self.offsets,
+                        self.dst_row, self.src_tok, self.xp, self.dtype, self.xp_scale, self.pws,
+                        self.pws_bytes, stream)
+            moe_grouped_swiglu_fwd(self.xp, self.xp_scale, W.struct, self.offsets, self.R, self.h13,
+                                   self.yp, self.yp_code, self.gws, self.gws_bytes, stream)
         moe_combine(self.yp, self.yp_code, self.dst_row, self.topk_w, T, h, k, self.y,
                     self.io_code, stream)
         return self.y

@@ -238,3 +238,24 @@ def test_grouped_bwd_fp8_tok_validation():
         assert call(**{name: None}) == L.MOE_ERR_ARG, name
     Wb = L.MoeWeights(L.MOE_BF16, 8, 256, 384, A.value, A.value, None, None, A.value, A.value, None, None)
     assert call(W=Wb) == L.MOE_ERR_DTYPE
+
+
+def test_dispatch_swiglu_fwd_validation():
+    """The tile-arrival forward rejects bad arguments before any launch."""
+    lib = L.lib()
+    need = lib.moe_dispatch_swiglu_fwd_workspace_size(500, 2, 256, 384, 8)
+    assert need > 0
+    Wb = L.MoeWeights(L.MOE_BF16, 8, 256, 384, A.value, A.value, None, None, None, None, None, None)
+
+    def call(W=Wb, T=500, k=2, yp_dtype=L.MOE_BF16, x=A, status=A, ws=A, wsb=need):
+        return lib.moe_dispatch_swiglu_fwd(x, A, T, k, A, A, A, A, ctypes.byref(W), A, None, A, yp_dtype, status,
+                                           ws, wsb, None)
+    assert call(wsb=need - 1) == L.MOE_ERR_WORKSPACE
+    assert call(k=0) == L.MOE_ERR_ARG
+    assert call(k=9) == L.MOE_ERR_ARG                 # k > E
+    assert call(T=-1) == L.MOE_ERR_ARG
+    assert call(x=None) == L.MOE_ERR_ARG
+    assert call(status=None) == L.MOE_ERR_ARG
+    assert call(yp_dtype=L.MOE_FP8_E4M3) == L.MOE_ERR_DTYPE
+    Wq = L.MoeWeights(L.MOE_FP8_E4M3, 8, 256, 384, A.value, A.value, A.value, A.value, None, None, None, None)
+    assert call(W=Wq) == L.MOE_ERR_DTYPE
