@@ -377,6 +377,21 @@ int moe_dispatch_swiglu_fwd(const void* x, const int32_t* topk_idx, int T, int k
                             size_t ws_bytes, void* stream);
 
 /*
+ * Test of FC1's bounded waits in moe_dispatch_swiglu_fwd (same arguments and
+ * checks): the index is built and FC1 and FC2 run, but the dispatch copy is
+ * left out and a wait gives up after 64 polls instead of 2^20, so every wait
+ * gives up and *status must read 1 once the stream has finished; xp is not
+ * written, and h13_save and yp hold FC1/FC2 of whatever xp held.  The kernels
+ * end normally; a later moe_dispatch_swiglu_fwd clears the status and the
+ * flags itself.
+ */
+int moe_dispatch_swiglu_fwd_wait_selftest(const void* x, const int32_t* topk_idx, int T, int k,
+                                          int32_t* counts, int32_t* offsets, int32_t* dst_row,
+                                          int32_t* src_tok, const moe_weights* W, void* xp,
+                                          void* h13_save, void* yp, int yp_dtype, int32_t* status,
+                                          void* ws, size_t ws_bytes, void* stream);
+
+/*
  * Router backward: gradients of  sum_t <dY_t, y_t> + L_aux  through the gate
  * (MegaScale-MoE paper review, §三 MoE layer structure: the gating network is
  * trainable), with the top-k selection held fixed.  For each token t,

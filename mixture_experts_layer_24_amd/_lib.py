@@ -55,6 +55,7 @@ SIGNATURES = {
                                            P, P, SZ, P]),
     "moe_dispatch_swiglu_fwd_workspace_size": (SZ, [I, I, I, I, I]),
     "moe_dispatch_swiglu_fwd": (I, [P, P, I, I, P, P, P, P, ctypes.POINTER(MoeWeights), P, P, P, I, P, P, SZ, P]),
+    "moe_dispatch_swiglu_fwd_wait_selftest": (I, [P, P, I, I, P, P, P, P, ctypes.POINTER(MoeWeights), P, P, P, I, P, P, SZ, P]),
     "moe_router_bwd_workspace_size": (SZ, [I, I, I]),
     "moe_router_bwd": (I, [P, P, I, P, P, P, P, P, I, I, I, I, F, I, P, P, P, P, P, P, P, P, SZ, P]),
     "moe_router_aux_workspace_size": (SZ, [I, I]),

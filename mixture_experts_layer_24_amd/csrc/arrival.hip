@@ -139,7 +139,7 @@ static int side_stream(SideStream** out) {
 int dispatch_swiglu_fwd(const void* x, const int32_t* topk_idx, int T, int k, int32_t* counts,
                         int32_t* offsets, int32_t* dst_row, int32_t* src_tok, const moe_weights* W,
                         void* xp, void* h13_save, void* yp, int yp_f32, int32_t* status, void* ws,
-                        hipStream_t s) {
+                        hipStream_t s, int spin_limit, bool copy) {
   const int h = W->h, hf = W->h_ffn, E = W->E, rows = T * k;
   unsigned char* w = static_cast<unsigned char*>(ws);
   void* iws = w;
@@ -157,23 +157,26 @@ int dispatch_swiglu_fwd(const void* x, const int32_t* topk_idx, int T, int k, in
   if ((rc = launch_status())) return rc;
   if (rows == 0) return MOE_OK;
   SideStream* ss = nullptr;
-  if ((rc = side_stream(&ss))) return rc;
-  // the copy on the side stream, after everything enqueued so far
-  if (hipEventRecord(ss->fork, s) != hipSuccess || hipStreamWaitEvent(ss->s, ss->fork, 0) != hipSuccess)
-    return MOE_ERR_HIP;
-  timer_begin(kTPermute, ss->s);
-  hipLaunchKernelGGL(dispatch_flag_kernel, dim3(ceil_div(rows, kArrRows)), dim3(256), 0, ss->s,
-                     static_cast<const uint16_t*>(x), src_tok, offsets, E, h,
-                     static_cast<uint16_t*>(xp), ready, done);
-  timer_end(kTPermute, ss->s);
-  if (hipEventRecord(ss->join, ss->s) != hipSuccess) return MOE_ERR_HIP;
+  if (copy && (rc = side_stream(&ss))) return rc;
+  // the copy on the side stream, after everything enqueued so far (left out
+  // only to test FC1's bounded waits)
+  if (copy) {
+    if (hipEventRecord(ss->fork, s) != hipSuccess || hipStreamWaitEvent(ss->s, ss->fork, 0) != hipSuccess)
+      return MOE_ERR_HIP;
+    timer_begin(kTPermute, ss->s);
+    hipLaunchKernelGGL(dispatch_flag_kernel, dim3(ceil_div(rows, kArrRows)), dim3(256), 0, ss->s,
+                       static_cast<const uint16_t*>(x), src_tok, offsets, E, h,
+                       static_cast<uint16_t*>(xp), ready, done);
+    timer_end(kTPermute, ss->s);
+    if (hipEventRecord(ss->join, ss->s) != hipSuccess) return MOE_ERR_HIP;
+  }
   // FC1 on the caller's stream, each row tile waiting for its rows
   GemmArgs a1{xp, nullptr, W->w13, nullptr, offsets, E, h, 2 * hf, rows, 0,
-              act, nullptr, h13_save, nullptr, nullptr, nullptr, 0, ready, done, status};
+              act, nullptr, h13_save, nullptr, nullptr, nullptr, 0, ready, done, status, spin_limit};
   splitk_ws_set<CfgA>(a1, split_ws);
   if ((rc = launch_gemm<CfgA, MOE_BF16, kModeFC1Arr, kSchedM>(a1, kTFc1, s))) return rc;
   // the caller's later work (FC2 first) after the copy
-  if (hipStreamWaitEvent(s, ss->join, 0) != hipSuccess) return MOE_ERR_HIP;
+  if (copy && hipStreamWaitEvent(s, ss->join, 0) != hipSuccess) return MOE_ERR_HIP;
   GemmArgs a2{act, nullptr, W->w2, nullptr, offsets, E, hf, h, rows, 0, yp, nullptr, nullptr, nullptr,
               nullptr, nullptr, yp_f32};
   splitk_ws_set<CfgA>(a2, split_ws);

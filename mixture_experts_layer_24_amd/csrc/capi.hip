@@ -442,10 +442,11 @@ size_t moe_dispatch_swiglu_fwd_workspace_size(int T, int k, int h, int h_ffn, in
   return moe_launch::arrival_ws_bytes(T, k, h, h_ffn, E);
 }
 
-int moe_dispatch_swiglu_fwd(const void* x, const int32_t* topk_idx, int T, int k, int32_t* counts,
-                            int32_t* offsets, int32_t* dst_row, int32_t* src_tok, const moe_weights* W,
-                            void* xp, void* h13_save, void* yp, int yp_dtype, int32_t* status, void* ws,
-                            size_t ws_bytes, void* stream) {
+static int dispatch_swiglu_fwd_checked(const void* x, const int32_t* topk_idx, int T, int k,
+                                       int32_t* counts, int32_t* offsets, int32_t* dst_row,
+                                       int32_t* src_tok, const moe_weights* W, void* xp, void* h13_save,
+                                       void* yp, int yp_dtype, int32_t* status, void* ws, size_t ws_bytes,
+                                       void* stream, int spin_limit, bool copy, const char* name) {
   int rc = check_weights(W);
   if (rc) return rc;
   REQ(W->dtype == MOE_BF16, MOE_ERR_DTYPE, "the tile-arrival forward needs BF16 weights");
@@ -461,8 +462,27 @@ int moe_dispatch_swiglu_fwd(const void* x, const int32_t* topk_idx, int T, int k
   moe_launch::clear_status();
   return launched(moe_launch::dispatch_swiglu_fwd(x, topk_idx, T, k, counts, offsets, dst_row, src_tok, W,
                                                   xp, h13_save, yp, yp_dtype == MOE_F32, status, ws,
-                                                  (hipStream_t)stream),
-                  "moe_dispatch_swiglu_fwd");
+                                                  (hipStream_t)stream, spin_limit, copy),
+                  name);
+}
+
+int moe_dispatch_swiglu_fwd(const void* x, const int32_t* topk_idx, int T, int k, int32_t* counts,
+                            int32_t* offsets, int32_t* dst_row, int32_t* src_tok, const moe_weights* W,
+                            void* xp, void* h13_save, void* yp, int yp_dtype, int32_t* status, void* ws,
+                            size_t ws_bytes, void* stream) {
+  return dispatch_swiglu_fwd_checked(x, topk_idx, T, k, counts, offsets, dst_row, src_tok, W, xp, h13_save,
+                                     yp, yp_dtype, status, ws, ws_bytes, stream, 1 << 20, true,
+                                     "moe_dispatch_swiglu_fwd");
+}
+
+int moe_dispatch_swiglu_fwd_wait_selftest(const void* x, const int32_t* topk_idx, int T, int k,
+                                          int32_t* counts, int32_t* offsets, int32_t* dst_row,
+                                          int32_t* src_tok, const moe_weights* W, void* xp,
+                                          void* h13_save, void* yp, int yp_dtype, int32_t* status,
+                                          void* ws, size_t ws_bytes, void* stream) {
+  return dispatch_swiglu_fwd_checked(x, topk_idx, T, k, counts, offsets, dst_row, src_tok, W, xp, h13_save,
+                                     yp, yp_dtype, status, ws, ws_bytes, stream, 64, false,
+                                     "moe_dispatch_swiglu_fwd_wait_selftest");
 }
 
 size_t moe_router_bwd_workspace_size(int T, int h, int E) {

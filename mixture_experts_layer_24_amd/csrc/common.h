@@ -211,7 +211,7 @@ size_t grouped_bwd_fp8_ws_bytes(int rows, int h, int h_ffn, int E);
 int dispatch_swiglu_fwd(const void* x, const int32_t* topk_idx, int T, int k, int32_t* counts,
                         int32_t* offsets, int32_t* dst_row, int32_t* src_tok, const moe_weights* W,
                         void* xp, void* h13_save, void* yp, int yp_f32, int32_t* status, void* ws,
-                        hipStream_t s);
+                        hipStream_t s, int spin_limit = 1 << 20, bool copy = true);
 size_t arrival_ws_bytes(int T, int k, int h, int h_ffn, int E);
 int num_cus();
 

@@ -97,10 +97,12 @@ struct GemmArgs {
   uint32_t* cnt;          // split-K arrival counters [kMaxGrid], zero before the launch
   int out_f32;            // FC2: 1 stores the output in fp32 (bf16 and FP8 operands too)
   // FC1Arr: rows of each expert that the dispatch copy has written and
-  // released, the rows written in all, and a word set to 1 if a wait gave up
+  // released, the rows written in all, a word set to 1 if a wait gave up, and
+  // the polls after which a wait gives up
   const uint32_t* ready;
   const uint32_t* done;
   int32_t* status;
+  int spin_limit;
 };
 
 // LDS byte position of 16-byte chunk c of row r (pitch RB bytes): chunks are
@@ -916,7 +918,7 @@ __global__ void __launch_bounds__(C::kThreads, C::kWavesPerSimd) grouped_gemm_ke
       f = split_flag;
       __syncthreads();
       if (f) break;
-      if (it == (1 << 20)) {  // ~0.5 s: the copy is not running beside this kernel
+      if (it >= g.spin_limit) {  // 2^20 polls, ~0.5 s: the copy is not running beside this kernel
         if (tid == 0) atomicOr(g.status, 1);
         f = 2;
         break;

@@ -171,6 +171,13 @@ def moe_dispatch_swiglu_fwd(x, topk_idx, T, k, counts, offsets, dst_row, src_tok
                                                _p(status), _p(ws), ws_bytes, _s(stream)))
 
 
+def moe_dispatch_swiglu_fwd_wait_selftest(x, topk_idx, T, k, counts, offsets, dst_row, src_tok, W, xp, h13_save,
+                                          yp, yp_dtype, status, ws, ws_bytes, stream=None):
+    return check(lib().moe_dispatch_swiglu_fwd_wait_selftest(
+        _p(x), _p(topk_idx), T, k, _p(counts), _p(offsets), _p(dst_row), _p(src_tok), ctypes.byref(W), _p(xp),
+        _p(h13_save), _p(yp), yp_dtype, _p(status), _p(ws), ws_bytes, _s(stream)))
+
+
 def moe_last_error() -> str:
     return lib().moe_last_error().decode()
 

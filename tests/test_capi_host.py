@@ -259,3 +259,8 @@ def test_dispatch_swiglu_fwd_validation():
     assert call(yp_dtype=L.MOE_FP8_E4M3) == L.MOE_ERR_DTYPE
     Wq = L.MoeWeights(L.MOE_FP8_E4M3, 8, 256, 384, A.value, A.value, A.value, A.value, None, None, None, None)
     assert call(W=Wq) == L.MOE_ERR_DTYPE
+    st = lib.moe_dispatch_swiglu_fwd_wait_selftest
+    assert st(A, A, 500, 2, A, A, A, A, ctypes.byref(Wb), A, None, A, L.MOE_BF16, A, A, need - 1,
+              None) == L.MOE_ERR_WORKSPACE
+    assert st(A, A, 500, 2, A, A, A, A, ctypes.byref(Wb), A, None, A, L.MOE_BF16, None, A, need,
+              None) == L.MOE_ERR_ARG

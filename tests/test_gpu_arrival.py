@@ -65,6 +65,33 @@ def test_arrival_forward_with_capacity_drop():
     _compare(wl, moe_synth.gen_all(wl, seed=6), capacity=160)
 
 
+def test_arrival_wait_gives_up_without_copy():
+    """FC1's waits are bounded: with the copy left out and a 64-poll limit
+    (the wait self-test entry) every wait gives up, the kernels end and the
+    status reads 1; the next real call clears it and matches the plain path."""
+    wl = moe_synth.WORKLOADS["mixtral"].scaled(name="wait", T=300, h=256, h_ffn=384, E=8, k=2)
+    say(f"tile arrival, waits forced to give up: {wl}")
+    inp = moe_synth.gen_all(wl, seed=7)
+    P = ops.PackedWeights(dev_tensor(inp["w1"]), dev_tensor(inp["w3"]), dev_tensor(inp["w2"]), MOE_BF16)
+    x, wg = dev_tensor(inp["x"]), dev_tensor(inp["w_gate"])
+    bias = torch.from_numpy(inp["bias"]).to(DEV)
+    ref = ops.MoELayer(wl.T, wl.h, wl.h_ffn, wl.E, wl.k, MOE_BF16, save_for_backward=True)
+    arr = ops.MoELayer(wl.T, wl.h, wl.h_ffn, wl.E, wl.k, MOE_BF16, save_for_backward=True)
+    ref.forward(x, wg, bias, P)
+    arr.forward(x, wg, bias, P, arrival=True)
+    torch.cuda.synchronize()
+    assert int(arr.arrival_status.item()) == 0
+    ops.moe_dispatch_swiglu_fwd_wait_selftest(x, arr.topk_idx, wl.T, wl.k, arr.counts, arr.offsets, arr.dst_row,
+                                              arr.src_tok, P.struct, arr.xp, arr.h13, arr.yp, arr.yp_code,
+                                              arr.arrival_status, arr.aws, arr.aws_bytes)
+    torch.cuda.synchronize()
+    assert int(arr.arrival_status.item()) == 1, "a wait with no copy beside it did not give up"
+    arr.forward(x, wg, bias, P, arrival=True)
+    torch.cuda.synchronize()
+    assert int(arr.arrival_status.item()) == 0
+    assert torch.equal(_bits(arr.y), _bits(ref.y))
+
+
 @pytest.mark.slow
 def test_arrival_forward_full_size_mixtral():
     """The Mixtral-shaped layer (T 8192, h 4096, h_ffn 14336, E 8, k 2)."""
