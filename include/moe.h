@@ -356,8 +356,7 @@ int moe_grouped_swiglu_bwd_fp8_tok(const void* dyp_q, const float* dyp_scale, co
  * after the whole exchange).  On one GPU the dispatch copy plays the
  * exchange: it runs on a second stream of the library's own, in row order,
  * and releases each expert's rows as they land; FC1 waits until a tile's
- * expert has landed whole before loading the tile (the flag is per expert, so
- * the workgroups that share the expert's slabs in L2 start together).  Results
+ * expert has landed whole before loading the tile.  Results
  * are those of moe_permute (index and BF16 copy) followed by
  * moe_grouped_swiglu_fwd, bit for bit.
  *   x [T][h] bf16; topk_idx [T][k] as for moe_permute; counts, offsets,

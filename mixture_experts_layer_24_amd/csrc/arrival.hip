@@ -10,11 +10,9 @@
 // order, and counts each expert's rows as they land; FC1 (GemmArgs::ready,
 // mode kModeFC1Arr) waits until all of a tile's expert has landed before
 // loading the tile's first slab.  The flag is per expert, not per 256-row
-// tile: the workgroups of one XCD take all row tiles of an expert against a
-// few weight blocks and reuse each other's slabs in L2 only while they stay in
-// step, and a persistent kernel whose workgroups start skewed stays skewed
-// (per-tile flags: Mixtral-shaped FC1 3.4 -> 4.2 ms).  FC2 then runs as in the
-// plain forward.
+// tile: E + 1 counters, and the workgroups of one XCD, which take the row
+// tiles of an expert against a few weight blocks, start together; flags per
+// row tile measured the same.  FC2 then runs as in the plain forward.
 // The copy, FC1 and FC2 compute exactly what moe_permute and
 // moe_grouped_swiglu_fwd compute, so the results are the same bit for bit.
 //
