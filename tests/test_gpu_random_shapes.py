@@ -1,6 +1,7 @@
 """GPU parity on seeded random shapes: the layer forward and backward (BF16),
-the FP8 forward, the FP8 backward and the router backward, routing fed the
-oracle's fp32 logits.
+the FP8 forward, the FP8 backward, the router backward and the tile-arrival
+forward (against the plain entries, bit for bit, on the GPU's own routing); the
+others with routing fed the oracle's fp32 logits.
 
 Shapes are drawn per seed: T from 1 to 700, h and h_ffn in {128, 256, 384}
 (one to three 128-wide blocks, so tiles end ragged in every dimension), E from
@@ -119,3 +120,14 @@ def test_random_shape_fp8_token_gather_bit_identical(seed):
     wl = moe_synth.WORKLOADS["dsmoe"].scaled(name=f"randg{seed}", dtype="fp8", **over)
     say(f"random shape (FP8 gather) {seed}: {wl}")
     gather_entry_matches(wl, moe_synth.gen_all(wl, seed=seed))
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_random_shape_arrival_bit_identical(seed):
+    """The tile-arrival forward (copy beside FC1, per-expert flags) equals
+    moe_permute + moe_grouped_swiglu_fwd bit for bit, with no wait giving up."""
+    from test_gpu_arrival import _compare
+    over = _shape(200 + seed)
+    wl = moe_synth.WORKLOADS["dsmoe"].scaled(name=f"randa{seed}", **over)
+    say(f"random shape (tile arrival) {seed}: {wl}")
+    _compare(wl, moe_synth.gen_all(wl, seed=seed))
