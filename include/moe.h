@@ -367,7 +367,9 @@ int moe_grouped_swiglu_bwd_fp8_tok(const void* dyp_q, const float* dyp_scale, co
  *   it, e.g. another process filling the GPU): then yp and h13_save are not
  *   valid.
  *   The call returns once everything is enqueued on `stream`; later work on
- *   `stream` runs after the copy too.
+ *   `stream` runs after the copy too.  The second stream is one per device,
+ *   shared by all calls: copies of calls on different streams run one after
+ *   another; calls that share ws, or any output, and overlap race.
  */
 size_t moe_dispatch_swiglu_fwd_workspace_size(int T, int k, int h, int h_ffn, int E);
 int moe_dispatch_swiglu_fwd(const void* x, const int32_t* topk_idx, int T, int k, int32_t* counts,
